@@ -1,0 +1,346 @@
+/*
+ * gdn_oracle.c -- plain CPU oracle for the GDN recurrent decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY (see gdn_oracle.h).  Build with
+ *   gcc -std=c99 -O2 -ffp-contract=off -fno-fast-math
+ * so that every fp32 multiply and add is rounded on its own and no reduction
+ * is re-associated or vectorised.  The loops follow the order in which the
+ * operator is stated: decay, key read-out, delta, rank-1 update, query
+ * read-out with the updated state.
+ */
+#include "gdn_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int dims_ok(int64_t n, int vh, int kh, int kd, int vd)
+{
+    return n >= 0 && vh > 0 && kh > 0 && kd > 0 && vd > 0 && vh % kh == 0;
+}
+
+/*
+ * One value head of one unit.  "Kestrel_VLLM #24", section 4 (delta
+ * recurrence kernel; one column dv of the state at a time) and Fig. 1 caption
+ * (alpha scale -> S.k -> (v - .) beta -> rank-1 add -> S.q with the updated
+ * state).  Per column dv:
+ *   pass 1 over dk: t = S[dk][dv] * alpha; S[dk][dv] = t; kv = kv + t * k[dk]
+ *   tmp = (v[dv] - kv) * beta
+ *   pass 2 over dk: t = S[dk][dv] + k[dk] * tmp; S[dk][dv] = t; oa = oa + t * q[dk]
+ *   o[dv] = oa
+ * Columns are independent; the folds over dk are strict left folds.
+ */
+static void step_head(float *Sh, const float *qh, const float *kh_,
+                      const float *vrow, float alpha, float bt, float *orow,
+                      int kd, int vd)
+{
+    for (int dv = 0; dv < vd; dv++) {
+        float kv = 0.0f;
+        for (int dk = 0; dk < kd; dk++) {
+            float t = Sh[(size_t)dk * vd + dv] * alpha;
+            Sh[(size_t)dk * vd + dv] = t;
+            kv = kv + t * kh_[dk];
+        }
+        float tmp = (vrow[dv] - kv) * bt;
+        float oa = 0.0f;
+        for (int dk = 0; dk < kd; dk++) {
+            float t = Sh[(size_t)dk * vd + dv] + kh_[dk] * tmp;
+            Sh[(size_t)dk * vd + dv] = t;
+            oa = oa + t * qh[dk];
+        }
+        if (orow)
+            orow[dv] = oa;
+    }
+}
+
+/* One unit, one step.  Value head i uses key head i / (vh/kh) ("Kestrel_VLLM
+ * #24", section 4: rep = vh/kh, key head = vi/rep). */
+static void step_unit(float *Su, const float *qu, const float *ku,
+                      const float *vu, const float *gu, const float *bu,
+                      float *ou, int vh, int kh, int kd, int vd)
+{
+    const int rep = vh / kh;
+    for (int i = 0; i < vh; i++) {
+        const int hh = i / rep;
+        const float alpha = expf(gu[i]);
+        step_head(Su + (size_t)i * kd * vd, qu + (size_t)hh * kd,
+                  ku + (size_t)hh * kd, vu + (size_t)i * vd, alpha, bu[i],
+                  ou ? ou + (size_t)i * vd : NULL, kd, vd);
+    }
+}
+
+int ref_gdn_step(float *S, const float *q, const float *k, const float *v,
+                 const float *g, const float *beta, float *o,
+                 int64_t n_units, int vh, int kh, int kd, int vd)
+{
+    if (!dims_ok(n_units, vh, kh, kd, vd))
+        return -1;
+    if (n_units == 0)
+        return 0;
+    if (!S || !q || !k || !v || !g || !beta || !o)
+        return -1;
+    for (int64_t u = 0; u < n_units; u++)
+        step_unit(S + (size_t)u * vh * kd * vd, q + (size_t)u * kh * kd,
+                  k + (size_t)u * kh * kd, v + (size_t)u * vh * vd,
+                  g + (size_t)u * vh, beta + (size_t)u * vh,
+                  o + (size_t)u * vh * vd, vh, kh, kd, vd);
+    return 0;
+}
+
+/* "Kestrel_VLLM #34", section 3.6: the recurrence is serial in time; M rows
+ * are M single steps in order, each with row m's inputs, the state advancing
+ * in place.  No chunked scan. */
+int ref_gdn_step_m(float *S, const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, float *o,
+                   int64_t n_units, int M, int vh, int kh, int kd, int vd)
+{
+    if (!dims_ok(n_units, vh, kh, kd, vd) || M < 0)
+        return -1;
+    if (n_units == 0 || M == 0)
+        return 0;
+    const size_t nqk = (size_t)n_units * kh * kd;
+    const size_t nv = (size_t)n_units * vh * vd;
+    const size_t ng = (size_t)n_units * vh;
+    for (int m = 0; m < M; m++) {
+        int rc = ref_gdn_step(S, q + m * nqk, k + m * nqk, v + m * nv,
+                              g + m * ng, beta + m * ng, o + m * nv,
+                              n_units, vh, kh, kd, vd);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
+/* "Kestrel_VLLM #24", section 3 (conv kernel): the history keeps the raw conv
+ * INPUT frames, oldest first; after use it shifts by one and the newest slot
+ * receives the current raw frame. */
+void ref_conv_push(float *hist, const float *raw, int conv_dim, int ck)
+{
+    const int nprev = ck - 1;
+    for (int j = 0; j + 1 < nprev; j++)
+        memcpy(hist + (size_t)j * conv_dim, hist + (size_t)(j + 1) * conv_dim,
+               (size_t)conv_dim * sizeof(float));
+    if (nprev > 0)
+        memcpy(hist + (size_t)(nprev - 1) * conv_dim, raw,
+               (size_t)conv_dim * sizeof(float));
+}
+
+/* "Kestrel_VLLM #34", section 3.7: mark is a plain copy of S and the conv
+ * history; the snapshot is one-shot. */
+int ref_gdn_mark(ref_slab *slab, const float *S, const float *hist)
+{
+    if (!slab || !S || !slab->S_snap)
+        return -1;
+    if (!dims_ok(slab->n_units, slab->vh, slab->kh, slab->kd, slab->vd))
+        return -1;
+    const size_t ns = (size_t)slab->n_units * slab->vh * slab->kd * slab->vd;
+    memcpy(slab->S_snap, S, ns * sizeof(float));
+    if (hist && slab->hist_snap && slab->hist_floats > 0)
+        memcpy(slab->hist_snap, hist,
+               (size_t)slab->n_units * slab->hist_floats * sizeof(float));
+    slab->armed = 1;
+    return 0;
+}
+
+/* Rollback to an accepted length: restore the marked bytes, then re-run the
+ * first accepted[u] single steps of unit u from the rows given to step_m;
+ * the conv history re-receives the same raw frames.  One-shot: disarms.
+ * ("Kestrel_VLLM #34", section 3.7: restore, then the caller replays single
+ * steps; here the replay is folded into the call.) */
+int ref_gdn_rollback(ref_slab *slab, float *S, float *hist,
+                     const float *q, const float *k, const float *v,
+                     const float *g, const float *beta,
+                     const float *xc_raw, int conv_dim, int ck,
+                     int M, const int32_t *accepted)
+{
+    if (!slab || !S || !accepted || !slab->armed || M < 0)
+        return -1;
+    const int64_t N = slab->n_units;
+    const int vh = slab->vh, kh = slab->kh, kd = slab->kd, vd = slab->vd;
+    for (int64_t u = 0; u < N; u++)
+        if (accepted[u] < 0 || accepted[u] > M)
+            return -1;
+    int any = 0;
+    for (int64_t u = 0; u < N; u++)
+        any |= accepted[u] > 0;
+    if (any && (!q || !k || !v || !g || !beta))
+        return -1;
+    const int with_hist = hist && slab->hist_snap && slab->hist_floats > 0;
+    if (with_hist && (ck < 2 || (int64_t)(ck - 1) * conv_dim != slab->hist_floats))
+        return -1;
+    if (with_hist && any && !xc_raw)
+        return -1;
+
+    const size_t per_s = (size_t)vh * kd * vd;
+    memcpy(S, slab->S_snap, (size_t)N * per_s * sizeof(float));
+    if (with_hist)
+        memcpy(hist, slab->hist_snap, (size_t)N * slab->hist_floats * sizeof(float));
+
+    const size_t nqk = (size_t)N * kh * kd, nv = (size_t)N * vh * vd, ng = (size_t)N * vh;
+    for (int64_t u = 0; u < N; u++) {
+        for (int m = 0; m < accepted[u]; m++) {
+            step_unit(S + (size_t)u * per_s, q + m * nqk + (size_t)u * kh * kd,
+                      k + m * nqk + (size_t)u * kh * kd,
+                      v + m * nv + (size_t)u * vh * vd, g + m * ng + (size_t)u * vh,
+                      beta + m * ng + (size_t)u * vh, NULL, vh, kh, kd, vd);
+            if (with_hist)
+                ref_conv_push(hist + (size_t)u * slab->hist_floats,
+                              xc_raw + ((size_t)m * N + (size_t)u) * conv_dim,
+                              conv_dim, ck);
+        }
+    }
+    slab->armed = 0;
+    return 0;
+}
+
+/* softplus with the two overflow guards of "Kestrel_VLLM #24", section 3
+ * (beta/g kernel): identity above 20, exp below -20, log1p(exp) between. */
+static float softplus_guarded(float xa)
+{
+    if (xa > 20.0f)
+        return xa;
+    if (xa < -20.0f)
+        return expf(xa);
+    return log1pf(expf(xa));
+}
+
+int ref_gdn_frontend(const float *x, const float *Wa, const float *Wb,
+                     const float *A_log, const float *dt_bias,
+                     const float *xc_raw, float *hist, const float *conv_w,
+                     float *q, float *k, float *v, float *g, float *beta,
+                     int B, int dim, int conv_dim, int ck,
+                     int vh, int kh, int kd, int vd)
+{
+    if (B < 0 || dim <= 0 || ck < 1 || !dims_ok(1, vh, kh, kd, vd))
+        return -1;
+    if (conv_dim != 2 * kh * kd + vh * vd)
+        return -1;
+    if (B == 0)
+        return 0;
+    if (!x || !Wa || !Wb || !A_log || !dt_bias || !xc_raw || !conv_w ||
+        !q || !k || !v || !g || !beta || (ck > 1 && !hist))
+        return -1;
+
+    const int nprev = ck - 1;
+    const int qk_w = kh * kd;
+    float *out = (float *)malloc((size_t)conv_dim * sizeof(float)); /* one row's conv output */
+    if (!out)
+        return -1;
+    const float q_scale = 1.0f / sqrtf((float)kd);
+
+    for (int b = 0; b < B; b++) {
+        const float *xb = x + (size_t)b * dim;
+        /* (i) paired GEMV ("Kestrel_VLLM #27", section 4.2): two same-shape
+         * row-times-vector products, a from Wa, b from Wb; left folds. */
+        for (int r = 0; r < vh; r++) {
+            float acc_a = 0.0f, acc_b = 0.0f;
+            for (int c = 0; c < dim; c++) {
+                acc_a = acc_a + Wa[(size_t)r * dim + c] * xb[c];
+                acc_b = acc_b + Wb[(size_t)r * dim + c] * xb[c];
+            }
+            /* (ii) gate and beta ("Kestrel_VLLM #24", section 3 and Fig. 1
+             * caption): the gate comes from a, in the log domain and
+             * negative; beta comes from b. */
+            const float xa = acc_a + dt_bias[r];
+            const float sp = softplus_guarded(xa);
+            g[(size_t)b * vh + r] = -expf(A_log[r]) * sp;
+            beta[(size_t)b * vh + r] = 1.0f / (1.0f + expf(-acc_b));
+        }
+
+        /* (iii) depthwise causal conv + SiLU per channel ("Kestrel_VLLM
+         * #24", section 3): taps 0..ck-2 over the history frames (oldest
+         * first), the last tap over the current raw input; then the history
+         * advances by the raw input; then silu(acc) = acc / (1 + exp(-acc)). */
+        const float *raw = xc_raw + (size_t)b * conv_dim;
+        float *hb = hist ? hist + (size_t)b * nprev * conv_dim : NULL;
+        for (int ch = 0; ch < conv_dim; ch++) {
+            const float *cw = conv_w + (size_t)ch * ck;
+            float acc = 0.0f;
+            for (int j = 0; j < nprev; j++)
+                acc = acc + cw[j] * hb[(size_t)j * conv_dim + ch];
+            acc = acc + cw[nprev] * raw[ch];
+            out[ch] = acc / (1.0f + expf(-acc));
+        }
+        if (hb)
+            ref_conv_push(hb, raw, conv_dim, ck);
+
+        /* (iv) split into q | k | v ("Kestrel_VLLM #34", section 3.6: the
+         * step receives the conv output at offsets 0, kh*kd, 2*kh*kd). */
+        float *qb = q + (size_t)b * qk_w, *kb = k + (size_t)b * qk_w;
+        memcpy(qb, out, (size_t)qk_w * sizeof(float));
+        memcpy(kb, out + qk_w, (size_t)qk_w * sizeof(float));
+        memcpy(v + (size_t)b * vh * vd, out + 2 * qk_w, (size_t)vh * vd * sizeof(float));
+
+        /* (v) per key head L2 normalisation ("Kestrel_VLLM #24", Fig. 1
+         * caption and section 4 name the step without a formula):
+         * x * (1/sqrt(sum x^2 + 1e-6)); q additionally * 1/sqrt(kd). */
+        for (int h = 0; h < kh; h++) {
+            float *qh = qb + (size_t)h * kd, *kk = kb + (size_t)h * kd;
+            float ssq = 0.0f, ssk = 0.0f;
+            for (int j = 0; j < kd; j++) {
+                ssq = ssq + qh[j] * qh[j];
+                ssk = ssk + kk[j] * kk[j];
+            }
+            const float iq = 1.0f / sqrtf(ssq + 1e-6f);
+            const float ik = 1.0f / sqrtf(ssk + 1e-6f);
+            for (int j = 0; j < kd; j++) {
+                qh[j] = (qh[j] * iq) * q_scale;
+                kk[j] = kk[j] * ik;
+            }
+        }
+    }
+    free(out);
+    return 0;
+}
+
+/*
+ * Double-precision brute force, re-associated: S' = alpha (I - beta k k^T) S
+ * + beta k v^T and o = S'^T q, with the kd x kd matrix P = alpha (I - beta k
+ * k^T) formed explicitly and multiplied into S.  Algebraically equal to the
+ * column-wise form of step_head: S'^T k-term expands as alpha S - alpha beta
+ * k (k^T S) + beta k v^T.
+ */
+int ref64_gdn_step(double *S, const double *q, const double *k,
+                   const double *v, const double *g, const double *beta,
+                   double *o, int64_t n_units, int vh, int kh, int kd, int vd)
+{
+    if (!dims_ok(n_units, vh, kh, kd, vd) || kd > 16 || vd > 16)
+        return -1;
+    if (!S || !q || !k || !v || !g || !beta || !o)
+        return -1;
+    const int rep = vh / kh;
+    for (int64_t u = 0; u < n_units; u++) {
+        for (int i = 0; i < vh; i++) {
+            const int hh = i / rep;
+            double *Sh = S + ((size_t)u * vh + i) * kd * vd;
+            const double *kk = k + ((size_t)u * kh + hh) * kd;
+            const double *qq = q + ((size_t)u * kh + hh) * kd;
+            const double *vv = v + ((size_t)u * vh + i) * vd;
+            const double alpha = exp(g[(size_t)u * vh + i]);
+            const double bt = beta[(size_t)u * vh + i];
+            double P[16][16], R[16][16];
+            for (int a = 0; a < kd; a++)
+                for (int c = 0; c < kd; c++)
+                    P[a][c] = alpha * ((a == c ? 1.0 : 0.0) - bt * kk[a] * kk[c]);
+            for (int a = 0; a < kd; a++)
+                for (int c = 0; c < vd; c++) {
+                    double s = 0.0;
+                    for (int e = 0; e < kd; e++)
+                        s += P[a][e] * Sh[(size_t)e * vd + c];
+                    R[a][c] = s + bt * kk[a] * vv[c];
+                }
+            for (int a = 0; a < kd; a++)
+                for (int c = 0; c < vd; c++)
+                    Sh[(size_t)a * vd + c] = R[a][c];
+            double *oo = o + ((size_t)u * vh + i) * vd;
+            for (int c = 0; c < vd; c++) {
+                double s = 0.0;
+                for (int a = 0; a < kd; a++)
+                    s += R[a][c] * qq[a];
+                oo[c] = s;
+            }
+        }
+    }
+    return 0;
+}

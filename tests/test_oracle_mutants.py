@@ -1,0 +1,102 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies ``oracle/gdn_oracle.c`` into a temporary directory, plants
+one plausible mistake (a dropped term, a flipped sign, a wrong index, a
+transposed operand, a swapped input), compiles it with the oracle's own flags
+and runs every pin against it.  At least one pin has to fail, otherwise the
+pins would not be able to tell that oracle from the correct one.  Runs on the
+CPU only.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTANTS = [
+    ("delta sign", "float tmp = (vrow[dv] - kv) * bt;", "float tmp = (vrow[dv] + kv) * bt;"),
+    ("beta dropped", "float tmp = (vrow[dv] - kv) * bt;", "float tmp = (vrow[dv] - kv);"),
+    ("decay dropped", "float t = Sh[(size_t)dk * vd + dv] * alpha;",
+     "float t = Sh[(size_t)dk * vd + dv];"),
+    ("key read-out before decay", "kv = kv + t * kh_[dk];",
+     "kv = kv + Sh[(size_t)dk * vd + dv] * kh_[dk] / (alpha + 1e-30f) * (alpha != 0.0f);"),
+    ("output from the old state", "oa = oa + t * qh[dk];",
+     "oa = oa + (t - kh_[dk] * tmp) * qh[dk];"),
+    ("output reads k instead of q", "oa = oa + t * qh[dk];", "oa = oa + t * kh_[dk];"),
+    ("rank-1 update uses q", "float t = Sh[(size_t)dk * vd + dv] + kh_[dk] * tmp;",
+     "float t = Sh[(size_t)dk * vd + dv] + qh[dk] * tmp;"),
+    ("head mapping modulo", "const int hh = i / rep;\n        const float alpha = expf(gu[i]);",
+     "const int hh = i % kh;\n        const float alpha = expf(gu[i]);"),
+    ("transposed state index", "Sh[(size_t)dk * vd + dv]", "Sh[(size_t)dv * kd + dk]"),
+    ("gate not exponentiated", "const float alpha = expf(gu[i]);", "const float alpha = gu[i];"),
+    ("unit offset of g", "g + (size_t)u * vh, beta + (size_t)u * vh,",
+     "g, beta + (size_t)u * vh,"),
+    ("step_m row stride", "g + m * ng, beta + m * ng", "g, beta + m * ng"),
+    ("rollback restores nothing", "memcpy(S, slab->S_snap, (size_t)N * per_s * sizeof(float));", ""),
+    ("rollback replays one step short", "for (int m = 0; m < accepted[u]; m++) {",
+     "for (int m = 0; m + 1 < accepted[u]; m++) {"),
+    ("rollback stays armed", "slab->armed = 0;", ""),
+    ("history newest slot", "memcpy(hist + (size_t)(nprev - 1) * conv_dim, raw,",
+     "memcpy(hist, raw,"),
+    ("history not shifted", "for (int j = 0; j + 1 < nprev; j++)\n        memcpy",
+     "for (int j = 0; j + 1 < 0; j++)\n        memcpy"),
+    ("beta from a", "beta[(size_t)b * vh + r] = 1.0f / (1.0f + expf(-acc_b));",
+     "beta[(size_t)b * vh + r] = 1.0f / (1.0f + expf(-acc_a));"),
+    ("beta sign", "1.0f / (1.0f + expf(-acc_b))", "1.0f / (1.0f + expf(acc_b))"),
+    ("gate sign", "g[(size_t)b * vh + r] = -expf(A_log[r]) * sp;",
+     "g[(size_t)b * vh + r] = expf(A_log[r]) * sp;"),
+    ("gate ignores A_log", "= -expf(A_log[r]) * sp;", "= -sp;"),
+    ("dt_bias dropped", "const float xa = acc_a + dt_bias[r];", "const float xa = acc_a;"),
+    ("low softplus branch", "return expf(xa);", "return 0.0f;"),
+    ("high softplus branch", "if (xa > 20.0f)\n        return xa;",
+     "if (xa > 20.0f)\n        return 20.0f;"),
+    ("conv taps reversed", "acc = acc + cw[j] * hb[(size_t)j * conv_dim + ch];",
+     "acc = acc + cw[nprev - 1 - j] * hb[(size_t)j * conv_dim + ch];"),
+    ("conv current tap dropped", "acc = acc + cw[nprev] * raw[ch];", ""),
+    ("silu dropped", "out[ch] = acc / (1.0f + expf(-acc));", "out[ch] = acc;"),
+    ("split k offset", "memcpy(kb, out + qk_w,", "memcpy(kb, out,"),
+    ("split v offset", "out + 2 * qk_w, (size_t)vh * vd", "out + qk_w, (size_t)vh * vd"),
+    ("norm epsilon dropped", "1.0f / sqrtf(ssq + 1e-6f)", "1.0f / sqrtf(ssq)"),
+    ("q scale dropped", "qh[j] = (qh[j] * iq) * q_scale;", "qh[j] = qh[j] * iq;"),
+    ("k normalised with q's norm", "kk[j] = kk[j] * ik;", "kk[j] = kk[j] * iq;"),
+]
+
+
+def _run_pins(orc):
+    failed = []
+    for pin in pins.PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def srcdir(tmp_path_factory):
+    d = tmp_path_factory.mktemp("mutants")
+    shutil.copy(os.path.join(os.path.dirname(oracle.SRC), "gdn_oracle.h"), d)
+    return d
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(srcdir, name, old, new):
+    src = open(oracle.SRC).read()
+    assert old in src, f"mutation site not found: {old!r}"
+    mutated = src.replace(old, new)
+    tag = "".join(c if c.isalnum() else "_" for c in name)
+    c_path = os.path.join(srcdir, f"m_{tag}.c")
+    with open(c_path, "w") as f:
+        f.write(mutated)
+    so = oracle.build(src=c_path, out=os.path.join(srcdir, f"m_{tag}.so"))
+    failed = _run_pins(oracle.Oracle(so))
+    assert failed, f"no pin caught the planted mistake '{name}'"
+
+
+def test_unmutated_copy_passes(srcdir):
+    c_path = os.path.join(srcdir, "clean.c")
+    shutil.copy(oracle.SRC, c_path)
+    so = oracle.build(src=c_path, out=os.path.join(srcdir, "clean.so"))
+    assert _run_pins(oracle.Oracle(so)) == []
