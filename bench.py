@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X GDN recurrent decode step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+
+Default workload (one "step" = one decode step of every state unit, one
+launch): 64 sequences x 48 GDN layers = 3072 independent fp32 states of
+48 value heads x 128 x 128 (9.66 GB), vh=48, kh=16, kd=vd=128, seeded
+synthetic inputs resident in HBM before timing.  Prints one JSON line with
+head-steps/s, the achieved algorithmic HBM bandwidth of the recurrence kernel
+against MI355X's 8 TB/s, the measured read+write copy floor, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Other --config values time the other workloads: 0 single sequence x 1 layer
+x 64 sequential steps (launch latency), 2 speculative verify (mark + 8-row
+step_m + rollback), 3 front end + step, 4 large batch, 5 large batch at
+kd=vd=64.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gated_deltanet_recurrent_amd as gdn  # noqa: E402
+import synth  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+NAMES = ("q", "k", "v", "g", "beta")
+METRIC = "GDN head-steps/sec and achieved HBM GB/s (% of MI355X peak), 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_amd", "csrc", "gdn_kernels.hip")
+
+
+def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
+    """Algorithmic HBM bytes of one head-step when `rows` steps share one
+    state read and one state write (rows=1: a plain step)."""
+    vh, kh, kd, vd = dims
+    rep = vh // kh
+    state = (kd * vd * 4 * (1 if read_state else 0) + kd * vd * 4) / rows
+    per_row = vd * 4 + (vd * 4 if write_o else 0) + 8 + 2 * kd * 4 / rep
+    return state + per_row
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload_key, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"recur_kernel_{workload_key}_counters.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", open(path).read(), flags=re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed(fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3            # seconds
+
+
+def cpu_threads():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return max(1, min(16, n or 1))
+
+
+def cpu_baseline_step(S_gpu, pool, dims, units, rows):
+    """The CPU oracle, as it stands, on `units` units x `rows` steps, split
+    over host threads by unit (units are independent)."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+
+    orc = oracle.load()
+    S = np.ascontiguousarray(S_gpu[:units].cpu().numpy())
+    xs = [{n: np.ascontiguousarray(pool[r % len(pool)][n][0, :units].cpu().numpy())
+           for n in NAMES} for r in range(rows)]
+    vh, kh, kd, vd = dims
+    th = min(cpu_threads(), units)
+    chunks = np.array_split(np.arange(units), th)
+
+    def work(ch):
+        lo, hi = int(ch[0]), int(ch[-1]) + 1
+        Sc = S[lo:hi]
+        o = np.zeros((hi - lo, vh, vd), np.float32)
+        for x in xs:
+            orc.gdn_step(Sc, *(np.ascontiguousarray(x[n][lo:hi]) for n in NAMES), o, dims)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(th) as ex:
+        list(ex.map(work, chunks))
+    dt = time.perf_counter() - t0
+    hs = units * vh * rows
+    return dict(value=hs / dt, unit="head-steps/s", cores=th, kind="oracle",
+                sample=f"{units} units x {rows} steps ({hs} head-steps) of the same workload, "
+                       f"{dt:.2f} s wall on {th} threads")
+
+
+def copy_floor(S, reps=5):
+    """Read+write floor: stream the state through the same 128-bit access
+    pattern and write it back in place."""
+    flat = S.view(-1)
+    gdn.stream_copy(flat, flat)
+    dt = timed(lambda i: gdn.stream_copy(flat, flat), reps, 1)
+    return 2 * flat.numel() * 4 * reps / dt / 1e9
+
+
+def bench_decode(cfg, steps, warmup, cpu):
+    dims = cfg["dims"]
+    vh = dims[0]
+    N = cfg["seqs"] * cfg["layers"]
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    pool = [synth.step_inputs(gen, N, dims, M=1, gate=cfg["gate"], device="cuda")
+            for _ in range(4)]
+    o = torch.empty((N, vh, dims[3]), device="cuda")
+    torch.cuda.synchronize()
+
+    def one(i):
+        x = pool[i % 4]
+        gdn.step(S, x["q"][0], x["k"][0], x["v"][0], x["g"][0], x["beta"][0], o=o)
+
+    dt = timed(one, steps, warmup)
+    hs_per_step = N * vh
+    bps = head_step_bytes(dims)
+    launch_s = dt / steps
+    bytes_launch = hs_per_step * bps
+    achieved = bytes_launch / launch_s / 1e9
+    floor = copy_floor(S)
+    key = {1: "b64x48", 4: "b512x8", 5: "b512x8_kd64"}.get(cfg["id"], f"cfg{cfg['id']}")
+    traffic = recorded_traffic(key, bytes_launch)
+    res = dict(
+        value=hs_per_step * steps / dt, ms_per_step=launch_s * 1e3,
+        roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
+                      unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic),
+        extra=dict(copy_floor_GBps=round(floor, 1),
+                   frac_of_copy_floor=round(achieved / floor, 4),
+                   algorithmic_bytes_per_launch=int(bytes_launch),
+                   bytes_per_head_step=round(bps, 2), head_steps_per_step=hs_per_step,
+                   kernel="recur_kernel", kernel_source_sha256_16=kernel_hash()))
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_step(S, pool, dims, units=min(N, 256), rows=8)
+    return res, dict(workload=cfg["name"], units=N, seqs=cfg["seqs"], layers=cfg["layers"],
+                     vh=dims[0], kh=dims[1], kd=dims[2], vd=dims[3],
+                     state_GB=round(N * vh * dims[2] * dims[3] * 4 / 1e9, 3),
+                     launch="one gdn_step launch over all units per step",
+                     inputs="pool of 4 seeded input sets, cycled")
+
+
+def bench_latency(cfg, steps, warmup, cpu):
+    """Single sequence, one layer: T sequential steps, launch-latency bound."""
+    dims = cfg["dims"]
+    vh = dims[0]
+    T = cfg["steps"]
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    S = synth.state(gen, 1, dims, device="cuda")
+    inp = synth.step_inputs(gen, 1, dims, M=T, device="cuda")
+    rows = [{n: inp[n][m] for n in NAMES} for m in range(T)]
+    o = torch.empty((1, vh, dims[3]), device="cuda")
+
+    def one(i):
+        for x in rows:
+            gdn.step(S, x["q"], x["k"], x["v"], x["g"], x["beta"], o=o)
+
+    dt = timed(one, steps, warmup)
+    launch_s = dt / (steps * T)
+    achieved = head_step_bytes(dims) * vh / launch_s / 1e9
+    res = dict(value=vh * T * steps / dt, ms_per_step=dt / steps * 1e3,
+               roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
+                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
+               extra=dict(us_per_call=round(launch_s * 1e6, 3),
+                          note="3 MiB state stays in L2/MALL: latency figure, not an HBM claim"))
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_step(S, [{n: inp[n][m:m + 1] for n in NAMES}
+                                                    for m in range(T)], dims, units=1, rows=T)
+    return res, dict(workload=cfg["name"], units=1, vh=vh, kd=dims[2], steps_per_iteration=T)
+
+
+def bench_verify(cfg, steps, warmup, cpu):
+    dims = cfg["dims"]
+    vh = dims[0]
+    L = cfg["layers"]
+    N = cfg["seqs"] * L
+    M = cfg["M"]
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    o = torch.empty((M, N, vh, dims[3]), device="cuda")
+    slab = gdn.Slab(N, dims)
+    rng = np.random.default_rng(cfg["seed"])
+    accs = [np.repeat(rng.integers(0, M + 1, cfg["seqs"]), L).astype(np.int32) for _ in range(8)]
+    args = [inp[n] for n in NAMES]
+
+    def one(i):
+        slab.mark(S)
+        gdn.step_m(S, *args, o=o)
+        slab.rollback(S, accs[i % 8], *args)
+
+    dt = timed(one, steps, warmup)
+    # step_m alone, for the kernel roofline
+    dt_m = timed(lambda i: gdn.step_m(S, *args, o=o), steps, 1)
+    bytes_m = N * vh * M * head_step_bytes(dims, rows=M)
+    achieved = bytes_m / (dt_m / steps) / 1e9
+    mean_a = float(np.mean([a.mean() for a in accs]))
+    res = dict(value=N * vh * M * steps / dt, ms_per_step=dt / steps * 1e3,
+               roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
+                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
+               extra=dict(step_m_ms=round(dt_m / steps * 1e3, 4), mean_accepted=mean_a,
+                          value_counts="drafted head-steps per second of the full cycle"))
+    return res, dict(workload=cfg["name"], units=N, M=M, vh=vh, kd=dims[2],
+                     cycle="gdn_mark + gdn_step_m(M=8) + gdn_rollback(accepted ~ U{0..8})")
+
+
+def bench_frontend(cfg, steps, warmup, cpu):
+    dims = cfg["dims"]
+    vh, kh, kd, vd = dims
+    B, T = cfg["seqs"], cfg["steps"]
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    S = synth.state(gen, B, dims, device="cuda")
+    w = synth.frontend_weights(gen, dims, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=T, device="cuda")
+    hist = fe["hist"]
+    out = dict(q=torch.empty((B, kh, kd), device="cuda"), k=torch.empty((B, kh, kd), device="cuda"),
+               v=torch.empty((B, vh, vd), device="cuda"), g=torch.empty((B, vh), device="cuda"),
+               beta=torch.empty((B, vh), device="cuda"))
+    o = torch.empty((B, vh, vd), device="cuda")
+
+    def one(i):
+        t = i % T
+        gdn.frontend(fe["x"][t], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"][t],
+                     hist, w["conv_w"], dims, out=out)
+        gdn.step(S, out["q"], out["k"], out["v"], out["g"], out["beta"], o=o)
+
+    dt = timed(one, steps, warmup)
+    cd = synth.conv_dim_of(dims)
+    fe_bytes = (B * 5120 * 4 + 2 * vh * 5120 * 4 + B * cd * 4 + 2 * B * 3 * cd * 4
+                + cd * 16 + B * (2 * kh * kd + vh * vd + 2 * vh) * 4)
+    total = B * vh * head_step_bytes(dims) + fe_bytes
+    achieved = total / (dt / steps) / 1e9
+    res = dict(value=B * vh * steps / dt, ms_per_step=dt / steps * 1e3,
+               roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
+                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
+               extra=dict(frontend_bytes=fe_bytes,
+                          note="384 MiB state is 1.5x the MALL: partly cache-resident"))
+    return res, dict(workload=cfg["name"], units=B, vh=vh, kd=kd, dim=5120, conv_dim=cd)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (every state unit is independent, so G GPUs would each run this "
+              "same kernel on N/G units with no communication).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    gdn.lib()
+    cfg = dict(synth.WORKLOADS[args.config])
+    cfg["id"] = args.config
+    runner = {0: bench_latency, 2: bench_verify, 3: bench_frontend}.get(args.config, bench_decode)
+    res, config = runner(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
+    line = dict(metric=METRIC, value=round(res["value"], 1), unit="head-steps/s", n_gpus=1,
+                steps=args.steps, warmup=args.warmup, ms_per_step=round(res["ms_per_step"], 5),
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+                data="synthetic", config=config, roofline=res["roofline"])
+    if "cpu_baseline" in res:
+        line["cpu_baseline"] = res["cpu_baseline"]
+    line["extra"] = res.get("extra", {})
+    line["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

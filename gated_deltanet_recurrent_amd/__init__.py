@@ -1,0 +1,208 @@
+"""Python binding of the MI355X GDN recurrent-step library (``libgdn_mi355x.so``).
+
+Argument marshalling only: every function checks that its torch tensors are
+fp32, contiguous and on a HIP device, derives the sizes from their shapes and
+calls the C ABI of ``include/gdn.h`` with raw device pointers and the current
+HIP stream.  All arithmetic runs in the library's gfx950 kernels; there is no
+fallback of any kind, and importing this package fails loudly when the
+library has not been built (``python -m gated_deltanet_recurrent_amd.build``).
+
+Operator: "Kestrel_VLLM #24: GDN linear attention on GPU", section 4 and
+Fig. 1 caption (decay, key read-out, delta, rank-1 update, query read-out with
+the updated state); M-step and mark/rollback: "Kestrel_VLLM #34: batched M
+rows", sections 3.6 and 3.7; front end: "Kestrel_VLLM #27: register residency
+and fused launch", section 4.2, and "#24", section 3.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn_mi355x.so")
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ESTATE, GDN_EDEVICE = 0, -1, -2, -3, -4
+
+# Every exported symbol of include/gdn.h.
+EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_slab_bytes", "gdn_slab_init",
+           "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_stream_copy")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, rc, what):
+        self.rc = rc
+        super().__init__(f"{what}: {lib().gdn_strerror(rc).decode()} (rc={rc})")
+
+
+class gdn_slab(C.Structure):
+    _fields_ = [("dev", C.c_void_p), ("bytes", C.c_int64), ("n_units", C.c_int64),
+                ("hist_floats", C.c_int64), ("vh", C.c_int32), ("kh", C.c_int32),
+                ("kd", C.c_int32), ("vd", C.c_int32), ("armed", C.c_int32),
+                ("magic", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m gated_deltanet_recurrent_amd.build` (there is no fallback path)")
+    L = C.CDLL(LIB_PATH)
+    P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
+    L.gdn_strerror.argtypes = [C.c_int]
+    L.gdn_strerror.restype = C.c_char_p
+    L.gdn_step.argtypes = [P] * 7 + [I64, I32, I32, I32, I32, P]
+    L.gdn_step_m.argtypes = [P] * 7 + [I64, I32, I32, I32, I32, I32, P]
+    L.gdn_slab_bytes.argtypes = [I64, I32, I32, I32, I32, I64]
+    L.gdn_slab_bytes.restype = I64
+    L.gdn_slab_init.argtypes = [C.POINTER(gdn_slab), P, I64, I64, I32, I32, I32, I32, I64]
+    L.gdn_mark.argtypes = [C.POINTER(gdn_slab), P, P, P]
+    L.gdn_rollback.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I32, I32, P, P]
+    L.gdn_frontend.argtypes = [P] * 13 + [I32] * 8 + [P]
+    L.gdn_stream_copy.argtypes = [P, P, I64, P]
+    for f in ("gdn_step", "gdn_step_m", "gdn_slab_init", "gdn_mark", "gdn_rollback",
+              "gdn_frontend", "gdn_stream_copy"):
+        getattr(L, f).restype = C.c_int
+    _lib = L
+    return L
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on a HIP device, got {t.device}")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name}: must be float32, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(rc, what):
+    if rc != GDN_OK:
+        raise GdnError(rc, what)
+
+
+def _state_dims(S, q, v):
+    """(n_units, vh, kh, kd, vd) from S [N][vh][kd][vd], q [.., N, kh, kd]."""
+    if S.dim() != 4 or q.dim() < 3:
+        raise ValueError("S must be [N][vh][kd][vd] and q [..][N][kh][kd]")
+    N, vh, kd, vd = S.shape
+    kh = q.shape[-2]
+    return N, vh, kh, kd, vd
+
+
+def step(S, q, k, v, g, beta, o=None, stream=None):
+    """One decode step for every unit (gdn_step).  S [N][vh][kd][vd] advances
+    in place; returns o [N][vh][vd]."""
+    N, vh, kh, kd, vd = _state_dims(S, q, v)
+    if o is None:
+        o = torch.empty((N, vh, vd), dtype=torch.float32, device=S.device)
+    _check(lib().gdn_step(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                          _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"), N, vh, kh, kd,
+                          vd, _stream(stream)), "gdn_step")
+    return o
+
+
+def step_m(S, q, k, v, g, beta, o=None, stream=None):
+    """M sequential steps (gdn_step_m); q, k [M][N][kh][kd], v [M][N][vh][vd],
+    g, beta [M][N][vh].  Returns o [M][N][vh][vd]."""
+    N, vh, kh, kd, vd = _state_dims(S, q, v)
+    M = q.shape[0]
+    if o is None:
+        o = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
+    _check(lib().gdn_step_m(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                            _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"), N, M, vh, kh,
+                            kd, vd, _stream(stream)), "gdn_step_m")
+    return o
+
+
+def slab_bytes(n_units, dims, hist_floats_per_unit=0):
+    vh, kh, kd, vd = dims
+    nb = lib().gdn_slab_bytes(n_units, vh, kh, kd, vd, hist_floats_per_unit)
+    if nb < 0:
+        raise GdnError(int(nb), "gdn_slab_bytes")
+    return int(nb)
+
+
+class Slab:
+    """Snapshot slab: host struct + device buffer (a torch uint8 tensor)."""
+
+    def __init__(self, n_units, dims, hist_floats_per_unit=0, device="cuda"):
+        vh, kh, kd, vd = dims
+        nb = slab_bytes(n_units, dims, hist_floats_per_unit)
+        self.buf = torch.empty(nb, dtype=torch.uint8, device=device)
+        self.s = gdn_slab()
+        _check(lib().gdn_slab_init(C.byref(self.s), C.c_void_p(self.buf.data_ptr()), nb,
+                                   n_units, vh, kh, kd, vd, hist_floats_per_unit),
+               "gdn_slab_init")
+
+    @property
+    def armed(self):
+        return int(self.s.armed)
+
+    def mark(self, S, hist=None, stream=None):
+        _check(lib().gdn_mark(C.byref(self.s), _dev(S, "S"), _dev(hist, "hist"),
+                              _stream(stream)), "gdn_mark")
+
+    def rollback(self, S, accepted, q=None, k=None, v=None, g=None, beta=None, hist=None,
+                 xc_raw=None, M=None, stream=None):
+        """accepted: host int32 per unit (list, numpy or CPU tensor)."""
+        acc = torch.as_tensor(accepted, dtype=torch.int32).contiguous().cpu()
+        if acc.numel() != self.s.n_units:
+            raise ValueError("accepted must hold one entry per unit")
+        if M is None:
+            M = q.shape[0] if q is not None else 1
+        conv_dim = xc_raw.shape[-1] if xc_raw is not None else (
+            hist.shape[-1] if hist is not None else 0)
+        _check(lib().gdn_rollback(C.byref(self.s), _dev(S, "S"), _dev(hist, "hist"),
+                                  _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(g, "g"),
+                                  _dev(beta, "beta"), _dev(xc_raw, "xc_raw"), conv_dim, M,
+                                  C.c_void_p(acc.data_ptr()), _stream(stream)),
+               "gdn_rollback")
+
+
+def frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None, stream=None):
+    """Front end for B rows (gdn_frontend).  Returns dict q, k, v, g, beta."""
+    vh, kh, kd, vd = dims
+    B, dim = x.shape
+    conv_dim = xc_raw.shape[-1]
+    ck = conv_w.shape[-1]
+    dev = x.device
+    if out is None:
+        out = dict(q=torch.empty((B, kh, kd), dtype=torch.float32, device=dev),
+                   k=torch.empty((B, kh, kd), dtype=torch.float32, device=dev),
+                   v=torch.empty((B, vh, vd), dtype=torch.float32, device=dev),
+                   g=torch.empty((B, vh), dtype=torch.float32, device=dev),
+                   beta=torch.empty((B, vh), dtype=torch.float32, device=dev))
+    _check(lib().gdn_frontend(
+        _dev(x, "x"), _dev(Wa, "Wa"), _dev(Wb, "Wb"), _dev(A_log, "A_log"),
+        _dev(dt_bias, "dt_bias"), _dev(xc_raw, "xc_raw"), _dev(hist, "hist"),
+        _dev(conv_w, "conv_w"), _dev(out["q"], "q"), _dev(out["k"], "k"), _dev(out["v"], "v"),
+        _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, dim, conv_dim, ck, vh, kh, kd, vd,
+        _stream(stream)), "gdn_frontend")
+    return out
+
+
+def stream_copy(dst, src, stream=None):
+    """128-bit streaming copy (the read+write floor); dst may be src."""
+    if dst.numel() != src.numel():
+        raise ValueError("dst and src sizes differ")
+    _check(lib().gdn_stream_copy(_dev(dst, "dst"), _dev(src, "src"), src.numel(),
+                                 _stream(stream)), "gdn_stream_copy")

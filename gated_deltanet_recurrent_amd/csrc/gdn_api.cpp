@@ -1,0 +1,266 @@
+// gdn_api.cpp -- the C ABI declared in include/gdn.h: argument validation on
+// the host, launch-shape choice, enqueue on the caller's stream.  Every check
+// happens before anything is enqueued, so a refused call changes nothing and
+// needs no device (the validation runs on machines without a GPU).
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "gdn_launch.h"
+
+namespace {
+
+constexpr int32_t kMaxM = 64;
+constexpr int32_t kMaxHeads = 4096;
+constexpr int32_t kSlabMagic = 0x47444e53;  // "GDNS"
+constexpr int64_t kAlign = 256;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Pointer p must be non-null and 16-byte aligned.
+bool ptr_ok(const void *p) { return p != nullptr && aligned16(p); }
+
+int check_dims(int32_t vh, int32_t kh, int32_t kd, int32_t vd) {
+  if (vh <= 0 || kh <= 0 || kd <= 0 || vd <= 0 || vh % kh != 0 || vh > kMaxHeads) return GDN_EINVAL;
+  if (kd != vd || (kd != 128 && kd != 64)) return GDN_EUNSUPPORTED;
+  return GDN_OK;
+}
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Launch-size limit: the grid of the recurrence kernel (tiles x lanes
+// work-items) must stay below 2^32.
+bool grid_fits(int64_t n_units, int32_t vh, int32_t kd) {
+  const int64_t tiles = n_units * vh;
+  return tiles <= (int64_t)0xFFFFFFFF / gdn::recur_lanes(kd);
+}
+
+int enq(int hip_rc) { return hip_rc == 0 ? GDN_OK : GDN_EDEVICE; }
+
+// Validation shared by gdn_step / gdn_step_m.  rows = M.
+int check_step(const float *S, const float *q, const float *k, const float *v, const float *g,
+               const float *beta, const float *o, int64_t n_units, int32_t rows, int32_t vh,
+               int32_t kh, int32_t kd, int32_t vd) {
+  int rc = check_dims(vh, kh, kd, vd);
+  if (rc) return rc;
+  if (n_units < 0) return GDN_EINVAL;
+  if (n_units == 0) return GDN_OK;
+  if (!grid_fits(n_units, vh, kd)) return GDN_EUNSUPPORTED;
+  if (!ptr_ok(S) || !ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o)) return GDN_EINVAL;
+  if (g == nullptr || beta == nullptr) return GDN_EINVAL;
+  const int64_t sb = n_units * vh * (int64_t)kd * vd * 4;
+  const int64_t qkb = (int64_t)rows * n_units * kh * kd * 4;
+  const int64_t vb = (int64_t)rows * n_units * vh * vd * 4;
+  const int64_t gb = (int64_t)rows * n_units * vh * 4;
+  if (overlaps(S, sb, q, qkb) || overlaps(S, sb, k, qkb) || overlaps(S, sb, v, vb) ||
+      overlaps(S, sb, o, vb) || overlaps(S, sb, g, gb) || overlaps(S, sb, beta, gb))
+    return GDN_EINVAL;
+  if (overlaps(o, vb, q, qkb) || overlaps(o, vb, k, qkb) || overlaps(o, vb, v, vb) ||
+      overlaps(o, vb, g, gb) || overlaps(o, vb, beta, gb))
+    return GDN_EINVAL;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_strerror(int rc) {
+  switch (rc) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument (NULL or misaligned pointer, bad size, aliasing, M or accepted out of range)";
+    case GDN_EUNSUPPORTED: return "unsupported shape (kd == vd must be 64 or 128; launch too large)";
+    case GDN_ESTATE: return "slab state error (not armed, history not marked, too small, or mismatched)";
+    case GDN_EDEVICE: return "HIP runtime error while enqueuing";
+    default: return "unknown error code";
+  }
+}
+
+int gdn_step(float *S, const float *q, const float *k, const float *v, const float *g,
+             const float *beta, float *o, int64_t n_units, int32_t vh, int32_t kh, int32_t kd,
+             int32_t vd, void *stream) {
+  int rc = check_step(S, q, k, v, g, beta, o, n_units, 1, vh, kh, kd, vd);
+  if (rc || n_units == 0) return rc;
+  return enq(gdn::launch_recur(kd, S, S, q, k, v, g, beta, o, nullptr, n_units, vh, kh, 1,
+                               (hipStream_t)stream));
+}
+
+int gdn_step_m(float *S, const float *q, const float *k, const float *v, const float *g,
+               const float *beta, float *o, int64_t n_units, int32_t M, int32_t vh, int32_t kh,
+               int32_t kd, int32_t vd, void *stream) {
+  if (M < 1 || M > kMaxM) return GDN_EINVAL;
+  int rc = check_step(S, q, k, v, g, beta, o, n_units, M, vh, kh, kd, vd);
+  if (rc || n_units == 0) return rc;
+  return enq(gdn::launch_recur(kd, S, S, q, k, v, g, beta, o, nullptr, n_units, vh, kh, M,
+                               (hipStream_t)stream));
+}
+
+int64_t gdn_slab_bytes(int64_t n_units, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+                       int64_t hist_floats_per_unit) {
+  int rc = check_dims(vh, kh, kd, vd);
+  if (rc) return rc;
+  if (n_units < 1 || hist_floats_per_unit < 0 || hist_floats_per_unit % 4 != 0) return GDN_EINVAL;
+  const int64_t s_bytes = align_up(n_units * vh * (int64_t)kd * vd * 4);
+  const int64_t h_bytes = align_up(n_units * hist_floats_per_unit * 4);
+  const int64_t a_bytes = align_up(n_units * 4);
+  return s_bytes + h_bytes + a_bytes;
+}
+
+int gdn_slab_init(gdn_slab *slab, void *dev, int64_t bytes, int64_t n_units, int32_t vh,
+                  int32_t kh, int32_t kd, int32_t vd, int64_t hist_floats_per_unit) {
+  if (slab == nullptr || dev == nullptr || (reinterpret_cast<uintptr_t>(dev) % kAlign) != 0)
+    return GDN_EINVAL;
+  const int64_t need = gdn_slab_bytes(n_units, vh, kh, kd, vd, hist_floats_per_unit);
+  if (need < 0) return (int)need;
+  if (bytes < need) return GDN_ESTATE;
+  memset(slab, 0, sizeof(*slab));
+  slab->dev = dev;
+  slab->bytes = bytes;
+  slab->n_units = n_units;
+  slab->hist_floats = hist_floats_per_unit;
+  slab->vh = vh;
+  slab->kh = kh;
+  slab->kd = kd;
+  slab->vd = vd;
+  slab->armed = 0;
+  slab->magic = kSlabMagic;
+  return GDN_OK;
+}
+
+namespace {
+
+bool slab_valid(const gdn_slab *sl) {
+  if (sl == nullptr || sl->magic != kSlabMagic || sl->dev == nullptr) return false;
+  const int64_t need = gdn_slab_bytes(sl->n_units, sl->vh, sl->kh, sl->kd, sl->vd, sl->hist_floats);
+  return need > 0 && sl->bytes >= need;
+}
+
+float *slab_S(const gdn_slab *sl) { return static_cast<float *>(sl->dev); }
+float *slab_hist(const gdn_slab *sl) {
+  return reinterpret_cast<float *>(static_cast<char *>(sl->dev) +
+                                   align_up(sl->n_units * sl->vh * (int64_t)sl->kd * sl->vd * 4));
+}
+int32_t *slab_accepted(const gdn_slab *sl) {
+  return reinterpret_cast<int32_t *>(reinterpret_cast<char *>(slab_hist(sl)) +
+                                     align_up(sl->n_units * sl->hist_floats * 4));
+}
+
+}  // namespace
+
+int gdn_mark(gdn_slab *slab, const float *S, const float *hist, void *stream) {
+  if (!slab_valid(slab)) return GDN_ESTATE;
+  if (!ptr_ok(S) || (hist != nullptr && !aligned16(hist))) return GDN_EINVAL;
+  if (hist != nullptr && slab->hist_floats == 0) return GDN_ESTATE;
+  const int64_t ns = slab->n_units * slab->vh * (int64_t)slab->kd * slab->vd;
+  const int64_t nh = slab->n_units * slab->hist_floats;
+  if (overlaps(S, ns * 4, slab->dev, slab->bytes) ||
+      (hist && overlaps(hist, nh * 4, slab->dev, slab->bytes)))
+    return GDN_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  int rc = enq(gdn::launch_copy(slab_S(slab), S, ns, s));
+  if (rc) return rc;
+  if (hist != nullptr) {
+    rc = enq(gdn::launch_copy(slab_hist(slab), hist, nh, s));
+    if (rc) return rc;
+  }
+  slab->armed = 1 | (hist != nullptr ? 2 : 0);
+  return GDN_OK;
+}
+
+int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const float *k,
+                 const float *v, const float *g, const float *beta, const float *xc_raw,
+                 int32_t conv_dim, int32_t M, const int32_t *accepted, void *stream) {
+  if (!slab_valid(slab)) return GDN_ESTATE;
+  if (!(slab->armed & 1)) return GDN_ESTATE;
+  if (hist != nullptr && !(slab->armed & 2)) return GDN_ESTATE;
+  if (M < 1 || M > kMaxM || accepted == nullptr || !ptr_ok(S)) return GDN_EINVAL;
+  const int64_t N = slab->n_units;
+  bool any = false;
+  for (int64_t u = 0; u < N; u++) {
+    if (accepted[u] < 0 || accepted[u] > M) return GDN_EINVAL;
+    any |= accepted[u] > 0;
+  }
+  const int vh = slab->vh, kh = slab->kh, kd = slab->kd, vd = slab->vd;
+  const int64_t ns = N * vh * (int64_t)kd * vd;
+  if (overlaps(S, ns * 4, slab->dev, slab->bytes)) return GDN_EINVAL;
+  if (any) {
+    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || g == nullptr || beta == nullptr)
+      return GDN_EINVAL;
+    const int64_t qkb = (int64_t)M * N * kh * kd * 4, vb = (int64_t)M * N * vh * vd * 4,
+                  gb = (int64_t)M * N * vh * 4;
+    if (overlaps(S, ns * 4, q, qkb) || overlaps(S, ns * 4, k, qkb) || overlaps(S, ns * 4, v, vb) ||
+        overlaps(S, ns * 4, g, gb) || overlaps(S, ns * 4, beta, gb))
+      return GDN_EINVAL;
+  }
+  const int ck = 4;
+  if (hist != nullptr) {
+    if (!aligned16(hist) || conv_dim <= 0 || conv_dim % 4 != 0 ||
+        (int64_t)(ck - 1) * conv_dim != slab->hist_floats)
+      return GDN_EINVAL;
+    if (overlaps(hist, N * slab->hist_floats * 4, slab->dev, slab->bytes)) return GDN_EINVAL;
+    if (any && !ptr_ok(xc_raw)) return GDN_EINVAL;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  // accepted[] travels with the stream: the copy is ordered before the
+  // kernels that read it, and the host array is consumed before return.
+  int32_t *d_acc = slab_accepted(slab);
+  if (hipMemcpyAsync(d_acc, accepted, (size_t)N * 4, hipMemcpyHostToDevice, s) != hipSuccess)
+    return GDN_EDEVICE;
+  int rc = enq(gdn::launch_recur(kd, slab_S(slab), S, q, k, v, g, beta, nullptr, d_acc, N, vh, kh,
+                                 M, s));
+  if (rc) return rc;
+  if (hist != nullptr) {
+    rc = enq(gdn::launch_hist_replay(hist, slab_hist(slab), xc_raw, d_acc, N, conv_dim, ck, s));
+    if (rc) return rc;
+  }
+  slab->armed = 0;
+  return GDN_OK;
+}
+
+int gdn_frontend(const float *x, const float *Wa, const float *Wb, const float *A_log,
+                 const float *dt_bias, const float *xc_raw, float *hist, const float *conv_w,
+                 float *q, float *k, float *v, float *g, float *beta, int32_t B, int32_t dim,
+                 int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+                 void *stream) {
+  int rc = check_dims(vh, kh, kd, vd);
+  if (rc) return rc;
+  if (ck != 4) return GDN_EUNSUPPORTED;
+  if (B < 0 || dim <= 0 || dim % 4 != 0 || conv_dim != 2 * kh * kd + vh * vd) return GDN_EINVAL;
+  if ((int64_t)B > 65535) return GDN_EUNSUPPORTED;   // grid y limit of the conv kernel
+  if (B == 0) return GDN_OK;
+  if (!ptr_ok(x) || !ptr_ok(Wa) || !ptr_ok(Wb) || !A_log || !dt_bias || !ptr_ok(xc_raw) ||
+      !ptr_ok(hist) || !ptr_ok(conv_w) || !ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !g || !beta)
+    return GDN_EINVAL;
+  const int64_t hb = (int64_t)B * (ck - 1) * conv_dim * 4;
+  const int64_t qkb = (int64_t)B * kh * kd * 4, vb = (int64_t)B * vh * vd * 4, gb = (int64_t)B * vh * 4;
+  const void *outs[5] = {q, k, v, g, beta};
+  const int64_t ob[5] = {qkb, qkb, vb, gb, gb};
+  for (int i = 0; i < 5; i++) {
+    if (overlaps(outs[i], ob[i], hist, hb) || overlaps(outs[i], ob[i], xc_raw, (int64_t)B * conv_dim * 4) ||
+        overlaps(outs[i], ob[i], x, (int64_t)B * dim * 4))
+      return GDN_EINVAL;
+    for (int j = i + 1; j < 5; j++)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return GDN_EINVAL;
+  }
+  if (overlaps(hist, hb, xc_raw, (int64_t)B * conv_dim * 4)) return GDN_EINVAL;
+  return enq(gdn::launch_frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g,
+                                  beta, B, dim, conv_dim, vh, kh, kd, (hipStream_t)stream));
+}
+
+int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream) {
+  if (n_floats < 0) return GDN_EINVAL;
+  if (n_floats == 0) return GDN_OK;
+  if (!ptr_ok(dst) || !ptr_ok(src)) return GDN_EINVAL;
+  if (dst != src && overlaps(dst, n_floats * 4, src, n_floats * 4)) return GDN_EINVAL;
+  return enq(gdn::launch_copy(dst, src, n_floats, (hipStream_t)stream));
+}
+
+}  // extern "C"

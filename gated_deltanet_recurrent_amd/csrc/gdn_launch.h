@@ -1,0 +1,41 @@
+// gdn_launch.h -- internal launchers of the gfx950 kernels (not part of the
+// C ABI).  Every launcher assumes its arguments were validated by the caller
+// in gdn_api.cpp and returns a hipError_t cast to int (0 = enqueued).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Lanes per workgroup of the recurrence kernel for a square head of size kd.
+int recur_lanes(int kd);
+
+// Recurrence over tiles (unit, value head).  Reads the state from S_src,
+// writes it to S_dst (may equal S_src).  Runs `M` steps per unit, or
+// steps[u] steps when `steps` (device int32 [n_units]) is non-null.  Inputs
+// are [rows][n_units][...]; o (nullable) is [rows][n_units][vh][kd].
+int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
+                 const float *k, const float *v, const float *g,
+                 const float *beta, float *o, const int32_t *steps,
+                 int64_t n_units, int vh, int kh, int M, hipStream_t s);
+
+// 128-bit streaming copy of n floats (src == dst allowed).
+int launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
+
+// Conv-history rollback: hist[u] = last (ck-1) frames of
+// [snap[u] frames..., xc_raw[0][u], ..., xc_raw[a-1][u]], a = accepted[u].
+int launch_hist_replay(float *hist, const float *snap, const float *xc_raw,
+                       const int32_t *accepted, int64_t n_units, int conv_dim,
+                       int ck, hipStream_t s);
+
+// Front end: paired GEMV + gate/beta, then conv + SiLU + history + split +
+// per key-head norm.
+int launch_frontend(const float *x, const float *Wa, const float *Wb,
+                    const float *A_log, const float *dt_bias,
+                    const float *xc_raw, float *hist, const float *conv_w,
+                    float *q, float *k, float *v, float *g, float *beta, int B,
+                    int dim, int conv_dim, int vh, int kh, int kd,
+                    hipStream_t s);
+
+}  // namespace gdn

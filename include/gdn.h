@@ -1,0 +1,162 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet recurrent decode step.
+ *
+ * Operator ("Kestrel_VLLM #24: GDN linear attention on GPU", section 4 and
+ * Fig. 1 caption; "Kestrel_VLLM #27: register residency and fused launch",
+ * section 3.1).  For every unit u (one sequence x layer state) and value head
+ * i, with key head h = i / (vh / kh):
+ *     alpha = exp(g[u][i])
+ *     S     = alpha * S                          (S = S[u][i], kd x vd, fp32)
+ *     kv    = S^T k[u][h]                        (decayed state)
+ *     tmp   = (v[u][i] - kv) * beta[u][i]
+ *     S     = S + k[u][h] tmp^T                  (rank-1 update, in place)
+ *     o[u][i] = S^T q[u][h]                      (updated state)
+ *
+ * Conventions shared by every call:
+ *  - Every pointer named as device memory is a device pointer (e.g. a torch
+ *    tensor's data_ptr) owned by the caller, fp32 unless stated, contiguous,
+ *    and 16-byte aligned.  The library allocates nothing and keeps no global
+ *    mutable state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
+ *    call validates its arguments on the host, enqueues its kernels on the
+ *    stream and returns without synchronising, except where noted.
+ *  - Return: GDN_OK (0) once enqueued, or a negative error code; on an error
+ *    nothing has been enqueued.  Shapes the kernels were not built for are
+ *    refused, never served by a slower fallback.
+ *  - Layouts (row-major; N = n_units; M = draft rows, 1 for a single step):
+ *      S        [N][vh][kd][vd]   dv fastest
+ *      q, k     [M][N][kh][kd]
+ *      v, o     [M][N][vh][vd]
+ *      g, beta  [M][N][vh]        g is the log-domain gate (<= 0 in use)
+ *    The unit order inside N is the caller's (sequence-major in the tests).
+ *  - Supported: kd == vd in {64, 128}, vh % kh == 0, vh <= 4096.
+ *  - S must not overlap q, k, v, g, beta or o.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_OK 0
+#define GDN_EINVAL (-1)       /* NULL/misaligned pointer, bad size, aliasing, bad M or accepted[] */
+#define GDN_EUNSUPPORTED (-2) /* a shape the kernels are not built for */
+#define GDN_ESTATE (-3)       /* slab not armed, too small, or mismatched */
+#define GDN_EDEVICE (-4)      /* the HIP runtime reported a launch or copy error */
+
+/* Text for an error code (static storage). */
+const char *gdn_strerror(int rc);
+
+/*
+ * One decode step for N units.  S is read and written in place; o receives
+ * S'^T q.  n_units == 0 is a no-op.
+ * ("Kestrel_VLLM #24", section 4: one state update per token per head.)
+ */
+int gdn_step(float *S, const float *q, const float *k, const float *v,
+             const float *g, const float *beta, float *o, int64_t n_units,
+             int32_t vh, int32_t kh, int32_t kd, int32_t vd, void *stream);
+
+/*
+ * M sequential steps for N units (speculative verify): step m uses row m of
+ * q, k, v, g, beta and writes row m of o; S advances in place through all M
+ * steps.  Bit-identical to M calls of gdn_step with the same rows.
+ * 1 <= M <= 64.  ("Kestrel_VLLM #34: batched M rows", section 3.6: the
+ * recurrence is serial in time, rows are M single steps.)
+ */
+int gdn_step_m(float *S, const float *q, const float *k, const float *v,
+               const float *g, const float *beta, float *o, int64_t n_units,
+               int32_t M, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+               void *stream);
+
+/*
+ * Snapshot slab for mark / rollback ("Kestrel_VLLM #34", section 3.7: the
+ * recurrent state and the conv history can only be restored from a copy; the
+ * snapshot is one-shot).  The struct lives in caller host memory; `dev`
+ * points at caller device memory of at least gdn_slab_bytes() bytes.  Fields
+ * are managed by the library; treat them as read-only.
+ */
+typedef struct gdn_slab {
+    void *dev;            /* device memory: S snapshot | hist snapshot | accepted[] */
+    int64_t bytes;        /* size of dev */
+    int64_t n_units;
+    int64_t hist_floats;  /* conv-history floats per unit, (ck-1)*conv_dim, or 0 */
+    int32_t vh, kh, kd, vd;
+    int32_t armed;        /* bit 0: state marked; bit 1: history marked */
+    int32_t magic;        /* set by gdn_slab_init */
+} gdn_slab;
+
+/* Device bytes a slab needs, or a negative error code for bad arguments. */
+int64_t gdn_slab_bytes(int64_t n_units, int32_t vh, int32_t kh, int32_t kd,
+                       int32_t vd, int64_t hist_floats_per_unit);
+
+/* Bind a slab to caller device memory `dev` (256-byte aligned) of `bytes`
+ * bytes.  Host only; leaves the slab disarmed. */
+int gdn_slab_init(gdn_slab *slab, void *dev, int64_t bytes, int64_t n_units,
+                  int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+                  int64_t hist_floats_per_unit);
+
+/* Copy S (and hist [N][hist_floats] unless NULL) into the slab and arm it.
+ * Re-marking an armed slab overwrites the snapshot. */
+int gdn_mark(gdn_slab *slab, const float *S, const float *hist, void *stream);
+
+/*
+ * Roll back to an accepted length: for every unit u, S (and hist, unless
+ * NULL) become the marked bytes advanced by accepted[u] single steps that use
+ * rows 0..accepted[u]-1 of the inputs given to gdn_step_m (q, k, v, g, beta,
+ * [M][N][...]); no o is written.  The history replays the raw conv input
+ * frames xc_raw [M][N][conv_dim] (needed only with hist; conv_dim*(ck-1) must
+ * equal the slab's hist_floats and ck = 4).  accepted is a HOST array of N
+ * int32 in 0..M; it is copied before the call returns.  accepted[u] == 0
+ * restores the marked bytes exactly; accepted[u] == M reproduces gdn_step_m
+ * bit for bit.  The slab is disarmed afterwards (one-shot): a rollback on a
+ * disarmed slab, or with hist when the history was not marked, returns
+ * GDN_ESTATE and changes nothing.
+ */
+int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q,
+                 const float *k, const float *v, const float *g,
+                 const float *beta, const float *xc_raw, int32_t conv_dim,
+                 int32_t M, const int32_t *accepted, void *stream);
+
+/*
+ * Front end of one GDN layer for B rows ("Kestrel_VLLM #27", section 4.2:
+ * the beta and a projections as one paired launch; "Kestrel_VLLM #24",
+ * section 3 and Fig. 1 caption: gate/beta transform, depthwise causal conv +
+ * SiLU with the history of raw conv inputs, split, per key-head norm):
+ *   a = Wa x_b, b = Wb x_b                     Wa, Wb [vh][dim]
+ *   g = -exp(A_log) * softplus(a + dt_bias)    softplus(z) = z above 20,
+ *                                              exp(z) below -20
+ *   beta = 1 / (1 + exp(-b))
+ *   c[ch] = silu(sum_{j<ck-1} conv_w[ch][j] hist[b][j][ch]
+ *                + conv_w[ch][ck-1] xc_raw[b][ch])
+ *   hist[b] shifts one frame towards the oldest slot; the newest gets xc_raw[b]
+ *   q = c[0 : kh*kd], k = c[kh*kd : 2*kh*kd], v = c[2*kh*kd : conv_dim]
+ *   per key head: q *= 1/sqrt(sum q^2 + 1e-6) * 1/sqrt(kd);
+ *                 k *= 1/sqrt(sum k^2 + 1e-6)
+ * x [B][dim] (dim % 4 == 0); A_log, dt_bias [vh]; xc_raw [B][conv_dim];
+ * hist [B][ck-1][conv_dim] in/out; conv_w [conv_dim][ck]; outputs q, k
+ * [B][kh][kd], v [B][vh][vd], g, beta [B][vh] feed gdn_step with N = B.
+ * conv_dim must equal 2*kh*kd + vh*vd; ck must be 4.
+ */
+int gdn_frontend(const float *x, const float *Wa, const float *Wb,
+                 const float *A_log, const float *dt_bias, const float *xc_raw,
+                 float *hist, const float *conv_w, float *q, float *k, float *v,
+                 float *g, float *beta, int32_t B, int32_t dim, int32_t conv_dim,
+                 int32_t ck, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+                 void *stream);
+
+/*
+ * Measurement aid: stream n_floats floats from src to dst with the same
+ * 128-bit non-temporal access pattern as the state stream (the read+write
+ * floor against which the step is read).  src == dst is allowed (read and
+ * write back in place).  Used by gdn_mark for its copy.
+ */
+int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

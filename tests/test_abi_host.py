@@ -1,0 +1,177 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+that include/gdn.h declares, and its argument validation refuses bad calls
+before anything is enqueued (so these tests need no GPU and never launch)."""
+import ctypes as C
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gated_deltanet_recurrent_amd as gdn
+from tests.helpers import max_rel_pages
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "gdn.h")
+GOLD = os.path.join(ROOT, "tests", "golden")
+
+D128 = (48, 16, 128, 128)
+FAKE = 0x7f0000000000        # 256-byte aligned stand-in address; never dereferenced
+NULLS = C.c_void_p(None)
+
+
+def fp(off=0):
+    return C.c_void_p(FAKE + off)
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*(gdn_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    L = gdn.lib()
+    names = declared_functions()
+    assert set(names) == set(gdn.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_covers_codes():
+    L = gdn.lib()
+    for rc in (0, -1, -2, -3, -4):
+        assert L.gdn_strerror(rc)
+    assert b"unknown" in L.gdn_strerror(-99)
+
+
+def step_call(S=None, q=None, k=None, v=None, g=None, beta=None, o=None, N=4, dims=D128):
+    vh, kh, kd, vd = dims
+    sb = N * vh * kd * vd * 4
+    S = fp(0) if S is None else S
+    q = fp(sb) if q is None else q
+    k = fp(sb + (1 << 20)) if k is None else k
+    v = fp(sb + (2 << 20)) if v is None else v
+    g = fp(sb + (3 << 20)) if g is None else g
+    beta = fp(sb + (4 << 20)) if beta is None else beta
+    o = fp(sb + (5 << 20)) if o is None else o
+    return gdn.lib().gdn_step(S, q, k, v, g, beta, o, N, vh, kh, kd, vd, NULLS)
+
+
+def test_step_validation():
+    L = gdn.lib()
+    assert step_call(dims=(48, 16, 96, 96)) == gdn.GDN_EUNSUPPORTED
+    assert step_call(dims=(48, 16, 128, 64)) == gdn.GDN_EUNSUPPORTED
+    assert step_call(dims=(48, 15, 128, 128)) == gdn.GDN_EINVAL      # vh % kh
+    assert step_call(N=-1) == gdn.GDN_EINVAL
+    assert step_call(N=0) == gdn.GDN_OK                                 # no-op, nothing enqueued
+    assert step_call(S=NULLS) == gdn.GDN_EINVAL
+    assert step_call(q=fp(4 * 48 * 128 * 128 * 4 + 4)) == gdn.GDN_EINVAL  # misaligned
+    assert step_call(g=NULLS) == gdn.GDN_EINVAL
+    assert step_call(o=fp(1024)) == gdn.GDN_EINVAL                      # o inside S
+    assert step_call(q=fp(4096)) == gdn.GDN_EINVAL                      # q inside S
+    # launch too large: tiles x 256 lanes must fit 32 bits
+    assert step_call(N=(1 << 32) // (256 * 48) + 1) == gdn.GDN_EUNSUPPORTED
+    vh, kh, kd, vd = D128
+    for M in (0, 65, -3):
+        assert L.gdn_step_m(fp(0), fp(1 << 30), fp(2 << 30), fp(3 << 30), fp(4 << 30),
+                            fp(5 << 30), fp(6 << 30), 4, M, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+
+
+def test_slab_bytes_and_init():
+    L = gdn.lib()
+    vh, kh, kd, vd = D128
+    assert L.gdn_slab_bytes(0, vh, kh, kd, vd, 0) == gdn.GDN_EINVAL
+    assert L.gdn_slab_bytes(4, vh, kh, kd, vd, 6) == gdn.GDN_EINVAL          # not a multiple of 4
+    assert L.gdn_slab_bytes(4, vh, kh, 32, 32, 0) == gdn.GDN_EUNSUPPORTED
+    nb = L.gdn_slab_bytes(3, vh, kh, kd, vd, 0)
+    assert nb == 3 * vh * kd * vd * 4 + 256
+    s = gdn.gdn_slab()
+    assert L.gdn_slab_init(C.byref(s), fp(0), nb - 1, 3, vh, kh, kd, vd, 0) == gdn.GDN_ESTATE
+    assert L.gdn_slab_init(C.byref(s), fp(16), nb, 3, vh, kh, kd, vd, 0) == gdn.GDN_EINVAL  # align
+    assert L.gdn_slab_init(C.byref(s), fp(0), nb, 3, vh, kh, kd, vd, 0) == gdn.GDN_OK
+    assert s.armed == 0 and s.n_units == 3
+
+
+def test_slab_size_matches_pages_state_sizes():
+    """The pages' own size figures for 48 layers of S and conv history."""
+    gold = json.load(open(os.path.join(GOLD, "state_sizes_p24.json")))
+    sh = gold["shape"]
+    L = gdn.lib()
+    n = sh["layers"]
+    hist = (sh["ck"] - 1) * sh["conv_dim"]
+    total = L.gdn_slab_bytes(n, sh["vh"], sh["kh"], sh["kd"], sh["vd"], hist)
+    s_only = L.gdn_slab_bytes(n, sh["vh"], sh["kh"], sh["kd"], sh["vd"], 0)
+    s_bytes = s_only - 256                       # minus the accepted[] area
+    h_bytes = total - s_only
+    assert round(s_bytes / 1e6, 1) == gold["state_S_MB"]
+    assert round(h_bytes / 1e6, 1) == gold["conv_history_MB"]
+    assert round((s_bytes + h_bytes) / 2**20, 1) == gold["state_plus_history_MiB"]
+
+
+def test_rollback_refusals_need_no_device():
+    L = gdn.lib()
+    vh, kh, kd, vd = D128
+    nb = L.gdn_slab_bytes(2, vh, kh, kd, vd, 3 * 10240)
+    s = gdn.gdn_slab()
+    assert L.gdn_slab_init(C.byref(s), fp(0), nb, 2, vh, kh, kd, vd, 3 * 10240) == 0
+    acc = (C.c_int32 * 2)(0, 1)
+    args = [fp(1 << 32), NULLS] + [fp((i + 2) << 32) for i in range(5)] + [NULLS]
+    # never marked: one-shot state error
+    assert L.gdn_rollback(C.byref(s), *args, 10240, 4, acc, NULLS) == gdn.GDN_ESTATE
+    # an uninitialised slab
+    bad = gdn.gdn_slab()
+    assert L.gdn_rollback(C.byref(bad), *args, 10240, 4, acc, NULLS) == gdn.GDN_ESTATE
+    assert L.gdn_mark(C.byref(bad), fp(1 << 32), NULLS, NULLS) == gdn.GDN_ESTATE
+    # armed state only (history not marked): a history rollback is refused
+    s.armed = 1
+    args_h = list(args)
+    args_h[1] = fp(9 << 32)
+    assert L.gdn_rollback(C.byref(s), *args_h, 10240, 4, acc, NULLS) == gdn.GDN_ESTATE
+    # accepted out of range / M out of range
+    acc_bad = (C.c_int32 * 2)(0, 5)
+    assert L.gdn_rollback(C.byref(s), *args, 10240, 4, acc_bad, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_rollback(C.byref(s), *args, 10240, 0, acc, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_rollback(C.byref(s), *args, 10240, 65, acc, NULLS) == gdn.GDN_EINVAL
+    # S inside the slab
+    args_s = list(args)
+    args_s[0] = fp(4096)
+    assert L.gdn_rollback(C.byref(s), *args_s, 10240, 4, acc, NULLS) == gdn.GDN_EINVAL
+    assert s.armed == 1        # refusals leave the slab as it was
+
+
+def test_frontend_validation():
+    L = gdn.lib()
+    vh, kh, kd, vd = D128
+    ptrs = [fp(i << 32) for i in range(13)]
+    cd = 2 * kh * kd + vh * vd
+    assert L.gdn_frontend(*ptrs, 4, 5120, cd + 4, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_frontend(*ptrs, 4, 5120, cd, 3, vh, kh, kd, vd, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_frontend(*ptrs, 4, 5122, cd, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_frontend(*ptrs, 0, 5120, cd, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_OK
+    p2 = list(ptrs)
+    p2[9] = p2[8]                                   # k aliases q
+    assert L.gdn_frontend(*p2, 4, 5120, cd, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+
+
+def test_stream_copy_validation():
+    L = gdn.lib()
+    assert L.gdn_stream_copy(fp(0), fp(64), 100, NULLS) == gdn.GDN_EINVAL   # overlap
+    assert L.gdn_stream_copy(fp(0), fp(1 << 20), -1, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_stream_copy(fp(0), fp(1 << 20), 0, NULLS) == gdn.GDN_OK
+
+
+def test_max_rel_metric_matches_pages_row():
+    gold = json.load(open(os.path.join(GOLD, "max_rel_p24.json")))
+    r = np.array([gold["max_abs_ref"], -3.0, 1.0])
+    x = r + np.array([gold["max_abs_err"], 1e-7, -5e-7])
+    assert abs(max_rel_pages(x, r) - gold["max_rel"]) / gold["max_rel"] < 2e-3
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        gdn.lib()

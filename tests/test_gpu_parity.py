@@ -1,0 +1,414 @@
+"""GPU parity: the gfx950 kernels (through the C ABI) against the CPU oracle.
+
+Floating point: per element |x - r| <= max(1e-5 |r|, 1e-6) on o, S and the
+front-end outputs.  Bit-exact: step_m against M single steps, rollback against
+single steps from the mark, rollback(0) against the marked bytes, the reset
+gate's closed form, the conv history, repeated runs.  Large workloads are
+checked on sampled units that the oracle recomputes one by one, in the same
+launch configuration the benchmark times (one launch over all units).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_recurrent_amd as gdn
+import synth
+from tests.helpers import assert_close, bits_equal, max_rel_pages
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "g", "beta")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    gdn.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def host(t):
+    return np.ascontiguousarray(t.detach().cpu().numpy())
+
+
+def host_rows(inp, idx):
+    """Inputs [M][N][...] restricted to units idx, on the host."""
+    ii = torch.as_tensor(idx, device=inp["q"].device)
+    return {n: np.ascontiguousarray(host(inp[n].index_select(1, ii))) for n in NAMES}
+
+
+def row0(inp):
+    return {n: inp[n][0] for n in NAMES}
+
+
+def ref_steps(orc, S, inp, dims, rows):
+    """Oracle: `rows` chained single steps; returns list of o."""
+    outs = []
+    for m in range(rows):
+        x = {n: np.ascontiguousarray(inp[n][m]) for n in NAMES}
+        o = np.zeros((S.shape[0], dims[0], dims[3]), np.float32)
+        orc.gdn_step(S, x["q"], x["k"], x["v"], x["g"], x["beta"], o, dims)
+        outs.append(o)
+    return outs
+
+
+# ---------------------------------------------------------------------------
+# single steps, small sizes: every element of every step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dims,N,T", [
+    (synth.DIMS128, 1, 64),          # single sequence, one layer, 64 decode steps
+    (synth.DIMS128, 7, 4),
+    (synth.DIMS64, 5, 6),
+    ((6, 2, 128, 128), 3, 5),
+    ((4, 4, 64, 64), 2, 5),
+    ((8, 1, 128, 128), 2, 3),
+])
+def test_step_chain_parity(orc, dims, N, T):
+    say(f"step chain dims={dims} N={N} T={T}")
+    gen = synth.make_gen(0, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=T, device="cuda")
+    S_ref = host(S)
+    inp_h = {n: host(inp[n]) for n in NAMES}
+    S_h = S_ref.copy()
+    worst = 0.0
+    for m in range(T):
+        o = gdn.step(S, *(inp[n][m] for n in NAMES))
+        x = {n: inp_h[n][m:m + 1] for n in NAMES}
+        o_ref = ref_steps(orc, S_h, x, dims, 1)[0]
+        assert_close(host(o), o_ref, f"o step {m}")
+        assert_close(host(S), S_h, f"S step {m}")
+        worst = max(worst, max_rel_pages(host(o), o_ref))
+    say(f"  worst max|err|/max|ref| over steps = {worst:.3e}")
+
+
+def test_step_writes_every_output_and_is_deterministic():
+    dims = synth.DIMS128
+    N = 9
+    gen = synth.make_gen(1, "cuda")
+    S0 = synth.state(gen, N, dims, device="cuda")
+    inp = row0(synth.step_inputs(gen, N, dims, device="cuda"))
+    runs = []
+    for _ in range(2):
+        S = S0.clone()
+        o = torch.full((N, dims[0], dims[3]), float("nan"), device="cuda")
+        gdn.step(S, *(inp[n] for n in NAMES), o=o)
+        assert not torch.isnan(o).any()
+        runs.append((host(S), host(o)))
+    assert bits_equal(runs[0][0], runs[1][0]) and bits_equal(runs[0][1], runs[1][1])
+
+
+def test_reset_gate_bit_exact_vs_oracle(orc):
+    """g = -inf: S' = fl(k fl(v beta)) on both sides, bit for bit."""
+    for dims in (synth.DIMS128, synth.DIMS64):
+        N = 3
+        gen = synth.make_gen(2, "cuda")
+        S = synth.state(gen, N, dims, device="cuda")
+        inp = row0(synth.step_inputs(gen, N, dims, device="cuda"))
+        inp["g"].fill_(float("-inf"))
+        S_h = host(S)
+        x = {n: host(inp[n]) for n in NAMES}
+        gdn.step(S, *(inp[n] for n in NAMES))
+        o_ref = np.zeros((N, dims[0], dims[3]), np.float32)
+        orc.gdn_step(S_h, x["q"], x["k"], x["v"], x["g"], x["beta"], o_ref, dims)
+        assert bits_equal(host(S), S_h)
+
+
+def test_unit_offsets_identical():
+    dims = synth.DIMS128
+    N = 6
+    gen = synth.make_gen(3, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = row0(synth.step_inputs(gen, N, dims, device="cuda"))
+    S[N - 1] = S[0]
+    for n in NAMES:
+        inp[n][N - 1] = inp[n][0]
+    o = gdn.step(S, *(inp[n] for n in NAMES))
+    assert bits_equal(host(S[0]), host(S[N - 1])) and bits_equal(host(o[0]), host(o[N - 1]))
+
+
+def test_step_on_side_stream(orc):
+    dims = synth.DIMS64
+    N = 4
+    gen = synth.make_gen(4, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = row0(synth.step_inputs(gen, N, dims, device="cuda"))
+    S_h = host(S)
+    x = {n: host(inp[n]) for n in NAMES}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o = gdn.step(S, *(inp[n] for n in NAMES))
+    torch.cuda.current_stream().wait_stream(side)
+    o_ref = np.zeros((N, dims[0], dims[3]), np.float32)
+    orc.gdn_step(S_h, x["q"], x["k"], x["v"], x["g"], x["beta"], o_ref, dims)
+    assert_close(host(o), o_ref, "o side stream")
+    assert_close(host(S), S_h, "S side stream")
+
+
+# ---------------------------------------------------------------------------
+# M-step, mark / rollback
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dims,M", [(synth.DIMS128, 8), (synth.DIMS64, 5), (synth.DIMS128, 1),
+                                    (synth.DIMS128, 64)])
+def test_step_m_bit_exact_and_parity(orc, dims, M):
+    say(f"step_m dims={dims} M={M}")
+    N = 3
+    gen = synth.make_gen(5, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    S1 = S.clone()
+    S_h = host(S)
+    o_m = gdn.step_m(S, *(inp[n] for n in NAMES))
+    for m in range(M):
+        o1 = gdn.step(S1, *(inp[n][m] for n in NAMES))
+        assert bits_equal(host(o1), host(o_m[m])), m
+    assert bits_equal(host(S), host(S1))
+    o_ref = np.zeros((M, N, dims[0], dims[3]), np.float32)
+    orc.gdn_step_m(S_h, *(host(inp[n]) for n in NAMES), o_ref, M, dims)
+    assert_close(host(o_m), o_ref, "o step_m")
+    assert_close(host(S), S_h, "S step_m")
+
+
+@pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
+def test_mark_rollback_bit_exact(orc, dims):
+    """mark -> step_m(M) -> rollback(accepted): each unit equals accepted[u]
+    GPU single steps from the mark (S and history, bit for bit); 0 restores
+    the marked bytes; M reproduces step_m; a second rollback is refused."""
+    say(f"mark/rollback dims={dims}")
+    vh, kh, kd, vd = dims
+    N, M = 6, 5
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(6, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    hist = torch.randn((N, 3, cd), generator=gen, device="cuda")
+    xc = torch.randn((M, N, cd), generator=gen, device="cuda")
+    S_mark, hist_mark = S.clone(), hist.clone()
+    slab = gdn.Slab(N, dims, hist_floats_per_unit=3 * cd)
+    slab.mark(S, hist)
+    assert slab.armed == 3
+    gdn.step_m(S, *(inp[n] for n in NAMES))
+    S_after_m = S.clone()
+    assert not bits_equal(host(S), host(S_mark))
+    hist.add_(1.0)                                 # the history advanced meanwhile
+    acc = [0, 1, 2, M, 3, M - 1]
+    slab.rollback(S, acc, *(inp[n] for n in NAMES), hist=hist, xc_raw=xc)
+    assert slab.armed == 0
+    # expected: GPU single steps from the mark
+    S_exp = S_mark.clone()
+    h_exp = host(hist_mark)
+    xc_h = host(xc)
+    for u in range(N):
+        Su = S_exp[u:u + 1]
+        for m in range(acc[u]):
+            gdn.step(Su, *(inp[n][m, u:u + 1].contiguous() for n in NAMES))
+        seq = np.concatenate([h_exp[u], xc_h[:acc[u], u]], axis=0)
+        h_exp[u] = seq[-3:]
+    assert bits_equal(host(S), host(S_exp))
+    assert bits_equal(host(hist), h_exp)
+    assert bits_equal(host(S[0]), host(S_mark[0]))
+    assert bits_equal(host(S[3]), host(S_after_m[3]))
+    # oracle agrees within tolerance
+    S_ref = host(S_mark)
+    rs = orc.slab(N, dims, hist_floats=3 * cd)
+    h_ref = host(hist_mark)
+    rs.mark(S_ref, h_ref)
+    o_tmp = np.zeros((M, N, vh, vd), np.float32)
+    orc.gdn_step_m(S_ref, *(host(inp[n]) for n in NAMES), o_tmp, M, dims)
+    rs.rollback(S_ref, h_ref, {n: host(inp[n]) for n in NAMES}, M, np.array(acc, np.int32),
+                xc_raw=xc_h, conv_dim=cd, ck=4)
+    assert_close(host(S), S_ref, "S rollback vs oracle")
+    assert bits_equal(host(hist), h_ref)
+    # one-shot
+    with pytest.raises(gdn.GdnError):
+        slab.rollback(S, acc, *(inp[n] for n in NAMES), hist=hist, xc_raw=xc)
+
+
+def test_rollback_state_only_and_zero_accept():
+    dims = synth.DIMS128
+    N, M = 4, 3
+    gen = synth.make_gen(7, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    S_mark = S.clone()
+    slab = gdn.Slab(N, dims)
+    slab.mark(S)
+    gdn.step_m(S, *(inp[n] for n in NAMES))
+    slab.rollback(S, [0] * N, M=M)                 # no inputs needed for a pure restore
+    assert bits_equal(host(S), host(S_mark))
+    # the history cannot be rolled back when it was not marked
+    slab.mark(S)
+    with pytest.raises(gdn.GdnError):
+        slab.rollback(S, [0] * N, M=M, hist=torch.zeros((N, 3, 10240), device="cuda"),
+                      xc_raw=torch.zeros((M, N, 10240), device="cuda"))
+
+
+# ---------------------------------------------------------------------------
+# front end
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dims,B,dim", [
+    (synth.DIMS128, 13, 5120),       # ragged against 8-row GEMV tiles
+    (synth.DIMS64, 9, 5120),
+    ((6, 2, 64, 64), 3, 100),        # conv_dim 640 < one 1024-channel block; dim not /1024
+    ((6, 3, 128, 128), 1, 2052),
+])
+def test_frontend_parity(orc, dims, B, dim):
+    say(f"frontend dims={dims} B={B} dim={dim}")
+    vh, kh, kd, vd = dims
+    gen = synth.make_gen(8, "cuda")
+    w = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=2, dim=dim, device="cuda")
+    hist = fe["hist"]
+    hist_h = host(hist)
+    wh = {n: host(t) for n, t in w.items()}
+    for t in range(2):
+        x, xc = fe["x"][t], fe["xc_raw"][t]
+        out = gdn.frontend(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], xc, hist,
+                           w["conv_w"], dims)
+        ref = dict(q=np.zeros((B, kh, kd), np.float32), k=np.zeros((B, kh, kd), np.float32),
+                   v=np.zeros((B, vh, vd), np.float32), g=np.zeros((B, vh), np.float32),
+                   beta=np.zeros((B, vh), np.float32))
+        orc.gdn_frontend(host(x), wh["Wa"], wh["Wb"], wh["A_log"], wh["dt_bias"], host(xc),
+                         hist_h, wh["conv_w"], ref["q"], ref["k"], ref["v"], ref["g"],
+                         ref["beta"], dims)
+        for n in NAMES:
+            assert_close(host(out[n]), ref[n], f"{n} t={t}")
+        assert bits_equal(host(hist), hist_h)
+
+
+def test_stream_copy_ragged():
+    for n in (1, 3, 4, 1000003, 4 * 256 * 4 * 3 + 5):
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        gdn.stream_copy(dst, src)
+        assert bits_equal(host(dst), host(src)), n
+        gdn.stream_copy(src, src)                  # in place: read and write back
+        assert bits_equal(host(dst), host(src)), n
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, one launch over all units, sampled units recomputed
+# ---------------------------------------------------------------------------
+
+def _sample(N, rng, k=10):
+    idx = sorted(set([0, 1, N // 2, N - 2, N - 1] + list(rng.choice(N, k, replace=False))))
+    return idx
+
+
+@pytest.mark.parametrize("wl", [1, 4, 5])
+def test_full_size_step_sampled(orc, wl):
+    cfg = synth.WORKLOADS[wl]
+    dims = cfg["dims"]
+    N = cfg["seqs"] * cfg["layers"]
+    say(f"full-size step: {cfg['name']} units={N} dims={dims}")
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=2, gate=cfg["gate"], device="cuda")
+    idx = _sample(N, np.random.default_rng(wl))
+    ii = torch.as_tensor(idx, device="cuda")
+    S_h = host(S.index_select(0, ii))
+    x_h = host_rows(inp, idx)
+    for m in range(2):
+        o = gdn.step(S, *(inp[n][m] for n in NAMES))
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all()
+        o_ref = ref_steps(orc, S_h, {n: x_h[n][m:m + 1] for n in NAMES}, dims, 1)[0]
+        assert_close(host(o.index_select(0, ii)), o_ref, f"o step {m}")
+        assert_close(host(S.index_select(0, ii)), S_h, f"S step {m}")
+    del S, inp
+
+
+def test_full_size_verify_cycle_sampled(orc):
+    """Speculative verify at full size: mark, step_m (M=8), rollback with an
+    accepted length per sequence shared by its 48 layers."""
+    cfg = synth.WORKLOADS[2]
+    dims = cfg["dims"]
+    L = cfg["layers"]
+    N = cfg["seqs"] * L
+    M = cfg["M"]
+    say(f"full-size verify: {cfg['name']} units={N}")
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    rng = np.random.default_rng(2)
+    a_seq = rng.integers(0, M + 1, cfg["seqs"])
+    acc = np.repeat(a_seq, L).astype(np.int32)     # unit = seq * layers + layer
+    idx = _sample(N, rng)
+    ii = torch.as_tensor(idx, device="cuda")
+    S_mark_h = host(S.index_select(0, ii))
+    slab = gdn.Slab(N, dims)
+    slab.mark(S)
+    o_m = gdn.step_m(S, *(inp[n] for n in NAMES))
+    S_m_h = host(S.index_select(0, ii))
+    o_m_h = host(o_m.index_select(1, ii))
+    slab.rollback(S, acc, *(inp[n] for n in NAMES))
+    torch.cuda.synchronize()
+    x_h = host_rows(inp, idx)
+    S_ref = S_mark_h.copy()
+    o_ref = np.zeros((M, len(idx), dims[0], dims[3]), np.float32)
+    orc.gdn_step_m(S_ref, *(x_h[n] for n in NAMES), o_ref, M, dims)
+    assert_close(o_m_h, o_ref, "o step_m")
+    assert_close(S_m_h, S_ref, "S step_m")
+    S_rb = host(S.index_select(0, ii))
+    rs = orc.slab(len(idx), dims)
+    S_ref = S_mark_h.copy()
+    rs.mark(S_ref)
+    orc.gdn_step_m(S_ref, *(x_h[n] for n in NAMES), o_ref, M, dims)
+    rs.rollback(S_ref, None, x_h, M, acc[idx])
+    assert_close(S_rb, S_ref, "S rollback")
+    for j, u in enumerate(idx):
+        if acc[u] == 0:
+            assert bits_equal(S_rb[j], S_mark_h[j])
+        if acc[u] == M:
+            assert bits_equal(S_rb[j], S_m_h[j])
+    del S, inp, slab
+
+
+def test_full_size_frontend_step_sampled(orc):
+    """Front end + step, 128 rows x 1 layer, 32 steps; 12 rows recomputed."""
+    cfg = synth.WORKLOADS[3]
+    dims = cfg["dims"]
+    vh, kh, kd, vd = dims
+    B, T = cfg["seqs"], cfg["steps"]
+    say(f"full-size frontend+step: {cfg['name']}")
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    S = synth.state(gen, B, dims, device="cuda")
+    w = synth.frontend_weights(gen, dims, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=T, device="cuda")
+    idx = _sample(B, np.random.default_rng(3), k=6)
+    ii = torch.as_tensor(idx, device="cuda")
+    S_h = host(S.index_select(0, ii))
+    hist = fe["hist"]
+    hist_h = host(hist.index_select(0, ii))
+    wh = {n: host(t) for n, t in w.items()}
+    Bs = len(idx)
+    for t in range(T):
+        x, xc = fe["x"][t], fe["xc_raw"][t]
+        out = gdn.frontend(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], xc, hist,
+                           w["conv_w"], dims)
+        o = gdn.step(S, out["q"], out["k"], out["v"], out["g"], out["beta"])
+        ref = dict(q=np.zeros((Bs, kh, kd), np.float32), k=np.zeros((Bs, kh, kd), np.float32),
+                   v=np.zeros((Bs, vh, vd), np.float32), g=np.zeros((Bs, vh), np.float32),
+                   beta=np.zeros((Bs, vh), np.float32))
+        orc.gdn_frontend(host(x.index_select(0, ii)), wh["Wa"], wh["Wb"], wh["A_log"],
+                         wh["dt_bias"], host(xc.index_select(0, ii)), hist_h, wh["conv_w"],
+                         ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"], dims)
+        for n in NAMES:
+            assert_close(host(out[n].index_select(0, ii)), ref[n], f"frontend {n} t={t}")
+        # the oracle's step runs on the oracle's own front-end outputs
+        o_ref = np.zeros((Bs, vh, vd), np.float32)
+        orc.gdn_step(S_h, ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"], o_ref, dims)
+        assert_close(host(o.index_select(0, ii)), o_ref, f"o t={t}")
+        assert_close(host(S.index_select(0, ii)), S_h, f"S t={t}")
+        assert bits_equal(host(hist.index_select(0, ii)), hist_h)
