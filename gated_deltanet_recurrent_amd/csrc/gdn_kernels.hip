@@ -213,8 +213,10 @@ static __device__ __forceinline__ void chunk_store(Stage<KD> &st, const ChunkReg
 // of step m is completed behind the first barrier of step m+1 (or after the
 // last step).
 // At most 64 VGPRs (8 waves per SIMD) so that two 16-wave workgroups share a
-// CU: two tiles in flight per CU.
-template <int KD>
+// CU: two tiles in flight per CU.  MULTI = false serves calls of at most MC
+// steps (one staging chunk, no prefetch registers); MULTI = true prefetches
+// chunk c+1 while chunk c runs.  Both execute the same per-step arithmetic.
+template <int KD, bool MULTI>
 __global__ __launch_bounds__(Geo<KD>::LANES) __attribute__((amdgpu_waves_per_eu(8)))
 void recur_kernel(RecurArgs a) {
   using G = Geo<KD>;
@@ -251,7 +253,7 @@ void recur_kernel(RecurArgs a) {
     Stage<KD> &sb = st[buf];
     chunk_store<KD>(sb, cr, t, nr);
     __syncthreads();
-    if (m0 + MC < steps) {
+    if (MULTI && m0 + MC < steps) {
       const int nn = steps - m0 - MC;
       chunk_load<KD>(cr, a, t, unit, head, hh, m0 + MC, nn < MC ? nn : MC);
     }
@@ -322,10 +324,18 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
   RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, n_units, vh, kh, M};
   const int64_t tiles = n_units * vh;
   if (tiles <= 0) return 0;
-  if (kd == 128)
-    hipLaunchKernelGGL(recur_kernel<128>, dim3((unsigned)tiles), dim3(Geo<128>::LANES), 0, s, a);
-  else
-    hipLaunchKernelGGL(recur_kernel<64>, dim3((unsigned)tiles), dim3(Geo<64>::LANES), 0, s, a);
+  const dim3 grid((unsigned)tiles);
+  if (kd == 128) {
+    if (M <= MC)
+      hipLaunchKernelGGL((recur_kernel<128, false>), grid, dim3(Geo<128>::LANES), 0, s, a);
+    else
+      hipLaunchKernelGGL((recur_kernel<128, true>), grid, dim3(Geo<128>::LANES), 0, s, a);
+  } else {
+    if (M <= MC)
+      hipLaunchKernelGGL((recur_kernel<64, false>), grid, dim3(Geo<64>::LANES), 0, s, a);
+    else
+      hipLaunchKernelGGL((recur_kernel<64, true>), grid, dim3(Geo<64>::LANES), 0, s, a);
+  }
   return (int)hipGetLastError();
 }
 
