@@ -76,29 +76,60 @@ static __device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) 
 // ---------------------------------------------------------------------------
 // Recurrence
 // ---------------------------------------------------------------------------
+//
+// Canonical summation order of the read-outs S^T k and S^T q for one column.
+// Rows are grouped as rg + RG*j (RG = kd/4 row groups, j = 0..3):
+//   p[rg]  = fma chain over j = 0..3 of S[rg + RG*j] * x[rg + RG*j]
+//   kd = 128: W[w] = p[2w] + p[2w+1] (w < 16);
+//             H0 = W0 + W1 + ... + W7, H1 = W8 + ... + W15 (left folds);
+//             sum = H0 + H1
+//   kd = 64:  W[w] = (p[4w] + p[4w+1]) + (p[4w+2] + p[4w+3]) (w < 4);
+//             sum = (W0 + W1) + (W2 + W3)
+// Two tile geometries compute exactly this tree, so every entry point gives
+// the same bits whichever geometry serves it:
+//   wide (single steps, bandwidth bound): 16 floats per lane, kd = 128 on
+//     1024 lanes, kd = 64 on 256 lanes; lane = (column group, row group);
+//   deep (several steps per call, arithmetic bound): 64 floats per lane,
+//     kd = 128 on 256 lanes, kd = 64 on one wave; lane = (column group,
+//     4 consecutive row groups), which keeps more tiles resident per CU and
+//     needs fewer cross-lane exchanges per element.
 
-// Tile geometry: every lane holds 16 floats of the tile (4 rows x 4 adjacent
-// columns), which measured fastest for both head sizes; kd = 128 uses 1024
-// lanes (16 wave64), kd = 64 uses 256 lanes.
+template <int KD>
+struct Canon {
+  static constexpr int RG = KD / 4;              // row groups (rows rg + RG*j)
+  static constexpr int CG = KD / 4;              // column groups of 4 columns
+  static constexpr int NWP = KD == 128 ? 16 : 4; // W partials
+};
+
+// Wide geometry.
 template <int KD>
 struct Geo {
   static constexpr int NW = KD * KD / (16 * 64);  // waves per tile
   static constexpr int LANES = 64 * NW;
-  static constexpr int CG = KD / 4;               // column groups (4 columns each)
-  static constexpr int RG = LANES / CG;           // row groups
+  static constexpr int CG = Canon<KD>::CG;
+  static constexpr int RG = LANES / CG;           // row groups, one per lane row
   static constexpr int R = KD / RG;               // rows per lane
   static constexpr int GPW = 64 / CG;             // row groups per wave
-  static constexpr int PER = NW / GPW;            // wave partials per final-sum lane group
-  static_assert(R == 4 && LANES >= 2 * KD && NW % GPW == 0, "tile geometry");
+  static constexpr int PER = NW / GPW;            // W partials per final-sum lane group
+  static_assert(R == 4 && RG == Canon<KD>::RG && NW == Canon<KD>::NWP, "wide geometry");
 };
 
-// Sum over the GPW row groups that share this lane's columns inside one wave
-// (lanes t, t^CG, ...).  Every add is commutative, so all those lanes end up
-// with the same bits.
+// Deep geometry.
+template <int KD>
+struct Deep {
+  static constexpr int LANES = KD * KD / 64;      // 64 floats per lane
+  static constexpr int CG = Canon<KD>::CG;
+  static constexpr int LG = LANES / CG;           // lane rows; each holds 4 row groups
+  static_assert(LG * 4 == Canon<KD>::RG, "deep geometry");
+};
+
+// Fold over the row groups that share this lane's columns inside one wave
+// (lanes t, t ^ CG, ...).  Every add is commutative, so all those lanes end
+// up with the same bits.
 template <int KD>
 static __device__ __forceinline__ f4 wave_fold(f4 p) {
 #pragma unroll
-  for (int off = Geo<KD>::CG; off < 64; off <<= 1) {
+  for (int off = Canon<KD>::CG; off < 64; off <<= 1) {
     p.x = p.x + __shfl_xor(p.x, off);
     p.y = p.y + __shfl_xor(p.y, off);
     p.z = p.z + __shfl_xor(p.z, off);
@@ -107,16 +138,17 @@ static __device__ __forceinline__ f4 wave_fold(f4 p) {
   return p;
 }
 
-// Final sum for wave 0 over the per-wave partials red[NW][CG], in a fixed
-// order: lane group h = lane / CG adds waves h*PER .. h*PER+PER-1, then the
-// groups are folded.  Valid in every lane of wave 0 for column group lane%CG.
+// Final sum over the W partials red[NWP][CG] by one wave: lane group
+// h = lane / CG left-folds partials h*PER .. h*PER + PER - 1, then the groups
+// are folded.  Valid in every lane of the wave for column group lane % CG.
 template <int KD>
-static __device__ __forceinline__ f4 tile_sum(const f4 (*red)[Geo<KD>::CG], int lane) {
-  using G = Geo<KD>;
-  const int cg = lane % G::CG, h = lane / G::CG;
-  f4 acc = red[h * G::PER][cg];
+static __device__ __forceinline__ f4 tile_sum(const f4 (*red)[Canon<KD>::CG], int lane) {
+  constexpr int CG = Canon<KD>::CG;
+  constexpr int PER = Canon<KD>::NWP / (64 / CG);
+  const int cg = lane % CG, h = lane / CG;
+  f4 acc = red[h * PER][cg];
 #pragma unroll
-  for (int i = 1; i < G::PER; i++) acc = acc + red[h * G::PER + i][cg];
+  for (int i = 1; i < PER; i++) acc = acc + red[h * PER + i][cg];
   return wave_fold<KD>(acc);
 }
 
@@ -130,49 +162,43 @@ struct RecurArgs {
   int vh, kh, M;
 };
 
-// Per-step inputs are staged through LDS in chunks of MC rows, double
-// buffered: the registers of each lane prefetch the next chunk while the
-// current one is consumed, so a multi-step call pays one global-load latency
-// per chunk rather than per step.
+// Per-step inputs are staged through LDS in chunks of MC rows.  q and k are
+// stored permuted, element rg*4 + j holding row rg + RG*j, so that a lane
+// reads the 4 values of one row group with a single 128-bit LDS load.  For
+// calls of more than MC rows the registers of each lane prefetch the next
+// chunk while the current one runs (double-buffered stage).
 constexpr int MC = 8;
 
 template <int KD>
 struct Stage {
-  float qk[MC][2 * KD];  // q | k of each row
+  float q[MC][KD];
+  float k[MC][KD];
   float v[MC][KD];
   float alpha[MC];       // exp(g)
   float beta[MC];
 };
 
-template <int KD>
+template <int KD, int LANES>
 struct ChunkRegs {
-  static constexpr int QKP = MC * 2 * KD / Geo<KD>::LANES;  // q|k floats per lane
-  static constexpr int VP = MC * KD / Geo<KD>::LANES;       // v floats per lane
-  float qk[QKP];
-  float v[VP];
+  static constexpr int E = MC * KD;                   // floats of q (or k, v) per chunk
+  static constexpr int P = (E + LANES - 1) / LANES;   // per lane
+  float q[P], k[P], v[P];
   float gb;  // g (lanes < MC) or beta (lanes MC .. 2*MC-1)
 };
 
-template <int KD>
-static __device__ __forceinline__ void chunk_load(ChunkRegs<KD> &c, const RecurArgs &a, int t,
-                                                  int64_t unit, int head, int hh, int m0, int nr) {
-  using G = Geo<KD>;
+template <int KD, int LANES>
+static __device__ __forceinline__ void chunk_load(ChunkRegs<KD, LANES> &c, const RecurArgs &a,
+                                                  int t, int64_t unit, int head, int hh, int m0,
+                                                  int nr) {
+  using C = ChunkRegs<KD, LANES>;
 #pragma unroll
-  for (int i = 0; i < ChunkRegs<KD>::QKP; i++) {
-    const int e = t + i * G::LANES;
-    const int r = e / (2 * KD), col = e % (2 * KD);
-    if (r < nr) {
-      const int64_t urow = (int64_t)(m0 + r) * a.n_units + unit;
-      c.qk[i] = col < KD ? a.q[(urow * a.kh + hh) * KD + col]
-                         : a.k[(urow * a.kh + hh) * KD + (col - KD)];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < ChunkRegs<KD>::VP; i++) {
-    const int e = t + i * G::LANES;
+  for (int i = 0; i < C::P; i++) {
+    const int e = t + i * LANES;
     const int r = e / KD, col = e % KD;
-    if (r < nr) {
+    if (e < C::E && r < nr) {
       const int64_t urow = (int64_t)(m0 + r) * a.n_units + unit;
+      c.q[i] = a.q[(urow * a.kh + hh) * KD + col];
+      c.k[i] = a.k[(urow * a.kh + hh) * KD + col];
       c.v[i] = a.v[(urow * a.vh + head) * KD + col];
     }
   }
@@ -185,19 +211,21 @@ static __device__ __forceinline__ void chunk_load(ChunkRegs<KD> &c, const RecurA
   }
 }
 
-template <int KD>
-static __device__ __forceinline__ void chunk_store(Stage<KD> &st, const ChunkRegs<KD> &c, int t,
-                                                   int nr) {
-  using G = Geo<KD>;
+template <int KD, int LANES>
+static __device__ __forceinline__ void chunk_store(Stage<KD> &st, const ChunkRegs<KD, LANES> &c,
+                                                   int t, int nr) {
+  using C = ChunkRegs<KD, LANES>;
+  constexpr int RG = Canon<KD>::RG;
 #pragma unroll
-  for (int i = 0; i < ChunkRegs<KD>::QKP; i++) {
-    const int e = t + i * G::LANES;
-    if (e / (2 * KD) < nr) (&st.qk[0][0])[e] = c.qk[i];
-  }
-#pragma unroll
-  for (int i = 0; i < ChunkRegs<KD>::VP; i++) {
-    const int e = t + i * G::LANES;
-    if (e / KD < nr) (&st.v[0][0])[e] = c.v[i];
+  for (int i = 0; i < C::P; i++) {
+    const int e = t + i * LANES;
+    const int r = e / KD, col = e % KD;
+    if (e < C::E && r < nr) {
+      const int pc = (col % RG) * 4 + col / RG;
+      st.q[r][pc] = c.q[i];
+      st.k[r][pc] = c.k[i];
+      st.v[r][col] = c.v[i];
+    }
   }
   if (t < 2 * MC && t % MC < nr) {
     if (t < MC)
@@ -207,41 +235,55 @@ static __device__ __forceinline__ void chunk_store(Stage<KD> &st, const ChunkReg
   }
 }
 
-// One workgroup per tile.  Per step: decay and S^T k partials; barrier; wave
-// 0 finishes S^T k and forms tmp = (v - kv) beta (and finishes the previous
-// step's output); barrier; rank-1 update and S^T q partials.  The output sum
-// of step m is completed behind the first barrier of step m+1 (or after the
-// last step).
-// At most 64 VGPRs (8 waves per SIMD) so that two 16-wave workgroups share a
-// CU: two tiles in flight per CU.  MULTI = false serves calls of at most MC
-// steps (one staging chunk, no prefetch registers); MULTI = true prefetches
-// chunk c+1 while chunk c runs.  Both execute the same per-step arithmetic.
+static __device__ __forceinline__ f4 lds4(const float *p) {
+  return *reinterpret_cast<const f4 *>(p);
+}
+
+struct TileIdx {
+  int64_t unit, tile_off;
+  int head, hh, steps;
+};
+
+static __device__ __forceinline__ TileIdx tile_index(const RecurArgs &a, int kdkd) {
+  TileIdx x;
+  const int64_t tile = xcd_contiguous(blockIdx.x, gridDim.x);
+  x.unit = tile / a.vh;
+  x.head = (int)(tile - x.unit * a.vh);
+  x.hh = x.head / (a.vh / a.kh);
+  x.steps = a.steps ? a.steps[x.unit] : a.M;
+  x.tile_off = tile * (int64_t)kdkd;
+  return x;
+}
+
+// ----- wide geometry -------------------------------------------------------
+//
+// Per step: decay and S^T k partials; barrier; wave 0 finishes S^T k, forms
+// tmp = (v - kv) beta and finishes the previous step's output; barrier;
+// rank-1 update and S^T q partials.  The output of the last step is finished
+// after the loop.  At most 64 VGPRs (8 waves per SIMD): two 16-wave
+// workgroups share a CU.
 template <int KD, bool MULTI>
 __global__ __launch_bounds__(Geo<KD>::LANES) __attribute__((amdgpu_waves_per_eu(8)))
-void recur_kernel(RecurArgs a) {
+void recur_wide_kernel(RecurArgs a) {
   using G = Geo<KD>;
-  __shared__ Stage<KD> st[2];
-  __shared__ f4 s_red_k[G::NW][G::CG];     // per-wave partials of S^T k
-  __shared__ f4 s_red_o[G::NW][G::CG];     // per-wave partials of S^T q
-  __shared__ f4 s_tmp[G::CG];              // (v - S^T k) * beta
+  constexpr int LANES = G::LANES;
+  __shared__ Stage<KD> st[MULTI ? 2 : 1];
+  __shared__ f4 s_red_k[G::NW][G::CG];
+  __shared__ f4 s_red_o[G::NW][G::CG];
+  __shared__ f4 s_tmp[G::CG];
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int cg = t % G::CG;
-  const int rg = t / G::CG;
-  const int64_t tile = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int64_t unit = tile / a.vh;
-  const int head = (int)(tile - unit * a.vh);
-  const int hh = head / (a.vh / a.kh);
-  const int steps = a.steps ? a.steps[unit] : a.M;
-  const int64_t tile_off = tile * (int64_t)(KD * KD);
-  const float *src = a.S_src + tile_off + rg * KD + 4 * cg;
-  float *dst = a.S_dst + tile_off + rg * KD + 4 * cg;
+  const int cg = t % G::CG, rg = t / G::CG;
+  const TileIdx ti = tile_index(a, KD * KD);
+  const int steps = ti.steps;
+  const float *src = a.S_src + ti.tile_off + rg * KD + 4 * cg;
+  float *dst = a.S_dst + ti.tile_off + rg * KD + 4 * cg;
 
-  // The first chunk of inputs is requested before the state so that its
-  // latency hides under the state stream.
-  ChunkRegs<KD> cr;
-  if (steps > 0) chunk_load<KD>(cr, a, t, unit, head, hh, 0, steps < MC ? steps : MC);
+  // the first chunk of inputs is requested before the state, so that its
+  // latency hides under the state stream
+  ChunkRegs<KD, LANES> cr;
+  if (steps > 0) chunk_load<KD, LANES>(cr, a, t, ti.unit, ti.head, ti.hh, 0, steps < MC ? steps : MC);
 
   f4 s[G::R];
 #pragma unroll
@@ -250,49 +292,47 @@ void recur_kernel(RecurArgs a) {
   int buf = 0;
   for (int m0 = 0; m0 < steps; m0 += MC) {
     const int nr = steps - m0 < MC ? steps - m0 : MC;
-    Stage<KD> &sb = st[buf];
-    chunk_store<KD>(sb, cr, t, nr);
+    Stage<KD> &sb = st[MULTI ? buf : 0];
+    chunk_store<KD, LANES>(sb, cr, t, nr);
     __syncthreads();
     if (MULTI && m0 + MC < steps) {
       const int nn = steps - m0 - MC;
-      chunk_load<KD>(cr, a, t, unit, head, hh, m0 + MC, nn < MC ? nn : MC);
+      chunk_load<KD, LANES>(cr, a, t, ti.unit, ti.head, ti.hh, m0 + MC, nn < MC ? nn : MC);
     }
     for (int r = 0; r < nr; r++) {
       const int m = m0 + r;
-      // decay, then S^T k over the decayed state
       const float alpha = sb.alpha[r];
+      const f4 kk = lds4(&sb.k[r][rg * 4]);
+      // decay, then S^T k over the decayed state
       f4 p = splat(0.0f);
 #pragma unroll
       for (int j = 0; j < G::R; j++) {
         s[j] = s[j] * alpha;
-        p = fma4(s[j], splat(sb.qk[r][KD + rg + G::RG * j]), p);
+        p = fma4(s[j], splat(kk[j]), p);
       }
       p = wave_fold<KD>(p);
       if (lane < G::CG) s_red_k[wave][lane] = p;
       __syncthreads();
       if (wave == 0) {
         const f4 kv = tile_sum<KD>(s_red_k, lane);
-        if (lane < G::CG) {
-          const f4 vcur = *reinterpret_cast<const f4 *>(&sb.v[r][4 * lane]);
-          s_tmp[lane] = (vcur - kv) * sb.beta[r];
-        }
+        if (lane < G::CG) s_tmp[lane] = (lds4(&sb.v[r][4 * lane]) - kv) * sb.beta[r];
         if (m > 0) {
           const f4 ov = tile_sum<KD>(s_red_o, lane);
           if (a.o != nullptr && lane < G::CG) {
-            const int64_t urow = (int64_t)(m - 1) * a.n_units + unit;
-            st4(a.o + (urow * a.vh + head) * KD + 4 * lane, ov);
+            const int64_t urow = (int64_t)(m - 1) * a.n_units + ti.unit;
+            st4(a.o + (urow * a.vh + ti.head) * KD + 4 * lane, ov);
           }
         }
       }
       __syncthreads();
       const f4 tmp = s_tmp[cg];
+      const f4 qq = lds4(&sb.q[r][rg * 4]);
       // rank-1 update, then S^T q with the updated state
       p = splat(0.0f);
 #pragma unroll
       for (int j = 0; j < G::R; j++) {
-        const int row = rg + G::RG * j;
-        s[j] = fma4(splat(sb.qk[r][KD + row]), tmp, s[j]);
-        p = fma4(s[j], splat(sb.qk[r][row]), p);
+        s[j] = fma4(splat(kk[j]), tmp, s[j]);
+        p = fma4(s[j], splat(qq[j]), p);
       }
       p = wave_fold<KD>(p);
       if (lane < G::CG) s_red_o[wave][lane] = p;
@@ -308,14 +348,168 @@ void recur_kernel(RecurArgs a) {
     if (wave == 0) {
       const f4 ov = tile_sum<KD>(s_red_o, lane);
       if (a.o != nullptr && lane < G::CG) {
-        const int64_t urow = (int64_t)(steps - 1) * a.n_units + unit;
-        st4(a.o + (urow * a.vh + head) * KD + 4 * lane, ov);
+        const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
+        st4(a.o + (urow * a.vh + ti.head) * KD + 4 * lane, ov);
       }
     }
   }
 }
 
+// ----- deep geometry -------------------------------------------------------
+//
+// Lane (cg, L) holds row groups 4L .. 4L+3 (16 rows x 4 columns) and forms
+// their p's itself.  kd = 128: the W partials go through LDS to wave 0 as in
+// the wide kernel (2 barriers per step); kd = 64: the whole tile is one wave
+// and both read-outs finish with in-wave shuffles (no barrier per step).
+template <int KD>
+static __device__ __forceinline__ void deep_partials(const f4 (&p)[4], f4 &w0, f4 &w1) {
+  if (KD == 128) {
+    w0 = p[0] + p[1];
+    w1 = p[2] + p[3];
+  } else {
+    w0 = (p[0] + p[1]) + (p[2] + p[3]);
+  }
+}
+
+template <int KD, bool MULTI>
+__global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a) {
+  using D = Deep<KD>;
+  constexpr int LANES = D::LANES, RG = Canon<KD>::RG, CG = D::CG;
+  constexpr bool XWAVE = KD == 128;             // partials cross waves
+  __shared__ Stage<KD> st[MULTI ? 2 : 1];
+  __shared__ f4 s_red_k[XWAVE ? Canon<KD>::NWP : 1][CG];
+  __shared__ f4 s_red_o[XWAVE ? Canon<KD>::NWP : 1][CG];
+  __shared__ f4 s_tmp[CG];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int cg = t % CG, L = t / CG;
+  const TileIdx ti = tile_index(a, KD * KD);
+  const int steps = ti.steps;
+  // element (i, j) of this lane: row 4L + i + RG*j
+  const float *src = a.S_src + ti.tile_off + (4 * L) * KD + 4 * cg;
+  float *dst = a.S_dst + ti.tile_off + (4 * L) * KD + 4 * cg;
+
+  ChunkRegs<KD, LANES> cr;
+  if (steps > 0) chunk_load<KD, LANES>(cr, a, t, ti.unit, ti.head, ti.hh, 0, steps < MC ? steps : MC);
+
+  f4 s[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) s[i][j] = ld_nt(src + (i + RG * j) * KD);
+
+  int buf = 0;
+  for (int m0 = 0; m0 < steps; m0 += MC) {
+    const int nr = steps - m0 < MC ? steps - m0 : MC;
+    Stage<KD> &sb = st[MULTI ? buf : 0];
+    chunk_store<KD, LANES>(sb, cr, t, nr);
+    __syncthreads();
+    if (MULTI && m0 + MC < steps) {
+      const int nn = steps - m0 - MC;
+      chunk_load<KD, LANES>(cr, a, t, ti.unit, ti.head, ti.hh, m0 + MC, nn < MC ? nn : MC);
+    }
+    for (int r = 0; r < nr; r++) {
+      const int m = m0 + r;
+      const int64_t urow = (int64_t)m * a.n_units + ti.unit;
+      const float alpha = sb.alpha[r];
+      f4 p[4], w0, w1 = splat(0.0f);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const f4 kk = lds4(&sb.k[r][(4 * L + i) * 4]);
+        p[i] = splat(0.0f);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          s[i][j] = s[i][j] * alpha;
+          p[i] = fma4(s[i][j], splat(kk[j]), p[i]);
+        }
+      }
+      deep_partials<KD>(p, w0, w1);
+      f4 tmp;
+      if (XWAVE) {
+        s_red_k[2 * L][cg] = w0;
+        s_red_k[2 * L + 1][cg] = w1;
+        __syncthreads();
+        if (wave == 0) {
+          const f4 kv = tile_sum<KD>(s_red_k, lane);
+          if (lane < CG) s_tmp[lane] = (lds4(&sb.v[r][4 * lane]) - kv) * sb.beta[r];
+          if (m > 0) {
+            const f4 ov = tile_sum<KD>(s_red_o, lane);
+            if (a.o != nullptr && lane < CG) {
+              const int64_t prow = (int64_t)(m - 1) * a.n_units + ti.unit;
+              st4(a.o + (prow * a.vh + ti.head) * KD + 4 * lane, ov);
+            }
+          }
+        }
+        __syncthreads();
+        tmp = s_tmp[cg];
+      } else {
+        const f4 kv = wave_fold<KD>(w0);
+        tmp = (lds4(&sb.v[r][4 * cg]) - kv) * sb.beta[r];
+      }
+      // rank-1 update, then S^T q with the updated state
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const f4 kk = lds4(&sb.k[r][(4 * L + i) * 4]);
+        const f4 qq = lds4(&sb.q[r][(4 * L + i) * 4]);
+        p[i] = splat(0.0f);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          s[i][j] = fma4(splat(kk[j]), tmp, s[i][j]);
+          p[i] = fma4(s[i][j], splat(qq[j]), p[i]);
+        }
+      }
+      deep_partials<KD>(p, w0, w1);
+      if (XWAVE) {
+        s_red_o[2 * L][cg] = w0;
+        s_red_o[2 * L + 1][cg] = w1;
+      } else {
+        const f4 ov = wave_fold<KD>(w0);
+        if (a.o != nullptr && L == 0) st4(a.o + (urow * a.vh + ti.head) * KD + 4 * cg, ov);
+      }
+    }
+    buf ^= 1;
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) st_nt(dst + (i + RG * j) * KD, s[i][j]);
+
+  if (XWAVE && steps > 0) {
+    __syncthreads();
+    if (wave == 0) {
+      const f4 ov = tile_sum<KD>(s_red_o, lane);
+      if (a.o != nullptr && lane < CG) {
+        const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
+        st4(a.o + (urow * a.vh + ti.head) * KD + 4 * lane, ov);
+      }
+    }
+  }
+}
+
+// Calls with M >= DEEP_MIN_M rows per unit run the deep geometry.
+#ifndef GDN_DEEP_MIN_M
+#define GDN_DEEP_MIN_M 2
+#endif
+
 int recur_lanes(int kd) { return kd == 128 ? Geo<128>::LANES : Geo<64>::LANES; }
+
+template <int KD>
+static void launch_recur_kd(const RecurArgs &a, int64_t tiles, hipStream_t s) {
+  const dim3 grid((unsigned)tiles);
+  if (a.M < GDN_DEEP_MIN_M) {
+    if (a.M <= MC)
+      hipLaunchKernelGGL((recur_wide_kernel<KD, false>), grid, dim3(Geo<KD>::LANES), 0, s, a);
+    else
+      hipLaunchKernelGGL((recur_wide_kernel<KD, true>), grid, dim3(Geo<KD>::LANES), 0, s, a);
+  } else {
+    if (a.M <= MC)
+      hipLaunchKernelGGL((recur_deep_kernel<KD, false>), grid, dim3(Deep<KD>::LANES), 0, s, a);
+    else
+      hipLaunchKernelGGL((recur_deep_kernel<KD, true>), grid, dim3(Deep<KD>::LANES), 0, s, a);
+  }
+}
 
 int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *k, const float *v, const float *g,
@@ -324,18 +518,10 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
   RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, n_units, vh, kh, M};
   const int64_t tiles = n_units * vh;
   if (tiles <= 0) return 0;
-  const dim3 grid((unsigned)tiles);
-  if (kd == 128) {
-    if (M <= MC)
-      hipLaunchKernelGGL((recur_kernel<128, false>), grid, dim3(Geo<128>::LANES), 0, s, a);
-    else
-      hipLaunchKernelGGL((recur_kernel<128, true>), grid, dim3(Geo<128>::LANES), 0, s, a);
-  } else {
-    if (M <= MC)
-      hipLaunchKernelGGL((recur_kernel<64, false>), grid, dim3(Geo<64>::LANES), 0, s, a);
-    else
-      hipLaunchKernelGGL((recur_kernel<64, true>), grid, dim3(Geo<64>::LANES), 0, s, a);
-  }
+  if (kd == 128)
+    launch_recur_kd<128>(a, tiles, s);
+  else
+    launch_recur_kd<64>(a, tiles, s);
   return (int)hipGetLastError();
 }
 
