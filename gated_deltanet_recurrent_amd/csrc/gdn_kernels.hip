@@ -600,13 +600,19 @@ int launch_hist_replay(float *hist, const float *snap, const float *xc_raw,
 // transform in the epilogue ("Kestrel_VLLM #27", section 4.2: both
 // projections in one launch; "Kestrel_VLLM #24", section 3: g from a, beta
 // from b).  A workgroup owns FB batch rows x FR rows of the stacked [Wa; Wb]
-// and splits the dot products across its 256 lanes (128-bit loads, lane
-// stride 1024 floats); the 32 partial sums per lane are reduced with a
-// transposing butterfly (32 shuffles per lane) and then across the 4 waves.
+// and splits the dot products across FE_LANES lanes (128-bit loads, two
+// chunks in flight per lane); the 32 partial sums per lane are reduced with a
+// transposing butterfly (32 shuffles per lane) and then across the waves in
+// a fixed order.
 // ---------------------------------------------------------------------------
 
 constexpr int FB = 8;   // batch rows per workgroup
 constexpr int FR = 4;   // stacked weight rows per workgroup
+#ifndef GDN_FE_LANES
+#define GDN_FE_LANES 512
+#endif
+constexpr int FE_LANES = GDN_FE_LANES;
+constexpr int FE_WAVES = FE_LANES / 64;
 
 static __device__ __forceinline__ float softplus_guarded(float z) {
   if (z > 20.0f) return z;
@@ -614,15 +620,31 @@ static __device__ __forceinline__ float softplus_guarded(float z) {
   return log1pf(expf(z));
 }
 
-__global__ __launch_bounds__(256) void fe_gemv_kernel(const float *x, const float *Wa,
-                                                      const float *Wb, const float *A_log,
-                                                      const float *dt_bias, float *g,
-                                                      float *beta, int B, int dim, int vh) {
-  __shared__ float s_w[4][FB * FR];
+static __device__ __forceinline__ void fe_accumulate(float (&acc)[FB * FR], const f4 (&w)[FR],
+                                                     const f4 (&xv)[FB]) {
+#pragma unroll
+  for (int b = 0; b < FB; b++)
+#pragma unroll
+    for (int r = 0; r < FR; r++) {
+      float s = acc[b * FR + r];
+      s = __builtin_fmaf(w[r].x, xv[b].x, s);
+      s = __builtin_fmaf(w[r].y, xv[b].y, s);
+      s = __builtin_fmaf(w[r].z, xv[b].z, s);
+      s = __builtin_fmaf(w[r].w, xv[b].w, s);
+      acc[b * FR + r] = s;
+    }
+}
+
+static __device__ __forceinline__ void fe_gemv_block(int bx, int by, const float *x,
+                                                     const float *Wa, const float *Wb,
+                                                     const float *A_log, const float *dt_bias,
+                                                     float *g, float *beta, int B, int dim,
+                                                     int vh) {
+  __shared__ float s_w[FE_WAVES][FB * FR];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int b0 = blockIdx.x * FB;
-  const int r0 = blockIdx.y * FR;
+  const int b0 = bx * FB;
+  const int r0 = by * FR;
 
   const float *wrow[FR];
 #pragma unroll
@@ -642,23 +664,30 @@ __global__ __launch_bounds__(256) void fe_gemv_kernel(const float *x, const floa
   float acc[FB * FR];
 #pragma unroll
   for (int i = 0; i < FB * FR; i++) acc[i] = 0.0f;
-  for (int c = 4 * t; c < dim; c += 4 * 256) {
-    f4 w[FR];
+  constexpr int STRIDE = 4 * FE_LANES;
+  int c = 4 * t;
+  for (; c + STRIDE < dim; c += 2 * STRIDE) {
+    f4 w0[FR], w1[FR], x0[FB], x1[FB];
 #pragma unroll
-    for (int r = 0; r < FR; r++) w[r] = ld4(wrow[r] + c);
+    for (int r = 0; r < FR; r++) {
+      w0[r] = ld4(wrow[r] + c);
+      w1[r] = ld4(wrow[r] + c + STRIDE);
+    }
 #pragma unroll
     for (int b = 0; b < FB; b++) {
-      const f4 xv = ld4(xrow[b] + c);
-#pragma unroll
-      for (int r = 0; r < FR; r++) {
-        float s = acc[b * FR + r];
-        s = __builtin_fmaf(w[r].x, xv.x, s);
-        s = __builtin_fmaf(w[r].y, xv.y, s);
-        s = __builtin_fmaf(w[r].z, xv.z, s);
-        s = __builtin_fmaf(w[r].w, xv.w, s);
-        acc[b * FR + r] = s;
-      }
+      x0[b] = ld4(xrow[b] + c);
+      x1[b] = ld4(xrow[b] + c + STRIDE);
     }
+    fe_accumulate(acc, w0, x0);
+    fe_accumulate(acc, w1, x1);
+  }
+  if (c < dim) {
+    f4 w0[FR], x0[FB];
+#pragma unroll
+    for (int r = 0; r < FR; r++) w0[r] = ld4(wrow[r] + c);
+#pragma unroll
+    for (int b = 0; b < FB; b++) x0[b] = ld4(xrow[b] + c);
+    fe_accumulate(acc, w0, x0);
   }
 
   // Transposing butterfly over the 64 lanes: after the step with offset 2^p
@@ -717,7 +746,9 @@ __global__ __launch_bounds__(256) void fe_gemv_kernel(const float *x, const floa
   if ((lane & 1) == 0) s_w[wave][lane >> 1] = v1;
   __syncthreads();
   if (t < FB * FR) {
-    const float sum = ((s_w[0][t] + s_w[1][t]) + s_w[2][t]) + s_w[3][t];
+    float sum = s_w[0][t];
+#pragma unroll
+    for (int w = 1; w < FE_WAVES; w++) sum = sum + s_w[w][t];
     const int b = b0 + t / FR;
     const int R = r0 + t % FR;
     if (b < B && R < 2 * vh) {
@@ -732,23 +763,27 @@ __global__ __launch_bounds__(256) void fe_gemv_kernel(const float *x, const floa
 }
 
 // ---------------------------------------------------------------------------
-// Front end, kernel B: depthwise causal conv (4 taps) + SiLU + history
+// Front end, conv part: depthwise causal conv (4 taps) + SiLU + history
 // advance + split + per key-head L2 norm ("Kestrel_VLLM #24", section 3 and
-// Fig. 1 caption).  One workgroup per (row, block of 1024 channels); each
-// lane owns 4 adjacent channels, whose 4 taps are one 16-float run of conv_w.
-// A key head (KD channels) is KD/4 adjacent lanes of one wave, so its sum of
-// squares is a shuffle reduction.  Head boundaries are multiples of KD and
-// blocks are multiples of 1024, so no head straddles two workgroups.
+// Fig. 1 caption).  Each half of a FE_LANES workgroup handles one batch row
+// and a block of 1024 channels; a lane owns 4 adjacent channels, whose 4
+// taps are one 16-float run of conv_w.  A key head (KD channels) is KD/4
+// adjacent lanes of one wave, so its sum of squares is a shuffle reduction.
+// Head boundaries are multiples of KD and blocks are multiples of 1024, so no
+// head straddles two blocks.
 // ---------------------------------------------------------------------------
 
+constexpr int CONV_ROWS = FE_LANES / 256;   // batch rows per conv block
+
 template <int KD>
-__global__ __launch_bounds__(256) void fe_conv_kernel(const float *xc_raw, float *hist,
-                                                      const float *conv_w, float *q, float *k,
-                                                      float *v, int conv_dim, int kh, int vh) {
-  const int t = threadIdx.x;
-  const int64_t b = blockIdx.y;
-  const int ch = blockIdx.x * 1024 + 4 * t;
-  const bool valid = ch < conv_dim;
+static __device__ __forceinline__ void fe_conv_block(int bx, int by, const float *xc_raw,
+                                                     float *hist, const float *conv_w, float *q,
+                                                     float *k, float *v, int B, int conv_dim,
+                                                     int kh, int vh) {
+  const int t = threadIdx.x % 256;
+  const int64_t b = (int64_t)by * CONV_ROWS + threadIdx.x / 256;
+  const int ch = bx * 1024 + 4 * t;
+  const bool valid = ch < conv_dim && b < B;     // b is uniform per wave
   const int qk_w = kh * KD;
   float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (valid) {
@@ -756,8 +791,7 @@ __global__ __launch_bounds__(256) void fe_conv_kernel(const float *xc_raw, float
     float *hb = hist + b * 3 * (int64_t)conv_dim + ch;
     const f4 h0 = ld4(hb), h1 = ld4(hb + conv_dim), h2 = ld4(hb + 2 * (int64_t)conv_dim);
     const float *w = conv_w + (int64_t)ch * 4;
-    const f4 w0 = ld4(w), w1 = ld4(w + 4), w2 = ld4(w + 8), w3 = ld4(w + 12);
-    const f4 wc[4] = {w0, w1, w2, w3};
+    const f4 wc[4] = {ld4(w), ld4(w + 4), ld4(w + 8), ld4(w + 12)};
     const float hr0[4] = {h0.x, h0.y, h0.z, h0.w};
     const float hr1[4] = {h1.x, h1.y, h1.z, h1.w};
     const float hr2[4] = {h2.x, h2.y, h2.z, h2.w};
@@ -785,15 +819,38 @@ __global__ __launch_bounds__(256) void fe_conv_kernel(const float *xc_raw, float
   const f4 o4 = {out[0], out[1], out[2], out[3]};
   if (ch < 2 * qk_w) {
     const float inv = 1.0f / sqrtf(ss + 1e-6f);
-    if (ch < qk_w) {
-      const float qs = inv * (1.0f / sqrtf((float)KD));
+    if (ch < qk_w)
       st4(q + b * qk_w + ch, (o4 * inv) * (1.0f / sqrtf((float)KD)));
-      (void)qs;
-    } else {
+    else
       st4(k + b * qk_w + (ch - qk_w), o4 * inv);
-    }
   } else {
     st4(v + b * (int64_t)vh * KD + (ch - 2 * qk_w), o4);
+  }
+}
+
+// One launch for the whole front end: the first n_gemv workgroups run the
+// paired GEMV, the rest the conv; the two parts are independent, so their
+// latency-bound and bandwidth-bound phases overlap on the device.
+struct FeArgs {
+  const float *x, *Wa, *Wb, *A_log, *dt_bias, *xc_raw;
+  float *hist;
+  const float *conv_w;
+  float *q, *k, *v, *g, *beta;
+  int B, dim, conv_dim, vh, kh;
+  int gemv_bx, conv_bx;   // x extents of the two parts
+  int n_gemv;             // workgroups of the GEMV part
+};
+
+template <int KD>
+__global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
+  const int id = blockIdx.x;
+  if (id < a.n_gemv) {
+    fe_gemv_block(id % a.gemv_bx, id / a.gemv_bx, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g,
+                  a.beta, a.B, a.dim, a.vh);
+  } else {
+    const int c = id - a.n_gemv;
+    fe_conv_block<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k, a.v,
+                      a.B, a.conv_dim, a.kh, a.vh);
   }
 }
 
@@ -804,16 +861,17 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
                     int dim, int conv_dim, int vh, int kh, int kd,
                     hipStream_t s) {
   if (B <= 0) return 0;
-  dim3 ga((unsigned)((B + FB - 1) / FB), (unsigned)((2 * vh + FR - 1) / FR));
-  hipLaunchKernelGGL(fe_gemv_kernel, ga, dim3(256), 0, s, x, Wa, Wb, A_log, dt_bias, g, beta,
-                     B, dim, vh);
-  dim3 gb((unsigned)((conv_dim + 1023) / 1024), (unsigned)B);
+  FeArgs a{x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta,
+           B, dim, conv_dim, vh, kh, 0, 0, 0};
+  a.gemv_bx = (B + FB - 1) / FB;
+  a.n_gemv = a.gemv_bx * ((2 * vh + FR - 1) / FR);
+  a.conv_bx = (conv_dim + 1023) / 1024;
+  const int n_conv = a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);
+  const dim3 grid((unsigned)(a.n_gemv + n_conv));
   if (kd == 128)
-    hipLaunchKernelGGL(fe_conv_kernel<128>, gb, dim3(256), 0, s, xc_raw, hist, conv_w, q, k, v,
-                       conv_dim, kh, vh);
+    hipLaunchKernelGGL(fe_kernel<128>, grid, dim3(FE_LANES), 0, s, a);
   else
-    hipLaunchKernelGGL(fe_conv_kernel<64>, gb, dim3(256), 0, s, xc_raw, hist, conv_w, q, k, v,
-                       conv_dim, kh, vh);
+    hipLaunchKernelGGL(fe_kernel<64>, grid, dim3(FE_LANES), 0, s, a);
   return (int)hipGetLastError();
 }
 
