@@ -58,7 +58,7 @@ def kernel_hash():
 def recorded_traffic(workload_key, launches_bytes):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"recur_kernel_{workload_key}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"recur_wide_kernel_{workload_key}_counters.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", open(path).read(), flags=re.M)
@@ -161,7 +161,7 @@ def bench_decode(cfg, steps, warmup, cpu):
                    frac_of_copy_floor=round(achieved / floor, 4),
                    algorithmic_bytes_per_launch=int(bytes_launch),
                    bytes_per_head_step=round(bps, 2), head_steps_per_step=hs_per_step,
-                   kernel="recur_kernel", kernel_source_sha256_16=kernel_hash()))
+                   kernel="recur_wide_kernel", kernel_source_sha256_16=kernel_hash()))
     if cpu:
         res["cpu_baseline"] = cpu_baseline_step(S, pool, dims, units=min(N, 256), rows=8)
     return res, dict(workload=cfg["name"], units=N, seqs=cfg["seqs"], layers=cfg["layers"],
