@@ -14,7 +14,7 @@ oracle timed on a bounded sample of the same workload.
 Other --config values time the other workloads: 0 single sequence x 1 layer
 x 64 sequential steps (launch latency), 2 speculative verify (mark + 8-row
 step_m + rollback), 3 front end + step, 4 large batch, 5 large batch at
-kd=vd=64.
+kd=vd=64, 6 speculative verify of one layer with its front end.
 """
 from __future__ import annotations
 
@@ -269,6 +269,47 @@ def bench_frontend(cfg, steps, warmup, cpu):
     return res, dict(workload=cfg["name"], units=B, vh=vh, kd=kd, dim=5120, conv_dim=cd)
 
 
+def bench_verify_frontend(cfg, steps, warmup, cpu):
+    """One layer's speculative verify with its front end: mark(S, hist),
+    front end for M draft rows, M-step recurrence, rollback(S, hist)."""
+    dims = cfg["dims"]
+    vh, kh, kd, vd = dims
+    B, M = cfg["seqs"], cfg["M"]
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    S = synth.state(gen, B, dims, device="cuda")
+    w = synth.frontend_weights(gen, dims, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=M, device="cuda")
+    hist = fe["hist"]
+    slab = gdn.Slab(B, dims, hist_floats_per_unit=3 * cd)
+    rows = dict(q=torch.empty((M, B, kh, kd), device="cuda"),
+                k=torch.empty((M, B, kh, kd), device="cuda"),
+                v=torch.empty((M, B, vh, vd), device="cuda"),
+                g=torch.empty((M, B, vh), device="cuda"),
+                beta=torch.empty((M, B, vh), device="cuda"))
+    o = torch.empty((M, B, vh, vd), device="cuda")
+    rng = np.random.default_rng(cfg["seed"])
+    accs = [rng.integers(0, M + 1, B).astype(np.int32) for _ in range(8)]
+    args = [rows[n] for n in NAMES]
+
+    def one(i):
+        slab.mark(S, hist)
+        gdn.frontend_m(fe["x"], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"], hist,
+                       w["conv_w"], dims, out=rows)
+        gdn.step_m(S, *args, o=o)
+        slab.rollback(S, accs[i % 8], *args, hist=hist, xc_raw=fe["xc_raw"])
+
+    dt = timed(one, steps, warmup)
+    res = dict(value=B * vh * M * steps / dt, ms_per_step=dt / steps * 1e3,
+               roofline=dict(bound="hbm", achieved=None, peak=PEAK_HBM_GBPS, unit="GB/s",
+                             frac=None, traffic=None),
+               extra=dict(value_counts="drafted head-steps per second of the full cycle",
+                          note="403 MB state: 1.6x the MALL, partly cache-resident"))
+    return res, dict(workload=cfg["name"], units=B, M=M, vh=vh, kd=kd, conv_dim=cd,
+                     cycle="gdn_mark(S, hist) + gdn_frontend_m + gdn_step_m + "
+                           "gdn_rollback(S, hist)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,7 +329,8 @@ def main():
     gdn.lib()
     cfg = dict(synth.WORKLOADS[args.config])
     cfg["id"] = args.config
-    runner = {0: bench_latency, 2: bench_verify, 3: bench_frontend}.get(args.config, bench_decode)
+    runner = {0: bench_latency, 2: bench_verify, 3: bench_frontend,
+              6: bench_verify_frontend}.get(args.config, bench_decode)
     res, config = runner(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
     line = dict(metric=METRIC, value=round(res["value"], 1), unit="head-steps/s", n_gpus=1,
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(res["ms_per_step"], 5),

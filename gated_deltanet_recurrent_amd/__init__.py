@@ -27,7 +27,7 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ESTATE, GDN_EDEVICE = 0, -1, -2, -3, -
 
 # Every exported symbol of include/gdn.h.
 EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_slab_bytes", "gdn_slab_init",
-           "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_stream_copy")
+           "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy")
 
 
 class GdnError(RuntimeError):
@@ -67,9 +67,10 @@ def lib():
     L.gdn_mark.argtypes = [C.POINTER(gdn_slab), P, P, P]
     L.gdn_rollback.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I32, I32, P, P]
     L.gdn_frontend.argtypes = [P] * 13 + [I32] * 8 + [P]
+    L.gdn_frontend_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_stream_copy.argtypes = [P, P, I64, P]
     for f in ("gdn_step", "gdn_step_m", "gdn_slab_init", "gdn_mark", "gdn_rollback",
-              "gdn_frontend", "gdn_stream_copy"):
+              "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy"):
         getattr(L, f).restype = C.c_int
     _lib = L
     return L
@@ -197,6 +198,30 @@ def frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None, st
         _dev(conv_w, "conv_w"), _dev(out["q"], "q"), _dev(out["k"], "k"), _dev(out["v"], "v"),
         _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, dim, conv_dim, ck, vh, kh, kd, vd,
         _stream(stream)), "gdn_frontend")
+    return out
+
+
+def frontend_m(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None, stream=None):
+    """Front end for M draft rows (gdn_frontend_m): x [M][B][dim], xc_raw
+    [M][B][conv_dim]; the history advances M frames.  Returns dict q, k, v, g,
+    beta laid out [M][B][...] (the rows gdn_step_m takes)."""
+    vh, kh, kd, vd = dims
+    M, B, dim = x.shape
+    conv_dim = xc_raw.shape[-1]
+    ck = conv_w.shape[-1]
+    dev = x.device
+    if out is None:
+        out = dict(q=torch.empty((M, B, kh, kd), dtype=torch.float32, device=dev),
+                   k=torch.empty((M, B, kh, kd), dtype=torch.float32, device=dev),
+                   v=torch.empty((M, B, vh, vd), dtype=torch.float32, device=dev),
+                   g=torch.empty((M, B, vh), dtype=torch.float32, device=dev),
+                   beta=torch.empty((M, B, vh), dtype=torch.float32, device=dev))
+    _check(lib().gdn_frontend_m(
+        _dev(x, "x"), _dev(Wa, "Wa"), _dev(Wb, "Wb"), _dev(A_log, "A_log"),
+        _dev(dt_bias, "dt_bias"), _dev(xc_raw, "xc_raw"), _dev(hist, "hist"),
+        _dev(conv_w, "conv_w"), _dev(out["q"], "q"), _dev(out["k"], "k"), _dev(out["v"], "v"),
+        _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, M, dim, conv_dim, ck, vh, kh, kd,
+        vd, _stream(stream)), "gdn_frontend_m")
     return out
 
 

@@ -225,34 +225,60 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const fl
   return GDN_OK;
 }
 
+namespace {
+
+int frontend_impl(const float *x, const float *Wa, const float *Wb, const float *A_log,
+                  const float *dt_bias, const float *xc_raw, float *hist, const float *conv_w,
+                  float *q, float *k, float *v, float *g, float *beta, int32_t B, int32_t M,
+                  int32_t dim, int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd,
+                  int32_t vd, void *stream) {
+  int rc = check_dims(vh, kh, kd, vd);
+  if (rc) return rc;
+  if (ck != 4) return GDN_EUNSUPPORTED;
+  if (B < 0 || M < 1 || M > kMaxM || dim <= 0 || dim % 4 != 0 ||
+      conv_dim != 2 * kh * kd + vh * vd)
+    return GDN_EINVAL;
+  if (B == 0) return GDN_OK;
+  if (gdn::frontend_workitems(B, M, conv_dim, vh) > (int64_t)0xFFFFFFFF) return GDN_EUNSUPPORTED;
+  if (!ptr_ok(x) || !ptr_ok(Wa) || !ptr_ok(Wb) || !A_log || !dt_bias || !ptr_ok(xc_raw) ||
+      !ptr_ok(hist) || !ptr_ok(conv_w) || !ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !g || !beta)
+    return GDN_EINVAL;
+  const int64_t rows = (int64_t)M * B;
+  const int64_t hb = (int64_t)B * (ck - 1) * conv_dim * 4;
+  const int64_t rawb = rows * conv_dim * 4, xb = rows * dim * 4;
+  const int64_t qkb = rows * kh * kd * 4, vb = rows * vh * vd * 4, gb = rows * vh * 4;
+  const void *outs[5] = {q, k, v, g, beta};
+  const int64_t ob[5] = {qkb, qkb, vb, gb, gb};
+  for (int i = 0; i < 5; i++) {
+    if (overlaps(outs[i], ob[i], hist, hb) || overlaps(outs[i], ob[i], xc_raw, rawb) ||
+        overlaps(outs[i], ob[i], x, xb))
+      return GDN_EINVAL;
+    for (int j = i + 1; j < 5; j++)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return GDN_EINVAL;
+  }
+  if (overlaps(hist, hb, xc_raw, rawb)) return GDN_EINVAL;
+  return enq(gdn::launch_frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g,
+                                  beta, B, M, dim, conv_dim, vh, kh, kd, (hipStream_t)stream));
+}
+
+}  // namespace
+
 int gdn_frontend(const float *x, const float *Wa, const float *Wb, const float *A_log,
                  const float *dt_bias, const float *xc_raw, float *hist, const float *conv_w,
                  float *q, float *k, float *v, float *g, float *beta, int32_t B, int32_t dim,
                  int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
                  void *stream) {
-  int rc = check_dims(vh, kh, kd, vd);
-  if (rc) return rc;
-  if (ck != 4) return GDN_EUNSUPPORTED;
-  if (B < 0 || dim <= 0 || dim % 4 != 0 || conv_dim != 2 * kh * kd + vh * vd) return GDN_EINVAL;
-  if ((int64_t)B > 65535) return GDN_EUNSUPPORTED;   // grid y limit of the conv kernel
-  if (B == 0) return GDN_OK;
-  if (!ptr_ok(x) || !ptr_ok(Wa) || !ptr_ok(Wb) || !A_log || !dt_bias || !ptr_ok(xc_raw) ||
-      !ptr_ok(hist) || !ptr_ok(conv_w) || !ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !g || !beta)
-    return GDN_EINVAL;
-  const int64_t hb = (int64_t)B * (ck - 1) * conv_dim * 4;
-  const int64_t qkb = (int64_t)B * kh * kd * 4, vb = (int64_t)B * vh * vd * 4, gb = (int64_t)B * vh * 4;
-  const void *outs[5] = {q, k, v, g, beta};
-  const int64_t ob[5] = {qkb, qkb, vb, gb, gb};
-  for (int i = 0; i < 5; i++) {
-    if (overlaps(outs[i], ob[i], hist, hb) || overlaps(outs[i], ob[i], xc_raw, (int64_t)B * conv_dim * 4) ||
-        overlaps(outs[i], ob[i], x, (int64_t)B * dim * 4))
-      return GDN_EINVAL;
-    for (int j = i + 1; j < 5; j++)
-      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return GDN_EINVAL;
-  }
-  if (overlaps(hist, hb, xc_raw, (int64_t)B * conv_dim * 4)) return GDN_EINVAL;
-  return enq(gdn::launch_frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g,
-                                  beta, B, dim, conv_dim, vh, kh, kd, (hipStream_t)stream));
+  return frontend_impl(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta, B, 1,
+                       dim, conv_dim, ck, vh, kh, kd, vd, stream);
+}
+
+int gdn_frontend_m(const float *x, const float *Wa, const float *Wb, const float *A_log,
+                   const float *dt_bias, const float *xc_raw, float *hist, const float *conv_w,
+                   float *q, float *k, float *v, float *g, float *beta, int32_t B, int32_t M,
+                   int32_t dim, int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd,
+                   int32_t vd, void *stream) {
+  return frontend_impl(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta, B, M,
+                       dim, conv_dim, ck, vh, kh, kd, vd, stream);
 }
 
 int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream) {

@@ -47,25 +47,34 @@ static __device__ __forceinline__ f4 splat(float x) { return f4{x, x, x, x}; }
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 // The state stream goes through raw buffer loads/stores so that its cache
-// policy can be set per instruction: loads are non-temporal (nt), stores
-// carry sc0 sc1 nt.  On a 50/50 read/write stream of 64 KiB tiles the store
-// policy measured 1.4% above nt alone.  A buffer resource covers one tile
-// (bounds = its size in bytes), so offsets are 32-bit.
+// policy can be set per instruction.  A state larger than the caches
+// (RESIDENT = false) is streamed with non-temporal loads (nt) and stores
+// carrying sc0 sc1 nt: on a 50/50 read/write stream of 64 KiB tiles that
+// store policy measured 1.4% above nt alone.  A state that fits in half the
+// 256 MiB MALL (RESIDENT = true) keeps the default policy, so that it can
+// stay cached between calls (one unit of 48 heads: 5.9 -> 5.2 us per step).
+// A buffer resource covers one tile (bounds = its size in bytes), so
+// offsets are 32-bit.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int POL_LOAD = 2;                 // nt
-constexpr int POL_STORE = 1 | 2 | 16;       // sc0 | nt | sc1
-constexpr int RSRC_FLAGS = 0x00020000;      // raw 32-bit buffer, gfx9 family
+constexpr int POL_STREAM_LOAD = 2;                 // nt
+constexpr int POL_STREAM_STORE = 1 | 2 | 16;       // sc0 | nt | sc1
+constexpr int RSRC_FLAGS = 0x00020000;             // raw 32-bit buffer, gfx9 family
+constexpr int64_t RESIDENT_MAX_BYTES = 128ll << 20;
 
 static __device__ __forceinline__ rsrc_t buf_rsrc(const float *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes, RSRC_FLAGS);
 }
 // voff: per-lane byte offset (VGPR); soff: wave-uniform byte offset (SGPR),
 // so that one VGPR addresses all of a lane's rows.
+template <bool RESIDENT = false>
 static __device__ __forceinline__ f4 ld_stream(rsrc_t r, int voff, int soff = 0) {
-  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL_LOAD));
+  return __builtin_bit_cast(
+      f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, RESIDENT ? 0 : POL_STREAM_LOAD));
 }
+template <bool RESIDENT = false>
 static __device__ __forceinline__ void st_stream(rsrc_t r, int voff, int soff, f4 x) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), r, voff, soff, POL_STORE);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), r, voff, soff,
+                                         RESIDENT ? 0 : POL_STREAM_STORE);
 }
 static __device__ __forceinline__ f4 ld4(const float *p) {
   return *reinterpret_cast<const f4 *>(p);
@@ -282,7 +291,7 @@ static __device__ __forceinline__ TileIdx tile_index(const RecurArgs &a, int kdk
 // 16-wave workgroups share a CU.
 // The wide geometry serves single-step calls (M < DEEP_MIN_M <= MC), so it
 // stages exactly one chunk and needs no prefetch registers.
-template <int KD>
+template <int KD, bool RESIDENT>
 __global__ __launch_bounds__(Geo<KD>::LANES) __attribute__((amdgpu_waves_per_eu(KD == 128 ? 8 : 6)))
 void recur_wide_kernel(RecurArgs a) {
   constexpr bool MULTI = false;
@@ -309,7 +318,7 @@ void recur_wide_kernel(RecurArgs a) {
 
   f4 s[G::R];
 #pragma unroll
-  for (int j = 0; j < G::R; j++) s[j] = ld_stream(src, lane_off, j * (G::RG * KD * 4));
+  for (int j = 0; j < G::R; j++) s[j] = ld_stream<RESIDENT>(src, lane_off, j * (G::RG * KD * 4));
 
   int buf = 0;
   for (int m0 = 0; m0 < steps; m0 += MC) {
@@ -363,7 +372,7 @@ void recur_wide_kernel(RecurArgs a) {
   }
 
 #pragma unroll
-  for (int j = 0; j < G::R; j++) st_stream(dst, lane_off, j * (G::RG * KD * 4), s[j]);
+  for (int j = 0; j < G::R; j++) st_stream<RESIDENT>(dst, lane_off, j * (G::RG * KD * 4), s[j]);
 
   if (steps > 0) {
     __syncthreads();
@@ -523,7 +532,10 @@ template <int KD>
 static void launch_recur_kd(const RecurArgs &a, int64_t tiles, hipStream_t s) {
   const dim3 grid((unsigned)tiles);
   if (a.M < GDN_DEEP_MIN_M) {
-    hipLaunchKernelGGL(recur_wide_kernel<KD>, grid, dim3(Geo<KD>::LANES), 0, s, a);
+    if (tiles * KD * KD * 4 <= RESIDENT_MAX_BYTES)
+      hipLaunchKernelGGL((recur_wide_kernel<KD, true>), grid, dim3(Geo<KD>::LANES), 0, s, a);
+    else
+      hipLaunchKernelGGL((recur_wide_kernel<KD, false>), grid, dim3(Geo<KD>::LANES), 0, s, a);
   } else {
     if (a.M <= MC)
       hipLaunchKernelGGL((recur_deep_kernel<KD, false>), grid, dim3(Deep<KD>::LANES), 0, s, a);
@@ -798,58 +810,79 @@ static __device__ __forceinline__ void fe_gemv_block(int bx, int by, const float
 // head straddles two blocks.
 // ---------------------------------------------------------------------------
 
-constexpr int CONV_ROWS = FE_LANES / 256;   // batch rows per conv block
+constexpr int CONV_ROWS = FE_LANES / 256;   // units per conv block
 
+// M rows of one unit: the 4-frame window [h0, h1, h2, raw_m] slides across
+// the rows (h0 <- h1, h1 <- h2, h2 <- raw_m), which is what M successive
+// single-row calls do to the history; every row uses the same arithmetic as a
+// single-row call, so the results are bit-identical to M such calls.  The
+// history is written once, after the last row.
 template <int KD>
 static __device__ __forceinline__ void fe_conv_block(int bx, int by, const float *xc_raw,
                                                      float *hist, const float *conv_w, float *q,
-                                                     float *k, float *v, int B, int conv_dim,
-                                                     int kh, int vh) {
+                                                     float *k, float *v, int B, int M,
+                                                     int conv_dim, int kh, int vh) {
   const int t = threadIdx.x % 256;
   const int64_t b = (int64_t)by * CONV_ROWS + threadIdx.x / 256;
   const int ch = bx * 1024 + 4 * t;
   const bool valid = ch < conv_dim && b < B;     // b is uniform per wave
   const int qk_w = kh * KD;
-  float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  f4 h0 = splat(0.0f), h1 = splat(0.0f), h2 = splat(0.0f);
+  f4 wc[4] = {splat(0.0f), splat(0.0f), splat(0.0f), splat(0.0f)};
+  float *hb = hist + b * 3 * (int64_t)conv_dim + ch;
   if (valid) {
-    const f4 raw = ld4(xc_raw + b * conv_dim + ch);
-    float *hb = hist + b * 3 * (int64_t)conv_dim + ch;
-    const f4 h0 = ld4(hb), h1 = ld4(hb + conv_dim), h2 = ld4(hb + 2 * (int64_t)conv_dim);
+    h0 = ld4(hb);
+    h1 = ld4(hb + conv_dim);
+    h2 = ld4(hb + 2 * (int64_t)conv_dim);
     const float *w = conv_w + (int64_t)ch * 4;
-    const f4 wc[4] = {ld4(w), ld4(w + 4), ld4(w + 8), ld4(w + 12)};
-    const float hr0[4] = {h0.x, h0.y, h0.z, h0.w};
-    const float hr1[4] = {h1.x, h1.y, h1.z, h1.w};
-    const float hr2[4] = {h2.x, h2.y, h2.z, h2.w};
-    const float rr[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      float acc = wc[c].x * hr0[c];
-      acc = __builtin_fmaf(wc[c].y, hr1[c], acc);
-      acc = __builtin_fmaf(wc[c].z, hr2[c], acc);
-      acc = __builtin_fmaf(wc[c].w, rr[c], acc);
-      out[c] = acc / (1.0f + expf(-acc));
-    }
-    st4(hb, h1);
-    st4(hb + conv_dim, h2);
-    st4(hb + 2 * (int64_t)conv_dim, raw);
+    for (int c = 0; c < 4; c++) wc[c] = ld4(w + 4 * c);
   }
-  // per key-head sum of squares over KD/4 lanes (every lane takes part)
-  float ss = out[0] * out[0];
-  ss = __builtin_fmaf(out[1], out[1], ss);
-  ss = __builtin_fmaf(out[2], out[2], ss);
-  ss = __builtin_fmaf(out[3], out[3], ss);
+  for (int m = 0; m < M; m++) {
+    const int64_t row = (int64_t)m * B + b;      // [M][B] row
+    float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (valid) {
+      const f4 raw = ld4(xc_raw + row * conv_dim + ch);
+      const float hr0[4] = {h0.x, h0.y, h0.z, h0.w};
+      const float hr1[4] = {h1.x, h1.y, h1.z, h1.w};
+      const float hr2[4] = {h2.x, h2.y, h2.z, h2.w};
+      const float rr[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int off = 1; off < KD / 4; off <<= 1) ss = ss + __shfl_xor(ss, off);
-  if (!valid) return;
-  const f4 o4 = {out[0], out[1], out[2], out[3]};
-  if (ch < 2 * qk_w) {
-    const float inv = 1.0f / sqrtf(ss + 1e-6f);
-    if (ch < qk_w)
-      st4(q + b * qk_w + ch, (o4 * inv) * (1.0f / sqrtf((float)KD)));
-    else
-      st4(k + b * qk_w + (ch - qk_w), o4 * inv);
-  } else {
-    st4(v + b * (int64_t)vh * KD + (ch - 2 * qk_w), o4);
+      for (int c = 0; c < 4; c++) {
+        float acc = wc[c].x * hr0[c];
+        acc = __builtin_fmaf(wc[c].y, hr1[c], acc);
+        acc = __builtin_fmaf(wc[c].z, hr2[c], acc);
+        acc = __builtin_fmaf(wc[c].w, rr[c], acc);
+        out[c] = acc / (1.0f + expf(-acc));
+      }
+      h0 = h1;
+      h1 = h2;
+      h2 = raw;
+    }
+    // per key-head sum of squares over KD/4 lanes (every lane takes part)
+    float ss = out[0] * out[0];
+    ss = __builtin_fmaf(out[1], out[1], ss);
+    ss = __builtin_fmaf(out[2], out[2], ss);
+    ss = __builtin_fmaf(out[3], out[3], ss);
+#pragma unroll
+    for (int off = 1; off < KD / 4; off <<= 1) ss = ss + __shfl_xor(ss, off);
+    if (valid) {
+      const f4 o4 = {out[0], out[1], out[2], out[3]};
+      if (ch < 2 * qk_w) {
+        const float inv = 1.0f / sqrtf(ss + 1e-6f);
+        if (ch < qk_w)
+          st4(q + row * qk_w + ch, (o4 * inv) * (1.0f / sqrtf((float)KD)));
+        else
+          st4(k + row * qk_w + (ch - qk_w), o4 * inv);
+      } else {
+        st4(v + row * (int64_t)vh * KD + (ch - 2 * qk_w), o4);
+      }
+    }
+  }
+  if (valid) {
+    st4(hb, h0);
+    st4(hb + conv_dim, h1);
+    st4(hb + 2 * (int64_t)conv_dim, h2);
   }
 }
 
@@ -861,7 +894,7 @@ struct FeArgs {
   float *hist;
   const float *conv_w;
   float *q, *k, *v, *g, *beta;
-  int B, dim, conv_dim, vh, kh;
+  int B, M, dim, conv_dim, vh, kh;
   int gemv_bx, conv_bx;   // x extents of the two parts
   int n_gemv;             // workgroups of the GEMV part
 };
@@ -870,25 +903,32 @@ template <int KD>
 __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
   const int id = blockIdx.x;
   if (id < a.n_gemv) {
+    // the GEMV rows of all M draft rows are independent: [M][B] = M*B rows
     fe_gemv_block(id % a.gemv_bx, id / a.gemv_bx, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g,
-                  a.beta, a.B, a.dim, a.vh);
+                  a.beta, a.M * a.B, a.dim, a.vh);
   } else {
     const int c = id - a.n_gemv;
     fe_conv_block<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k, a.v,
-                      a.B, a.conv_dim, a.kh, a.vh);
+                      a.B, a.M, a.conv_dim, a.kh, a.vh);
   }
+}
+
+int64_t frontend_workitems(int64_t B, int64_t M, int64_t conv_dim, int64_t vh) {
+  const int64_t n_gemv = ((M * B + FB - 1) / FB) * ((2 * vh + FR - 1) / FR);
+  const int64_t n_conv = ((conv_dim + 1023) / 1024) * ((B + CONV_ROWS - 1) / CONV_ROWS);
+  return (n_gemv + n_conv) * FE_LANES;
 }
 
 int launch_frontend(const float *x, const float *Wa, const float *Wb,
                     const float *A_log, const float *dt_bias,
                     const float *xc_raw, float *hist, const float *conv_w,
-                    float *q, float *k, float *v, float *g, float *beta, int B,
+                    float *q, float *k, float *v, float *g, float *beta, int B, int M,
                     int dim, int conv_dim, int vh, int kh, int kd,
                     hipStream_t s) {
-  if (B <= 0) return 0;
+  if (B <= 0 || M <= 0) return 0;
   FeArgs a{x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta,
-           B, dim, conv_dim, vh, kh, 0, 0, 0};
-  a.gemv_bx = (B + FB - 1) / FB;
+           B, M, dim, conv_dim, vh, kh, 0, 0, 0};
+  a.gemv_bx = (M * B + FB - 1) / FB;
   a.n_gemv = a.gemv_bx * ((2 * vh + FR - 1) / FR);
   a.conv_bx = (conv_dim + 1023) / 1024;
   const int n_conv = a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);

@@ -29,12 +29,17 @@ int launch_hist_replay(float *hist, const float *snap, const float *xc_raw,
                        const int32_t *accepted, int64_t n_units, int conv_dim,
                        int ck, hipStream_t s);
 
-// Front end: paired GEMV + gate/beta, then conv + SiLU + history + split +
-// per key-head norm.
+// Front end for M rows of B units: paired GEMV + gate/beta over all M*B
+// rows, and conv + SiLU + history + split + per key-head norm with the
+// history advancing one frame per row.  x [M][B][dim], xc_raw [M][B][...],
+// outputs [M][B][...].
+// Work-items the front-end launch needs (its grid must stay below 2^32).
+int64_t frontend_workitems(int64_t B, int64_t M, int64_t conv_dim, int64_t vh);
+
 int launch_frontend(const float *x, const float *Wa, const float *Wb,
                     const float *A_log, const float *dt_bias,
                     const float *xc_raw, float *hist, const float *conv_w,
-                    float *q, float *k, float *v, float *g, float *beta, int B,
+                    float *q, float *k, float *v, float *g, float *beta, int B, int M,
                     int dim, int conv_dim, int vh, int kh, int kd,
                     hipStream_t s);
 

@@ -148,6 +148,23 @@ int gdn_frontend(const float *x, const float *Wa, const float *Wb,
                  void *stream);
 
 /*
+ * Front end for M draft rows of B units in one call (speculative verify):
+ * equivalent, bit for bit, to M successive gdn_frontend calls where call m
+ * takes row m of x [M][B][dim] and xc_raw [M][B][conv_dim] and the history
+ * advances one frame per row; outputs q, k [M][B][kh][kd], v [M][B][vh][vd],
+ * g, beta [M][B][vh] are exactly the rows gdn_step_m takes (N = B).
+ * 1 <= M <= 64; other arguments as gdn_frontend.  ("Kestrel_VLLM #34",
+ * section 3.6: the per-row conv/norm/step chain runs serially over the M rows
+ * with the history advancing in place.)
+ */
+int gdn_frontend_m(const float *x, const float *Wa, const float *Wb,
+                   const float *A_log, const float *dt_bias, const float *xc_raw,
+                   float *hist, const float *conv_w, float *q, float *k, float *v,
+                   float *g, float *beta, int32_t B, int32_t M, int32_t dim,
+                   int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd,
+                   int32_t vd, void *stream);
+
+/*
  * Measurement aid: stream n_floats floats from src to dst with the same
  * 128-bit non-temporal access pattern as the state stream (the read+write
  * floor against which the step is read).  src == dst is allowed (read and

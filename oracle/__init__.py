@@ -85,9 +85,10 @@ class Oracle:
         lib.ref_conv_push.argtypes = [P, P, I, I]
         lib.ref_conv_push.restype = None
         lib.ref_gdn_frontend.argtypes = [P] * 13 + [I] * 8
+        lib.ref_gdn_frontend_m.argtypes = [P] * 13 + [I] * 9
         lib.ref64_gdn_step.argtypes = [P] * 7 + [L, I, I, I, I]
-        for f in ("ref_gdn_step", "ref_gdn_step_m", "ref_gdn_mark",
-                  "ref_gdn_rollback", "ref_gdn_frontend", "ref64_gdn_step"):
+        for f in ("ref_gdn_step", "ref_gdn_step_m", "ref_gdn_mark", "ref_gdn_rollback",
+                  "ref_gdn_frontend", "ref_gdn_frontend_m", "ref64_gdn_step"):
             getattr(lib, f).restype = C.c_int
         self.lib = lib
         self.path = path
@@ -129,6 +130,20 @@ class Oracle:
             _f32(v, "v", True), _f32(g, "g", True), _f32(beta, "beta", True),
             B, dim, conv_dim, ck, vh, kh, kd, vd)
         _check(rc, "ref_gdn_frontend")
+
+    def gdn_frontend_m(self, x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w,
+                       q, k, v, g, beta, dims, ck=4):
+        """M draft rows: x [M][B][dim], xc_raw [M][B][conv_dim], outputs [M][B][...]."""
+        vh, kh, kd, vd = dims
+        M, B, dim = x.shape
+        conv_dim = xc_raw.shape[-1]
+        rc = self.lib.ref_gdn_frontend_m(
+            _f32(x, "x"), _f32(Wa, "Wa"), _f32(Wb, "Wb"), _f32(A_log, "A_log"),
+            _f32(dt_bias, "dt_bias"), _f32(xc_raw, "xc_raw"), _f32(hist, "hist", True),
+            _f32(conv_w, "conv_w"), _f32(q, "q", True), _f32(k, "k", True),
+            _f32(v, "v", True), _f32(g, "g", True), _f32(beta, "beta", True),
+            B, M, dim, conv_dim, ck, vh, kh, kd, vd)
+        _check(rc, "ref_gdn_frontend_m")
 
     def gdn_step64(self, S, q, k, v, g, beta, o, dims):
         """Double-precision brute-force step (tiny shapes, kd, vd <= 16)."""

@@ -294,6 +294,30 @@ int ref_gdn_frontend(const float *x, const float *Wa, const float *Wb,
     return 0;
 }
 
+/* "Kestrel_VLLM #34", section 3.6: the M draft rows run the per-row front end
+ * serially, the conv history advancing in place; inputs and outputs are
+ * [M][B][...]. */
+int ref_gdn_frontend_m(const float *x, const float *Wa, const float *Wb,
+                       const float *A_log, const float *dt_bias,
+                       const float *xc_raw, float *hist, const float *conv_w,
+                       float *q, float *k, float *v, float *g, float *beta,
+                       int B, int M, int dim, int conv_dim, int ck,
+                       int vh, int kh, int kd, int vd)
+{
+    if (M < 0 || B < 0)
+        return -1;
+    for (int m = 0; m < M; m++) {
+        const size_t r = (size_t)m * B;
+        int rc = ref_gdn_frontend(x + r * dim, Wa, Wb, A_log, dt_bias, xc_raw + r * conv_dim,
+                                  hist, conv_w, q + r * kh * kd, k + r * kh * kd,
+                                  v + r * vh * vd, g + r * vh, beta + r * vh,
+                                  B, dim, conv_dim, ck, vh, kh, kd, vd);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
 /*
  * Double-precision brute force, re-associated: S' = alpha (I - beta k k^T) S
  * + beta k v^T and o = S'^T q, with the kd x kd matrix P = alpha (I - beta k

@@ -102,6 +102,16 @@ int ref_gdn_frontend(const float *x, const float *Wa, const float *Wb,
                      int B, int dim, int conv_dim, int ck,
                      int vh, int kh, int kd, int vd);
 
+/* M draft rows of the front end: M successive ref_gdn_frontend calls, row m
+ * taking x [M][B][dim] and xc_raw [M][B][conv_dim] row m, the history
+ * advancing once per row; outputs [M][B][...]. */
+int ref_gdn_frontend_m(const float *x, const float *Wa, const float *Wb,
+                       const float *A_log, const float *dt_bias,
+                       const float *xc_raw, float *hist, const float *conv_w,
+                       float *q, float *k, float *v, float *g, float *beta,
+                       int B, int M, int dim, int conv_dim, int ck,
+                       int vh, int kh, int kd, int vd);
+
 /* Double-precision brute force of one step for tiny shapes, in the
  * re-associated matrix form S' = alpha (I - beta k k^T) S + beta k v^T,
  * o = S'^T q, built from explicit kd x kd and kd x vd matrices.  Same

@@ -126,4 +126,6 @@ WORKLOADS = {
             seqs=512, layers=8, dims=DIMS128, steps=50, gate="alpha-uniform", seed=4),
     5: dict(name="large batch kd=vd=64, 512 sequences x 8 layers, 50 steps",
             seqs=512, layers=8, dims=DIMS64, steps=50, gate="alpha-uniform", seed=5),
+    6: dict(name="verify with front end, 128 sequences x 1 layer, M=8 drafts",
+            seqs=128, layers=1, dims=DIMS128, M=8, gate=None, seed=6),
 }

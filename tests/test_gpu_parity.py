@@ -7,6 +7,8 @@ gate's closed form, the conv history, repeated runs.  Large workloads are
 checked on sampled units that the oracle recomputes one by one, in the same
 launch configuration the benchmark times (one launch over all units).
 """
+import ctypes as C
+
 import numpy as np
 import pytest
 import torch
@@ -285,6 +287,93 @@ def test_frontend_parity(orc, dims, B, dim):
         for n in NAMES:
             assert_close(host(out[n]), ref[n], f"{n} t={t}")
         assert bits_equal(host(hist), hist_h)
+
+
+@pytest.mark.parametrize("dims,B,M", [(synth.DIMS128, 5, 3), (synth.DIMS64, 3, 8),
+                                      (synth.DIMS128, 2, 1)])
+def test_frontend_m_bit_exact_and_parity(orc, dims, B, M):
+    """M draft rows in one call == M single-row GPU calls (bit for bit), and
+    the oracle's M-row front end within tolerance (history bit for bit)."""
+    say(f"frontend_m dims={dims} B={B} M={M}")
+    vh, kh, kd, vd = dims
+    gen = synth.make_gen(9, "cuda")
+    w = synth.frontend_weights(gen, dims, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=M, device="cuda")
+    h0 = fe["hist"].clone()
+    hist_m = fe["hist"].clone()
+    out_m = gdn.frontend_m(fe["x"], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"],
+                           hist_m, w["conv_w"], dims)
+    hist_1 = h0.clone()
+    for m in range(M):
+        one = gdn.frontend(fe["x"][m], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"],
+                           fe["xc_raw"][m], hist_1, w["conv_w"], dims)
+        for n in NAMES:
+            assert bits_equal(host(out_m[n][m]), host(one[n])), (n, m)
+    assert bits_equal(host(hist_m), host(hist_1))
+    wh = {n: host(t) for n, t in w.items()}
+    ref = dict(q=np.zeros((M, B, kh, kd), np.float32), k=np.zeros((M, B, kh, kd), np.float32),
+               v=np.zeros((M, B, vh, vd), np.float32), g=np.zeros((M, B, vh), np.float32),
+               beta=np.zeros((M, B, vh), np.float32))
+    h_ref = host(h0)
+    orc.gdn_frontend_m(host(fe["x"]), wh["Wa"], wh["Wb"], wh["A_log"], wh["dt_bias"],
+                       host(fe["xc_raw"]), h_ref, wh["conv_w"], ref["q"], ref["k"], ref["v"],
+                       ref["g"], ref["beta"], dims)
+    for n in NAMES:
+        assert_close(host(out_m[n]), ref[n], f"frontend_m {n}")
+    assert bits_equal(host(hist_m), h_ref)
+
+
+def test_verify_cycle_with_frontend(orc):
+    """mark(S, hist) -> frontend_m -> step_m -> rollback(S, hist): the whole
+    speculative-verify chain of one layer against the oracle's chain."""
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    B, M = 6, 4
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(10, "cuda")
+    S = synth.state(gen, B, dims, device="cuda")
+    w = synth.frontend_weights(gen, dims, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=M, device="cuda")
+    hist = fe["hist"]
+    S_h, hist_h = host(S), host(hist)
+    acc = [0, 1, 4, 2, 3, 4]
+    slab = gdn.Slab(B, dims, hist_floats_per_unit=3 * cd)
+    slab.mark(S, hist)
+    rows = gdn.frontend_m(fe["x"], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"],
+                          hist, w["conv_w"], dims)
+    o = gdn.step_m(S, *(rows[n] for n in NAMES))
+    slab.rollback(S, acc, *(rows[n] for n in NAMES), hist=hist, xc_raw=fe["xc_raw"])
+    # oracle chain
+    wh = {n: host(t) for n, t in w.items()}
+    ref = dict(q=np.zeros((M, B, kh, kd), np.float32), k=np.zeros((M, B, kh, kd), np.float32),
+               v=np.zeros((M, B, vh, vd), np.float32), g=np.zeros((M, B, vh), np.float32),
+               beta=np.zeros((M, B, vh), np.float32))
+    rs = orc.slab(B, dims, hist_floats=3 * cd)
+    rs.mark(S_h, hist_h)
+    orc.gdn_frontend_m(host(fe["x"]), wh["Wa"], wh["Wb"], wh["A_log"], wh["dt_bias"],
+                       host(fe["xc_raw"]), hist_h, wh["conv_w"], ref["q"], ref["k"], ref["v"],
+                       ref["g"], ref["beta"], dims)
+    o_ref = np.zeros((M, B, vh, vd), np.float32)
+    orc.gdn_step_m(S_h, *(ref[n] for n in NAMES), o_ref, M, dims)
+    assert_close(host(o), o_ref, "o verify")
+    rs.rollback(S_h, hist_h, ref, M, np.array(acc, np.int32), xc_raw=host(fe["xc_raw"]),
+                conv_dim=cd, ck=4)
+    assert_close(host(S), S_h, "S after rollback")
+    assert bits_equal(host(hist), hist_h)
+
+
+def test_zero_sized_calls_are_no_ops():
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    e = torch.empty(0, device="cuda")
+    L = gdn.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
+    assert L.gdn_step(P(e), P(e), P(e), P(e), P(e), P(e), P(e), 0, vh, kh, kd, vd,
+                      C.c_void_p(st)) == 0
+    assert L.gdn_frontend(*([P(e)] * 13), 0, 5120, synth.conv_dim_of(dims), 4, vh, kh, kd, vd,
+                          C.c_void_p(st)) == 0
+    torch.cuda.synchronize()
 
 
 def test_stream_copy_ragged():

@@ -454,3 +454,27 @@ def test_oracle_refuses_bad_arguments(orc):
     z = np.zeros(64, np.float32)
     with pytest.raises(ValueError):
         orc.gdn_step(S, z, z, z, z, z, z, dims)
+
+
+def test_frontend_m_rows_equal_single_calls(orc):
+    """The oracle's M-row front end is M single-row calls with the history
+    advancing once per row (row strides of x, xc_raw and every output)."""
+    vh, kh, kd, vd = FE_DIMS
+    r = _rng(53)
+    M, B = 3, 2
+    d = fe_case(r, B)
+    xs = r.normal(size=(M, B, d["x"].shape[1])).astype(np.float32)
+    raws = r.normal(size=(M, B, d["xc_raw"].shape[1])).astype(np.float32)
+    h_m = d["hist"].copy()
+    outs = dict(q=np.zeros((M, B, kh, kd), np.float32), k=np.zeros((M, B, kh, kd), np.float32),
+                v=np.zeros((M, B, vh, vd), np.float32), g=np.zeros((M, B, vh), np.float32),
+                beta=np.zeros((M, B, vh), np.float32))
+    orc.gdn_frontend_m(xs, d["Wa"], d["Wb"], d["A_log"], d["dt_bias"], raws, h_m, d["conv_w"],
+                       outs["q"], outs["k"], outs["v"], outs["g"], outs["beta"], FE_DIMS)
+    for m in range(M):
+        d["x"] = np.ascontiguousarray(xs[m])
+        d["xc_raw"] = np.ascontiguousarray(raws[m])
+        one = run_fe(orc, d)
+        for n in ("q", "k", "v", "g", "beta"):
+            assert bits_equal(outs[n][m], one[n]), (n, m)
+    assert bits_equal(h_m, d["hist"])
