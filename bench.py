@@ -189,10 +189,21 @@ def bench_latency(cfg, steps, warmup, cpu):
     dt = timed(one, steps, warmup)
     launch_s = dt / (steps * T)
     achieved = head_step_bytes(dims) * vh / launch_s / 1e9
+    # the same T-step chain captured once as a HIP graph and replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one(0)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one(0)
+    dt_g = timed(lambda i: graph.replay(), steps, warmup)
     res = dict(value=vh * T * steps / dt, ms_per_step=dt / steps * 1e3,
                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
                              unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
                extra=dict(us_per_call=round(launch_s * 1e6, 3),
+                          us_per_step_graph_replay=round(dt_g / (steps * T) * 1e6, 3),
                           note="3 MiB state stays in L2/MALL: latency figure, not an HBM claim"))
     if cpu:
         res["cpu_baseline"] = cpu_baseline_step(S, [{n: inp[n][m:m + 1] for n in NAMES}
