@@ -14,7 +14,8 @@ oracle timed on a bounded sample of the same workload.
 Other --config values time the other workloads: 0 single sequence x 1 layer
 x 64 sequential steps (launch latency), 2 speculative verify (mark + 8-row
 step_m + rollback), 3 front end + step, 4 large batch, 5 large batch at
-kd=vd=64, 6 speculative verify of one layer with its front end.
+kd=vd=64, 6 speculative verify of one layer with its front end, 7 the
+batched decode of workload 1 with the gated RMSNorm fused on the output.
 """
 from __future__ import annotations
 
@@ -137,21 +138,31 @@ def bench_decode(cfg, steps, warmup, cpu):
     S = synth.state(gen, N, dims, device="cuda")
     pool = [synth.step_inputs(gen, N, dims, M=1, gate=cfg["gate"], device="cuda")
             for _ in range(4)]
+    gated = cfg.get("gated", False)
+    if gated:
+        for x in pool:
+            x["z"] = torch.randn((1, N, vh, dims[3]), generator=gen, device="cuda")
+        norm_w = 1.0 + 0.1 * torch.randn((dims[3],), generator=gen, device="cuda")
     o = torch.empty((N, vh, dims[3]), device="cuda")
     torch.cuda.synchronize()
 
     def one(i):
         x = pool[i % 4]
-        gdn.step(S, x["q"][0], x["k"][0], x["v"][0], x["g"][0], x["beta"][0], o=o)
+        if gated:
+            gdn.step_gated(S, x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], norm_w, 1e-6,
+                           out=o.view(1, N, vh, dims[3]))
+        else:
+            gdn.step(S, x["q"][0], x["k"][0], x["v"][0], x["g"][0], x["beta"][0], o=o)
 
     dt = timed(one, steps, warmup)
     hs_per_step = N * vh
-    bps = head_step_bytes(dims)
+    bps = head_step_bytes(dims) + (dims[3] * 4 if gated else 0)   # + the gate z
     launch_s = dt / steps
     bytes_launch = hs_per_step * bps
     achieved = bytes_launch / launch_s / 1e9
     floor = copy_floor(S)
-    key = {1: "b64x48", 4: "b512x8", 5: "b512x8_kd64"}.get(cfg["id"], f"cfg{cfg['id']}")
+    key = {1: "b64x48", 4: "b512x8", 5: "b512x8_kd64", 7: "b64x48_gated"}.get(
+        cfg["id"], f"cfg{cfg['id']}")
     traffic = recorded_traffic(key, bytes_launch)
     res = dict(
         value=hs_per_step * steps / dt, ms_per_step=launch_s * 1e3,

@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(_PKG, "libgdn_mi355x.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ESTATE, GDN_EDEVICE = 0, -1, -2, -3, -4
 
 # Every exported symbol of include/gdn.h.
-EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_slab_bytes", "gdn_slab_init",
+EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_bytes",
+           "gdn_slab_init",
            "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy")
 
 
@@ -61,6 +62,7 @@ def lib():
     L.gdn_strerror.restype = C.c_char_p
     L.gdn_step.argtypes = [P] * 7 + [I64, I32, I32, I32, I32, P]
     L.gdn_step_m.argtypes = [P] * 7 + [I64, I32, I32, I32, I32, I32, P]
+    L.gdn_step_gated.argtypes = [P] * 8 + [C.c_float, P, I64, I32, I32, I32, I32, I32, P]
     L.gdn_slab_bytes.argtypes = [I64, I32, I32, I32, I32, I64]
     L.gdn_slab_bytes.restype = I64
     L.gdn_slab_init.argtypes = [C.POINTER(gdn_slab), P, I64, I64, I32, I32, I32, I32, I64]
@@ -69,7 +71,7 @@ def lib():
     L.gdn_frontend.argtypes = [P] * 13 + [I32] * 8 + [P]
     L.gdn_frontend_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_stream_copy.argtypes = [P, P, I64, P]
-    for f in ("gdn_step", "gdn_step_m", "gdn_slab_init", "gdn_mark", "gdn_rollback",
+    for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark", "gdn_rollback",
               "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy"):
         getattr(L, f).restype = C.c_int
     _lib = L
@@ -132,6 +134,21 @@ def step_m(S, q, k, v, g, beta, o=None, stream=None):
                             _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"), N, M, vh, kh,
                             kd, vd, _stream(stream)), "gdn_step_m")
     return o
+
+
+def step_gated(S, q, k, v, g, beta, z, norm_w, eps=1e-6, out=None, stream=None):
+    """M steps with the gated RMSNorm fused on the output (gdn_step_gated).
+    q, k [M][N][kh][kd]; v, z [M][N][vh][vd]; g, beta [M][N][vh]; norm_w
+    [vd].  Returns out [M][N][vh][vd]."""
+    N, vh, kh, kd, vd = _state_dims(S, q, v)
+    M = q.shape[0]
+    if out is None:
+        out = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
+    _check(lib().gdn_step_gated(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                _dev(g, "g"), _dev(beta, "beta"), _dev(z, "z"),
+                                _dev(norm_w, "norm_w"), float(eps), _dev(out, "out"), N, M, vh,
+                                kh, kd, vd, _stream(stream)), "gdn_step_gated")
+    return out
 
 
 def slab_bytes(n_units, dims, hist_floats_per_unit=0):

@@ -185,6 +185,9 @@ struct RecurArgs {
   const float *q, *k, *v, *g, *beta;
   float *o;              // nullable: rollback writes no output
   const int32_t *steps;  // nullable: per-unit step counts
+  const float *z;        // gated output only: gate z [rows][N][vh][vd]
+  const float *norm_w;   // gated output only: RMSNorm weight [vd]
+  float eps;             // gated output only
   int64_t n_units;
   int vh, kh, M;
 };
@@ -196,28 +199,30 @@ struct RecurArgs {
 // chunk while the current one runs (double-buffered stage).
 constexpr int MC = 8;
 
-template <int KD>
+template <int KD, bool GATED>
 struct Stage {
   float q[MC][KD];
   float k[MC][KD];
   float v[MC][KD];
+  float z[GATED ? MC : 1][GATED ? KD : 1];   // gate of the fused RMSNorm
   float alpha[MC];       // exp(g)
   float beta[MC];
 };
 
-template <int KD, int LANES>
+template <int KD, int LANES, bool GATED>
 struct ChunkRegs {
   static constexpr int E = MC * KD;                   // floats of q (or k, v) per chunk
   static constexpr int P = (E + LANES - 1) / LANES;   // per lane
   float q[P], k[P], v[P];
+  float z[GATED ? P : 1];
   float gb;  // g (lanes < MC) or beta (lanes MC .. 2*MC-1)
 };
 
-template <int KD, int LANES>
-static __device__ __forceinline__ void chunk_load(ChunkRegs<KD, LANES> &c, const RecurArgs &a,
-                                                  int t, int64_t unit, int head, int hh, int m0,
-                                                  int nr) {
-  using C = ChunkRegs<KD, LANES>;
+template <int KD, int LANES, bool GATED>
+static __device__ __forceinline__ void chunk_load(ChunkRegs<KD, LANES, GATED> &c,
+                                                  const RecurArgs &a, int t, int64_t unit,
+                                                  int head, int hh, int m0, int nr) {
+  using C = ChunkRegs<KD, LANES, GATED>;
 #pragma unroll
   for (int i = 0; i < C::P; i++) {
     const int e = t + i * LANES;
@@ -227,6 +232,7 @@ static __device__ __forceinline__ void chunk_load(ChunkRegs<KD, LANES> &c, const
       c.q[i] = a.q[(urow * a.kh + hh) * KD + col];
       c.k[i] = a.k[(urow * a.kh + hh) * KD + col];
       c.v[i] = a.v[(urow * a.vh + head) * KD + col];
+      if constexpr (GATED) c.z[i] = a.z[(urow * a.vh + head) * KD + col];
     }
   }
   if (t < 2 * MC) {
@@ -238,10 +244,11 @@ static __device__ __forceinline__ void chunk_load(ChunkRegs<KD, LANES> &c, const
   }
 }
 
-template <int KD, int LANES>
-static __device__ __forceinline__ void chunk_store(Stage<KD> &st, const ChunkRegs<KD, LANES> &c,
-                                                   int t, int nr) {
-  using C = ChunkRegs<KD, LANES>;
+template <int KD, int LANES, bool GATED>
+static __device__ __forceinline__ void chunk_store(Stage<KD, GATED> &st,
+                                                   const ChunkRegs<KD, LANES, GATED> &c, int t,
+                                                   int nr) {
+  using C = ChunkRegs<KD, LANES, GATED>;
   constexpr int RG = Canon<KD>::RG;
 #pragma unroll
   for (int i = 0; i < C::P; i++) {
@@ -252,6 +259,7 @@ static __device__ __forceinline__ void chunk_store(Stage<KD> &st, const ChunkReg
       st.q[r][pc] = c.q[i];
       st.k[r][pc] = c.k[i];
       st.v[r][col] = c.v[i];
+      if constexpr (GATED) st.z[r][col] = c.z[i];
     }
   }
   if (t < 2 * MC && t % MC < nr) {
@@ -264,6 +272,36 @@ static __device__ __forceinline__ void chunk_store(Stage<KD> &st, const ChunkReg
 
 static __device__ __forceinline__ f4 lds4(const float *p) {
   return *reinterpret_cast<const f4 *>(p);
+}
+
+// Writes one head's output for columns 4*cg .. 4*cg+3.  Called by every lane
+// of a wave whose lane groups of CG lanes all hold the full output row (the
+// fold below reduces across the CG lanes of a group); lanes with `write` set
+// store.  GATED applies the gated RMSNorm of the layer's output step
+// ("Kestrel_VLLM #24", Fig. 1 caption, step 6; the pages give no formula, the
+// model family's definition is used): out = (o * 1/sqrt(mean(o^2) + eps)) *
+// w * silu(z), per value head over its vd outputs.
+template <int KD, bool GATED>
+static __device__ __forceinline__ void emit_o(const RecurArgs &a, int64_t urow, int head, int cg,
+                                              bool write, f4 ov, const float *zrow) {
+  if constexpr (GATED) {
+    const f4 wn = ld4(a.norm_w + 4 * cg);   // 512 B shared by all tiles: an L2 hit
+    float ss = ov.x * ov.x;
+    ss = __builtin_fmaf(ov.y, ov.y, ss);
+    ss = __builtin_fmaf(ov.z, ov.z, ss);
+    ss = __builtin_fmaf(ov.w, ov.w, ss);
+#pragma unroll
+    for (int off = 1; off < Canon<KD>::CG; off <<= 1) ss = ss + __shfl_xor(ss, off);
+    const float rinv = 1.0f / sqrtf(ss / (float)KD + a.eps);
+    const f4 z = lds4(zrow + 4 * cg);
+    f4 sz;
+    sz.x = z.x / (1.0f + expf(-z.x));
+    sz.y = z.y / (1.0f + expf(-z.y));
+    sz.z = z.z / (1.0f + expf(-z.z));
+    sz.w = z.w / (1.0f + expf(-z.w));
+    ov = ((ov * rinv) * wn) * sz;
+  }
+  if (write) st4(a.o + (urow * a.vh + head) * KD + 4 * cg, ov);
 }
 
 struct TileIdx {
@@ -284,20 +322,17 @@ static __device__ __forceinline__ TileIdx tile_index(const RecurArgs &a, int kdk
 
 // ----- wide geometry -------------------------------------------------------
 //
-// Per step: decay and S^T k partials; barrier; wave 0 finishes S^T k, forms
-// tmp = (v - kv) beta and finishes the previous step's output; barrier;
-// rank-1 update and S^T q partials.  The output of the last step is finished
-// after the loop.  kd = 128: at most 64 VGPRs (8 waves per SIMD), so two
-// 16-wave workgroups share a CU.
-// The wide geometry serves single-step calls (M < DEEP_MIN_M <= MC), so it
-// stages exactly one chunk and needs no prefetch registers.
-template <int KD, bool RESIDENT>
+// Serves single-step calls (M = 1; rollback with M = 1 runs 0 or 1 step per
+// unit).  Decay and S^T k partials; barrier; wave 0 finishes S^T k and forms
+// tmp = (v - kv) beta; barrier; rank-1 update and S^T q partials; barrier;
+// wave 0 finishes the output.  kd = 128: at most 64 VGPRs (8 waves per SIMD),
+// so two 16-wave workgroups share a CU.
+template <int KD, bool RESIDENT, bool GATED>
 __global__ __launch_bounds__(Geo<KD>::LANES) __attribute__((amdgpu_waves_per_eu(KD == 128 ? 8 : 6)))
 void recur_wide_kernel(RecurArgs a) {
-  constexpr bool MULTI = false;
   using G = Geo<KD>;
   constexpr int LANES = G::LANES;
-  __shared__ Stage<KD> st[MULTI ? 2 : 1];
+  __shared__ Stage<KD, GATED> sb;
   __shared__ f4 s_red_k[G::NW][G::CG];
   __shared__ f4 s_red_o[G::NW][G::CG];
   __shared__ f4 s_tmp[G::CG];
@@ -306,82 +341,62 @@ void recur_wide_kernel(RecurArgs a) {
   const int lane = t & 63, wave = t >> 6;
   const int cg = t % G::CG, rg = t / G::CG;
   const TileIdx ti = tile_index(a, KD * KD);
-  const int steps = ti.steps;
+  const bool run = ti.steps > 0;       // uniform per workgroup
   const rsrc_t src = buf_rsrc(a.S_src + ti.tile_off, KD * KD * 4);
   const rsrc_t dst = buf_rsrc(a.S_dst + ti.tile_off, KD * KD * 4);
   const int lane_off = (rg * KD + 4 * cg) * 4;
 
-  // the first chunk of inputs is requested before the state, so that its
-  // latency hides under the state stream
-  ChunkRegs<KD, LANES> cr;
-  if (steps > 0) chunk_load<KD, LANES>(cr, a, t, ti.unit, ti.head, ti.hh, 0, steps < MC ? steps : MC);
+  // the inputs are requested before the state, so that their latency hides
+  // under the state stream
+  ChunkRegs<KD, LANES, GATED> cr;
+  if (run) chunk_load<KD, LANES, GATED>(cr, a, t, ti.unit, ti.head, ti.hh, 0, 1);
 
   f4 s[G::R];
 #pragma unroll
   for (int j = 0; j < G::R; j++) s[j] = ld_stream<RESIDENT>(src, lane_off, j * (G::RG * KD * 4));
 
-  int buf = 0;
-  for (int m0 = 0; m0 < steps; m0 += MC) {
-    const int nr = steps - m0 < MC ? steps - m0 : MC;
-    Stage<KD> &sb = st[MULTI ? buf : 0];
-    chunk_store<KD, LANES>(sb, cr, t, nr);
+  if (run) {
+    chunk_store<KD, LANES, GATED>(sb, cr, t, 1);
     __syncthreads();
-    if (MULTI && m0 + MC < steps) {
-      const int nn = steps - m0 - MC;
-      chunk_load<KD, LANES>(cr, a, t, ti.unit, ti.head, ti.hh, m0 + MC, nn < MC ? nn : MC);
-    }
-    for (int r = 0; r < nr; r++) {
-      const int m = m0 + r;
-      const float alpha = sb.alpha[r];
-      const f4 kk = lds4(&sb.k[r][rg * 4]);
-      // decay, then S^T k over the decayed state
-      f4 p = splat(0.0f);
+    const float alpha = sb.alpha[0];
+    const f4 kk = lds4(&sb.k[0][rg * 4]);
+    // decay, then S^T k over the decayed state
+    f4 p = splat(0.0f);
 #pragma unroll
-      for (int j = 0; j < G::R; j++) {
-        s[j] = s[j] * alpha;
-        p = fma4(s[j], splat(kk[j]), p);
-      }
-      p = wave_fold<KD>(p);
-      if (lane < G::CG) s_red_k[wave][lane] = p;
-      __syncthreads();
-      if (wave == 0) {
-        const f4 kv = tile_sum<KD>(s_red_k, lane);
-        if (lane < G::CG) s_tmp[lane] = (lds4(&sb.v[r][4 * lane]) - kv) * sb.beta[r];
-        if (m > 0) {
-          const f4 ov = tile_sum<KD>(s_red_o, lane);
-          if (a.o != nullptr && lane < G::CG) {
-            const int64_t urow = (int64_t)(m - 1) * a.n_units + ti.unit;
-            st4(a.o + (urow * a.vh + ti.head) * KD + 4 * lane, ov);
-          }
-        }
-      }
-      __syncthreads();
-      const f4 tmp = s_tmp[cg];
-      const f4 qq = lds4(&sb.q[r][rg * 4]);
-      // rank-1 update, then S^T q with the updated state
-      p = splat(0.0f);
-#pragma unroll
-      for (int j = 0; j < G::R; j++) {
-        s[j] = fma4(splat(kk[j]), tmp, s[j]);
-        p = fma4(s[j], splat(qq[j]), p);
-      }
-      p = wave_fold<KD>(p);
-      if (lane < G::CG) s_red_o[wave][lane] = p;
+    for (int j = 0; j < G::R; j++) {
+      s[j] = s[j] * alpha;
+      p = fma4(s[j], splat(kk[j]), p);
     }
-    buf ^= 1;
+    p = wave_fold<KD>(p);
+    if (lane < G::CG) s_red_k[wave][lane] = p;
+    __syncthreads();
+    if (wave == 0) {
+      const f4 kv = tile_sum<KD>(s_red_k, lane);
+      if (lane < G::CG) s_tmp[lane] = (lds4(&sb.v[0][4 * lane]) - kv) * sb.beta[0];
+    }
+    __syncthreads();
+    const f4 tmp = s_tmp[cg];
+    const f4 qq = lds4(&sb.q[0][rg * 4]);
+    // rank-1 update, then S^T q with the updated state
+    p = splat(0.0f);
+#pragma unroll
+    for (int j = 0; j < G::R; j++) {
+      s[j] = fma4(splat(kk[j]), tmp, s[j]);
+      p = fma4(s[j], splat(qq[j]), p);
+    }
+    p = wave_fold<KD>(p);
+    if (lane < G::CG) s_red_o[wave][lane] = p;
   }
 
 #pragma unroll
   for (int j = 0; j < G::R; j++) st_stream<RESIDENT>(dst, lane_off, j * (G::RG * KD * 4), s[j]);
 
-  if (steps > 0) {
+  if (run) {
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 0 && a.o != nullptr) {
       const f4 ov = tile_sum<KD>(s_red_o, lane);
-      if (a.o != nullptr && lane < G::CG) {
-        const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
-        st4(a.o + (urow * a.vh + ti.head) * KD + 4 * lane, ov);
-      }
+      emit_o<KD, GATED>(a, ti.unit, ti.head, lane % G::CG, lane < G::CG, ov,
+                        &sb.z[0][0]);
     }
   }
 }
@@ -402,12 +417,12 @@ static __device__ __forceinline__ void deep_partials(const f4 (&p)[4], f4 &w0, f
   }
 }
 
-template <int KD, bool MULTI>
+template <int KD, bool MULTI, bool GATED>
 __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a) {
   using D = Deep<KD>;
   constexpr int LANES = D::LANES, RG = Canon<KD>::RG, CG = D::CG;
   constexpr bool XWAVE = KD == 128;             // partials cross waves
-  __shared__ Stage<KD> st[MULTI ? 2 : 1];
+  __shared__ Stage<KD, GATED> st[MULTI ? 2 : 1];
   __shared__ f4 s_red_k[XWAVE ? Canon<KD>::NWP : 1][CG];
   __shared__ f4 s_red_o[XWAVE ? Canon<KD>::NWP : 1][CG];
   __shared__ f4 s_tmp[CG];
@@ -422,8 +437,9 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
   const rsrc_t dst = buf_rsrc(a.S_dst + ti.tile_off, KD * KD * 4);
   const int lane_off = ((4 * L) * KD + 4 * cg) * 4;
 
-  ChunkRegs<KD, LANES> cr;
-  if (steps > 0) chunk_load<KD, LANES>(cr, a, t, ti.unit, ti.head, ti.hh, 0, steps < MC ? steps : MC);
+  ChunkRegs<KD, LANES, GATED> cr;
+  if (steps > 0) chunk_load<KD, LANES, GATED>(cr, a, t, ti.unit, ti.head, ti.hh, 0, steps < MC ? steps : MC);
+  const float *zprev = nullptr;
 
   f4 s[4][4];
 #pragma unroll
@@ -434,12 +450,12 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
   int buf = 0;
   for (int m0 = 0; m0 < steps; m0 += MC) {
     const int nr = steps - m0 < MC ? steps - m0 : MC;
-    Stage<KD> &sb = st[MULTI ? buf : 0];
-    chunk_store<KD, LANES>(sb, cr, t, nr);
+    Stage<KD, GATED> &sb = st[MULTI ? buf : 0];
+    chunk_store<KD, LANES, GATED>(sb, cr, t, nr);
     __syncthreads();
     if (MULTI && m0 + MC < steps) {
       const int nn = steps - m0 - MC;
-      chunk_load<KD, LANES>(cr, a, t, ti.unit, ti.head, ti.hh, m0 + MC, nn < MC ? nn : MC);
+      chunk_load<KD, LANES, GATED>(cr, a, t, ti.unit, ti.head, ti.hh, m0 + MC, nn < MC ? nn : MC);
     }
     for (int r = 0; r < nr; r++) {
       const int m = m0 + r;
@@ -465,12 +481,10 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
         if (wave == 0) {
           const f4 kv = tile_sum<KD>(s_red_k, lane);
           if (lane < CG) s_tmp[lane] = (lds4(&sb.v[r][4 * lane]) - kv) * sb.beta[r];
-          if (m > 0) {
+          if (m > 0 && a.o != nullptr) {
             const f4 ov = tile_sum<KD>(s_red_o, lane);
-            if (a.o != nullptr && lane < CG) {
-              const int64_t prow = (int64_t)(m - 1) * a.n_units + ti.unit;
-              st4(a.o + (prow * a.vh + ti.head) * KD + 4 * lane, ov);
-            }
+            const int64_t prow = (int64_t)(m - 1) * a.n_units + ti.unit;
+            emit_o<KD, GATED>(a, prow, ti.head, lane % CG, lane < CG, ov, zprev);
           }
         }
         __syncthreads();
@@ -495,10 +509,11 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
       if (XWAVE) {
         s_red_o[2 * L][cg] = w0;
         s_red_o[2 * L + 1][cg] = w1;
-      } else {
+      } else if (a.o != nullptr) {
         const f4 ov = wave_fold<KD>(w0);
-        if (a.o != nullptr && L == 0) st4(a.o + (urow * a.vh + ti.head) * KD + 4 * cg, ov);
+        emit_o<KD, GATED>(a, urow, ti.head, cg, L == 0, ov, &sb.z[GATED ? r : 0][0]);
       }
+      if constexpr (GATED) zprev = &sb.z[r][0];
     }
     buf ^= 1;
   }
@@ -510,51 +525,55 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
 
   if (XWAVE && steps > 0) {
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 0 && a.o != nullptr) {
       const f4 ov = tile_sum<KD>(s_red_o, lane);
-      if (a.o != nullptr && lane < CG) {
-        const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
-        st4(a.o + (urow * a.vh + ti.head) * KD + 4 * lane, ov);
-      }
+      const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
+      emit_o<KD, GATED>(a, urow, ti.head, lane % CG, lane < CG, ov, zprev);
     }
   }
 }
 
-// Calls with M >= DEEP_MIN_M rows per unit run the deep geometry.
-#ifndef GDN_DEEP_MIN_M
-#define GDN_DEEP_MIN_M 2
-#endif
-static_assert(GDN_DEEP_MIN_M >= 2 && GDN_DEEP_MIN_M <= MC + 1, "wide kernel stages one chunk");
+// Calls with M >= 2 rows per unit run the deep geometry; single steps the
+// wide one.
 
 int recur_lanes(int kd) { return kd == 128 ? Geo<128>::LANES : Geo<64>::LANES; }
 
-template <int KD>
+template <int KD, bool GATED>
 static void launch_recur_kd(const RecurArgs &a, int64_t tiles, hipStream_t s) {
   const dim3 grid((unsigned)tiles);
-  if (a.M < GDN_DEEP_MIN_M) {
+  if (a.M == 1) {
     if (tiles * KD * KD * 4 <= RESIDENT_MAX_BYTES)
-      hipLaunchKernelGGL((recur_wide_kernel<KD, true>), grid, dim3(Geo<KD>::LANES), 0, s, a);
+      hipLaunchKernelGGL((recur_wide_kernel<KD, true, GATED>), grid, dim3(Geo<KD>::LANES), 0, s, a);
     else
-      hipLaunchKernelGGL((recur_wide_kernel<KD, false>), grid, dim3(Geo<KD>::LANES), 0, s, a);
+      hipLaunchKernelGGL((recur_wide_kernel<KD, false, GATED>), grid, dim3(Geo<KD>::LANES), 0, s, a);
   } else {
     if (a.M <= MC)
-      hipLaunchKernelGGL((recur_deep_kernel<KD, false>), grid, dim3(Deep<KD>::LANES), 0, s, a);
+      hipLaunchKernelGGL((recur_deep_kernel<KD, false, GATED>), grid, dim3(Deep<KD>::LANES), 0, s, a);
     else
-      hipLaunchKernelGGL((recur_deep_kernel<KD, true>), grid, dim3(Deep<KD>::LANES), 0, s, a);
+      hipLaunchKernelGGL((recur_deep_kernel<KD, true, GATED>), grid, dim3(Deep<KD>::LANES), 0, s, a);
   }
 }
 
 int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *k, const float *v, const float *g,
                  const float *beta, float *o, const int32_t *steps,
-                 int64_t n_units, int vh, int kh, int M, hipStream_t s) {
-  RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, n_units, vh, kh, M};
+                 int64_t n_units, int vh, int kh, int M, hipStream_t s,
+                 const float *z, const float *norm_w, float eps) {
+  RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, z, norm_w, eps, n_units, vh, kh, M};
   const int64_t tiles = n_units * vh;
   if (tiles <= 0) return 0;
-  if (kd == 128)
-    launch_recur_kd<128>(a, tiles, s);
-  else
-    launch_recur_kd<64>(a, tiles, s);
+  const bool gated = z != nullptr;
+  if (kd == 128) {
+    if (gated)
+      launch_recur_kd<128, true>(a, tiles, s);
+    else
+      launch_recur_kd<128, false>(a, tiles, s);
+  } else {
+    if (gated)
+      launch_recur_kd<64, true>(a, tiles, s);
+    else
+      launch_recur_kd<64, false>(a, tiles, s);
+  }
   return (int)hipGetLastError();
 }
 

@@ -72,6 +72,23 @@ int gdn_step_m(float *S, const float *q, const float *k, const float *v,
                void *stream);
 
 /*
+ * M sequential steps (1 <= M <= 64; M = 1 is a single step) whose output goes
+ * through the layer's gated RMSNorm in the same launch, so the raw read-out
+ * never reaches memory ("Kestrel_VLLM #24", Fig. 1 caption, step 6: gated
+ * RMSNorm after the recurrence, one group per value head; the pages give no
+ * formula, this is the model family's definition):
+ *   out[m][u][i][:] = (o / sqrt(mean(o^2) + eps)) * norm_w * silu(z[m][u][i][:])
+ * with o = S'^T q of that step and silu(z) = z / (1 + exp(-z)).
+ * z, out [M][N][vh][vd]; norm_w [vd]; 0 <= eps <= 1.  S advances exactly as
+ * in gdn_step_m (same bits).
+ */
+int gdn_step_gated(float *S, const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, const float *z,
+                   const float *norm_w, float eps, float *out, int64_t n_units,
+                   int32_t M, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+                   void *stream);
+
+/*
  * Snapshot slab for mark / rollback ("Kestrel_VLLM #34", section 3.7: the
  * recurrent state and the conv history can only be restored from a copy; the
  * snapshot is one-shot).  The struct lives in caller host memory; `dev`

@@ -87,6 +87,8 @@ class Oracle:
         lib.ref_gdn_frontend.argtypes = [P] * 13 + [I] * 8
         lib.ref_gdn_frontend_m.argtypes = [P] * 13 + [I] * 9
         lib.ref64_gdn_step.argtypes = [P] * 7 + [L, I, I, I, I]
+        lib.ref_gdn_gated_norm.argtypes = [P, P, P, C.c_float, P, L, I]
+        lib.ref_gdn_gated_norm.restype = C.c_int
         for f in ("ref_gdn_step", "ref_gdn_step_m", "ref_gdn_mark", "ref_gdn_rollback",
                   "ref_gdn_frontend", "ref_gdn_frontend_m", "ref64_gdn_step"):
             getattr(lib, f).restype = C.c_int
@@ -144,6 +146,14 @@ class Oracle:
             _f32(v, "v", True), _f32(g, "g", True), _f32(beta, "beta", True),
             B, M, dim, conv_dim, ck, vh, kh, kd, vd)
         _check(rc, "ref_gdn_frontend_m")
+
+    def gated_norm(self, o, z, w, eps, out):
+        """Gated RMSNorm over the last axis (vd) of o, z -> out."""
+        vd = o.shape[-1]
+        rows = o.size // vd
+        rc = self.lib.ref_gdn_gated_norm(_f32(o, "o"), _f32(z, "z"), _f32(w, "w"), float(eps),
+                                         _f32(out, "out", True), rows, vd)
+        _check(rc, "ref_gdn_gated_norm")
 
     def gdn_step64(self, S, q, k, v, g, beta, o, dims):
         """Double-precision brute-force step (tiny shapes, kd, vd <= 16)."""

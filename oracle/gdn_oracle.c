@@ -318,6 +318,34 @@ int ref_gdn_frontend_m(const float *x, const float *Wa, const float *Wb,
     return 0;
 }
 
+/* Gated RMSNorm of the layer output ("Kestrel_VLLM #24", Fig. 1 caption,
+ * step 6, after the recurrence; one group per value head; no formula on the
+ * pages, the model family's definition is used): per row of vd outputs,
+ * ms = (sum o^2) / vd, r = 1/sqrt(ms + eps),
+ * out = ((o * r) * w) * silu(z), silu(z) = z / (1 + exp(-z)). */
+int ref_gdn_gated_norm(const float *o, const float *z, const float *w, float eps,
+                       float *out, int64_t rows, int vd)
+{
+    if (rows < 0 || vd <= 0 || !(eps >= 0.0f))
+        return -1;
+    if (rows == 0)
+        return 0;
+    if (!o || !z || !w || !out)
+        return -1;
+    for (int64_t r = 0; r < rows; r++) {
+        const float *orow = o + (size_t)r * vd, *zrow = z + (size_t)r * vd;
+        float ss = 0.0f;
+        for (int c = 0; c < vd; c++)
+            ss = ss + orow[c] * orow[c];
+        const float rinv = 1.0f / sqrtf(ss / (float)vd + eps);
+        for (int c = 0; c < vd; c++) {
+            const float sz = zrow[c] / (1.0f + expf(-zrow[c]));
+            out[(size_t)r * vd + c] = ((orow[c] * rinv) * w[c]) * sz;
+        }
+    }
+    return 0;
+}
+
 /*
  * Double-precision brute force, re-associated: S' = alpha (I - beta k k^T) S
  * + beta k v^T and o = S'^T q, with the kd x kd matrix P = alpha (I - beta k

@@ -112,6 +112,12 @@ int ref_gdn_frontend_m(const float *x, const float *Wa, const float *Wb,
                        int B, int M, int dim, int conv_dim, int ck,
                        int vh, int kh, int kd, int vd);
 
+/* Gated RMSNorm of the output, per row of vd values:
+ * out = (o / sqrt(mean(o^2) + eps)) * w * silu(z).  o, z, out [rows][vd];
+ * w [vd]. */
+int ref_gdn_gated_norm(const float *o, const float *z, const float *w, float eps,
+                       float *out, int64_t rows, int vd);
+
 /* Double-precision brute force of one step for tiny shapes, in the
  * re-associated matrix form S' = alpha (I - beta k k^T) S + beta k v^T,
  * o = S'^T q, built from explicit kd x kd and kd x vd matrices.  Same

@@ -128,4 +128,6 @@ WORKLOADS = {
             seqs=512, layers=8, dims=DIMS64, steps=50, gate="alpha-uniform", seed=5),
     6: dict(name="verify with front end, 128 sequences x 1 layer, M=8 drafts",
             seqs=128, layers=1, dims=DIMS128, M=8, gate=None, seed=6),
+    7: dict(name="batched decode with gated RMSNorm output, 64 sequences x 48 layers",
+            seqs=64, layers=48, dims=DIMS128, steps=100, gate="softplus", seed=7, gated=True),
 }

@@ -6,7 +6,8 @@ FLOOR = 1e-6    # absolute floor for elements produced by cancellation
 
 
 def tol_violations(x, r, rel=REL, floor=FLOOR):
-    """Count of elements with |x - r| > max(rel*|r|, floor)."""
+    """Count of elements with |x - r| > max(rel*|r|, floor); floor may be an
+    array broadcast against r."""
     x = np.asarray(x, np.float64)
     r = np.asarray(r, np.float64)
     bad = np.abs(x - r) > np.maximum(rel * np.abs(r), floor)
@@ -21,7 +22,7 @@ def assert_close(x, r, what="", rel=REL, floor=FLOOR):
     n = tol_violations(x, r, rel, floor)
     if n:
         err = np.abs(x - r)
-        i = int(np.argmax(err - np.maximum(rel * np.abs(r), floor)))
+        i = int(np.argmax(err - np.broadcast_to(np.maximum(rel * np.abs(r), floor), err.shape)))
         raise AssertionError(
             f"{what}: {n}/{x.size} elements out of tolerance; worst at flat index "
             f"{i}: got {x.ravel()[i]!r} want {r.ravel()[i]!r}")

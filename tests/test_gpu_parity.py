@@ -362,6 +362,47 @@ def test_verify_cycle_with_frontend(orc):
     assert bits_equal(host(hist), hist_h)
 
 
+@pytest.mark.parametrize("dims,M", [(synth.DIMS128, 1), (synth.DIMS128, 5), (synth.DIMS64, 1),
+                                    (synth.DIMS64, 3)])
+def test_step_gated_parity(orc, dims, M):
+    """Gated RMSNorm fused on the output: the state advances exactly as in
+    the ungated call (bits); the output matches the oracle's step followed by
+    the oracle's gated norm; M rows equal M single gated steps (bits)."""
+    say(f"step_gated dims={dims} M={M}")
+    vh, kh, kd, vd = dims
+    N = 4
+    gen = synth.make_gen(12, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    z = torch.randn((M, N, vh, vd), generator=gen, device="cuda")
+    w = 1.0 + 0.1 * torch.randn((vd,), generator=gen, device="cuda")
+    eps = 1e-6
+    S_plain = S.clone()
+    S_h = host(S)
+    out = gdn.step_gated(S, *(inp[n] for n in NAMES), z, w, eps)
+    if M == 1:
+        gdn.step(S_plain, *(inp[n][0] for n in NAMES))
+    else:
+        gdn.step_m(S_plain, *(inp[n] for n in NAMES))
+    assert bits_equal(host(S), host(S_plain))
+    o_ref = np.zeros((M, N, vh, vd), np.float32)
+    orc.gdn_step_m(S_h, *(host(inp[n]) for n in NAMES), o_ref, M, dims)
+    g_ref = np.zeros_like(o_ref)
+    orc.gated_norm(o_ref, host(z), host(w), eps, g_ref)
+    # out = o * s with s = w * silu(z) / sqrt(mean(o^2) + eps): o's tolerance
+    # (1e-5 relative, 1e-6 absolute) carries over, its absolute floor scaled by s
+    o64, z64 = o_ref.astype(np.float64), host(z).astype(np.float64)
+    rinv = 1.0 / np.sqrt(np.mean(o64 ** 2, axis=-1, keepdims=True) + eps)
+    scale = np.abs(rinv * host(w).astype(np.float64) * z64 / (1.0 + np.exp(-z64)))
+    assert_close(host(out), g_ref, "gated out", rel=1e-5, floor=1e-6 * scale)
+    if M > 1:
+        S1 = synth.state(synth.make_gen(12, "cuda"), N, dims, device="cuda")
+        for m in range(M):
+            o1 = gdn.step_gated(S1, *(inp[n][m:m + 1].contiguous() for n in NAMES),
+                                z[m:m + 1].contiguous(), w, eps)
+            assert bits_equal(host(o1[0]), host(out[m])), m
+
+
 def test_graph_replay_matches_eager():
     """A captured chain of 8 single steps (the per-token launch chain) replays
     bit-identically to eager execution, several times, with eager work and

@@ -61,6 +61,15 @@ MUTANTS = [
     ("norm epsilon dropped", "1.0f / sqrtf(ssq + 1e-6f)", "1.0f / sqrtf(ssq)"),
     ("q scale dropped", "qh[j] = (qh[j] * iq) * q_scale;", "qh[j] = qh[j] * iq;"),
     ("k normalised with q's norm", "kk[j] = kk[j] * ik;", "kk[j] = kk[j] * iq;"),
+    ("gated norm over the sum", "1.0f / sqrtf(ss / (float)vd + eps)", "1.0f / sqrtf(ss + eps)"),
+    ("gated norm eps outside the root", "1.0f / sqrtf(ss / (float)vd + eps)",
+     "1.0f / (sqrtf(ss / (float)vd) + eps)"),
+    ("gated norm without the root", "1.0f / sqrtf(ss / (float)vd + eps)",
+     "1.0f / (ss / (float)vd + eps)"),
+    ("gate sigmoid instead of silu", "const float sz = zrow[c] / (1.0f + expf(-zrow[c]));",
+     "const float sz = 1.0f / (1.0f + expf(-zrow[c]));"),
+    ("norm weight dropped", "out[(size_t)r * vd + c] = ((orow[c] * rinv) * w[c]) * sz;",
+     "out[(size_t)r * vd + c] = (orow[c] * rinv) * sz;"),
 ]
 
 

@@ -440,6 +440,42 @@ def pin_fe_history_advance(orc):
         assert bits_equal(d["hist"], np.ascontiguousarray(seq[:, -3:])), t
 
 
+# --------------------------------------------------------------------------
+# gated RMSNorm of the output
+# --------------------------------------------------------------------------
+
+def _gnorm(orc, o, z, w, eps):
+    out = np.zeros_like(o)
+    orc.gated_norm(o, z, w, eps, out)
+    return out
+
+
+def pin_gated_norm_closed_forms(orc):
+    """out = (o / sqrt(mean(o^2) + eps)) * w * silu(z), per row:
+    z = 0 gives 0 exactly; z = 30 gives silu = 30 exactly in fp32, so with
+    w = 1 and eps = 0 the mean square of out is 900 (a mean over vd, not a
+    sum); scaling o by 4 leaves out unchanged bit for bit (eps = 0); a row of
+    equal entries c = 1e-3 with eps = 1e-6 gives 30/sqrt(2) (eps inside the
+    root); the gate enters as z * sigmoid(z); w scales each column."""
+    r = _rng(59)
+    vd = 16
+    o = r.normal(size=(3, vd)).astype(np.float32)
+    w1 = np.ones(vd, np.float32)
+    assert np.all(_gnorm(orc, o, np.zeros_like(o), w1, 1e-6) == 0.0)
+    z30 = np.full_like(o, 30.0)
+    out = _gnorm(orc, o, z30, w1, 0.0)
+    assert np.allclose(np.mean(out.astype(np.float64) ** 2, axis=1), 900.0, rtol=2e-6)
+    assert bits_equal(_gnorm(orc, (o * 4).astype(np.float32), z30, w1, 0.0), out)
+    c = np.full((1, vd), 1e-3, np.float32)
+    assert np.allclose(_gnorm(orc, c, np.full_like(c, 30.0), w1, 1e-6), 30 / np.sqrt(2), rtol=1e-5)
+    z = r.normal(size=o.shape).astype(np.float32)
+    base = _gnorm(orc, o, z30, w1, 1e-6) / 30.0
+    assert_close(_gnorm(orc, o, z, w1, 1e-6), base * z * expit(z.astype(np.float64)),
+                 "silu gate", rel=1e-5, floor=1e-7)
+    w = r.normal(size=vd).astype(np.float32)
+    assert_close(_gnorm(orc, o, z30, w, 1e-6), (base * 30.0) * w, "weight", rel=1e-6, floor=1e-7)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
