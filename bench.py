@@ -238,11 +238,16 @@ def bench_verify(cfg, steps, warmup, cpu):
     args = [inp[n] for n in NAMES]
 
     def one(i):
+        slab.mark_step_m(S, *args, o=o)          # mark fused into the M-step pass
+        slab.rollback(S, accs[i % 8], *args)
+
+    def one_unfused(i):
         slab.mark(S)
         gdn.step_m(S, *args, o=o)
         slab.rollback(S, accs[i % 8], *args)
 
     dt = timed(one, steps, warmup)
+    dt_unfused = timed(one_unfused, steps, 1)
     # step_m alone, for the kernel roofline
     dt_m = timed(lambda i: gdn.step_m(S, *args, o=o), steps, 1)
     bytes_m = N * vh * M * head_step_bytes(dims, rows=M)
@@ -252,9 +257,10 @@ def bench_verify(cfg, steps, warmup, cpu):
                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
                              unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
                extra=dict(step_m_ms=round(dt_m / steps * 1e3, 4), mean_accepted=mean_a,
+                          cycle_ms_separate_mark=round(dt_unfused / steps * 1e3, 4),
                           value_counts="drafted head-steps per second of the full cycle"))
     return res, dict(workload=cfg["name"], units=N, M=M, vh=vh, kd=dims[2],
-                     cycle="gdn_mark + gdn_step_m(M=8) + gdn_rollback(accepted ~ U{0..8})")
+                     cycle="gdn_mark_step_m(M=8) + gdn_rollback(accepted ~ U{0..8})")
 
 
 def bench_frontend(cfg, steps, warmup, cpu):

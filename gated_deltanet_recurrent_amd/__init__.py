@@ -27,7 +27,7 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ESTATE, GDN_EDEVICE = 0, -1, -2, -3, -
 
 # Every exported symbol of include/gdn.h.
 EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_bytes",
-           "gdn_slab_init",
+           "gdn_slab_init", "gdn_mark_step_m",
            "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy")
 
 
@@ -67,11 +67,12 @@ def lib():
     L.gdn_slab_bytes.restype = I64
     L.gdn_slab_init.argtypes = [C.POINTER(gdn_slab), P, I64, I64, I32, I32, I32, I32, I64]
     L.gdn_mark.argtypes = [C.POINTER(gdn_slab), P, P, P]
+    L.gdn_mark_step_m.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I64, I32, I32, I32, I32, I32, P]
     L.gdn_rollback.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I32, I32, P, P]
     L.gdn_frontend.argtypes = [P] * 13 + [I32] * 8 + [P]
     L.gdn_frontend_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_stream_copy.argtypes = [P, P, I64, P]
-    for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark", "gdn_rollback",
+    for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark_step_m", "gdn_mark", "gdn_rollback",
               "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy"):
         getattr(L, f).restype = C.c_int
     _lib = L
@@ -178,6 +179,19 @@ class Slab:
     def mark(self, S, hist=None, stream=None):
         _check(lib().gdn_mark(C.byref(self.s), _dev(S, "S"), _dev(hist, "hist"),
                               _stream(stream)), "gdn_mark")
+
+    def mark_step_m(self, S, q, k, v, g, beta, hist=None, o=None, stream=None):
+        """gdn_mark_step_m: mark S (and hist) and run M steps, reading S once.
+        Returns o [M][N][vh][vd]."""
+        N, vh, kh, kd, vd = _state_dims(S, q, v)
+        M = q.shape[0]
+        if o is None:
+            o = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
+        _check(lib().gdn_mark_step_m(C.byref(self.s), _dev(S, "S"), _dev(hist, "hist"),
+                                     _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(g, "g"),
+                                     _dev(beta, "beta"), _dev(o, "o"), N, M, vh, kh, kd, vd,
+                                     _stream(stream)), "gdn_mark_step_m")
+        return o
 
     def rollback(self, S, accepted, q=None, k=None, v=None, g=None, beta=None, hist=None,
                  xc_raw=None, M=None, stream=None):

@@ -193,6 +193,41 @@ int gdn_mark(gdn_slab *slab, const float *S, const float *hist, void *stream) {
   return GDN_OK;
 }
 
+int gdn_mark_step_m(gdn_slab *slab, float *S, const float *hist, const float *q, const float *k,
+                    const float *v, const float *g, const float *beta, float *o, int64_t n_units,
+                    int32_t M, int32_t vh, int32_t kh, int32_t kd, int32_t vd, void *stream) {
+  if (!slab_valid(slab)) return GDN_ESTATE;
+  if (n_units != slab->n_units || vh != slab->vh || kh != slab->kh || kd != slab->kd ||
+      vd != slab->vd)
+    return GDN_ESTATE;
+  if (M < 1 || M > kMaxM) return GDN_EINVAL;
+  int rc = check_step(S, q, k, v, g, beta, o, n_units, M, vh, kh, kd, vd);
+  if (rc) return rc;
+  if (hist != nullptr && !aligned16(hist)) return GDN_EINVAL;
+  if (hist != nullptr && slab->hist_floats == 0) return GDN_ESTATE;
+  const int64_t ns = slab->n_units * slab->vh * (int64_t)slab->kd * slab->vd;
+  const int64_t nh = slab->n_units * slab->hist_floats;
+  const int64_t qkb = (int64_t)M * n_units * kh * kd * 4, vb = (int64_t)M * n_units * vh * vd * 4,
+                gb = (int64_t)M * n_units * vh * 4;
+  const void *ins[6] = {q, k, v, g, beta, o};
+  const int64_t ib[6] = {qkb, qkb, vb, gb, gb, vb};
+  if (overlaps(S, ns * 4, slab->dev, slab->bytes) ||
+      (hist && overlaps(hist, nh * 4, slab->dev, slab->bytes)))
+    return GDN_EINVAL;
+  for (int i = 0; i < 6; i++)
+    if (overlaps(ins[i], ib[i], slab->dev, slab->bytes)) return GDN_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (hist != nullptr) {
+    rc = enq(gdn::launch_copy(slab_hist(slab), hist, nh, s));
+    if (rc) return rc;
+  }
+  rc = enq(gdn::launch_recur(kd, S, S, q, k, v, g, beta, o, nullptr, n_units, vh, kh, M, s,
+                             nullptr, nullptr, 0.0f, slab_S(slab)));
+  if (rc) return rc;
+  slab->armed = 1 | (hist != nullptr ? 2 : 0);
+  return GDN_OK;
+}
+
 int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const float *k,
                  const float *v, const float *g, const float *beta, const float *xc_raw,
                  int32_t conv_dim, int32_t M, const int32_t *accepted, void *stream) {

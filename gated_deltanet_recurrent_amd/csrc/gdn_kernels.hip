@@ -188,6 +188,7 @@ struct RecurArgs {
   const float *z;        // gated output only: gate z [rows][N][vh][vd]
   const float *norm_w;   // gated output only: RMSNorm weight [vd]
   float eps;             // gated output only
+  float *snap;           // nullable: the loaded state is also written here (mark)
   int64_t n_units;
   int vh, kh, M;
 };
@@ -354,6 +355,11 @@ void recur_wide_kernel(RecurArgs a) {
   f4 s[G::R];
 #pragma unroll
   for (int j = 0; j < G::R; j++) s[j] = ld_stream<RESIDENT>(src, lane_off, j * (G::RG * KD * 4));
+  if (a.snap != nullptr) {            // fused mark: the tile as loaded, before the step
+    const rsrc_t snp = buf_rsrc(a.snap + ti.tile_off, KD * KD * 4);
+#pragma unroll
+    for (int j = 0; j < G::R; j++) st_stream<false>(snp, lane_off, j * (G::RG * KD * 4), s[j]);
+  }
 
   if (run) {
     chunk_store<KD, LANES, GATED>(sb, cr, t, 1);
@@ -446,6 +452,13 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
   for (int j = 0; j < 4; j++)
 #pragma unroll
     for (int i = 0; i < 4; i++) s[i][j] = ld_stream(src, lane_off, (i + RG * j) * KD * 4);
+  if (a.snap != nullptr) {            // fused mark: the tile as loaded, before the steps
+    const rsrc_t snp = buf_rsrc(a.snap + ti.tile_off, KD * KD * 4);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) st_stream(snp, lane_off, (i + RG * j) * KD * 4, s[i][j]);
+  }
 
   int buf = 0;
   for (int m0 = 0; m0 < steps; m0 += MC) {
@@ -558,8 +571,8 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *k, const float *v, const float *g,
                  const float *beta, float *o, const int32_t *steps,
                  int64_t n_units, int vh, int kh, int M, hipStream_t s,
-                 const float *z, const float *norm_w, float eps) {
-  RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, z, norm_w, eps, n_units, vh, kh, M};
+                 const float *z, const float *norm_w, float eps, float *snap) {
+  RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, z, norm_w, eps, snap, n_units, vh, kh, M};
   const int64_t tiles = n_units * vh;
   if (tiles <= 0) return 0;
   const bool gated = z != nullptr;

@@ -16,12 +16,15 @@ int recur_lanes(int kd);
 // steps[u] steps when `steps` (device int32 [n_units]) is non-null.  Inputs
 // are [rows][n_units][...]; o (nullable) is [rows][n_units][vh][kd].  With a
 // non-null z ([rows][n_units][vh][kd]) the output goes through the gated
-// RMSNorm with weight norm_w [kd] and eps.
+// RMSNorm with weight norm_w [kd] and eps.  With a non-null snap (same
+// layout as the state) every tile is also written there as loaded, before
+// its first step (a mark fused into the step).
 int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *k, const float *v, const float *g,
                  const float *beta, float *o, const int32_t *steps,
                  int64_t n_units, int vh, int kh, int M, hipStream_t s,
-                 const float *z = nullptr, const float *norm_w = nullptr, float eps = 0.0f);
+                 const float *z = nullptr, const float *norm_w = nullptr, float eps = 0.0f,
+                 float *snap = nullptr);
 
 // 128-bit streaming copy of n floats (src == dst allowed).
 int launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);

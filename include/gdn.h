@@ -120,6 +120,19 @@ int gdn_slab_init(gdn_slab *slab, void *dev, int64_t bytes, int64_t n_units,
 int gdn_mark(gdn_slab *slab, const float *S, const float *hist, void *stream);
 
 /*
+ * gdn_mark(slab, S, hist) followed by gdn_step_m(S, ..., M), with the state
+ * read from memory once: each tile is written to the snapshot as loaded and
+ * then advanced.  Same results, bit for bit, as the two calls; arms the slab
+ * like gdn_mark.  n_units and the dims must equal the slab's (else
+ * GDN_ESTATE).  ("Kestrel_VLLM #34", section 3.7: mark before the M-row
+ * verify.)
+ */
+int gdn_mark_step_m(gdn_slab *slab, float *S, const float *hist, const float *q,
+                    const float *k, const float *v, const float *g,
+                    const float *beta, float *o, int64_t n_units, int32_t M,
+                    int32_t vh, int32_t kh, int32_t kd, int32_t vd, void *stream);
+
+/*
  * Roll back to an accepted length: for every unit u, S (and hist, unless
  * NULL) become the marked bytes advanced by accepted[u] single steps that use
  * rows 0..accepted[u]-1 of the inputs given to gdn_step_m (q, k, v, g, beta,

@@ -142,6 +142,23 @@ def test_rollback_refusals_need_no_device():
     assert s.armed == 1        # refusals leave the slab as it was
 
 
+def test_mark_step_m_refusals_need_no_device():
+    L = gdn.lib()
+    vh, kh, kd, vd = D128
+    nb = L.gdn_slab_bytes(2, vh, kh, kd, vd, 0)
+    s = gdn.gdn_slab()
+    assert L.gdn_slab_init(C.byref(s), fp(0), nb, 2, vh, kh, kd, vd, 0) == 0
+    ptrs = [fp((i + 2) << 32) for i in range(7)]   # S, q, k, v, g, beta, o
+    args = [ptrs[0], NULLS] + ptrs[1:]
+    assert L.gdn_mark_step_m(C.byref(gdn.gdn_slab()), *args, 2, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_ESTATE
+    assert L.gdn_mark_step_m(C.byref(s), *args, 3, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_ESTATE
+    assert L.gdn_mark_step_m(C.byref(s), *args, 2, 4, vh, kh, 64, 64, NULLS) == gdn.GDN_ESTATE
+    assert L.gdn_mark_step_m(C.byref(s), *args, 2, 0, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+    args_h = [ptrs[0], fp(9 << 32)] + ptrs[1:]     # history given, slab has none
+    assert L.gdn_mark_step_m(C.byref(s), *args_h, 2, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_ESTATE
+    assert s.armed == 0
+
+
 def test_frontend_validation():
     L = gdn.lib()
     vh, kh, kd, vd = D128

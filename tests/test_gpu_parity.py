@@ -236,6 +236,82 @@ def test_mark_rollback_bit_exact(orc, dims):
         slab.rollback(S, acc, *(inp[n] for n in NAMES), hist=hist, xc_raw=xc)
 
 
+@pytest.mark.parametrize("dims,M", [(synth.DIMS128, 8), (synth.DIMS64, 12), (synth.DIMS128, 1)])
+def test_mark_step_m_fused(dims, M):
+    """gdn_mark_step_m == gdn_mark + gdn_step_m: same state, outputs and
+    snapshot bits (rollback(0) restores the marked bytes), history marked."""
+    say(f"mark_step_m dims={dims} M={M}")
+    vh, kh, kd, vd = dims
+    N = 5
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(13, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    hist = torch.randn((N, 3, cd), generator=gen, device="cuda")
+    S_mark = S.clone()
+    S2 = S.clone()
+    slab = gdn.Slab(N, dims, hist_floats_per_unit=3 * cd)
+    o = slab.mark_step_m(S, *(inp[n] for n in NAMES), hist=hist)
+    assert slab.armed == 3
+    slab2 = gdn.Slab(N, dims, hist_floats_per_unit=3 * cd)
+    slab2.mark(S2, hist)
+    o2 = gdn.step_m(S2, *(inp[n] for n in NAMES))
+    assert bits_equal(host(S), host(S2)) and bits_equal(host(o), host(o2))
+    hist_mark = host(hist)
+    hist.add_(1.0)
+    slab.rollback(S, [0] * N, *(inp[n] for n in NAMES), hist=hist,
+                  xc_raw=torch.zeros((M, N, cd), device="cuda"))
+    assert bits_equal(host(S), host(S_mark))
+    assert bits_equal(host(hist), hist_mark)
+    # a mismatched slab is refused
+    small = gdn.Slab(N - 1, dims)
+    with pytest.raises(gdn.GdnError):
+        small.mark_step_m(S, *(inp[n] for n in NAMES))
+
+
+@pytest.mark.parametrize("dims,M", [(synth.DIMS64, 12), (synth.DIMS128, 10)])
+def test_many_rows_prefetch_paths(orc, dims, M):
+    """M > 8 rows run the prefetching instance: step_m, gated step and
+    rollback against single steps (bits) and the oracle."""
+    say(f"prefetch paths dims={dims} M={M}")
+    vh, kh, kd, vd = dims
+    N = 3
+    gen = synth.make_gen(14, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    S0 = S.clone()
+    S_h = host(S)
+    slab = gdn.Slab(N, dims)
+    slab.mark(S)
+    o = gdn.step_m(S, *(inp[n] for n in NAMES))
+    S1 = S0.clone()
+    for m in range(M):
+        o1 = gdn.step(S1, *(inp[n][m] for n in NAMES))
+        assert bits_equal(host(o1), host(o[m])), m
+    assert bits_equal(host(S), host(S1))
+    o_ref = np.zeros((M, N, vh, vd), np.float32)
+    orc.gdn_step_m(S_h, *(host(inp[n]) for n in NAMES), o_ref, M, dims)
+    assert_close(host(o), o_ref, "o many rows")
+    assert_close(host(S), S_h, "S many rows")
+    acc = [M, 9, 2]
+    slab.rollback(S, acc, *(inp[n] for n in NAMES))
+    for u in range(N):
+        Su = S0[u:u + 1].clone()
+        for m in range(acc[u]):
+            gdn.step(Su, *(inp[n][m, u:u + 1].contiguous() for n in NAMES))
+        assert bits_equal(host(S[u:u + 1]), host(Su)), u
+    z = torch.randn((M, N, vh, vd), generator=gen, device="cuda")
+    w = torch.ones((vd,), device="cuda")
+    Sg = S0.clone()
+    out = gdn.step_gated(Sg, *(inp[n] for n in NAMES), z, w, 1e-6)
+    assert bits_equal(host(Sg), host(S1))
+    Sg1 = S0.clone()
+    for m in range(M):
+        og = gdn.step_gated(Sg1, *(inp[n][m:m + 1].contiguous() for n in NAMES),
+                            z[m:m + 1].contiguous(), w, 1e-6)
+        assert bits_equal(host(og[0]), host(out[m])), m
+
+
 def test_rollback_state_only_and_zero_accept():
     dims = synth.DIMS128
     N, M = 4, 3
