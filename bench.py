@@ -246,8 +246,16 @@ def bench_verify(cfg, steps, warmup, cpu):
         gdn.step_m(S, *args, o=o)
         slab.rollback(S, accs[i % 8], *args)
 
+    acc_dev = [torch.from_numpy(a).to("cuda") for a in accs]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def one_verify_commit(i):                   # no snapshot: verify, then commit in place
+        gdn.verify_m(S, *args, o=o)
+        gdn.commit(S, acc_dev[i % 8], *args, status=status)
+
     dt = timed(one, steps, warmup)
     dt_unfused = timed(one_unfused, steps, 1)
+    dt_vc = timed(one_verify_commit, steps, 1)
     # step_m alone, for the kernel roofline
     dt_m = timed(lambda i: gdn.step_m(S, *args, o=o), steps, 1)
     bytes_m = N * vh * M * head_step_bytes(dims, rows=M)
@@ -258,6 +266,7 @@ def bench_verify(cfg, steps, warmup, cpu):
                              unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
                extra=dict(step_m_ms=round(dt_m / steps * 1e3, 4), mean_accepted=mean_a,
                           cycle_ms_separate_mark=round(dt_unfused / steps * 1e3, 4),
+                          cycle_ms_verify_commit=round(dt_vc / steps * 1e3, 4),
                           value_counts="drafted head-steps per second of the full cycle"))
     return res, dict(workload=cfg["name"], units=N, M=M, vh=vh, kd=dims[2],
                      cycle="gdn_mark_step_m(M=8) + gdn_rollback(accepted ~ U{0..8})")
@@ -327,11 +336,22 @@ def bench_verify_frontend(cfg, steps, warmup, cpu):
         gdn.step_m(S, *args, o=o)
         slab.rollback(S, accs[i % 8], *args, hist=hist, xc_raw=fe["xc_raw"])
 
+    acc_dev = [torch.from_numpy(a).to("cuda") for a in accs]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def one_verify_commit(i):
+        gdn.frontend_verify_m(fe["x"], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"],
+                              hist, w["conv_w"], dims, out=rows)
+        gdn.verify_m(S, *args, o=o)
+        gdn.commit(S, acc_dev[i % 8], *args, hist=hist, xc_raw=fe["xc_raw"], status=status)
+
     dt = timed(one, steps, warmup)
+    dt_vc = timed(one_verify_commit, steps, 1)
     res = dict(value=B * vh * M * steps / dt, ms_per_step=dt / steps * 1e3,
                roofline=dict(bound="hbm", achieved=None, peak=PEAK_HBM_GBPS, unit="GB/s",
                              frac=None, traffic=None),
                extra=dict(value_counts="drafted head-steps per second of the full cycle",
+                          cycle_ms_verify_commit=round(dt_vc / steps * 1e3, 4),
                           note="403 MB state: 1.6x the MALL, partly cache-resident"))
     return res, dict(workload=cfg["name"], units=B, M=M, vh=vh, kd=kd, conv_dim=cd,
                      cycle="gdn_mark(S, hist) + gdn_frontend_m + gdn_step_m + "

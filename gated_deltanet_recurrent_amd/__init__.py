@@ -27,7 +27,8 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ESTATE, GDN_EDEVICE = 0, -1, -2, -3, -
 
 # Every exported symbol of include/gdn.h.
 EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_bytes",
-           "gdn_slab_init", "gdn_mark_step_m",
+           "gdn_slab_init", "gdn_mark_step_m", "gdn_verify_m", "gdn_commit",
+           "gdn_frontend_verify_m",
            "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy")
 
 
@@ -72,8 +73,12 @@ def lib():
     L.gdn_frontend.argtypes = [P] * 13 + [I32] * 8 + [P]
     L.gdn_frontend_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_stream_copy.argtypes = [P, P, I64, P]
+    L.gdn_verify_m.argtypes = [P] * 7 + [I64, I32, I32, I32, I32, I32, P]
+    L.gdn_commit.argtypes = [P] * 8 + [I32, I64, I32, I32, I32, I32, I32, P, P, P]
+    L.gdn_frontend_verify_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark_step_m", "gdn_mark", "gdn_rollback",
-              "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy"):
+              "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_verify_m",
+              "gdn_commit", "gdn_frontend_verify_m"):
         getattr(L, f).restype = C.c_int
     _lib = L
     return L
@@ -253,6 +258,64 @@ def frontend_m(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None, 
         _dev(conv_w, "conv_w"), _dev(out["q"], "q"), _dev(out["k"], "k"), _dev(out["v"], "v"),
         _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, M, dim, conv_dim, ck, vh, kh, kd,
         vd, _stream(stream)), "gdn_frontend_m")
+    return out
+
+
+def verify_m(S, q, k, v, g, beta, o=None, stream=None):
+    """Outputs of M draft rows without advancing S (gdn_verify_m)."""
+    N, vh, kh, kd, vd = _state_dims(S, q, v)
+    M = q.shape[0]
+    if o is None:
+        o = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
+    _check(lib().gdn_verify_m(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                              _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"), N, M, vh, kh, kd,
+                              vd, _stream(stream)), "gdn_verify_m")
+    return o
+
+
+def _int32_dev(t, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.int32 \
+            or not t.is_contiguous():
+        raise TypeError(f"{name}: need a contiguous int32 tensor on a HIP device")
+    return C.c_void_p(t.data_ptr())
+
+
+def commit(S, accepted, q, k, v, g, beta, hist=None, xc_raw=None, status=None, stream=None):
+    """Apply the accepted prefix of the M rows given to verify_m (gdn_commit).
+    accepted: int32 device tensor [N]; status: int32 device tensor [1] or
+    None (set to 1 when an entry is out of range)."""
+    N, vh, kh, kd, vd = _state_dims(S, q, v)
+    M = q.shape[0]
+    conv_dim = xc_raw.shape[-1] if xc_raw is not None else 0
+    _check(lib().gdn_commit(_dev(S, "S"), _dev(hist, "hist"), _dev(q, "q"), _dev(k, "k"),
+                            _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"),
+                            _dev(xc_raw, "xc_raw"), conv_dim, N, M, vh, kh, kd, vd,
+                            _int32_dev(accepted, "accepted"), _int32_dev(status, "status"),
+                            _stream(stream)), "gdn_commit")
+
+
+def frontend_verify_m(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None,
+                      stream=None):
+    """frontend_m without advancing the history (gdn_frontend_verify_m)."""
+    vh, kh, kd, vd = dims
+    M, B, dim = x.shape
+    conv_dim = xc_raw.shape[-1]
+    ck = conv_w.shape[-1]
+    dev = x.device
+    if out is None:
+        out = dict(q=torch.empty((M, B, kh, kd), dtype=torch.float32, device=dev),
+                   k=torch.empty((M, B, kh, kd), dtype=torch.float32, device=dev),
+                   v=torch.empty((M, B, vh, vd), dtype=torch.float32, device=dev),
+                   g=torch.empty((M, B, vh), dtype=torch.float32, device=dev),
+                   beta=torch.empty((M, B, vh), dtype=torch.float32, device=dev))
+    _check(lib().gdn_frontend_verify_m(
+        _dev(x, "x"), _dev(Wa, "Wa"), _dev(Wb, "Wb"), _dev(A_log, "A_log"),
+        _dev(dt_bias, "dt_bias"), _dev(xc_raw, "xc_raw"), _dev(hist, "hist"),
+        _dev(conv_w, "conv_w"), _dev(out["q"], "q"), _dev(out["k"], "k"), _dev(out["v"], "v"),
+        _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, M, dim, conv_dim, ck, vh, kh, kd,
+        vd, _stream(stream)), "gdn_frontend_verify_m")
     return out
 
 

@@ -271,7 +271,8 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const fl
                                  M, s));
   if (rc) return rc;
   if (hist != nullptr) {
-    rc = enq(gdn::launch_hist_replay(hist, slab_hist(slab), xc_raw, d_acc, N, conv_dim, ck, s));
+    rc = enq(gdn::launch_hist_replay(hist, slab_hist(slab), xc_raw, d_acc, N, conv_dim, M,
+                                     nullptr, s));
     if (rc) return rc;
   }
   slab->armed = 0;
@@ -284,7 +285,7 @@ int frontend_impl(const float *x, const float *Wa, const float *Wb, const float 
                   const float *dt_bias, const float *xc_raw, float *hist, const float *conv_w,
                   float *q, float *k, float *v, float *g, float *beta, int32_t B, int32_t M,
                   int32_t dim, int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd,
-                  int32_t vd, void *stream) {
+                  int32_t vd, bool write_hist, void *stream) {
   int rc = check_dims(vh, kh, kd, vd);
   if (rc) return rc;
   if (ck != 4) return GDN_EUNSUPPORTED;
@@ -311,7 +312,8 @@ int frontend_impl(const float *x, const float *Wa, const float *Wb, const float 
   }
   if (overlaps(hist, hb, xc_raw, rawb)) return GDN_EINVAL;
   return enq(gdn::launch_frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g,
-                                  beta, B, M, dim, conv_dim, vh, kh, kd, (hipStream_t)stream));
+                                  beta, B, M, dim, conv_dim, vh, kh, kd, write_hist,
+                                  (hipStream_t)stream));
 }
 
 }  // namespace
@@ -322,7 +324,7 @@ int gdn_frontend(const float *x, const float *Wa, const float *Wb, const float *
                  int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
                  void *stream) {
   return frontend_impl(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta, B, 1,
-                       dim, conv_dim, ck, vh, kh, kd, vd, stream);
+                       dim, conv_dim, ck, vh, kh, kd, vd, true, stream);
 }
 
 int gdn_frontend_m(const float *x, const float *Wa, const float *Wb, const float *A_log,
@@ -331,7 +333,69 @@ int gdn_frontend_m(const float *x, const float *Wa, const float *Wb, const float
                    int32_t dim, int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd,
                    int32_t vd, void *stream) {
   return frontend_impl(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta, B, M,
-                       dim, conv_dim, ck, vh, kh, kd, vd, stream);
+                       dim, conv_dim, ck, vh, kh, kd, vd, true, stream);
+}
+
+int gdn_frontend_verify_m(const float *x, const float *Wa, const float *Wb, const float *A_log,
+                          const float *dt_bias, const float *xc_raw, const float *hist,
+                          const float *conv_w, float *q, float *k, float *v, float *g,
+                          float *beta, int32_t B, int32_t M, int32_t dim, int32_t conv_dim,
+                          int32_t ck, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+                          void *stream) {
+  return frontend_impl(x, Wa, Wb, A_log, dt_bias, xc_raw, const_cast<float *>(hist), conv_w, q,
+                       k, v, g, beta, B, M, dim, conv_dim, ck, vh, kh, kd, vd, false, stream);
+}
+
+int gdn_verify_m(const float *S, const float *q, const float *k, const float *v, const float *g,
+                 const float *beta, float *o, int64_t n_units, int32_t M, int32_t vh, int32_t kh,
+                 int32_t kd, int32_t vd, void *stream) {
+  if (M < 1 || M > kMaxM) return GDN_EINVAL;
+  int rc = check_step(S, q, k, v, g, beta, o, n_units, M, vh, kh, kd, vd);
+  if (rc || n_units == 0) return rc;
+  return enq(gdn::launch_recur(kd, S, nullptr, q, k, v, g, beta, o, nullptr, n_units, vh, kh, M,
+                               (hipStream_t)stream));
+}
+
+int gdn_commit(float *S, float *hist, const float *q, const float *k, const float *v,
+               const float *g, const float *beta, const float *xc_raw, int32_t conv_dim,
+               int64_t n_units, int32_t M, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+               const int32_t *accepted, int32_t *status, void *stream) {
+  if (M < 1 || M > kMaxM) return GDN_EINVAL;
+  int rc = check_dims(vh, kh, kd, vd);
+  if (rc) return rc;
+  if (n_units < 0) return GDN_EINVAL;
+  if (n_units == 0) return GDN_OK;
+  if (!grid_fits(n_units, vh, kd)) return GDN_EUNSUPPORTED;
+  const uintptr_t amask = 3u;
+  if (accepted == nullptr || (reinterpret_cast<uintptr_t>(accepted) & amask) ||
+      (status != nullptr && (reinterpret_cast<uintptr_t>(status) & amask)))
+    return GDN_EINVAL;
+  if (!ptr_ok(S) || !ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || g == nullptr || beta == nullptr)
+    return GDN_EINVAL;
+  const int64_t sb = n_units * vh * (int64_t)kd * vd * 4;
+  const int64_t qkb = (int64_t)M * n_units * kh * kd * 4, vb = (int64_t)M * n_units * vh * vd * 4,
+                gb = (int64_t)M * n_units * vh * 4;
+  const void *ins[6] = {q, k, v, g, beta, accepted};
+  const int64_t ib[6] = {qkb, qkb, vb, gb, gb, n_units * 4};
+  for (int i = 0; i < 6; i++)
+    if (overlaps(S, sb, ins[i], ib[i])) return GDN_EINVAL;
+  if (status != nullptr && overlaps(S, sb, status, 4)) return GDN_EINVAL;
+  const int ck = 4;
+  const int64_t hb = n_units * (ck - 1) * (int64_t)conv_dim * 4;
+  if (hist != nullptr) {
+    if (!aligned16(hist) || !ptr_ok(xc_raw) || conv_dim <= 0 || conv_dim % 4 != 0)
+      return GDN_EINVAL;
+    if (overlaps(hist, hb, S, sb) || overlaps(hist, hb, xc_raw, (int64_t)M * n_units * conv_dim * 4) ||
+        overlaps(hist, hb, accepted, n_units * 4))
+      return GDN_EINVAL;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  rc = enq(gdn::launch_recur(kd, S, S, q, k, v, g, beta, nullptr, accepted, n_units, vh, kh, M, s,
+                             nullptr, nullptr, 0.0f, nullptr, status));
+  if (rc) return rc;
+  if (hist != nullptr)
+    rc = enq(gdn::launch_hist_replay(hist, hist, xc_raw, accepted, n_units, conv_dim, M, status, s));
+  return rc;
 }
 
 int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream) {

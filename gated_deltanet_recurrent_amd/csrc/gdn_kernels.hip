@@ -189,6 +189,7 @@ struct RecurArgs {
   const float *norm_w;   // gated output only: RMSNorm weight [vd]
   float eps;             // gated output only
   float *snap;           // nullable: the loaded state is also written here (mark)
+  int32_t *status;       // nullable: set to 1 when a per-unit step count is out of range
   int64_t n_units;
   int vh, kh, M;
 };
@@ -317,6 +318,10 @@ static __device__ __forceinline__ TileIdx tile_index(const RecurArgs &a, int kdk
   x.head = (int)(tile - x.unit * a.vh);
   x.hh = x.head / (a.vh / a.kh);
   x.steps = a.steps ? a.steps[x.unit] : a.M;
+  if (x.steps < 0 || x.steps > a.M) {   // device-supplied counts: refuse the unit
+    if (a.status != nullptr && threadIdx.x == 0) a.status[0] = 1;
+    x.steps = 0;
+  }
   x.tile_off = tile * (int64_t)kdkd;
   return x;
 }
@@ -343,8 +348,9 @@ void recur_wide_kernel(RecurArgs a) {
   const int cg = t % G::CG, rg = t / G::CG;
   const TileIdx ti = tile_index(a, KD * KD);
   const bool run = ti.steps > 0;       // uniform per workgroup
+  // an in-place update with nothing to run leaves the tile as it is
+  if (!run && a.S_src == a.S_dst && a.snap == nullptr) return;
   const rsrc_t src = buf_rsrc(a.S_src + ti.tile_off, KD * KD * 4);
-  const rsrc_t dst = buf_rsrc(a.S_dst + ti.tile_off, KD * KD * 4);
   const int lane_off = (rg * KD + 4 * cg) * 4;
 
   // the inputs are requested before the state, so that their latency hides
@@ -394,8 +400,11 @@ void recur_wide_kernel(RecurArgs a) {
     if (lane < G::CG) s_red_o[wave][lane] = p;
   }
 
+  if (a.S_dst != nullptr) {            // null: outputs only, the state is left as it was
+    const rsrc_t dst = buf_rsrc(a.S_dst + ti.tile_off, KD * KD * 4);
 #pragma unroll
-  for (int j = 0; j < G::R; j++) st_stream<RESIDENT>(dst, lane_off, j * (G::RG * KD * 4), s[j]);
+    for (int j = 0; j < G::R; j++) st_stream<RESIDENT>(dst, lane_off, j * (G::RG * KD * 4), s[j]);
+  }
 
   if (run) {
     __syncthreads();
@@ -438,9 +447,10 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
   const int cg = t % CG, L = t / CG;
   const TileIdx ti = tile_index(a, KD * KD);
   const int steps = ti.steps;
+  // an in-place update with nothing to run leaves the tile as it is
+  if (steps == 0 && a.S_src == a.S_dst && a.snap == nullptr) return;
   // element (i, j) of this lane: row 4L + i + RG*j
   const rsrc_t src = buf_rsrc(a.S_src + ti.tile_off, KD * KD * 4);
-  const rsrc_t dst = buf_rsrc(a.S_dst + ti.tile_off, KD * KD * 4);
   const int lane_off = ((4 * L) * KD + 4 * cg) * 4;
 
   ChunkRegs<KD, LANES, GATED> cr;
@@ -531,10 +541,13 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
     buf ^= 1;
   }
 
+  if (a.S_dst != nullptr) {            // null: outputs only, the state is left as it was
+    const rsrc_t dst = buf_rsrc(a.S_dst + ti.tile_off, KD * KD * 4);
 #pragma unroll
-  for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 4; j++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) st_stream(dst, lane_off, (i + RG * j) * KD * 4, s[i][j]);
+      for (int i = 0; i < 4; i++) st_stream(dst, lane_off, (i + RG * j) * KD * 4, s[i][j]);
+  }
 
   if (XWAVE && steps > 0) {
     __syncthreads();
@@ -571,8 +584,10 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *k, const float *v, const float *g,
                  const float *beta, float *o, const int32_t *steps,
                  int64_t n_units, int vh, int kh, int M, hipStream_t s,
-                 const float *z, const float *norm_w, float eps, float *snap) {
-  RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, z, norm_w, eps, snap, n_units, vh, kh, M};
+                 const float *z, const float *norm_w, float eps, float *snap,
+                 int32_t *status) {
+  RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, z, norm_w, eps, snap, status,
+              n_units, vh, kh, M};
   const int64_t tiles = n_units * vh;
   if (tiles <= 0) return 0;
   const bool gated = z != nullptr;
@@ -634,33 +649,44 @@ int launch_copy(float *dst, const float *src, int64_t n, hipStream_t s) {
 // Conv-history rollback: pure data movement, bit-exact.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void hist_replay_kernel(float *hist, const float *snap,
+__global__ __launch_bounds__(256) void hist_replay_kernel(float *hist, const float *src,
                                                           const float *xc_raw,
                                                           const int32_t *accepted,
-                                                          int64_t n_units, int conv_dim,
-                                                          int nprev) {
+                                                          int64_t n_units, int conv_dim, int M,
+                                                          int32_t *status) {
+  constexpr int NPREV = 3;             // ck = 4
   const int64_t u = blockIdx.y;
   const int c4 = blockIdx.x * 256 + threadIdx.x;
-  if (4 * c4 >= conv_dim) return;
-  const int acc = accepted[u];
-  const int64_t hbase = u * (int64_t)nprev * conv_dim + 4 * c4;
-  for (int j = 0; j < nprev; j++) {
-    // frame j of the history after acc pushes is element acc + j of the
-    // sequence [old frames 0..nprev-1, raw 0..acc-1]
-    const int idx = acc + j;
-    const float *from = idx < nprev ? snap + u * (int64_t)nprev * conv_dim + (int64_t)idx * conv_dim + 4 * c4
-                                    : xc_raw + ((int64_t)(idx - nprev) * n_units + u) * conv_dim + 4 * c4;
-    st4(hist + hbase + (int64_t)j * conv_dim, ld4(from));
+  int acc = accepted[u];
+  if (acc < 0 || acc > M) {            // device-supplied counts: refuse the unit
+    if (status != nullptr && threadIdx.x == 0) status[0] = 1;
+    acc = 0;
   }
+  if (4 * c4 >= conv_dim) return;
+  if (acc == 0 && src == hist) return; // in place, nothing accepted: unchanged
+  const int64_t hbase = u * (int64_t)NPREV * conv_dim + 4 * c4;
+  // frame j of the history after acc pushes is element acc + j of the
+  // sequence [old frames 0..NPREV-1, raw 0..acc-1]; all frames are read
+  // before any is written, so src may be hist itself
+  f4 fr[NPREV];
+#pragma unroll
+  for (int j = 0; j < NPREV; j++) {
+    const int idx = acc + j;
+    const float *from = idx < NPREV ? src + hbase + (int64_t)idx * conv_dim
+                                    : xc_raw + ((int64_t)(idx - NPREV) * n_units + u) * conv_dim + 4 * c4;
+    fr[j] = ld4(from);
+  }
+#pragma unroll
+  for (int j = 0; j < NPREV; j++) st4(hist + hbase + (int64_t)j * conv_dim, fr[j]);
 }
 
-int launch_hist_replay(float *hist, const float *snap, const float *xc_raw,
-                       const int32_t *accepted, int64_t n_units, int conv_dim,
-                       int ck, hipStream_t s) {
+int launch_hist_replay(float *hist, const float *src, const float *xc_raw,
+                       const int32_t *accepted, int64_t n_units, int conv_dim, int M,
+                       int32_t *status, hipStream_t s) {
   if (n_units <= 0) return 0;
   dim3 grid((unsigned)((conv_dim / 4 + 255) / 256), (unsigned)n_units);
-  hipLaunchKernelGGL(hist_replay_kernel, grid, dim3(256), 0, s, hist, snap, xc_raw, accepted,
-                     n_units, conv_dim, ck - 1);
+  hipLaunchKernelGGL(hist_replay_kernel, grid, dim3(256), 0, s, hist, src, xc_raw, accepted,
+                     n_units, conv_dim, M, status);
   return (int)hipGetLastError();
 }
 
@@ -853,7 +879,8 @@ template <int KD>
 static __device__ __forceinline__ void fe_conv_block(int bx, int by, const float *xc_raw,
                                                      float *hist, const float *conv_w, float *q,
                                                      float *k, float *v, int B, int M,
-                                                     int conv_dim, int kh, int vh) {
+                                                     int conv_dim, int kh, int vh,
+                                                     bool write_hist) {
   const int t = threadIdx.x % 256;
   const int64_t b = (int64_t)by * CONV_ROWS + threadIdx.x / 256;
   const int ch = bx * 1024 + 4 * t;
@@ -911,7 +938,7 @@ static __device__ __forceinline__ void fe_conv_block(int bx, int by, const float
       }
     }
   }
-  if (valid) {
+  if (valid && write_hist) {
     st4(hb, h0);
     st4(hb + conv_dim, h1);
     st4(hb + 2 * (int64_t)conv_dim, h2);
@@ -927,6 +954,7 @@ struct FeArgs {
   const float *conv_w;
   float *q, *k, *v, *g, *beta;
   int B, M, dim, conv_dim, vh, kh;
+  int write_hist;         // 0: the history is read but left as it was
   int gemv_bx, conv_bx;   // x extents of the two parts
   int n_gemv;             // workgroups of the GEMV part
 };
@@ -941,7 +969,7 @@ __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
   } else {
     const int c = id - a.n_gemv;
     fe_conv_block<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k, a.v,
-                      a.B, a.M, a.conv_dim, a.kh, a.vh);
+                      a.B, a.M, a.conv_dim, a.kh, a.vh, a.write_hist != 0);
   }
 }
 
@@ -955,11 +983,11 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
                     const float *A_log, const float *dt_bias,
                     const float *xc_raw, float *hist, const float *conv_w,
                     float *q, float *k, float *v, float *g, float *beta, int B, int M,
-                    int dim, int conv_dim, int vh, int kh, int kd,
+                    int dim, int conv_dim, int vh, int kh, int kd, bool write_hist,
                     hipStream_t s) {
   if (B <= 0 || M <= 0) return 0;
   FeArgs a{x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta,
-           B, M, dim, conv_dim, vh, kh, 0, 0, 0};
+           B, M, dim, conv_dim, vh, kh, write_hist ? 1 : 0, 0, 0, 0};
   a.gemv_bx = (M * B + FB - 1) / FB;
   a.n_gemv = a.gemv_bx * ((2 * vh + FR - 1) / FR);
   a.conv_bx = (conv_dim + 1023) / 1024;

@@ -18,22 +18,27 @@ int recur_lanes(int kd);
 // non-null z ([rows][n_units][vh][kd]) the output goes through the gated
 // RMSNorm with weight norm_w [kd] and eps.  With a non-null snap (same
 // layout as the state) every tile is also written there as loaded, before
-// its first step (a mark fused into the step).
+// its first step (a mark fused into the step).  A null S_dst computes the
+// outputs only and leaves the state untouched.  Step counts read from
+// `steps` outside 0..M run no step for that unit and set *status = 1
+// (status nullable); with S_src == S_dst such a unit is left as it was.
 int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *k, const float *v, const float *g,
                  const float *beta, float *o, const int32_t *steps,
                  int64_t n_units, int vh, int kh, int M, hipStream_t s,
                  const float *z = nullptr, const float *norm_w = nullptr, float eps = 0.0f,
-                 float *snap = nullptr);
+                 float *snap = nullptr, int32_t *status = nullptr);
 
 // 128-bit streaming copy of n floats (src == dst allowed).
 int launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
 
-// Conv-history rollback: hist[u] = last (ck-1) frames of
-// [snap[u] frames..., xc_raw[0][u], ..., xc_raw[a-1][u]], a = accepted[u].
-int launch_hist_replay(float *hist, const float *snap, const float *xc_raw,
-                       const int32_t *accepted, int64_t n_units, int conv_dim,
-                       int ck, hipStream_t s);
+// Conv-history replay (ck = 4): hist[u] = last 3 frames of
+// [src[u] frames..., xc_raw[0][u], ..., xc_raw[a-1][u]], a = accepted[u];
+// src may be hist itself.  a outside 0..M: the unit gets a = 0 and *status
+// is set to 1 (status nullable).
+int launch_hist_replay(float *hist, const float *src, const float *xc_raw,
+                       const int32_t *accepted, int64_t n_units, int conv_dim, int M,
+                       int32_t *status, hipStream_t s);
 
 // Front end for M rows of B units: paired GEMV + gate/beta over all M*B
 // rows, and conv + SiLU + history + split + per key-head norm with the
@@ -46,7 +51,7 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
                     const float *A_log, const float *dt_bias,
                     const float *xc_raw, float *hist, const float *conv_w,
                     float *q, float *k, float *v, float *g, float *beta, int B, int M,
-                    int dim, int conv_dim, int vh, int kh, int kd,
+                    int dim, int conv_dim, int vh, int kh, int kd, bool write_hist,
                     hipStream_t s);
 
 }  // namespace gdn

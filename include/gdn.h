@@ -151,6 +151,39 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q,
                  int32_t M, const int32_t *accepted, void *stream);
 
 /*
+ * Speculative verify without a snapshot.  The M draft rows are evaluated
+ * against the state, which is left untouched; the accepted prefix is
+ * applied afterwards by gdn_commit.  A verify + commit cycle reads the state
+ * twice and writes it once, against five state passes for mark + step_m +
+ * rollback (snapshot copy, M-step read/write, restore read/write), and needs
+ * no slab.  Same results, bit for bit, as gdn_mark + gdn_step_m +
+ * gdn_rollback with the same rows and accepted lengths.
+ *
+ * gdn_verify_m: o [M][N][vh][vd] as gdn_step_m would produce them; S is read
+ * only.  1 <= M <= 64.
+ */
+int gdn_verify_m(const float *S, const float *q, const float *k,
+                 const float *v, const float *g, const float *beta, float *o,
+                 int64_t n_units, int32_t M, int32_t vh, int32_t kh, int32_t kd,
+                 int32_t vd, void *stream);
+
+/*
+ * gdn_commit: advance every unit u by accepted[u] single steps using rows
+ * 0..accepted[u]-1 of the inputs given to gdn_verify_m, in place; with hist
+ * (nullable) the conv history [N][3][conv_dim] receives the raw conv input
+ * frames xc_raw [M][N][conv_dim] of those rows.  accepted is a DEVICE array
+ * of N int32, read by the kernels (so the whole cycle can be captured into a
+ * graph).  An entry outside 0..M leaves that unit's state and history
+ * unchanged and sets *status = 1 (status: device int32, nullable; never
+ * cleared by the library).  Units with accepted[u] == 0 are not touched.
+ */
+int gdn_commit(float *S, float *hist, const float *q, const float *k,
+               const float *v, const float *g, const float *beta,
+               const float *xc_raw, int32_t conv_dim, int64_t n_units, int32_t M,
+               int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+               const int32_t *accepted, int32_t *status, void *stream);
+
+/*
  * Front end of one GDN layer for B rows ("Kestrel_VLLM #27", section 4.2:
  * the beta and a projections as one paired launch; "Kestrel_VLLM #24",
  * section 3 and Fig. 1 caption: gate/beta transform, depthwise causal conv +
@@ -193,6 +226,19 @@ int gdn_frontend_m(const float *x, const float *Wa, const float *Wb,
                    float *g, float *beta, int32_t B, int32_t M, int32_t dim,
                    int32_t conv_dim, int32_t ck, int32_t vh, int32_t kh, int32_t kd,
                    int32_t vd, void *stream);
+
+/*
+ * gdn_frontend_m without advancing the history: the M draft rows see the
+ * history as gdn_frontend_m would, but hist is only read.  Pair with
+ * gdn_commit, which pushes the accepted rows' raw frames into the history.
+ */
+int gdn_frontend_verify_m(const float *x, const float *Wa, const float *Wb,
+                          const float *A_log, const float *dt_bias,
+                          const float *xc_raw, const float *hist,
+                          const float *conv_w, float *q, float *k, float *v,
+                          float *g, float *beta, int32_t B, int32_t M,
+                          int32_t dim, int32_t conv_dim, int32_t ck, int32_t vh,
+                          int32_t kh, int32_t kd, int32_t vd, void *stream);
 
 /*
  * Measurement aid: stream n_floats floats from src to dst with the same

@@ -159,6 +159,27 @@ def test_mark_step_m_refusals_need_no_device():
     assert s.armed == 0
 
 
+def test_verify_commit_refusals_need_no_device():
+    L = gdn.lib()
+    vh, kh, kd, vd = D128
+    ptrs = [fp((i + 2) << 32) for i in range(9)]
+    S, q, k, v, g, beta, o, xc, hist = ptrs
+    assert L.gdn_verify_m(S, q, k, v, g, beta, o, 4, 0, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_verify_m(S, q, k, v, g, beta, fp((2 << 32) + 4096), 4, 2, vh, kh, kd, vd,
+                          NULLS) == gdn.GDN_EINVAL                   # o inside S
+    acc = fp(20 << 32)
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 2, vh, kh, kd, vd, NULLS, NULLS,
+                        NULLS) == gdn.GDN_EINVAL                       # no accepted array
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 2, vh, kh, kd, vd,
+                        fp((20 << 32) + 2), NULLS, NULLS) == gdn.GDN_EINVAL   # misaligned
+    assert L.gdn_commit(S, hist, q, k, v, g, beta, NULLS, 10240, 4, 2, vh, kh, kd, vd, acc, NULLS,
+                        NULLS) == gdn.GDN_EINVAL                       # history without raws
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 65, vh, kh, kd, vd, acc, NULLS,
+                        NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 0, 2, vh, kh, kd, vd, acc, NULLS,
+                        NULLS) == gdn.GDN_OK                           # nothing to do
+
+
 def test_frontend_validation():
     L = gdn.lib()
     vh, kh, kd, vd = D128

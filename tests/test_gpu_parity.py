@@ -479,6 +479,135 @@ def test_step_gated_parity(orc, dims, M):
             assert bits_equal(host(o1[0]), host(out[m])), m
 
 
+@pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
+def test_verify_commit_equals_snapshot_protocol(dims):
+    """verify_m + commit(accepted) gives the same outputs, state and conv
+    history, bit for bit, as mark + step_m + rollback(accepted); verify_m
+    leaves the state untouched."""
+    say(f"verify/commit dims={dims}")
+    vh, kh, kd, vd = dims
+    N, M = 6, 5
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(15, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    hist = torch.randn((N, 3, cd), generator=gen, device="cuda")
+    xc = torch.randn((M, N, cd), generator=gen, device="cuda")
+    acc = [0, 1, 2, M, 3, 4]
+    args = [inp[n] for n in NAMES]
+    # snapshot protocol
+    S_a, h_a = S.clone(), hist.clone()
+    slab = gdn.Slab(N, dims, hist_floats_per_unit=3 * cd)
+    slab.mark(S_a, h_a)
+    o_a = gdn.step_m(S_a, *args)
+    slab.rollback(S_a, acc, *args, hist=h_a, xc_raw=xc)
+    # verify / commit protocol
+    S_b, h_b = S.clone(), hist.clone()
+    o_b = gdn.verify_m(S_b, *args)
+    assert bits_equal(host(S_b), host(S))
+    acc_dev = torch.tensor(acc, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gdn.commit(S_b, acc_dev, *args, hist=h_b, xc_raw=xc, status=status)
+    assert bits_equal(host(o_a), host(o_b))
+    assert bits_equal(host(S_a), host(S_b))
+    assert bits_equal(host(h_a), host(h_b))
+    assert int(status.item()) == 0
+
+
+def test_commit_refuses_out_of_range_counts():
+    """Device-supplied counts outside 0..M leave that unit unchanged and raise
+    the status flag; the other units are committed normally."""
+    dims = synth.DIMS128
+    N, M = 4, 3
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(16, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    hist = torch.randn((N, 3, cd), generator=gen, device="cuda")
+    xc = torch.randn((M, N, cd), generator=gen, device="cuda")
+    S0, h0 = S.clone(), hist.clone()
+    acc = torch.tensor([1, M + 1, -1, 2], dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gdn.commit(S, acc, *(inp[n] for n in NAMES), hist=hist, xc_raw=xc, status=status)
+    assert int(status.item()) == 1
+    for u in (1, 2):
+        assert bits_equal(host(S[u]), host(S0[u])) and bits_equal(host(hist[u]), host(h0[u]))
+    for u, a in ((0, 1), (3, 2)):
+        Su = S0[u:u + 1].clone()
+        for m in range(a):
+            gdn.step(Su, *(inp[n][m, u:u + 1].contiguous() for n in NAMES))
+        assert bits_equal(host(S[u:u + 1]), host(Su)), u
+        seq = np.concatenate([host(h0[u]), host(xc[:a, u])], axis=0)
+        assert bits_equal(host(hist[u]), seq[-3:]), u
+
+
+def test_verify_cycle_graph_replay():
+    """One layer's speculative cycle without a snapshot -- front end for the M
+    draft rows (history read only), verify, commit with device-side accepted
+    lengths -- captured as a graph and replayed three times against eager
+    execution of the same cycle, bit for bit."""
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    B, M = 4, 3
+    gen = synth.make_gen(17, "cuda")
+    S0 = synth.state(gen, B, dims, device="cuda")
+    w = synth.frontend_weights(gen, dims, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=M, device="cuda")
+    h0 = fe["hist"].clone()
+    acc = torch.tensor([3, 0, 1, 2], dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rows = dict(q=torch.empty((M, B, kh, kd), device="cuda"),
+                k=torch.empty((M, B, kh, kd), device="cuda"),
+                v=torch.empty((M, B, vh, vd), device="cuda"),
+                g=torch.empty((M, B, vh), device="cuda"),
+                beta=torch.empty((M, B, vh), device="cuda"))
+    o = torch.empty((M, B, vh, vd), device="cuda")
+    S, hist = S0.clone(), h0.clone()
+
+    def cycle():
+        gdn.frontend_verify_m(fe["x"], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"],
+                              hist, w["conv_w"], dims, out=rows)
+        gdn.verify_m(S, *(rows[n] for n in NAMES), o=o)
+        gdn.commit(S, acc, *(rows[n] for n in NAMES), hist=hist, xc_raw=fe["xc_raw"],
+                   status=status)
+
+    cycle()
+    torch.cuda.synchronize()
+    S_e, h_e, o_e = host(S), host(hist), host(o)
+    # the eager cycle agrees with the snapshot protocol driven by frontend_m
+    S_s, h_s = S0.clone(), h0.clone()
+    slab = gdn.Slab(B, dims, hist_floats_per_unit=3 * synth.conv_dim_of(dims))
+    slab.mark(S_s, h_s)
+    rows_s = gdn.frontend_m(fe["x"], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"],
+                            h_s, w["conv_w"], dims)
+    o_s = gdn.step_m(S_s, *(rows_s[n] for n in NAMES))
+    slab.rollback(S_s, host(acc), *(rows_s[n] for n in NAMES), hist=h_s, xc_raw=fe["xc_raw"])
+    assert bits_equal(host(S_s), S_e) and bits_equal(host(h_s), h_e) and bits_equal(host(o_s), o_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        S.copy_(S0)
+        hist.copy_(h0)
+        cycle()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cycle()
+    for rep in range(3):
+        S.copy_(S0)
+        hist.copy_(h0)
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert bits_equal(host(S), S_e) and bits_equal(host(hist), h_e), rep
+        assert bits_equal(host(o), o_e), rep
+        gdn.step(S0.clone(), *(rows[n][0] for n in NAMES))   # eager work between replays
+        torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    del graph
+
+
 def test_graph_replay_matches_eager():
     """A captured chain of 8 single steps (the per-token launch chain) replays
     bit-identically to eager execution, several times, with eager work and
