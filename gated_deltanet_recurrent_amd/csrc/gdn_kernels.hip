@@ -963,9 +963,14 @@ template <int KD>
 __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
   const int id = blockIdx.x;
   if (id < a.n_gemv) {
-    // the GEMV rows of all M draft rows are independent: [M][B] = M*B rows
-    fe_gemv_block(id % a.gemv_bx, id / a.gemv_bx, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g,
-                  a.beta, a.M * a.B, a.dim, a.vh);
+    // Each XCD takes a contiguous, batch-major range of GEMV blocks, so its
+    // L2 holds a few batch rows of x and the weights once, instead of every
+    // L2 pulling in all of x and all of W.  The GEMV rows of all M draft rows
+    // are independent: [M][B] = M*B rows.
+    const int g = (int)xcd_contiguous(id, a.n_gemv);
+    const int r_tiles = a.n_gemv / a.gemv_bx;
+    fe_gemv_block(g / r_tiles, g % r_tiles, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g, a.beta,
+                  a.M * a.B, a.dim, a.vh);
   } else {
     const int c = id - a.n_gemv;
     fe_conv_block<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k, a.v,
