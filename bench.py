@@ -52,8 +52,18 @@ def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
     return state + per_row
 
 
+RECUR_END_MARK = b"// Streaming copy"
+
+
 def kernel_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] of the part of the kernel source the recurrence kernels are
+    built from: the shared helpers and the recurrence section (everything
+    before the streaming-copy section)."""
+    src = open(KERNEL_SRC, "rb").read()
+    cut = src.find(RECUR_END_MARK)
+    if cut < 0:
+        raise RuntimeError("kernel source layout changed: streaming-copy marker not found")
+    return hashlib.sha256(src[:cut]).hexdigest()[:16]
 
 
 def recorded_traffic(workload_key, launches_bytes):
