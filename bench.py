@@ -167,6 +167,22 @@ def bench_decode(cfg, steps, warmup, cpu):
     dt = timed(one, steps, warmup)
     hs_per_step = N * vh
     bps = head_step_bytes(dims) + (dims[3] * 4 if gated else 0)   # + the gate z
+    per_layer = {}
+    if not gated and cfg["layers"] > 1:
+        # the same step as one launch per layer (each over that layer's
+        # seqs units, contiguous), the way a model walks its layers
+        L, Bq = cfg["layers"], cfg["seqs"]
+        views = [[S[l * Bq:(l + 1) * Bq]] +
+                 [[x[n][0][l * Bq:(l + 1) * Bq] for n in NAMES] for x in pool] +
+                 [o[l * Bq:(l + 1) * Bq]] for l in range(L)]
+
+        def layers(i):
+            for v in views:
+                gdn.step(v[0], *v[1 + i % 4], o=v[5])
+
+        dt_l = timed(layers, steps, warmup)
+        per_layer = dict(per_layer_launches=L, per_layer_ms_per_step=round(dt_l / steps * 1e3, 4),
+                         per_layer_GBps=round(hs_per_step * bps * steps / dt_l / 1e9, 1))
     launch_s = dt / steps
     bytes_launch = hs_per_step * bps
     achieved = bytes_launch / launch_s / 1e9
@@ -182,7 +198,8 @@ def bench_decode(cfg, steps, warmup, cpu):
                    frac_of_copy_floor=round(achieved / floor, 4),
                    algorithmic_bytes_per_launch=int(bytes_launch),
                    bytes_per_head_step=round(bps, 2), head_steps_per_step=hs_per_step,
-                   kernel="recur_wide_kernel", kernel_source_sha256_16=kernel_hash()))
+                   kernel="recur_wide_kernel", kernel_source_sha256_16=kernel_hash(),
+                   **per_layer))
     if cpu:
         res["cpu_baseline"] = cpu_baseline_step(S, pool, dims, units=min(N, 256), rows=8)
     return res, dict(workload=cfg["name"], units=N, seqs=cfg["seqs"], layers=cfg["layers"],
@@ -220,11 +237,15 @@ def bench_latency(cfg, steps, warmup, cpu):
     with torch.cuda.graph(graph):
         one(0)
     dt_g = timed(lambda i: graph.replay(), steps, warmup)
+    # the same T steps as one gdn_step_m(M=T) call
+    o_m = torch.empty((T, 1, vh, dims[3]), device="cuda")
+    dt_m = timed(lambda i: gdn.step_m(S, *(inp[n] for n in NAMES), o=o_m), steps, warmup)
     res = dict(value=vh * T * steps / dt, ms_per_step=dt / steps * 1e3,
                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
                              unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
                extra=dict(us_per_call=round(launch_s * 1e6, 3),
                           us_per_step_graph_replay=round(dt_g / (steps * T) * 1e6, 3),
+                          us_per_step_step_m=round(dt_m / (steps * T) * 1e6, 3),
                           note="3 MiB state stays in L2/MALL: latency figure, not an HBM claim"))
     if cpu:
         res["cpu_baseline"] = cpu_baseline_step(S, [{n: inp[n][m:m + 1] for n in NAMES}
