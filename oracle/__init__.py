@@ -89,6 +89,8 @@ class Oracle:
         lib.ref64_gdn_step.argtypes = [P] * 7 + [L, I, I, I, I]
         lib.ref_gdn_gated_norm.argtypes = [P, P, P, C.c_float, P, L, I]
         lib.ref_gdn_gated_norm.restype = C.c_int
+        lib.ref_gdn_proj.argtypes = [P, P, P, L, I, I]
+        lib.ref_gdn_proj.restype = C.c_int
         for f in ("ref_gdn_step", "ref_gdn_step_m", "ref_gdn_mark", "ref_gdn_rollback",
                   "ref_gdn_frontend", "ref_gdn_frontend_m", "ref64_gdn_step"):
             getattr(lib, f).restype = C.c_int
@@ -154,6 +156,15 @@ class Oracle:
         rc = self.lib.ref_gdn_gated_norm(_f32(o, "o"), _f32(z, "z"), _f32(w, "w"), float(eps),
                                          _f32(out, "out", True), rows, vd)
         _check(rc, "ref_gdn_gated_norm")
+
+    def proj(self, x, W, y):
+        """y [rows][R] = x [rows][C] . W [R][C]^T, left folds over C."""
+        R, Cc = W.shape
+        rows = x.size // Cc
+        if x.size != rows * Cc or y.size != rows * R:
+            raise ValueError("proj: shapes of x, W, y do not agree")
+        rc = self.lib.ref_gdn_proj(_f32(x, "x"), _f32(W, "W"), _f32(y, "y", True), rows, R, Cc)
+        _check(rc, "ref_gdn_proj")
 
     def gdn_step64(self, S, q, k, v, g, beta, o, dims):
         """Double-precision brute-force step (tiny shapes, kd, vd <= 16)."""

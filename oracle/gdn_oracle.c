@@ -346,6 +346,33 @@ int ref_gdn_gated_norm(const float *o, const float *z, const float *w, float eps
     return 0;
 }
 
+/* The layer's dense projections ("Kestrel_VLLM #24", Fig. 1 caption, steps
+ * 1 and 7: in_proj_qkv feeding the conv, in_proj_z feeding the output gate,
+ * out_proj after the gated norm; "Kestrel_VLLM #34", section 3.6: for M
+ * draft rows the projections take all rows at once so that the weights are
+ * read once, each row giving what a one-row call gives).  Per row r and
+ * output o: acc = 0; acc = acc + W[o][c] * x[r][c] for c = 0..C-1. */
+int ref_gdn_proj(const float *x, const float *W, float *y, int64_t rows, int R, int C)
+{
+    if (rows < 0 || R <= 0 || C <= 0)
+        return -1;
+    if (rows == 0)
+        return 0;
+    if (!x || !W || !y)
+        return -1;
+    for (int64_t r = 0; r < rows; r++) {
+        const float *xr = x + (size_t)r * C;
+        for (int o = 0; o < R; o++) {
+            const float *wo = W + (size_t)o * C;
+            float acc = 0.0f;
+            for (int c = 0; c < C; c++)
+                acc = acc + wo[c] * xr[c];
+            y[(size_t)r * R + o] = acc;
+        }
+    }
+    return 0;
+}
+
 /*
  * Double-precision brute force, re-associated: S' = alpha (I - beta k k^T) S
  * + beta k v^T and o = S'^T q, with the kd x kd matrix P = alpha (I - beta k

@@ -118,6 +118,14 @@ int ref_gdn_frontend_m(const float *x, const float *Wa, const float *Wb,
 int ref_gdn_gated_norm(const float *o, const float *z, const float *w, float eps,
                        float *out, int64_t rows, int vd);
 
+/* Dense projection of the layer (the in_proj and out_proj products):
+ * y[r][o] = sum over c of W[o][c] * x[r][c], a strict left fold over
+ * c = 0..C-1 with every product and sum rounded to fp32 on its own.
+ * x [rows][C], W [R][C] (row-major, one output per row), y [rows][R].
+ * Each row is computed on its own, so M rows in one call equal M one-row
+ * calls. */
+int ref_gdn_proj(const float *x, const float *W, float *y, int64_t rows, int R, int C);
+
 /* Double-precision brute force of one step for tiny shapes, in the
  * re-associated matrix form S' = alpha (I - beta k k^T) S + beta k v^T,
  * o = S'^T q, built from explicit kd x kd and kd x vd matrices.  Same

@@ -70,6 +70,15 @@ MUTANTS = [
      "const float sz = 1.0f / (1.0f + expf(-zrow[c]));"),
     ("norm weight dropped", "out[(size_t)r * vd + c] = ((orow[c] * rinv) * w[c]) * sz;",
      "out[(size_t)r * vd + c] = (orow[c] * rinv) * sz;"),
+    ("projection weight transposed", "acc = acc + wo[c] * xr[c];",
+     "acc = acc + W[(size_t)c * R + o] * xr[c];"),
+    ("projection last term dropped", "for (int c = 0; c < C; c++)\n                acc = acc + wo[c]",
+     "for (int c = 0; c + 1 < C; c++)\n                acc = acc + wo[c]"),
+    ("projection x row stride", "const float *xr = x + (size_t)r * C;", "const float *xr = x;"),
+    ("projection output transposed", "y[(size_t)r * R + o] = acc;",
+     "y[(size_t)o * rows + r] = acc;"),
+    ("projection folds in double", "float acc = 0.0f;\n            for (int c = 0; c < C; c++)",
+     "double acc = 0.0;\n            for (int c = 0; c < C; c++)"),
 ]
 
 

@@ -476,6 +476,64 @@ def pin_gated_norm_closed_forms(orc):
     assert_close(_gnorm(orc, o, z30, w, 1e-6), (base * 30.0) * w, "weight", rel=1e-6, floor=1e-7)
 
 
+# --------------------------------------------------------------------------
+# dense projections (in_proj / out_proj)
+# --------------------------------------------------------------------------
+
+def _proj(orc, x, W):
+    y = np.zeros((x.shape[0], W.shape[0]), np.float32)
+    orc.proj(np.ascontiguousarray(x), np.ascontiguousarray(W), y)
+    return y
+
+
+def pin_proj_one_hot_and_exact(orc):
+    """y = x W^T.  A one-hot row x = e_c selects column c of W exactly (each
+    row with its own c, the last column included); small integer operands make
+    every product and partial sum exact in fp32, so y equals the integer
+    product; R != C so that a transposed operand cannot pass."""
+    r = _rng(61)
+    R, C = 7, 12
+    W = r.normal(size=(R, C)).astype(np.float32)
+    cols = [C - 1, 0, 5, 11, 3]
+    x = np.zeros((len(cols), C), np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = _proj(orc, x, W)
+    for i, c in enumerate(cols):
+        assert bits_equal(y[i], np.ascontiguousarray(W[:, c])), (i, c)
+    Wi = r.integers(-8, 9, size=(R, C))
+    xi = r.integers(-8, 9, size=(4, C))
+    y = _proj(orc, xi.astype(np.float32), Wi.astype(np.float32))
+    assert np.array_equal(y.astype(np.int64), xi @ Wi.T)
+
+
+def pin_proj_left_fold_in_fp32(orc):
+    """The sum over c is a left fold with every partial sum rounded to fp32:
+    for the terms (2^24, 1, -2^24, 1) the fold gives ((2^24 + 1) - 2^24) + 1
+    = 0 + 1 = 1 (2^24 + 1 rounds to 2^24), while the exact sum, and a fold in
+    the reverse order, give 2."""
+    W = np.array([[2.0 ** 24, 1.0, -(2.0 ** 24), 1.0]], np.float32)
+    x = np.ones((1, 4), np.float32)
+    assert _proj(orc, x, W)[0, 0] == 1.0
+
+
+def pin_proj_brute_force_fp64(orc):
+    """Random operands at the layer's inner size: within 1e-6 of the sum of
+    |W x| terms from a double-precision dot product (a dropped or misplaced
+    term is about 2e-4 of that sum); M rows in one call equal one-row calls."""
+    r = _rng(67)
+    R, C = 24, 5120
+    W = r.normal(0, 0.02, size=(R, C)).astype(np.float32)
+    x = r.normal(size=(3, C)).astype(np.float32)
+    y = _proj(orc, x, W)
+    W64, x64 = W.astype(np.float64), x.astype(np.float64)
+    ref = x64 @ W64.T
+    mag = np.abs(x64) @ np.abs(W64).T
+    assert np.all(np.abs(y - ref) <= 1e-6 * mag)
+    for i in range(3):
+        assert bits_equal(_proj(orc, x[i:i + 1], W)[0], y[i])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
