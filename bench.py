@@ -389,6 +389,89 @@ def bench_verify_frontend(cfg, steps, warmup, cpu):
                            "gdn_rollback(S, hist)")
 
 
+PEAK_MFMA_F32_TFLOPS = 157.3
+
+
+def bench_layer(cfg, steps, warmup, cpu):
+    """Whole GDN layers: in_proj_qkv + in_proj_z (one launch), front end,
+    recurrence with the gated RMSNorm, out_proj; the output of layer l is the
+    input x of layer l + 1.  Weights are f32, packed once before timing."""
+    dims = cfg["dims"]
+    vh, kh, kd, vd = dims
+    B, L, dim = cfg["seqs"], cfg["layers"], synth.FE_DIM
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    layers = []
+    for _ in range(L):
+        pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
+        lw = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
+        for n in ("W_qkv", "W_z", "W_out"):
+            packed = gdn.proj_pack(pw[n])
+            del pw[n]
+            lw[n] = packed
+        lw["norm_w"] = pw["norm_w"]
+        lw["S"] = synth.state(gen, B, dims, device="cuda")
+        lw["hist"] = torch.randn((B, 3, cd), generator=gen, device="cuda")
+        layers.append(lw)
+    torch.cuda.empty_cache()
+    x0 = torch.randn((B, dim), generator=gen, device="cuda")
+    xs = [torch.empty((B, dim), device="cuda") for _ in range(L)]
+    xc = torch.empty((B, cd), device="cuda")
+    z = torch.empty((B, vh * vd), device="cuda")
+    out = torch.empty((1, B, vh, vd), device="cuda")
+    fe = dict(q=torch.empty((B, kh, kd), device="cuda"), k=torch.empty((B, kh, kd), device="cuda"),
+              v=torch.empty((B, vh, vd), device="cuda"), g=torch.empty((B, vh), device="cuda"),
+              beta=torch.empty((B, vh), device="cuda"))
+
+    def one(i):
+        x = x0
+        for l, w in enumerate(layers):
+            gdn.proj(x, w["W_qkv"], w["W_z"], y0=xc, y1=z)
+            gdn.frontend(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], xc, w["hist"],
+                         w["conv_w"], dims, out=fe)
+            gdn.step_gated(w["S"], *(fe[n].unsqueeze(0) for n in NAMES), z.view(1, B, vh, vd),
+                           w["norm_w"], 1e-6, out=out)
+            gdn.proj(out.view(B, vh * vd), w["W_out"], y0=xs[l])
+            x = xs[l]
+
+    dt = timed(one, steps, warmup)
+    # the projections alone, layer after layer, for the kernel roofline
+    dt_in = timed(lambda i: [gdn.proj(x0, w["W_qkv"], w["W_z"], y0=xc, y1=z) for w in layers],
+                  steps, 1)
+    h = out.view(B, vh * vd)
+    dt_out = timed(lambda i: [gdn.proj(h, w["W_out"], y0=xs[0]) for w in layers], steps, 1)
+    w_in = (cd + vh * vd) * dim * 4
+    w_out = dim * vh * vd * 4
+    in_bytes = w_in + B * dim * 4 + B * (cd + vh * vd) * 4
+    out_bytes = w_out + B * vh * vd * 4 + B * dim * 4
+    in_flop = 2 * B * (cd + vh * vd) * dim
+    out_flop = 2 * B * dim * vh * vd
+    t_in, t_out = dt_in / (steps * L), dt_out / (steps * L)
+    ridge = PEAK_MFMA_F32_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)     # ~19.7 flop/B
+    if in_flop / in_bytes >= ridge:   # 2B flop per 4-byte weight: matrix cores from B ~ 40
+        roof = dict(bound="mfma", achieved=round(in_flop / t_in / 1e12, 2),
+                    peak=PEAK_MFMA_F32_TFLOPS, unit="TFLOP/s",
+                    frac=round(in_flop / t_in / 1e12 / PEAK_MFMA_F32_TFLOPS, 4), traffic=None)
+    else:
+        roof = dict(bound="hbm", achieved=round(in_bytes / t_in / 1e9, 1), peak=PEAK_HBM_GBPS,
+                    unit="GB/s", frac=round(in_bytes / t_in / 1e9 / PEAK_HBM_GBPS, 4),
+                    traffic=None)
+    res = dict(value=B * vh * L * steps / dt, ms_per_step=dt / steps * 1e3, roofline=roof,
+               extra=dict(kernel="proj_kernel (in_proj_qkv + in_proj_z, one launch)",
+                          in_proj_us=round(t_in * 1e6, 2), out_proj_us=round(t_out * 1e6, 2),
+                          in_proj_GBps=round(in_bytes / t_in / 1e9, 1),
+                          out_proj_GBps=round(out_bytes / t_out / 1e9, 1),
+                          in_proj_TFLOPs=round(in_flop / t_in / 1e12, 2),
+                          out_proj_TFLOPs=round(out_flop / t_out / 1e12, 2),
+                          layer_us=round(dt / (steps * L) * 1e6, 2),
+                          in_proj_bytes_per_launch=in_bytes, in_proj_flop_per_launch=in_flop,
+                          weights_GB=round(L * (w_in + w_out) / 1e9, 3)))
+    return res, dict(workload=cfg["name"], units=B * L, seqs=B, layers=L, vh=vh, kd=kd,
+                     dim=dim, conv_dim=cd,
+                     chain="gdn_proj(W_qkv, W_z) + gdn_frontend + gdn_step_gated + "
+                           "gdn_proj(W_out) per layer")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,7 +492,8 @@ def main():
     cfg = dict(synth.WORKLOADS[args.config])
     cfg["id"] = args.config
     runner = {0: bench_latency, 2: bench_verify, 3: bench_frontend,
-              6: bench_verify_frontend}.get(args.config, bench_decode)
+              6: bench_verify_frontend, 8: bench_layer, 9: bench_layer}.get(args.config,
+                                                                          bench_decode)
     res, config = runner(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
     line = dict(metric=METRIC, value=round(res["value"], 1), unit="head-steps/s", n_gpus=1,
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(res["ms_per_step"], 5),

@@ -29,7 +29,8 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ESTATE, GDN_EDEVICE = 0, -1, -2, -3, -
 EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_bytes",
            "gdn_slab_init", "gdn_mark_step_m", "gdn_verify_m", "gdn_commit",
            "gdn_frontend_verify_m",
-           "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy")
+           "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy",
+           "gdn_proj", "gdn_proj_pack")
 
 
 class GdnError(RuntimeError):
@@ -76,9 +77,11 @@ def lib():
     L.gdn_verify_m.argtypes = [P] * 7 + [I64, I32, I32, I32, I32, I32, P]
     L.gdn_commit.argtypes = [P] * 8 + [I32, I64, I32, I32, I32, I32, I32, P, P, P]
     L.gdn_frontend_verify_m.argtypes = [P] * 13 + [I32] * 9 + [P]
+    L.gdn_proj.argtypes = [P, I64, I32, P, I32, P, P, I32, P, P]
+    L.gdn_proj_pack.argtypes = [P, P, I32, I32, P]
     for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark_step_m", "gdn_mark", "gdn_rollback",
               "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_verify_m",
-              "gdn_commit", "gdn_frontend_verify_m"):
+              "gdn_commit", "gdn_frontend_verify_m", "gdn_proj", "gdn_proj_pack"):
         getattr(L, f).restype = C.c_int
     _lib = L
     return L
@@ -317,6 +320,41 @@ def frontend_verify_m(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out
         _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, M, dim, conv_dim, ck, vh, kh, kd,
         vd, _stream(stream)), "gdn_frontend_verify_m")
     return out
+
+
+def proj_pack(W, out=None, stream=None):
+    """Weights W [R][C] (row-major) in the packed order gdn_proj reads
+    (gdn_proj_pack); returns a tensor of the same shape holding that order."""
+    if W.dim() != 2:
+        raise ValueError("W must be [R][C]")
+    if out is None:
+        out = torch.empty_like(W)
+    _check(lib().gdn_proj_pack(_dev(W, "W"), _dev(out, "Wp"), W.shape[0], W.shape[1],
+                               _stream(stream)), "gdn_proj_pack")
+    return out
+
+
+def proj(x, W0, W1=None, y0=None, y1=None, stream=None):
+    """Dense projection(s) of the layer (gdn_proj): y0 = x W0^T and, with W1,
+    y1 = x W1^T in the same launch.  x [..., C] (leading axes are rows);
+    W0, W1: [R][C] weights already packed by proj_pack; outputs [..., R].
+    Returns y0, or (y0, y1) when W1 is given."""
+    Cc = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    rows = x.numel() // Cc if Cc else 0
+    for W, nm in ((W0, "W0"), (W1, "W1")):
+        if W is not None and (W.dim() != 2 or W.shape[1] != Cc):
+            raise ValueError(f"{nm} must be [R][{Cc}]")
+    if y0 is None:
+        y0 = torch.empty(lead + (W0.shape[0],), dtype=torch.float32, device=x.device)
+    if W1 is not None and y1 is None:
+        y1 = torch.empty(lead + (W1.shape[0],), dtype=torch.float32, device=x.device)
+    if y0.numel() != rows * W0.shape[0] or (W1 is not None and y1.numel() != rows * W1.shape[0]):
+        raise ValueError("output sizes do not match rows x R")
+    R1 = W1.shape[0] if W1 is not None else 0
+    _check(lib().gdn_proj(_dev(x, "x"), rows, Cc, _dev(W0, "W0"), W0.shape[0], _dev(y0, "y0"),
+                          _dev(W1, "W1"), R1, _dev(y1, "y1"), _stream(stream)), "gdn_proj")
+    return y0 if W1 is None else (y0, y1)
 
 
 def stream_copy(dst, src, stream=None):

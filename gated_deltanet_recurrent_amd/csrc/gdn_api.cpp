@@ -406,4 +406,36 @@ int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream
   return enq(gdn::launch_copy(dst, src, n_floats, (hipStream_t)stream));
 }
 
+int gdn_proj_pack(const float *W, float *Wp, int32_t R, int32_t C, void *stream) {
+  if (R <= 0 || C <= 0) return GDN_EINVAL;
+  if (C % 128 != 0 || R % 16 != 0) return GDN_EUNSUPPORTED;
+  if (!ptr_ok(W) || !ptr_ok(Wp)) return GDN_EINVAL;
+  const int64_t wb = (int64_t)R * C * 4;
+  if (overlaps(W, wb, Wp, wb)) return GDN_EINVAL;
+  return enq(gdn::launch_proj_pack(W, Wp, R, C, (hipStream_t)stream));
+}
+
+int gdn_proj(const float *x, int64_t rows, int32_t C, const float *W0, int32_t R0, float *y0,
+             const float *W1, int32_t R1, float *y1, void *stream) {
+  if (rows < 0 || C <= 0 || R0 <= 0) return GDN_EINVAL;
+  if (W1 == nullptr) {
+    if (R1 != 0 || y1 != nullptr) return GDN_EINVAL;
+  } else if (R1 <= 0) {
+    return GDN_EINVAL;
+  }
+  if (C % 128 != 0 || R0 % 16 != 0 || (W1 != nullptr && R1 % 16 != 0)) return GDN_EUNSUPPORTED;
+  if (rows == 0) return GDN_OK;
+  if (!ptr_ok(x) || !ptr_ok(W0) || !ptr_ok(y0)) return GDN_EINVAL;
+  if (W1 != nullptr && (!ptr_ok(W1) || !ptr_ok(y1))) return GDN_EINVAL;
+  if (gdn::proj_workgroups(rows, R0, R1) > (int64_t)0xFFFFFFFF / 512) return GDN_EUNSUPPORTED;
+  const int64_t xb = rows * C * 4, w0b = (int64_t)R0 * C * 4, y0b = rows * R0 * 4;
+  const int64_t w1b = (int64_t)R1 * C * 4, y1b = rows * R1 * 4;
+  if (overlaps(y0, y0b, x, xb) || overlaps(y0, y0b, W0, w0b) || overlaps(y0, y0b, W1, w1b))
+    return GDN_EINVAL;
+  if (W1 != nullptr && (overlaps(y1, y1b, x, xb) || overlaps(y1, y1b, W0, w0b) ||
+                        overlaps(y1, y1b, W1, w1b) || overlaps(y1, y1b, y0, y0b)))
+    return GDN_EINVAL;
+  return enq(gdn::launch_proj(x, rows, C, W0, R0, y0, W1, R1, y1, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1005,4 +1005,267 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
   return (int)hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Dense layer projections on the matrix cores: y[r][o] = sum_c W[o][c] x[r][c]
+// ("Kestrel_VLLM #24", Fig. 1 caption, steps 1 and 7: in_proj_qkv, in_proj_z
+// and out_proj; "Kestrel_VLLM #34", section 3.6: all draft rows in one pass
+// over the weights, each row giving what a one-row call gives).
+//
+// With 1-16 rows the product streams the weights once and is bound by HBM;
+// with 64 and more rows it is a dense fp32 contraction (32 flop per weight
+// byte at 64 rows, above the ridge), so it runs on v_mfma_f32_16x16x4_f32
+// throughout.  Operand layout of that instruction (checked on gfx950): lane
+// l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and receives
+// D[4 (l / 16) + t][l % 16] in accumulator register t.  Here A is a block of
+// 16 rows of x, B a block of 16 weight rows (transposed), so one lane loads
+// the 4 consecutive columns 4 (l / 16) .. +3 of one x row and of one weight
+// row with a 128-bit load and feeds them to 4 successive MFMAs.
+//
+// The weights are stored once, at load time, in that operand order
+// (gdn_proj_pack): slab s of 16 weight rows, 16-column block kb, lane l hold
+// W[16 s + l % 16][16 kb + 4 (l / 16) .. +3] as the 1 KiB block
+// Wp[(s (C / 16) + kb) 256 + 4 l ..].  A wave then streams its weights as
+// contiguous 1 KiB loads; read row-major, every load touched 16 rows in
+// 64-byte pieces and the call ran 25-30% slower at 1 row.
+//
+// Canonical summation, independent of the row count and of the tiling: C is
+// cut into PJ_SEG equal segments; each segment is summed by one MFMA chain
+// over its 16-column blocks in ascending order (block kb, MFMA step s adds
+// the terms of columns kb + 4 i + s, i = 0..3); the PJ_SEG segment sums are
+// then folded left to right.  A row's result therefore does not depend on
+// which other rows share the call, and every tile shape gives the same bits.
+//
+// A workgroup is PJ_SEG waves, wave w owning segment w for a tile of 16 RB
+// rows x 16 OJ outputs; the segment sums meet in LDS and are folded there.
+// Workgroups are ordered output-slab major, row-group minor, and laid out
+// contiguously per XCD, so the row groups sharing a weight slab run on one
+// L2.  Two products over the same x (in_proj_qkv and in_proj_z) share one
+// launch.
+// ---------------------------------------------------------------------------
+
+constexpr int PJ_SEG = 8;                 // segments of C, one wave each
+constexpr int PJ_LANES = 64 * PJ_SEG;
+#ifndef GDN_PJ_MIN_WG
+#define GDN_PJ_MIN_WG 128
+#endif
+#ifndef GDN_PJ_MIN_WG1
+#define GDN_PJ_MIN_WG1 256
+#endif
+#ifndef GDN_PJ_U1
+#define GDN_PJ_U1 4
+#endif
+
+struct ProjProblem {
+  const float *W;
+  float *y;
+  int R;
+  int blocks;       // workgroups: (R / (16 OJ)) * row_groups
+};
+
+struct ProjArgs {
+  const float *x;
+  int64_t rows;
+  int C;
+  int row_groups;
+  ProjProblem p[2];
+};
+
+typedef float pj_acc __attribute__((ext_vector_type(4)));
+
+// Weight loads: with a single row group each weight is read exactly once, so
+// it is streamed past the caches (nt) and leaves L2 to x; with several row
+// groups the default policy lets the groups sharing a slab hit in L2.
+template <bool STREAM>
+static __device__ __forceinline__ f4 ld_w(rsrc_t r, int voff) {
+  return __builtin_bit_cast(
+      f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, STREAM ? POL_STREAM_LOAD : 0));
+}
+
+// RB row blocks x OJ output slabs per wave, U 16-column blocks per trip.
+template <int RB, int OJ, int U, bool STREAM>
+__global__ __launch_bounds__(PJ_LANES) void proj_kernel(ProjArgs a) {
+  __shared__ pj_acc red[PJ_SEG][RB * OJ][64];
+  const int b = (int)xcd_contiguous(blockIdx.x, gridDim.x);
+  const bool second = b >= a.p[0].blocks;
+  const float *W = second ? a.p[1].W : a.p[0].W;
+  float *y = second ? a.p[1].y : a.p[0].y;
+  const int R = second ? a.p[1].R : a.p[0].R;
+  const int lb = second ? b - a.p[0].blocks : b;
+  const int slab = lb / a.row_groups, rgp = lb - slab * a.row_groups;
+  const int o0 = slab * 16 * OJ;
+  const int64_t r0 = (int64_t)rgp * 16 * RB;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int j = l & 15, kq = l >> 4;
+  const int C = a.C;
+  const int seg = C / PJ_SEG;
+  const int k0 = wave * seg + 4 * kq;
+
+  // one buffer resource over the workgroup's OJ packed slabs (< 2 GiB); the
+  // 16-column block at column c of slab oj starts at float oj 16 C + 16 c
+  const rsrc_t wr = buf_rsrc(W + (int64_t)o0 * C, 16 * OJ * C * 4);
+  int wo[OJ];
+#pragma unroll
+  for (int oj = 0; oj < OJ; oj++) wo[oj] = (16 * oj * C + 16 * wave * seg + 4 * l) * 4;
+  const float *xp[RB];
+  bool xon[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++) {
+    const int64_t row = r0 + 16 * rb + j;
+    xon[rb] = row < a.rows;
+    xp[rb] = a.x + (xon[rb] ? row : 0) * C + k0;
+  }
+
+  pj_acc acc[RB][OJ];
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+    for (int oj = 0; oj < OJ; oj++) acc[rb][oj] = pj_acc{0.f, 0.f, 0.f, 0.f};
+
+  int kb = 0;
+  for (; kb + 16 * U <= seg; kb += 16 * U) {
+    f4 w[U][OJ], xv[U][RB];
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int oj = 0; oj < OJ; oj++) w[u][oj] = ld_w<STREAM>(wr, wo[oj] + (kb + 16 * u) * 64);
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++) xv[u][rb] = xon[rb] ? ld4(xp[rb] + kb + 16 * u) : splat(0.f);
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int s = 0; s < 4; s++)
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+          for (int oj = 0; oj < OJ; oj++)
+            acc[rb][oj] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u][rb][s], w[u][oj][s],
+                                                               acc[rb][oj], 0, 0, 0);
+  }
+  for (; kb < seg; kb += 16) {             // the rest of a segment, one block at a time
+    f4 w[OJ], xv[RB];
+#pragma unroll
+    for (int oj = 0; oj < OJ; oj++) w[oj] = ld_w<STREAM>(wr, wo[oj] + kb * 64);
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++) xv[rb] = xon[rb] ? ld4(xp[rb] + kb) : splat(0.f);
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+        for (int oj = 0; oj < OJ; oj++)
+          acc[rb][oj] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[rb][s], w[oj][s], acc[rb][oj],
+                                                             0, 0, 0);
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+    for (int oj = 0; oj < OJ; oj++) red[wave][rb * OJ + oj][l] = acc[rb][oj];
+  __syncthreads();
+  // fold the segment sums left to right; element e = (tile, lane, register t)
+  // is float e of every segment's block of LDS
+  constexpr int ELEMS = RB * OJ * 256;
+  const float *redf = reinterpret_cast<const float *>(red);
+  for (int e = threadIdx.x; e < ELEMS; e += PJ_LANES) {
+    const int tile = e >> 8, ll = (e >> 2) & 63, t = e & 3;
+    float sum = redf[e];
+#pragma unroll
+    for (int w = 1; w < PJ_SEG; w++) sum = sum + redf[w * ELEMS + e];
+    const int rb = tile / OJ, oj = tile - rb * OJ;
+    const int64_t row = r0 + 16 * rb + 4 * (ll >> 4) + t;
+    if (row < a.rows) y[row * R + o0 + 16 * oj + (ll & 15)] = sum;
+  }
+}
+
+// Tile shape of a call: row blocks per tile by the row count; then the
+// widest output slab group (1, 2 or 4 slabs of 16) that divides both R / 16
+// and still leaves enough workgroups: with one row block the call streams the
+// weights and needs >= GDN_PJ_MIN_WG1 workgroups to spread that stream over
+// every CU; with more rows it is bound by the matrix cores and x traffic, and
+// >= GDN_PJ_MIN_WG suffice.  More slabs per wave share each x load among more
+// outputs.  The choice never changes a result (canonical summation above).
+struct ProjShape {
+  int rb, oj, row_groups;
+};
+
+static ProjShape proj_shape(int64_t rows, int R0, int R1) {
+  ProjShape sh;
+  sh.rb = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+  sh.row_groups = (int)((rows + 16 * sh.rb - 1) / (16 * sh.rb));
+  const int64_t min_wg = sh.rb == 1 ? GDN_PJ_MIN_WG1 : GDN_PJ_MIN_WG;
+  sh.oj = 1;
+  for (int oj = 4; oj > 1; oj >>= 1) {
+    const bool divides = (R0 / 16) % oj == 0 && (R1 / 16) % oj == 0;
+    const int64_t wg = ((int64_t)R0 / (16 * oj) + (int64_t)R1 / (16 * oj)) * sh.row_groups;
+    if (divides && wg >= min_wg) {
+      sh.oj = oj;
+      break;
+    }
+  }
+  return sh;
+}
+
+int64_t proj_workgroups(int64_t rows, int R0, int R1) {
+  const ProjShape sh = proj_shape(rows, R0, R1);
+  return ((int64_t)R0 / (16 * sh.oj) + (int64_t)R1 / (16 * sh.oj)) * sh.row_groups;
+}
+
+template <int RB, int OJ, int U>
+static void launch_proj_t(const ProjArgs &a, bool stream, hipStream_t s) {
+  const dim3 grid((unsigned)(a.p[0].blocks + a.p[1].blocks));
+  if (RB < 4 || stream)       // fewer than 4 row blocks: always one row group
+    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, true>), grid, dim3(PJ_LANES), 0, s, a);
+  else
+    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, RB < 4>), grid, dim3(PJ_LANES), 0, s, a);
+}
+
+// Weight packing (one launch per matrix, pure data movement): thread i
+// writes packed float4 i, gathered from its row-major place.
+__global__ __launch_bounds__(256) void proj_pack_kernel(const float *W, float *Wp, int C,
+                                                        int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const int l = (int)(i & 63);
+  const int64_t blk = i >> 6;                      // s (C / 16) + kb
+  const int64_t s = blk / (C / 16), kb = blk - s * (C / 16);
+  const int64_t row = 16 * s + (l & 15), col = 16 * kb + 4 * (l >> 4);
+  st4(Wp + 4 * i, ld4(W + row * C + col));
+}
+
+int launch_proj_pack(const float *W, float *Wp, int R, int C, hipStream_t s) {
+  const int64_t n4 = (int64_t)R * C / 4;
+  if (n4 <= 0) return 0;
+  hipLaunchKernelGGL(proj_pack_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, W,
+                     Wp, C, n4);
+  return (int)hipGetLastError();
+}
+
+int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, float *y0,
+                const float *W1, int R1, float *y1, hipStream_t s) {
+  if (rows <= 0) return 0;
+  const ProjShape sh = proj_shape(rows, R0, W1 ? R1 : 0);
+  ProjArgs a{};
+  a.x = x;
+  a.rows = rows;
+  a.C = C;
+  a.row_groups = sh.row_groups;
+  a.p[0] = ProjProblem{W0, y0, R0, R0 / (16 * sh.oj) * sh.row_groups};
+  a.p[1] = ProjProblem{W1, y1, R1, W1 ? R1 / (16 * sh.oj) * sh.row_groups : 0};
+  const bool stream = sh.row_groups == 1;
+  switch (sh.rb * 8 + sh.oj) {
+    case 1 * 8 + 1: launch_proj_t<1, 1, GDN_PJ_U1>(a, true, s); break;
+    case 1 * 8 + 2: launch_proj_t<1, 2, GDN_PJ_U1>(a, true, s); break;
+    case 1 * 8 + 4: launch_proj_t<1, 4, 2>(a, true, s); break;
+    case 2 * 8 + 1: launch_proj_t<2, 1, 4>(a, true, s); break;
+    case 2 * 8 + 2: launch_proj_t<2, 2, 4>(a, true, s); break;
+    case 2 * 8 + 4: launch_proj_t<2, 4, 2>(a, true, s); break;
+    case 4 * 8 + 1: launch_proj_t<4, 1, 4>(a, stream, s); break;
+    case 4 * 8 + 2: launch_proj_t<4, 2, 4>(a, stream, s); break;
+    default: launch_proj_t<4, 4, 2>(a, stream, s); break;
+  }
+  return (int)hipGetLastError();
+}
+
 }  // namespace gdn

@@ -54,4 +54,13 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
                     int dim, int conv_dim, int vh, int kh, int kd, bool write_hist,
                     hipStream_t s);
 
+// Dense projection y[r][o] = sum_c W[o][c] x[r][c] for rows r of x
+// [rows][C]; W0 (R0 x C, packed by launch_proj_pack) -> y0 [rows][R0] and,
+// when W1 is non-null, W1 -> y1 [rows][R1] in the same launch.
+// C % 128 == 0, R % 16 == 0.
+int launch_proj_pack(const float *W, float *Wp, int R, int C, hipStream_t s);
+int64_t proj_workgroups(int64_t rows, int R0, int R1);
+int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, float *y0,
+                const float *W1, int R1, float *y1, hipStream_t s);
+
 }  // namespace gdn

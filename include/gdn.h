@@ -248,6 +248,47 @@ int gdn_frontend_verify_m(const float *x, const float *Wa, const float *Wb,
  */
 int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream);
 
+/*
+ * Weight packing for gdn_proj: copies a row-major weight matrix W [R][C] into
+ * the matrix-core operand order that gdn_proj streams.  Packed slab s of 16
+ * rows, 16-column block kb and lane l = 0..63 hold
+ *   Wp[((s * (C / 16) + kb) * 64 + l) * 4 + i] = W[16 s + l % 16][16 kb + 4 (l / 16) + i]
+ * for i = 0..3 (same size as W; a pure permutation, bit-exact).  Done once
+ * per weight matrix, when the weights are loaded.
+ *   W, Wp: fp32 device arrays, 16-byte aligned, not overlapping.
+ * Errors: GDN_EINVAL for a null or misaligned pointer, R <= 0, C <= 0 or
+ * overlapping arrays; GDN_EUNSUPPORTED when C is not a multiple of 128 or R
+ * not a multiple of 16.
+ */
+int gdn_proj_pack(const float *W, float *Wp, int32_t R, int32_t C, void *stream);
+
+/*
+ * Dense projections of the layer: y0[r][o] = sum over c of W0[o][c] * x[r][c]
+ * for r < rows, o < R0 and, when W1 is non-null, y1 likewise from W1 [R1][C]
+ * in the same launch (the two input projections share x).
+ * ("Kestrel_VLLM #24", Fig. 1 caption, steps 1 and 7: in_proj_qkv gives the
+ * conv input, in_proj_z the output gate, out_proj maps the gated output back
+ * to the model width; "Kestrel_VLLM #34", section 3.6: the projections take
+ * all draft rows at once and read the weights once.)
+ *   x  [rows][C] row-major; y0 [rows][R0]; y1 [rows][R1];
+ *   W0, W1: R x C weights in the packed order of gdn_proj_pack
+ *   (fp32 device arrays, 16-byte aligned; W1 == NULL requires R1 == 0 and
+ *   y1 == NULL).
+ * Each row's result is independent of the other rows in the call and of the
+ * row count, bit for bit: one call over M rows equals M one-row calls.  The
+ * sum over c runs in a fixed order of fp32 operations (8 equal segments of C,
+ * each an ascending chain of matrix-core steps, then folded left to right),
+ * so it differs from a left fold by rounding only.
+ * Ownership: every buffer belongs to the caller; nothing is allocated.
+ * Errors: GDN_EINVAL for a null or misaligned pointer, rows < 0, C <= 0,
+ * R <= 0, or an output overlapping an input or the other output;
+ * GDN_EUNSUPPORTED when C is not a multiple of 128, R not a multiple of 16,
+ * or the launch would exceed the grid limit.  rows == 0 is a no-op.
+ */
+int gdn_proj(const float *x, int64_t rows, int32_t C,
+             const float *W0, int32_t R0, float *y0,
+             const float *W1, int32_t R1, float *y1, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,8 @@ GPU", section 6, at vh=48, kh=16, kd=vd=128, dim=5120, ck=4):
   "alpha-uniform" variant: alpha ~ U[0.5, 1], g = ln(alpha), beta ~ U(0, 1)
 Front end: x ~ N(0, 1) [B][dim]; Wa, Wb ~ N(0, 0.01) [vh][dim]; raw conv
 input and initial history ~ N(0, 1); conv_w, A_log, dt_bias ~ N(0, 0.5).
+Projections (in_proj_qkv, in_proj_z, out_proj) ~ N(0, 0.02); gated-norm
+weight ~ 1 + N(0, 0.1).
 The transforms run in float64 and are rounded once to fp32.
 """
 from __future__ import annotations
@@ -101,6 +103,20 @@ def frontend_weights(gen, dims, dim=FE_DIM, ck=CONV_K, device="cpu"):
     )
 
 
+def proj_weights(gen, dims, dim=FE_DIM, std=0.02, device="cpu"):
+    """Projection weights of one layer, all ~ N(0, std): W_qkv [conv_dim][dim]
+    (conv input), W_z [vh*vd][dim] (output gate), W_out [dim][vh*vd]; and the
+    gated-norm weight norm_w [vd] ~ 1 + N(0, 0.1)."""
+    vh, kh, kd, vd = dims
+    cd = conv_dim_of(dims)
+    return dict(
+        W_qkv=_normal(gen, (cd, dim), std, device),
+        W_z=_normal(gen, (vh * vd, dim), std, device),
+        W_out=_normal(gen, (dim, vh * vd), std, device),
+        norm_w=1.0 + _normal(gen, (vd,), 0.1, device),
+    )
+
+
 def frontend_inputs(gen, B, dims, T=1, dim=FE_DIM, ck=CONV_K, device="cpu"):
     """x [T][B][dim] ~ N(0,1); raw conv input xc_raw [T][B][conv_dim] ~ N(0,1);
     initial history hist [B][ck-1][conv_dim] ~ N(0,1)."""
@@ -130,4 +146,8 @@ WORKLOADS = {
             seqs=128, layers=1, dims=DIMS128, M=8, gate=None, seed=6),
     7: dict(name="batched decode with gated RMSNorm output, 64 sequences x 48 layers",
             seqs=64, layers=48, dims=DIMS128, steps=100, gate="softplus", seed=7, gated=True),
+    8: dict(name="whole-layer decode with f32 projections, 1 sequence x 8 layers",
+            seqs=1, layers=8, dims=DIMS128, gate=None, seed=8),
+    9: dict(name="whole-layer decode with f32 projections, 64 sequences x 8 layers",
+            seqs=64, layers=8, dims=DIMS128, gate=None, seed=9),
 }

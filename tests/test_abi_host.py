@@ -201,6 +201,50 @@ def test_stream_copy_validation():
     assert L.gdn_stream_copy(fp(0), fp(1 << 20), 0, NULLS) == gdn.GDN_OK
 
 
+def test_proj_validation():
+    """gdn_proj refuses bad shapes, pointers and overlaps before any launch."""
+    L = gdn.lib()
+    x, W0, y0, W1, y1 = (fp(i << 36) for i in range(5))
+    ok = (x, 4, 5120, W0, 10240, y0, W1, 6144, y1, NULLS)
+    args = list(ok)
+    args[2] = 5120 + 64                                  # C not a multiple of 128
+    assert L.gdn_proj(*args) == gdn.GDN_EUNSUPPORTED
+    args = list(ok)
+    args[4] = 10248                                      # R0 not a multiple of 16
+    assert L.gdn_proj(*args) == gdn.GDN_EUNSUPPORTED
+    args = list(ok)
+    args[7] = 6152
+    assert L.gdn_proj(*args) == gdn.GDN_EUNSUPPORTED
+    for i, bad in ((1, -1), (2, 0), (4, 0), (7, 0)):
+        args = list(ok)
+        args[i] = bad
+        assert L.gdn_proj(*args) == gdn.GDN_EINVAL, (i, bad)
+    assert L.gdn_proj(x, 4, 5120, W0, 10240, y0, NULLS, 16, NULLS, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj(x, 4, 5120, W0, 10240, y0, NULLS, 0, y1, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj(x, 4, 5120, NULLS, 10240, y0, NULLS, 0, NULLS, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj(fp(4), 4, 5120, W0, 10240, y0, NULLS, 0, NULLS, NULLS) == gdn.GDN_EINVAL
+    # outputs overlapping an input or each other
+    assert L.gdn_proj(x, 4, 5120, W0, 10240, fp(64), NULLS, 0, NULLS, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj(x, 4, 5120, W0, 10240, y0, W1, 6144, fp((2 << 36) + 256),
+                      NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj(x, 4, 5120, W0, 10240, y0, W1, 6144, fp((3 << 36) + 1024),
+                      NULLS) == gdn.GDN_EINVAL
+    # no rows: nothing to do, nothing launched
+    assert L.gdn_proj(x, 0, 5120, W0, 10240, y0, W1, 6144, y1, NULLS) == gdn.GDN_OK
+
+
+def test_proj_pack_validation():
+    L = gdn.lib()
+    W, Wp = fp(0), fp(1 << 36)
+    assert L.gdn_proj_pack(W, Wp, 10240, 5120 + 64, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_proj_pack(W, Wp, 10248, 5120, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_proj_pack(W, Wp, 0, 5120, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_pack(W, Wp, 16, -128, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_pack(W, fp(4096), 16, 128, NULLS) == gdn.GDN_EINVAL     # overlap
+    assert L.gdn_proj_pack(fp(8), Wp, 16, 128, NULLS) == gdn.GDN_EINVAL       # misaligned
+    assert L.gdn_proj_pack(NULLS, Wp, 16, 128, NULLS) == gdn.GDN_EINVAL
+
+
 def test_max_rel_metric_matches_pages_row():
     gold = json.load(open(os.path.join(GOLD, "max_rel_p24.json")))
     r = np.array([gold["max_abs_ref"], -3.0, 1.0])

@@ -1,0 +1,235 @@
+"""GPU parity of the dense layer projections (gdn_proj, on the matrix cores)
+and of one whole GDN layer decode step assembled from the C ABI.
+
+Floating point: per element |y - r| <= max(1e-5 |r|, 1e-6 sum_c |W[o][c] x[c]|).
+The second term is the rounding budget of a length-C fp32 dot product taken in
+a different order than the oracle's left fold (typically ~5e-8 of that sum);
+a dropped or misplaced term costs ~2e-4 of it.  Bit-exact: a row's result
+against the same row in calls with other row counts (every tile shape), one
+launch of two products against two launches, one-hot rows against the weight
+column, the packed weight order against its index definition.  The
+whole-layer chain is also compared end to end with the pages' layer
+criterion, max|err| / max|ref| <= 1e-4 ("Kestrel_VLLM #24", section 6).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_recurrent_amd as gdn
+import synth
+from tests.helpers import assert_close, bits_equal, max_rel_pages
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "g", "beta")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    gdn.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def host(t):
+    return np.ascontiguousarray(t.detach().cpu().numpy())
+
+
+def pack_np(W):
+    """The packed order gdn_proj_pack documents, by index arithmetic on the
+    host: slab s, column block kb, lane l = 16 (c4) + j, element i."""
+    R, C = W.shape
+    return np.ascontiguousarray(
+        W.reshape(R // 16, 16, C // 16, 4, 4).transpose(0, 2, 3, 1, 4).reshape(R, C))
+
+
+def ref_proj(orc, x, W):
+    y = np.zeros((x.shape[0], W.shape[0]), np.float32)
+    orc.proj(np.ascontiguousarray(x), np.ascontiguousarray(W), y)
+    return y
+
+
+def proj_floor(x, W):
+    return 1e-6 * (np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T)
+
+
+def operands(seed, rows, R, C):
+    gen = synth.make_gen(seed, "cuda")
+    W = 0.02 * torch.randn((R, C), generator=gen, device="cuda")
+    x = torch.randn((rows, C), generator=gen, device="cuda")
+    return x, W
+
+
+@pytest.mark.parametrize("rows,R,C", [(1, 64, 128), (5, 48, 640), (16, 256, 1024),
+                                      (17, 128, 512), (40, 96, 1152), (64, 512, 5120),
+                                      (70, 160, 6144)])
+def test_proj_parity(orc, rows, R, C):
+    """Every tile shape (1, 2 and 4 row blocks; ragged last row group;
+    segments with and without a tail) against the oracle."""
+    say(f"proj rows={rows} R={R} C={C}")
+    x, W = operands(20 + rows, rows, R, C)
+    y = gdn.proj(x, gdn.proj_pack(W))
+    xh, Wh = host(x), host(W)
+    assert_close(host(y), ref_proj(orc, xh, Wh), f"proj {rows}x{R}x{C}", rel=1e-5,
+                 floor=proj_floor(xh, Wh))
+
+
+def test_proj_rows_are_independent_bit_exact():
+    """A row gives the same bits whatever else shares the call: one call over
+    70 rows (4 row blocks per tile, ragged tail) against calls over 1, 6, 16
+    and 32 rows (1 and 2 row blocks per tile)."""
+    say("proj row independence")
+    rows, R, C = 70, 96, 1536
+    x, W = operands(31, rows, R, C)
+    Wp = gdn.proj_pack(W)
+    full = host(gdn.proj(x, Wp))
+    for lo, hi in ((0, 1), (5, 6), (69, 70), (64, 70), (0, 16), (16, 48), (30, 62)):
+        part = host(gdn.proj(x[lo:hi].contiguous(), Wp))
+        assert bits_equal(part, np.ascontiguousarray(full[lo:hi])), (lo, hi)
+
+
+def test_proj_one_hot_rows_select_weight_columns():
+    """x = e_c gives column c of W exactly (every other term is +0)."""
+    say("proj one-hot")
+    R, C = 64, 1024
+    _, W = operands(37, 1, R, C)
+    cols = [0, 1, 127, 128, 511, 640, C - 1]
+    x = torch.zeros((len(cols), C), device="cuda")
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = host(gdn.proj(x, gdn.proj_pack(W)))
+    Wh = host(W)
+    for i, c in enumerate(cols):
+        assert bits_equal(y[i], np.ascontiguousarray(Wh[:, c])), c
+
+
+def test_proj_two_products_share_one_launch():
+    """in_proj_qkv and in_proj_z in one launch equal two separate launches."""
+    say("proj paired")
+    rows, C = 9, 640
+    x, W0 = operands(41, rows, 160, C)
+    _, W1 = operands(43, rows, 48, C)
+    W0, W1 = gdn.proj_pack(W0), gdn.proj_pack(W1)
+    y0, y1 = gdn.proj(x, W0, W1)
+    assert bits_equal(host(y0), host(gdn.proj(x, W0)))
+    assert bits_equal(host(y1), host(gdn.proj(x, W1)))
+
+
+@pytest.mark.parametrize("R,C", [(16, 128), (48, 640), (10240, 5120), (5120, 6144)])
+def test_proj_pack_layout(R, C):
+    """gdn_proj_pack is the documented permutation, bit for bit."""
+    say(f"proj_pack R={R} C={C}")
+    _, W = operands(59, 1, R, C)
+    assert bits_equal(host(gdn.proj_pack(W)), pack_np(host(W)))
+
+
+def test_proj_no_rows_is_a_no_op():
+    x = torch.empty((0, 512), device="cuda")
+    W = gdn.proj_pack(torch.ones((32, 512), device="cuda"))
+    y = torch.full((0, 32), 7.0, device="cuda")
+    assert gdn.proj(x, W, y0=y).numel() == 0
+
+
+@pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
+def test_proj_layer_sizes_sampled(orc, dims):
+    """The layer's full projection sizes at 64 rows, in the launches the
+    benchmark times (in_proj_qkv + in_proj_z paired, then out_proj), checked
+    on sampled rows that the oracle recomputes."""
+    say(f"proj layer sizes dims={dims}")
+    vh, kh, kd, vd = dims
+    rows, dim = 64, synth.FE_DIM
+    gen = synth.make_gen(47, "cuda")
+    w = synth.proj_weights(gen, dims, device="cuda")
+    x = torch.randn((rows, dim), generator=gen, device="cuda")
+    h = torch.randn((rows, vh * vd), generator=gen, device="cuda")
+    wp = {n: gdn.proj_pack(w[n]) for n in ("W_qkv", "W_z", "W_out")}
+    xc, z = gdn.proj(x, wp["W_qkv"], wp["W_z"])
+    y = gdn.proj(h, wp["W_out"])
+    pick = [0, 29, 63]
+    xh, hh = host(x)[pick], host(h)[pick]
+    for name, got, inp, W in (("W_qkv", xc, xh, w["W_qkv"]), ("W_z", z, xh, w["W_z"]),
+                              ("W_out", y, hh, w["W_out"])):
+        Wh = host(W)
+        assert_close(host(got)[pick], ref_proj(orc, inp, Wh), name, rel=1e-5,
+                     floor=proj_floor(inp, Wh))
+
+
+def test_layer_decode_chain(orc):
+    """One GDN layer, two tokens, B sequences, entirely through the C ABI:
+    in_proj_qkv + in_proj_z -> front end (gate/beta, conv + SiLU, split, norms)
+    -> step with the gated RMSNorm -> out_proj.  Each stage matches the oracle
+    run on the GPU's own inputs to that stage; the whole chain matches the
+    oracle's chain under the pages' layer criterion; state and history
+    advance as the oracle's do."""
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    B, dim, T, eps = 3, 512, 2, 1e-6
+    cd = synth.conv_dim_of(dims)
+    say(f"layer chain B={B} dim={dim} T={T}")
+    gen = synth.make_gen(53, "cuda")
+    pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
+    fw = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
+    S = synth.state(gen, B, dims, device="cuda")
+    hist = torch.randn((B, 3, cd), generator=gen, device="cuda")
+    xs = torch.randn((T, B, dim), generator=gen, device="cuda")
+    W = {n: host(t) for n, t in {**pw, **fw}.items()}
+    wp = {n: gdn.proj_pack(pw[n]) for n in ("W_qkv", "W_z", "W_out")}
+    S_ref, hist_ref = host(S), host(hist)
+    for t in range(T):
+        x = xs[t]
+        xc, z = gdn.proj(x, wp["W_qkv"], wp["W_z"])
+        hist_in = host(hist)
+        fe = gdn.frontend(x, fw["Wa"], fw["Wb"], fw["A_log"], fw["dt_bias"], xc, hist,
+                          fw["conv_w"], dims)
+        S_in = host(S)
+        out = gdn.step_gated(S, *(fe[n].unsqueeze(0) for n in NAMES),
+                             z.view(1, B, vh, vd), pw["norm_w"], eps)
+        y = gdn.proj(out.view(B, vh * vd), wp["W_out"])
+
+        # stage by stage, the oracle fed the GPU's own stage inputs
+        xh = host(x)
+        assert_close(host(xc), ref_proj(orc, xh, W["W_qkv"]), "xc_raw", rel=1e-5,
+                     floor=proj_floor(xh, W["W_qkv"]))
+        assert_close(host(z), ref_proj(orc, xh, W["W_z"]), "z", rel=1e-5,
+                     floor=proj_floor(xh, W["W_z"]))
+        ref = {n: np.zeros(host(fe[n]).shape, np.float32) for n in NAMES}
+        orc.gdn_frontend(xh, W["Wa"], W["Wb"], W["A_log"], W["dt_bias"], host(xc), hist_in,
+                         W["conv_w"], ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"], dims)
+        for n in NAMES:
+            assert_close(host(fe[n]), ref[n], f"front end {n}")
+        assert bits_equal(host(hist), hist_in)
+        o_ref = np.zeros((B, vh, vd), np.float32)
+        orc.gdn_step(S_in, *(host(fe[n]) for n in NAMES), o_ref, dims)
+        g_ref = np.zeros_like(o_ref)
+        orc.gated_norm(o_ref, host(z).reshape(B, vh, vd), W["norm_w"], eps, g_ref)
+        o64, z64 = o_ref.astype(np.float64), host(z).reshape(B, vh, vd).astype(np.float64)
+        rinv = 1.0 / np.sqrt(np.mean(o64 ** 2, axis=-1, keepdims=True) + eps)
+        scale = np.abs(rinv * W["norm_w"].astype(np.float64) * z64 / (1.0 + np.exp(-z64)))
+        assert_close(host(out)[0], g_ref, "gated out", rel=1e-5, floor=1e-6 * scale)
+        assert_close(host(S), S_in, "state", rel=1e-5, floor=1e-6)
+        oh = host(out).reshape(B, vh * vd)
+        assert_close(host(y), ref_proj(orc, oh, W["W_out"]), "y", rel=1e-5,
+                     floor=proj_floor(oh, W["W_out"]))
+
+        # the oracle's own chain from the initial inputs
+        xc_r = ref_proj(orc, xh, W["W_qkv"])
+        z_r = ref_proj(orc, xh, W["W_z"])
+        fr = {n: np.zeros(ref[n].shape, np.float32) for n in NAMES}
+        orc.gdn_frontend(xh, W["Wa"], W["Wb"], W["A_log"], W["dt_bias"], xc_r, hist_ref,
+                         W["conv_w"], fr["q"], fr["k"], fr["v"], fr["g"], fr["beta"], dims)
+        o_r = np.zeros((B, vh, vd), np.float32)
+        orc.gdn_step(S_ref, *(fr[n] for n in NAMES), o_r, dims)
+        gn_r = np.zeros_like(o_r)
+        orc.gated_norm(o_r, z_r.reshape(B, vh, vd), W["norm_w"], eps, gn_r)
+        y_r = ref_proj(orc, gn_r.reshape(B, vh * vd), W["W_out"])
+        for b in range(B):
+            assert max_rel_pages(host(y)[b], y_r[b]) <= 1e-4, (t, b)
+        assert max_rel_pages(host(S), S_ref) <= 1e-4
+        assert bits_equal(host(hist), hist_ref) or max_rel_pages(host(hist), hist_ref) <= 1e-4
