@@ -52,31 +52,39 @@ def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
     return state + per_row
 
 
-RECUR_END_MARK = b"// Streaming copy"
+# The parts of the kernel source each measured kernel is built from (shared
+# helpers at the top, then its own section), so that an edit elsewhere in the
+# file does not invalidate its recorded counters.
+HASH_SECTIONS = {
+    "recur_wide_kernel": ((None, b"// Streaming copy"),),
+    "proj_kernel": ((None, b"// Recurrence\n"), (b"// Dense layer projections", None)),
+}
 
 
-def kernel_hash():
-    """sha256[:16] of the part of the kernel source the recurrence kernels are
-    built from: the shared helpers and the recurrence section (everything
-    before the streaming-copy section)."""
+def kernel_hash(kernel="recur_wide_kernel"):
+    """sha256[:16] of the kernel-source sections `kernel` is built from."""
     src = open(KERNEL_SRC, "rb").read()
-    cut = src.find(RECUR_END_MARK)
-    if cut < 0:
-        raise RuntimeError("kernel source layout changed: streaming-copy marker not found")
-    return hashlib.sha256(src[:cut]).hexdigest()[:16]
+    h = hashlib.sha256()
+    for start, end in HASH_SECTIONS[kernel]:
+        a = 0 if start is None else src.find(start)
+        b = len(src) if end is None else src.find(end)
+        if a < 0 or b < 0:
+            raise RuntimeError(f"kernel source layout changed: section marker of {kernel} not found")
+        h.update(src[a:b])
+    return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload_key, launches_bytes):
+def recorded_traffic(workload_key, launches_bytes, kernel="recur_wide_kernel"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"recur_wide_kernel_{workload_key}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_key}_counters.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", open(path).read(), flags=re.M)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_sha256_16") != kernel_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -440,6 +448,9 @@ def bench_layer(cfg, steps, warmup, cpu):
                   steps, 1)
     h = out.view(B, vh * vd)
     dt_out = timed(lambda i: [gdn.proj(h, w["W_out"], y0=xs[0]) for w in layers], steps, 1)
+    # read+write floor over one packed weight matrix (also calibrates counters)
+    flat = layers[0]["W_qkv"].view(-1)
+    floor = copy_floor(layers[0]["W_qkv"])
     w_in = (cd + vh * vd) * dim * 4
     w_out = dim * vh * vd * 4
     in_bytes = w_in + B * dim * 4 + B * (cd + vh * vd) * 4
@@ -447,15 +458,17 @@ def bench_layer(cfg, steps, warmup, cpu):
     in_flop = 2 * B * (cd + vh * vd) * dim
     out_flop = 2 * B * dim * vh * vd
     t_in, t_out = dt_in / (steps * L), dt_out / (steps * L)
+    key = f"layer_b{B}"
     ridge = PEAK_MFMA_F32_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)     # ~19.7 flop/B
     if in_flop / in_bytes >= ridge:   # 2B flop per 4-byte weight: matrix cores from B ~ 40
         roof = dict(bound="mfma", achieved=round(in_flop / t_in / 1e12, 2),
                     peak=PEAK_MFMA_F32_TFLOPS, unit="TFLOP/s",
-                    frac=round(in_flop / t_in / 1e12 / PEAK_MFMA_F32_TFLOPS, 4), traffic=None)
+                    frac=round(in_flop / t_in / 1e12 / PEAK_MFMA_F32_TFLOPS, 4),
+                    traffic=recorded_traffic(key, in_bytes, kernel="proj_kernel"))
     else:
         roof = dict(bound="hbm", achieved=round(in_bytes / t_in / 1e9, 1), peak=PEAK_HBM_GBPS,
                     unit="GB/s", frac=round(in_bytes / t_in / 1e9 / PEAK_HBM_GBPS, 4),
-                    traffic=None)
+                    traffic=recorded_traffic(key, in_bytes, kernel="proj_kernel"))
     res = dict(value=B * vh * L * steps / dt, ms_per_step=dt / steps * 1e3, roofline=roof,
                extra=dict(kernel="proj_kernel (in_proj_qkv + in_proj_z, one launch)",
                           in_proj_us=round(t_in * 1e6, 2), out_proj_us=round(t_out * 1e6, 2),
@@ -465,7 +478,9 @@ def bench_layer(cfg, steps, warmup, cpu):
                           out_proj_TFLOPs=round(out_flop / t_out / 1e12, 2),
                           layer_us=round(dt / (steps * L) * 1e6, 2),
                           in_proj_bytes_per_launch=in_bytes, in_proj_flop_per_launch=in_flop,
-                          weights_GB=round(L * (w_in + w_out) / 1e9, 3)))
+                          weights_GB=round(L * (w_in + w_out) / 1e9, 3),
+                          copy_floor_GBps=round(floor, 1), copy_bytes=flat.numel() * 4,
+                          kernel_source_sha256_16=kernel_hash("proj_kernel")))
     return res, dict(workload=cfg["name"], units=B * L, seqs=B, layers=L, vh=vh, kd=kd,
                      dim=dim, conv_dim=cd,
                      chain="gdn_proj(W_qkv, W_z) + gdn_frontend + gdn_step_gated + "
