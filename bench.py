@@ -52,12 +52,13 @@ def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
     return state + per_row
 
 
-# The parts of the kernel source each measured kernel is built from (shared
-# helpers at the top, then its own section), so that an edit elsewhere in the
-# file does not invalidate its recorded counters.
+# The parts of the kernel source each measured kernel is built from (the
+# shared helpers after the file's header comment, then its own section), so
+# that an edit elsewhere in the file does not invalidate its recorded
+# counters.
 HASH_SECTIONS = {
-    "recur_wide_kernel": ((None, b"// Streaming copy"),),
-    "proj_kernel": ((None, b"// Recurrence\n"), (b"// Dense layer projections", None)),
+    "recur_wide_kernel": ((b"namespace gdn {", b"// Streaming copy"),),
+    "proj_kernel": ((b"namespace gdn {", b"// Recurrence\n"), (b"// Dense layer projections", None)),
 }
 
 

@@ -7,12 +7,16 @@
 // not by arithmetic, and uses no MFMA.  The design streams each 64 KiB state
 // tile through VGPRs exactly once per call:
 //
-//  * one workgroup per tile (unit, value head); every lane holds 16 floats
+//  * one lane group per tile (unit, value head); every lane holds 16 floats
 //    of it: 4 adjacent columns (dv = 4*(t % (kd/4)) .. +3) of the rows
 //    dk = rg + RG*j, j = 0..3, rg = t / (kd/4), RG = lanes / (kd/4) row groups.
-//    kd = 128 uses 1024 lanes (16 wave64), kd = 64 uses 256.  A wave-wide
-//    128-bit load covers 1 KiB of consecutive rows, so every state access is
-//    a fully coalesced global_load_dwordx4, all issued before any arithmetic.
+//    kd = 128 uses 1024 lanes (16 wave64) per tile and one tile per
+//    workgroup; kd = 64 uses 256 lanes per tile and four adjacent tiles of
+//    one unit per workgroup, so that every workgroup streams 64 KiB of
+//    consecutive state (one 16 KiB tile per workgroup measured 2.8% slower).
+//    A wave-wide 128-bit load covers 1 KiB of consecutive rows, so every state
+//    access is a fully coalesced global_load_dwordx4, all issued before any
+//    arithmetic.
 //  * the key/query read-outs (sums over dk) are done per lane over its rows,
 //    folded inside each wave with cross-lane shuffles, and finished by wave 0
 //    from one LDS partial per wave, in a fixed order.
@@ -311,9 +315,10 @@ struct TileIdx {
   int head, hh, steps;
 };
 
-static __device__ __forceinline__ TileIdx tile_index(const RecurArgs &a, int kdkd) {
+static __device__ __forceinline__ TileIdx tile_index(const RecurArgs &a, int kdkd, int tpw = 1,
+                                                     int sub = 0) {
   TileIdx x;
-  const int64_t tile = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t tile = xcd_contiguous(blockIdx.x, gridDim.x) * tpw + sub;
   x.unit = tile / a.vh;
   x.head = (int)(tile - x.unit * a.vh);
   x.hh = x.head / (a.vh / a.kh);
@@ -329,25 +334,33 @@ static __device__ __forceinline__ TileIdx tile_index(const RecurArgs &a, int kdk
 // ----- wide geometry -------------------------------------------------------
 //
 // Serves single-step calls (M = 1; rollback with M = 1 runs 0 or 1 step per
-// unit).  Decay and S^T k partials; barrier; wave 0 finishes S^T k and forms
-// tmp = (v - kv) beta; barrier; rank-1 update and S^T q partials; barrier;
-// wave 0 finishes the output.  kd = 128: at most 64 VGPRs (8 waves per SIMD),
-// so two 16-wave workgroups share a CU.
-template <int KD, bool RESIDENT, bool GATED>
-__global__ __launch_bounds__(Geo<KD>::LANES) __attribute__((amdgpu_waves_per_eu(KD == 128 ? 8 : 6)))
+// unit).  Decay and S^T k partials; barrier; wave 0 of each tile finishes
+// S^T k and forms tmp = (v - kv) beta; barrier; rank-1 update and S^T q
+// partials; barrier; wave 0 of each tile finishes the output.  TPW tiles of
+// one unit share a workgroup (lane group t / Geo::LANES owns tile TPW*b + that
+// index), so every lane group takes the same branches and barriers.
+// kd = 128: at most 64 VGPRs (8 waves per SIMD), so two 16-wave workgroups
+// share a CU.
+template <int KD, bool RESIDENT, bool GATED, int TPW>
+__global__ __launch_bounds__(Geo<KD>::LANES * TPW) __attribute__((amdgpu_waves_per_eu(KD == 128 ? 8 : 6)))
 void recur_wide_kernel(RecurArgs a) {
   using G = Geo<KD>;
   constexpr int LANES = G::LANES;
-  __shared__ Stage<KD, GATED> sb;
-  __shared__ f4 s_red_k[G::NW][G::CG];
-  __shared__ f4 s_red_o[G::NW][G::CG];
-  __shared__ f4 s_tmp[G::CG];
+  __shared__ Stage<KD, GATED> sb_all[TPW];
+  __shared__ f4 s_red_k_all[TPW][G::NW][G::CG];
+  __shared__ f4 s_red_o_all[TPW][G::NW][G::CG];
+  __shared__ f4 s_tmp_all[TPW][G::CG];
 
-  const int t = threadIdx.x;
+  const int sub = TPW == 1 ? 0 : (int)threadIdx.x / LANES;   // tile of this lane group
+  const int t = TPW == 1 ? (int)threadIdx.x : (int)threadIdx.x % LANES;
+  Stage<KD, GATED> &sb = sb_all[sub];
+  f4 (*s_red_k)[G::CG] = s_red_k_all[sub];
+  f4 (*s_red_o)[G::CG] = s_red_o_all[sub];
+  f4 *s_tmp = s_tmp_all[sub];
   const int lane = t & 63, wave = t >> 6;
   const int cg = t % G::CG, rg = t / G::CG;
-  const TileIdx ti = tile_index(a, KD * KD);
-  const bool run = ti.steps > 0;       // uniform per workgroup
+  const TileIdx ti = tile_index(a, KD * KD, TPW, sub);
+  const bool run = ti.steps > 0;       // uniform per workgroup (its tiles share a unit)
   // an in-place update with nothing to run leaves the tile as it is
   if (!run && a.S_src == a.S_dst && a.snap == nullptr) return;
   const rsrc_t src = buf_rsrc(a.S_src + ti.tile_off, KD * KD * 4);
@@ -568,10 +581,24 @@ template <int KD, bool GATED>
 static void launch_recur_kd(const RecurArgs &a, int64_t tiles, hipStream_t s) {
   const dim3 grid((unsigned)tiles);
   if (a.M == 1) {
-    if (tiles * KD * KD * 4 <= RESIDENT_MAX_BYTES)
-      hipLaunchKernelGGL((recur_wide_kernel<KD, true, GATED>), grid, dim3(Geo<KD>::LANES), 0, s, a);
-    else
-      hipLaunchKernelGGL((recur_wide_kernel<KD, false, GATED>), grid, dim3(Geo<KD>::LANES), 0, s, a);
+    // kd = 64: four adjacent heads of one unit per workgroup, so that a
+    // workgroup streams 64 KiB of consecutive state like a kd = 128 one
+    constexpr int TPW = KD == 64 ? 4 : 1;
+    if (TPW > 1 && a.vh % TPW == 0) {
+      const dim3 g4((unsigned)(tiles / TPW));
+      if (tiles * KD * KD * 4 <= RESIDENT_MAX_BYTES)
+        hipLaunchKernelGGL((recur_wide_kernel<KD, true, GATED, TPW>), g4,
+                           dim3(Geo<KD>::LANES * TPW), 0, s, a);
+      else
+        hipLaunchKernelGGL((recur_wide_kernel<KD, false, GATED, TPW>), g4,
+                           dim3(Geo<KD>::LANES * TPW), 0, s, a);
+    } else if (tiles * KD * KD * 4 <= RESIDENT_MAX_BYTES) {
+      hipLaunchKernelGGL((recur_wide_kernel<KD, true, GATED, 1>), grid, dim3(Geo<KD>::LANES), 0,
+                         s, a);
+    } else {
+      hipLaunchKernelGGL((recur_wide_kernel<KD, false, GATED, 1>), grid, dim3(Geo<KD>::LANES), 0,
+                         s, a);
+    }
   } else {
     if (a.M <= MC)
       hipLaunchKernelGGL((recur_deep_kernel<KD, false, GATED>), grid, dim3(Deep<KD>::LANES), 0, s, a);
