@@ -1100,8 +1100,10 @@ struct ProjArgs {
 typedef float pj_acc __attribute__((ext_vector_type(4)));
 
 // Weight loads: with a single row group each weight is read exactly once, so
-// it is streamed past the caches (nt) and leaves L2 to x; with several row
-// groups the default policy lets the groups sharing a slab hit in L2.
+// it is streamed past the caches (nt) and leaves L2 to x.  Tiles of 4 row
+// blocks over several row groups use the default policy, so that the groups
+// sharing a slab hit in L2; tiles of 1 or 2 row blocks (at most two row
+// groups by the shape rule below) measured faster streaming.
 template <bool STREAM>
 static __device__ __forceinline__ f4 ld_w(rsrc_t r, int voff) {
   return __builtin_bit_cast(
@@ -1206,43 +1208,51 @@ __global__ __launch_bounds__(PJ_LANES) void proj_kernel(ProjArgs a) {
   }
 }
 
-// Tile shape of a call: row blocks per tile by the row count; then the
-// widest output slab group (1, 2 or 4 slabs of 16) that divides both R / 16
-// and still leaves enough workgroups: with one row block the call streams the
-// weights and needs >= GDN_PJ_MIN_WG1 workgroups to spread that stream over
-// every CU; with more rows it is bound by the matrix cores and x traffic, and
-// >= GDN_PJ_MIN_WG suffice.  More slabs per wave share each x load among more
-// outputs.  The choice never changes a result (canonical summation above).
+// Tile shape of a call.  Up to 16 rows (one row block) the call streams the
+// weights: the widest output slab group (1, 2 or 4 slabs of 16) dividing
+// R / 16 that still leaves >= GDN_PJ_MIN_WG1 workgroups, to spread the stream
+// over every CU.  Beyond 16 rows it is bound by the matrix cores and by x
+// traffic: the widest slab group dividing R / 16 (each x load then serves
+// more outputs), then the most row blocks per tile (up to the rows present)
+// that still leave >= GDN_PJ_MIN_WG workgroups.  Measured at 64 rows:
+// out_proj (R = 5120) 2 row blocks x 4 slabs 70 us, 4 x 2 96 us, 4 x 4
+// 128 us; in_proj 4 x 4 128 us.  The choice never changes a result
+// (canonical summation above).
 struct ProjShape {
   int rb, oj, row_groups;
 };
 
+static int64_t proj_tiles(int64_t rows, int R0, int R1, int rb, int oj) {
+  const int64_t groups = (rows + 16 * rb - 1) / (16 * rb);
+  return ((int64_t)R0 / (16 * oj) + (int64_t)R1 / (16 * oj)) * groups;
+}
+
 static ProjShape proj_shape(int64_t rows, int R0, int R1) {
   ProjShape sh;
-  sh.rb = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
-  sh.row_groups = (int)((rows + 16 * sh.rb - 1) / (16 * sh.rb));
-  const int64_t min_wg = sh.rb == 1 ? GDN_PJ_MIN_WG1 : GDN_PJ_MIN_WG;
+  const int rb_max = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
   sh.oj = 1;
   for (int oj = 4; oj > 1; oj >>= 1) {
     const bool divides = (R0 / 16) % oj == 0 && (R1 / 16) % oj == 0;
-    const int64_t wg = ((int64_t)R0 / (16 * oj) + (int64_t)R1 / (16 * oj)) * sh.row_groups;
-    if (divides && wg >= min_wg) {
+    if (divides && (rb_max > 1 || proj_tiles(rows, R0, R1, 1, oj) >= GDN_PJ_MIN_WG1)) {
       sh.oj = oj;
       break;
     }
   }
+  sh.rb = rb_max;
+  while (sh.rb > 1 && proj_tiles(rows, R0, R1, sh.rb, sh.oj) < GDN_PJ_MIN_WG) sh.rb >>= 1;
+  sh.row_groups = (int)((rows + 16 * sh.rb - 1) / (16 * sh.rb));
   return sh;
 }
 
 int64_t proj_workgroups(int64_t rows, int R0, int R1) {
   const ProjShape sh = proj_shape(rows, R0, R1);
-  return ((int64_t)R0 / (16 * sh.oj) + (int64_t)R1 / (16 * sh.oj)) * sh.row_groups;
+  return proj_tiles(rows, R0, R1, sh.rb, sh.oj);
 }
 
 template <int RB, int OJ, int U>
 static void launch_proj_t(const ProjArgs &a, bool stream, hipStream_t s) {
   const dim3 grid((unsigned)(a.p[0].blocks + a.p[1].blocks));
-  if (RB < 4 || stream)       // fewer than 4 row blocks: always one row group
+  if (RB < 4 || stream)       // see ld_w
     hipLaunchKernelGGL((proj_kernel<RB, OJ, U, true>), grid, dim3(PJ_LANES), 0, s, a);
   else
     hipLaunchKernelGGL((proj_kernel<RB, OJ, U, RB < 4>), grid, dim3(PJ_LANES), 0, s, a);
