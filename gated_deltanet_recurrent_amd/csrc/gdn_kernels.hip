@@ -1151,26 +1151,69 @@ __global__ __launch_bounds__(PJ_LANES) void proj_kernel(ProjArgs a) {
     for (int oj = 0; oj < OJ; oj++) acc[rb][oj] = pj_acc{0.f, 0.f, 0.f, 0.f};
 
   int kb = 0;
-  for (; kb + 16 * U <= seg; kb += 16 * U) {
-    f4 w[U][OJ], xv[U][RB];
+  if constexpr (RB == 1) {
+    // software-pipelined: the loads of trip i + 1 are issued before the
+    // MFMAs of trip i (same MFMA order as the plain loop below).  Measured
+    // 3-17% faster up to 16 rows (weights streamed at 6.6 TB/s); with 2 or 4
+    // row blocks the second set of operand registers costs more occupancy
+    // than it gains.
+    f4 wn[U][OJ], xn[U][RB];
+    auto issue = [&](int k) {
 #pragma unroll
-    for (int u = 0; u < U; u++)
+      for (int u = 0; u < U; u++)
 #pragma unroll
-      for (int oj = 0; oj < OJ; oj++) w[u][oj] = ld_w<STREAM>(wr, wo[oj] + (kb + 16 * u) * 64);
+        for (int oj = 0; oj < OJ; oj++) wn[u][oj] = ld_w<STREAM>(wr, wo[oj] + (k + 16 * u) * 64);
 #pragma unroll
-    for (int u = 0; u < U; u++)
-#pragma unroll
-      for (int rb = 0; rb < RB; rb++) xv[u][rb] = xon[rb] ? ld4(xp[rb] + kb + 16 * u) : splat(0.f);
-#pragma unroll
-    for (int u = 0; u < U; u++)
-#pragma unroll
-      for (int s = 0; s < 4; s++)
+      for (int u = 0; u < U; u++)
 #pragma unroll
         for (int rb = 0; rb < RB; rb++)
+          xn[u][rb] = xon[rb] ? ld4(xp[rb] + k + 16 * u) : splat(0.f);
+    };
+    if (16 * U <= seg) issue(0);
+    for (; kb + 16 * U <= seg; kb += 16 * U) {
+      f4 w[U][OJ], xv[U][RB];
 #pragma unroll
-          for (int oj = 0; oj < OJ; oj++)
-            acc[rb][oj] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u][rb][s], w[u][oj][s],
-                                                               acc[rb][oj], 0, 0, 0);
+      for (int u = 0; u < U; u++) {
+#pragma unroll
+        for (int oj = 0; oj < OJ; oj++) w[u][oj] = wn[u][oj];
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) xv[u][rb] = xn[u][rb];
+      }
+      if (kb + 32 * U <= seg) issue(kb + 16 * U);
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+#pragma unroll
+          for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+            for (int oj = 0; oj < OJ; oj++)
+              acc[rb][oj] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u][rb][s], w[u][oj][s],
+                                                                 acc[rb][oj], 0, 0, 0);
+    }
+  } else {
+    for (; kb + 16 * U <= seg; kb += 16 * U) {
+      f4 w[U][OJ], xv[U][RB];
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int oj = 0; oj < OJ; oj++) w[u][oj] = ld_w<STREAM>(wr, wo[oj] + (kb + 16 * u) * 64);
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+          xv[u][rb] = xon[rb] ? ld4(xp[rb] + kb + 16 * u) : splat(0.f);
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+#pragma unroll
+          for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+            for (int oj = 0; oj < OJ; oj++)
+              acc[rb][oj] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u][rb][s], w[u][oj][s],
+                                                                 acc[rb][oj], 0, 0, 0);
+    }
   }
   for (; kb < seg; kb += 16) {             // the rest of a segment, one block at a time
     f4 w[OJ], xv[RB];
