@@ -444,6 +444,17 @@ def bench_layer(cfg, steps, warmup, cpu):
             x = xs[l]
 
     dt = timed(one, steps, warmup)
+    # the same chain captured once as a HIP graph and replayed (no launch gaps
+    # from the host); it contains no memset node
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one(0)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one(0)
+    dt_g = timed(lambda i: graph.replay(), steps, 2)
     # the projections alone, layer after layer, for the kernel roofline
     dt_in = timed(lambda i: [gdn.proj(x0, w["W_qkv"], w["W_z"], y0=xc, y1=z) for w in layers],
                   steps, 1)
@@ -478,6 +489,7 @@ def bench_layer(cfg, steps, warmup, cpu):
                           in_proj_TFLOPs=round(in_flop / t_in / 1e12, 2),
                           out_proj_TFLOPs=round(out_flop / t_out / 1e12, 2),
                           layer_us=round(dt / (steps * L) * 1e6, 2),
+                          layer_us_graph_replay=round(dt_g / (steps * L) * 1e6, 2),
                           in_proj_bytes_per_launch=in_bytes, in_proj_flop_per_launch=in_flop,
                           weights_GB=round(L * (w_in + w_out) / 1e9, 3),
                           copy_floor_GBps=round(floor, 1), copy_bytes=flat.numel() * 4,
