@@ -69,10 +69,12 @@ def operands(seed, rows, R, C):
 
 @pytest.mark.parametrize("rows,R,C", [(1, 64, 128), (5, 48, 640), (16, 256, 1024),
                                       (17, 128, 512), (40, 96, 1152), (64, 512, 5120),
-                                      (70, 160, 6144)])
+                                      (70, 160, 6144), (150, 4096, 256), (48, 4096, 384)])
 def test_proj_parity(orc, rows, R, C):
-    """Every tile shape (1, 2 and 4 row blocks; ragged last row group;
-    segments with and without a tail) against the oracle."""
+    """Every tile shape against the oracle: 1, 2 and 4 row blocks, 1, 2 and 4
+    output slabs per wave, one and several row groups (150 x 4096: 4 row
+    blocks over 3 row groups, the weights read through L2), a ragged last row
+    group, segments with and without a tail."""
     say(f"proj rows={rows} R={R} C={C}")
     x, W = operands(20 + rows, rows, R, C)
     y = gdn.proj(x, gdn.proj_pack(W))
@@ -91,6 +93,20 @@ def test_proj_rows_are_independent_bit_exact():
     Wp = gdn.proj_pack(W)
     full = host(gdn.proj(x, Wp))
     for lo, hi in ((0, 1), (5, 6), (69, 70), (64, 70), (0, 16), (16, 48), (30, 62)):
+        part = host(gdn.proj(x[lo:hi].contiguous(), Wp))
+        assert bits_equal(part, np.ascontiguousarray(full[lo:hi])), (lo, hi)
+
+
+def test_proj_rows_are_independent_across_tile_shapes():
+    """The same, with an output count that lets the call pick 1, 2 and 4 row
+    blocks per tile and several row groups: 150 rows against slices of 1, 20,
+    33, 64 and 100 rows."""
+    say("proj row independence, large R")
+    rows, R, C = 150, 4096, 256
+    x, W = operands(71, rows, R, C)
+    Wp = gdn.proj_pack(W)
+    full = host(gdn.proj(x, Wp))
+    for lo, hi in ((7, 8), (0, 20), (100, 133), (30, 94), (50, 150)):
         part = host(gdn.proj(x[lo:hi].contiguous(), Wp))
         assert bits_equal(part, np.ascontiguousarray(full[lo:hi])), (lo, hi)
 
