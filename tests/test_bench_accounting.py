@@ -1,0 +1,33 @@
+"""The benchmark's byte and flop accounting, pinned to the sizes written out
+by hand (no GPU: only the arithmetic of bench.py is exercised)."""
+import bench
+import synth
+
+
+def test_head_step_bytes_kd128():
+    # S read + write 2*128*128*4, v 512, o 512, g + beta 8, q + k 2*128*4 / 3
+    assert abs(bench.head_step_bytes(synth.DIMS128) - (131072 + 512 + 512 + 8 + 1024 / 3)) < 1e-9
+    assert round(bench.head_step_bytes(synth.DIMS128), 2) == 132445.33
+
+
+def test_head_step_bytes_kd64():
+    assert abs(bench.head_step_bytes(synth.DIMS64) - (32768 + 256 + 256 + 8 + 512 / 3)) < 1e-9
+    assert round(bench.head_step_bytes(synth.DIMS64), 2) == 33458.67
+
+
+def test_m_step_bytes_share_one_state_pass():
+    # M rows: the state is read and written once for all rows
+    b8 = bench.head_step_bytes(synth.DIMS128, rows=8)
+    assert abs(b8 - (131072 / 8 + 512 + 512 + 8 + 1024 / 3)) < 1e-9
+
+
+def test_headline_launch_bytes():
+    # 64 sequences x 48 layers x 48 value heads per launch
+    hs = 64 * 48 * 48
+    assert hs == 147456
+    assert round(hs * bench.head_step_bytes(synth.DIMS128)) == 19529859072
+
+
+def test_kernel_hash_sections_exist():
+    for k in bench.HASH_SECTIONS:
+        assert len(bench.kernel_hash(k)) == 16
