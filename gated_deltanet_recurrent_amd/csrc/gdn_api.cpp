@@ -406,9 +406,17 @@ int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream
   return enq(gdn::launch_copy(dst, src, n_floats, (hipStream_t)stream));
 }
 
+// Projection size limits: a workgroup addresses its (at most 64) packed
+// weight rows with 32-bit byte offsets (64 * C * 4 < 2^31), and the packing
+// grid (R * C / 4 lanes) stays below 2^32.
+constexpr int32_t kProjMaxC = 1 << 22;
+constexpr int64_t kProjMaxRC = (int64_t)1 << 40;
+constexpr int64_t kProjMaxRows = (int64_t)1 << 31;
+
 int gdn_proj_pack(const float *W, float *Wp, int32_t R, int32_t C, void *stream) {
   if (R <= 0 || C <= 0) return GDN_EINVAL;
   if (C % 128 != 0 || R % 16 != 0) return GDN_EUNSUPPORTED;
+  if (C > kProjMaxC || (int64_t)R * C > kProjMaxRC) return GDN_EUNSUPPORTED;
   if (!ptr_ok(W) || !ptr_ok(Wp)) return GDN_EINVAL;
   const int64_t wb = (int64_t)R * C * 4;
   if (overlaps(W, wb, Wp, wb)) return GDN_EINVAL;
@@ -424,6 +432,9 @@ int gdn_proj(const float *x, int64_t rows, int32_t C, const float *W0, int32_t R
     return GDN_EINVAL;
   }
   if (C % 128 != 0 || R0 % 16 != 0 || (W1 != nullptr && R1 % 16 != 0)) return GDN_EUNSUPPORTED;
+  if (C > kProjMaxC || rows > kProjMaxRows || (int64_t)R0 * C > kProjMaxRC ||
+      (int64_t)R1 * C > kProjMaxRC)
+    return GDN_EUNSUPPORTED;
   if (rows == 0) return GDN_OK;
   if (!ptr_ok(x) || !ptr_ok(W0) || !ptr_ok(y0)) return GDN_EINVAL;
   if (W1 != nullptr && (!ptr_ok(W1) || !ptr_ok(y1))) return GDN_EINVAL;

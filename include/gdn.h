@@ -257,8 +257,8 @@ int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream
  * per weight matrix, when the weights are loaded.
  *   W, Wp: fp32 device arrays, 16-byte aligned, not overlapping.
  * Errors: GDN_EINVAL for a null or misaligned pointer, R <= 0, C <= 0 or
- * overlapping arrays; GDN_EUNSUPPORTED when C is not a multiple of 128 or R
- * not a multiple of 16.
+ * overlapping arrays; GDN_EUNSUPPORTED when C is not a multiple of 128, R not
+ * a multiple of 16, C > 2^22 or R * C > 2^40.
  */
 int gdn_proj_pack(const float *W, float *Wp, int32_t R, int32_t C, void *stream);
 
@@ -283,7 +283,8 @@ int gdn_proj_pack(const float *W, float *Wp, int32_t R, int32_t C, void *stream)
  * Errors: GDN_EINVAL for a null or misaligned pointer, rows < 0, C <= 0,
  * R <= 0, or an output overlapping an input or the other output;
  * GDN_EUNSUPPORTED when C is not a multiple of 128, R not a multiple of 16,
- * or the launch would exceed the grid limit.  rows == 0 is a no-op.
+ * C > 2^22, R * C > 2^40, rows > 2^31, or the launch would exceed the grid
+ * limit.  rows == 0 is a no-op.
  */
 int gdn_proj(const float *x, int64_t rows, int32_t C,
              const float *W0, int32_t R0, float *y0,

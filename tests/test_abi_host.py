@@ -229,6 +229,11 @@ def test_proj_validation():
                       NULLS) == gdn.GDN_EINVAL
     assert L.gdn_proj(x, 4, 5120, W0, 10240, y0, W1, 6144, fp((3 << 36) + 1024),
                       NULLS) == gdn.GDN_EINVAL
+    # sizes beyond the 32-bit weight addressing or the grid are refused
+    assert L.gdn_proj(x, 4, (1 << 22) + 128, W0, 16, y0, NULLS, 0, NULLS,
+                      NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_proj(x, (1 << 31) + 1, 5120, W0, 16, y0, NULLS, 0, NULLS,
+                      NULLS) == gdn.GDN_EUNSUPPORTED
     # no rows: nothing to do, nothing launched
     assert L.gdn_proj(x, 0, 5120, W0, 10240, y0, W1, 6144, y1, NULLS) == gdn.GDN_OK
 
@@ -243,6 +248,8 @@ def test_proj_pack_validation():
     assert L.gdn_proj_pack(W, fp(4096), 16, 128, NULLS) == gdn.GDN_EINVAL     # overlap
     assert L.gdn_proj_pack(fp(8), Wp, 16, 128, NULLS) == gdn.GDN_EINVAL       # misaligned
     assert L.gdn_proj_pack(NULLS, Wp, 16, 128, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_pack(W, Wp, 16, (1 << 22) + 128, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_proj_pack(W, Wp, 1 << 30, 1 << 12, NULLS) == gdn.GDN_EUNSUPPORTED
 
 
 def test_max_rel_metric_matches_pages_row():
