@@ -249,3 +249,69 @@ def test_layer_decode_chain(orc):
             assert max_rel_pages(host(y)[b], y_r[b]) <= 1e-4, (t, b)
         assert max_rel_pages(host(S), S_ref) <= 1e-4
         assert bits_equal(host(hist), hist_ref) or max_rel_pages(host(hist), hist_ref) <= 1e-4
+
+
+def test_layer_verify_chain(orc):
+    """One GDN layer verifying M draft rows for B sequences, as the M-row path
+    runs it ("Kestrel_VLLM #34", section 3.6): the input projections over all
+    M*B rows in one launch, mark(S, hist), the front end for M rows, M gated
+    steps, out_proj over all rows, then rollback to per-sequence accepted
+    lengths.  Outputs match the oracle's chain under the pages' layer
+    criterion; the rolled-back state matches the oracle's replay; the history
+    holds exactly the last 3 raw frames of the accepted prefix."""
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    B, M, dim, eps = 2, 4, 512, 1e-6
+    cd = synth.conv_dim_of(dims)
+    say(f"layer verify chain B={B} M={M} dim={dim}")
+    gen = synth.make_gen(79, "cuda")
+    pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
+    fw = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
+    S = synth.state(gen, B, dims, device="cuda")
+    hist = torch.randn((B, 3, cd), generator=gen, device="cuda")
+    x = torch.randn((M, B, dim), generator=gen, device="cuda")
+    W = {n: host(t) for n, t in {**pw, **fw}.items()}
+    wp = {n: gdn.proj_pack(pw[n]) for n in ("W_qkv", "W_z", "W_out")}
+    accepted = [3, 0]
+    S0, hist0 = host(S), host(hist)
+
+    xc, z = gdn.proj(x.view(M * B, dim), wp["W_qkv"], wp["W_z"])
+    xc = xc.view(M, B, cd)
+    slab = gdn.Slab(B, dims, hist_floats_per_unit=3 * cd)
+    slab.mark(S, hist)
+    fe = gdn.frontend_m(x, fw["Wa"], fw["Wb"], fw["A_log"], fw["dt_bias"], xc, hist,
+                        fw["conv_w"], dims)
+    rows = [fe[n] for n in NAMES]
+    out = gdn.step_gated(S, *rows, z.view(M, B, vh, vd), pw["norm_w"], eps)
+    y = gdn.proj(out.view(M * B, vh * vd), wp["W_out"]).view(M, B, dim)
+    slab.rollback(S, accepted, *rows, hist=hist, xc_raw=xc)
+
+    # the oracle's chain from the same inputs
+    xh = host(x).reshape(M * B, dim)
+    xc_r = ref_proj(orc, xh, W["W_qkv"]).reshape(M, B, cd)
+    z_r = ref_proj(orc, xh, W["W_z"]).reshape(M, B, vh, vd)
+    fr = dict(q=np.zeros((M, B, kh, kd), np.float32), k=np.zeros((M, B, kh, kd), np.float32),
+              v=np.zeros((M, B, vh, vd), np.float32), g=np.zeros((M, B, vh), np.float32),
+              beta=np.zeros((M, B, vh), np.float32))
+    h_r = hist0.copy()
+    oslab = orc.slab(B, dims, hist_floats=3 * cd)
+    S_r = S0.copy()
+    oslab.mark(S_r, h_r)
+    orc.gdn_frontend_m(host(x), W["Wa"], W["Wb"], W["A_log"], W["dt_bias"], xc_r, h_r,
+                       W["conv_w"], fr["q"], fr["k"], fr["v"], fr["g"], fr["beta"], dims)
+    o_r = np.zeros((M, B, vh, vd), np.float32)
+    orc.gdn_step_m(S_r, *(fr[n] for n in NAMES), o_r, M, dims)
+    g_r = np.zeros_like(o_r)
+    orc.gated_norm(o_r, z_r, W["norm_w"], eps, g_r)
+    y_r = ref_proj(orc, g_r.reshape(M * B, vh * vd), W["W_out"]).reshape(M, B, dim)
+    oslab.rollback(S_r, h_r, fr, M, accepted, xc_raw=xc_r, conv_dim=cd)
+
+    for m in range(M):
+        for b in range(B):
+            assert max_rel_pages(host(y)[m, b], y_r[m, b]) <= 1e-4, (m, b)
+    assert max_rel_pages(host(S), S_r) <= 1e-4
+    # history: the last 3 frames of [initial history, accepted raw rows]
+    xch = host(xc)
+    for b, a in enumerate(accepted):
+        seq = np.concatenate([hist0[b], xch[:a, b]], axis=0)
+        assert bits_equal(host(hist)[b], np.ascontiguousarray(seq[-3:])), b
