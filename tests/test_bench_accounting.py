@@ -31,3 +31,22 @@ def test_headline_launch_bytes():
 def test_kernel_hash_sections_exist():
     for k in bench.HASH_SECTIONS:
         assert len(bench.kernel_hash(k)) == 16
+
+
+def test_projection_shapes_reproduce_pages_weight_bytes():
+    """The projection shapes read from the pages (one output per weight row)
+    give the f32 weight bytes per layer and per token that the pages print."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "layer_weights_p24.json")))
+    sh = gold["shape"]
+    dims = (sh["vh"], sh["kh"], sh["kd"], sh["vd"])
+    dim, vh, vd = sh["dim"], sh["vh"], sh["vd"]
+    cd = synth.conv_dim_of(dims)
+    floats = cd * dim + vh * vd * dim + 2 * vh * dim + dim * vh * vd
+    per_layer = 4 * floats
+    assert round(per_layer / 2**20) == gold["f32_weights_per_layer_MiB"]
+    assert round(sh["layers"] * per_layer / 2**30) == gold["f32_weights_per_token_GiB"]
+    # the benchmark's whole-layer weight bytes are the three large matrices
+    assert synth.FE_DIM == dim and cd == 10240
