@@ -30,7 +30,7 @@ EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab
            "gdn_slab_init", "gdn_mark_step_m", "gdn_verify_m", "gdn_commit",
            "gdn_frontend_verify_m",
            "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy",
-           "gdn_proj", "gdn_proj_pack")
+           "gdn_proj", "gdn_proj_pack", "gdn_verify_m_gated")
 
 
 class GdnError(RuntimeError):
@@ -79,9 +79,11 @@ def lib():
     L.gdn_frontend_verify_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_proj.argtypes = [P, I64, I32, P, I32, P, P, I32, P, P]
     L.gdn_proj_pack.argtypes = [P, P, I32, I32, P]
+    L.gdn_verify_m_gated.argtypes = [P] * 8 + [C.c_float, P, I64, I32, I32, I32, I32, I32, P]
     for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark_step_m", "gdn_mark", "gdn_rollback",
               "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_verify_m",
-              "gdn_commit", "gdn_frontend_verify_m", "gdn_proj", "gdn_proj_pack"):
+              "gdn_commit", "gdn_frontend_verify_m", "gdn_proj", "gdn_proj_pack",
+              "gdn_verify_m_gated"):
         getattr(L, f).restype = C.c_int
     _lib = L
     return L
@@ -283,6 +285,20 @@ def _int32_dev(t, name):
             or not t.is_contiguous():
         raise TypeError(f"{name}: need a contiguous int32 tensor on a HIP device")
     return C.c_void_p(t.data_ptr())
+
+
+def verify_m_gated(S, q, k, v, g, beta, z, norm_w, eps=1e-6, out=None, stream=None):
+    """Gated outputs of M draft rows without advancing S (gdn_verify_m_gated).
+    z [M][N][vh][vd]; norm_w [vd].  Returns out [M][N][vh][vd]."""
+    N, vh, kh, kd, vd = _state_dims(S, q, v)
+    M = q.shape[0]
+    if out is None:
+        out = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
+    _check(lib().gdn_verify_m_gated(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                    _dev(g, "g"), _dev(beta, "beta"), _dev(z, "z"),
+                                    _dev(norm_w, "norm_w"), float(eps), _dev(out, "out"), N, M,
+                                    vh, kh, kd, vd, _stream(stream)), "gdn_verify_m_gated")
+    return out
 
 
 def commit(S, accepted, q, k, v, g, beta, hist=None, xc_raw=None, status=None, stream=None):

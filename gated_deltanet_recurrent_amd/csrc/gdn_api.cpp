@@ -356,6 +356,23 @@ int gdn_verify_m(const float *S, const float *q, const float *k, const float *v,
                                (hipStream_t)stream));
 }
 
+int gdn_verify_m_gated(const float *S, const float *q, const float *k, const float *v,
+                       const float *g, const float *beta, const float *z, const float *norm_w,
+                       float eps, float *out, int64_t n_units, int32_t M, int32_t vh,
+                       int32_t kh, int32_t kd, int32_t vd, void *stream) {
+  if (M < 1 || M > kMaxM) return GDN_EINVAL;
+  if (!(eps >= 0.0f) || eps > 1.0f) return GDN_EINVAL;   // also refuses NaN
+  int rc = check_step(S, q, k, v, g, beta, out, n_units, M, vh, kh, kd, vd);
+  if (rc || n_units == 0) return rc;
+  if (!ptr_ok(z) || !ptr_ok(norm_w)) return GDN_EINVAL;
+  const int64_t sb = n_units * vh * (int64_t)kd * vd * 4;
+  const int64_t zb = (int64_t)M * n_units * vh * vd * 4;
+  if (overlaps(out, zb, z, zb) || overlaps(out, zb, norm_w, vd * 4) || overlaps(S, sb, out, zb))
+    return GDN_EINVAL;
+  return enq(gdn::launch_recur(kd, S, nullptr, q, k, v, g, beta, out, nullptr, n_units, vh, kh,
+                               M, (hipStream_t)stream, z, norm_w, eps));
+}
+
 int gdn_commit(float *S, float *hist, const float *q, const float *k, const float *v,
                const float *g, const float *beta, const float *xc_raw, int32_t conv_dim,
                int64_t n_units, int32_t M, int32_t vh, int32_t kh, int32_t kd, int32_t vd,

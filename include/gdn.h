@@ -168,6 +168,20 @@ int gdn_verify_m(const float *S, const float *q, const float *k,
                  int32_t vd, void *stream);
 
 /*
+ * gdn_verify_m_gated: the outputs gdn_step_gated would produce for the M
+ * draft rows (each head's read-out through the gated RMSNorm,
+ * "Kestrel_VLLM #24", Fig. 1 caption, step 6), S read only, bit for bit.
+ * z [M][N][vh][vd] (the gate), norm_w [vd], 0 <= eps <= 1, out
+ * [M][N][vh][vd].  The accepted prefix is then applied by gdn_commit as for
+ * gdn_verify_m.  Errors as gdn_step_gated.
+ */
+int gdn_verify_m_gated(const float *S, const float *q, const float *k,
+                       const float *v, const float *g, const float *beta,
+                       const float *z, const float *norm_w, float eps, float *out,
+                       int64_t n_units, int32_t M, int32_t vh, int32_t kh, int32_t kd,
+                       int32_t vd, void *stream);
+
+/*
  * gdn_commit: advance every unit u by accepted[u] single steps using rows
  * 0..accepted[u]-1 of the inputs given to gdn_verify_m, in place; with hist
  * (nullable) the conv history [N][3][conv_dim] receives the raw conv input

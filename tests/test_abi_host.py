@@ -178,6 +178,18 @@ def test_verify_commit_refusals_need_no_device():
                         NULLS) == gdn.GDN_EINVAL
     assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 0, 2, vh, kh, kd, vd, acc, NULLS,
                         NULLS) == gdn.GDN_OK                           # nothing to do
+    z, w = fp(30 << 32), fp(31 << 32)
+    eps = C.c_float(1e-6)
+    assert L.gdn_verify_m_gated(S, q, k, v, g, beta, z, w, eps, o, 4, 0, vh, kh, kd, vd,
+                                NULLS) == gdn.GDN_EINVAL                # M = 0
+    assert L.gdn_verify_m_gated(S, q, k, v, g, beta, z, w, C.c_float(float("nan")), o, 4, 2,
+                                vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_verify_m_gated(S, q, k, v, g, beta, z, w, eps, fp((30 << 32) + 1024), 4, 2,
+                                vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL  # out overlaps z
+    assert L.gdn_verify_m_gated(S, q, k, v, g, beta, NULLS, w, eps, o, 4, 2, vh, kh, kd, vd,
+                                NULLS) == gdn.GDN_EINVAL                # no gate
+    assert L.gdn_verify_m_gated(S, q, k, v, g, beta, z, w, eps, o, 0, 2, vh, kh, kd, vd,
+                                NULLS) == gdn.GDN_OK                    # nothing to do
 
 
 def test_frontend_validation():

@@ -479,6 +479,26 @@ def test_step_gated_parity(orc, dims, M):
             assert bits_equal(host(o1[0]), host(out[m])), m
 
 
+@pytest.mark.parametrize("dims,M", [(synth.DIMS128, 1), (synth.DIMS128, 5), (synth.DIMS128, 10),
+                                    (synth.DIMS64, 1), (synth.DIMS64, 6)])
+def test_verify_m_gated_equals_step_gated(dims, M):
+    """gdn_verify_m_gated gives the outputs of gdn_step_gated bit for bit
+    (single-step, M-step and prefetching instances) and leaves S untouched."""
+    say(f"verify_m_gated dims={dims} M={M}")
+    vh, kh, kd, vd = dims
+    N = 3
+    gen = synth.make_gen(14, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    z = torch.randn((M, N, vh, vd), generator=gen, device="cuda")
+    w = 1.0 + 0.1 * torch.randn((vd,), generator=gen, device="cuda")
+    S0 = host(S)
+    out_v = gdn.verify_m_gated(S, *(inp[n] for n in NAMES), z, w, 1e-6)
+    assert bits_equal(host(S), S0)
+    out_s = gdn.step_gated(S.clone(), *(inp[n] for n in NAMES), z, w, 1e-6)
+    assert bits_equal(host(out_v), host(out_s))
+
+
 @pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
 def test_verify_commit_equals_snapshot_protocol(dims):
     """verify_m + commit(accepted) gives the same outputs, state and conv

@@ -315,3 +315,57 @@ def test_layer_verify_chain(orc):
     for b, a in enumerate(accepted):
         seq = np.concatenate([hist0[b], xch[:a, b]], axis=0)
         assert bits_equal(host(hist)[b], np.ascontiguousarray(seq[-3:])), b
+
+
+def test_layer_verify_chain_snapshot_free_equals_snapshot():
+    """The same layer verify without a snapshot: the input projections, the
+    front end for M rows without advancing the history, the gated outputs
+    without advancing the state, out_proj, then commit of the accepted
+    lengths from a device array.  Outputs, state and history equal the
+    snapshot protocol's (mark, front end, gated steps, out_proj, rollback)
+    bit for bit."""
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    B, M, dim, eps = 3, 5, 512, 1e-6
+    cd = synth.conv_dim_of(dims)
+    say(f"layer verify chain, snapshot-free vs snapshot, B={B} M={M}")
+    gen = synth.make_gen(83, "cuda")
+    pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
+    fw = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
+    S0 = synth.state(gen, B, dims, device="cuda")
+    hist0 = torch.randn((B, 3, cd), generator=gen, device="cuda")
+    x = torch.randn((M, B, dim), generator=gen, device="cuda")
+    wp = {n: gdn.proj_pack(pw[n]) for n in ("W_qkv", "W_z", "W_out")}
+    accepted = [4, 0, 5]
+
+    def front(hist, verify):
+        xc, z = gdn.proj(x.view(M * B, dim), wp["W_qkv"], wp["W_z"])
+        xc = xc.view(M, B, cd)
+        f = gdn.frontend_verify_m if verify else gdn.frontend_m
+        fe = f(x, fw["Wa"], fw["Wb"], fw["A_log"], fw["dt_bias"], xc, hist, fw["conv_w"], dims)
+        return xc, z.view(M, B, vh, vd), [fe[n] for n in NAMES]
+
+    # snapshot protocol
+    S1, h1 = S0.clone(), hist0.clone()
+    slab = gdn.Slab(B, dims, hist_floats_per_unit=3 * cd)
+    slab.mark(S1, h1)
+    xc1, z1, rows1 = front(h1, verify=False)
+    out1 = gdn.step_gated(S1, *rows1, z1, pw["norm_w"], eps)
+    y1 = gdn.proj(out1.view(M * B, vh * vd), wp["W_out"])
+    slab.rollback(S1, accepted, *rows1, hist=h1, xc_raw=xc1)
+
+    # snapshot-free protocol
+    S2, h2 = S0.clone(), hist0.clone()
+    xc2, z2, rows2 = front(h2, verify=True)
+    assert bits_equal(host(h2), host(hist0))           # the history is not advanced
+    out2 = gdn.verify_m_gated(S2, *rows2, z2, pw["norm_w"], eps)
+    assert bits_equal(host(S2), host(S0))              # nor the state
+    y2 = gdn.proj(out2.view(M * B, vh * vd), wp["W_out"])
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc = torch.tensor(accepted, dtype=torch.int32, device="cuda")
+    gdn.commit(S2, acc, *rows2, hist=h2, xc_raw=xc2, status=status)
+
+    assert int(status.item()) == 0
+    assert bits_equal(host(y1), host(y2))
+    assert bits_equal(host(S1), host(S2))
+    assert bits_equal(host(h1), host(h2))
