@@ -500,6 +500,79 @@ def bench_layer(cfg, steps, warmup, cpu):
                            "gdn_proj(W_out) per layer")
 
 
+def bench_layer_verify(cfg, steps, warmup, cpu):
+    """Whole GDN layers verifying M draft rows without a snapshot: the input
+    projections over all M*B rows, the M-row front end without advancing the
+    history, the gated outputs without advancing the state, out_proj over all
+    rows, then commit of per-sequence accepted lengths (device array).  The
+    output of layer l (its M rows) is the input of layer l + 1."""
+    dims = cfg["dims"]
+    vh, kh, kd, vd = dims
+    B, L, M, dim = cfg["seqs"], cfg["layers"], cfg["M"], synth.FE_DIM
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(cfg["seed"], "cuda")
+    layers = []
+    for _ in range(L):
+        pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
+        lw = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
+        for n in ("W_qkv", "W_z", "W_out"):
+            packed = gdn.proj_pack(pw[n])
+            del pw[n]
+            lw[n] = packed
+        lw["norm_w"] = pw["norm_w"]
+        lw["S"] = synth.state(gen, B, dims, device="cuda")
+        lw["hist"] = torch.randn((B, 3, cd), generator=gen, device="cuda")
+        layers.append(lw)
+    torch.cuda.empty_cache()
+    rows = M * B
+    x0 = torch.randn((M, B, dim), generator=gen, device="cuda")
+    xs = [torch.empty((M, B, dim), device="cuda") for _ in range(L)]
+    xc = torch.empty((rows, cd), device="cuda")
+    z = torch.empty((rows, vh * vd), device="cuda")
+    out = torch.empty((M, B, vh, vd), device="cuda")
+    fe = dict(q=torch.empty((M, B, kh, kd), device="cuda"),
+              k=torch.empty((M, B, kh, kd), device="cuda"),
+              v=torch.empty((M, B, vh, vd), device="cuda"), g=torch.empty((M, B, vh), device="cuda"),
+              beta=torch.empty((M, B, vh), device="cuda"))
+    rng = np.random.default_rng(cfg["seed"])
+    accs = [torch.from_numpy(rng.integers(0, M + 1, B).astype(np.int32)).to("cuda")
+            for _ in range(8)]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rows_in = [fe[n] for n in NAMES]
+
+    def one(i):
+        x = x0
+        for l, w in enumerate(layers):
+            gdn.proj(x.view(rows, dim), w["W_qkv"], w["W_z"], y0=xc, y1=z)
+            gdn.frontend_verify_m(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"],
+                                  xc.view(M, B, cd), w["hist"], w["conv_w"], dims, out=fe)
+            gdn.verify_m_gated(w["S"], *rows_in, z.view(M, B, vh, vd), w["norm_w"], 1e-6,
+                               out=out)
+            gdn.proj(out.view(rows, vh * vd), w["W_out"], y0=xs[l].view(rows, dim))
+            gdn.commit(w["S"], accs[i % 8], *rows_in, hist=w["hist"],
+                       xc_raw=xc.view(M, B, cd), status=status)
+            x = xs[l]
+
+    dt = timed(one, steps, warmup)
+    dt_in = timed(lambda i: [gdn.proj(x0.view(rows, dim), w["W_qkv"], w["W_z"], y0=xc, y1=z)
+                             for w in layers], steps, 1)
+    in_bytes = (cd + vh * vd) * dim * 4 + rows * dim * 4 + rows * (cd + vh * vd) * 4
+    t_in = dt_in / (steps * L)
+    roof = dict(bound="hbm", achieved=round(in_bytes / t_in / 1e9, 1), peak=PEAK_HBM_GBPS,
+                unit="GB/s", frac=round(in_bytes / t_in / 1e9 / PEAK_HBM_GBPS, 4), traffic=None)
+    res = dict(value=B * vh * M * L * steps / dt, ms_per_step=dt / steps * 1e3, roofline=roof,
+               extra=dict(value_counts="drafted head-steps per second of the full cycle",
+                          layer_us=round(dt / (steps * L) * 1e6, 2),
+                          in_proj_us=round(t_in * 1e6, 2),
+                          kernel="proj_kernel (in_proj_qkv + in_proj_z over M*B rows)",
+                          in_proj_bytes_per_launch=in_bytes,
+                          mean_accepted=float(np.mean([a.float().mean().item() for a in accs]))))
+    return res, dict(workload=cfg["name"], units=B * L, seqs=B, layers=L, M=M, vh=vh, kd=kd,
+                     dim=dim, conv_dim=cd,
+                     chain="gdn_proj(W_qkv, W_z) + gdn_frontend_verify_m + gdn_verify_m_gated + "
+                           "gdn_proj(W_out) + gdn_commit per layer")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -520,8 +593,8 @@ def main():
     cfg = dict(synth.WORKLOADS[args.config])
     cfg["id"] = args.config
     runner = {0: bench_latency, 2: bench_verify, 3: bench_frontend,
-              6: bench_verify_frontend, 8: bench_layer, 9: bench_layer}.get(args.config,
-                                                                          bench_decode)
+              6: bench_verify_frontend, 8: bench_layer, 9: bench_layer,
+              10: bench_layer_verify}.get(args.config, bench_decode)
     res, config = runner(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
     line = dict(metric=METRIC, value=round(res["value"], 1), unit="head-steps/s", n_gpus=1,
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(res["ms_per_step"], 5),

@@ -150,4 +150,6 @@ WORKLOADS = {
             seqs=1, layers=8, dims=DIMS128, gate=None, seed=8),
     9: dict(name="whole-layer decode with f32 projections, 64 sequences x 8 layers",
             seqs=64, layers=8, dims=DIMS128, gate=None, seed=9),
+    10: dict(name="whole-layer speculative verify with f32 projections, 1 sequence x 8 layers, "
+                  "M=8 drafts", seqs=1, layers=8, dims=DIMS128, M=8, gate=None, seed=10),
 }
