@@ -77,7 +77,9 @@ const char *gdn_strerror(int rc) {
   switch (rc) {
     case GDN_OK: return "ok";
     case GDN_EINVAL: return "invalid argument (NULL or misaligned pointer, bad size, aliasing, M or accepted out of range)";
-    case GDN_EUNSUPPORTED: return "unsupported shape (kd == vd must be 64 or 128; launch too large)";
+    case GDN_EUNSUPPORTED:
+      return "unsupported shape (recurrence: kd == vd must be 64 or 128; projection: C a multiple "
+             "of 128, R of 16; or a launch too large)";
     case GDN_ESTATE: return "slab state error (not armed, history not marked, too small, or mismatched)";
     case GDN_EDEVICE: return "HIP runtime error while enqueuing";
     default: return "unknown error code";
