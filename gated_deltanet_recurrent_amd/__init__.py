@@ -11,7 +11,11 @@ Operator: "Kestrel_VLLM #24: GDN linear attention on GPU", section 4 and
 Fig. 1 caption (decay, key read-out, delta, rank-1 update, query read-out with
 the updated state); M-step and mark/rollback: "Kestrel_VLLM #34: batched M
 rows", sections 3.6 and 3.7; front end: "Kestrel_VLLM #27: register residency
-and fused launch", section 4.2, and "#24", section 3.
+and fused launch", section 4.2, and "#24", section 3; dense projections:
+"#24", Fig. 1 caption, steps 1 and 7, and "#34", section 3.6.
+
+Every tensor's element count is checked against the sizes passed with it,
+because the C ABI receives raw pointers and cannot check them itself.
 """
 from __future__ import annotations
 
@@ -103,6 +107,29 @@ def _dev(t, name):
     return C.c_void_p(t.data_ptr())
 
 
+def _sized(t, n, name):
+    """_dev plus an element-count check: the C ABI takes raw pointers, so a
+    tensor smaller than the sizes passed with it would be read or written
+    out of bounds on the device."""
+    if t is None:
+        return None
+    p = _dev(t, name)
+    if t.numel() != n:
+        raise ValueError(f"{name}: has {t.numel()} elements, the call needs {n}")
+    return p
+
+
+def _rows(S, q, k, v, g, beta, M, o=None, o_name="o"):
+    """Pointers of the per-row inputs of M steps over the units of S, each
+    size-checked: q, k [M][N][kh][kd]; v, o [M][N][vh][vd]; g, beta [M][N][vh]."""
+    N, vh, kd, vd = S.shape
+    kh = q.shape[-2]
+    qk = M * N * kh * kd
+    return [_sized(q, qk, "q"), _sized(k, qk, "k"), _sized(v, M * N * vh * vd, "v"),
+            _sized(g, M * N * vh, "g"), _sized(beta, M * N * vh, "beta")] + (
+        [_sized(o, M * N * vh * vd, o_name)] if o is not None else [])
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return C.c_void_p(s.cuda_stream)
@@ -128,8 +155,7 @@ def step(S, q, k, v, g, beta, o=None, stream=None):
     N, vh, kh, kd, vd = _state_dims(S, q, v)
     if o is None:
         o = torch.empty((N, vh, vd), dtype=torch.float32, device=S.device)
-    _check(lib().gdn_step(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                          _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"), N, vh, kh, kd,
+    _check(lib().gdn_step(_dev(S, "S"), *_rows(S, q, k, v, g, beta, 1, o), N, vh, kh, kd,
                           vd, _stream(stream)), "gdn_step")
     return o
 
@@ -141,8 +167,7 @@ def step_m(S, q, k, v, g, beta, o=None, stream=None):
     M = q.shape[0]
     if o is None:
         o = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
-    _check(lib().gdn_step_m(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                            _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"), N, M, vh, kh,
+    _check(lib().gdn_step_m(_dev(S, "S"), *_rows(S, q, k, v, g, beta, M, o), N, M, vh, kh,
                             kd, vd, _stream(stream)), "gdn_step_m")
     return o
 
@@ -155,9 +180,9 @@ def step_gated(S, q, k, v, g, beta, z, norm_w, eps=1e-6, out=None, stream=None):
     M = q.shape[0]
     if out is None:
         out = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
-    _check(lib().gdn_step_gated(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                                _dev(g, "g"), _dev(beta, "beta"), _dev(z, "z"),
-                                _dev(norm_w, "norm_w"), float(eps), _dev(out, "out"), N, M, vh,
+    _check(lib().gdn_step_gated(_dev(S, "S"), *_rows(S, q, k, v, g, beta, M),
+                                _sized(z, M * N * vh * vd, "z"), _sized(norm_w, vd, "norm_w"),
+                                float(eps), _sized(out, M * N * vh * vd, "out"), N, M, vh,
                                 kh, kd, vd, _stream(stream)), "gdn_step_gated")
     return out
 
@@ -186,8 +211,19 @@ class Slab:
     def armed(self):
         return int(self.s.armed)
 
+    def _state_sizes(self):
+        sl = self.s
+        return sl.n_units * sl.vh * sl.kd * sl.vd, sl.n_units * sl.hist_floats
+
+    def _hist(self, hist):
+        # a slab without a history area: the C ABI refuses any hist (GDN_ESTATE)
+        # before anything is enqueued, so there is no size to check
+        nh = self.s.n_units * self.s.hist_floats
+        return _sized(hist, nh, "hist") if nh else _dev(hist, "hist")
+
     def mark(self, S, hist=None, stream=None):
-        _check(lib().gdn_mark(C.byref(self.s), _dev(S, "S"), _dev(hist, "hist"),
+        ns = self._state_sizes()[0]
+        _check(lib().gdn_mark(C.byref(self.s), _sized(S, ns, "S"), self._hist(hist),
                               _stream(stream)), "gdn_mark")
 
     def mark_step_m(self, S, q, k, v, g, beta, hist=None, o=None, stream=None):
@@ -197,9 +233,10 @@ class Slab:
         M = q.shape[0]
         if o is None:
             o = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
-        _check(lib().gdn_mark_step_m(C.byref(self.s), _dev(S, "S"), _dev(hist, "hist"),
-                                     _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(g, "g"),
-                                     _dev(beta, "beta"), _dev(o, "o"), N, M, vh, kh, kd, vd,
+        ns = self._state_sizes()[0]
+        _check(lib().gdn_mark_step_m(C.byref(self.s), _sized(S, ns, "S"),
+                                     self._hist(hist),
+                                     *_rows(S, q, k, v, g, beta, M, o), N, M, vh, kh, kd, vd,
                                      _stream(stream)), "gdn_mark_step_m")
         return o
 
@@ -213,11 +250,28 @@ class Slab:
             M = q.shape[0] if q is not None else 1
         conv_dim = xc_raw.shape[-1] if xc_raw is not None else (
             hist.shape[-1] if hist is not None else 0)
-        _check(lib().gdn_rollback(C.byref(self.s), _dev(S, "S"), _dev(hist, "hist"),
-                                  _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(g, "g"),
-                                  _dev(beta, "beta"), _dev(xc_raw, "xc_raw"), conv_dim, M,
-                                  C.c_void_p(acc.data_ptr()), _stream(stream)),
+        ns = self._state_sizes()[0]
+        rows = _rows(S, q, k, v, g, beta, M) if q is not None else [None] * 5
+        _check(lib().gdn_rollback(C.byref(self.s), _sized(S, ns, "S"), self._hist(hist),
+                                  *rows,
+                                  _sized(xc_raw, M * self.s.n_units * conv_dim, "xc_raw"),
+                                  conv_dim, M, C.c_void_p(acc.data_ptr()), _stream(stream)),
                "gdn_rollback")
+
+
+def _fe_args(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, out, dims, M, B, dim):
+    """Size-checked pointers of a front-end call over M rows of B units."""
+    vh, kh, kd, vd = dims
+    conv_dim = xc_raw.shape[-1]
+    ck = conv_w.shape[-1]
+    return [_sized(x, M * B * dim, "x"), _sized(Wa, vh * dim, "Wa"), _sized(Wb, vh * dim, "Wb"),
+            _sized(A_log, vh, "A_log"), _sized(dt_bias, vh, "dt_bias"),
+            _sized(xc_raw, M * B * conv_dim, "xc_raw"),
+            _sized(hist, B * (ck - 1) * conv_dim, "hist"),
+            _sized(conv_w, conv_dim * ck, "conv_w"),
+            _sized(out["q"], M * B * kh * kd, "q"), _sized(out["k"], M * B * kh * kd, "k"),
+            _sized(out["v"], M * B * vh * vd, "v"), _sized(out["g"], M * B * vh, "g"),
+            _sized(out["beta"], M * B * vh, "beta")]
 
 
 def frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None, stream=None):
@@ -234,11 +288,8 @@ def frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None, st
                    g=torch.empty((B, vh), dtype=torch.float32, device=dev),
                    beta=torch.empty((B, vh), dtype=torch.float32, device=dev))
     _check(lib().gdn_frontend(
-        _dev(x, "x"), _dev(Wa, "Wa"), _dev(Wb, "Wb"), _dev(A_log, "A_log"),
-        _dev(dt_bias, "dt_bias"), _dev(xc_raw, "xc_raw"), _dev(hist, "hist"),
-        _dev(conv_w, "conv_w"), _dev(out["q"], "q"), _dev(out["k"], "k"), _dev(out["v"], "v"),
-        _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, dim, conv_dim, ck, vh, kh, kd, vd,
-        _stream(stream)), "gdn_frontend")
+        *_fe_args(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, out, dims, 1, B, dim),
+        B, dim, conv_dim, ck, vh, kh, kd, vd, _stream(stream)), "gdn_frontend")
     return out
 
 
@@ -258,11 +309,8 @@ def frontend_m(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None, 
                    g=torch.empty((M, B, vh), dtype=torch.float32, device=dev),
                    beta=torch.empty((M, B, vh), dtype=torch.float32, device=dev))
     _check(lib().gdn_frontend_m(
-        _dev(x, "x"), _dev(Wa, "Wa"), _dev(Wb, "Wb"), _dev(A_log, "A_log"),
-        _dev(dt_bias, "dt_bias"), _dev(xc_raw, "xc_raw"), _dev(hist, "hist"),
-        _dev(conv_w, "conv_w"), _dev(out["q"], "q"), _dev(out["k"], "k"), _dev(out["v"], "v"),
-        _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, M, dim, conv_dim, ck, vh, kh, kd,
-        vd, _stream(stream)), "gdn_frontend_m")
+        *_fe_args(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, out, dims, M, B, dim),
+        B, M, dim, conv_dim, ck, vh, kh, kd, vd, _stream(stream)), "gdn_frontend_m")
     return out
 
 
@@ -272,18 +320,19 @@ def verify_m(S, q, k, v, g, beta, o=None, stream=None):
     M = q.shape[0]
     if o is None:
         o = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
-    _check(lib().gdn_verify_m(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                              _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"), N, M, vh, kh, kd,
-                              vd, _stream(stream)), "gdn_verify_m")
+    _check(lib().gdn_verify_m(_dev(S, "S"), *_rows(S, q, k, v, g, beta, M, o), N, M, vh, kh,
+                              kd, vd, _stream(stream)), "gdn_verify_m")
     return o
 
 
-def _int32_dev(t, name):
+def _int32_dev(t, name, n):
     if t is None:
         return None
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.int32 \
             or not t.is_contiguous():
         raise TypeError(f"{name}: need a contiguous int32 tensor on a HIP device")
+    if t.numel() != n:
+        raise ValueError(f"{name}: has {t.numel()} elements, the call needs {n}")
     return C.c_void_p(t.data_ptr())
 
 
@@ -294,9 +343,10 @@ def verify_m_gated(S, q, k, v, g, beta, z, norm_w, eps=1e-6, out=None, stream=No
     M = q.shape[0]
     if out is None:
         out = torch.empty((M, N, vh, vd), dtype=torch.float32, device=S.device)
-    _check(lib().gdn_verify_m_gated(_dev(S, "S"), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                                    _dev(g, "g"), _dev(beta, "beta"), _dev(z, "z"),
-                                    _dev(norm_w, "norm_w"), float(eps), _dev(out, "out"), N, M,
+    _check(lib().gdn_verify_m_gated(_dev(S, "S"), *_rows(S, q, k, v, g, beta, M),
+                                    _sized(z, M * N * vh * vd, "z"),
+                                    _sized(norm_w, vd, "norm_w"), float(eps),
+                                    _sized(out, M * N * vh * vd, "out"), N, M,
                                     vh, kh, kd, vd, _stream(stream)), "gdn_verify_m_gated")
     return out
 
@@ -308,11 +358,11 @@ def commit(S, accepted, q, k, v, g, beta, hist=None, xc_raw=None, status=None, s
     N, vh, kh, kd, vd = _state_dims(S, q, v)
     M = q.shape[0]
     conv_dim = xc_raw.shape[-1] if xc_raw is not None else 0
-    _check(lib().gdn_commit(_dev(S, "S"), _dev(hist, "hist"), _dev(q, "q"), _dev(k, "k"),
-                            _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"),
-                            _dev(xc_raw, "xc_raw"), conv_dim, N, M, vh, kh, kd, vd,
-                            _int32_dev(accepted, "accepted"), _int32_dev(status, "status"),
-                            _stream(stream)), "gdn_commit")
+    _check(lib().gdn_commit(_dev(S, "S"), _sized(hist, N * 3 * conv_dim, "hist"),
+                            *_rows(S, q, k, v, g, beta, M),
+                            _sized(xc_raw, M * N * conv_dim, "xc_raw"), conv_dim, N, M, vh, kh,
+                            kd, vd, _int32_dev(accepted, "accepted", N),
+                            _int32_dev(status, "status", 1), _stream(stream)), "gdn_commit")
 
 
 def frontend_verify_m(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None,
@@ -330,11 +380,8 @@ def frontend_verify_m(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out
                    g=torch.empty((M, B, vh), dtype=torch.float32, device=dev),
                    beta=torch.empty((M, B, vh), dtype=torch.float32, device=dev))
     _check(lib().gdn_frontend_verify_m(
-        _dev(x, "x"), _dev(Wa, "Wa"), _dev(Wb, "Wb"), _dev(A_log, "A_log"),
-        _dev(dt_bias, "dt_bias"), _dev(xc_raw, "xc_raw"), _dev(hist, "hist"),
-        _dev(conv_w, "conv_w"), _dev(out["q"], "q"), _dev(out["k"], "k"), _dev(out["v"], "v"),
-        _dev(out["g"], "g"), _dev(out["beta"], "beta"), B, M, dim, conv_dim, ck, vh, kh, kd,
-        vd, _stream(stream)), "gdn_frontend_verify_m")
+        *_fe_args(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, out, dims, M, B, dim),
+        B, M, dim, conv_dim, ck, vh, kh, kd, vd, _stream(stream)), "gdn_frontend_verify_m")
     return out
 
 

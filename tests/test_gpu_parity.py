@@ -263,9 +263,10 @@ def test_mark_step_m_fused(dims, M):
                   xc_raw=torch.zeros((M, N, cd), device="cuda"))
     assert bits_equal(host(S), host(S_mark))
     assert bits_equal(host(hist), hist_mark)
-    # a mismatched slab is refused
+    # a mismatched slab is refused (by the binding's size check before the C
+    # ABI's own GDN_ESTATE refusal, which the host-side tests exercise)
     small = gdn.Slab(N - 1, dims)
-    with pytest.raises(gdn.GdnError):
+    with pytest.raises((gdn.GdnError, ValueError)):
         small.mark_step_m(S, *(inp[n] for n in NAMES))
 
 
@@ -807,3 +808,37 @@ def test_full_size_frontend_step_sampled(orc):
         assert_close(host(o.index_select(0, ii)), o_ref, f"o t={t}")
         assert_close(host(S.index_select(0, ii)), S_h, f"S t={t}")
         assert bits_equal(host(hist.index_select(0, ii)), hist_h)
+
+
+def test_binding_refuses_mis_sized_tensors():
+    """The binding checks every tensor's element count before calling the C
+    ABI (which receives raw pointers): a short or long buffer is refused with
+    ValueError and nothing is launched."""
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    N, M = 2, 3
+    gen = synth.make_gen(15, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    S0 = host(S)
+    row = [inp[n][0] for n in NAMES]
+    for i, name in enumerate(NAMES):
+        bad = list(row)
+        bad[i] = bad[i].reshape(-1)[:-4].contiguous()          # 4 elements short
+        with pytest.raises(ValueError, match=name):
+            gdn.step(S, *bad)
+    with pytest.raises(ValueError, match="o"):
+        gdn.step(S, *row, o=torch.empty((N, vh, vd - 4), device="cuda"))
+    with pytest.raises(ValueError, match="v"):
+        gdn.step_m(S, *(inp[n] for n in NAMES[:2]), inp["v"][:2].contiguous(), inp["g"],
+                   inp["beta"])
+    with pytest.raises(ValueError, match="accepted"):
+        gdn.commit(S, torch.zeros(N + 1, dtype=torch.int32, device="cuda"),
+                   *(inp[n] for n in NAMES))
+    w = synth.frontend_weights(gen, dims, dim=256, device="cuda")
+    fe = synth.frontend_inputs(gen, N, dims, dim=256, device="cuda")
+    with pytest.raises(ValueError, match="hist"):
+        gdn.frontend(fe["x"][0], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"][0],
+                     fe["hist"][:1].contiguous(), w["conv_w"], dims)
+    torch.cuda.synchronize()
+    assert bits_equal(host(S), S0)
