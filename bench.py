@@ -210,7 +210,7 @@ def bench_decode(cfg, steps, warmup, cpu):
                    kernel="recur_wide_kernel", kernel_source_sha256_16=kernel_hash(),
                    **per_layer))
     if cpu:
-        res["cpu_baseline"] = cpu_baseline_step(S, pool, dims, units=min(N, 256), rows=8)
+        res["cpu_baseline"] = cpu_baseline_step(S, pool, dims, units=min(N, 1024), rows=8)
     return res, dict(workload=cfg["name"], units=N, seqs=cfg["seqs"], layers=cfg["layers"],
                      vh=dims[0], kh=dims[1], kd=dims[2], vd=dims[3],
                      state_GB=round(N * vh * dims[2] * dims[3] * 4 / 1e9, 3),
