@@ -498,9 +498,12 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
       const int64_t urow = (int64_t)m * a.n_units + ti.unit;
       const float alpha = sb.alpha[r];
       f4 p[4], w0, w1 = splat(0.0f);
+      f4 kkr[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) kkr[i] = lds4(&sb.k[r][(4 * L + i) * 4]);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const f4 kk = lds4(&sb.k[r][(4 * L + i) * 4]);
+        const f4 kk = kkr[i];
         p[i] = splat(0.0f);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -517,11 +520,11 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
         if (wave == 0) {
           const f4 kv = tile_sum<KD>(s_red_k, lane);
           if (lane < CG) s_tmp[lane] = (lds4(&sb.v[r][4 * lane]) - kv) * sb.beta[r];
-          if (m > 0 && a.o != nullptr) {
-            const f4 ov = tile_sum<KD>(s_red_o, lane);
-            const int64_t prow = (int64_t)(m - 1) * a.n_units + ti.unit;
-            emit_o<KD, GATED>(a, prow, ti.head, lane % CG, lane < CG, ov, zprev);
-          }
+        } else if (wave == 1 && m > 0 && a.o != nullptr) {
+          // the previous step's output, in parallel with wave 0's S^T k
+          const f4 ov = tile_sum<KD>(s_red_o, lane);
+          const int64_t prow = (int64_t)(m - 1) * a.n_units + ti.unit;
+          emit_o<KD, GATED>(a, prow, ti.head, lane % CG, lane < CG, ov, zprev);
         }
         __syncthreads();
         tmp = s_tmp[cg];
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
       // rank-1 update, then S^T q with the updated state
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const f4 kk = lds4(&sb.k[r][(4 * L + i) * 4]);
+        const f4 kk = kkr[i];
         const f4 qq = lds4(&sb.q[r][(4 * L + i) * 4]);
         p[i] = splat(0.0f);
 #pragma unroll
