@@ -91,6 +91,10 @@ class Oracle:
         lib.ref_gdn_gated_norm.restype = C.c_int
         lib.ref_gdn_proj.argtypes = [P, P, P, L, I, I]
         lib.ref_gdn_proj.restype = C.c_int
+        lib.ref_half_to_float.argtypes = [P, P, L]
+        lib.ref_half_to_float.restype = None
+        lib.ref_gdn_proj_q4.argtypes = [P, P, P, P, L, I, I]
+        lib.ref_gdn_proj_q4.restype = C.c_int
         for f in ("ref_gdn_step", "ref_gdn_step_m", "ref_gdn_mark", "ref_gdn_rollback",
                   "ref_gdn_frontend", "ref_gdn_frontend_m", "ref64_gdn_step"):
             getattr(lib, f).restype = C.c_int
@@ -165,6 +169,30 @@ class Oracle:
             raise ValueError("proj: shapes of x, W, y do not agree")
         rc = self.lib.ref_gdn_proj(_f32(x, "x"), _f32(W, "W"), _f32(y, "y", True), rows, R, Cc)
         _check(rc, "ref_gdn_proj")
+
+    def half_to_float(self, h):
+        """binary16 bit patterns (uint16 array) -> float32 values."""
+        h = np.ascontiguousarray(h, dtype=np.uint16)
+        f = np.zeros(h.shape, np.float32)
+        self.lib.ref_half_to_float(h.ctypes.data_as(C.c_void_p), f.ctypes.data_as(C.c_void_p),
+                                   h.size)
+        return f
+
+    def proj_q4(self, x, q, scale, y):
+        """y [rows][R] = x . W^T with W decoded from q [R][C/2] (uint8) and
+        scale [R][C/32] (binary16 bit patterns, uint16)."""
+        R = q.shape[0]
+        Cc = 2 * q.shape[1]
+        rows = x.size // Cc
+        for a, t, nm in ((q, np.uint8, "q"), (scale, np.uint16, "scale")):
+            if a.dtype != t or not a.flags.c_contiguous:
+                raise TypeError(f"{nm}: need a C-contiguous {t.__name__} array")
+        if scale.shape != (R, Cc // 32) or x.size != rows * Cc or y.size != rows * R:
+            raise ValueError("proj_q4: shapes of x, q, scale, y do not agree")
+        rc = self.lib.ref_gdn_proj_q4(_f32(x, "x"), q.ctypes.data_as(C.c_void_p),
+                                      scale.ctypes.data_as(C.c_void_p), _f32(y, "y", True),
+                                      rows, R, Cc)
+        _check(rc, "ref_gdn_proj_q4")
 
     def gdn_step64(self, S, q, k, v, g, beta, o, dims):
         """Double-precision brute-force step (tiny shapes, kd, vd <= 16)."""

@@ -373,6 +373,63 @@ int ref_gdn_proj(const float *x, const float *W, float *y, int64_t rows, int R, 
     return 0;
 }
 
+/* binary16: sign bit, 5-bit exponent e (bias 15), 10-bit fraction f.
+ * e = 0: zero or subnormal, f * 2^-24; 0 < e < 31: (1024 + f) * 2^(e - 25);
+ * e = 31: infinity (f = 0) or NaN.  Every finite value is exact in binary32.
+ * (The half-precision block scales of "Kestrel_VLLM #24", section 12, whose
+ * conversion the page states is exact and unique for every non-NaN input.) */
+static float half_to_float(uint16_t h)
+{
+    const int e = (h >> 10) & 0x1f;
+    const int f = h & 0x3ff;
+    float mag;
+    if (e == 0)
+        mag = ldexpf((float)f, -24);
+    else if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexpf((float)(1024 + f), e - 25);
+    return (h & 0x8000) ? -mag : mag;
+}
+
+void ref_half_to_float(const uint16_t *h, float *f, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        f[i] = half_to_float(h[i]);
+}
+
+/* The 4-bit projection of the q4 tier ("Kestrel_VLLM #24", section 8: the
+ * three large projections read 4-bit weights with f32 activations; section
+ * 12: signed 4-bit values times a half-precision block scale; the 63.9 MB of
+ * weights it reads per layer fixes 32 weights per scale).  The weight is
+ * formed exactly, then the strict left fold of ref_gdn_proj. */
+int ref_gdn_proj_q4(const float *x, const uint8_t *q, const uint16_t *scale, float *y,
+                    int64_t rows, int R, int C)
+{
+    if (rows < 0 || R <= 0 || C <= 0 || C % 32 != 0)
+        return -1;
+    if (rows == 0)
+        return 0;
+    if (!x || !q || !scale || !y)
+        return -1;
+    for (int64_t r = 0; r < rows; r++) {
+        const float *xr = x + (size_t)r * C;
+        for (int o = 0; o < R; o++) {
+            const uint8_t *qo = q + (size_t)o * (C / 2);
+            const uint16_t *so = scale + (size_t)o * (C / 32);
+            float acc = 0.0f;
+            for (int c = 0; c < C; c++) {
+                const int nib = (c & 1) ? (qo[c / 2] >> 4) : (qo[c / 2] & 0x0f);
+                const int n = (nib ^ 8) - 8;
+                const float w = (float)n * half_to_float(so[c / 32]);
+                acc = acc + w * xr[c];
+            }
+            y[(size_t)r * R + o] = acc;
+        }
+    }
+    return 0;
+}
+
 /*
  * Double-precision brute force, re-associated: S' = alpha (I - beta k k^T) S
  * + beta k v^T and o = S'^T q, with the kd x kd matrix P = alpha (I - beta k

@@ -126,6 +126,18 @@ int ref_gdn_gated_norm(const float *o, const float *z, const float *w, float eps
  * calls. */
 int ref_gdn_proj(const float *x, const float *W, float *y, int64_t rows, int R, int C);
 
+/* IEEE 754 binary16 -> binary32 of n values (bit patterns in h). */
+void ref_half_to_float(const uint16_t *h, float *f, int64_t n);
+
+/* The projection with 4-bit weights: W[o][c] = n * s, n the signed
+ * (two's complement) 4-bit value of element c of row o, s the binary16 scale
+ * shared by the 32 elements of its block.  q [R][C/2] bytes: element 2i in
+ * the low nibble of byte i, element 2i+1 in the high nibble; scale [R][C/32]
+ * binary16 bit patterns.  Every W[o][c] is exact in fp32; then y is the
+ * strict left fold of ref_gdn_proj.  C must be a multiple of 32. */
+int ref_gdn_proj_q4(const float *x, const uint8_t *q, const uint16_t *scale, float *y,
+                    int64_t rows, int R, int C);
+
 /* Double-precision brute force of one step for tiny shapes, in the
  * re-associated matrix form S' = alpha (I - beta k k^T) S + beta k v^T,
  * o = S'^T q, built from explicit kd x kd and kd x vd matrices.  Same

@@ -50,3 +50,11 @@ def test_projection_shapes_reproduce_pages_weight_bytes():
     assert round(sh["layers"] * per_layer / 2**30) == gold["f32_weights_per_token_GiB"]
     # the benchmark's whole-layer weight bytes are the three large matrices
     assert synth.FE_DIM == dim and cd == 10240
+    # the q4 layer: 4-bit weights with one binary16 scale per 32 for the three
+    # large projections; in_proj_a / in_proj_b and the conv weights stay f32
+    large = cd * dim + vh * vd * dim + dim * vh * vd
+    q4 = large // 2 + (large // 32) * 2 + 4 * (2 * vh * dim + cd * 4)
+    assert round(q4 / 2**20, 1) == gold["q4_weights_per_layer_MiB"]
+    for block in (16, 64):                          # other block sizes miss the printed size
+        other = large // 2 + (large // block) * 2 + 4 * (2 * vh * dim + cd * 4)
+        assert round(other / 2**20, 1) != gold["q4_weights_per_layer_MiB"]

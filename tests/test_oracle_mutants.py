@@ -79,6 +79,13 @@ MUTANTS = [
      "y[(size_t)o * rows + r] = acc;"),
     ("projection folds in double", "float acc = 0.0f;\n            for (int c = 0; c < C; c++)",
      "double acc = 0.0;\n            for (int c = 0; c < C; c++)"),
+    ("q4 nibble order swapped", "(c & 1) ? (qo[c / 2] >> 4) : (qo[c / 2] & 0x0f)",
+     "(c & 1) ? (qo[c / 2] & 0x0f) : (qo[c / 2] >> 4)"),
+    ("q4 nibbles unsigned", "const int n = (nib ^ 8) - 8;", "const int n = nib;"),
+    ("q4 scale block of 64", "half_to_float(so[c / 32])", "half_to_float(so[c / 64])"),
+    ("half exponent bias", "ldexpf((float)(1024 + f), e - 25)", "ldexpf((float)(1024 + f), e - 24)"),
+    ("half subnormals flushed", "mag = ldexpf((float)f, -24);", "mag = 0.0f;"),
+    ("half sign dropped", "return (h & 0x8000) ? -mag : mag;", "return mag;"),
 ]
 
 

@@ -534,6 +534,69 @@ def pin_proj_brute_force_fp64(orc):
         assert bits_equal(_proj(orc, x[i:i + 1], W)[0], y[i])
 
 
+def pin_half_to_float_all_patterns(orc):
+    """binary16 -> binary32 for all 65536 bit patterns equals numpy's
+    float16 conversion (NaN for NaN): zeros, subnormals, normals, infinities,
+    both signs."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.half_to_float(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert bits_equal(got[~nan], ref[~nan])
+
+
+def _q4_case(r, R, C):
+    q = r.integers(0, 256, size=(R, C // 2)).astype(np.uint8)
+    sc = (r.normal(0, 0.01, size=(R, C // 32)) + 0.0).astype(np.float16)
+    return q, np.ascontiguousarray(sc.view(np.uint16))
+
+
+def _q4_decode(q, scale):
+    """numpy decode: low nibble is the even element, two's complement, times
+    the block's scale (float16 -> float32 is exact, so is the product)."""
+    R = q.shape[0]
+    nib = np.stack([q & 0x0F, q >> 4], axis=-1).reshape(R, -1).astype(np.int32)
+    n = ((nib ^ 8) - 8).astype(np.float32)
+    s = scale.view(np.float16).astype(np.float32)
+    return np.ascontiguousarray(n * np.repeat(s, 32, axis=1))
+
+
+def pin_proj_q4_is_the_decoded_f32_projection(orc):
+    """The 4-bit projection equals the f32 projection of the weights decoded
+    by numpy (nibble order, sign, 32-weight scale blocks, the scale's
+    conversion), bit for bit; a one-hot row returns the decoded column."""
+    r = _rng(73)
+    R, C = 24, 256
+    q, sc = _q4_case(r, R, C)
+    x = r.normal(size=(3, C)).astype(np.float32)
+    y4 = np.zeros((3, R), np.float32)
+    orc.proj_q4(x, q, sc, y4)
+    Wd = _q4_decode(q, sc)
+    assert bits_equal(y4, _proj(orc, x, Wd))
+    e = np.zeros((1, C), np.float32)
+    e[0, C - 33] = 1.0
+    y1 = np.zeros((1, R), np.float32)
+    orc.proj_q4(e, q, sc, y1)
+    assert bits_equal(y1[0], np.ascontiguousarray(Wd[:, C - 33]))
+
+
+def pin_proj_q4_closed_form(orc):
+    """Byte 0x9F holds -1 (low nibble 0xF) then -7 (high nibble 0x9); with
+    scale 0.5 and x = (1, 10) the output is -0.5 - 35 = -35.5; 0x80 is 0 then
+    -8 (the most negative value)."""
+    C = 32
+    q = np.zeros((2, C // 2), np.uint8)
+    q[0, 0] = 0x9F
+    q[1, 0] = 0x80
+    sc = np.array([[0.5], [0.25]], np.float16).view(np.uint16)
+    x = np.zeros((1, C), np.float32)
+    x[0, 0], x[0, 1] = 1.0, 10.0
+    y = np.zeros((1, 2), np.float32)
+    orc.proj_q4(x, q, np.ascontiguousarray(sc), y)
+    assert y[0, 0] == -35.5 and y[0, 1] == -20.0
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
