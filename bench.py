@@ -56,9 +56,12 @@ def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
 # shared helpers after the file's header comment, then its own section), so
 # that an edit elsewhere in the file does not invalidate its recorded
 # counters.
+_Q4_SECTION = b"// " + b"-" * 75 + b"\n// Dense layer projections with 4-bit weights"
 HASH_SECTIONS = {
     "recur_wide_kernel": ((b"namespace gdn {", b"// Streaming copy"),),
-    "proj_kernel": ((b"namespace gdn {", b"// Recurrence\n"), (b"// Dense layer projections", None)),
+    "proj_kernel": ((b"namespace gdn {", b"// Recurrence\n"),
+                    (b"// Dense layer projections", _Q4_SECTION), (b"}  // namespace gdn", None)),
+    "proj_q4_kernel": ((b"namespace gdn {", b"// Recurrence\n"), (_Q4_SECTION, None)),
 }
 
 

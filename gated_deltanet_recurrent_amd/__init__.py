@@ -34,7 +34,8 @@ EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab
            "gdn_slab_init", "gdn_mark_step_m", "gdn_verify_m", "gdn_commit",
            "gdn_frontend_verify_m",
            "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy",
-           "gdn_proj", "gdn_proj_pack", "gdn_verify_m_gated")
+           "gdn_proj", "gdn_proj_pack", "gdn_verify_m_gated", "gdn_proj_q4_bytes",
+           "gdn_proj_q4_pack", "gdn_proj_q4")
 
 
 class GdnError(RuntimeError):
@@ -84,10 +85,14 @@ def lib():
     L.gdn_proj.argtypes = [P, I64, I32, P, I32, P, P, I32, P, P]
     L.gdn_proj_pack.argtypes = [P, P, I32, I32, P]
     L.gdn_verify_m_gated.argtypes = [P] * 8 + [C.c_float, P, I64, I32, I32, I32, I32, I32, P]
+    L.gdn_proj_q4_bytes.argtypes = [I32, I32]
+    L.gdn_proj_q4_bytes.restype = I64
+    L.gdn_proj_q4_pack.argtypes = [P, P, P, I32, I32, P]
+    L.gdn_proj_q4.argtypes = [P, I64, I32, P, I32, P, P, I32, P, P]
     for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark_step_m", "gdn_mark", "gdn_rollback",
               "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_verify_m",
               "gdn_commit", "gdn_frontend_verify_m", "gdn_proj", "gdn_proj_pack",
-              "gdn_verify_m_gated"):
+              "gdn_verify_m_gated", "gdn_proj_q4_pack", "gdn_proj_q4"):
         getattr(L, f).restype = C.c_int
     _lib = L
     return L
@@ -418,6 +423,78 @@ def proj(x, W0, W1=None, y0=None, y1=None, stream=None):
     _check(lib().gdn_proj(_dev(x, "x"), rows, Cc, _dev(W0, "W0"), W0.shape[0], _dev(y0, "y0"),
                           _dev(W1, "W1"), R1, _dev(y1, "y1"), _stream(stream)), "gdn_proj")
     return y0 if W1 is None else (y0, y1)
+
+
+def _dev_bytes(t, name, dtypes):
+    """Device pointer of a contiguous tensor of one of the given dtypes."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on a HIP device, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: must be one of {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def proj_q4_bytes(R, C_):
+    """Bytes of a packed 4-bit [R][C] weight matrix (gdn_proj_q4_bytes)."""
+    n = lib().gdn_proj_q4_bytes(R, C_)
+    if n < 0:
+        raise GdnError(GDN_EUNSUPPORTED, f"gdn_proj_q4_bytes: R={R}, C={C_} not supported")
+    return n
+
+
+def proj_q4_pack(q, scale, out=None, stream=None):
+    """4-bit weights in the packed order gdn_proj_q4 reads (gdn_proj_q4_pack).
+    q: uint8 [R][C/2] (element 2i in the low nibble of byte i, two's
+    complement); scale: [R][C/32] binary16 (float16, or int16 bit patterns).
+    Returns uint8 [R/64][36 C]: one row per group of 64 weight rows."""
+    if q.dim() != 2 or scale.dim() != 2:
+        raise ValueError("q must be [R][C/2] and scale [R][C/32]")
+    R, Cc = q.shape[0], 2 * q.shape[1]
+    if tuple(scale.shape) != (R, Cc // 32) or Cc % 32:
+        raise ValueError(f"scale must be [{R}][{Cc // 32}] for q of shape {tuple(q.shape)}")
+    n = proj_q4_bytes(R, Cc)
+    if out is None:
+        out = torch.empty((R // 64, 36 * Cc), dtype=torch.uint8, device=q.device)
+    if out.numel() != n:
+        raise ValueError(f"out must hold {n} bytes")
+    _check(lib().gdn_proj_q4_pack(_dev_bytes(q, "q", (torch.uint8,)),
+                                  _dev_bytes(scale, "scale", (torch.float16, torch.int16)),
+                                  _dev_bytes(out, "Wq", (torch.uint8,)), R, Cc,
+                                  _stream(stream)), "gdn_proj_q4_pack")
+    return out
+
+
+def proj_q4(x, Wq0, Wq1=None, y0=None, y1=None, stream=None):
+    """proj with 4-bit weights (gdn_proj_q4): Wq0, Wq1 packed by proj_q4_pack
+    (uint8 [R/64][36 C]); x [..., C] with 1 to 16 rows.  Returns y0, or
+    (y0, y1) when Wq1 is given."""
+    Cc = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    rows = x.numel() // Cc if Cc else 0
+    Rs = []
+    for W, nm in ((Wq0, "Wq0"), (Wq1, "Wq1")):
+        if W is None:
+            Rs.append(0)
+            continue
+        if W.dim() != 2 or W.shape[1] != 36 * Cc:
+            raise ValueError(f"{nm} must be a packed [R/64][{36 * Cc}] uint8 matrix")
+        Rs.append(64 * W.shape[0])
+    if y0 is None:
+        y0 = torch.empty(lead + (Rs[0],), dtype=torch.float32, device=x.device)
+    if Wq1 is not None and y1 is None:
+        y1 = torch.empty(lead + (Rs[1],), dtype=torch.float32, device=x.device)
+    if y0.numel() != rows * Rs[0] or (Wq1 is not None and y1.numel() != rows * Rs[1]):
+        raise ValueError("output sizes do not match rows x R")
+    _check(lib().gdn_proj_q4(_dev(x, "x"), rows, Cc, _dev_bytes(Wq0, "Wq0", (torch.uint8,)),
+                             Rs[0], _dev(y0, "y0"), _dev_bytes(Wq1, "Wq1", (torch.uint8,)), Rs[1],
+                             _dev(y1, "y1"), _stream(stream)), "gdn_proj_q4")
+    return y0 if Wq1 is None else (y0, y1)
 
 
 def stream_copy(dst, src, stream=None):

@@ -431,6 +431,7 @@ int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream
 constexpr int32_t kProjMaxC = 1 << 22;
 constexpr int64_t kProjMaxRC = (int64_t)1 << 40;
 constexpr int64_t kProjMaxRows = (int64_t)1 << 31;
+constexpr int64_t kProjQ4MaxRows = 16;   // the 4-bit path: one row block (decode, verify)
 
 int gdn_proj_pack(const float *W, float *Wp, int32_t R, int32_t C, void *stream) {
   if (R <= 0 || C <= 0) return GDN_EINVAL;
@@ -466,6 +467,47 @@ int gdn_proj(const float *x, int64_t rows, int32_t C, const float *W0, int32_t R
                         overlaps(y1, y1b, W1, w1b) || overlaps(y1, y1b, y0, y0b)))
     return GDN_EINVAL;
   return enq(gdn::launch_proj(x, rows, C, W0, R0, y0, W1, R1, y1, (hipStream_t)stream));
+}
+
+int64_t gdn_proj_q4_bytes(int32_t R, int32_t C) {
+  if (R <= 0 || C <= 0 || R % 64 != 0 || C % 512 != 0) return -1;
+  return (int64_t)R * C / 16 * 9;
+}
+
+int gdn_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int32_t R, int32_t C,
+                     void *stream) {
+  if (R <= 0 || C <= 0) return GDN_EINVAL;
+  if (C % 512 != 0 || R % 64 != 0) return GDN_EUNSUPPORTED;
+  if (C > kProjMaxC || (int64_t)R * C > kProjMaxRC) return GDN_EUNSUPPORTED;
+  if (!ptr_ok(q) || !ptr_ok(scale) || !ptr_ok(Wq)) return GDN_EINVAL;
+  const int64_t qb = (int64_t)R * C / 2, sb = (int64_t)R * C / 16, wb = qb + sb;
+  if (overlaps(q, qb, Wq, wb) || overlaps(scale, sb, Wq, wb)) return GDN_EINVAL;
+  return enq(gdn::launch_proj_q4_pack(q, scale, Wq, R, C, (hipStream_t)stream));
+}
+
+int gdn_proj_q4(const float *x, int64_t rows, int32_t C, const void *Wq0, int32_t R0, float *y0,
+                const void *Wq1, int32_t R1, float *y1, void *stream) {
+  if (rows < 0 || C <= 0 || R0 <= 0) return GDN_EINVAL;
+  if (Wq1 == nullptr) {
+    if (R1 != 0 || y1 != nullptr) return GDN_EINVAL;
+  } else if (R1 <= 0) {
+    return GDN_EINVAL;
+  }
+  if (C % 512 != 0 || R0 % 64 != 0 || (Wq1 != nullptr && R1 % 64 != 0)) return GDN_EUNSUPPORTED;
+  if (C > kProjMaxC || rows > kProjQ4MaxRows || (int64_t)R0 * C > kProjMaxRC ||
+      (int64_t)R1 * C > kProjMaxRC)
+    return GDN_EUNSUPPORTED;
+  if (rows == 0) return GDN_OK;
+  if (!ptr_ok(x) || !ptr_ok(Wq0) || !ptr_ok(y0)) return GDN_EINVAL;
+  if (Wq1 != nullptr && (!ptr_ok(Wq1) || !ptr_ok(y1))) return GDN_EINVAL;
+  const int64_t xb = rows * C * 4, w0b = (int64_t)R0 * C / 16 * 9, y0b = rows * R0 * 4;
+  const int64_t w1b = (int64_t)R1 * C / 16 * 9, y1b = rows * R1 * 4;
+  if (overlaps(y0, y0b, x, xb) || overlaps(y0, y0b, Wq0, w0b) || overlaps(y0, y0b, Wq1, w1b))
+    return GDN_EINVAL;
+  if (Wq1 != nullptr && (overlaps(y1, y1b, x, xb) || overlaps(y1, y1b, Wq0, w0b) ||
+                         overlaps(y1, y1b, Wq1, w1b) || overlaps(y1, y1b, y0, y0b)))
+    return GDN_EINVAL;
+  return enq(gdn::launch_proj_q4(x, rows, C, Wq0, R0, y0, Wq1, R1, y1, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1351,4 +1351,226 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
   return (int)hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Dense layer projections with 4-bit weights
+// ---------------------------------------------------------------------------
+//
+// Up to 16 rows the product is bound by the weight stream, and a 4-bit weight
+// is 0.56 bytes: the matrix-core kernel above, whose 16-row operand is mostly
+// empty at these sizes, would hold it near 1.5 TB/s of weights.  Here a lane
+// owns one output and one of 16 column segments.  It decodes each 32-column
+// block of its weights once (the 4-bit values spread into bytes, one convert
+// each, one exact fma with the block's scale: (n + 8) s - 8 s = n s) and runs
+// one fma chain per row against x, which all lanes of a wave read at the same
+// address (scalar loads).  A workgroup holds 64 outputs x 16 segments; the
+// segment sums are folded in LDS.  Summation order of y[r][o]: 16 equal
+// segments of C, each an ascending fma chain over its columns, then folded
+// left to right: fixed, and independent of the row count.
+//
+// Packed layout, per 64-output group g and 32-column block b (1152 bytes):
+// output 64 g + l holds 16 bytes at 16 l, where byte k of dword d holds
+// u = n + 8 (n the signed 4-bit value) of column 32 b + 8 d + k in its low
+// nibble and of column 32 b + 8 d + 4 + k in its high nibble; then the 64
+// binary16 scales of the block at 1024 + 2 l.
+
+constexpr int Q4_SEGS = 16;
+constexpr int Q4_LANES = 64 * Q4_SEGS;
+constexpr int Q4_BLOCK_BYTES = 1152;
+constexpr int Q4_PF = 4;                       // blocks in flight per wave
+// x staged in LDS when rows x C floats fit this many bytes; else scalar loads
+constexpr int Q4_XLDS_MAX = 96 << 10;
+// a buffer offset beyond every resource's range: the load returns zeros and
+// touches no memory (prefetch slots past a segment's last block)
+constexpr int Q4_OOB = (int)0x80000000u;
+
+struct Q4Problem {
+  const uint8_t *W;
+  float *y;
+  int R;
+  int groups;                                  // R / 64
+};
+struct Q4Args {
+  const float *x;
+  int C;
+  Q4Problem p[2];
+};
+
+template <int NR, bool XLDS>
+__global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
+  __shared__ float red[Q4_SEGS][NR][64];
+  extern __shared__ __align__(16) float xl[];  // [NR][C] when XLDS
+  const int b = (int)xcd_contiguous(blockIdx.x, gridDim.x);
+  const bool second = b >= a.p[0].groups;
+  const uint8_t *W = second ? a.p[1].W : a.p[0].W;
+  float *y = second ? a.p[1].y : a.p[0].y;
+  const int R = second ? a.p[1].R : a.p[0].R;
+  const int g = second ? b - a.p[0].groups : b;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l = threadIdx.x & 63;
+  const int C = a.C, nblk = C / 32, sblk = nblk / Q4_SEGS;
+  const int blk0 = wave * sblk;
+  // one buffer resource over the group's packed bytes (< 2^31 for C <= 2^22)
+  const rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(W + (int64_t)g * nblk * Q4_BLOCK_BYTES), 0, nblk * Q4_BLOCK_BYTES,
+      RSRC_FLAGS);
+
+  u4 qb[Q4_PF];
+  unsigned sb[Q4_PF];
+  // every trip issues its loads (no branch around them, so the wait counts
+  // stay exact and the prefetch depth holds); slots past the segment's end
+  // read out of range
+  auto issue = [&](int slot, int t) {
+    const bool ok = t < sblk;
+    const int soff = __builtin_amdgcn_readfirstlane((blk0 + t) * Q4_BLOCK_BYTES);
+    qb[slot] = __builtin_bit_cast(
+        u4, __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? 16 * l : Q4_OOB, soff,
+                                                  POL_STREAM_LOAD));
+    sb[slot] = __builtin_amdgcn_raw_buffer_load_b16(wr, ok ? 1024 + 2 * l : Q4_OOB, soff,
+                                                    POL_STREAM_LOAD);
+  };
+#pragma unroll
+  for (int p = 0; p < Q4_PF; p++) issue(p, p);
+
+  const float *xs;
+  int xstride;
+  if constexpr (XLDS) {
+    const f4 *src = reinterpret_cast<const f4 *>(a.x);
+    f4 *dst = reinterpret_cast<f4 *>(xl);
+    for (int i = threadIdx.x; i < NR * C / 4; i += Q4_LANES) dst[i] = src[i];
+    __syncthreads();
+    xs = xl + blk0 * 32;
+  } else {
+    xs = a.x + blk0 * 32;
+  }
+  xstride = C;
+
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; r++) acc[r] = 0.f;
+  auto block = [&](const u4 &q, unsigned sbits, int t) {
+    const float sf = (float)__builtin_bit_cast(_Float16, (unsigned short)sbits);
+    const float m8 = -8.f * sf;
+    float w[32];
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      unsigned lo = q[d] & 0x0f0f0f0fu, hi = (q[d] >> 4) & 0x0f0f0f0fu;
+      // opaque to the optimizer, so that each byte converts in one
+      // instruction (v_cvt_f32_ubyte0..3) rather than an extract and a convert
+      __asm__("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        w[8 * d + k] = __builtin_fmaf((float)((lo >> (8 * k)) & 0xffu), sf, m8);
+        w[8 * d + 4 + k] = __builtin_fmaf((float)((hi >> (8 * k)) & 0xffu), sf, m8);
+      }
+    }
+    const float *xb = xs + t * 32;
+#pragma unroll
+    for (int r = 0; r < NR; r++)
+#pragma unroll
+      for (int i = 0; i < 32; i++)
+        acc[r] = __builtin_fmaf(w[i], xb[(int64_t)r * xstride + i], acc[r]);
+  };
+
+  for (int t0 = 0; t0 < sblk; t0 += Q4_PF) {
+#pragma unroll
+    for (int p = 0; p < Q4_PF; p++) {
+      // the slot is consumed before it is refilled, so each load lands in
+      // the register its consumer reads (no copies, no drain at the loop end)
+      const int t = t0 + p;
+      if (t < sblk) block(qb[p], sb[p], t);
+      issue(p, t + Q4_PF);
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < NR; r++) red[wave][r][l] = acc[r];
+  __syncthreads();
+  if (threadIdx.x < NR * 64) {
+    const int r = threadIdx.x >> 6, ll = threadIdx.x & 63;
+    float sum = red[0][r][ll];
+#pragma unroll
+    for (int w = 1; w < Q4_SEGS; w++) sum = sum + red[w][r][ll];
+    y[(int64_t)r * R + 64 * g + ll] = sum;
+  }
+}
+
+// 4-bit packing: thread (group g, block b, lane l) writes output 64 g + l's
+// 16 bytes of block b and its scale.
+__global__ __launch_bounds__(256) void proj_q4_pack_kernel(const uint8_t *q, const uint16_t *scale,
+                                                           uint8_t *Wq, int C, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int l = (int)(i & 63);
+  const int64_t gb = i >> 6;                   // g * (C / 32) + b
+  const int nblk = C / 32;
+  const int64_t g = gb / nblk;
+  const int bb = (int)(gb - g * nblk);
+  const int64_t o = 64 * g + l;
+  const uint8_t *src = q + o * (C / 2) + 16 * bb;
+  auto u = [&](int c) -> unsigned {            // biased value of column c of the block
+    const unsigned by = src[c >> 1];
+    return (((c & 1) ? by >> 4 : by) & 15u) ^ 8u;
+  };
+  u4 out;
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    unsigned wd = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) wd |= (u(8 * d + k) | (u(8 * d + 4 + k) << 4)) << (8 * k);
+    out[d] = wd;
+  }
+  uint8_t *dst = Wq + gb * Q4_BLOCK_BYTES;
+  *reinterpret_cast<u4 *>(dst + 16 * l) = out;
+  reinterpret_cast<uint16_t *>(dst + 1024)[l] = scale[o * nblk + bb];
+}
+
+int launch_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int R, int C,
+                        hipStream_t s) {
+  const int64_t n = (int64_t)R * (C / 32);
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(proj_q4_pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, q,
+                     scale, static_cast<uint8_t *>(Wq), C, n);
+  return (int)hipGetLastError();
+}
+
+template <int NR>
+static void launch_q4_rows(const Q4Args &a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.p[0].groups + a.p[1].groups));
+  const size_t xb = (size_t)NR * a.C * 4;
+  if (xb <= (size_t)Q4_XLDS_MAX)
+    hipLaunchKernelGGL((proj_q4_kernel<NR, true>), grid, dim3(Q4_LANES), xb, s, a);
+  else
+    hipLaunchKernelGGL((proj_q4_kernel<NR, false>), grid, dim3(Q4_LANES), 0, s, a);
+}
+
+int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0, float *y0,
+                   const void *Wq1, int R1, float *y1, hipStream_t s) {
+  if (rows <= 0) return 0;
+  if (rows > 16 || C % (32 * Q4_SEGS) != 0) return (int)hipErrorInvalidValue;
+  Q4Args a{};
+  a.x = x;
+  a.C = C;
+  a.p[0] = Q4Problem{static_cast<const uint8_t *>(Wq0), y0, R0, R0 / 64};
+  a.p[1] = Q4Problem{static_cast<const uint8_t *>(Wq1), y1, R1, Wq1 ? R1 / 64 : 0};
+  switch (rows) {
+    case 1: launch_q4_rows<1>(a, s); break;
+    case 2: launch_q4_rows<2>(a, s); break;
+    case 3: launch_q4_rows<3>(a, s); break;
+    case 4: launch_q4_rows<4>(a, s); break;
+    case 5: launch_q4_rows<5>(a, s); break;
+    case 6: launch_q4_rows<6>(a, s); break;
+    case 7: launch_q4_rows<7>(a, s); break;
+    case 8: launch_q4_rows<8>(a, s); break;
+    case 9: launch_q4_rows<9>(a, s); break;
+    case 10: launch_q4_rows<10>(a, s); break;
+    case 11: launch_q4_rows<11>(a, s); break;
+    case 12: launch_q4_rows<12>(a, s); break;
+    case 13: launch_q4_rows<13>(a, s); break;
+    case 14: launch_q4_rows<14>(a, s); break;
+    case 15: launch_q4_rows<15>(a, s); break;
+    default: launch_q4_rows<16>(a, s); break;
+  }
+  return (int)hipGetLastError();
+}
+
 }  // namespace gdn

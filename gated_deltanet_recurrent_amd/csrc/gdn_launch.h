@@ -59,6 +59,14 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
 // when W1 is non-null, W1 -> y1 [rows][R1] in the same launch.
 // C % 128 == 0, R % 16 == 0.
 int launch_proj_pack(const float *W, float *Wp, int R, int C, hipStream_t s);
+
+// The same projection with 4-bit weights packed by launch_proj_q4_pack from
+// q [R][C/2] bytes and binary16 scales [R][C/32] (9 C / 16 bytes per row);
+// 1 to 16 rows, R % 64 == 0, C % 512 == 0.
+int launch_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int R, int C,
+                        hipStream_t s);
+int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0, float *y0,
+                   const void *Wq1, int R1, float *y1, hipStream_t s);
 int64_t proj_workgroups(int64_t rows, int R0, int R1);
 int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, float *y0,
                 const float *W1, int R1, float *y1, hipStream_t s);

@@ -304,6 +304,60 @@ int gdn_proj(const float *x, int64_t rows, int32_t C,
              const float *W0, int32_t R0, float *y0,
              const float *W1, int32_t R1, float *y1, void *stream);
 
+/*
+ * Bytes of a 4-bit weight matrix [R][C] packed by gdn_proj_q4_pack: 9 C / 16
+ * per row (C / 2 bytes of 4-bit values and C / 32 binary16 scales).
+ * Returns -1 when R or C is not positive, R is not a multiple of 64 or C not a
+ * multiple of 512.
+ */
+int64_t gdn_proj_q4_bytes(int32_t R, int32_t C);
+
+/*
+ * Packing of 4-bit weights for gdn_proj_q4 ("Kestrel_VLLM #24", section 8:
+ * the large projections read 4-bit weights with f32 activations; section 12:
+ * each weight is a signed 4-bit value times a binary16 scale shared by its
+ * block; the per-layer weight size fixes a block of 32).  The source format:
+ *   q [R][C / 2] bytes, element 2 i of a row in the low nibble of byte i and
+ *     element 2 i + 1 in the high nibble, each a two's-complement value -8..7;
+ *   scale [R][C / 32] finite binary16 bit patterns, scale b covering elements
+ *     32 b .. 32 b + 31 of its row.
+ * The packed order, per group g of 64 rows and 32-column block b (1152
+ * bytes): row 64 g + l holds 16 bytes at offset 16 l, where byte k of 32-bit
+ * word d holds n + 8 of column 32 b + 8 d + k in its low nibble and of column
+ * 32 b + 8 d + 4 + k in its high nibble; the 64 scales of the block follow at
+ * offset 1024 + 2 l.  Groups and blocks are stored g-major.  No value is
+ * rounded: the packing is a re-arrangement plus the fixed offset of 8.
+ *   q, scale, Wq: device arrays, 16-byte aligned, Wq of gdn_proj_q4_bytes(R, C)
+ *   bytes, not overlapping the sources.
+ * Errors: GDN_EINVAL for a null or misaligned pointer, R <= 0, C <= 0 or
+ * overlapping arrays; GDN_EUNSUPPORTED when C is not a multiple of 512, R not
+ * a multiple of 64, C > 2^22 or R * C > 2^40.
+ */
+int gdn_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int32_t R, int32_t C,
+                     void *stream);
+
+/*
+ * gdn_proj with 4-bit weights packed by gdn_proj_q4_pack, for 1 to 16 rows
+ * (the decode and draft-verify sizes): y0[r][o] = sum over c of W0[o][c] *
+ * x[r][c], with W0[o][c] = n * s formed exactly in fp32 from the 4-bit value n
+ * and its block's scale s, and y1 likewise from Wq1 in the same launch
+ * ("Kestrel_VLLM #24", section 8 and Fig. 1 caption, steps 1 and 7).
+ * The sum runs in a fixed order of fp32 operations: 16 equal segments of C,
+ * each an ascending chain of fused multiply-adds, then folded left to right.
+ * It differs from a left fold by rounding only, and a row's result does not
+ * depend on the other rows of the call or on their number.
+ *   x [rows][C] fp32; y0 [rows][R0], y1 [rows][R1] fp32; Wq0, Wq1 packed
+ *   (16-byte aligned; Wq1 == NULL requires R1 == 0 and y1 == NULL).
+ * Ownership: every buffer belongs to the caller; nothing is allocated.
+ * Errors: GDN_EINVAL for a null or misaligned pointer, rows < 0, C <= 0,
+ * R <= 0, or an output overlapping an input or the other output;
+ * GDN_EUNSUPPORTED when C is not a multiple of 512, R not a multiple of 64,
+ * C > 2^22, R * C > 2^40 or rows > 16.  rows == 0 is a no-op.
+ */
+int gdn_proj_q4(const float *x, int64_t rows, int32_t C,
+                const void *Wq0, int32_t R0, float *y0,
+                const void *Wq1, int32_t R1, float *y1, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

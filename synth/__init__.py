@@ -117,6 +117,30 @@ def proj_weights(gen, dims, dim=FE_DIM, std=0.02, device="cpu"):
     )
 
 
+def q4_weights(gen, R, C, std=0.02, device="cpu"):
+    """A random 4-bit weight matrix [R][C] in the source format: q uint8
+    [R][C/2] (every byte value equally likely, so every 4-bit value -8..7 in
+    either nibble) and scale float16 [R][C/32], drawn uniform in
+    [0.5, 1.5] x std / 4.61 (4.61 ~ the spread of a uniform 4-bit value), so
+    the decoded weights have about the spread of proj_weights."""
+    q = torch.randint(0, 256, (R, C // 2), generator=gen, dtype=torch.int32, device=device)
+    u = torch.rand((R, C // 32), generator=gen, dtype=torch.float32, device=device)
+    return q.to(torch.uint8), ((0.5 + u) * (std / 4.61)).to(torch.float16)
+
+
+def proj_weights_q4(gen, dims, dim=FE_DIM, std=0.02, device="cpu"):
+    """proj_weights with the three large matrices as 4-bit weights: dict of
+    (q, scale) pairs for W_qkv, W_z, W_out, and the f32 norm_w."""
+    vh, kh, kd, vd = dims
+    cd = conv_dim_of(dims)
+    return dict(
+        W_qkv=q4_weights(gen, cd, dim, std, device),
+        W_z=q4_weights(gen, vh * vd, dim, std, device),
+        W_out=q4_weights(gen, dim, vh * vd, std, device),
+        norm_w=1.0 + _normal(gen, (vd,), 0.1, device),
+    )
+
+
 def frontend_inputs(gen, B, dims, T=1, dim=FE_DIM, ck=CONV_K, device="cpu"):
     """x [T][B][dim] ~ N(0,1); raw conv input xc_raw [T][B][conv_dim] ~ N(0,1);
     initial history hist [B][ck-1][conv_dim] ~ N(0,1)."""
@@ -152,4 +176,6 @@ WORKLOADS = {
             seqs=64, layers=8, dims=DIMS128, gate=None, seed=9),
     10: dict(name="whole-layer speculative verify with f32 projections, 1 sequence x 8 layers, "
                   "M=8 drafts", seqs=1, layers=8, dims=DIMS128, M=8, gate=None, seed=10),
+    11: dict(name="whole-layer decode with 4-bit projections, 1 sequence x 8 layers",
+             seqs=1, layers=8, dims=DIMS128, gate=None, seed=11, q4=True),
 }

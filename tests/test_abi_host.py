@@ -276,3 +276,55 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         gdn.lib()
+
+
+def test_proj_q4_bytes():
+    """Packed 4-bit size: C/2 bytes of values and C/32 binary16 scales per row."""
+    L = gdn.lib()
+    assert L.gdn_proj_q4_bytes(10240, 5120) == 10240 * (5120 // 2 + 5120 // 32 * 2)
+    assert L.gdn_proj_q4_bytes(64, 512) == 64 * 288
+    for R, Cc in ((0, 512), (64, 0), (16, 512), (96, 512), (64, 384), (-64, 512)):
+        assert L.gdn_proj_q4_bytes(R, Cc) == -1, (R, Cc)
+
+
+def test_proj_q4_pack_validation():
+    L = gdn.lib()
+    q, sc, Wq = fp(0), fp(1 << 36), fp(2 << 36)
+    assert L.gdn_proj_q4_pack(q, sc, Wq, 10240, 5120 + 128, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_proj_q4_pack(q, sc, Wq, 10240 + 16, 5120, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_proj_q4_pack(q, sc, Wq, 64, (1 << 22) + 512, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_proj_q4_pack(q, sc, Wq, 0, 5120, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4_pack(q, sc, Wq, 64, -512, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4_pack(NULLS, sc, Wq, 64, 512, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4_pack(q, fp(8), Wq, 64, 512, NULLS) == gdn.GDN_EINVAL   # misaligned
+    # the packed output (64 * 288 bytes) overlapping the values or the scales
+    assert L.gdn_proj_q4_pack(q, sc, fp(8192), 64, 512, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4_pack(q, sc, fp((1 << 36) + 256), 64, 512, NULLS) == gdn.GDN_EINVAL
+
+
+def test_proj_q4_validation():
+    """gdn_proj_q4 refuses bad shapes, more than 16 rows, bad pointers and
+    overlaps before any launch."""
+    L = gdn.lib()
+    x, W0, y0, W1, y1 = (fp(i << 36) for i in range(5))
+    ok = (x, 4, 5120, W0, 10240, y0, W1, 6144, y1, NULLS)
+    for i, bad in ((2, 5120 + 128), (4, 10248), (4, 10240 + 16), (7, 6144 + 32), (1, 17)):
+        args = list(ok)
+        args[i] = bad
+        assert L.gdn_proj_q4(*args) == gdn.GDN_EUNSUPPORTED, (i, bad)
+    for i, bad in ((1, -1), (2, 0), (4, 0), (7, 0)):
+        args = list(ok)
+        args[i] = bad
+        assert L.gdn_proj_q4(*args) == gdn.GDN_EINVAL, (i, bad)
+    assert L.gdn_proj_q4(x, 4, 5120, W0, 10240, y0, NULLS, 16, NULLS, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4(x, 4, 5120, W0, 10240, y0, NULLS, 0, y1, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4(x, 4, 5120, NULLS, 10240, y0, NULLS, 0, NULLS, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4(fp(4), 4, 5120, W0, 10240, y0, NULLS, 0, NULLS,
+                         NULLS) == gdn.GDN_EINVAL
+    # outputs overlapping the packed weights (10240 x 5120 x 9/16 bytes) or each other
+    assert L.gdn_proj_q4(x, 4, 5120, W0, 10240, fp((1 << 36) + 29491200 - 16), NULLS, 0,
+                         NULLS, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4(x, 4, 5120, W0, 10240, y0, W1, 6144, fp((2 << 36) + 256),
+                         NULLS) == gdn.GDN_EINVAL
+    # the end of the weights just before y0 is no overlap; no rows is a no-op
+    assert L.gdn_proj_q4(x, 0, 5120, W0, 10240, y0, W1, 6144, y1, NULLS) == gdn.GDN_OK

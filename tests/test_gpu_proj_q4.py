@@ -1,0 +1,279 @@
+"""GPU parity of the projections with 4-bit weights (gdn_proj_q4_pack,
+gdn_proj_q4), through the C ABI.
+
+The 4-bit reading ("Kestrel_VLLM #24", sections 8 and 12): each weight is a
+signed 4-bit value times the binary16 scale of its block of 32, exact in fp32.
+Floating point: per element |y - r| <= max(1e-5 |r|, 1e-6 sum_c |W[o][c] x[c]|)
+against the oracle's proj_q4 (a strict left fold; the kernel sums in 16
+segments of fused multiply-adds, so the two differ by rounding only).
+Bit-exact: every result when all partial sums are exact (integer-valued x,
+power-of-two scales: any order gives the same bits), a row's result against
+the same row in calls of every other row count, one launch of two products
+against two launches, the packed order against its index definition in
+include/gdn.h, and closed forms (all -8, all 7, one-hot columns).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_recurrent_amd as gdn
+import synth
+from tests.helpers import assert_close, bits_equal, max_rel_pages
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "g", "beta")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    gdn.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def host(t):
+    return np.ascontiguousarray(t.detach().cpu().numpy())
+
+
+def decode_np(q, sc):
+    """4-bit values (low nibble = even element, two's complement) times the
+    block's binary16 scale, with numpy's float16."""
+    q = np.asarray(q, np.uint8)
+    n = np.empty((q.shape[0], 2 * q.shape[1]), np.int16)
+    n[:, 0::2] = q & 15
+    n[:, 1::2] = q >> 4
+    n = np.where(n >= 8, n - 16, n).astype(np.float32)
+    s = np.asarray(sc).view(np.float16).astype(np.float32)
+    return np.ascontiguousarray(n * np.repeat(s, 32, axis=1))
+
+
+def pack_q4_np(q, sc):
+    """The packed order documented in include/gdn.h, by index arithmetic: per
+    64-row group g and 32-column block b, row 64 g + l owns 16 bytes at 16 l,
+    byte k of word d = (n + 8 of column 8 d + k) | (n + 8 of column 8 d + 4 + k)
+    << 4; then the block's 64 scales."""
+    q = np.asarray(q, np.uint8)
+    R, C = q.shape[0], 2 * q.shape[1]
+    nib = np.empty((R, C), np.uint8)
+    nib[:, 0::2] = q & 15
+    nib[:, 1::2] = q >> 4
+    u = (nib ^ 8).reshape(R, C // 32, 4, 2, 4)            # row, block, d, half, k
+    byte = (u[:, :, :, 0, :] | (u[:, :, :, 1, :] << 4)).reshape(R, C // 32, 16)
+    vals = byte.reshape(R // 64, 64, C // 32, 16).transpose(0, 2, 1, 3).reshape(R // 64, C // 32, 1024)
+    scl = np.ascontiguousarray(np.asarray(sc).view(np.uint16).reshape(R // 64, 64, C // 32)
+                               .transpose(0, 2, 1))
+    out = np.concatenate([vals, scl.view(np.uint8).reshape(R // 64, C // 32, 128)], axis=2)
+    return np.ascontiguousarray(out.reshape(R // 64, 36 * C))
+
+
+def q4_operands(seed, rows, R, C):
+    gen = synth.make_gen(seed, "cuda")
+    q, sc = synth.q4_weights(gen, R, C, device="cuda")
+    x = torch.randn((rows, C), generator=gen, device="cuda")
+    return x, q, sc
+
+
+def ref_q4(orc, x, q, sc):
+    y = np.zeros((x.shape[0], q.shape[0]), np.float32)
+    orc.proj_q4(np.ascontiguousarray(x), host(q), host(sc).view(np.uint16), y)
+    return y
+
+
+def proj_floor(x, W):
+    return 1e-6 * (np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T)
+
+
+@pytest.mark.parametrize("R,C", [(64, 512), (192, 1024), (10240, 5120), (5120, 6144)])
+def test_q4_pack_layout(R, C):
+    say(f"proj_q4_pack R={R} C={C}")
+    _, q, sc = q4_operands(61, 1, R, C)
+    Wq = gdn.proj_q4_pack(q, sc)
+    assert Wq.numel() == gdn.proj_q4_bytes(R, C) == R * C * 9 // 16
+    assert bits_equal(host(Wq), pack_q4_np(host(q), host(sc)))
+
+
+@pytest.mark.parametrize("rows,R,C", [(1, 64, 512), (3, 192, 1024), (8, 320, 1536),
+                                      (16, 512, 5120), (1, 10240, 5120), (16, 5120, 6144)])
+def test_q4_exact_when_every_partial_sum_is_exact(orc, rows, R, C):
+    """Integer x in [-3, 3] and power-of-two scales 2^-2 .. 2^2: every product
+    and partial sum is a multiple of 2^-2 below 2^22, so any summation order
+    gives the oracle's bits; a dropped, repeated or misplaced term, a wrong
+    nibble or a wrong scale shows as an exact mismatch."""
+    say(f"proj_q4 exact sums rows={rows} R={R} C={C}")
+    gen = synth.make_gen(70 + rows, "cuda")
+    q = torch.randint(0, 256, (R, C // 2), generator=gen, device="cuda").to(torch.uint8)
+    e = torch.randint(-2, 3, (R, C // 32), generator=gen, device="cuda").float()
+    sc = torch.pow(2.0, e).to(torch.float16)
+    x = torch.randint(-3, 4, (rows, C), generator=gen, device="cuda").float()
+    y = host(gdn.proj_q4(x, gdn.proj_q4_pack(q, sc)))
+    assert bits_equal(y, ref_q4(orc, host(x), q, sc))
+
+
+@pytest.mark.parametrize("rows,R,C", [(1, 64, 512), (5, 320, 1536), (11, 448, 2048),
+                                      (16, 1024, 5120)])
+def test_q4_parity(orc, rows, R, C):
+    say(f"proj_q4 parity rows={rows} R={R} C={C}")
+    x, q, sc = q4_operands(80 + rows, rows, R, C)
+    y = gdn.proj_q4(x, gdn.proj_q4_pack(q, sc))
+    xh = host(x)
+    Wd = decode_np(host(q), host(sc))
+    assert_close(host(y), ref_q4(orc, xh, q, sc), f"proj_q4 {rows}x{R}x{C}", rel=1e-5,
+                 floor=proj_floor(xh, Wd))
+
+
+def test_q4_scales_of_every_kind(orc):
+    """Scales drawn over every finite binary16 pattern of magnitude below 64
+    (zero, subnormals, normals, both signs): the decoded weights stay exact, so
+    the result stays within tolerance of the oracle."""
+    say("proj_q4 any finite scale")
+    rows, R, C = 4, 64, 1024
+    gen = synth.make_gen(91, "cuda")
+    q = torch.randint(0, 256, (R, C // 2), generator=gen, device="cuda").to(torch.uint8)
+    mag = torch.randint(0, 0x5400, (R, C // 32), generator=gen, device="cuda")   # |s| < 64
+    sign = torch.randint(0, 2, (R, C // 32), generator=gen, device="cuda") << 15
+    sc = (mag | sign).to(torch.int32).to(torch.int16)
+    x = torch.randn((rows, C), generator=gen, device="cuda")
+    y4 = gdn.proj_q4(x, gdn.proj_q4_pack(q, sc))
+    Wd = decode_np(host(q), host(sc))
+    assert np.isfinite(Wd).all()
+    xh = host(x)
+    assert_close(host(y4), ref_q4(orc, xh, q, sc), "proj_q4 any scale", rel=1e-5,
+                 floor=proj_floor(xh, Wd))
+
+
+def test_q4_extreme_values_and_one_hot_columns():
+    """All bytes 0x88 (every value -8) or 0x77 (every value 7) with scale 1
+    and x = 1 give -8 C and 7 C exactly; one-hot rows select a decoded column
+    exactly."""
+    say("proj_q4 closed forms")
+    R, C = 64, 512
+    one = torch.ones((R, C // 32), device="cuda").to(torch.float16)
+    x1 = torch.ones((1, C), device="cuda")
+    for byte, val in ((0x88, -8.0), (0x77, 7.0)):
+        q = torch.full((R, C // 2), byte, dtype=torch.uint8, device="cuda")
+        y = host(gdn.proj_q4(x1, gdn.proj_q4_pack(q, one)))
+        assert (y == val * C).all(), (byte, y[0, :4])
+    _, q, sc = q4_operands(97, 1, R, C)
+    cols = [0, 1, 31, 32, 63, 64, 300, C - 1]
+    x = torch.zeros((len(cols), C), device="cuda")
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = host(gdn.proj_q4(x, gdn.proj_q4_pack(q, sc)))
+    Wd = decode_np(host(q), host(sc))
+    for i, c in enumerate(cols):
+        assert bits_equal(y[i], np.ascontiguousarray(Wd[:, c])), c
+
+
+def test_q4_rows_are_independent_and_paired_launch_matches():
+    """A row's bits do not depend on the other rows of the call: a 16-row call
+    against calls over every row count 1..15 (each its own kernel instance);
+    the paired launch (in_proj_qkv + in_proj_z) equals two single launches."""
+    say("proj_q4 row independence, pairing")
+    rows, C = 16, 1024
+    x, q0, s0 = q4_operands(101, rows, 192, C)
+    _, q1, s1 = q4_operands(103, 1, 64, C)
+    W0, W1 = gdn.proj_q4_pack(q0, s0), gdn.proj_q4_pack(q1, s1)
+    full0, full1 = gdn.proj_q4(x, W0, W1)
+    full0, full1 = host(full0), host(full1)
+    assert bits_equal(full0, host(gdn.proj_q4(x, W0)))
+    assert bits_equal(full1, host(gdn.proj_q4(x, W1)))
+    for n in range(1, 16):
+        lo = (5 * n) % (17 - n)
+        part = host(gdn.proj_q4(x[lo:lo + n].contiguous(), W0, W1)[0])
+        assert bits_equal(part, np.ascontiguousarray(full0[lo:lo + n])), (lo, n)
+
+
+def test_q4_refuses_more_than_16_rows_and_accepts_none():
+    say("proj_q4 row limits")
+    x, q, sc = q4_operands(107, 17, 64, 512)
+    W = gdn.proj_q4_pack(q, sc)
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.proj_q4(x, W)
+    assert e.value.rc == gdn.GDN_EUNSUPPORTED
+    y = torch.full((0, 64), 7.0, device="cuda")
+    assert gdn.proj_q4(x[:0], W, y0=y).numel() == 0
+
+
+@pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
+def test_q4_layer_sizes_sampled(orc, dims):
+    """The layer's full projection sizes with 4-bit weights at 1 and 16 rows,
+    in the launches the benchmark times, on rows the oracle recomputes."""
+    vh, kh, kd, vd = dims
+    dim = synth.FE_DIM
+    gen = synth.make_gen(113, "cuda")
+    w = synth.proj_weights_q4(gen, dims, device="cuda")
+    wq = {n: gdn.proj_q4_pack(*w[n]) for n in ("W_qkv", "W_z", "W_out")}
+    for rows, pick in ((1, [0]), (16, [0, 9, 15])):
+        say(f"proj_q4 layer sizes dims={dims} rows={rows}")
+        x = torch.randn((rows, dim), generator=gen, device="cuda")
+        h = torch.randn((rows, vh * vd), generator=gen, device="cuda")
+        xc, z = gdn.proj_q4(x, wq["W_qkv"], wq["W_z"])
+        y = gdn.proj_q4(h, wq["W_out"])
+        xh, hh = host(x)[pick], host(h)[pick]
+        for name, got, inp in (("W_qkv", xc, xh), ("W_z", z, xh), ("W_out", y, hh)):
+            q, sc = w[name]
+            assert_close(host(got)[pick], ref_q4(orc, inp, q, sc), name, rel=1e-5,
+                         floor=proj_floor(inp, decode_np(host(q), host(sc))))
+
+
+def test_q4_layer_decode_chain(orc):
+    """One GDN layer decoding two tokens with 4-bit projections, entirely
+    through the C ABI: each projection matches the oracle's proj_q4 on the
+    GPU's own inputs to it, and the chain matches the oracle's chain under the
+    pages' layer criterion max|err| / max|ref| <= 1e-4 ("Kestrel_VLLM #24",
+    section 6)."""
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    B, dim, T, eps = 2, 512, 2, 1e-6
+    cd = synth.conv_dim_of(dims)
+    say(f"q4 layer chain B={B} dim={dim} T={T}")
+    gen = synth.make_gen(127, "cuda")
+    pw = synth.proj_weights_q4(gen, dims, dim=dim, device="cuda")
+    fw = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
+    S = synth.state(gen, B, dims, device="cuda")
+    hist = torch.randn((B, 3, cd), generator=gen, device="cuda")
+    xs = torch.randn((T, B, dim), generator=gen, device="cuda")
+    big = ("W_qkv", "W_z", "W_out")
+    wq = {n: gdn.proj_q4_pack(*pw[n]) for n in big}
+    W = {n: host(t) for n, t in fw.items()}
+    qh = {n: (host(pw[n][0]), host(pw[n][1]).view(np.uint16)) for n in big}
+    dec = {n: decode_np(*qh[n]) for n in big}
+    S_r, hist_r = host(S), host(hist)
+
+    def proj_r(x, n):
+        y = np.zeros((x.shape[0], qh[n][0].shape[0]), np.float32)
+        orc.proj_q4(np.ascontiguousarray(x), qh[n][0], qh[n][1], y)
+        return y
+
+    for t in range(T):
+        xc, z = gdn.proj_q4(xs[t], wq["W_qkv"], wq["W_z"])
+        fe = gdn.frontend(xs[t], fw["Wa"], fw["Wb"], fw["A_log"], fw["dt_bias"], xc, hist,
+                          fw["conv_w"], dims)
+        out = gdn.step_gated(S, *(fe[n].unsqueeze(0) for n in NAMES),
+                             z.view(1, B, vh, vd), pw["norm_w"], eps)
+        oh = host(out).reshape(B, vh * vd)
+        y = host(gdn.proj_q4(out.view(B, vh * vd), wq["W_out"]))
+        xh = host(xs[t])
+        for name, got, inp in (("W_qkv", host(xc), xh), ("W_z", host(z), xh), ("W_out", y, oh)):
+            assert_close(got, proj_r(inp, name), name, rel=1e-5, floor=proj_floor(inp, dec[name]))
+
+        xc_r, z_r = proj_r(xh, "W_qkv"), proj_r(xh, "W_z")
+        fr = {n: np.zeros(tuple(fe[n].shape), np.float32) for n in NAMES}
+        orc.gdn_frontend(xh, W["Wa"], W["Wb"], W["A_log"], W["dt_bias"], xc_r, hist_r,
+                         W["conv_w"], fr["q"], fr["k"], fr["v"], fr["g"], fr["beta"], dims)
+        o_r = np.zeros((B, vh, vd), np.float32)
+        orc.gdn_step(S_r, *(fr[n] for n in NAMES), o_r, dims)
+        gn_r = np.zeros_like(o_r)
+        orc.gated_norm(o_r, z_r.reshape(B, vh, vd), host(pw["norm_w"]), eps, gn_r)
+        y_r = proj_r(gn_r.reshape(B, vh * vd), "W_out")
+        for b in range(B):
+            assert max_rel_pages(y[b], y_r[b]) <= 1e-4, (t, b)
+    assert max_rel_pages(host(S), S_r) <= 1e-4
