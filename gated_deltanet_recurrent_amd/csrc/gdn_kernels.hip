@@ -1359,13 +1359,20 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 // is 0.56 bytes: the matrix-core kernel above, whose 16-row operand is mostly
 // empty at these sizes, would hold it near 1.5 TB/s of weights.  Here a lane
 // owns one output and one of 16 column segments.  It decodes each 32-column
-// block of its weights once (the 4-bit values spread into bytes, one convert
-// each, one exact fma with the block's scale: (n + 8) s - 8 s = n s) and runs
-// one fma chain per row against x, which all lanes of a wave read at the same
-// address (scalar loads).  A workgroup holds 64 outputs x 16 segments; the
-// segment sums are folded in LDS.  Summation order of y[r][o]: 16 equal
-// segments of C, each an ascending fma chain over its columns, then folded
-// left to right: fixed, and independent of the row count.
+// block of its weights once and runs one fma chain per row against x, which
+// all lanes of a wave read at the same address (scalar loads, the next row's
+// issued before the current row's chain).  A workgroup holds 64 outputs x 16
+// segments; the segment sums are folded in LDS.  Summation order of y[r][o]:
+// 16 equal segments of C, each an ascending fma chain over its columns, then
+// folded left to right: fixed, and independent of the row count.
+//
+// Decode: two 4-bit values are masked into the mantissas of a pair of
+// binary16 numbers in one instruction, (q & m) | 0x6400 6400, giving 1024 + u
+// or 1024 + 16 u (u = n + 8, as packed); one mixed-precision fma per weight
+// then forms n s exactly: (1024 + u) s - 1032 s, or (1024 + 16 u) (s / 16) -
+// 72 s.  Every product is exact in the fma and n s is representable, so the
+// single rounding is exact (1032 s and 72 s are exact in fp32 since 1032 and
+// 72 have two set bits each).
 //
 // Packed layout, per 64-output group g and 32-column block b (1152 bytes):
 // output 64 g + l holds 16 bytes at 16 l, where byte k of dword d holds
@@ -1377,8 +1384,6 @@ constexpr int Q4_SEGS = 16;
 constexpr int Q4_LANES = 64 * Q4_SEGS;
 constexpr int Q4_BLOCK_BYTES = 1152;
 constexpr int Q4_PF = 4;                       // blocks in flight per wave
-// x staged in LDS when rows x C floats fit this many bytes; else scalar loads
-constexpr int Q4_XLDS_MAX = 96 << 10;
 // a buffer offset beyond every resource's range: the load returns zeros and
 // touches no memory (prefetch slots past a segment's last block)
 constexpr int Q4_OOB = (int)0x80000000u;
@@ -1395,10 +1400,23 @@ struct Q4Args {
   Q4Problem p[2];
 };
 
-template <int NR, bool XLDS>
+// (x & m) | c in one instruction: the mask from a scalar register, the
+// constant from a vector register (a VOP3 takes no literal on this target)
+static __device__ __forceinline__ unsigned and_or(unsigned x, unsigned m, unsigned c) {
+  unsigned r;
+  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
+static __device__ __forceinline__ float half_lo(unsigned p) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(p & 0xffffu));
+}
+static __device__ __forceinline__ float half_hi(unsigned p) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(p >> 16));
+}
+
+template <int NR>
 __global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
   __shared__ float red[Q4_SEGS][NR][64];
-  extern __shared__ __align__(16) float xl[];  // [NR][C] when XLDS
   const int b = (int)xcd_contiguous(blockIdx.x, gridDim.x);
   const bool second = b >= a.p[0].groups;
   const uint8_t *W = second ? a.p[1].W : a.p[0].W;
@@ -1413,6 +1431,7 @@ __global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
   const rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(W + (int64_t)g * nblk * Q4_BLOCK_BYTES), 0, nblk * Q4_BLOCK_BYTES,
       RSRC_FLAGS);
+  const float *xs = a.x + blk0 * 32;           // this wave's segment of row 0
 
   u4 qb[Q4_PF];
   unsigned sb[Q4_PF];
@@ -1431,44 +1450,47 @@ __global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
 #pragma unroll
   for (int p = 0; p < Q4_PF; p++) issue(p, p);
 
-  const float *xs;
-  int xstride;
-  if constexpr (XLDS) {
-    const f4 *src = reinterpret_cast<const f4 *>(a.x);
-    f4 *dst = reinterpret_cast<f4 *>(xl);
-    for (int i = threadIdx.x; i < NR * C / 4; i += Q4_LANES) dst[i] = src[i];
-    __syncthreads();
-    xs = xl + blk0 * 32;
-  } else {
-    xs = a.x + blk0 * 32;
-  }
-  xstride = C;
-
   float acc[NR];
 #pragma unroll
   for (int r = 0; r < NR; r++) acc[r] = 0.f;
+  unsigned base = 0x64006400u;                 // binary16 1024 in both halves
+  __asm__("" : "+v"(base));                    // kept in a vector register
   auto block = [&](const u4 &q, unsigned sbits, int t) {
     const float sf = (float)__builtin_bit_cast(_Float16, (unsigned short)sbits);
-    const float m8 = -8.f * sf;
+    const float m1032 = -1032.f * sf, sf16 = 0.0625f * sf, m72 = -72.f * sf;
     float w[32];
 #pragma unroll
     for (int d = 0; d < 4; d++) {
-      unsigned lo = q[d] & 0x0f0f0f0fu, hi = (q[d] >> 4) & 0x0f0f0f0fu;
-      // opaque to the optimizer, so that each byte converts in one
-      // instruction (v_cvt_f32_ubyte0..3) rather than an extract and a convert
-      __asm__("" : "+v"(lo), "+v"(hi));
-#pragma unroll
-      for (int k = 0; k < 4; k++) {
-        w[8 * d + k] = __builtin_fmaf((float)((lo >> (8 * k)) & 0xffu), sf, m8);
-        w[8 * d + 4 + k] = __builtin_fmaf((float)((hi >> (8 * k)) & 0xffu), sf, m8);
-      }
+      const unsigned qd = q[d], q8 = qd >> 8;
+      const unsigned p0 = and_or(qd, 0x000f000fu, base);   // nibbles 0, 4: 1024 + u
+      const unsigned p1 = and_or(qd, 0x00f000f0u, base);   // nibbles 1, 5: 1024 + 16 u
+      const unsigned p2 = and_or(q8, 0x000f000fu, base);   // nibbles 2, 6
+      const unsigned p3 = and_or(q8, 0x00f000f0u, base);   // nibbles 3, 7
+      // nibble j of word d is column 8 d + j / 2 + 4 (j % 2)
+      w[8 * d + 0] = __builtin_fmaf(half_lo(p0), sf, m1032);
+      w[8 * d + 2] = __builtin_fmaf(half_hi(p0), sf, m1032);
+      w[8 * d + 4] = __builtin_fmaf(half_lo(p1), sf16, m72);
+      w[8 * d + 6] = __builtin_fmaf(half_hi(p1), sf16, m72);
+      w[8 * d + 1] = __builtin_fmaf(half_lo(p2), sf, m1032);
+      w[8 * d + 3] = __builtin_fmaf(half_hi(p2), sf, m1032);
+      w[8 * d + 5] = __builtin_fmaf(half_lo(p3), sf16, m72);
+      w[8 * d + 7] = __builtin_fmaf(half_hi(p3), sf16, m72);
     }
     const float *xb = xs + t * 32;
+    float xc[32], xn[32];
 #pragma unroll
-    for (int r = 0; r < NR; r++)
+    for (int i = 0; i < 32; i++) xc[i] = xb[i];
 #pragma unroll
-      for (int i = 0; i < 32; i++)
-        acc[r] = __builtin_fmaf(w[i], xb[(int64_t)r * xstride + i], acc[r]);
+    for (int r = 0; r < NR; r++) {
+      if (r + 1 < NR) {
+#pragma unroll
+        for (int i = 0; i < 32; i++) xn[i] = xb[(int64_t)(r + 1) * C + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 32; i++) acc[r] = __builtin_fmaf(w[i], xc[i], acc[r]);
+#pragma unroll
+      for (int i = 0; i < 32; i++) xc[i] = xn[i];
+    }
   };
 
   for (int t0 = 0; t0 < sblk; t0 += Q4_PF) {
@@ -1535,12 +1557,8 @@ int launch_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int R
 
 template <int NR>
 static void launch_q4_rows(const Q4Args &a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.p[0].groups + a.p[1].groups));
-  const size_t xb = (size_t)NR * a.C * 4;
-  if (xb <= (size_t)Q4_XLDS_MAX)
-    hipLaunchKernelGGL((proj_q4_kernel<NR, true>), grid, dim3(Q4_LANES), xb, s, a);
-  else
-    hipLaunchKernelGGL((proj_q4_kernel<NR, false>), grid, dim3(Q4_LANES), 0, s, a);
+  hipLaunchKernelGGL(proj_q4_kernel<NR>, dim3((unsigned)(a.p[0].groups + a.p[1].groups)),
+                     dim3(Q4_LANES), 0, s, a);
 }
 
 int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0, float *y0,
