@@ -15,7 +15,10 @@ Other --config values time the other workloads: 0 single sequence x 1 layer
 x 64 sequential steps (launch latency), 2 speculative verify (mark + 8-row
 step_m + rollback), 3 front end + step, 4 large batch, 5 large batch at
 kd=vd=64, 6 speculative verify of one layer with its front end, 7 the
-batched decode of workload 1 with the gated RMSNorm fused on the output.
+batched decode of workload 1 with the gated RMSNorm fused on the output,
+8 and 9 whole layers (projections, front end, gated step) with f32 weights
+for 1 and 64 sequences, 10 the whole-layer speculative verify, 11 whole
+layers with 4-bit weights and binary16 block scales for 1 sequence.
 """
 from __future__ import annotations
 
@@ -105,6 +108,20 @@ def timed(fn, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / 1e3            # seconds
+
+
+def timed_graph(fn, steps, warmup):
+    """fn(0) captured once as a HIP graph, then `steps` replays timed like
+    timed(): the launch chain without host gaps (fn must allocate nothing)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn(0)
+    return timed(lambda i: graph.replay(), steps, warmup)
 
 
 def cpu_threads():
@@ -407,18 +424,26 @@ PEAK_MFMA_F32_TFLOPS = 157.3
 def bench_layer(cfg, steps, warmup, cpu):
     """Whole GDN layers: in_proj_qkv + in_proj_z (one launch), front end,
     recurrence with the gated RMSNorm, out_proj; the output of layer l is the
-    input x of layer l + 1.  Weights are f32, packed once before timing."""
+    input x of layer l + 1.  Weights are f32 (gdn_proj) or, with cfg["q4"],
+    4-bit values with binary16 block scales (gdn_proj_q4), packed once before
+    timing.  The chain is timed both as launched from the host and as one HIP
+    graph replay (no host gaps); the projections alone are timed as graph
+    replays of their L launches."""
     dims = cfg["dims"]
     vh, kh, kd, vd = dims
     B, L, dim = cfg["seqs"], cfg["layers"], synth.FE_DIM
+    q4 = bool(cfg.get("q4"))
     cd = synth.conv_dim_of(dims)
     gen = synth.make_gen(cfg["seed"], "cuda")
     layers = []
     for _ in range(L):
-        pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
+        if q4:
+            pw = synth.proj_weights_q4(gen, dims, dim=dim, device="cuda")
+        else:
+            pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
         lw = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
         for n in ("W_qkv", "W_z", "W_out"):
-            packed = gdn.proj_pack(pw[n])
+            packed = gdn.proj_q4_pack(*pw[n]) if q4 else gdn.proj_pack(pw[n])
             del pw[n]
             lw[n] = packed
         lw["norm_w"] = pw["norm_w"]
@@ -426,6 +451,7 @@ def bench_layer(cfg, steps, warmup, cpu):
         lw["hist"] = torch.randn((B, 3, cd), generator=gen, device="cuda")
         layers.append(lw)
     torch.cuda.empty_cache()
+    proj = gdn.proj_q4 if q4 else gdn.proj
     x0 = torch.randn((B, dim), generator=gen, device="cuda")
     xs = [torch.empty((B, dim), device="cuda") for _ in range(L)]
     xc = torch.empty((B, cd), device="cuda")
@@ -438,69 +464,65 @@ def bench_layer(cfg, steps, warmup, cpu):
     def one(i):
         x = x0
         for l, w in enumerate(layers):
-            gdn.proj(x, w["W_qkv"], w["W_z"], y0=xc, y1=z)
+            proj(x, w["W_qkv"], w["W_z"], y0=xc, y1=z)
             gdn.frontend(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], xc, w["hist"],
                          w["conv_w"], dims, out=fe)
             gdn.step_gated(w["S"], *(fe[n].unsqueeze(0) for n in NAMES), z.view(1, B, vh, vd),
                            w["norm_w"], 1e-6, out=out)
-            gdn.proj(out.view(B, vh * vd), w["W_out"], y0=xs[l])
+            proj(out.view(B, vh * vd), w["W_out"], y0=xs[l])
             x = xs[l]
 
     dt = timed(one, steps, warmup)
-    # the same chain captured once as a HIP graph and replayed (no launch gaps
-    # from the host); it contains no memset node
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        one(0)
-    torch.cuda.current_stream().wait_stream(side)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        one(0)
-    dt_g = timed(lambda i: graph.replay(), steps, 2)
+    # the same chain captured once as a HIP graph and replayed; it contains
+    # no memset node
+    dt_g = timed_graph(one, steps, 2)
     # the projections alone, layer after layer, for the kernel roofline
-    dt_in = timed(lambda i: [gdn.proj(x0, w["W_qkv"], w["W_z"], y0=xc, y1=z) for w in layers],
-                  steps, 1)
+    dt_in = timed_graph(lambda i: [proj(x0, w["W_qkv"], w["W_z"], y0=xc, y1=z) for w in layers],
+                        steps, 1)
     h = out.view(B, vh * vd)
-    dt_out = timed(lambda i: [gdn.proj(h, w["W_out"], y0=xs[0]) for w in layers], steps, 1)
+    dt_out = timed_graph(lambda i: [proj(h, w["W_out"], y0=xs[0]) for w in layers], steps, 1)
     # read+write floor over one packed weight matrix (also calibrates counters)
     flat = layers[0]["W_qkv"].view(-1)
-    floor = copy_floor(layers[0]["W_qkv"])
-    w_in = (cd + vh * vd) * dim * 4
-    w_out = dim * vh * vd * 4
+    floor = copy_floor(layers[0]["W_qkv"].view(torch.float32) if q4 else layers[0]["W_qkv"])
+    wbytes = (lambda R, C_: R * C_ * 9 // 16) if q4 else (lambda R, C_: R * C_ * 4)
+    w_in = wbytes(cd + vh * vd, dim)
+    w_out = wbytes(dim, vh * vd)
     in_bytes = w_in + B * dim * 4 + B * (cd + vh * vd) * 4
     out_bytes = w_out + B * vh * vd * 4 + B * dim * 4
     in_flop = 2 * B * (cd + vh * vd) * dim
     out_flop = 2 * B * dim * vh * vd
     t_in, t_out = dt_in / (steps * L), dt_out / (steps * L)
-    key = f"layer_b{B}"
+    kname = "proj_q4_kernel" if q4 else "proj_kernel"
+    key = f"layer_q4_b{B}" if q4 else f"layer_b{B}"
     ridge = PEAK_MFMA_F32_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)     # ~19.7 flop/B
-    if in_flop / in_bytes >= ridge:   # 2B flop per 4-byte weight: matrix cores from B ~ 40
+    if not q4 and in_flop / in_bytes >= ridge:   # 2B flop per 4-byte weight: from B ~ 40
         roof = dict(bound="mfma", achieved=round(in_flop / t_in / 1e12, 2),
                     peak=PEAK_MFMA_F32_TFLOPS, unit="TFLOP/s",
                     frac=round(in_flop / t_in / 1e12 / PEAK_MFMA_F32_TFLOPS, 4),
-                    traffic=recorded_traffic(key, in_bytes, kernel="proj_kernel"))
+                    traffic=recorded_traffic(key, in_bytes, kernel=kname))
     else:
         roof = dict(bound="hbm", achieved=round(in_bytes / t_in / 1e9, 1), peak=PEAK_HBM_GBPS,
                     unit="GB/s", frac=round(in_bytes / t_in / 1e9 / PEAK_HBM_GBPS, 4),
-                    traffic=recorded_traffic(key, in_bytes, kernel="proj_kernel"))
-    res = dict(value=B * vh * L * steps / dt, ms_per_step=dt / steps * 1e3, roofline=roof,
-               extra=dict(kernel="proj_kernel (in_proj_qkv + in_proj_z, one launch)",
+                    traffic=recorded_traffic(key, in_bytes, kernel=kname))
+    desc = ("gdn_proj_q4" if q4 else "gdn_proj")
+    res = dict(value=B * vh * L * steps / dt_g, ms_per_step=dt_g / steps * 1e3, roofline=roof,
+               extra=dict(kernel=f"{kname} (in_proj_qkv + in_proj_z, one launch)",
+                          timing="value and ms_per_step: the chain as one HIP graph replay",
                           in_proj_us=round(t_in * 1e6, 2), out_proj_us=round(t_out * 1e6, 2),
                           in_proj_GBps=round(in_bytes / t_in / 1e9, 1),
                           out_proj_GBps=round(out_bytes / t_out / 1e9, 1),
                           in_proj_TFLOPs=round(in_flop / t_in / 1e12, 2),
                           out_proj_TFLOPs=round(out_flop / t_out / 1e12, 2),
-                          layer_us=round(dt / (steps * L) * 1e6, 2),
+                          layer_us_host_launched=round(dt / (steps * L) * 1e6, 2),
                           layer_us_graph_replay=round(dt_g / (steps * L) * 1e6, 2),
                           in_proj_bytes_per_launch=in_bytes, in_proj_flop_per_launch=in_flop,
                           weights_GB=round(L * (w_in + w_out) / 1e9, 3),
-                          copy_floor_GBps=round(floor, 1), copy_bytes=flat.numel() * 4,
-                          kernel_source_sha256_16=kernel_hash("proj_kernel")))
+                          copy_floor_GBps=round(floor, 1), copy_bytes=flat.numel() * flat.element_size(),
+                          kernel_source_sha256_16=kernel_hash(kname)))
     return res, dict(workload=cfg["name"], units=B * L, seqs=B, layers=L, vh=vh, kd=kd,
-                     dim=dim, conv_dim=cd,
-                     chain="gdn_proj(W_qkv, W_z) + gdn_frontend + gdn_step_gated + "
-                           "gdn_proj(W_out) per layer")
+                     dim=dim, conv_dim=cd, weights="4-bit + binary16 scale per 32" if q4 else "f32",
+                     chain=f"{desc}(W_qkv, W_z) + gdn_frontend + gdn_step_gated + "
+                           f"{desc}(W_out) per layer")
 
 
 def bench_layer_verify(cfg, steps, warmup, cpu):
@@ -597,7 +619,7 @@ def main():
     cfg["id"] = args.config
     runner = {0: bench_latency, 2: bench_verify, 3: bench_frontend,
               6: bench_verify_frontend, 8: bench_layer, 9: bench_layer,
-              10: bench_layer_verify}.get(args.config, bench_decode)
+              10: bench_layer_verify, 11: bench_layer}.get(args.config, bench_decode)
     res, config = runner(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
     line = dict(metric=METRIC, value=round(res["value"], 1), unit="head-steps/s", n_gpus=1,
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(res["ms_per_step"], 5),
