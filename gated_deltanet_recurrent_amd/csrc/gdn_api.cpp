@@ -470,14 +470,14 @@ int gdn_proj(const float *x, int64_t rows, int32_t C, const float *W0, int32_t R
 }
 
 int64_t gdn_proj_q4_bytes(int32_t R, int32_t C) {
-  if (R <= 0 || C <= 0 || R % 64 != 0 || C % 512 != 0) return -1;
+  if (R <= 0 || C <= 0 || R % 64 != 0 || C % 1024 != 0) return -1;
   return (int64_t)R * C / 16 * 9;
 }
 
 int gdn_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int32_t R, int32_t C,
                      void *stream) {
   if (R <= 0 || C <= 0) return GDN_EINVAL;
-  if (C % 512 != 0 || R % 64 != 0) return GDN_EUNSUPPORTED;
+  if (C % 1024 != 0 || R % 64 != 0) return GDN_EUNSUPPORTED;
   if (C > kProjMaxC || (int64_t)R * C > kProjMaxRC) return GDN_EUNSUPPORTED;
   if (!ptr_ok(q) || !ptr_ok(scale) || !ptr_ok(Wq)) return GDN_EINVAL;
   const int64_t qb = (int64_t)R * C / 2, sb = (int64_t)R * C / 16, wb = qb + sb;
@@ -493,7 +493,7 @@ int gdn_proj_q4(const float *x, int64_t rows, int32_t C, const void *Wq0, int32_
   } else if (R1 <= 0) {
     return GDN_EINVAL;
   }
-  if (C % 512 != 0 || R0 % 64 != 0 || (Wq1 != nullptr && R1 % 64 != 0)) return GDN_EUNSUPPORTED;
+  if (C % 1024 != 0 || R0 % 64 != 0 || (Wq1 != nullptr && R1 % 64 != 0)) return GDN_EUNSUPPORTED;
   if (C > kProjMaxC || rows > kProjQ4MaxRows || (int64_t)R0 * C > kProjMaxRC ||
       (int64_t)R1 * C > kProjMaxRC)
     return GDN_EUNSUPPORTED;

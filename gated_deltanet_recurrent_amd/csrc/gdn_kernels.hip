@@ -1358,13 +1358,25 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 // Up to 16 rows the product is bound by the weight stream, and a 4-bit weight
 // is 0.56 bytes: the matrix-core kernel above, whose 16-row operand is mostly
 // empty at these sizes, would hold it near 1.5 TB/s of weights.  Here a lane
-// owns one output and one of 16 column segments.  It decodes each 32-column
-// block of its weights once and runs one fma chain per row against x, which
-// all lanes of a wave read at the same address (scalar loads, the next row's
-// issued before the current row's chain).  A workgroup holds 64 outputs x 16
-// segments; the segment sums are folded in LDS.  Summation order of y[r][o]:
-// 16 equal segments of C, each an ascending fma chain over its columns, then
-// folded left to right: fixed, and independent of the row count.
+// owns one output and a column segment.  It decodes each 32-column block of
+// its weights once and runs one fma chain per row against x, which all lanes
+// of a wave read at the same address (scalar loads, the next row's issued
+// before the current row's chain).
+//
+// Summation order of y[r][o], fixed and independent of the row count: C is
+// cut into 32 equal segments, each an ascending fma chain over its columns;
+// segments 0..15 are folded left to right, so are segments 16..31, and the
+// two sums are added.  Two launch shapes compute exactly that:
+//  - one workgroup per 64-output group (16 waves; wave w chains segments w
+//    and 16 + w into separate accumulators; both folds in LDS), for launches
+//    with enough groups to fill the chip;
+//  - two workgroups per group (workgroup h, wave w: segment 16 h + w), each
+//    folding its 16 segment sums and adding the result into y, which a fill
+//    kernel zeroed first.  With exactly two addends on +0 the result does not
+//    depend on their arrival order (fp addition is commutative, and a chain
+//    started at +0 never ends at -0), so it is bit-identical to the first
+//    shape.  Used when the launch has fewer groups than the chip has CUs
+//    (out_proj: 80 groups).
 //
 // Decode: two 4-bit values are masked into the mantissas of a pair of
 // binary16 numbers in one instruction, (q & m) | 0x6400 6400, giving 1024 + u
@@ -1380,19 +1392,23 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 // nibble and of column 32 b + 8 d + 4 + k in its high nibble; then the 64
 // binary16 scales of the block at 1024 + 2 l.
 
-constexpr int Q4_SEGS = 16;
+// launches with fewer 64-output groups than this take two workgroups per group
+#ifndef GDN_Q4_SPLIT_BELOW
+#define GDN_Q4_SPLIT_BELOW 256
+#endif
+constexpr int Q4_SEGS = 16;                    // waves per workgroup
 constexpr int Q4_LANES = 64 * Q4_SEGS;
 constexpr int Q4_BLOCK_BYTES = 1152;
 constexpr int Q4_PF = 4;                       // blocks in flight per wave
 // a buffer offset beyond every resource's range: the load returns zeros and
-// touches no memory (prefetch slots past a segment's last block)
+// touches no memory (prefetch slots past a wave's last block)
 constexpr int Q4_OOB = (int)0x80000000u;
 
 struct Q4Problem {
   const uint8_t *W;
   float *y;
   int R;
-  int groups;                                  // R / 64
+  int wgs;                                     // workgroups: R / 64, x 2 when split
 };
 struct Q4Args {
   const float *x;
@@ -1414,33 +1430,43 @@ static __device__ __forceinline__ float half_hi(unsigned p) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(p >> 16));
 }
 
-template <int NR>
+// SPLIT: two workgroups per group (each one half of C), else one
+template <int NR, bool SPLIT>
 __global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
   __shared__ float red[Q4_SEGS][NR][64];
   const int b = (int)xcd_contiguous(blockIdx.x, gridDim.x);
-  const bool second = b >= a.p[0].groups;
+  const bool second = b >= a.p[0].wgs;
   const uint8_t *W = second ? a.p[1].W : a.p[0].W;
   float *y = second ? a.p[1].y : a.p[0].y;
   const int R = second ? a.p[1].R : a.p[0].R;
-  const int g = second ? b - a.p[0].groups : b;
+  const int gh = second ? b - a.p[0].wgs : b;
+  const int g = SPLIT ? gh >> 1 : gh;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int l = threadIdx.x & 63;
-  const int C = a.C, nblk = C / 32, sblk = nblk / Q4_SEGS;
-  const int blk0 = wave * sblk;
+  const int C = a.C, nblk = C / 32, sblk = nblk / (2 * Q4_SEGS);
+  // this wave's segments: one (SPLIT) or w and 16 + w, as trips t = 0 ..
+  // nt - 1 over blocks; trip t of the second segment starts at sblk
+  const int seg0 = SPLIT ? (gh & 1) * Q4_SEGS + wave : wave;
+  const int nt = SPLIT ? sblk : 2 * sblk;
+  auto blk_of = [&](int t) {
+    if constexpr (SPLIT)
+      return seg0 * sblk + t;
+    else
+      return t < sblk ? seg0 * sblk + t : (Q4_SEGS + wave) * sblk + (t - sblk);
+  };
   // one buffer resource over the group's packed bytes (< 2^31 for C <= 2^22)
   const rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(W + (int64_t)g * nblk * Q4_BLOCK_BYTES), 0, nblk * Q4_BLOCK_BYTES,
       RSRC_FLAGS);
-  const float *xs = a.x + blk0 * 32;           // this wave's segment of row 0
 
   u4 qb[Q4_PF];
   unsigned sb[Q4_PF];
   // every trip issues its loads (no branch around them, so the wait counts
-  // stay exact and the prefetch depth holds); slots past the segment's end
-  // read out of range
+  // stay exact and the prefetch depth holds); slots past the last trip read
+  // out of range
   auto issue = [&](int slot, int t) {
-    const bool ok = t < sblk;
-    const int soff = __builtin_amdgcn_readfirstlane((blk0 + t) * Q4_BLOCK_BYTES);
+    const bool ok = t < nt;
+    const int soff = __builtin_amdgcn_readfirstlane((ok ? blk_of(t) : 0) * Q4_BLOCK_BYTES);
     qb[slot] = __builtin_bit_cast(
         u4, __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? 16 * l : Q4_OOB, soff,
                                                   POL_STREAM_LOAD));
@@ -1450,12 +1476,15 @@ __global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
 #pragma unroll
   for (int p = 0; p < Q4_PF; p++) issue(p, p);
 
-  float acc[NR];
+  float acc0[NR], acc1[NR];                    // first and second segment
 #pragma unroll
-  for (int r = 0; r < NR; r++) acc[r] = 0.f;
+  for (int r = 0; r < NR; r++) acc0[r] = acc1[r] = 0.f;
   unsigned base = 0x64006400u;                 // binary16 1024 in both halves
   __asm__("" : "+v"(base));                    // kept in a vector register
-  auto block = [&](const u4 &q, unsigned sbits, int t) {
+  // x at the start of each of the wave's segments, row 0
+  const float *xs0 = a.x + seg0 * sblk * 32;
+  const float *xs1 = SPLIT ? xs0 : a.x + (Q4_SEGS + wave) * sblk * 32;
+  auto block = [&](const u4 &q, unsigned sbits, const float *xb, float (&acc)[NR]) {
     const float sf = (float)__builtin_bit_cast(_Float16, (unsigned short)sbits);
     const float m1032 = -1032.f * sf, sf16 = 0.0625f * sf, m72 = -72.f * sf;
     float w[32];
@@ -1476,7 +1505,6 @@ __global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
       w[8 * d + 5] = __builtin_fmaf(half_lo(p3), sf16, m72);
       w[8 * d + 7] = __builtin_fmaf(half_hi(p3), sf16, m72);
     }
-    const float *xb = xs + t * 32;
     float xc[32], xn[32];
 #pragma unroll
     for (int i = 0; i < 32; i++) xc[i] = xb[i];
@@ -1493,27 +1521,57 @@ __global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
     }
   };
 
-  for (int t0 = 0; t0 < sblk; t0 += Q4_PF) {
+  for (int t0 = 0; t0 < nt; t0 += Q4_PF) {
 #pragma unroll
     for (int p = 0; p < Q4_PF; p++) {
       // the slot is consumed before it is refilled, so each load lands in
       // the register its consumer reads (no copies, no drain at the loop end)
       const int t = t0 + p;
-      if (t < sblk) block(qb[p], sb[p], t);
+      if (t < nt) {
+        if (SPLIT || t < sblk)
+          block(qb[p], sb[p], xs0 + t * 32, acc0);
+        else
+          block(qb[p], sb[p], xs1 + (t - sblk) * 32, acc1);
+      }
       issue(p, t + Q4_PF);
     }
   }
 
+  // left fold of the workgroup's 16 segment sums (per accumulator set)
+  const int r_f = threadIdx.x >> 6, l_f = threadIdx.x & 63;
+  auto fold = [&](float (&acc)[NR]) -> float {
 #pragma unroll
-  for (int r = 0; r < NR; r++) red[wave][r][l] = acc[r];
-  __syncthreads();
-  if (threadIdx.x < NR * 64) {
-    const int r = threadIdx.x >> 6, ll = threadIdx.x & 63;
-    float sum = red[0][r][ll];
+    for (int r = 0; r < NR; r++) red[wave][r][l] = acc[r];
+    __syncthreads();
+    float sum = 0.f;
+    if (threadIdx.x < NR * 64) {
+      sum = red[0][r_f][l_f];
 #pragma unroll
-    for (int w = 1; w < Q4_SEGS; w++) sum = sum + red[w][r][ll];
-    y[(int64_t)r * R + 64 * g + ll] = sum;
+      for (int w = 1; w < Q4_SEGS; w++) sum = sum + red[w][r_f][l_f];
+    }
+    return sum;
+  };
+  float sum = fold(acc0);
+  if constexpr (!SPLIT) {
+    __syncthreads();                           // every fold read before the next writes
+    sum = sum + fold(acc1);
   }
+  if (threadIdx.x < NR * 64) {
+    float *dst = y + (int64_t)r_f * R + 64 * g + l_f;
+    if constexpr (SPLIT)
+      atomicAdd(dst, sum);                     // two addends on +0: order-free
+    else
+      *dst = sum;
+  }
+}
+
+__global__ __launch_bounds__(256) void q4_zero_kernel(float *y0, int64_t n0, float *y1,
+                                                      int64_t n1) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n0)
+    y0[i] = 0.f;
+  else if (i - n0 < n1)
+    y1[i - n0] = 0.f;
 }
 
 // 4-bit packing: thread (group g, block b, lane l) writes output 64 g + l's
@@ -1556,37 +1614,50 @@ int launch_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int R
 }
 
 template <int NR>
-static void launch_q4_rows(const Q4Args &a, hipStream_t s) {
-  hipLaunchKernelGGL(proj_q4_kernel<NR>, dim3((unsigned)(a.p[0].groups + a.p[1].groups)),
-                     dim3(Q4_LANES), 0, s, a);
+static void launch_q4_rows(const Q4Args &a, bool split, hipStream_t s) {
+  const dim3 grid((unsigned)(a.p[0].wgs + a.p[1].wgs));
+  if (split)
+    hipLaunchKernelGGL((proj_q4_kernel<NR, true>), grid, dim3(Q4_LANES), 0, s, a);
+  else
+    hipLaunchKernelGGL((proj_q4_kernel<NR, false>), grid, dim3(Q4_LANES), 0, s, a);
 }
 
 int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0, float *y0,
                    const void *Wq1, int R1, float *y1, hipStream_t s) {
   if (rows <= 0) return 0;
-  if (rows > 16 || C % (32 * Q4_SEGS) != 0) return (int)hipErrorInvalidValue;
+  if (rows > 16 || C % (64 * Q4_SEGS) != 0) return (int)hipErrorInvalidValue;
+  // two workgroups per group when one per group would leave CUs idle (both
+  // shapes give the same bits)
+  const int groups = R0 / 64 + (Wq1 ? R1 / 64 : 0);
+  const bool split = groups < GDN_Q4_SPLIT_BELOW;
+  const int f = split ? 2 : 1;
   Q4Args a{};
   a.x = x;
   a.C = C;
-  a.p[0] = Q4Problem{static_cast<const uint8_t *>(Wq0), y0, R0, R0 / 64};
-  a.p[1] = Q4Problem{static_cast<const uint8_t *>(Wq1), y1, R1, Wq1 ? R1 / 64 : 0};
+  a.p[0] = Q4Problem{static_cast<const uint8_t *>(Wq0), y0, R0, R0 / 64 * f};
+  a.p[1] = Q4Problem{static_cast<const uint8_t *>(Wq1), y1, R1, Wq1 ? R1 / 64 * f : 0};
+  if (split) {
+    const int64_t n0 = rows * R0, n1 = Wq1 ? rows * R1 : 0;
+    hipLaunchKernelGGL(q4_zero_kernel, dim3((unsigned)((n0 + n1 + 255) / 256)), dim3(256), 0, s,
+                       y0, n0, y1, n1);
+  }
   switch (rows) {
-    case 1: launch_q4_rows<1>(a, s); break;
-    case 2: launch_q4_rows<2>(a, s); break;
-    case 3: launch_q4_rows<3>(a, s); break;
-    case 4: launch_q4_rows<4>(a, s); break;
-    case 5: launch_q4_rows<5>(a, s); break;
-    case 6: launch_q4_rows<6>(a, s); break;
-    case 7: launch_q4_rows<7>(a, s); break;
-    case 8: launch_q4_rows<8>(a, s); break;
-    case 9: launch_q4_rows<9>(a, s); break;
-    case 10: launch_q4_rows<10>(a, s); break;
-    case 11: launch_q4_rows<11>(a, s); break;
-    case 12: launch_q4_rows<12>(a, s); break;
-    case 13: launch_q4_rows<13>(a, s); break;
-    case 14: launch_q4_rows<14>(a, s); break;
-    case 15: launch_q4_rows<15>(a, s); break;
-    default: launch_q4_rows<16>(a, s); break;
+    case 1: launch_q4_rows<1>(a, split, s); break;
+    case 2: launch_q4_rows<2>(a, split, s); break;
+    case 3: launch_q4_rows<3>(a, split, s); break;
+    case 4: launch_q4_rows<4>(a, split, s); break;
+    case 5: launch_q4_rows<5>(a, split, s); break;
+    case 6: launch_q4_rows<6>(a, split, s); break;
+    case 7: launch_q4_rows<7>(a, split, s); break;
+    case 8: launch_q4_rows<8>(a, split, s); break;
+    case 9: launch_q4_rows<9>(a, split, s); break;
+    case 10: launch_q4_rows<10>(a, split, s); break;
+    case 11: launch_q4_rows<11>(a, split, s); break;
+    case 12: launch_q4_rows<12>(a, split, s); break;
+    case 13: launch_q4_rows<13>(a, split, s); break;
+    case 14: launch_q4_rows<14>(a, split, s); break;
+    case 15: launch_q4_rows<15>(a, split, s); break;
+    default: launch_q4_rows<16>(a, split, s); break;
   }
   return (int)hipGetLastError();
 }

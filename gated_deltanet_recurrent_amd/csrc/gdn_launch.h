@@ -62,7 +62,7 @@ int launch_proj_pack(const float *W, float *Wp, int R, int C, hipStream_t s);
 
 // The same projection with 4-bit weights packed by launch_proj_q4_pack from
 // q [R][C/2] bytes and binary16 scales [R][C/32] (9 C / 16 bytes per row);
-// 1 to 16 rows, R % 64 == 0, C % 512 == 0.
+// 1 to 16 rows, R % 64 == 0, C % 1024 == 0.
 int launch_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int R, int C,
                         hipStream_t s);
 int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0, float *y0,

@@ -308,7 +308,7 @@ int gdn_proj(const float *x, int64_t rows, int32_t C,
  * Bytes of a 4-bit weight matrix [R][C] packed by gdn_proj_q4_pack: 9 C / 16
  * per row (C / 2 bytes of 4-bit values and C / 32 binary16 scales).
  * Returns -1 when R or C is not positive, R is not a multiple of 64 or C not a
- * multiple of 512.
+ * multiple of 1024.
  */
 int64_t gdn_proj_q4_bytes(int32_t R, int32_t C);
 
@@ -330,7 +330,7 @@ int64_t gdn_proj_q4_bytes(int32_t R, int32_t C);
  *   q, scale, Wq: device arrays, 16-byte aligned, Wq of gdn_proj_q4_bytes(R, C)
  *   bytes, not overlapping the sources.
  * Errors: GDN_EINVAL for a null or misaligned pointer, R <= 0, C <= 0 or
- * overlapping arrays; GDN_EUNSUPPORTED when C is not a multiple of 512, R not
+ * overlapping arrays; GDN_EUNSUPPORTED when C is not a multiple of 1024, R not
  * a multiple of 64, C > 2^22 or R * C > 2^40.
  */
 int gdn_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int32_t R, int32_t C,
@@ -342,16 +342,18 @@ int gdn_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int32_t 
  * x[r][c], with W0[o][c] = n * s formed exactly in fp32 from the 4-bit value n
  * and its block's scale s, and y1 likewise from Wq1 in the same launch
  * ("Kestrel_VLLM #24", section 8 and Fig. 1 caption, steps 1 and 7).
- * The sum runs in a fixed order of fp32 operations: 16 equal segments of C,
- * each an ascending chain of fused multiply-adds, then folded left to right.
- * It differs from a left fold by rounding only, and a row's result does not
- * depend on the other rows of the call or on their number.
+ * The sum runs in a fixed order of fp32 operations: C is cut into 32 equal
+ * segments, each an ascending chain of fused multiply-adds; segments 0..15
+ * are folded left to right, so are segments 16..31, and the two sums are
+ * added.  It differs from a left fold by rounding only, and a row's result
+ * does not depend on the other rows of the call, on their number, or on
+ * whether the matrix shares the launch with a second one.
  *   x [rows][C] fp32; y0 [rows][R0], y1 [rows][R1] fp32; Wq0, Wq1 packed
  *   (16-byte aligned; Wq1 == NULL requires R1 == 0 and y1 == NULL).
  * Ownership: every buffer belongs to the caller; nothing is allocated.
  * Errors: GDN_EINVAL for a null or misaligned pointer, rows < 0, C <= 0,
  * R <= 0, or an output overlapping an input or the other output;
- * GDN_EUNSUPPORTED when C is not a multiple of 512, R not a multiple of 64,
+ * GDN_EUNSUPPORTED when C is not a multiple of 1024, R not a multiple of 64,
  * C > 2^22, R * C > 2^40 or rows > 16.  rows == 0 is a no-op.
  */
 int gdn_proj_q4(const float *x, int64_t rows, int32_t C,

@@ -282,8 +282,8 @@ def test_proj_q4_bytes():
     """Packed 4-bit size: C/2 bytes of values and C/32 binary16 scales per row."""
     L = gdn.lib()
     assert L.gdn_proj_q4_bytes(10240, 5120) == 10240 * (5120 // 2 + 5120 // 32 * 2)
-    assert L.gdn_proj_q4_bytes(64, 512) == 64 * 288
-    for R, Cc in ((0, 512), (64, 0), (16, 512), (96, 512), (64, 384), (-64, 512)):
+    assert L.gdn_proj_q4_bytes(64, 1024) == 64 * 576
+    for R, Cc in ((0, 1024), (64, 0), (16, 1024), (96, 1024), (64, 512), (64, 1536), (-64, 1024)):
         assert L.gdn_proj_q4_bytes(R, Cc) == -1, (R, Cc)
 
 
@@ -292,14 +292,14 @@ def test_proj_q4_pack_validation():
     q, sc, Wq = fp(0), fp(1 << 36), fp(2 << 36)
     assert L.gdn_proj_q4_pack(q, sc, Wq, 10240, 5120 + 128, NULLS) == gdn.GDN_EUNSUPPORTED
     assert L.gdn_proj_q4_pack(q, sc, Wq, 10240 + 16, 5120, NULLS) == gdn.GDN_EUNSUPPORTED
-    assert L.gdn_proj_q4_pack(q, sc, Wq, 64, (1 << 22) + 512, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_proj_q4_pack(q, sc, Wq, 64, (1 << 22) + 1024, NULLS) == gdn.GDN_EUNSUPPORTED
     assert L.gdn_proj_q4_pack(q, sc, Wq, 0, 5120, NULLS) == gdn.GDN_EINVAL
-    assert L.gdn_proj_q4_pack(q, sc, Wq, 64, -512, NULLS) == gdn.GDN_EINVAL
-    assert L.gdn_proj_q4_pack(NULLS, sc, Wq, 64, 512, NULLS) == gdn.GDN_EINVAL
-    assert L.gdn_proj_q4_pack(q, fp(8), Wq, 64, 512, NULLS) == gdn.GDN_EINVAL   # misaligned
-    # the packed output (64 * 288 bytes) overlapping the values or the scales
-    assert L.gdn_proj_q4_pack(q, sc, fp(8192), 64, 512, NULLS) == gdn.GDN_EINVAL
-    assert L.gdn_proj_q4_pack(q, sc, fp((1 << 36) + 256), 64, 512, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4_pack(q, sc, Wq, 64, -1024, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4_pack(NULLS, sc, Wq, 64, 1024, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4_pack(q, fp(8), Wq, 64, 1024, NULLS) == gdn.GDN_EINVAL   # misaligned
+    # the packed output (64 * 576 bytes) overlapping the values or the scales
+    assert L.gdn_proj_q4_pack(q, sc, fp(8192), 64, 1024, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_proj_q4_pack(q, sc, fp((1 << 36) + 256), 64, 1024, NULLS) == gdn.GDN_EINVAL
 
 
 def test_proj_q4_validation():
@@ -308,7 +308,8 @@ def test_proj_q4_validation():
     L = gdn.lib()
     x, W0, y0, W1, y1 = (fp(i << 36) for i in range(5))
     ok = (x, 4, 5120, W0, 10240, y0, W1, 6144, y1, NULLS)
-    for i, bad in ((2, 5120 + 128), (4, 10248), (4, 10240 + 16), (7, 6144 + 32), (1, 17)):
+    for i, bad in ((2, 5120 + 128), (2, 5120 + 512), (4, 10248), (4, 10240 + 16), (7, 6144 + 32),
+                   (1, 17)):
         args = list(ok)
         args[i] = bad
         assert L.gdn_proj_q4(*args) == gdn.GDN_EUNSUPPORTED, (i, bad)

@@ -4,12 +4,13 @@ gdn_proj_q4), through the C ABI.
 The 4-bit reading ("Kestrel_VLLM #24", sections 8 and 12): each weight is a
 signed 4-bit value times the binary16 scale of its block of 32, exact in fp32.
 Floating point: per element |y - r| <= max(1e-5 |r|, 1e-6 sum_c |W[o][c] x[c]|)
-against the oracle's proj_q4 (a strict left fold; the kernel sums in 16
-segments of fused multiply-adds, so the two differ by rounding only).
+against the oracle's proj_q4 (a strict left fold; the kernel sums 32 segments
+of fused multiply-adds in two folds of 16, so the two differ by rounding only).
 Bit-exact: every result when all partial sums are exact (integer-valued x,
 power-of-two scales: any order gives the same bits), a row's result against
 the same row in calls of every other row count, one launch of two products
-against two launches, the packed order against its index definition in
+against two launches, the two launch shapes (one or two workgroups per output
+group) against each other, the packed order against its index definition in
 include/gdn.h, and closed forms (all -8, all 7, one-hot columns).
 """
 import numpy as np
@@ -91,7 +92,7 @@ def proj_floor(x, W):
     return 1e-6 * (np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T)
 
 
-@pytest.mark.parametrize("R,C", [(64, 512), (192, 1024), (10240, 5120), (5120, 6144)])
+@pytest.mark.parametrize("R,C", [(64, 1024), (192, 2048), (10240, 5120), (5120, 6144)])
 def test_q4_pack_layout(R, C):
     say(f"proj_q4_pack R={R} C={C}")
     _, q, sc = q4_operands(61, 1, R, C)
@@ -100,8 +101,9 @@ def test_q4_pack_layout(R, C):
     assert bits_equal(host(Wq), pack_q4_np(host(q), host(sc)))
 
 
-@pytest.mark.parametrize("rows,R,C", [(1, 64, 512), (3, 192, 1024), (8, 320, 1536),
-                                      (16, 512, 5120), (1, 10240, 5120), (16, 5120, 6144)])
+@pytest.mark.parametrize("rows,R,C", [(1, 64, 1024), (3, 192, 2048), (8, 320, 3072),
+                                      (16, 512, 5120), (1, 10240, 5120), (16, 5120, 6144),
+                                      (5, 16384, 1024)])
 def test_q4_exact_when_every_partial_sum_is_exact(orc, rows, R, C):
     """Integer x in [-3, 3] and power-of-two scales 2^-2 .. 2^2: every product
     and partial sum is a multiple of 2^-2 below 2^22, so any summation order
@@ -117,8 +119,8 @@ def test_q4_exact_when_every_partial_sum_is_exact(orc, rows, R, C):
     assert bits_equal(y, ref_q4(orc, host(x), q, sc))
 
 
-@pytest.mark.parametrize("rows,R,C", [(1, 64, 512), (5, 320, 1536), (11, 448, 2048),
-                                      (16, 1024, 5120)])
+@pytest.mark.parametrize("rows,R,C", [(1, 64, 1024), (5, 320, 3072), (11, 448, 2048),
+                                      (16, 1024, 5120), (2, 16384, 1024)])
 def test_q4_parity(orc, rows, R, C):
     say(f"proj_q4 parity rows={rows} R={R} C={C}")
     x, q, sc = q4_operands(80 + rows, rows, R, C)
@@ -134,7 +136,7 @@ def test_q4_scales_of_every_kind(orc):
     (zero, subnormals, normals, both signs): the decoded weights stay exact, so
     the result stays within tolerance of the oracle."""
     say("proj_q4 any finite scale")
-    rows, R, C = 4, 64, 1024
+    rows, R, C = 4, 64, 2048
     gen = synth.make_gen(91, "cuda")
     q = torch.randint(0, 256, (R, C // 2), generator=gen, device="cuda").to(torch.uint8)
     mag = torch.randint(0, 0x5400, (R, C // 32), generator=gen, device="cuda")   # |s| < 64
@@ -154,7 +156,7 @@ def test_q4_extreme_values_and_one_hot_columns():
     and x = 1 give -8 C and 7 C exactly; one-hot rows select a decoded column
     exactly."""
     say("proj_q4 closed forms")
-    R, C = 64, 512
+    R, C = 64, 1024
     one = torch.ones((R, C // 32), device="cuda").to(torch.float16)
     x1 = torch.ones((1, C), device="cuda")
     for byte, val in ((0x88, -8.0), (0x77, 7.0)):
@@ -162,7 +164,7 @@ def test_q4_extreme_values_and_one_hot_columns():
         y = host(gdn.proj_q4(x1, gdn.proj_q4_pack(q, one)))
         assert (y == val * C).all(), (byte, y[0, :4])
     _, q, sc = q4_operands(97, 1, R, C)
-    cols = [0, 1, 31, 32, 63, 64, 300, C - 1]
+    cols = [0, 1, 31, 32, 63, 64, 300, 511, 512, C - 1]
     x = torch.zeros((len(cols), C), device="cuda")
     for i, c in enumerate(cols):
         x[i, c] = 1.0
@@ -191,9 +193,32 @@ def test_q4_rows_are_independent_and_paired_launch_matches():
         assert bits_equal(part, np.ascontiguousarray(full0[lo:lo + n])), (lo, n)
 
 
+def test_q4_launch_shapes_agree_bit_for_bit():
+    """A launch with fewer 64-output groups than CUs takes two workgroups per
+    group (half sums added into y); a larger one takes one.  The same matrix
+    alone (192 outputs: split) and paired with a 16384-output matrix (one
+    workgroup per group) gives the same bits, at 1, 7 and 16 rows; so does
+    the large matrix alone (one workgroup per group) against its half-size
+    slices (split)."""
+    say("proj_q4 launch shapes")
+    C = 2048
+    _, q0, s0 = q4_operands(131, 1, 192, C)
+    _, q1, s1 = q4_operands(137, 1, 16384, C)
+    W0, W1 = gdn.proj_q4_pack(q0, s0), gdn.proj_q4_pack(q1, s1)
+    W1a, W1b = gdn.proj_q4_pack(q1[:8192].contiguous(), s1[:8192].contiguous()), \
+        gdn.proj_q4_pack(q1[8192:].contiguous(), s1[8192:].contiguous())
+    for rows in (1, 7, 16):
+        x = torch.randn((rows, C), generator=synth.make_gen(139 + rows, "cuda"), device="cuda")
+        alone = host(gdn.proj_q4(x, W0))
+        paired, big = gdn.proj_q4(x, W0, W1)
+        assert bits_equal(alone, host(paired)), rows
+        halves = np.concatenate([host(gdn.proj_q4(x, W1a)), host(gdn.proj_q4(x, W1b))], axis=1)
+        assert bits_equal(host(big), halves), rows
+
+
 def test_q4_refuses_more_than_16_rows_and_accepts_none():
     say("proj_q4 row limits")
-    x, q, sc = q4_operands(107, 17, 64, 512)
+    x, q, sc = q4_operands(107, 17, 64, 1024)
     W = gdn.proj_q4_pack(q, sc)
     with pytest.raises(gdn.GdnError) as e:
         gdn.proj_q4(x, W)
@@ -232,7 +257,7 @@ def test_q4_layer_decode_chain(orc):
     section 6)."""
     dims = synth.DIMS128
     vh, kh, kd, vd = dims
-    B, dim, T, eps = 2, 512, 2, 1e-6
+    B, dim, T, eps = 2, 1024, 2, 1e-6
     cd = synth.conv_dim_of(dims)
     say(f"q4 layer chain B={B} dim={dim} T={T}")
     gen = synth.make_gen(127, "cuda")
