@@ -18,7 +18,8 @@ kd=vd=64, 6 speculative verify of one layer with its front end, 7 the
 batched decode of workload 1 with the gated RMSNorm fused on the output,
 8 and 9 whole layers (projections, front end, gated step) with f32 weights
 for 1 and 64 sequences, 10 the whole-layer speculative verify, 11 whole
-layers with 4-bit weights and binary16 block scales for 1 sequence.
+layers with 4-bit weights and binary16 block scales for 1 sequence, 12 the
+whole-layer speculative verify with 4-bit weights.
 """
 from __future__ import annotations
 
@@ -530,18 +531,26 @@ def bench_layer_verify(cfg, steps, warmup, cpu):
     projections over all M*B rows, the M-row front end without advancing the
     history, the gated outputs without advancing the state, out_proj over all
     rows, then commit of per-sequence accepted lengths (device array).  The
-    output of layer l (its M rows) is the input of layer l + 1."""
+    output of layer l (its M rows) is the input of layer l + 1.  Weights are
+    f32 or, with cfg["q4"], 4-bit with binary16 block scales.  The cycle is
+    timed as one HIP graph replay (value; every replay commits the same
+    accepted lengths) and as launched from the host (accepted lengths cycled
+    over 8 draws)."""
     dims = cfg["dims"]
     vh, kh, kd, vd = dims
     B, L, M, dim = cfg["seqs"], cfg["layers"], cfg["M"], synth.FE_DIM
+    q4 = bool(cfg.get("q4"))
     cd = synth.conv_dim_of(dims)
     gen = synth.make_gen(cfg["seed"], "cuda")
     layers = []
     for _ in range(L):
-        pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
+        if q4:
+            pw = synth.proj_weights_q4(gen, dims, dim=dim, device="cuda")
+        else:
+            pw = synth.proj_weights(gen, dims, dim=dim, device="cuda")
         lw = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
         for n in ("W_qkv", "W_z", "W_out"):
-            packed = gdn.proj_pack(pw[n])
+            packed = gdn.proj_q4_pack(*pw[n]) if q4 else gdn.proj_pack(pw[n])
             del pw[n]
             lw[n] = packed
         lw["norm_w"] = pw["norm_w"]
@@ -565,37 +574,46 @@ def bench_layer_verify(cfg, steps, warmup, cpu):
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     rows_in = [fe[n] for n in NAMES]
 
+    proj = gdn.proj_q4 if q4 else gdn.proj
+
     def one(i):
         x = x0
         for l, w in enumerate(layers):
-            gdn.proj(x.view(rows, dim), w["W_qkv"], w["W_z"], y0=xc, y1=z)
+            proj(x.view(rows, dim), w["W_qkv"], w["W_z"], y0=xc, y1=z)
             gdn.frontend_verify_m(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"],
                                   xc.view(M, B, cd), w["hist"], w["conv_w"], dims, out=fe)
             gdn.verify_m_gated(w["S"], *rows_in, z.view(M, B, vh, vd), w["norm_w"], 1e-6,
                                out=out)
-            gdn.proj(out.view(rows, vh * vd), w["W_out"], y0=xs[l].view(rows, dim))
+            proj(out.view(rows, vh * vd), w["W_out"], y0=xs[l].view(rows, dim))
             gdn.commit(w["S"], accs[i % 8], *rows_in, hist=w["hist"],
                        xc_raw=xc.view(M, B, cd), status=status)
             x = xs[l]
 
     dt = timed(one, steps, warmup)
-    dt_in = timed(lambda i: [gdn.proj(x0.view(rows, dim), w["W_qkv"], w["W_z"], y0=xc, y1=z)
-                             for w in layers], steps, 1)
-    in_bytes = (cd + vh * vd) * dim * 4 + rows * dim * 4 + rows * (cd + vh * vd) * 4
+    dt_g = timed_graph(one, steps, 2)
+    dt_in = timed_graph(lambda i: [proj(x0.view(rows, dim), w["W_qkv"], w["W_z"], y0=xc, y1=z)
+                                   for w in layers], steps, 1)
+    wb = 9 / 16 if q4 else 4
+    in_bytes = int((cd + vh * vd) * dim * wb) + rows * dim * 4 + rows * (cd + vh * vd) * 4
     t_in = dt_in / (steps * L)
     roof = dict(bound="hbm", achieved=round(in_bytes / t_in / 1e9, 1), peak=PEAK_HBM_GBPS,
                 unit="GB/s", frac=round(in_bytes / t_in / 1e9 / PEAK_HBM_GBPS, 4), traffic=None)
-    res = dict(value=B * vh * M * L * steps / dt, ms_per_step=dt / steps * 1e3, roofline=roof,
+    kname = "proj_q4_kernel" if q4 else "proj_kernel"
+    desc = "gdn_proj_q4" if q4 else "gdn_proj"
+    res = dict(value=B * vh * M * L * steps / dt_g, ms_per_step=dt_g / steps * 1e3, roofline=roof,
                extra=dict(value_counts="drafted head-steps per second of the full cycle",
-                          layer_us=round(dt / (steps * L) * 1e6, 2),
+                          timing="value and ms_per_step: the cycle as one HIP graph replay",
+                          layer_us_graph_replay=round(dt_g / (steps * L) * 1e6, 2),
+                          layer_us_host_launched=round(dt / (steps * L) * 1e6, 2),
                           in_proj_us=round(t_in * 1e6, 2),
-                          kernel="proj_kernel (in_proj_qkv + in_proj_z over M*B rows)",
+                          kernel=f"{kname} (in_proj_qkv + in_proj_z over M*B rows)",
                           in_proj_bytes_per_launch=in_bytes,
+                          kernel_source_sha256_16=kernel_hash(kname),
                           mean_accepted=float(np.mean([a.float().mean().item() for a in accs]))))
     return res, dict(workload=cfg["name"], units=B * L, seqs=B, layers=L, M=M, vh=vh, kd=kd,
-                     dim=dim, conv_dim=cd,
-                     chain="gdn_proj(W_qkv, W_z) + gdn_frontend_verify_m + gdn_verify_m_gated + "
-                           "gdn_proj(W_out) + gdn_commit per layer")
+                     dim=dim, conv_dim=cd, weights="4-bit + binary16 scale per 32" if q4 else "f32",
+                     chain=f"{desc}(W_qkv, W_z) + gdn_frontend_verify_m + gdn_verify_m_gated + "
+                           f"{desc}(W_out) + gdn_commit per layer")
 
 
 def main():
@@ -619,7 +637,8 @@ def main():
     cfg["id"] = args.config
     runner = {0: bench_latency, 2: bench_verify, 3: bench_frontend,
               6: bench_verify_frontend, 8: bench_layer, 9: bench_layer,
-              10: bench_layer_verify, 11: bench_layer}.get(args.config, bench_decode)
+              10: bench_layer_verify, 11: bench_layer,
+              12: bench_layer_verify}.get(args.config, bench_decode)
     res, config = runner(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
     line = dict(metric=METRIC, value=round(res["value"], 1), unit="head-steps/s", n_gpus=1,
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(res["ms_per_step"], 5),

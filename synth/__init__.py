@@ -178,4 +178,7 @@ WORKLOADS = {
                   "M=8 drafts", seqs=1, layers=8, dims=DIMS128, M=8, gate=None, seed=10),
     11: dict(name="whole-layer decode with 4-bit projections, 1 sequence x 8 layers",
              seqs=1, layers=8, dims=DIMS128, gate=None, seed=11, q4=True),
+    12: dict(name="whole-layer speculative verify with 4-bit projections, 1 sequence x 8 "
+                  "layers, M=8 drafts", seqs=1, layers=8, dims=DIMS128, M=8, gate=None, seed=12,
+             q4=True),
 }
