@@ -429,6 +429,104 @@ void recur_wide_kernel(RecurArgs a) {
   }
 }
 
+// ----- wide geometry, several steps ---------------------------------------
+//
+// Up to MC steps per call for launches with few tiles (a handful of units,
+// where the deep geometry leaves most CUs idle and each step waits on a
+// 256-lane tile): the wide lane layout, four times the lanes per tile, with
+// the deep kernel's step loop (all rows staged at once; the output of step
+// m - 1 is completed by wave 1 in parallel with wave 0's S^T k of step m).
+// Same canonical tree, so the same bits as the deep and single-step kernels.
+template <int KD, bool GATED>
+__global__ __launch_bounds__(Geo<KD>::LANES) void recur_widem_kernel(RecurArgs a) {
+  using G = Geo<KD>;
+  constexpr int LANES = G::LANES;
+  __shared__ Stage<KD, GATED> sb;
+  __shared__ f4 s_red_k[G::NW][G::CG];
+  __shared__ f4 s_red_o[G::NW][G::CG];
+  __shared__ f4 s_tmp[G::CG];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int cg = t % G::CG, rg = t / G::CG;
+  const TileIdx ti = tile_index(a, KD * KD);
+  const int steps = ti.steps;          // 0 .. M <= MC
+  // an in-place update with nothing to run leaves the tile as it is
+  if (steps == 0 && a.S_src == a.S_dst && a.snap == nullptr) return;
+  const rsrc_t src = buf_rsrc(a.S_src + ti.tile_off, KD * KD * 4);
+  const int lane_off = (rg * KD + 4 * cg) * 4;
+
+  ChunkRegs<KD, LANES, GATED> cr;
+  if (steps > 0) chunk_load<KD, LANES, GATED>(cr, a, t, ti.unit, ti.head, ti.hh, 0, steps);
+
+  // few tiles: the state stays cache-resident between calls (default policy)
+  f4 s[G::R];
+#pragma unroll
+  for (int j = 0; j < G::R; j++) s[j] = ld_stream<true>(src, lane_off, j * (G::RG * KD * 4));
+  if (a.snap != nullptr) {            // fused mark: the tile as loaded, before the steps
+    const rsrc_t snp = buf_rsrc(a.snap + ti.tile_off, KD * KD * 4);
+#pragma unroll
+    for (int j = 0; j < G::R; j++) st_stream<false>(snp, lane_off, j * (G::RG * KD * 4), s[j]);
+  }
+
+  const float *zprev = nullptr;
+  if (steps > 0) {
+    chunk_store<KD, LANES, GATED>(sb, cr, t, steps);
+    __syncthreads();
+    for (int r = 0; r < steps; r++) {
+      const float alpha = sb.alpha[r];
+      const f4 kk = lds4(&sb.k[r][rg * 4]);
+      // decay, then S^T k over the decayed state
+      f4 p = splat(0.0f);
+#pragma unroll
+      for (int j = 0; j < G::R; j++) {
+        s[j] = s[j] * alpha;
+        p = fma4(s[j], splat(kk[j]), p);
+      }
+      p = wave_fold<KD>(p);
+      if (lane < G::CG) s_red_k[wave][lane] = p;
+      __syncthreads();
+      if (wave == 0) {
+        const f4 kv = tile_sum<KD>(s_red_k, lane);
+        if (lane < G::CG) s_tmp[lane] = (lds4(&sb.v[r][4 * lane]) - kv) * sb.beta[r];
+      } else if (wave == 1 && r > 0 && a.o != nullptr) {
+        // the previous step's output, in parallel with wave 0's S^T k
+        const f4 ov = tile_sum<KD>(s_red_o, lane);
+        const int64_t prow = (int64_t)(r - 1) * a.n_units + ti.unit;
+        emit_o<KD, GATED>(a, prow, ti.head, lane % G::CG, lane < G::CG, ov, zprev);
+      }
+      __syncthreads();
+      const f4 tmp = s_tmp[cg];
+      const f4 qq = lds4(&sb.q[r][rg * 4]);
+      // rank-1 update, then S^T q with the updated state
+      p = splat(0.0f);
+#pragma unroll
+      for (int j = 0; j < G::R; j++) {
+        s[j] = fma4(splat(kk[j]), tmp, s[j]);
+        p = fma4(s[j], splat(qq[j]), p);
+      }
+      p = wave_fold<KD>(p);
+      if (lane < G::CG) s_red_o[wave][lane] = p;
+      if constexpr (GATED) zprev = &sb.z[r][0];
+    }
+  }
+
+  if (a.S_dst != nullptr) {            // null: outputs only, the state is left as it was
+    const rsrc_t dst = buf_rsrc(a.S_dst + ti.tile_off, KD * KD * 4);
+#pragma unroll
+    for (int j = 0; j < G::R; j++) st_stream<true>(dst, lane_off, j * (G::RG * KD * 4), s[j]);
+  }
+
+  if (steps > 0) {
+    __syncthreads();
+    if (wave == 0 && a.o != nullptr) {
+      const f4 ov = tile_sum<KD>(s_red_o, lane);
+      const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
+      emit_o<KD, GATED>(a, urow, ti.head, lane % G::CG, lane < G::CG, ov, zprev);
+    }
+  }
+}
+
 // ----- deep geometry -------------------------------------------------------
 //
 // Lane (cg, L) holds row groups 4L .. 4L+3 (16 rows x 4 columns) and forms
@@ -575,8 +673,12 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
   }
 }
 
-// Calls with M >= 2 rows per unit run the deep geometry; single steps the
-// wide one.
+// Single steps run the wide geometry.  Calls with M >= 2 rows per unit run
+// the deep geometry, except launches of fewer than GDN_WIDEM_BELOW tiles with
+// M <= MC, which run the wide one step after step (same bits either way).
+#ifndef GDN_WIDEM_BELOW
+#define GDN_WIDEM_BELOW 1024
+#endif
 
 int recur_lanes(int kd) { return kd == 128 ? Geo<128>::LANES : Geo<64>::LANES; }
 
@@ -602,6 +704,8 @@ static void launch_recur_kd(const RecurArgs &a, int64_t tiles, hipStream_t s) {
       hipLaunchKernelGGL((recur_wide_kernel<KD, false, GATED, 1>), grid, dim3(Geo<KD>::LANES), 0,
                          s, a);
     }
+  } else if (a.M <= MC && tiles < GDN_WIDEM_BELOW) {
+    hipLaunchKernelGGL((recur_widem_kernel<KD, GATED>), grid, dim3(Geo<KD>::LANES), 0, s, a);
   } else {
     if (a.M <= MC)
       hipLaunchKernelGGL((recur_deep_kernel<KD, false, GATED>), grid, dim3(Deep<KD>::LANES), 0, s, a);

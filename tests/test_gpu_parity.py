@@ -181,6 +181,44 @@ def test_step_m_bit_exact_and_parity(orc, dims, M):
     assert_close(host(S), S_h, "S step_m")
 
 
+@pytest.mark.parametrize("dims,N", [(synth.DIMS128, 24), (synth.DIMS64, 11)])
+@pytest.mark.parametrize("M", [2, 8])
+def test_m_step_geometries_agree(dims, N, M):
+    """Launches of fewer than 1024 tiles with M <= 8 run the wide geometry step
+    after step, larger ones the deep geometry: a launch over N units (>= 1024
+    tiles) against launches over slices of 1 and 3 units, bit for bit, for
+    step_m, the gated step, verify_m_gated (no state store) and commit with
+    per-unit counts (including 0 and M)."""
+    say(f"M-step geometries dims={dims} N={N} M={M}")
+    vh, vd = dims[0], dims[3]
+    assert N * vh >= 1024
+    gen = synth.make_gen(41 + M, "cuda")
+    S0 = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    z = torch.randn((M, N, vh, vd), generator=gen, device="cuda")
+    w = 1.0 + 0.1 * torch.randn((vd,), generator=gen, device="cuda")
+    acc = torch.tensor([(3 * u) % (M + 1) for u in range(N)], dtype=torch.int32, device="cuda")
+
+    def run(lo, hi):
+        sl = {n: inp[n][:, lo:hi].contiguous() for n in NAMES}
+        zz = z[:, lo:hi].contiguous()
+        S = S0[lo:hi].clone()
+        o = host(gdn.step_m(S, *(sl[n] for n in NAMES)))
+        Sg = S0[lo:hi].clone()
+        og = host(gdn.step_gated(Sg, *(sl[n] for n in NAMES), zz, w, 1e-6))
+        Sv = S0[lo:hi].clone()
+        ov = host(gdn.verify_m_gated(Sv, *(sl[n] for n in NAMES), zz, w, 1e-6))
+        gdn.commit(Sv, acc[lo:hi].contiguous(), *(sl[n] for n in NAMES))
+        return o, host(S), og, host(Sg), ov, host(Sv)
+
+    full = run(0, N)
+    for lo, hi in ((0, 1), (N - 3, N), (N // 2, N // 2 + 1)):
+        part = run(lo, hi)
+        for i, (a, b) in enumerate(zip(full, part)):
+            sl = (slice(None), slice(lo, hi)) if a.ndim == 4 and i % 2 == 0 else slice(lo, hi)
+            assert bits_equal(np.ascontiguousarray(a[sl]), b), (lo, hi, i)
+
+
 @pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
 def test_mark_rollback_bit_exact(orc, dims):
     """mark -> step_m(M) -> rollback(accepted): each unit equals accepted[u]
