@@ -119,6 +119,22 @@ def test_q4_exact_when_every_partial_sum_is_exact(orc, rows, R, C):
     assert bits_equal(y, ref_q4(orc, host(x), q, sc))
 
 
+@pytest.mark.parametrize("rows,R,C", [(2, 64, 131072), (1, 16384, 16384)])
+def test_q4_large_sizes_exact(orc, rows, R, C):
+    """Long segments (C = 2^17: 128 blocks per wave, two workgroups per
+    group) and a launch of 256 groups (one workgroup per group) with
+    C = 2^14, on exactly summable operands (integer x, power-of-two scales):
+    bit-exact against the oracle."""
+    say(f"proj_q4 large rows={rows} R={R} C={C}")
+    gen = synth.make_gen(151 + rows, "cuda")
+    q = torch.randint(0, 256, (R, C // 2), generator=gen, device="cuda").to(torch.uint8)
+    e = torch.randint(-2, 1, (R, C // 32), generator=gen, device="cuda").float()
+    sc = torch.pow(2.0, e).to(torch.float16)
+    x = torch.randint(-3, 4, (rows, C), generator=gen, device="cuda").float()
+    y = host(gdn.proj_q4(x, gdn.proj_q4_pack(q, sc)))
+    assert bits_equal(y, ref_q4(orc, host(x), q, sc))
+
+
 @pytest.mark.parametrize("rows,R,C", [(1, 64, 1024), (5, 320, 3072), (11, 448, 2048),
                                       (16, 1024, 5120), (2, 16384, 1024)])
 def test_q4_parity(orc, rows, R, C):
@@ -214,6 +230,31 @@ def test_q4_launch_shapes_agree_bit_for_bit():
         assert bits_equal(alone, host(paired)), rows
         halves = np.concatenate([host(gdn.proj_q4(x, W1a)), host(gdn.proj_q4(x, W1b))], axis=1)
         assert bits_equal(host(big), halves), rows
+
+
+def test_q4_binding_refuses_wrong_tensors():
+    """The binding refuses a wrong dtype, a wrong shape or a wrong-size output
+    before calling the C ABI, and the C ABI refuses shapes outside its limits."""
+    say("proj_q4 binding refusals")
+    x, q, sc = q4_operands(109, 2, 64, 1024)
+    W = gdn.proj_q4_pack(q, sc)
+    with pytest.raises(TypeError, match="q"):
+        gdn.proj_q4_pack(q.to(torch.int32), sc)
+    with pytest.raises(TypeError, match="scale"):
+        gdn.proj_q4_pack(q, sc.float())
+    with pytest.raises(ValueError, match="scale"):
+        gdn.proj_q4_pack(q, sc[:, :-1].contiguous())
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.proj_q4_pack(q[:, :256].contiguous(), sc[:, :16].contiguous())   # C = 512
+    assert e.value.rc == gdn.GDN_EUNSUPPORTED
+    with pytest.raises(ValueError, match="Wq0"):
+        gdn.proj_q4(x, W.view(-1)[: W.numel() // 2].view(W.shape[0] // 2 or 1, -1))
+    with pytest.raises(TypeError, match="Wq0"):
+        gdn.proj_q4(x, W.view(torch.int8))
+    with pytest.raises(ValueError, match="output"):
+        gdn.proj_q4(x, W, y0=torch.empty((2, 63), device="cuda"))
+    with pytest.raises(TypeError, match="x"):
+        gdn.proj_q4(x.double(), W)
 
 
 def test_q4_refuses_more_than_16_rows_and_accepts_none():
