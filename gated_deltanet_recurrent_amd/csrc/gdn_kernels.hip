@@ -1079,6 +1079,59 @@ static __device__ __forceinline__ void fe_conv_block(int bx, int by, const float
   }
 }
 
+// One GEMV row per call (one sequence, one draft row): a workgroup per
+// stacked weight row (2 vh of them instead of 2 vh / FR), every lane's chunks
+// requested at once.  Each lane's chain over its columns and the lane pairing
+// of the butterfly (offsets 32, 16, 8, 4, 2, 1) are those of fe_gemv_block,
+// and every add is commutative, so the results are the same bits.
+static __device__ __forceinline__ void fe_gemv_row(int R, const float *x, const float *Wa,
+                                                   const float *Wb, const float *A_log,
+                                                   const float *dt_bias, float *g, float *beta,
+                                                   int dim, int vh) {
+  __shared__ float s_w1[FE_WAVES];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const float *wrow = R < vh ? Wa + (int64_t)R * dim : Wb + (int64_t)(R - vh) * dim;
+  constexpr int STRIDE = 4 * FE_LANES;
+  constexpr int DEPTH = 4;                      // chunks per lane in flight
+  float acc = 0.0f;
+  for (int c0 = 4 * t; c0 < dim; c0 += DEPTH * STRIDE) {
+    f4 w[DEPTH], xv[DEPTH];
+#pragma unroll
+    for (int k = 0; k < DEPTH; k++) {
+      const int c = c0 + k * STRIDE;
+      if (c < dim) {
+        w[k] = ld4(wrow + c);
+        xv[k] = ld4(x + c);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < DEPTH; k++) {
+      if (c0 + k * STRIDE < dim) {
+        acc = __builtin_fmaf(w[k].x, xv[k].x, acc);
+        acc = __builtin_fmaf(w[k].y, xv[k].y, acc);
+        acc = __builtin_fmaf(w[k].z, xv[k].z, acc);
+        acc = __builtin_fmaf(w[k].w, xv[k].w, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc = acc + __shfl_xor(acc, off);
+  if (lane == 0) s_w1[wave] = acc;
+  __syncthreads();
+  if (t == 0) {
+    float sum = s_w1[0];
+#pragma unroll
+    for (int w = 1; w < FE_WAVES; w++) sum = sum + s_w1[w];
+    if (R < vh) {
+      const float sp = softplus_guarded(sum + dt_bias[R]);
+      g[R] = -expf(A_log[R]) * sp;
+    } else {
+      beta[R - vh] = 1.0f / (1.0f + expf(-sum));
+    }
+  }
+}
+
 // One launch for the whole front end: the first n_gemv workgroups run the
 // paired GEMV, the rest the conv; the two parts are independent, so their
 // latency-bound and bandwidth-bound phases overlap on the device.
@@ -1102,9 +1155,13 @@ __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
     // L2 pulling in all of x and all of W.  The GEMV rows of all M draft rows
     // are independent: [M][B] = M*B rows.
     const int g = (int)xcd_contiguous(id, a.n_gemv);
-    const int r_tiles = a.n_gemv / a.gemv_bx;
-    fe_gemv_block(g / r_tiles, g % r_tiles, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g, a.beta,
-                  a.M * a.B, a.dim, a.vh);
+    if (a.M * a.B == 1) {
+      fe_gemv_row(g, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g, a.beta, a.dim, a.vh);
+    } else {
+      const int r_tiles = a.n_gemv / a.gemv_bx;
+      fe_gemv_block(g / r_tiles, g % r_tiles, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g,
+                    a.beta, a.M * a.B, a.dim, a.vh);
+    }
   } else {
     const int c = id - a.n_gemv;
     fe_conv_block<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k, a.v,
@@ -1113,7 +1170,7 @@ __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
 }
 
 int64_t frontend_workitems(int64_t B, int64_t M, int64_t conv_dim, int64_t vh) {
-  const int64_t n_gemv = ((M * B + FB - 1) / FB) * ((2 * vh + FR - 1) / FR);
+  const int64_t n_gemv = M * B == 1 ? 2 * vh : ((M * B + FB - 1) / FB) * ((2 * vh + FR - 1) / FR);
   const int64_t n_conv = ((conv_dim + 1023) / 1024) * ((B + CONV_ROWS - 1) / CONV_ROWS);
   return (n_gemv + n_conv) * FE_LANES;
 }
@@ -1128,7 +1185,7 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
   FeArgs a{x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta,
            B, M, dim, conv_dim, vh, kh, write_hist ? 1 : 0, 0, 0, 0};
   a.gemv_bx = (M * B + FB - 1) / FB;
-  a.n_gemv = a.gemv_bx * ((2 * vh + FR - 1) / FR);
+  a.n_gemv = M * B == 1 ? 2 * vh : a.gemv_bx * ((2 * vh + FR - 1) / FR);
   a.conv_bx = (conv_dim + 1023) / 1024;
   const int n_conv = a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);
   const dim3 grid((unsigned)(a.n_gemv + n_conv));

@@ -405,10 +405,13 @@ def test_frontend_parity(orc, dims, B, dim):
 
 
 @pytest.mark.parametrize("dims,B,M", [(synth.DIMS128, 5, 3), (synth.DIMS64, 3, 8),
-                                      (synth.DIMS128, 2, 1)])
+                                      (synth.DIMS128, 2, 1), (synth.DIMS128, 1, 8),
+                                      (synth.DIMS64, 1, 3)])
 def test_frontend_m_bit_exact_and_parity(orc, dims, B, M):
     """M draft rows in one call == M single-row GPU calls (bit for bit), and
-    the oracle's M-row front end within tolerance (history bit for bit)."""
+    the oracle's M-row front end within tolerance (history bit for bit).  With
+    B = 1 the single-row calls take the one-row GEMV (a workgroup per weight
+    row) and the M-row call the batched one."""
     say(f"frontend_m dims={dims} B={B} M={M}")
     vh, kh, kd, vd = dims
     gen = synth.make_gen(9, "cuda")
