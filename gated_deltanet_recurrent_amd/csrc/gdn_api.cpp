@@ -269,14 +269,11 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const fl
   int32_t *d_acc = slab_accepted(slab);
   if (hipMemcpyAsync(d_acc, accepted, (size_t)N * 4, hipMemcpyHostToDevice, s) != hipSuccess)
     return GDN_EDEVICE;
+  // the history replay runs in the same launch as the state replay
   int rc = enq(gdn::launch_recur(kd, slab_S(slab), S, q, k, v, g, beta, nullptr, d_acc, N, vh, kh,
-                                 M, s));
+                                 M, s, nullptr, nullptr, 0.0f, nullptr, nullptr, hist,
+                                 slab_hist(slab), xc_raw, conv_dim));
   if (rc) return rc;
-  if (hist != nullptr) {
-    rc = enq(gdn::launch_hist_replay(hist, slab_hist(slab), xc_raw, d_acc, N, conv_dim, M,
-                                     nullptr, s));
-    if (rc) return rc;
-  }
   slab->armed = 0;
   return GDN_OK;
 }
@@ -409,12 +406,10 @@ int gdn_commit(float *S, float *hist, const float *q, const float *k, const floa
       return GDN_EINVAL;
   }
   hipStream_t s = (hipStream_t)stream;
-  rc = enq(gdn::launch_recur(kd, S, S, q, k, v, g, beta, nullptr, accepted, n_units, vh, kh, M, s,
-                             nullptr, nullptr, 0.0f, nullptr, status));
-  if (rc) return rc;
-  if (hist != nullptr)
-    rc = enq(gdn::launch_hist_replay(hist, hist, xc_raw, accepted, n_units, conv_dim, M, status, s));
-  return rc;
+  // the history replay runs in the same launch as the state replay
+  return enq(gdn::launch_recur(kd, S, S, q, k, v, g, beta, nullptr, accepted, n_units, vh, kh, M, s,
+                               nullptr, nullptr, 0.0f, nullptr, status, hist, hist, xc_raw,
+                               conv_dim));
 }
 
 int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream) {

@@ -196,6 +196,13 @@ struct RecurArgs {
   int32_t *status;       // nullable: set to 1 when a per-unit step count is out of range
   int64_t n_units;
   int vh, kh, M;
+  // nullable: the conv history replayed in the same launch (M-step kernels):
+  // workgroups past the tiles' push steps[u] raw rows into hist[u]
+  float *hist;
+  const float *hist_src; // hist itself (commit) or its snapshot (rollback)
+  const float *xc_raw;   // [M][N][conv_dim]
+  int conv_dim;
+  int64_t tile_wgs;      // workgroups of the tiles; the rest replay history
 };
 
 // Per-step inputs are staged through LDS in chunks of MC rows.  q and k are
@@ -429,6 +436,47 @@ void recur_wide_kernel(RecurArgs a) {
   }
 }
 
+// Conv-history replay of unit u, float4 channels c4 (pure data movement,
+// bit-exact): frame j after acc pushes is element acc + j of the sequence
+// [old frames 0..2, raw rows 0..acc-1]; all frames are read before any is
+// written, so src may be hist itself.  A count outside 0..M leaves the unit
+// as it was and sets status.
+static __device__ __forceinline__ void hist_replay_at(float *hist, const float *src,
+                                                      const float *xc_raw,
+                                                      const int32_t *accepted, int64_t n_units,
+                                                      int conv_dim, int M, int32_t *status,
+                                                      int64_t u, int c4, bool report) {
+  constexpr int NPREV = 3;             // ck = 4
+  int acc = accepted[u];
+  if (acc < 0 || acc > M) {            // device-supplied counts: refuse the unit
+    if (status != nullptr && report) status[0] = 1;
+    acc = 0;
+  }
+  if (4 * c4 >= conv_dim) return;
+  if (acc == 0 && src == hist) return; // in place, nothing accepted: unchanged
+  const int64_t hbase = u * (int64_t)NPREV * conv_dim + 4 * c4;
+  f4 fr[NPREV];
+#pragma unroll
+  for (int j = 0; j < NPREV; j++) {
+    const int idx = acc + j;
+    const float *from = idx < NPREV ? src + hbase + (int64_t)idx * conv_dim
+                                    : xc_raw + ((int64_t)(idx - NPREV) * n_units + u) * conv_dim + 4 * c4;
+    fr[j] = ld4(from);
+  }
+#pragma unroll
+  for (int j = 0; j < NPREV; j++) st4(hist + hbase + (int64_t)j * conv_dim, fr[j]);
+}
+
+// History work of an M-step launch: item i of LANES float4 channels.
+template <int LANES>
+static __device__ __forceinline__ void hist_item(const RecurArgs &a, int64_t item) {
+  const int64_t per_unit = (a.conv_dim / 4 + LANES - 1) / LANES;
+  const int64_t u = item / per_unit;
+  const int c4 = (int)(item - u * per_unit) * LANES + (int)threadIdx.x;
+  hist_replay_at(a.hist, a.hist_src, a.xc_raw, a.steps, a.n_units, a.conv_dim, a.M, a.status, u,
+                 c4, threadIdx.x == 0);
+}
+
 // ----- wide geometry, several steps ---------------------------------------
 //
 // Up to MC steps per call for launches with few tiles (a handful of units,
@@ -446,6 +494,13 @@ __global__ __launch_bounds__(Geo<KD>::LANES) void recur_widem_kernel(RecurArgs a
   __shared__ f4 s_red_o[G::NW][G::CG];
   __shared__ f4 s_tmp[G::CG];
 
+  if (a.hist != nullptr) {             // uniform per workgroup
+    const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
+    if (bid >= a.tile_wgs) {
+      hist_item<LANES>(a, bid - a.tile_wgs);
+      return;
+    }
+  }
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int cg = t % G::CG, rg = t / G::CG;
@@ -553,6 +608,13 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
   __shared__ f4 s_red_o[XWAVE ? Canon<KD>::NWP : 1][CG];
   __shared__ f4 s_tmp[CG];
 
+  if (a.hist != nullptr) {             // uniform per workgroup
+    const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
+    if (bid >= a.tile_wgs) {
+      hist_item<LANES>(a, bid - a.tile_wgs);
+      return;
+    }
+  }
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int cg = t % CG, L = t / CG;
@@ -682,9 +744,15 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
 
 int recur_lanes(int kd) { return kd == 128 ? Geo<128>::LANES : Geo<64>::LANES; }
 
+// Workgroups that replay the history after the tiles' workgroups.
+static int64_t hist_wgs(const RecurArgs &a, int lanes) {
+  return a.hist == nullptr ? 0 : a.n_units * ((a.conv_dim / 4 + lanes - 1) / lanes);
+}
+
 template <int KD, bool GATED>
-static void launch_recur_kd(const RecurArgs &a, int64_t tiles, hipStream_t s) {
+static void launch_recur_kd(RecurArgs a, int64_t tiles, hipStream_t s) {
   const dim3 grid((unsigned)tiles);
+  a.tile_wgs = tiles;
   if (a.M == 1) {
     // kd = 64: four adjacent heads of one unit per workgroup, so that a
     // workgroup streams 64 KiB of consecutive state like a kd = 128 one
@@ -705,12 +773,14 @@ static void launch_recur_kd(const RecurArgs &a, int64_t tiles, hipStream_t s) {
                          s, a);
     }
   } else if (a.M <= MC && tiles < GDN_WIDEM_BELOW) {
-    hipLaunchKernelGGL((recur_widem_kernel<KD, GATED>), grid, dim3(Geo<KD>::LANES), 0, s, a);
+    const dim3 g2((unsigned)(tiles + hist_wgs(a, Geo<KD>::LANES)));
+    hipLaunchKernelGGL((recur_widem_kernel<KD, GATED>), g2, dim3(Geo<KD>::LANES), 0, s, a);
   } else {
+    const dim3 g2((unsigned)(tiles + hist_wgs(a, Deep<KD>::LANES)));
     if (a.M <= MC)
-      hipLaunchKernelGGL((recur_deep_kernel<KD, false, GATED>), grid, dim3(Deep<KD>::LANES), 0, s, a);
+      hipLaunchKernelGGL((recur_deep_kernel<KD, false, GATED>), g2, dim3(Deep<KD>::LANES), 0, s, a);
     else
-      hipLaunchKernelGGL((recur_deep_kernel<KD, true, GATED>), grid, dim3(Deep<KD>::LANES), 0, s, a);
+      hipLaunchKernelGGL((recur_deep_kernel<KD, true, GATED>), g2, dim3(Deep<KD>::LANES), 0, s, a);
   }
 }
 
@@ -719,11 +789,26 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *beta, float *o, const int32_t *steps,
                  int64_t n_units, int vh, int kh, int M, hipStream_t s,
                  const float *z, const float *norm_w, float eps, float *snap,
-                 int32_t *status) {
+                 int32_t *status, float *hist, const float *hist_src, const float *xc_raw,
+                 int conv_dim) {
   RecurArgs a{S_src, S_dst, q, k, v, g, beta, o, steps, z, norm_w, eps, snap, status,
-              n_units, vh, kh, M};
+              n_units, vh, kh, M, nullptr, nullptr, nullptr, 0, 0};
   const int64_t tiles = n_units * vh;
   if (tiles <= 0) return 0;
+  if (hist != nullptr) {
+    if (M == 1) {
+      // single steps run the wide kernel, which has no history part: the
+      // replay is its own launch
+      const int rc = launch_hist_replay(hist, hist_src, xc_raw, steps, n_units, conv_dim, M,
+                                        status, s);
+      if (rc) return rc;
+    } else {
+      a.hist = hist;
+      a.hist_src = hist_src;
+      a.xc_raw = xc_raw;
+      a.conv_dim = conv_dim;
+    }
+  }
   const bool gated = z != nullptr;
   if (kd == 128) {
     if (gated)
@@ -788,30 +873,8 @@ __global__ __launch_bounds__(256) void hist_replay_kernel(float *hist, const flo
                                                           const int32_t *accepted,
                                                           int64_t n_units, int conv_dim, int M,
                                                           int32_t *status) {
-  constexpr int NPREV = 3;             // ck = 4
-  const int64_t u = blockIdx.y;
-  const int c4 = blockIdx.x * 256 + threadIdx.x;
-  int acc = accepted[u];
-  if (acc < 0 || acc > M) {            // device-supplied counts: refuse the unit
-    if (status != nullptr && threadIdx.x == 0) status[0] = 1;
-    acc = 0;
-  }
-  if (4 * c4 >= conv_dim) return;
-  if (acc == 0 && src == hist) return; // in place, nothing accepted: unchanged
-  const int64_t hbase = u * (int64_t)NPREV * conv_dim + 4 * c4;
-  // frame j of the history after acc pushes is element acc + j of the
-  // sequence [old frames 0..NPREV-1, raw 0..acc-1]; all frames are read
-  // before any is written, so src may be hist itself
-  f4 fr[NPREV];
-#pragma unroll
-  for (int j = 0; j < NPREV; j++) {
-    const int idx = acc + j;
-    const float *from = idx < NPREV ? src + hbase + (int64_t)idx * conv_dim
-                                    : xc_raw + ((int64_t)(idx - NPREV) * n_units + u) * conv_dim + 4 * c4;
-    fr[j] = ld4(from);
-  }
-#pragma unroll
-  for (int j = 0; j < NPREV; j++) st4(hist + hbase + (int64_t)j * conv_dim, fr[j]);
+  hist_replay_at(hist, src, xc_raw, accepted, n_units, conv_dim, M, status, blockIdx.y,
+                 blockIdx.x * 256 + threadIdx.x, threadIdx.x == 0);
 }
 
 int launch_hist_replay(float *hist, const float *src, const float *xc_raw,

@@ -27,7 +27,9 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *beta, float *o, const int32_t *steps,
                  int64_t n_units, int vh, int kh, int M, hipStream_t s,
                  const float *z = nullptr, const float *norm_w = nullptr, float eps = 0.0f,
-                 float *snap = nullptr, int32_t *status = nullptr);
+                 float *snap = nullptr, int32_t *status = nullptr, float *hist = nullptr,
+                 const float *hist_src = nullptr, const float *xc_raw = nullptr,
+                 int conv_dim = 0);
 
 // 128-bit streaming copy of n floats (src == dst allowed).
 int launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
