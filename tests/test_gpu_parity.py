@@ -576,6 +576,38 @@ def test_verify_commit_equals_snapshot_protocol(dims):
     assert int(status.item()) == 0
 
 
+@pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
+def test_single_row_commit_and_rollback_with_history(dims):
+    """M = 1: the state replay runs the single-step kernel and the history its
+    own launch.  Accepted 1 equals one step and one pushed frame; accepted 0
+    leaves state and history as they were (bit for bit, both entry points)."""
+    say(f"M=1 commit/rollback with history dims={dims}")
+    vh, kh, kd, vd = dims
+    N, conv_dim = 5, synth.conv_dim_of(dims)
+    gen = synth.make_gen(63, "cuda")
+    S0 = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=1, device="cuda")
+    h0 = torch.randn((N, 3, conv_dim), generator=gen, device="cuda")
+    xc = torch.randn((1, N, conv_dim), generator=gen, device="cuda")
+    acc = [1, 0, 1, 1, 0]
+    S1 = S0.clone()
+    gdn.step(S1, *(inp[n][0] for n in NAMES))
+    S_want = torch.stack([S1[u] if a else S0[u] for u, a in enumerate(acc)])
+    h_want = torch.stack([torch.cat([h0[u, 1:], xc[0, u:u + 1]]) if a else h0[u]
+                          for u, a in enumerate(acc)])
+    S_c, h_c = S0.clone(), h0.clone()
+    gdn.commit(S_c, torch.tensor(acc, dtype=torch.int32, device="cuda"),
+               *(inp[n] for n in NAMES), hist=h_c, xc_raw=xc)
+    assert bits_equal(host(S_c), host(S_want)) and bits_equal(host(h_c), host(h_want))
+    slab = gdn.Slab(N, dims, hist_floats_per_unit=3 * conv_dim)
+    S_r, h_r = S0.clone(), h0.clone()
+    slab.mark(S_r, hist=h_r)
+    gdn.step(S_r, *(inp[n][0] for n in NAMES))
+    h_r.normal_(generator=gen)                     # clobbered, restored by the rollback
+    slab.rollback(S_r, acc, *(inp[n] for n in NAMES), hist=h_r, xc_raw=xc)
+    assert bits_equal(host(S_r), host(S_want)) and bits_equal(host(h_r), host(h_want))
+
+
 def test_commit_refuses_out_of_range_counts():
     """Device-supplied counts outside 0..M leave that unit unchanged and raise
     the status flag; the other units are committed normally."""
