@@ -87,6 +87,47 @@ static __device__ __forceinline__ void st4(float *p, f4 x) {
   *reinterpret_cast<f4 *>(p) = x;
 }
 
+// The value of lane (lane ^ OFF) of the wave, without the LDS crossbar:
+// v_permlane32_swap / v_permlane16_swap (gfx950) for 32 and 16, DPP row_ror:8
+// and quad_perm for 8, 2 and 1, ds_swizzle's bitmask mode for 4.  Every lane
+// of the wave must be active.
+template <int OFF>
+static __device__ __forceinline__ float lane_xor(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  unsigned r;
+  if constexpr (OFF == 32) {
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r = (threadIdx.x & 32) ? p[0] : p[1];
+  } else if constexpr (OFF == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    r = (threadIdx.x & 16) ? p[0] : p[1];
+  } else if constexpr (OFF == 8) {
+    r = __builtin_amdgcn_update_dpp(0u, u, 0x128, 0xf, 0xf, false);   // row_ror:8
+  } else if constexpr (OFF == 4) {
+    r = __builtin_amdgcn_ds_swizzle(u, 0x1f | (4 << 10));              // xor 4 in 32 lanes
+  } else if constexpr (OFF == 2) {
+    r = __builtin_amdgcn_update_dpp(0u, u, 0x4e, 0xf, 0xf, false);    // quad_perm [2,3,0,1]
+  } else {
+    static_assert(OFF == 1, "lane_xor: offsets 1, 2, 4, 8, 16, 32");
+    r = __builtin_amdgcn_update_dpp(0u, u, 0xb1, 0xf, 0xf, false);    // quad_perm [1,0,3,2]
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// v + v of lane (lane ^ OFF), for OFF = FROM, 2 FROM, ... up to TO - 1.
+// XB: through the LDS crossbar (ds_bpermute) instead, which costs the
+// bandwidth-bound single-step kernel less issue time (0.25% in a same-box
+// A/B); both move the same values, so the sums are the same bits.
+template <int FROM, int TO, bool XB = false>
+static __device__ __forceinline__ float xor_fold(float v) {
+  if constexpr (FROM < TO) {
+    v = v + (XB ? __shfl_xor(v, FROM) : lane_xor<FROM>(v));
+    return xor_fold<2 * FROM, TO, XB>(v);
+  } else {
+    return v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup -> tile mapping
 // ---------------------------------------------------------------------------
@@ -157,22 +198,19 @@ struct Deep {
 // Fold over the row groups that share this lane's columns inside one wave
 // (lanes t, t ^ CG, ...).  Every add is commutative, so all those lanes end
 // up with the same bits.
-template <int KD>
+template <int KD, bool XB = false>
 static __device__ __forceinline__ f4 wave_fold(f4 p) {
-#pragma unroll
-  for (int off = Canon<KD>::CG; off < 64; off <<= 1) {
-    p.x = p.x + __shfl_xor(p.x, off);
-    p.y = p.y + __shfl_xor(p.y, off);
-    p.z = p.z + __shfl_xor(p.z, off);
-    p.w = p.w + __shfl_xor(p.w, off);
-  }
+  p.x = xor_fold<Canon<KD>::CG, 64, XB>(p.x);
+  p.y = xor_fold<Canon<KD>::CG, 64, XB>(p.y);
+  p.z = xor_fold<Canon<KD>::CG, 64, XB>(p.z);
+  p.w = xor_fold<Canon<KD>::CG, 64, XB>(p.w);
   return p;
 }
 
 // Final sum over the W partials red[NWP][CG] by one wave: lane group
 // h = lane / CG left-folds partials h*PER .. h*PER + PER - 1, then the groups
 // are folded.  Valid in every lane of the wave for column group lane % CG.
-template <int KD>
+template <int KD, bool XB = false>
 static __device__ __forceinline__ f4 tile_sum(const f4 (*red)[Canon<KD>::CG], int lane) {
   constexpr int CG = Canon<KD>::CG;
   constexpr int PER = Canon<KD>::NWP / (64 / CG);
@@ -180,7 +218,7 @@ static __device__ __forceinline__ f4 tile_sum(const f4 (*red)[Canon<KD>::CG], in
   f4 acc = red[h * PER][cg];
 #pragma unroll
   for (int i = 1; i < PER; i++) acc = acc + red[h * PER + i][cg];
-  return wave_fold<KD>(acc);
+  return wave_fold<KD, XB>(acc);
 }
 
 struct RecurArgs {
@@ -294,7 +332,7 @@ static __device__ __forceinline__ f4 lds4(const float *p) {
 // ("Kestrel_VLLM #24", Fig. 1 caption, step 6; the pages give no formula, the
 // model family's definition is used): out = (o * 1/sqrt(mean(o^2) + eps)) *
 // w * silu(z), per value head over its vd outputs.
-template <int KD, bool GATED>
+template <int KD, bool GATED, bool XB = false>
 static __device__ __forceinline__ void emit_o(const RecurArgs &a, int64_t urow, int head, int cg,
                                               bool write, f4 ov, const float *zrow) {
   if constexpr (GATED) {
@@ -303,8 +341,7 @@ static __device__ __forceinline__ void emit_o(const RecurArgs &a, int64_t urow, 
     ss = __builtin_fmaf(ov.y, ov.y, ss);
     ss = __builtin_fmaf(ov.z, ov.z, ss);
     ss = __builtin_fmaf(ov.w, ov.w, ss);
-#pragma unroll
-    for (int off = 1; off < Canon<KD>::CG; off <<= 1) ss = ss + __shfl_xor(ss, off);
+    ss = xor_fold<1, Canon<KD>::CG, XB>(ss);
     const float rinv = 1.0f / sqrtf(ss / (float)KD + a.eps);
     const f4 z = lds4(zrow + 4 * cg);
     f4 sz;
@@ -399,11 +436,11 @@ void recur_wide_kernel(RecurArgs a) {
       s[j] = s[j] * alpha;
       p = fma4(s[j], splat(kk[j]), p);
     }
-    p = wave_fold<KD>(p);
+    p = wave_fold<KD, true>(p);
     if (lane < G::CG) s_red_k[wave][lane] = p;
     __syncthreads();
     if (wave == 0) {
-      const f4 kv = tile_sum<KD>(s_red_k, lane);
+      const f4 kv = tile_sum<KD, true>(s_red_k, lane);
       if (lane < G::CG) s_tmp[lane] = (lds4(&sb.v[0][4 * lane]) - kv) * sb.beta[0];
     }
     __syncthreads();
@@ -416,7 +453,7 @@ void recur_wide_kernel(RecurArgs a) {
       s[j] = fma4(splat(kk[j]), tmp, s[j]);
       p = fma4(s[j], splat(qq[j]), p);
     }
-    p = wave_fold<KD>(p);
+    p = wave_fold<KD, true>(p);
     if (lane < G::CG) s_red_o[wave][lane] = p;
   }
 
@@ -429,8 +466,8 @@ void recur_wide_kernel(RecurArgs a) {
   if (run) {
     __syncthreads();
     if (wave == 0 && a.o != nullptr) {
-      const f4 ov = tile_sum<KD>(s_red_o, lane);
-      emit_o<KD, GATED>(a, ti.unit, ti.head, lane % G::CG, lane < G::CG, ov,
+      const f4 ov = tile_sum<KD, true>(s_red_o, lane);
+      emit_o<KD, GATED, true>(a, ti.unit, ti.head, lane % G::CG, lane < G::CG, ov,
                         &sb.z[0][0]);
     }
   }
@@ -994,7 +1031,7 @@ static __device__ __forceinline__ void fe_gemv_block(int bx, int by, const float
     for (int i = 0; i < 16; i++) {
       const float send = up ? acc[i] : acc[16 + i];
       const float keep = up ? acc[16 + i] : acc[i];
-      v16[i] = keep + __shfl_xor(send, 32);
+      v16[i] = keep + lane_xor<32>(send);
     }
   }
   float v8[8];
@@ -1004,7 +1041,7 @@ static __device__ __forceinline__ void fe_gemv_block(int bx, int by, const float
     for (int i = 0; i < 8; i++) {
       const float send = up ? v16[i] : v16[8 + i];
       const float keep = up ? v16[8 + i] : v16[i];
-      v8[i] = keep + __shfl_xor(send, 16);
+      v8[i] = keep + lane_xor<16>(send);
     }
   }
   float v4[4];
@@ -1014,7 +1051,7 @@ static __device__ __forceinline__ void fe_gemv_block(int bx, int by, const float
     for (int i = 0; i < 4; i++) {
       const float send = up ? v8[i] : v8[4 + i];
       const float keep = up ? v8[4 + i] : v8[i];
-      v4[i] = keep + __shfl_xor(send, 8);
+      v4[i] = keep + lane_xor<8>(send);
     }
   }
   float v2[2];
@@ -1024,7 +1061,7 @@ static __device__ __forceinline__ void fe_gemv_block(int bx, int by, const float
     for (int i = 0; i < 2; i++) {
       const float send = up ? v4[i] : v4[2 + i];
       const float keep = up ? v4[2 + i] : v4[i];
-      v2[i] = keep + __shfl_xor(send, 4);
+      v2[i] = keep + lane_xor<4>(send);
     }
   }
   float v1;
@@ -1032,9 +1069,9 @@ static __device__ __forceinline__ void fe_gemv_block(int bx, int by, const float
     const bool up = lane & 2;
     const float send = up ? v2[0] : v2[1];
     const float keep = up ? v2[1] : v2[0];
-    v1 = keep + __shfl_xor(send, 2);
+    v1 = keep + lane_xor<2>(send);
   }
-  v1 = v1 + __shfl_xor(v1, 1);
+  v1 = v1 + lane_xor<1>(v1);
   if ((lane & 1) == 0) s_w[wave][lane >> 1] = v1;
   __syncthreads();
   if (t < FB * FR) {
@@ -1120,8 +1157,7 @@ static __device__ __forceinline__ void fe_conv_block(int bx, int by, const float
     ss = __builtin_fmaf(out[1], out[1], ss);
     ss = __builtin_fmaf(out[2], out[2], ss);
     ss = __builtin_fmaf(out[3], out[3], ss);
-#pragma unroll
-    for (int off = 1; off < KD / 4; off <<= 1) ss = ss + __shfl_xor(ss, off);
+    ss = xor_fold<1, KD / 4>(ss);
     if (valid) {
       const f4 o4 = {out[0], out[1], out[2], out[3]};
       if (ch < 2 * qk_w) {
@@ -1178,8 +1214,12 @@ static __device__ __forceinline__ void fe_gemv_row(int R, const float *x, const 
       }
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc = acc + __shfl_xor(acc, off);
+  acc = acc + lane_xor<32>(acc);
+  acc = acc + lane_xor<16>(acc);
+  acc = acc + lane_xor<8>(acc);
+  acc = acc + lane_xor<4>(acc);
+  acc = acc + lane_xor<2>(acc);
+  acc = acc + lane_xor<1>(acc);
   if (lane == 0) s_w1[wave] = acc;
   __syncthreads();
   if (t == 0) {
