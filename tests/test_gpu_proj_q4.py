@@ -343,3 +343,48 @@ def test_q4_layer_decode_chain(orc):
         for b in range(B):
             assert max_rel_pages(y[b], y_r[b]) <= 1e-4, (t, b)
     assert max_rel_pages(host(S), S_r) <= 1e-4
+
+
+def test_q4_graph_replay_matches_eager():
+    """The layer's 4-bit projections captured as a HIP graph (in_proj: one
+    workgroup per group; out_proj: two workgroups per group, whose fill
+    kernel and atomic adds must run on every replay) replay bit-identically
+    to eager calls, several times, with eager work and synchronisations in
+    between and the outputs dirtied before each replay."""
+    say("proj_q4 graph replay")
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    gen = synth.make_gen(157, "cuda")
+    w = synth.proj_weights_q4(gen, dims, device="cuda")
+    wq = {n: gdn.proj_q4_pack(*w[n]) for n in ("W_qkv", "W_z", "W_out")}
+    rows = 3
+    x = torch.randn((rows, synth.FE_DIM), generator=gen, device="cuda")
+    h = torch.randn((rows, vh * vd), generator=gen, device="cuda")
+    e_xc, e_z = gdn.proj_q4(x, wq["W_qkv"], wq["W_z"])
+    e_y = gdn.proj_q4(h, wq["W_out"])
+    torch.cuda.synchronize()
+    xc, z, y = torch.empty_like(e_xc), torch.empty_like(e_z), torch.empty_like(e_y)
+
+    def chain():
+        gdn.proj_q4(x, wq["W_qkv"], wq["W_z"], y0=xc, y1=z)
+        gdn.proj_q4(h, wq["W_out"], y0=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                  # warm-up outside capture
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    for rep in range(3):
+        for t in (xc, z, y):
+            t.fill_(float(rep + 1))                # dirty outputs: the fill must clear y
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in ((xc, e_xc), (z, e_z), (y, e_y)):
+            assert bits_equal(host(got), host(want)), rep
+        gdn.proj_q4(h, wq["W_out"])                 # eager work between replays
+        torch.cuda.synchronize()
+    del graph
