@@ -1,38 +1,33 @@
 // gdn_kernels.hip -- gfx950 (MI355X, CDNA4) kernels of the Gated DeltaNet
-// recurrent decode step, its M-step / rollback forms and its front end.
+// recurrent decode step, its M-step / rollback / verify forms, its front end
+// and the layer's dense projections.
 //
-// The step ("Kestrel_VLLM #24: GDN linear attention on GPU", section 4 and
-// Fig. 1 caption) is a GEMV plus a rank-1 update per (unit, value head) over
-// a kd x vd fp32 state: 0.87 flop per byte, so it is bound by HBM bandwidth,
-// not by arithmetic, and uses no MFMA.  The design streams each 64 KiB state
-// tile through VGPRs exactly once per call:
-//
-//  * one lane group per tile (unit, value head); every lane holds 16 floats
-//    of it: 4 adjacent columns (dv = 4*(t % (kd/4)) .. +3) of the rows
-//    dk = rg + RG*j, j = 0..3, rg = t / (kd/4), RG = lanes / (kd/4) row groups.
-//    kd = 128 uses 1024 lanes (16 wave64) per tile and one tile per
-//    workgroup; kd = 64 uses 256 lanes per tile and four adjacent tiles of
-//    one unit per workgroup, so that every workgroup streams 64 KiB of
-//    consecutive state (one 16 KiB tile per workgroup measured 2.8% slower).
-//    A wave-wide 128-bit load covers 1 KiB of consecutive rows, so every state
-//    access is a fully coalesced global_load_dwordx4, all issued before any
-//    arithmetic.
-//  * the key/query read-outs (sums over dk) are done per lane over its rows,
-//    folded inside each wave with cross-lane shuffles, and finished by wave 0
-//    from one LDS partial per wave, in a fixed order.
+// Recurrence.  The step ("Kestrel_VLLM #24: GDN linear attention on GPU",
+// section 4 and Fig. 1 caption) is a GEMV plus a rank-1 update per (unit,
+// value head) over a kd x vd fp32 state: 0.87 flop per byte, so it is bound
+// by HBM bandwidth, not by arithmetic, and uses no MFMA.  Each 64 KiB state
+// tile streams through VGPRs exactly once per call:
+//  * wide geometry (single steps; also M <= 8 steps for launches of few
+//    tiles): 16 floats per lane, 4 adjacent columns of the rows rg + RG*j;
+//    kd = 128 on 1024 lanes per tile, kd = 64 on 256 lanes with four tiles of
+//    one unit per workgroup.  A wave-wide 128-bit load covers 1 KiB of
+//    consecutive rows, all issued before any arithmetic.
+//  * deep geometry (M steps): 64 floats per lane, more tiles per CU and fewer
+//    cross-lane exchanges per element; the tile stays in VGPRs across all M
+//    steps (read once, written once).
+//  * all geometries compute one canonical summation tree for the read-outs,
+//    so step, step_m, rollback, verify and commit agree bit for bit whichever
+//    geometry serves them; FMA use is explicit (this file is compiled with
+//    -ffp-contract=off and fuses only where an fma builtin says so).
 //  * workgroups are remapped so that each XCD streams a contiguous range of
-//    tiles.
-//  * the per-step inputs (q, k of the tile's key head, v, g, beta) are staged
-//    in LDS in double-buffered chunks of 8 rows, prefetched one chunk ahead.
-//  * the state is streamed with raw buffer loads (nt) and stores (sc0 sc1 nt):
-//    it is touched once per call and would only evict useful lines from L2 /
-//    MALL.
-//  * the M-step form keeps the tile in VGPRs across all M steps (read once,
-//    written once); rollback is the same kernel reading the snapshot and
-//    running accepted[u] steps.  gdn_step, gdn_step_m and gdn_rollback thus
-//    execute the identical per-step instruction sequence (bit-identical
-//    results), with FMA use fixed explicitly: this file is compiled with
-//    -ffp-contract=off and fuses only where __builtin_elementwise_fma says so.
+//    tiles; the state is streamed with raw buffer loads (nt) and stores
+//    (sc0 sc1 nt); per-step inputs are staged in LDS in chunks of 8 rows.
+// Front end (section 3 and Fig. 1 caption): the paired beta / a GEMV with the
+// gate transform and the causal conv + SiLU + q/k normalisation in one launch.
+// Projections (Fig. 1 caption, steps 1 and 7): f32 weights on the fp32
+// matrix cores in packed operand order, and 4-bit weights with binary16 block
+// scales on a VALU kernel (section 8 and 12), each with a fixed summation
+// order independent of the row count.
 #include "gdn_launch.h"
 
 #include <hip/hip_runtime.h>
