@@ -72,6 +72,9 @@ def ref_steps(orc, S, inp, dims, rows):
     ((6, 2, 128, 128), 3, 5),
     ((4, 4, 64, 64), 2, 5),
     ((8, 1, 128, 128), 2, 3),
+    ((6, 2, 64, 64), 3, 4),          # kd = 64, vh not a multiple of 4: one tile per workgroup
+    ((1, 1, 128, 128), 4, 3),        # one head
+    ((1, 1, 64, 64), 5, 3),
 ])
 def test_step_chain_parity(orc, dims, N, T):
     say(f"step chain dims={dims} N={N} T={T}")
@@ -161,7 +164,8 @@ def test_step_on_side_stream(orc):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dims,M", [(synth.DIMS128, 8), (synth.DIMS64, 5), (synth.DIMS128, 1),
-                                    (synth.DIMS128, 64)])
+                                    (synth.DIMS128, 64), ((6, 2, 64, 64), 4),
+                                    ((1, 1, 128, 128), 8), ((6, 2, 64, 64), 12)])
 def test_step_m_bit_exact_and_parity(orc, dims, M):
     say(f"step_m dims={dims} M={M}")
     N = 3
