@@ -1,9 +1,9 @@
 """Python binding of the MI355X GDN recurrent-step library (``libgdn_mi355x.so``).
 
 Argument marshalling only: every function checks that its torch tensors are
-fp32, contiguous and on a HIP device, derives the sizes from their shapes and
-calls the C ABI of ``include/gdn.h`` with raw device pointers and the current
-HIP stream.  All arithmetic runs in the library's gfx950 kernels; there is no
+fp32 (the 4-bit weights: uint8 values and binary16 scales), contiguous and on
+a HIP device, derives the sizes from their shapes and calls the C ABI of
+``include/gdn.h`` with raw device pointers and the current HIP stream.  All arithmetic runs in the library's gfx950 kernels; there is no
 fallback of any kind, and importing this package fails loudly when the
 library has not been built (``python -m gated_deltanet_recurrent_amd.build``).
 
@@ -12,7 +12,8 @@ Fig. 1 caption (decay, key read-out, delta, rank-1 update, query read-out with
 the updated state); M-step and mark/rollback: "Kestrel_VLLM #34: batched M
 rows", sections 3.6 and 3.7; front end: "Kestrel_VLLM #27: register residency
 and fused launch", section 4.2, and "#24", section 3; dense projections:
-"#24", Fig. 1 caption, steps 1 and 7, and "#34", section 3.6.
+"#24", Fig. 1 caption, steps 1 and 7, and "#34", section 3.6; their 4-bit
+weights: "#24", sections 8 and 12.
 
 Every tensor's element count is checked against the sizes passed with it,
 because the C ABI receives raw pointers and cannot check them itself.
