@@ -1341,7 +1341,10 @@ constexpr int PJ_LANES = 64 * PJ_SEG;
 #define GDN_PJ_MIN_WG1 256
 #endif
 #ifndef GDN_PJ_U2_ROWS
-#define GDN_PJ_U2_ROWS 8        // up to this many rows, 2 blocks per trip for 1-2 slabs
+#define GDN_PJ_U2_ROWS 8        // few rows: up to this many
+#endif
+#ifndef GDN_PJ_MIN_WG_FEW
+#define GDN_PJ_MIN_WG_FEW 1024
 #endif
 
 struct ProjProblem {
@@ -1515,8 +1518,10 @@ __global__ __launch_bounds__(PJ_LANES) void proj_kernel(ProjArgs a) {
 
 // Tile shape of a call.  Up to 16 rows (one row block) the call streams the
 // weights: the widest output slab group (1, 2 or 4 slabs of 16) dividing
-// R / 16 that still leaves >= GDN_PJ_MIN_WG1 workgroups, to spread the stream
-// over every CU.  Beyond 16 rows it is bound by the matrix cores and by x
+// R / 16 that still leaves >= GDN_PJ_MIN_WG1 workgroups (GDN_PJ_MIN_WG_FEW up
+// to 8 rows), to spread the stream over every CU: in_proj at 1 to 4 rows
+// takes 52 us with 1024 one-slab workgroups against 55 us with 256 four-slab
+// ones, but 66 against 54 us at 16 rows.  Beyond 16 rows it is bound by the matrix cores and by x
 // traffic: the widest slab group dividing R / 16 (each x load then serves
 // more outputs), then the most row blocks per tile (up to the rows present)
 // that still leave >= GDN_PJ_MIN_WG workgroups.  Measured at 64 rows:
@@ -1535,10 +1540,11 @@ static int64_t proj_tiles(int64_t rows, int R0, int R1, int rb, int oj) {
 static ProjShape proj_shape(int64_t rows, int R0, int R1) {
   ProjShape sh;
   const int rb_max = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+  const int64_t min_wg1 = rows <= GDN_PJ_U2_ROWS ? GDN_PJ_MIN_WG_FEW : GDN_PJ_MIN_WG1;
   sh.oj = 1;
   for (int oj = 4; oj > 1; oj >>= 1) {
     const bool divides = (R0 / 16) % oj == 0 && (R1 / 16) % oj == 0;
-    if (divides && (rb_max > 1 || proj_tiles(rows, R0, R1, 1, oj) >= GDN_PJ_MIN_WG1)) {
+    if (divides && (rb_max > 1 || proj_tiles(rows, R0, R1, 1, oj) >= min_wg1)) {
       sh.oj = oj;
       break;
     }
@@ -1597,15 +1603,20 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
   a.p[1] = ProjProblem{W1, y1, R1, W1 ? R1 / (16 * sh.oj) * sh.row_groups : 0};
   const bool stream = sh.row_groups == 1;
   switch (sh.rb * 8 + sh.oj) {
-    // one row block: 2 blocks per trip up to 8 rows (out_proj at one row
-    // 28.7 -> 24.4 us), 4 beyond; the MFMA order is the same either way
+    // one row block: up to 8 rows, 2 blocks per trip unless the grid has
+    // >= GDN_PJ_MIN_WG_FEW workgroups (out_proj at one row 28.7 -> 24.4 us;
+    // in_proj keeps 4), 4 beyond; the MFMA order is the same either way
     case 1 * 8 + 1:
-      if (rows <= GDN_PJ_U2_ROWS) launch_proj_t<1, 1, 2>(a, true, s);
-      else launch_proj_t<1, 1, 4>(a, true, s);
+      if (rows <= GDN_PJ_U2_ROWS && a.p[0].blocks + a.p[1].blocks < GDN_PJ_MIN_WG_FEW)
+        launch_proj_t<1, 1, 2>(a, true, s);
+      else
+        launch_proj_t<1, 1, 4>(a, true, s);
       break;
     case 1 * 8 + 2:
-      if (rows <= GDN_PJ_U2_ROWS) launch_proj_t<1, 2, 2>(a, true, s);
-      else launch_proj_t<1, 2, 4>(a, true, s);
+      if (rows <= GDN_PJ_U2_ROWS && a.p[0].blocks + a.p[1].blocks < GDN_PJ_MIN_WG_FEW)
+        launch_proj_t<1, 2, 2>(a, true, s);
+      else
+        launch_proj_t<1, 2, 4>(a, true, s);
       break;
     case 1 * 8 + 4: launch_proj_t<1, 4, 2>(a, true, s); break;
     case 2 * 8 + 1: launch_proj_t<2, 1, 4>(a, true, s); break;
