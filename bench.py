@@ -145,10 +145,12 @@ def cpu_baseline_step(S_gpu, pool, dims, units, rows):
     th = min(cpu_threads(), units)
     chunks = np.array_split(np.arange(units), th)
 
+    o_last = np.zeros((units, vh, vd), np.float32)
+
     def work(ch):
         lo, hi = int(ch[0]), int(ch[-1]) + 1
         Sc = S[lo:hi]
-        o = np.zeros((hi - lo, vh, vd), np.float32)
+        o = o_last[lo:hi]
         for x in xs:
             orc.gdn_step(Sc, *(np.ascontiguousarray(x[n][lo:hi]) for n in NAMES), o, dims)
 
@@ -157,9 +159,27 @@ def cpu_baseline_step(S_gpu, pool, dims, units, rows):
         list(ex.map(work, chunks))
     dt = time.perf_counter() - t0
     hs = units * vh * rows
-    return dict(value=hs / dt, unit="head-steps/s", cores=th, kind="oracle",
-                sample=f"{units} units x {rows} steps ({hs} head-steps) of the same workload, "
-                       f"{dt:.2f} s wall on {th} threads")
+    res = dict(value=hs / dt, unit="head-steps/s", cores=th, kind="oracle",
+               sample=f"{units} units x {rows} steps ({hs} head-steps) of the same workload, "
+                      f"{dt:.2f} s wall on {th} threads")
+    return res, S, o_last
+
+
+def sample_parity(S0, pool, units, rows, S_ref, o_ref):
+    """The GPU's own run of the baseline's sample (same initial state and
+    inputs, single-step launches) against the oracle's result: elements
+    outside |x - r| <= max(1e-5 |r|, 1e-6), and the pages' max|err| / max|ref|."""
+    S = S0.clone()
+    for r in range(rows):
+        o = gdn.step(S, *(pool[r % len(pool)][n][0, :units].contiguous() for n in NAMES))
+    out = {}
+    for name, got, ref in (("o", o, o_ref), ("S", S, S_ref)):
+        x = got.cpu().numpy().astype(np.float64)
+        r = ref.astype(np.float64)
+        err = np.abs(x - r)
+        out[f"{name}_elements_out_of_tolerance"] = int(np.sum(err > np.maximum(1e-5 * np.abs(r), 1e-6)))
+        out[f"{name}_max_rel_pages"] = float(err.max() / np.abs(r).max())
+    return dict(units=units, steps=rows, **out)
 
 
 def copy_floor(S, reps=5):
@@ -232,7 +252,11 @@ def bench_decode(cfg, steps, warmup, cpu):
                    kernel="recur_wide_kernel", kernel_source_sha256_16=kernel_hash(),
                    **per_layer))
     if cpu:
-        res["cpu_baseline"] = cpu_baseline_step(S, pool, dims, units=min(N, 1024), rows=8)
+        units = min(N, 1024)
+        S0 = S[:units].clone()
+        res["cpu_baseline"], S_ref, o_ref = cpu_baseline_step(S, pool, dims, units=units, rows=8)
+        # outside the timed region: the GPU on the same sample, against the oracle
+        res["extra"]["parity_sample"] = sample_parity(S0, pool, units, 8, S_ref, o_ref)
     return res, dict(workload=cfg["name"], units=N, seqs=cfg["seqs"], layers=cfg["layers"],
                      vh=dims[0], kh=dims[1], kd=dims[2], vd=dims[3],
                      state_GB=round(N * vh * dims[2] * dims[3] * 4 / 1e9, 3),
@@ -279,8 +303,10 @@ def bench_latency(cfg, steps, warmup, cpu):
                           us_per_step_step_m=round(dt_m / (steps * T) * 1e6, 3),
                           note="3 MiB state stays in L2/MALL: latency figure, not an HBM claim"))
     if cpu:
-        res["cpu_baseline"] = cpu_baseline_step(S, [{n: inp[n][m:m + 1] for n in NAMES}
-                                                    for m in range(T)], dims, units=1, rows=T)
+        pool1 = [{n: inp[n][m:m + 1] for n in NAMES} for m in range(T)]
+        S0 = S[:1].clone()
+        res["cpu_baseline"], S_ref, o_ref = cpu_baseline_step(S, pool1, dims, units=1, rows=T)
+        res["extra"]["parity_sample"] = sample_parity(S0, pool1, 1, T, S_ref, o_ref)
     return res, dict(workload=cfg["name"], units=1, vh=vh, kd=dims[2], steps_per_iteration=T)
 
 
