@@ -1230,6 +1230,106 @@ static __device__ __forceinline__ void fe_gemv_row(int R, const float *x, const 
   }
 }
 
+// 2 to 8 GEMV rows (a few sequences, or one sequence's draft rows): a
+// workgroup per stacked weight row and all 8 batch slots (4 times the
+// workgroups of fe_gemv_block), three chunks per lane in flight.  Each slot's
+// chain and the butterfly's lane pairing (offsets 32, 16, 8, then 4, 2, 1)
+// are those of fe_gemv_block, so the results are the same bits.
+static __device__ __forceinline__ void fe_gemv_col8(int bx, int R, const float *x,
+                                                    const float *Wa, const float *Wb,
+                                                    const float *A_log, const float *dt_bias,
+                                                    float *g, float *beta, int B, int dim,
+                                                    int vh) {
+  __shared__ float s_w8[FE_WAVES][FB];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int b0 = bx * FB;
+  const float *wrow = R < vh ? Wa + (int64_t)R * dim : Wb + (int64_t)(R - vh) * dim;
+  const float *xrow[FB];
+#pragma unroll
+  for (int b = 0; b < FB; b++) {
+    int bb = b0 + b;
+    if (bb >= B) bb = B - 1;                       // clamped rows are never written
+    xrow[b] = x + (int64_t)bb * dim;
+  }
+  constexpr int STRIDE = 4 * FE_LANES;
+  constexpr int DEPTH = 3;                         // chunks per lane in flight
+  float acc[FB];
+#pragma unroll
+  for (int b = 0; b < FB; b++) acc[b] = 0.0f;
+  for (int c0 = 4 * t; c0 < dim; c0 += DEPTH * STRIDE) {
+    f4 w[DEPTH], xv[DEPTH][FB];
+#pragma unroll
+    for (int k = 0; k < DEPTH; k++) {
+      const int c = c0 + k * STRIDE;
+      if (c < dim) {
+        w[k] = ld4(wrow + c);
+#pragma unroll
+        for (int b = 0; b < FB; b++) xv[k][b] = ld4(xrow[b] + c);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < DEPTH; k++) {
+      if (c0 + k * STRIDE < dim) {
+#pragma unroll
+        for (int b = 0; b < FB; b++) {
+          float s = acc[b];
+          s = __builtin_fmaf(w[k].x, xv[k][b].x, s);
+          s = __builtin_fmaf(w[k].y, xv[k][b].y, s);
+          s = __builtin_fmaf(w[k].z, xv[k][b].z, s);
+          s = __builtin_fmaf(w[k].w, xv[k][b].w, s);
+          acc[b] = s;
+        }
+      }
+    }
+  }
+  // transposing butterfly over 8 slots (offsets 32, 16, 8), then plain adds
+  float v4[4], v2[2], v1;
+  {
+    const bool up = lane & 32;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float send = up ? acc[i] : acc[4 + i];
+      const float keep = up ? acc[4 + i] : acc[i];
+      v4[i] = keep + lane_xor<32>(send);
+    }
+  }
+  {
+    const bool up = lane & 16;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const float send = up ? v4[i] : v4[2 + i];
+      const float keep = up ? v4[2 + i] : v4[i];
+      v2[i] = keep + lane_xor<16>(send);
+    }
+  }
+  {
+    const bool up = lane & 8;
+    const float send = up ? v2[0] : v2[1];
+    const float keep = up ? v2[1] : v2[0];
+    v1 = keep + lane_xor<8>(send);
+  }
+  v1 = v1 + lane_xor<4>(v1);
+  v1 = v1 + lane_xor<2>(v1);
+  v1 = v1 + lane_xor<1>(v1);
+  if ((lane & 7) == 0) s_w8[wave][lane >> 3] = v1;   // slot 4 b5 + 2 b4 + b3
+  __syncthreads();
+  if (t < FB) {
+    float sum = s_w8[0][t];
+#pragma unroll
+    for (int w = 1; w < FE_WAVES; w++) sum = sum + s_w8[w][t];
+    const int b = b0 + t;
+    if (b < B) {
+      if (R < vh) {
+        const float sp = softplus_guarded(sum + dt_bias[R]);
+        g[(int64_t)b * vh + R] = -expf(A_log[R]) * sp;
+      } else {
+        beta[(int64_t)b * vh + (R - vh)] = 1.0f / (1.0f + expf(-sum));
+      }
+    }
+  }
+}
+
 // One launch for the whole front end: the first n_gemv workgroups run the
 // paired GEMV, the rest the conv; the two parts are independent, so their
 // latency-bound and bandwidth-bound phases overlap on the device.
@@ -1255,6 +1355,9 @@ __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
     const int g = (int)xcd_contiguous(id, a.n_gemv);
     if (a.M * a.B == 1) {
       fe_gemv_row(g, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g, a.beta, a.dim, a.vh);
+    } else if (a.M * a.B <= FB) {
+      fe_gemv_col8(0, g, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g, a.beta, a.M * a.B, a.dim,
+                   a.vh);
     } else {
       const int r_tiles = a.n_gemv / a.gemv_bx;
       fe_gemv_block(g / r_tiles, g % r_tiles, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g,
@@ -1268,7 +1371,7 @@ __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
 }
 
 int64_t frontend_workitems(int64_t B, int64_t M, int64_t conv_dim, int64_t vh) {
-  const int64_t n_gemv = M * B == 1 ? 2 * vh : ((M * B + FB - 1) / FB) * ((2 * vh + FR - 1) / FR);
+  const int64_t n_gemv = M * B <= FB ? 2 * vh : ((M * B + FB - 1) / FB) * ((2 * vh + FR - 1) / FR);
   const int64_t n_conv = ((conv_dim + 1023) / 1024) * ((B + CONV_ROWS - 1) / CONV_ROWS);
   return (n_gemv + n_conv) * FE_LANES;
 }
@@ -1283,7 +1386,7 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
   FeArgs a{x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta,
            B, M, dim, conv_dim, vh, kh, write_hist ? 1 : 0, 0, 0, 0};
   a.gemv_bx = (M * B + FB - 1) / FB;
-  a.n_gemv = M * B == 1 ? 2 * vh : a.gemv_bx * ((2 * vh + FR - 1) / FR);
+  a.n_gemv = M * B <= FB ? 2 * vh : a.gemv_bx * ((2 * vh + FR - 1) / FR);
   a.conv_bx = (conv_dim + 1023) / 1024;
   const int n_conv = a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);
   const dim3 grid((unsigned)(a.n_gemv + n_conv));
