@@ -287,6 +287,15 @@ def test_proj_q4_bytes():
         assert L.gdn_proj_q4_bytes(R, Cc) == -1, (R, Cc)
 
 
+def test_smoke_shapes_pass_host_validation():
+    """The 4-bit projection smoke() runs has a shape the library accepts (the
+    size query validates it on the host, no GPU needed)."""
+    import __graft_entry__ as entry
+    rows, R, Cc = entry.SMOKE_Q4
+    assert 1 <= rows <= 16
+    assert gdn.lib().gdn_proj_q4_bytes(R, Cc) == R * (Cc // 2 + Cc // 32 * 2)
+
+
 def test_proj_q4_pack_validation():
     L = gdn.lib()
     q, sc, Wq = fp(0), fp(1 << 36), fp(2 << 36)
