@@ -652,7 +652,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: the library and this benchmark run on one GPU; --gpus {args.gpus} is not "
               "supported (every state unit is independent, so G GPUs would each run this "
               "same kernel on N/G units with no communication).", file=sys.stderr)
         sys.exit(2)
