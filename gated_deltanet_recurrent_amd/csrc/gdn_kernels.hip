@@ -1330,9 +1330,12 @@ static __device__ __forceinline__ void fe_gemv_col8(int bx, int R, const float *
   }
 }
 
-// One launch for the whole front end: the first n_gemv workgroups run the
-// paired GEMV, the rest the conv; the two parts are independent, so their
-// latency-bound and bandwidth-bound phases overlap on the device.
+// One launch for the whole front end: the first n_conv workgroups run the
+// conv, the rest the paired GEMV; the two parts are independent, so their
+// latency-bound and bandwidth-bound phases overlap on the device (the conv
+// workgroups, whose rows run one after another, are dispatched first).  GS
+// picks the GEMV shape (0: one row, 1: 2..8 rows, 2: more), one instance
+// each so that each keeps its own register budget.
 struct FeArgs {
   const float *x, *Wa, *Wb, *A_log, *dt_bias, *xc_raw;
   float *hist;
@@ -1342,20 +1345,21 @@ struct FeArgs {
   int write_hist;         // 0: the history is read but left as it was
   int gemv_bx, conv_bx;   // x extents of the two parts
   int n_gemv;             // workgroups of the GEMV part
+  int n_conv;             // workgroups of the conv part
 };
 
-template <int KD>
+template <int KD, int GS>
 __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
-  const int id = blockIdx.x;
-  if (id < a.n_gemv) {
+  if ((int)blockIdx.x >= a.n_conv) {
+    const int id = (int)blockIdx.x - a.n_conv;
     // Each XCD takes a contiguous, batch-major range of GEMV blocks, so its
     // L2 holds a few batch rows of x and the weights once, instead of every
     // L2 pulling in all of x and all of W.  The GEMV rows of all M draft rows
     // are independent: [M][B] = M*B rows.
     const int g = (int)xcd_contiguous(id, a.n_gemv);
-    if (a.M * a.B == 1) {
+    if constexpr (GS == 0) {
       fe_gemv_row(g, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g, a.beta, a.dim, a.vh);
-    } else if (a.M * a.B <= FB) {
+    } else if constexpr (GS == 1) {
       fe_gemv_col8(0, g, a.x, a.Wa, a.Wb, a.A_log, a.dt_bias, a.g, a.beta, a.M * a.B, a.dim,
                    a.vh);
     } else {
@@ -1364,7 +1368,7 @@ __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
                     a.beta, a.M * a.B, a.dim, a.vh);
     }
   } else {
-    const int c = id - a.n_gemv;
+    const int c = (int)blockIdx.x;
     fe_conv_block<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k, a.v,
                       a.B, a.M, a.conv_dim, a.kh, a.vh, a.write_hist != 0);
   }
@@ -1384,16 +1388,18 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
                     hipStream_t s) {
   if (B <= 0 || M <= 0) return 0;
   FeArgs a{x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta,
-           B, M, dim, conv_dim, vh, kh, write_hist ? 1 : 0, 0, 0, 0};
+           B, M, dim, conv_dim, vh, kh, write_hist ? 1 : 0, 0, 0, 0, 0};
   a.gemv_bx = (M * B + FB - 1) / FB;
   a.n_gemv = M * B <= FB ? 2 * vh : a.gemv_bx * ((2 * vh + FR - 1) / FR);
   a.conv_bx = (conv_dim + 1023) / 1024;
-  const int n_conv = a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);
-  const dim3 grid((unsigned)(a.n_gemv + n_conv));
+  a.n_conv = a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);
+  const dim3 grid((unsigned)(a.n_gemv + a.n_conv));
+  const int gs = M * B == 1 ? 0 : M * B <= FB ? 1 : 2;
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(FE_LANES), 0, s, a); };
   if (kd == 128)
-    hipLaunchKernelGGL(fe_kernel<128>, grid, dim3(FE_LANES), 0, s, a);
+    gs == 0 ? go(fe_kernel<128, 0>) : gs == 1 ? go(fe_kernel<128, 1>) : go(fe_kernel<128, 2>);
   else
-    hipLaunchKernelGGL(fe_kernel<64>, grid, dim3(FE_LANES), 0, s, a);
+    gs == 0 ? go(fe_kernel<64, 0>) : gs == 1 ? go(fe_kernel<64, 1>) : go(fe_kernel<64, 2>);
   return (int)hipGetLastError();
 }
 
