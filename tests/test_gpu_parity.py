@@ -410,12 +410,14 @@ def test_frontend_parity(orc, dims, B, dim):
 
 @pytest.mark.parametrize("dims,B,M", [(synth.DIMS128, 5, 3), (synth.DIMS64, 3, 8),
                                       (synth.DIMS128, 2, 1), (synth.DIMS128, 1, 8),
-                                      (synth.DIMS64, 1, 3)])
+                                      (synth.DIMS64, 1, 3), (synth.DIMS128, 1, 12),
+                                      (synth.DIMS128, 3, 3)])
 def test_frontend_m_bit_exact_and_parity(orc, dims, B, M):
     """M draft rows in one call == M single-row GPU calls (bit for bit), and
-    the oracle's M-row front end within tolerance (history bit for bit).  With
-    B = 1 the single-row calls take the one-row GEMV (a workgroup per weight
-    row) and the M-row call the batched one."""
+    the oracle's M-row front end within tolerance (history bit for bit).  The
+    GEMV has three shapes (one row; 2 to 8 rows; more), and the cases pair
+    each with the others: B = 1 against M = 3, 8 (2-8 rows) and 12 (more), B
+    = 3 or 5 (2-8 rows) against 9 or 15 rows (more, the first ragged)."""
     say(f"frontend_m dims={dims} B={B} M={M}")
     vh, kh, kd, vd = dims
     gen = synth.make_gen(9, "cuda")
