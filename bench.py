@@ -232,8 +232,13 @@ def bench_decode(cfg, steps, warmup, cpu):
                 gdn.step(v[0], *v[1 + i % 4], o=v[5])
 
         dt_l = timed(layers, steps, warmup)
+        # the same 48 launches replayed as one graph: what is left of the gap
+        # between them is the device's own (one grid drains before the next
+        # fills), not the host's launch cost
+        dt_lg = timed_graph(layers, steps, warmup)
         per_layer = dict(per_layer_launches=L, per_layer_ms_per_step=round(dt_l / steps * 1e3, 4),
-                         per_layer_GBps=round(hs_per_step * bps * steps / dt_l / 1e9, 1))
+                         per_layer_GBps=round(hs_per_step * bps * steps / dt_l / 1e9, 1),
+                         per_layer_graph_ms_per_step=round(dt_lg / steps * 1e3, 4))
     launch_s = dt / steps
     bytes_launch = hs_per_step * bps
     achieved = bytes_launch / launch_s / 1e9
