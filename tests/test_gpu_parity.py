@@ -127,6 +127,39 @@ def test_reset_gate_bit_exact_vs_oracle(orc):
         assert bits_equal(host(S), S_h)
 
 
+@pytest.mark.parametrize("dims,N,M", [(synth.DIMS128, 3, 1), (synth.DIMS64, 3, 1),
+                                      (synth.DIMS128, 3, 3), (synth.DIMS128, 24, 3)])
+def test_nan_stays_in_its_tile(orc, dims, N, M):
+    """A NaN planted in one state element spreads only as IEEE arithmetic
+    carries it inside its own (unit, head) tile: after M steps (single-step,
+    few-tile and many-tile M-step kernels) the NaN positions of S and o equal
+    the oracle's, the finite elements agree within tolerance, and every other
+    tile stays finite (a wrong tile, row or column offset would spread it)."""
+    say(f"nan isolation dims={dims} N={N} M={M}")
+    vh, kh, kd, vd = dims
+    gen = synth.make_gen(17, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    u, h, i, j = 1, vh // 2 + 1, kd // 3, vd - 2
+    S[u, h, i, j] = float("nan")
+    S_h = host(S)
+    x = {n: host(inp[n]) for n in NAMES}
+    if M == 1:
+        o = gdn.step(S, *(inp[n][0] for n in NAMES)).unsqueeze(0)
+    else:
+        o = gdn.step_m(S, *(inp[n] for n in NAMES))
+    o_ref = np.stack(ref_steps(orc, S_h, x, dims, M))
+    got_S, got_o = host(S), host(o)
+    for got, ref, what in ((got_S, S_h, "S"), (got_o, o_ref, "o")):
+        nan = np.isnan(ref)
+        assert nan.any(), what
+        assert np.array_equal(np.isnan(got), nan), what
+        assert_close(got[~nan], ref[~nan], what)
+    others = np.ones((N, vh), bool)
+    others[u, h] = False
+    assert np.isfinite(got_S[others]).all() and np.isfinite(got_o[:, others]).all()
+
+
 def test_unit_offsets_identical():
     dims = synth.DIMS128
     N = 6
