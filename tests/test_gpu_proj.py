@@ -126,6 +126,32 @@ def test_proj_one_hot_rows_select_weight_columns():
         assert bits_equal(y[i], np.ascontiguousarray(Wh[:, c])), c
 
 
+@pytest.mark.parametrize("rows,R,C", [(3, 96, 1536), (70, 96, 1536), (150, 4096, 256)])
+def test_proj_nan_reaches_only_its_row_and_output(rows, R, C):
+    """A NaN weight W[o][c] makes exactly column o of y NaN, and a NaN in
+    x[r] exactly row r; every other element keeps the bits of the NaN-free
+    call.  A wrong permutation in the packed operand order, or a tile that
+    read another row's x, would move or spread the NaN."""
+    say(f"proj NaN isolation rows={rows} R={R} C={C}")
+    x, W = operands(91, rows, R, C)
+    clean = host(gdn.proj(x, gdn.proj_pack(W)))
+    o, c, r = R // 2 + 3, C - 5, rows // 2
+    Wn = W.clone()
+    Wn[o, c] = float("nan")
+    y = host(gdn.proj(x, gdn.proj_pack(Wn)))
+    nan = np.zeros_like(clean, bool)
+    nan[:, o] = True
+    assert np.array_equal(np.isnan(y), nan)
+    assert bits_equal(y[~nan], clean[~nan])
+    xn = x.clone()
+    xn[r, 7] = float("nan")
+    y = host(gdn.proj(xn, gdn.proj_pack(W)))
+    nan = np.zeros_like(clean, bool)
+    nan[r, :] = True
+    assert np.array_equal(np.isnan(y), nan)
+    assert bits_equal(y[~nan], clean[~nan])
+
+
 def test_proj_two_products_share_one_launch():
     """in_proj_qkv and in_proj_z in one launch equal two separate launches."""
     say("proj paired")

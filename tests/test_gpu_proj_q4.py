@@ -209,6 +209,27 @@ def test_q4_rows_are_independent_and_paired_launch_matches():
         assert bits_equal(part, np.ascontiguousarray(full0[lo:lo + n])), (lo, n)
 
 
+@pytest.mark.parametrize("rows,R", [(1, 16384), (7, 192), (16, 192)])
+def test_q4_nan_in_x_reaches_only_its_row(rows, R):
+    """A NaN in x[r] makes exactly row r of y NaN (every weight is finite, a
+    zero weight included: 0 x NaN is NaN); the other rows keep the bits of
+    the NaN-free call, in both launch shapes (one and two workgroups per
+    output group)."""
+    say(f"proj_q4 NaN isolation rows={rows} R={R}")
+    C = 2048
+    x, q, sc = q4_operands(151, rows, R, C)
+    Wq = gdn.proj_q4_pack(q, sc)
+    clean = host(gdn.proj_q4(x, Wq))
+    r = rows // 2
+    xn = x.clone()
+    xn[r, C - 3] = float("nan")
+    y = host(gdn.proj_q4(xn, Wq))
+    nan = np.zeros_like(clean, bool)
+    nan[r, :] = True
+    assert np.array_equal(np.isnan(y), nan)
+    assert bits_equal(y[~nan], clean[~nan])
+
+
 def test_q4_launch_shapes_agree_bit_for_bit():
     """A launch with fewer 64-output groups than CUs takes two workgroups per
     group (half sums added into y); a larger one takes one.  The same matrix
