@@ -441,6 +441,49 @@ def test_frontend_parity(orc, dims, B, dim):
         assert bits_equal(host(hist), hist_h)
 
 
+@pytest.mark.parametrize("dims,B", [(synth.DIMS128, 5), (synth.DIMS128, 13), (synth.DIMS64, 3)])
+def test_frontend_nan_stays_in_its_sequence(orc, dims, B):
+    """A NaN in one sequence's hidden input x, and another in one raw conv
+    channel of a second sequence: the NaN positions of q, k, v, g, beta and
+    the history equal the oracle's, the finite elements agree within
+    tolerance, and the other sequences keep the bits of the NaN-free call."""
+    say(f"frontend NaN isolation dims={dims} B={B}")
+    vh, kh, kd, vd = dims
+    gen = synth.make_gen(23, "cuda")
+    w = synth.frontend_weights(gen, dims, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=1, device="cuda")
+    x, xc, h0 = fe["x"][0], fe["xc_raw"][0], fe["hist"]
+    hist_c = h0.clone()
+    clean = gdn.frontend(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], xc, hist_c,
+                         w["conv_w"], dims)
+    clean = {n: host(t) for n, t in clean.items()}
+    bx, bc = 1, B - 1
+    x, xc = x.clone(), xc.clone()
+    x[bx, 17] = float("nan")
+    xc[bc, kh * kd + 5] = float("nan")             # a channel of the k part
+    hist = h0.clone()
+    out = gdn.frontend(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], xc, hist, w["conv_w"],
+                       dims)
+    wh = {n: host(t) for n, t in w.items()}
+    ref = dict(q=np.zeros((B, kh, kd), np.float32), k=np.zeros((B, kh, kd), np.float32),
+               v=np.zeros((B, vh, vd), np.float32), g=np.zeros((B, vh), np.float32),
+               beta=np.zeros((B, vh), np.float32))
+    hist_h = host(h0)
+    orc.gdn_frontend(host(x), wh["Wa"], wh["Wb"], wh["A_log"], wh["dt_bias"], host(xc), hist_h,
+                     wh["conv_w"], ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"], dims)
+    any_nan = False
+    for n in NAMES:
+        got, r = host(out[n]), ref[n]
+        nan = np.isnan(r)
+        any_nan |= bool(nan.any())
+        assert np.array_equal(np.isnan(got), nan), n
+        assert_close(got[~nan], r[~nan], n)
+        keep = [b for b in range(B) if b not in (bx, bc)]
+        assert bits_equal(got[keep], clean[n][keep]), n
+    assert any_nan
+    assert np.array_equal(np.isnan(host(hist)), np.isnan(hist_h))
+
+
 @pytest.mark.parametrize("dims,B,M", [(synth.DIMS128, 5, 3), (synth.DIMS64, 3, 8),
                                       (synth.DIMS128, 2, 1), (synth.DIMS128, 1, 8),
                                       (synth.DIMS64, 1, 3), (synth.DIMS128, 1, 12),
