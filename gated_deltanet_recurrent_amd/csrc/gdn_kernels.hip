@@ -767,9 +767,148 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
   }
 }
 
-// Single steps run the wide geometry.  Calls with M >= 2 rows per unit run
-// the deep geometry, except launches of fewer than GDN_WIDEM_BELOW tiles with
-// M <= MC, which run the wide one step after step (same bits either way).
+// ----- split geometry, several steps (kd = 128, few tiles) ----------------
+//
+// With a sequence or two per launch, the wide M-step kernel runs one
+// 1024-lane workgroup per tile: four waves per SIMD on a few dozen CUs, and
+// each step waits on two barriers and one wave's fold.  Here SPLIT_NS
+// workgroups serve a tile, one per KD / SPLIT_NS columns.  The columns of S
+// are independent (S^T k and S^T q reduce over rows only), so a workgroup
+// holds every row of its columns and needs no other.  Lane t is (row group
+// t / SPLIT_CG, column group t % SPLIT_CG): the W partial of row groups 2w
+// and 2w + 1 pairs lanes t and t ^ SPLIT_CG; the 16 W partials go through LDS
+// (double-buffered by step parity), and every lane folds them for its own
+// column group (H0, H1, H0 + H1).  That is the canonical tree, so the bits
+// are those of the other geometries, with one barrier per step.  Ungated
+// calls only: the gated RMSNorm needs the whole head's output in one
+// workgroup (a second pass over the raw outputs cost more than it saved).
+constexpr int SPLIT_NS = 4;                                  // workgroups per tile
+constexpr int SPLIT_CG = Canon<128>::CG / SPLIT_NS;          // column groups per workgroup
+constexpr int SPLIT_LANES = Canon<128>::RG * SPLIT_CG;       // 256
+
+// Left folds of W partials 0..7 and 8..15 for column group lane % SPLIT_CG,
+// then their sum (lanes l and l ^ SPLIT_CG hold the two folds).
+static __device__ __forceinline__ f4 split_sum(const f4 (*red)[SPLIT_CG], int lane) {
+  constexpr int PER = Canon<128>::NWP / 2;
+  const int h = (lane / SPLIT_CG) & 1, c = lane % SPLIT_CG;
+  f4 acc = red[h * PER][c];
+#pragma unroll
+  for (int i = 1; i < PER; i++) acc = acc + red[h * PER + i][c];
+  acc.x = acc.x + lane_xor<SPLIT_CG>(acc.x);
+  acc.y = acc.y + lane_xor<SPLIT_CG>(acc.y);
+  acc.z = acc.z + lane_xor<SPLIT_CG>(acc.z);
+  acc.w = acc.w + lane_xor<SPLIT_CG>(acc.w);
+  return acc;
+}
+
+// p[rg] + p[rg ^ 1]: the partner row group sits SPLIT_CG lanes away
+static __device__ __forceinline__ f4 split_pair(f4 p) {
+  p.x = p.x + lane_xor<SPLIT_CG>(p.x);
+  p.y = p.y + lane_xor<SPLIT_CG>(p.y);
+  p.z = p.z + lane_xor<SPLIT_CG>(p.z);
+  p.w = p.w + lane_xor<SPLIT_CG>(p.w);
+  return p;
+}
+
+__global__ __launch_bounds__(SPLIT_LANES) void recur_split_kernel(RecurArgs a) {
+  constexpr int KD = 128, RG = Canon<KD>::RG, NWP = Canon<KD>::NWP;
+  __shared__ Stage<KD, false> sb;
+  __shared__ f4 s_red_k[2][NWP][SPLIT_CG];
+  __shared__ f4 s_red_o[2][NWP][SPLIT_CG];
+
+  const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
+  if (a.hist != nullptr && bid >= a.tile_wgs) {   // uniform per workgroup
+    hist_item<SPLIT_LANES>(a, bid - a.tile_wgs);
+    return;
+  }
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int cg = t % SPLIT_CG, rg = t / SPLIT_CG;
+  // the tile and this workgroup's columns (the SPLIT_NS workgroups of a tile
+  // are adjacent, so they share an XCD and its L2 copy of q, k, v)
+  const int64_t tile = bid / SPLIT_NS;
+  const int col0 = 4 * ((int)(bid - tile * SPLIT_NS) * SPLIT_CG + cg);
+  const int64_t unit = tile / a.vh;
+  const int head = (int)(tile - unit * a.vh);
+  const int hh = head / (a.vh / a.kh);
+  int steps = a.steps ? a.steps[unit] : a.M;
+  if (steps < 0 || steps > a.M) {      // device-supplied counts: refuse the unit
+    if (a.status != nullptr && t == 0) a.status[0] = 1;
+    steps = 0;
+  }
+  if (steps == 0 && a.S_src == a.S_dst && a.snap == nullptr) return;
+  const int64_t tile_off = tile * (int64_t)(KD * KD);
+  const rsrc_t src = buf_rsrc(a.S_src + tile_off, KD * KD * 4);
+  const int lane_off = (rg * KD + col0) * 4;
+
+  ChunkRegs<KD, SPLIT_LANES, false> cr;
+  if (steps > 0) chunk_load<KD, SPLIT_LANES, false>(cr, a, t, unit, head, hh, 0, steps);
+  f4 s[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) s[j] = ld_stream<true>(src, lane_off, j * (RG * KD * 4));
+  if (a.snap != nullptr) {            // fused mark: the tile as loaded, before the steps
+    const rsrc_t snp = buf_rsrc(a.snap + tile_off, KD * KD * 4);
+#pragma unroll
+    for (int j = 0; j < 4; j++) st_stream<false>(snp, lane_off, j * (RG * KD * 4), s[j]);
+  }
+  // the output of row r for this workgroup's columns
+  auto emit = [&](int r, int par) {
+    const f4 ov = split_sum(s_red_o[par], lane);
+    if (lane < SPLIT_CG) {
+      const int64_t urow = (int64_t)r * a.n_units + unit;
+      st4(a.o + (urow * a.vh + head) * KD + 4 * ((col0 / 4 - cg) + lane), ov);
+    }
+  };
+
+  if (steps > 0) {
+    chunk_store<KD, SPLIT_LANES, false>(sb, cr, t, steps);
+    __syncthreads();
+    for (int r = 0; r < steps; r++) {
+      const int par = r & 1;
+      const float alpha = sb.alpha[r];
+      const f4 kk = lds4(&sb.k[r][rg * 4]);
+      // decay, then S^T k partials over the decayed state
+      f4 p = splat(0.0f);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        s[j] = s[j] * alpha;
+        p = fma4(s[j], splat(kk[j]), p);
+      }
+      p = split_pair(p);
+      if ((rg & 1) == 0) s_red_k[par][rg >> 1][cg] = p;
+      __syncthreads();
+      // the previous row's output, beside every wave's fold of S^T k
+      if (wave == 1 && r > 0 && a.o != nullptr) emit(r - 1, par ^ 1);
+      const f4 kv = split_sum(s_red_k[par], lane);
+      const f4 tmp = (lds4(&sb.v[r][col0]) - kv) * sb.beta[r];
+      const f4 qq = lds4(&sb.q[r][rg * 4]);
+      // rank-1 update, then S^T q partials with the updated state
+      p = splat(0.0f);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        s[j] = fma4(splat(kk[j]), tmp, s[j]);
+        p = fma4(s[j], splat(qq[j]), p);
+      }
+      p = split_pair(p);
+      if ((rg & 1) == 0) s_red_o[par][rg >> 1][cg] = p;
+    }
+  }
+
+  if (a.S_dst != nullptr) {            // null: outputs only, the state is left as it was
+    const rsrc_t dst = buf_rsrc(a.S_dst + tile_off, KD * KD * 4);
+#pragma unroll
+    for (int j = 0; j < 4; j++) st_stream<true>(dst, lane_off, j * (RG * KD * 4), s[j]);
+  }
+  if (steps > 0) {
+    __syncthreads();
+    if (wave == 0 && a.o != nullptr) emit(steps - 1, (steps - 1) & 1);
+  }
+}
+
+// Launches of fewer than GDN_WIDEM_BELOW tiles with M <= MC rows per unit run
+// the split geometry (kd = 128, ungated); otherwise single steps run the wide
+// geometry, and M >= 2 rows the wide one step after step (few tiles) or the
+// deep geometry.  The same bits whichever serves a call.
 #ifndef GDN_WIDEM_BELOW
 #define GDN_WIDEM_BELOW 1024
 #endif
@@ -785,7 +924,11 @@ template <int KD, bool GATED>
 static void launch_recur_kd(RecurArgs a, int64_t tiles, hipStream_t s) {
   const dim3 grid((unsigned)tiles);
   a.tile_wgs = tiles;
-  if (a.M == 1) {
+  if (KD == 128 && !GATED && a.M <= MC && tiles < GDN_WIDEM_BELOW) {
+    a.tile_wgs = tiles * SPLIT_NS;
+    const dim3 g2((unsigned)(a.tile_wgs + hist_wgs(a, SPLIT_LANES)));
+    hipLaunchKernelGGL(recur_split_kernel, g2, dim3(SPLIT_LANES), 0, s, a);
+  } else if (a.M == 1) {
     // kd = 64: four adjacent heads of one unit per workgroup, so that a
     // workgroup streams 64 KiB of consecutive state like a kd = 128 one
     constexpr int TPW = KD == 64 ? 4 : 1;
