@@ -63,7 +63,7 @@ def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
 _Q4_SECTION = b"// " + b"-" * 75 + b"\n// Dense layer projections with 4-bit weights"
 HASH_SECTIONS = {
     "recur_wide_kernel": ((b"namespace gdn {", b"// ----- wide geometry, several steps"),
-                          (b"// Single steps run the wide geometry", b"// Streaming copy")),
+                          (b"// Launches of fewer than GDN_WIDEM_BELOW tiles", b"// Streaming copy")),
     "proj_kernel": ((b"namespace gdn {", b"// Recurrence\n"),
                     (b"// Dense layer projections", _Q4_SECTION), (b"}  // namespace gdn", None)),
     "proj_q4_kernel": ((b"namespace gdn {", b"// Recurrence\n"), (_Q4_SECTION, None)),
