@@ -152,14 +152,16 @@ static __device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) 
 //             sum = H0 + H1
 //   kd = 64:  W[w] = (p[4w] + p[4w+1]) + (p[4w+2] + p[4w+3]) (w < 4);
 //             sum = (W0 + W1) + (W2 + W3)
-// Two tile geometries compute exactly this tree, so every entry point gives
+// Three tile geometries compute exactly this tree, so every entry point gives
 // the same bits whichever geometry serves it:
 //   wide (single steps, bandwidth bound): 16 floats per lane, kd = 128 on
 //     1024 lanes, kd = 64 on 256 lanes; lane = (column group, row group);
 //   deep (several steps per call, arithmetic bound): 64 floats per lane,
 //     kd = 128 on 256 lanes, kd = 64 on one wave; lane = (column group,
 //     4 consecutive row groups), which keeps more tiles resident per CU and
-//     needs fewer cross-lane exchanges per element.
+//     needs fewer cross-lane exchanges per element;
+//   split (few tiles, latency bound, kd = 128): the wide lane layout over a
+//     quarter of the columns, four workgroups per tile.
 
 template <int KD>
 struct Canon {
