@@ -907,12 +907,19 @@ __global__ __launch_bounds__(SPLIT_LANES) void recur_split_kernel(RecurArgs a) {
   }
 }
 
-// Launches of fewer than GDN_WIDEM_BELOW tiles with M <= MC rows per unit run
-// the split geometry (kd = 128, ungated); otherwise single steps run the wide
-// geometry, and M >= 2 rows the wide one step after step (few tiles) or the
-// deep geometry.  The same bits whichever serves a call.
+// Launches of fewer than GDN_WIDEM_BELOW tiles with M <= MC rows per unit and
+// at most GDN_FEW_TILE_ROWS tile-rows (tiles x M) run the split geometry (kd =
+// 128, ungated); otherwise single steps run the wide geometry, and M >= 2 rows
+// the wide one step after step (the same few-tile bound) or the deep
+// geometry.  The same bits whichever serves a call.  The bound is where the
+// deep kernel's throughput overtakes the few-tile kernels' latency (step_m at
+// M = 8: split 13.4 against 14.8 us at 192 tiles, 20.6 against 18.0 at 384;
+// at M = 2 split is ahead up to 1008 tiles).
 #ifndef GDN_WIDEM_BELOW
 #define GDN_WIDEM_BELOW 1024
+#endif
+#ifndef GDN_FEW_TILE_ROWS
+#define GDN_FEW_TILE_ROWS 2048
 #endif
 
 int recur_lanes(int kd) { return kd == 128 ? Geo<128>::LANES : Geo<64>::LANES; }
@@ -926,7 +933,8 @@ template <int KD, bool GATED>
 static void launch_recur_kd(RecurArgs a, int64_t tiles, hipStream_t s) {
   const dim3 grid((unsigned)tiles);
   a.tile_wgs = tiles;
-  if (KD == 128 && !GATED && a.M <= MC && tiles < GDN_WIDEM_BELOW) {
+  const bool few = a.M <= MC && tiles < GDN_WIDEM_BELOW && tiles * a.M <= GDN_FEW_TILE_ROWS;
+  if (KD == 128 && !GATED && few) {
     a.tile_wgs = tiles * SPLIT_NS;
     const dim3 g2((unsigned)(a.tile_wgs + hist_wgs(a, SPLIT_LANES)));
     hipLaunchKernelGGL(recur_split_kernel, g2, dim3(SPLIT_LANES), 0, s, a);
@@ -949,7 +957,7 @@ static void launch_recur_kd(RecurArgs a, int64_t tiles, hipStream_t s) {
       hipLaunchKernelGGL((recur_wide_kernel<KD, false, GATED, 1>), grid, dim3(Geo<KD>::LANES), 0,
                          s, a);
     }
-  } else if (a.M <= MC && tiles < GDN_WIDEM_BELOW) {
+  } else if (few) {
     const dim3 g2((unsigned)(tiles + hist_wgs(a, Geo<KD>::LANES)));
     hipLaunchKernelGGL((recur_widem_kernel<KD, GATED>), g2, dim3(Geo<KD>::LANES), 0, s, a);
   } else {
