@@ -527,6 +527,9 @@ __global__ __launch_bounds__(Geo<KD>::LANES) void recur_widem_kernel(RecurArgs a
   __shared__ f4 s_red_k[G::NW][G::CG];
   __shared__ f4 s_red_o[G::NW][G::CG];
   __shared__ f4 s_tmp[G::CG];
+  // gated: the folded output rows, normalised after the last step (the
+  // RMSNorm of each row then runs on its own wave, off the step chain)
+  __shared__ f4 s_orow[GATED ? MC : 1][G::CG];
 
   if (a.hist != nullptr) {             // uniform per workgroup
     const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -581,8 +584,12 @@ __global__ __launch_bounds__(Geo<KD>::LANES) void recur_widem_kernel(RecurArgs a
       } else if (wave == 1 && r > 0 && a.o != nullptr) {
         // the previous step's output, in parallel with wave 0's S^T k
         const f4 ov = tile_sum<KD>(s_red_o, lane);
-        const int64_t prow = (int64_t)(r - 1) * a.n_units + ti.unit;
-        emit_o<KD, GATED>(a, prow, ti.head, lane % G::CG, lane < G::CG, ov, zprev);
+        if constexpr (GATED) {
+          if (lane < G::CG) s_orow[r - 1][lane] = ov;
+        } else {
+          const int64_t prow = (int64_t)(r - 1) * a.n_units + ti.unit;
+          emit_o<KD, GATED>(a, prow, ti.head, lane % G::CG, lane < G::CG, ov, zprev);
+        }
       }
       __syncthreads();
       const f4 tmp = s_tmp[cg];
@@ -610,8 +617,22 @@ __global__ __launch_bounds__(Geo<KD>::LANES) void recur_widem_kernel(RecurArgs a
     __syncthreads();
     if (wave == 0 && a.o != nullptr) {
       const f4 ov = tile_sum<KD>(s_red_o, lane);
-      const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
-      emit_o<KD, GATED>(a, urow, ti.head, lane % G::CG, lane < G::CG, ov, zprev);
+      if constexpr (GATED) {
+        if (lane < G::CG) s_orow[steps - 1][lane] = ov;
+      } else {
+        const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
+        emit_o<KD, GATED>(a, urow, ti.head, lane % G::CG, lane < G::CG, ov, zprev);
+      }
+    }
+    if constexpr (GATED) {
+      __syncthreads();
+      if (a.o != nullptr) {
+        for (int r = wave; r < steps; r += G::NW) {
+          const int64_t urow = (int64_t)r * a.n_units + ti.unit;
+          emit_o<KD, GATED>(a, urow, ti.head, lane % G::CG, lane < G::CG,
+                            s_orow[r][lane % G::CG], &sb.z[r][0]);
+        }
+      }
     }
   }
 }
