@@ -1347,6 +1347,87 @@ static __device__ __forceinline__ void fe_conv_block(int bx, int by, const float
   }
 }
 
+// M draft rows at once (M >= 2): wave m of a workgroup takes row m (and m +
+// FE_WAVES, ...) of one sequence over CONV_RCH channels.  Row m's taps are
+// raw rows m - 3 .. m, those before row 0 from the history, so the rows need
+// not wait on each other as the sliding window above does; each row uses that
+// window's arithmetic on the same frames, so the bits are the same.  The new
+// history (the last three frames) is read before a barrier and written after
+// it, once every row of the workgroup has read the old one.
+constexpr int CONV_RCH = 256;   // channels per row-parallel workgroup
+// up to this many sequences (frontend_m at M = 8: 1 sequence 7.1 -> 4.6 us,
+// 8 sequences 9.3 -> 7.2; from 16 the window's single read of each frame
+// wins, 10.9 against 11.2 us, and 54 against 62 at 128)
+#ifndef GDN_CONV_ROWS_MAX_B
+#define GDN_CONV_ROWS_MAX_B 8
+#endif
+
+template <int KD>
+static __device__ __forceinline__ void fe_conv_rows(int bx, int b, const float *xc_raw, float *hist,
+                                                    const float *conv_w, float *q, float *k,
+                                                    float *v, int B, int M, int conv_dim, int kh,
+                                                    int vh, bool write_hist) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ch = bx * CONV_RCH + 4 * lane;
+  const bool valid = ch < conv_dim;
+  const int qk_w = kh * KD;
+  float *hb = hist + (int64_t)b * 3 * conv_dim + ch;
+  // raw frame f of sequence b; f < 0: history frame 3 + f (oldest first)
+  auto frame = [&](int f) -> f4 {
+    return f < 0 ? ld4(hb + (int64_t)(3 + f) * conv_dim)
+                 : ld4(xc_raw + ((int64_t)f * B + b) * conv_dim + ch);
+  };
+  f4 wc[4] = {splat(0.0f), splat(0.0f), splat(0.0f), splat(0.0f)};
+  if (valid) {
+    const float *w = conv_w + (int64_t)ch * 4;
+#pragma unroll
+    for (int c = 0; c < 4; c++) wc[c] = ld4(w + 4 * c);
+  }
+  for (int m = wave; m < M; m += FE_WAVES) {    // uniform per wave
+    const int64_t row = (int64_t)m * B + b;      // [M][B] row
+    float out[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (valid) {
+      const f4 h0 = frame(m - 3), h1 = frame(m - 2), h2 = frame(m - 1), raw = frame(m);
+      const float hr0[4] = {h0.x, h0.y, h0.z, h0.w};
+      const float hr1[4] = {h1.x, h1.y, h1.z, h1.w};
+      const float hr2[4] = {h2.x, h2.y, h2.z, h2.w};
+      const float rr[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        float acc = wc[c].x * hr0[c];
+        acc = __builtin_fmaf(wc[c].y, hr1[c], acc);
+        acc = __builtin_fmaf(wc[c].z, hr2[c], acc);
+        acc = __builtin_fmaf(wc[c].w, rr[c], acc);
+        out[c] = acc / (1.0f + expf(-acc));
+      }
+    }
+    // per key-head sum of squares over KD/4 lanes (every lane takes part)
+    float ss = out[0] * out[0];
+    ss = __builtin_fmaf(out[1], out[1], ss);
+    ss = __builtin_fmaf(out[2], out[2], ss);
+    ss = __builtin_fmaf(out[3], out[3], ss);
+    ss = xor_fold<1, KD / 4>(ss);
+    if (valid) {
+      const f4 o4 = {out[0], out[1], out[2], out[3]};
+      if (ch < 2 * qk_w) {
+        const float inv = 1.0f / sqrtf(ss + 1e-6f);
+        if (ch < qk_w)
+          st4(q + row * qk_w + ch, (o4 * inv) * (1.0f / sqrtf((float)KD)));
+        else
+          st4(k + row * qk_w + (ch - qk_w), o4 * inv);
+      } else {
+        st4(v + row * (int64_t)vh * KD + (ch - 2 * qk_w), o4);
+      }
+    }
+  }
+  if (write_hist) {                               // uniform
+    f4 hn = splat(0.0f);
+    if (valid && wave < 3) hn = frame(M - 3 + wave);
+    __syncthreads();
+    if (valid && wave < 3) st4(hb + (int64_t)wave * conv_dim, hn);
+  }
+}
+
 // One GEMV row per call (one sequence, one draft row): a workgroup per
 // stacked weight row (2 vh of them instead of 2 vh / FR), every lane's chunks
 // requested at once.  Each lane's chain over its columns and the lane pairing
@@ -1507,9 +1588,10 @@ static __device__ __forceinline__ void fe_gemv_col8(int bx, int R, const float *
 // One launch for the whole front end: the first n_conv workgroups run the
 // conv, the rest the paired GEMV; the two parts are independent, so their
 // latency-bound and bandwidth-bound phases overlap on the device (the conv
-// workgroups, whose rows run one after another, are dispatched first).  GS
-// picks the GEMV shape (0: one row, 1: 2..8 rows, 2: more), one instance
-// each so that each keeps its own register budget.
+// workgroups are dispatched first).  GS picks the GEMV shape (0: one row, 1:
+// 2..8 rows, 2: more) and CR the conv (0: a sliding window per sequence for
+// single rows, 1: M >= 2 rows in parallel), one instance each so that each
+// keeps its own register budget.
 struct FeArgs {
   const float *x, *Wa, *Wb, *A_log, *dt_bias, *xc_raw;
   float *hist;
@@ -1522,7 +1604,7 @@ struct FeArgs {
   int n_conv;             // workgroups of the conv part
 };
 
-template <int KD, int GS>
+template <int KD, int GS, bool CR>
 __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
   if ((int)blockIdx.x >= a.n_conv) {
     const int id = (int)blockIdx.x - a.n_conv;
@@ -1543,14 +1625,20 @@ __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
     }
   } else {
     const int c = (int)blockIdx.x;
-    fe_conv_block<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k, a.v,
-                      a.B, a.M, a.conv_dim, a.kh, a.vh, a.write_hist != 0);
+    if constexpr (CR)
+      fe_conv_rows<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k, a.v,
+                       a.B, a.M, a.conv_dim, a.kh, a.vh, a.write_hist != 0);
+    else
+      fe_conv_block<KD>(c % a.conv_bx, c / a.conv_bx, a.xc_raw, a.hist, a.conv_w, a.q, a.k,
+                        a.v, a.B, a.M, a.conv_dim, a.kh, a.vh, a.write_hist != 0);
   }
 }
 
 int64_t frontend_workitems(int64_t B, int64_t M, int64_t conv_dim, int64_t vh) {
   const int64_t n_gemv = M * B <= FB ? 2 * vh : ((M * B + FB - 1) / FB) * ((2 * vh + FR - 1) / FR);
-  const int64_t n_conv = ((conv_dim + 1023) / 1024) * ((B + CONV_ROWS - 1) / CONV_ROWS);
+  const int64_t n_conv = M >= 2 && B <= GDN_CONV_ROWS_MAX_B
+                             ? ((conv_dim + CONV_RCH - 1) / CONV_RCH) * B
+                                : ((conv_dim + 1023) / 1024) * ((B + CONV_ROWS - 1) / CONV_ROWS);
   return (n_gemv + n_conv) * FE_LANES;
 }
 
@@ -1565,15 +1653,25 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
            B, M, dim, conv_dim, vh, kh, write_hist ? 1 : 0, 0, 0, 0, 0};
   a.gemv_bx = (M * B + FB - 1) / FB;
   a.n_gemv = M * B <= FB ? 2 * vh : a.gemv_bx * ((2 * vh + FR - 1) / FR);
-  a.conv_bx = (conv_dim + 1023) / 1024;
-  a.n_conv = a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);
+  const bool cr = M >= 2 && B <= GDN_CONV_ROWS_MAX_B;
+  a.conv_bx = cr ? (conv_dim + CONV_RCH - 1) / CONV_RCH : (conv_dim + 1023) / 1024;
+  a.n_conv = cr ? a.conv_bx * B : a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);
   const dim3 grid((unsigned)(a.n_gemv + a.n_conv));
   const int gs = M * B == 1 ? 0 : M * B <= FB ? 1 : 2;
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(FE_LANES), 0, s, a); };
-  if (kd == 128)
-    gs == 0 ? go(fe_kernel<128, 0>) : gs == 1 ? go(fe_kernel<128, 1>) : go(fe_kernel<128, 2>);
-  else
-    gs == 0 ? go(fe_kernel<64, 0>) : gs == 1 ? go(fe_kernel<64, 1>) : go(fe_kernel<64, 2>);
+  if (kd == 128) {
+    if (cr)
+      gs == 1 ? go(fe_kernel<128, 1, true>) : go(fe_kernel<128, 2, true>);
+    else
+      gs == 0 ? go(fe_kernel<128, 0, false>) : gs == 1 ? go(fe_kernel<128, 1, false>)
+              : go(fe_kernel<128, 2, false>);
+  } else {
+    if (cr)
+      gs == 1 ? go(fe_kernel<64, 1, true>) : go(fe_kernel<64, 2, true>);
+    else
+      gs == 0 ? go(fe_kernel<64, 0, false>) : gs == 1 ? go(fe_kernel<64, 1, false>)
+              : go(fe_kernel<64, 2, false>);
+  }
   return (int)hipGetLastError();
 }
 

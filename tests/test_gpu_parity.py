@@ -487,13 +487,17 @@ def test_frontend_nan_stays_in_its_sequence(orc, dims, B):
 @pytest.mark.parametrize("dims,B,M", [(synth.DIMS128, 5, 3), (synth.DIMS64, 3, 8),
                                       (synth.DIMS128, 2, 1), (synth.DIMS128, 1, 8),
                                       (synth.DIMS64, 1, 3), (synth.DIMS128, 1, 12),
-                                      (synth.DIMS128, 3, 3)])
+                                      (synth.DIMS128, 3, 3), (synth.DIMS128, 9, 3),
+                                      (synth.DIMS64, 10, 2)])
 def test_frontend_m_bit_exact_and_parity(orc, dims, B, M):
     """M draft rows in one call == M single-row GPU calls (bit for bit), and
     the oracle's M-row front end within tolerance (history bit for bit).  The
     GEMV has three shapes (one row; 2 to 8 rows; more), and the cases pair
     each with the others: B = 1 against M = 3, 8 (2-8 rows) and 12 (more), B
-    = 3 or 5 (2-8 rows) against 9 or 15 rows (more, the first ragged)."""
+    = 3 or 5 (2-8 rows) against 9 or 15 rows (more, the first ragged).  The
+    conv of an M-row call runs its rows in parallel up to 8 sequences and
+    slides one window per sequence beyond (B = 9, 10), as single-row calls
+    always do."""
     say(f"frontend_m dims={dims} B={B} M={M}")
     vh, kh, kd, vd = dims
     gen = synth.make_gen(9, "cuda")
