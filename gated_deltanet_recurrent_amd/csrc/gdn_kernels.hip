@@ -15,6 +15,9 @@
 //  * deep geometry (M steps): 64 floats per lane, more tiles per CU and fewer
 //    cross-lane exchanges per element; the tile stays in VGPRs across all M
 //    steps (read once, written once).
+//  * split geometry (ungated calls on a few tiles, kd = 128): the wide lane
+//    layout over a quarter of a tile's columns, four workgroups per tile, one
+//    barrier per step; for the latency-bound single-sequence case.
 //  * all geometries compute one canonical summation tree for the read-outs,
 //    so step, step_m, rollback, verify and commit agree bit for bit whichever
 //    geometry serves them; FMA use is explicit (this file is compiled with
@@ -23,7 +26,8 @@
 //    tiles; the state is streamed with raw buffer loads (nt) and stores
 //    (sc0 sc1 nt); per-step inputs are staged in LDS in chunks of 8 rows.
 // Front end (section 3 and Fig. 1 caption): the paired beta / a GEMV with the
-// gate transform and the causal conv + SiLU + q/k normalisation in one launch.
+// gate transform and the causal conv + SiLU + q/k normalisation in one launch
+// (M draft rows of a few sequences run their conv rows in parallel).
 // Projections (Fig. 1 caption, steps 1 and 7): f32 weights on the fp32
 // matrix cores in packed operand order, and 4-bit weights with binary16 block
 // scales on a VALU kernel (section 8 and 12), each with a fixed summation
