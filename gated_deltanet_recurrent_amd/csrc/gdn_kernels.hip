@@ -523,6 +523,8 @@ static __device__ __forceinline__ void hist_item(const RecurArgs &a, int64_t ite
 // the deep kernel's step loop (all rows staged at once; the output of step
 // m - 1 is completed by wave 1 in parallel with wave 0's S^T k of step m).
 // Same canonical tree, so the same bits as the deep and single-step kernels.
+// Serves the gated calls and kd = 64; ungated kd = 128 calls on few tiles
+// take the split geometry below.
 template <int KD, bool GATED>
 __global__ __launch_bounds__(Geo<KD>::LANES) void recur_widem_kernel(RecurArgs a) {
   using G = Geo<KD>;
