@@ -218,17 +218,18 @@ def test_step_m_bit_exact_and_parity(orc, dims, M):
     assert_close(host(S), S_h, "S step_m")
 
 
-@pytest.mark.parametrize("dims,N", [(synth.DIMS128, 24), (synth.DIMS64, 11)])
+@pytest.mark.parametrize("dims,N", [(synth.DIMS128, 24), (synth.DIMS64, 11), (synth.DIMS128, 8)])
 @pytest.mark.parametrize("M", [2, 8])
 def test_m_step_geometries_agree(dims, N, M):
-    """Launches of fewer than 1024 tiles with M <= 8 run the wide geometry step
-    after step, larger ones the deep geometry: a launch over N units (>= 1024
-    tiles) against launches over slices of 1 and 3 units, bit for bit, for
-    step_m, the gated step, verify_m_gated (no state store) and commit with
-    per-unit counts (including 0 and M)."""
+    """Launches of fewer than 1024 tiles, M <= 8 and tiles x M <= 2048 run the
+    few-tile kernels (split when ungated at kd = 128, else the wide geometry
+    step after step), the others the deep geometry: a launch over N units
+    against launches over slices of 1 and 3 units, bit for bit, for step_m,
+    the gated step, verify_m_gated (no state store) and commit with per-unit
+    counts (including 0 and M).  N = 24 and 11 are deep at both M; N = 8 (384
+    tiles) is deep at M = 8 and few-tile at M = 2."""
     say(f"M-step geometries dims={dims} N={N} M={M}")
     vh, vd = dims[0], dims[3]
-    assert N * vh >= 1024
     gen = synth.make_gen(41 + M, "cuda")
     S0 = synth.state(gen, N, dims, device="cuda")
     inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
