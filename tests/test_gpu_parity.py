@@ -489,7 +489,7 @@ def test_frontend_nan_stays_in_its_sequence(orc, dims, B):
                                       (synth.DIMS128, 2, 1), (synth.DIMS128, 1, 8),
                                       (synth.DIMS64, 1, 3), (synth.DIMS128, 1, 12),
                                       (synth.DIMS128, 3, 3), (synth.DIMS128, 9, 3),
-                                      (synth.DIMS64, 10, 2)])
+                                      (synth.DIMS64, 10, 2), (synth.DIMS128, 4, 2)])
 def test_frontend_m_bit_exact_and_parity(orc, dims, B, M):
     """M draft rows in one call == M single-row GPU calls (bit for bit), and
     the oracle's M-row front end within tolerance (history bit for bit).  The
