@@ -218,6 +218,36 @@ def test_step_m_bit_exact_and_parity(orc, dims, M):
     assert_close(host(S), S_h, "S step_m")
 
 
+def test_single_step_geometries_agree_at_the_tile_boundary():
+    """Single steps of fewer than 1024 tiles run the split geometry (ungated),
+    larger ones the wide geometry: 22 units (1056 tiles) against their first
+    21 units (1008 tiles) and a single unit, bit for bit, ungated and gated."""
+    say("single-step geometries at 1024 tiles")
+    dims = synth.DIMS128
+    vh, vd = dims[0], dims[3]
+    N = 22
+    gen = synth.make_gen(61, "cuda")
+    S0 = synth.state(gen, N, dims, device="cuda")
+    inp = row0(synth.step_inputs(gen, N, dims, device="cuda"))
+    z = torch.randn((1, N, vh, vd), generator=gen, device="cuda")
+    w = 1.0 + 0.1 * torch.randn((vd,), generator=gen, device="cuda")
+
+    def run(n):
+        S = S0[:n].clone()
+        o = host(gdn.step(S, *(inp[k][:n].contiguous() for k in NAMES)))
+        Sg = S0[:n].clone()
+        og = host(gdn.step_gated(Sg, *(inp[k][:n].contiguous().unsqueeze(0) for k in NAMES),
+                                 z[:, :n].contiguous(), w, 1e-6))
+        return o, host(S), og, host(Sg)
+
+    full = run(N)
+    for n in (N - 1, 1):
+        part = run(n)
+        for a, b in zip(full, part):
+            sl = np.ascontiguousarray(a[:, :n] if a.ndim == 4 and a.shape[0] == 1 else a[:n])
+            assert bits_equal(sl, b), n
+
+
 @pytest.mark.parametrize("dims,N", [(synth.DIMS128, 24), (synth.DIMS64, 11), (synth.DIMS128, 8)])
 @pytest.mark.parametrize("M", [2, 8])
 def test_m_step_geometries_agree(dims, N, M):
