@@ -4,8 +4,9 @@
  * TEST INFRASTRUCTURE ONLY (see gdn_oracle.h).  Build with
  *   gcc -std=c99 -O2 -ffp-contract=off -fno-fast-math
  * so that every fp32 multiply and add is rounded on its own and no reduction
- * is re-associated or vectorised.  The loops follow the order in which the
- * operator is stated: decay, key read-out, delta, rank-1 update, query
+ * is re-associated (the compiler may still process independent columns side
+ * by side, which changes no rounding).  The passes follow the order in which
+ * the operator is stated: decay, key read-out, delta, rank-1 update, query
  * read-out with the updated state.
  */
 #include "gdn_oracle.h"
@@ -21,52 +22,64 @@ static int dims_ok(int64_t n, int vh, int kh, int kd, int vd)
 }
 
 /*
- * One value head of one unit.  "Kestrel_VLLM #24", section 4 (delta
- * recurrence kernel; one column dv of the state at a time) and Fig. 1 caption
- * (alpha scale -> S.k -> (v - .) beta -> rank-1 add -> S.q with the updated
- * state).  Per column dv:
- *   pass 1 over dk: t = S[dk][dv] * alpha; S[dk][dv] = t; kv = kv + t * k[dk]
- *   tmp = (v[dv] - kv) * beta
- *   pass 2 over dk: t = S[dk][dv] + k[dk] * tmp; S[dk][dv] = t; oa = oa + t * q[dk]
- *   o[dv] = oa
- * Columns are independent; the folds over dk are strict left folds.
+ * The operator on one (unit, value head) tile, stated as whole-tile passes
+ * ("Kestrel_VLLM #24", Fig. 1 caption, step 5: alpha scale, then S.k, then
+ * (v - .) beta, then the rank-1 add, then S.q on the updated state; section 4
+ * fixes the tile layout st[r][c], r over kd, c over vd):
+ *   1. st      <- decay * st                       (every element)
+ *   2. kread   <- st^T kvec                        (decayed tile)
+ *   3. delta   <- (vvec - kread) * b
+ *   4. st      <- st + kvec delta^T                (rank-1 update)
+ *   5. out     <- st^T qvec                        (updated tile)
+ * Each read-out element is a strict left fold over r = 0..kd-1, and every
+ * multiply and add is rounded to fp32 on its own.  out may be NULL (no
+ * read-out wanted).
  */
-static void step_head(float *Sh, const float *qh, const float *kh_,
-                      const float *vrow, float alpha, float bt, float *orow,
-                      int kd, int vd)
+static void tile_update(float *st, const float *qvec, const float *kvec,
+                        const float *vvec, float decay, float b, float *out,
+                        int kd, int vd)
 {
-    for (int dv = 0; dv < vd; dv++) {
-        float kv = 0.0f;
-        for (int dk = 0; dk < kd; dk++) {
-            float t = Sh[(size_t)dk * vd + dv] * alpha;
-            Sh[(size_t)dk * vd + dv] = t;
-            kv = kv + t * kh_[dk];
-        }
-        float tmp = (vrow[dv] - kv) * bt;
-        float oa = 0.0f;
-        for (int dk = 0; dk < kd; dk++) {
-            float t = Sh[(size_t)dk * vd + dv] + kh_[dk] * tmp;
-            Sh[(size_t)dk * vd + dv] = t;
-            oa = oa + t * qh[dk];
-        }
-        if (orow)
-            orow[dv] = oa;
-    }
+    float kread[vd], delta[vd];
+
+    for (int r = 0; r < kd; r++)
+        for (int c = 0; c < vd; c++)
+            st[(size_t)r * vd + c] = st[(size_t)r * vd + c] * decay;
+
+    for (int c = 0; c < vd; c++)
+        kread[c] = 0.0f;
+    for (int r = 0; r < kd; r++)
+        for (int c = 0; c < vd; c++)
+            kread[c] = kread[c] + st[(size_t)r * vd + c] * kvec[r];
+
+    for (int c = 0; c < vd; c++)
+        delta[c] = (vvec[c] - kread[c]) * b;
+
+    for (int r = 0; r < kd; r++)
+        for (int c = 0; c < vd; c++)
+            st[(size_t)r * vd + c] = st[(size_t)r * vd + c] + kvec[r] * delta[c];
+
+    if (!out)
+        return;
+    for (int c = 0; c < vd; c++)
+        out[c] = 0.0f;
+    for (int r = 0; r < kd; r++)
+        for (int c = 0; c < vd; c++)
+            out[c] = out[c] + st[(size_t)r * vd + c] * qvec[r];
 }
 
-/* One unit, one step.  Value head i uses key head i / (vh/kh) ("Kestrel_VLLM
- * #24", section 4: rep = vh/kh, key head = vi/rep). */
-static void step_unit(float *Su, const float *qu, const float *ku,
-                      const float *vu, const float *gu, const float *bu,
-                      float *ou, int vh, int kh, int kd, int vd)
+/* One unit: every value head i of the unit, with its key head
+ * i / (vh / kh) ("Kestrel_VLLM #24", section 4: three value heads share each
+ * key head, value head i taking key head i / rep). */
+static void unit_update(float *Su, const float *qu, const float *ku,
+                        const float *vu, const float *gu, const float *bu,
+                        float *ou, int vh, int kh, int kd, int vd)
 {
-    const int rep = vh / kh;
+    const int group = vh / kh;
     for (int i = 0; i < vh; i++) {
-        const int hh = i / rep;
-        const float alpha = expf(gu[i]);
-        step_head(Su + (size_t)i * kd * vd, qu + (size_t)hh * kd,
-                  ku + (size_t)hh * kd, vu + (size_t)i * vd, alpha, bu[i],
-                  ou ? ou + (size_t)i * vd : NULL, kd, vd);
+        const int key = i / group;
+        tile_update(Su + (size_t)i * kd * vd, qu + (size_t)key * kd,
+                    ku + (size_t)key * kd, vu + (size_t)i * vd, expf(gu[i]), bu[i],
+                    ou ? ou + (size_t)i * vd : NULL, kd, vd);
     }
 }
 
@@ -81,10 +94,10 @@ int ref_gdn_step(float *S, const float *q, const float *k, const float *v,
     if (!S || !q || !k || !v || !g || !beta || !o)
         return -1;
     for (int64_t u = 0; u < n_units; u++)
-        step_unit(S + (size_t)u * vh * kd * vd, q + (size_t)u * kh * kd,
-                  k + (size_t)u * kh * kd, v + (size_t)u * vh * vd,
-                  g + (size_t)u * vh, beta + (size_t)u * vh,
-                  o + (size_t)u * vh * vd, vh, kh, kd, vd);
+        unit_update(S + (size_t)u * vh * kd * vd, q + (size_t)u * kh * kd,
+                    k + (size_t)u * kh * kd, v + (size_t)u * vh * vd,
+                    g + (size_t)u * vh, beta + (size_t)u * vh,
+                    o + (size_t)u * vh * vd, vh, kh, kd, vd);
     return 0;
 }
 
@@ -112,18 +125,17 @@ int ref_gdn_step_m(float *S, const float *q, const float *k, const float *v,
     return 0;
 }
 
-/* "Kestrel_VLLM #24", section 3 (conv kernel): the history keeps the raw conv
- * INPUT frames, oldest first; after use it shifts by one and the newest slot
- * receives the current raw frame. */
+/* The conv history is a queue of the last ck - 1 raw conv INPUT frames,
+ * oldest first ("Kestrel_VLLM #24", section 3): a new frame enters at the
+ * back and the oldest leaves at the front. */
 void ref_conv_push(float *hist, const float *raw, int conv_dim, int ck)
 {
-    const int nprev = ck - 1;
-    for (int j = 0; j + 1 < nprev; j++)
-        memcpy(hist + (size_t)j * conv_dim, hist + (size_t)(j + 1) * conv_dim,
-               (size_t)conv_dim * sizeof(float));
-    if (nprev > 0)
-        memcpy(hist + (size_t)(nprev - 1) * conv_dim, raw,
-               (size_t)conv_dim * sizeof(float));
+    const int frames = ck - 1;
+    if (frames < 1)
+        return;
+    const size_t fb = (size_t)conv_dim * sizeof(float);
+    memmove(hist, hist + conv_dim, (size_t)(frames - 1) * fb);
+    memcpy(hist + (size_t)(frames - 1) * conv_dim, raw, fb);
 }
 
 /* "Kestrel_VLLM #34", section 3.7: mark is a plain copy of S and the conv
@@ -177,32 +189,37 @@ int ref_gdn_rollback(ref_slab *slab, float *S, float *hist,
     if (with_hist)
         memcpy(hist, slab->hist_snap, (size_t)N * slab->hist_floats * sizeof(float));
 
-    const size_t nqk = (size_t)N * kh * kd, nv = (size_t)N * vh * vd, ng = (size_t)N * vh;
+    /* row m of an input laid out [M][N][w] starts at (m * N + u) * w for unit u */
     for (int64_t u = 0; u < N; u++) {
         for (int m = 0; m < accepted[u]; m++) {
-            step_unit(S + (size_t)u * per_s, q + m * nqk + (size_t)u * kh * kd,
-                      k + m * nqk + (size_t)u * kh * kd,
-                      v + m * nv + (size_t)u * vh * vd, g + m * ng + (size_t)u * vh,
-                      beta + m * ng + (size_t)u * vh, NULL, vh, kh, kd, vd);
+            const size_t row = (size_t)m * N + (size_t)u;
+            unit_update(S + (size_t)u * per_s, q + row * kh * kd, k + row * kh * kd,
+                        v + row * vh * vd, g + row * vh, beta + row * vh, NULL,
+                        vh, kh, kd, vd);
             if (with_hist)
                 ref_conv_push(hist + (size_t)u * slab->hist_floats,
-                              xc_raw + ((size_t)m * N + (size_t)u) * conv_dim,
-                              conv_dim, ck);
+                              xc_raw + row * conv_dim, conv_dim, ck);
         }
     }
     slab->armed = 0;
     return 0;
 }
 
-/* softplus with the two overflow guards of "Kestrel_VLLM #24", section 3
- * (beta/g kernel): identity above 20, exp below -20, log1p(exp) between. */
-static float softplus_guarded(float xa)
+/* The log-domain gate from the a projection ("Kestrel_VLLM #24", section 3
+ * and Fig. 1 caption): g = -exp(A_log) * softplus(a + dt_bias), with
+ * softplus(z) = log(1 + e^z) taken as z itself for z > 20 and as e^z for
+ * z < -20, where the dropped term lies below fp32 resolution. */
+static float log_gate(float a, float A_log, float dt_bias)
 {
-    if (xa > 20.0f)
-        return xa;
-    if (xa < -20.0f)
-        return expf(xa);
-    return log1pf(expf(xa));
+    const float z = a + dt_bias;
+    float softplus;
+    if (z > 20.0f)
+        softplus = z;
+    else if (z < -20.0f)
+        softplus = expf(z);
+    else
+        softplus = log1pf(expf(z));
+    return -expf(A_log) * softplus;
 }
 
 int ref_gdn_frontend(const float *x, const float *Wa, const float *Wb,
@@ -222,7 +239,6 @@ int ref_gdn_frontend(const float *x, const float *Wa, const float *Wb,
         !q || !k || !v || !g || !beta || (ck > 1 && !hist))
         return -1;
 
-    const int nprev = ck - 1;
     const int qk_w = kh * kd;
     float *out = (float *)malloc((size_t)conv_dim * sizeof(float)); /* one row's conv output */
     if (!out)
@@ -242,9 +258,7 @@ int ref_gdn_frontend(const float *x, const float *Wa, const float *Wb,
             /* (ii) gate and beta ("Kestrel_VLLM #24", section 3 and Fig. 1
              * caption): the gate comes from a, in the log domain and
              * negative; beta comes from b. */
-            const float xa = acc_a + dt_bias[r];
-            const float sp = softplus_guarded(xa);
-            g[(size_t)b * vh + r] = -expf(A_log[r]) * sp;
+            g[(size_t)b * vh + r] = log_gate(acc_a, A_log[r], dt_bias[r]);
             beta[(size_t)b * vh + r] = 1.0f / (1.0f + expf(-acc_b));
         }
 
@@ -252,18 +266,19 @@ int ref_gdn_frontend(const float *x, const float *Wa, const float *Wb,
          * #24", section 3): taps 0..ck-2 over the history frames (oldest
          * first), the last tap over the current raw input; then the history
          * advances by the raw input; then silu(acc) = acc / (1 + exp(-acc)). */
-        const float *raw = xc_raw + (size_t)b * conv_dim;
-        float *hb = hist ? hist + (size_t)b * nprev * conv_dim : NULL;
+        const float *frames[ck];                 /* the window, oldest first */
+        float *queue = hist ? hist + (size_t)b * (ck - 1) * conv_dim : NULL;
+        for (int j = 0; j + 1 < ck; j++)
+            frames[j] = queue + (size_t)j * conv_dim;
+        frames[ck - 1] = xc_raw + (size_t)b * conv_dim;
         for (int ch = 0; ch < conv_dim; ch++) {
-            const float *cw = conv_w + (size_t)ch * ck;
-            float acc = 0.0f;
-            for (int j = 0; j < nprev; j++)
-                acc = acc + cw[j] * hb[(size_t)j * conv_dim + ch];
-            acc = acc + cw[nprev] * raw[ch];
-            out[ch] = acc / (1.0f + expf(-acc));
+            float y = 0.0f;
+            for (int j = 0; j < ck; j++)
+                y = y + conv_w[(size_t)ch * ck + j] * frames[j][ch];
+            out[ch] = y / (1.0f + expf(-y));
         }
-        if (hb)
-            ref_conv_push(hb, raw, conv_dim, ck);
+        if (queue)
+            ref_conv_push(queue, frames[ck - 1], conv_dim, ck);
 
         /* (iv) split into q | k | v ("Kestrel_VLLM #34", section 3.6: the
          * step receives the conv output at offsets 0, kh*kd, 2*kh*kd). */
@@ -434,7 +449,7 @@ int ref_gdn_proj_q4(const float *x, const uint8_t *q, const uint16_t *scale, flo
  * Double-precision brute force, re-associated: S' = alpha (I - beta k k^T) S
  * + beta k v^T and o = S'^T q, with the kd x kd matrix P = alpha (I - beta k
  * k^T) formed explicitly and multiplied into S.  Algebraically equal to the
- * column-wise form of step_head: S'^T k-term expands as alpha S - alpha beta
+ * whole-tile passes of tile_update: S'^T k-term expands as alpha S - alpha beta
  * k (k^T S) + beta k v^T.
  */
 int ref64_gdn_step(double *S, const double *q, const double *k,

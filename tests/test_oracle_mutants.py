@@ -16,21 +16,23 @@ import oracle
 from tests import test_oracle_pins as pins
 
 MUTANTS = [
-    ("delta sign", "float tmp = (vrow[dv] - kv) * bt;", "float tmp = (vrow[dv] + kv) * bt;"),
-    ("beta dropped", "float tmp = (vrow[dv] - kv) * bt;", "float tmp = (vrow[dv] - kv);"),
-    ("decay dropped", "float t = Sh[(size_t)dk * vd + dv] * alpha;",
-     "float t = Sh[(size_t)dk * vd + dv];"),
-    ("key read-out before decay", "kv = kv + t * kh_[dk];",
-     "kv = kv + Sh[(size_t)dk * vd + dv] * kh_[dk] / (alpha + 1e-30f) * (alpha != 0.0f);"),
-    ("output from the old state", "oa = oa + t * qh[dk];",
-     "oa = oa + (t - kh_[dk] * tmp) * qh[dk];"),
-    ("output reads k instead of q", "oa = oa + t * qh[dk];", "oa = oa + t * kh_[dk];"),
-    ("rank-1 update uses q", "float t = Sh[(size_t)dk * vd + dv] + kh_[dk] * tmp;",
-     "float t = Sh[(size_t)dk * vd + dv] + qh[dk] * tmp;"),
-    ("head mapping modulo", "const int hh = i / rep;\n        const float alpha = expf(gu[i]);",
-     "const int hh = i % kh;\n        const float alpha = expf(gu[i]);"),
-    ("transposed state index", "Sh[(size_t)dk * vd + dv]", "Sh[(size_t)dv * kd + dk]"),
-    ("gate not exponentiated", "const float alpha = expf(gu[i]);", "const float alpha = gu[i];"),
+    ("delta sign", "delta[c] = (vvec[c] - kread[c]) * b;", "delta[c] = (vvec[c] + kread[c]) * b;"),
+    ("beta dropped", "delta[c] = (vvec[c] - kread[c]) * b;", "delta[c] = (vvec[c] - kread[c]);"),
+    ("decay dropped", "st[(size_t)r * vd + c] = st[(size_t)r * vd + c] * decay;",
+     "st[(size_t)r * vd + c] = st[(size_t)r * vd + c] * 1.0f;"),
+    ("key read-out before decay",
+     "kread[c] = kread[c] + st[(size_t)r * vd + c] * kvec[r];",
+     "kread[c] = kread[c] + st[(size_t)r * vd + c] / (decay + 1e-30f) * (decay != 0.0f) * kvec[r];"),
+    ("output from the old state", "out[c] = out[c] + st[(size_t)r * vd + c] * qvec[r];",
+     "out[c] = out[c] + (st[(size_t)r * vd + c] - kvec[r] * delta[c]) * qvec[r];"),
+    ("output reads k instead of q", "out[c] = out[c] + st[(size_t)r * vd + c] * qvec[r];",
+     "out[c] = out[c] + st[(size_t)r * vd + c] * kvec[r];"),
+    ("rank-1 update uses q",
+     "st[(size_t)r * vd + c] = st[(size_t)r * vd + c] + kvec[r] * delta[c];",
+     "st[(size_t)r * vd + c] = st[(size_t)r * vd + c] + qvec[r] * delta[c];"),
+    ("head mapping modulo", "const int key = i / group;", "const int key = i % kh;"),
+    ("transposed state index", "st[(size_t)r * vd + c]", "st[(size_t)c * kd + r]"),
+    ("gate not exponentiated", "expf(gu[i]), bu[i]", "gu[i], bu[i]"),
     ("unit offset of g", "g + (size_t)u * vh, beta + (size_t)u * vh,",
      "g, beta + (size_t)u * vh,"),
     ("step_m row stride", "g + m * ng, beta + m * ng", "g, beta + m * ng"),
@@ -38,24 +40,23 @@ MUTANTS = [
     ("rollback replays one step short", "for (int m = 0; m < accepted[u]; m++) {",
      "for (int m = 0; m + 1 < accepted[u]; m++) {"),
     ("rollback stays armed", "slab->armed = 0;", ""),
-    ("history newest slot", "memcpy(hist + (size_t)(nprev - 1) * conv_dim, raw,",
-     "memcpy(hist, raw,"),
-    ("history not shifted", "for (int j = 0; j + 1 < nprev; j++)\n        memcpy",
-     "for (int j = 0; j + 1 < 0; j++)\n        memcpy"),
+    ("history newest slot", "memcpy(hist + (size_t)(frames - 1) * conv_dim, raw, fb);",
+     "memcpy(hist, raw, fb);"),
+    ("history not shifted", "memmove(hist, hist + conv_dim, (size_t)(frames - 1) * fb);", ""),
     ("beta from a", "beta[(size_t)b * vh + r] = 1.0f / (1.0f + expf(-acc_b));",
      "beta[(size_t)b * vh + r] = 1.0f / (1.0f + expf(-acc_a));"),
     ("beta sign", "1.0f / (1.0f + expf(-acc_b))", "1.0f / (1.0f + expf(acc_b))"),
-    ("gate sign", "g[(size_t)b * vh + r] = -expf(A_log[r]) * sp;",
-     "g[(size_t)b * vh + r] = expf(A_log[r]) * sp;"),
-    ("gate ignores A_log", "= -expf(A_log[r]) * sp;", "= -sp;"),
-    ("dt_bias dropped", "const float xa = acc_a + dt_bias[r];", "const float xa = acc_a;"),
-    ("low softplus branch", "return expf(xa);", "return 0.0f;"),
-    ("high softplus branch", "if (xa > 20.0f)\n        return xa;",
-     "if (xa > 20.0f)\n        return 20.0f;"),
-    ("conv taps reversed", "acc = acc + cw[j] * hb[(size_t)j * conv_dim + ch];",
-     "acc = acc + cw[nprev - 1 - j] * hb[(size_t)j * conv_dim + ch];"),
-    ("conv current tap dropped", "acc = acc + cw[nprev] * raw[ch];", ""),
-    ("silu dropped", "out[ch] = acc / (1.0f + expf(-acc));", "out[ch] = acc;"),
+    ("gate sign", "return -expf(A_log) * softplus;", "return expf(A_log) * softplus;"),
+    ("gate ignores A_log", "return -expf(A_log) * softplus;", "return -softplus;"),
+    ("dt_bias dropped", "const float z = a + dt_bias;", "const float z = a;"),
+    ("low softplus branch", "softplus = expf(z);", "softplus = 0.0f;"),
+    ("high softplus branch", "if (z > 20.0f)\n        softplus = z;",
+     "if (z > 20.0f)\n        softplus = 20.0f;"),
+    ("conv taps reversed", "y = y + conv_w[(size_t)ch * ck + j] * frames[j][ch];",
+     "y = y + conv_w[(size_t)ch * ck + (ck - 1 - j)] * frames[j][ch];"),
+    ("conv current tap dropped", "for (int j = 0; j < ck; j++)\n                y = y + conv_w",
+     "for (int j = 0; j + 1 < ck; j++)\n                y = y + conv_w"),
+    ("silu dropped", "out[ch] = y / (1.0f + expf(-y));", "out[ch] = y;"),
     ("split k offset", "memcpy(kb, out + qk_w,", "memcpy(kb, out,"),
     ("split v offset", "out + 2 * qk_w, (size_t)vh * vd", "out + qk_w, (size_t)vh * vd"),
     ("norm epsilon dropped", "1.0f / sqrtf(ssq + 1e-6f)", "1.0f / sqrtf(ssq)"),
