@@ -36,7 +36,7 @@ EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab
            "gdn_frontend_verify_m",
            "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy",
            "gdn_proj", "gdn_proj_pack", "gdn_verify_m_gated", "gdn_proj_q4_bytes",
-           "gdn_proj_q4_pack", "gdn_proj_q4")
+           "gdn_proj_q4_pack", "gdn_proj_q4", "gdn_stream_read", "gdn_stream_read_words")
 
 
 class GdnError(RuntimeError):
@@ -76,12 +76,15 @@ def lib():
     L.gdn_slab_init.argtypes = [C.POINTER(gdn_slab), P, I64, I64, I32, I32, I32, I32, I64]
     L.gdn_mark.argtypes = [C.POINTER(gdn_slab), P, P, P]
     L.gdn_mark_step_m.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I64, I32, I32, I32, I32, I32, P]
-    L.gdn_rollback.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I32, I32, P, P]
+    L.gdn_rollback.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I32, I32, I32, P, P]
     L.gdn_frontend.argtypes = [P] * 13 + [I32] * 8 + [P]
     L.gdn_frontend_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_stream_copy.argtypes = [P, P, I64, P]
+    L.gdn_stream_read.argtypes = [P, I64, P, P]
+    L.gdn_stream_read_words.argtypes = [I64]
+    L.gdn_stream_read_words.restype = I64
     L.gdn_verify_m.argtypes = [P] * 7 + [I64, I32, I32, I32, I32, I32, P]
-    L.gdn_commit.argtypes = [P] * 8 + [I32, I64, I32, I32, I32, I32, I32, P, P, P]
+    L.gdn_commit.argtypes = [P] * 8 + [I32, I32, I64, I32, I32, I32, I32, I32, P, P, P]
     L.gdn_frontend_verify_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_proj.argtypes = [P, I64, I32, P, I32, P, P, I32, P, P]
     L.gdn_proj_pack.argtypes = [P, P, I32, I32, P]
@@ -91,7 +94,8 @@ def lib():
     L.gdn_proj_q4_pack.argtypes = [P, P, P, I32, I32, P]
     L.gdn_proj_q4.argtypes = [P, I64, I32, P, I32, P, P, I32, P, P]
     for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark_step_m", "gdn_mark", "gdn_rollback",
-              "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_verify_m",
+              "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_stream_read",
+              "gdn_verify_m",
               "gdn_commit", "gdn_frontend_verify_m", "gdn_proj", "gdn_proj_pack",
               "gdn_verify_m_gated", "gdn_proj_q4_pack", "gdn_proj_q4"):
         getattr(L, f).restype = C.c_int
@@ -261,7 +265,7 @@ class Slab:
         _check(lib().gdn_rollback(C.byref(self.s), _sized(S, ns, "S"), self._hist(hist),
                                   *rows,
                                   _sized(xc_raw, M * self.s.n_units * conv_dim, "xc_raw"),
-                                  conv_dim, M, C.c_void_p(acc.data_ptr()), _stream(stream)),
+                                  conv_dim, 4, M, C.c_void_p(acc.data_ptr()), _stream(stream)),
                "gdn_rollback")
 
 
@@ -366,7 +370,7 @@ def commit(S, accepted, q, k, v, g, beta, hist=None, xc_raw=None, status=None, s
     conv_dim = xc_raw.shape[-1] if xc_raw is not None else 0
     _check(lib().gdn_commit(_dev(S, "S"), _sized(hist, N * 3 * conv_dim, "hist"),
                             *_rows(S, q, k, v, g, beta, M),
-                            _sized(xc_raw, M * N * conv_dim, "xc_raw"), conv_dim, N, M, vh, kh,
+                            _sized(xc_raw, M * N * conv_dim, "xc_raw"), conv_dim, 4, N, M, vh, kh,
                             kd, vd, _int32_dev(accepted, "accepted", N),
                             _int32_dev(status, "status", 1), _stream(stream)), "gdn_commit")
 
@@ -504,3 +508,19 @@ def stream_copy(dst, src, stream=None):
         raise ValueError("dst and src sizes differ")
     _check(lib().gdn_stream_copy(_dev(dst, "dst"), _dev(src, "src"), src.numel(),
                                  _stream(stream)), "gdn_stream_copy")
+
+
+def stream_read(src, words=None, stream=None):
+    """Read-only floor (gdn_stream_read): streams src and returns one uint32
+    word per 128 KiB chunk, the XOR of the chunk's 32-bit words (as an int32
+    tensor holding the same bits)."""
+    n = src.numel()
+    nw = int(lib().gdn_stream_read_words(max(n, 1)))
+    if words is None:
+        words = torch.empty(nw, dtype=torch.int32, device=src.device)
+    if words.dtype != torch.int32 or not words.is_contiguous() or words.numel() != nw \
+            or words.device.type != "cuda":
+        raise ValueError(f"words: need a contiguous int32 HIP tensor of {nw} elements")
+    _check(lib().gdn_stream_read(_dev(src, "src"), n, C.c_void_p(words.data_ptr()),
+                                 _stream(stream)), "gdn_stream_read")
+    return words

@@ -16,6 +16,7 @@ constexpr int32_t kMaxM = 64;
 constexpr int32_t kMaxHeads = 4096;
 constexpr int32_t kSlabMagic = 0x47444e53;  // "GDNS"
 constexpr int64_t kAlign = 256;
+constexpr int32_t kConvK = 4;       // conv kernel width the kernels are built for
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -232,7 +233,8 @@ int gdn_mark_step_m(gdn_slab *slab, float *S, const float *hist, const float *q,
 
 int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const float *k,
                  const float *v, const float *g, const float *beta, const float *xc_raw,
-                 int32_t conv_dim, int32_t M, const int32_t *accepted, void *stream) {
+                 int32_t conv_dim, int32_t ck, int32_t M, const int32_t *accepted,
+                 void *stream) {
   if (!slab_valid(slab)) return GDN_ESTATE;
   if (!(slab->armed & 1)) return GDN_ESTATE;
   if (hist != nullptr && !(slab->armed & 2)) return GDN_ESTATE;
@@ -255,8 +257,8 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const fl
         overlaps(S, ns * 4, g, gb) || overlaps(S, ns * 4, beta, gb))
       return GDN_EINVAL;
   }
-  const int ck = 4;
   if (hist != nullptr) {
+    if (ck != kConvK) return GDN_EUNSUPPORTED;
     if (!aligned16(hist) || conv_dim <= 0 || conv_dim % 4 != 0 ||
         (int64_t)(ck - 1) * conv_dim != slab->hist_floats)
       return GDN_EINVAL;
@@ -264,11 +266,12 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const fl
     if (any && !ptr_ok(xc_raw)) return GDN_EINVAL;
   }
   hipStream_t s = (hipStream_t)stream;
-  // accepted[] travels with the stream: the copy is ordered before the
-  // kernels that read it, and the host array is consumed before return.
+  // accepted[] reaches the slab's count area through kernel arguments, so the
+  // host array is consumed before return and the counts are ordered on the
+  // stream before the kernels that read them.
   int32_t *d_acc = slab_accepted(slab);
-  if (hipMemcpyAsync(d_acc, accepted, (size_t)N * 4, hipMemcpyHostToDevice, s) != hipSuccess)
-    return GDN_EDEVICE;
+  int rc0 = enq(gdn::launch_stage_counts(d_acc, accepted, N, s));
+  if (rc0) return rc0;
   // the history replay runs in the same launch as the state replay
   int rc = enq(gdn::launch_recur(kd, slab_S(slab), S, q, k, v, g, beta, nullptr, d_acc, N, vh, kh,
                                  M, s, nullptr, nullptr, 0.0f, nullptr, nullptr, hist,
@@ -287,7 +290,7 @@ int frontend_impl(const float *x, const float *Wa, const float *Wb, const float 
                   int32_t vd, bool write_hist, void *stream) {
   int rc = check_dims(vh, kh, kd, vd);
   if (rc) return rc;
-  if (ck != 4) return GDN_EUNSUPPORTED;
+  if (ck != kConvK) return GDN_EUNSUPPORTED;
   if (B < 0 || M < 1 || M > kMaxM || dim <= 0 || dim % 4 != 0 ||
       conv_dim != 2 * kh * kd + vh * vd)
     return GDN_EINVAL;
@@ -374,8 +377,8 @@ int gdn_verify_m_gated(const float *S, const float *q, const float *k, const flo
 
 int gdn_commit(float *S, float *hist, const float *q, const float *k, const float *v,
                const float *g, const float *beta, const float *xc_raw, int32_t conv_dim,
-               int64_t n_units, int32_t M, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
-               const int32_t *accepted, int32_t *status, void *stream) {
+               int32_t ck, int64_t n_units, int32_t M, int32_t vh, int32_t kh, int32_t kd,
+               int32_t vd, const int32_t *accepted, int32_t *status, void *stream) {
   if (M < 1 || M > kMaxM) return GDN_EINVAL;
   int rc = check_dims(vh, kh, kd, vd);
   if (rc) return rc;
@@ -396,8 +399,8 @@ int gdn_commit(float *S, float *hist, const float *q, const float *k, const floa
   for (int i = 0; i < 6; i++)
     if (overlaps(S, sb, ins[i], ib[i])) return GDN_EINVAL;
   if (status != nullptr && overlaps(S, sb, status, 4)) return GDN_EINVAL;
-  const int ck = 4;
-  const int64_t hb = n_units * (ck - 1) * (int64_t)conv_dim * 4;
+  if (hist != nullptr && ck != kConvK) return GDN_EUNSUPPORTED;
+  const int64_t hb = n_units * (kConvK - 1) * (int64_t)conv_dim * 4;
   if (hist != nullptr) {
     if (!aligned16(hist) || !ptr_ok(xc_raw) || conv_dim <= 0 || conv_dim % 4 != 0)
       return GDN_EINVAL;
@@ -418,6 +421,20 @@ int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream
   if (!ptr_ok(dst) || !ptr_ok(src)) return GDN_EINVAL;
   if (dst != src && overlaps(dst, n_floats * 4, src, n_floats * 4)) return GDN_EINVAL;
   return enq(gdn::launch_copy(dst, src, n_floats, (hipStream_t)stream));
+}
+
+int64_t gdn_stream_read_words(int64_t n_floats) {
+  if (n_floats < 1) return GDN_EINVAL;
+  return gdn::read_chunks(n_floats);
+}
+
+int gdn_stream_read(const float *src, int64_t n_floats, uint32_t *words, void *stream) {
+  if (n_floats < 0) return GDN_EINVAL;
+  if (n_floats == 0) return GDN_OK;
+  if (!ptr_ok(src) || words == nullptr || (reinterpret_cast<uintptr_t>(words) & 3u))
+    return GDN_EINVAL;
+  if (overlaps(src, n_floats * 4, words, gdn::read_chunks(n_floats) * 4)) return GDN_EINVAL;
+  return enq(gdn::launch_read(src, n_floats, words, (hipStream_t)stream));
 }
 
 // Projection size limits: a workgroup addresses its (at most 64) packed

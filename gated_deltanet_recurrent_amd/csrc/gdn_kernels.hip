@@ -934,20 +934,16 @@ __global__ __launch_bounds__(SPLIT_LANES) void recur_split_kernel(RecurArgs a) {
   }
 }
 
-// Launches of fewer than GDN_WIDEM_BELOW tiles with M <= MC rows per unit and
-// at most GDN_FEW_TILE_ROWS tile-rows (tiles x M) run the split geometry (kd =
+// Launches of fewer than kWidemBelow tiles with M <= MC rows per unit and
+// at most kFewTileRows tile-rows (tiles x M) run the split geometry (kd =
 // 128, ungated); otherwise single steps run the wide geometry, and M >= 2 rows
 // the wide one step after step (the same few-tile bound) or the deep
 // geometry.  The same bits whichever serves a call.  The bound is where the
 // deep kernel's throughput overtakes the few-tile kernels' latency (step_m at
 // M = 8: split 13.4 against 14.8 us at 192 tiles, 20.6 against 18.0 at 384;
 // at M = 2 split is ahead up to 1008 tiles).
-#ifndef GDN_WIDEM_BELOW
-#define GDN_WIDEM_BELOW 1024
-#endif
-#ifndef GDN_FEW_TILE_ROWS
-#define GDN_FEW_TILE_ROWS 2048
-#endif
+constexpr int64_t kWidemBelow = 1024;
+constexpr int64_t kFewTileRows = 2048;
 
 int recur_lanes(int kd) { return kd == 128 ? Geo<128>::LANES : Geo<64>::LANES; }
 
@@ -960,7 +956,7 @@ template <int KD, bool GATED>
 static void launch_recur_kd(RecurArgs a, int64_t tiles, hipStream_t s) {
   const dim3 grid((unsigned)tiles);
   a.tile_wgs = tiles;
-  const bool few = a.M <= MC && tiles < GDN_WIDEM_BELOW && tiles * a.M <= GDN_FEW_TILE_ROWS;
+  const bool few = a.M <= MC && tiles < kWidemBelow && tiles * a.M <= kFewTileRows;
   if (KD == 128 && !GATED && few) {
     a.tile_wgs = tiles * SPLIT_NS;
     const dim3 g2((unsigned)(a.tile_wgs + hist_wgs(a, SPLIT_LANES)));
@@ -1077,6 +1073,89 @@ int launch_copy(float *dst, const float *src, int64_t n, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Read-only floor: stream n floats with 128-bit non-temporal loads, 256 lanes
+// x 32 loads per workgroup (the shape that reads fastest), and write one
+// 32-bit word per 128 KiB chunk, the XOR of the chunk's words, so that the
+// loads cannot be dropped and the result can be checked.
+// ---------------------------------------------------------------------------
+
+constexpr int READ_LANES = 256;
+constexpr int READ_F4 = 32;
+constexpr int64_t READ_CHUNK4 = READ_LANES * READ_F4;   // float4 per chunk
+
+__global__ __launch_bounds__(READ_LANES) void read_kernel(const float *src, int64_t n4,
+                                                          int64_t n, uint32_t *words) {
+  __shared__ uint32_t s_x[READ_LANES / 64];
+  const int64_t c = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t first = c * READ_CHUNK4;
+  const int64_t cnt = n4 - first < READ_CHUNK4 ? n4 - first : READ_CHUNK4;
+  // loads past cnt are outside the buffer's bounds and return zeros
+  const rsrc_t rs = buf_rsrc(src + 4 * first, (int)(cnt > 0 ? cnt * 16 : 0));
+  f4 x[READ_F4];
+#pragma unroll
+  for (int u = 0; u < READ_F4; u++) x[u] = ld_stream(rs, threadIdx.x * 16, u * READ_LANES * 16);
+  uint32_t h = 0;
+#pragma unroll
+  for (int u = 0; u < READ_F4; u++)
+    h ^= __float_as_uint(x[u].x) ^ __float_as_uint(x[u].y) ^ __float_as_uint(x[u].z) ^
+         __float_as_uint(x[u].w);
+  // the last chunk also takes the 0..3 floats past the last whole float4
+  if (c == gridDim.x - 1 && threadIdx.x < n - 4 * n4) h ^= __float_as_uint(src[4 * n4 + threadIdx.x]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) h ^= (uint32_t)__shfl_xor((int)h, off);
+  if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = h;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < READ_LANES / 64; i++) w ^= s_x[i];
+    words[c] = w;
+  }
+}
+
+// chunk c holds floats [4 READ_CHUNK4 c, 4 READ_CHUNK4 (c + 1)); the last one
+// may hold no whole float4, only the 1..3 floats past the last one
+int64_t read_chunks(int64_t n) {
+  const int64_t c = (n + 4 * READ_CHUNK4 - 1) / (4 * READ_CHUNK4);
+  return c < 1 ? 1 : c;
+}
+
+int launch_read(const float *src, int64_t n, uint32_t *words, hipStream_t s) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)read_chunks(n)), dim3(READ_LANES), 0, s, src,
+                     n / 4, n, words);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-unit step counts from a host array, handed to the device by value: the
+// counts of up to COUNT_CHUNK units travel in one launch's kernel arguments,
+// which the runtime copies when the launch is enqueued, so the host array is
+// no longer read once the call returns (no host-memory copy is left pending).
+// ---------------------------------------------------------------------------
+
+constexpr int COUNT_CHUNK = 1024;
+struct CountChunk {
+  uint8_t c[COUNT_CHUNK];   // counts 0..64
+};
+
+__global__ __launch_bounds__(256) void count_stage_kernel(int32_t *dst, int n, CountChunk ch) {
+  for (int i = threadIdx.x; i < n; i += 256) dst[i] = ch.c[i];
+}
+
+int launch_stage_counts(int32_t *dst, const int32_t *host, int64_t n, hipStream_t s) {
+  for (int64_t base = 0; base < n; base += COUNT_CHUNK) {
+    const int len = (int)(n - base < COUNT_CHUNK ? n - base : COUNT_CHUNK);
+    CountChunk ch;
+    for (int i = 0; i < COUNT_CHUNK; i++) ch.c[i] = i < len ? (uint8_t)host[base + i] : 0;
+    hipLaunchKernelGGL(count_stage_kernel, dim3(1), dim3(256), 0, s, dst + base, len, ch);
+    const int rc = (int)hipGetLastError();
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
 // Conv-history rollback: pure data movement, bit-exact.
 // ---------------------------------------------------------------------------
 
@@ -1112,16 +1191,18 @@ int launch_hist_replay(float *hist, const float *src, const float *xc_raw,
 
 constexpr int FB = 8;   // batch rows per workgroup
 constexpr int FR = 4;   // stacked weight rows per workgroup
-#ifndef GDN_FE_LANES
-#define GDN_FE_LANES 512
-#endif
-constexpr int FE_LANES = GDN_FE_LANES;
+constexpr int FE_LANES = 512;
 constexpr int FE_WAVES = FE_LANES / 64;
 
-static __device__ __forceinline__ float softplus_guarded(float z) {
-  if (z > 20.0f) return z;
-  if (z < -20.0f) return expf(z);
-  return log1pf(expf(z));
+// The log-domain gate g = -exp(A_log) softplus(a + dt_bias) ("Kestrel_VLLM
+// #24", section 3).  softplus(z) = log(1 + e^z) is z itself to fp32 precision
+// above 20 and e^z below -20; one exp serves all three ranges (its argument
+// is capped at 20 by a compare, so a NaN z stays NaN).
+static __device__ __forceinline__ float log_gate(float a, float A_log, float dt_bias) {
+  const float z = a + dt_bias;
+  const float e = expf(z > 20.0f ? 20.0f : z);
+  const float sp = z > 20.0f ? z : z < -20.0f ? e : log1pf(e);
+  return -expf(A_log) * sp;
 }
 
 static __device__ __forceinline__ void fe_accumulate(float (&acc)[FB * FR], const f4 (&w)[FR],
@@ -1257,8 +1338,7 @@ static __device__ __forceinline__ void fe_gemv_block(int bx, int by, const float
     const int R = r0 + t % FR;
     if (b < B && R < 2 * vh) {
       if (R < vh) {
-        const float sp = softplus_guarded(sum + dt_bias[R]);
-        g[(int64_t)b * vh + R] = -expf(A_log[R]) * sp;
+        g[(int64_t)b * vh + R] = log_gate(sum, A_log[R], dt_bias[R]);
       } else {
         beta[(int64_t)b * vh + (R - vh)] = 1.0f / (1.0f + expf(-sum));
       }
@@ -1364,9 +1444,7 @@ constexpr int CONV_RCH = 256;   // channels per row-parallel workgroup
 // up to this many sequences (frontend_m at M = 8: 1 sequence 7.1 -> 4.6 us,
 // 8 sequences 9.3 -> 7.2; from 16 the window's single read of each frame
 // wins, 10.9 against 11.2 us, and 54 against 62 at 128)
-#ifndef GDN_CONV_ROWS_MAX_B
-#define GDN_CONV_ROWS_MAX_B 8
-#endif
+constexpr int kConvRowsMaxB = 8;
 
 template <int KD>
 static __device__ __forceinline__ void fe_conv_rows(int bx, int b, const float *xc_raw, float *hist,
@@ -1483,8 +1561,7 @@ static __device__ __forceinline__ void fe_gemv_row(int R, const float *x, const 
 #pragma unroll
     for (int w = 1; w < FE_WAVES; w++) sum = sum + s_w1[w];
     if (R < vh) {
-      const float sp = softplus_guarded(sum + dt_bias[R]);
-      g[R] = -expf(A_log[R]) * sp;
+      g[R] = log_gate(sum, A_log[R], dt_bias[R]);
     } else {
       beta[R - vh] = 1.0f / (1.0f + expf(-sum));
     }
@@ -1582,8 +1659,7 @@ static __device__ __forceinline__ void fe_gemv_col8(int bx, int R, const float *
     const int b = b0 + t;
     if (b < B) {
       if (R < vh) {
-        const float sp = softplus_guarded(sum + dt_bias[R]);
-        g[(int64_t)b * vh + R] = -expf(A_log[R]) * sp;
+        g[(int64_t)b * vh + R] = log_gate(sum, A_log[R], dt_bias[R]);
       } else {
         beta[(int64_t)b * vh + (R - vh)] = 1.0f / (1.0f + expf(-sum));
       }
@@ -1642,7 +1718,7 @@ __global__ __launch_bounds__(FE_LANES) void fe_kernel(FeArgs a) {
 
 int64_t frontend_workitems(int64_t B, int64_t M, int64_t conv_dim, int64_t vh) {
   const int64_t n_gemv = M * B <= FB ? 2 * vh : ((M * B + FB - 1) / FB) * ((2 * vh + FR - 1) / FR);
-  const int64_t n_conv = M >= 2 && B <= GDN_CONV_ROWS_MAX_B
+  const int64_t n_conv = M >= 2 && B <= kConvRowsMaxB
                              ? ((conv_dim + CONV_RCH - 1) / CONV_RCH) * B
                                 : ((conv_dim + 1023) / 1024) * ((B + CONV_ROWS - 1) / CONV_ROWS);
   return (n_gemv + n_conv) * FE_LANES;
@@ -1659,7 +1735,7 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
            B, M, dim, conv_dim, vh, kh, write_hist ? 1 : 0, 0, 0, 0, 0};
   a.gemv_bx = (M * B + FB - 1) / FB;
   a.n_gemv = M * B <= FB ? 2 * vh : a.gemv_bx * ((2 * vh + FR - 1) / FR);
-  const bool cr = M >= 2 && B <= GDN_CONV_ROWS_MAX_B;
+  const bool cr = M >= 2 && B <= kConvRowsMaxB;
   a.conv_bx = cr ? (conv_dim + CONV_RCH - 1) / CONV_RCH : (conv_dim + 1023) / 1024;
   a.n_conv = cr ? a.conv_bx * B : a.conv_bx * ((B + CONV_ROWS - 1) / CONV_ROWS);
   const dim3 grid((unsigned)(a.n_gemv + a.n_conv));
@@ -1721,18 +1797,10 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
 
 constexpr int PJ_SEG = 8;                 // segments of C, one wave each
 constexpr int PJ_LANES = 64 * PJ_SEG;
-#ifndef GDN_PJ_MIN_WG
-#define GDN_PJ_MIN_WG 128
-#endif
-#ifndef GDN_PJ_MIN_WG1
-#define GDN_PJ_MIN_WG1 256
-#endif
-#ifndef GDN_PJ_U2_ROWS
-#define GDN_PJ_U2_ROWS 8        // few rows: up to this many
-#endif
-#ifndef GDN_PJ_MIN_WG_FEW
-#define GDN_PJ_MIN_WG_FEW 1024
-#endif
+constexpr int64_t kPjMinWg = 128;
+constexpr int64_t kPjMinWg1 = 256;
+constexpr int64_t kPjU2Rows = 8;        // few rows: up to this many
+constexpr int64_t kPjMinWgFew = 1024;
 
 struct ProjProblem {
   const float *W;
@@ -1905,13 +1973,13 @@ __global__ __launch_bounds__(PJ_LANES) void proj_kernel(ProjArgs a) {
 
 // Tile shape of a call.  Up to 16 rows (one row block) the call streams the
 // weights: the widest output slab group (1, 2 or 4 slabs of 16) dividing
-// R / 16 that still leaves >= GDN_PJ_MIN_WG1 workgroups (GDN_PJ_MIN_WG_FEW up
+// R / 16 that still leaves >= kPjMinWg1 workgroups (kPjMinWgFew up
 // to 8 rows), to spread the stream over every CU: in_proj at 1 to 4 rows
 // takes 52 us with 1024 one-slab workgroups against 55 us with 256 four-slab
 // ones, but 66 against 54 us at 16 rows.  Beyond 16 rows it is bound by the matrix cores and by x
 // traffic: the widest slab group dividing R / 16 (each x load then serves
 // more outputs), then the most row blocks per tile (up to the rows present)
-// that still leave >= GDN_PJ_MIN_WG workgroups.  Measured at 64 rows:
+// that still leave >= kPjMinWg workgroups.  Measured at 64 rows:
 // out_proj (R = 5120) 2 row blocks x 4 slabs 70 us, 4 x 2 96 us, 4 x 4
 // 128 us; in_proj 4 x 4 128 us.  The choice never changes a result
 // (canonical summation above).
@@ -1927,7 +1995,7 @@ static int64_t proj_tiles(int64_t rows, int R0, int R1, int rb, int oj) {
 static ProjShape proj_shape(int64_t rows, int R0, int R1) {
   ProjShape sh;
   const int rb_max = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
-  const int64_t min_wg1 = rows <= GDN_PJ_U2_ROWS ? GDN_PJ_MIN_WG_FEW : GDN_PJ_MIN_WG1;
+  const int64_t min_wg1 = rows <= kPjU2Rows ? kPjMinWgFew : kPjMinWg1;
   sh.oj = 1;
   for (int oj = 4; oj > 1; oj >>= 1) {
     const bool divides = (R0 / 16) % oj == 0 && (R1 / 16) % oj == 0;
@@ -1937,7 +2005,7 @@ static ProjShape proj_shape(int64_t rows, int R0, int R1) {
     }
   }
   sh.rb = rb_max;
-  while (sh.rb > 1 && proj_tiles(rows, R0, R1, sh.rb, sh.oj) < GDN_PJ_MIN_WG) sh.rb >>= 1;
+  while (sh.rb > 1 && proj_tiles(rows, R0, R1, sh.rb, sh.oj) < kPjMinWg) sh.rb >>= 1;
   sh.row_groups = (int)((rows + 16 * sh.rb - 1) / (16 * sh.rb));
   return sh;
 }
@@ -1991,16 +2059,16 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
   const bool stream = sh.row_groups == 1;
   switch (sh.rb * 8 + sh.oj) {
     // one row block: up to 8 rows, 2 blocks per trip unless the grid has
-    // >= GDN_PJ_MIN_WG_FEW workgroups (out_proj at one row 28.7 -> 24.4 us;
+    // >= kPjMinWgFew workgroups (out_proj at one row 28.7 -> 24.4 us;
     // in_proj keeps 4), 4 beyond; the MFMA order is the same either way
     case 1 * 8 + 1:
-      if (rows <= GDN_PJ_U2_ROWS && a.p[0].blocks + a.p[1].blocks < GDN_PJ_MIN_WG_FEW)
+      if (rows <= kPjU2Rows && a.p[0].blocks + a.p[1].blocks < kPjMinWgFew)
         launch_proj_t<1, 1, 2>(a, true, s);
       else
         launch_proj_t<1, 1, 4>(a, true, s);
       break;
     case 1 * 8 + 2:
-      if (rows <= GDN_PJ_U2_ROWS && a.p[0].blocks + a.p[1].blocks < GDN_PJ_MIN_WG_FEW)
+      if (rows <= kPjU2Rows && a.p[0].blocks + a.p[1].blocks < kPjMinWgFew)
         launch_proj_t<1, 2, 2>(a, true, s);
       else
         launch_proj_t<1, 2, 4>(a, true, s);
@@ -2058,9 +2126,7 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 // binary16 scales of the block at 1024 + 2 l.
 
 // launches with fewer 64-output groups than this take two workgroups per group
-#ifndef GDN_Q4_SPLIT_BELOW
-#define GDN_Q4_SPLIT_BELOW 256
-#endif
+constexpr int64_t kQ4SplitBelow = 256;
 constexpr int Q4_SEGS = 16;                    // waves per workgroup
 constexpr int Q4_LANES = 64 * Q4_SEGS;
 constexpr int Q4_BLOCK_BYTES = 1152;
@@ -2294,7 +2360,7 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   // two workgroups per group when one per group would leave CUs idle (both
   // shapes give the same bits)
   const int groups = R0 / 64 + (Wq1 ? R1 / 64 : 0);
-  const bool split = groups < GDN_Q4_SPLIT_BELOW;
+  const bool split = groups < kQ4SplitBelow;
   const int f = split ? 2 : 1;
   Q4Args a{};
   a.x = x;

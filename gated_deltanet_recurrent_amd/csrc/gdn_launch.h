@@ -34,6 +34,15 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
 // 128-bit streaming copy of n floats (src == dst allowed).
 int launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
 
+// Read-only stream of n floats; words[c] = XOR of the 32-bit words of chunk
+// c (read_chunks(n) chunks of 128 KiB, the last one ragged).
+int64_t read_chunks(int64_t n);
+int launch_read(const float *src, int64_t n, uint32_t *words, hipStream_t s);
+
+// dst[u] = host[u] for u < n (each 0..255), through kernel arguments: the host
+// array is not read after the call returns.
+int launch_stage_counts(int32_t *dst, const int32_t *host, int64_t n, hipStream_t s);
+
 // Conv-history replay (ck = 4): hist[u] = last 3 frames of
 // [src[u] frames..., xc_raw[0][u], ..., xc_raw[a-1][u]], a = accepted[u];
 // src may be hist itself.  a outside 0..M: the unit gets a = 0 and *status

@@ -20,9 +20,13 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
  *    call validates its arguments on the host, enqueues its kernels on the
  *    stream and returns without synchronising, except where noted.
- *  - Return: GDN_OK (0) once enqueued, or a negative error code; on an error
- *    nothing has been enqueued.  Shapes the kernels were not built for are
- *    refused, never served by a slower fallback.
+ *  - Return: GDN_OK (0) once enqueued, or a negative error code.  On a
+ *    refusal (GDN_EINVAL, GDN_EUNSUPPORTED, GDN_ESTATE) nothing has been
+ *    enqueued and nothing has changed; GDN_EDEVICE reports a runtime failure,
+ *    possibly after part of the call's work was enqueued.  Shapes the kernels
+ *    were not built for are refused, never served by a slower fallback
+ *    ("Kestrel_VLLM #34", section 3.5: a path that was not validated is
+ *    refused rather than taken silently).
  *  - Layouts (row-major; N = n_units; M = draft rows, 1 for a single step):
  *      S        [N][vh][kd][vd]   dv fastest
  *      q, k     [M][N][kh][kd]
@@ -105,18 +109,33 @@ typedef struct gdn_slab {
     int32_t magic;        /* set by gdn_slab_init */
 } gdn_slab;
 
-/* Device bytes a slab needs, or a negative error code for bad arguments. */
+/* Device bytes a slab for n_units units needs: the state snapshot, the
+ * conv-history snapshot (hist_floats_per_unit floats per unit, 0 for none,
+ * a multiple of 4) and the per-unit count area, each 256-byte aligned.  The
+ * caller sizes the slab for the largest call it will make, not the current
+ * one ("Kestrel_VLLM #34", section 3.5: the draft-row buffer is allocated for
+ * the maximum row count), and queries the size before allocating
+ * ("Kestrel_VLLM #24", section 10: a size query before the copy, a refusal
+ * rather than a truncation).  Returns the byte count, or GDN_EINVAL /
+ * GDN_EUNSUPPORTED for bad dims, n_units < 1 or a bad hist size. */
 int64_t gdn_slab_bytes(int64_t n_units, int32_t vh, int32_t kh, int32_t kd,
                        int32_t vd, int64_t hist_floats_per_unit);
 
 /* Bind a slab to caller device memory `dev` (256-byte aligned) of `bytes`
- * bytes.  Host only; leaves the slab disarmed. */
+ * bytes ("Kestrel_VLLM #34", section 3.7: the snapshot of the state and of
+ * the conv history).  Host only, enqueues nothing; leaves the slab disarmed.
+ * Errors: GDN_EINVAL for a null slab or dev, a misaligned dev or bad sizes;
+ * GDN_ESTATE when bytes < gdn_slab_bytes(...). */
 int gdn_slab_init(gdn_slab *slab, void *dev, int64_t bytes, int64_t n_units,
                   int32_t vh, int32_t kh, int32_t kd, int32_t vd,
                   int64_t hist_floats_per_unit);
 
-/* Copy S (and hist [N][hist_floats] unless NULL) into the slab and arm it.
- * Re-marking an armed slab overwrites the snapshot. */
+/* Copy S (and hist [N][hist_floats] unless NULL) into the slab and arm it
+ * ("Kestrel_VLLM #34", section 3.7: the recurrent state and the conv history
+ * cannot be recomputed backwards, so a copy is taken before the draft rows
+ * run).  Re-marking an armed slab overwrites the snapshot.  Errors:
+ * GDN_ESTATE for an uninitialised slab or a hist on a slab without a history
+ * area; GDN_EINVAL for a bad pointer or S / hist overlapping the slab. */
 int gdn_mark(gdn_slab *slab, const float *S, const float *hist, void *stream);
 
 /*
@@ -125,7 +144,12 @@ int gdn_mark(gdn_slab *slab, const float *S, const float *hist, void *stream);
  * then advanced.  Same results, bit for bit, as the two calls; arms the slab
  * like gdn_mark.  n_units and the dims must equal the slab's (else
  * GDN_ESTATE).  ("Kestrel_VLLM #34", section 3.7: mark before the M-row
- * verify.)
+ * verify.)  hist is copied as it stands at this call, so it must still be
+ * the history the draft rows were computed from: pair this call with
+ * gdn_frontend_verify_m, which leaves the history as it was.  After
+ * gdn_frontend_m the history already holds the draft rows' frames, and a
+ * rollback would push the accepted frames a second time (mark with gdn_mark
+ * before gdn_frontend_m instead).
  */
 int gdn_mark_step_m(gdn_slab *slab, float *S, const float *hist, const float *q,
                     const float *k, const float *v, const float *g,
@@ -136,19 +160,24 @@ int gdn_mark_step_m(gdn_slab *slab, float *S, const float *hist, const float *q,
  * Roll back to an accepted length: for every unit u, S (and hist, unless
  * NULL) become the marked bytes advanced by accepted[u] single steps that use
  * rows 0..accepted[u]-1 of the inputs given to gdn_step_m (q, k, v, g, beta,
- * [M][N][...]); no o is written.  The history replays the raw conv input
- * frames xc_raw [M][N][conv_dim] (needed only with hist; conv_dim*(ck-1) must
- * equal the slab's hist_floats and ck = 4).  accepted is a HOST array of N
- * int32 in 0..M; it is copied before the call returns.  accepted[u] == 0
- * restores the marked bytes exactly; accepted[u] == M reproduces gdn_step_m
- * bit for bit.  The slab is disarmed afterwards (one-shot): a rollback on a
- * disarmed slab, or with hist when the history was not marked, returns
- * GDN_ESTATE and changes nothing.
+ * [M][N][...]); no o is written ("Kestrel_VLLM #34", section 3.7: restore the
+ * snapshot, then re-run the accepted rows; the snapshot is one-shot).  The
+ * history replays the raw conv input frames xc_raw [M][N][conv_dim] (needed
+ * only with hist): ck is the conv kernel width, which must be 4 (else
+ * GDN_EUNSUPPORTED), and conv_dim * (ck - 1) must equal the slab's
+ * hist_floats (else GDN_EINVAL); both are ignored when hist is NULL.
+ * accepted is a HOST array of N int32 in 0..M (else GDN_EINVAL).  The counts
+ * reach the device inside the arguments of the call's launches, so the array
+ * is no longer read once the call returns, whatever memory holds it.
+ * accepted[u] == 0 restores the marked bytes exactly; accepted[u] == M
+ * reproduces gdn_step_m bit for bit.  The slab is disarmed afterwards: a
+ * rollback on a disarmed slab, or with hist when the history was not marked,
+ * returns GDN_ESTATE and changes nothing.
  */
 int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q,
                  const float *k, const float *v, const float *g,
                  const float *beta, const float *xc_raw, int32_t conv_dim,
-                 int32_t M, const int32_t *accepted, void *stream);
+                 int32_t ck, int32_t M, const int32_t *accepted, void *stream);
 
 /*
  * Speculative verify without a snapshot.  The M draft rows are evaluated
@@ -184,17 +213,20 @@ int gdn_verify_m_gated(const float *S, const float *q, const float *k,
 /*
  * gdn_commit: advance every unit u by accepted[u] single steps using rows
  * 0..accepted[u]-1 of the inputs given to gdn_verify_m, in place; with hist
- * (nullable) the conv history [N][3][conv_dim] receives the raw conv input
- * frames xc_raw [M][N][conv_dim] of those rows.  accepted is a DEVICE array
+ * (nullable) the conv history [N][ck-1][conv_dim] receives the raw conv input
+ * frames xc_raw [M][N][conv_dim] of those rows (ck must be 4, else
+ * GDN_EUNSUPPORTED; ignored when hist is NULL).  accepted is a DEVICE array
  * of N int32, read by the kernels (so the whole cycle can be captured into a
  * graph).  An entry outside 0..M leaves that unit's state and history
  * unchanged and sets *status = 1 (status: device int32, nullable; never
  * cleared by the library).  Units with accepted[u] == 0 are not touched.
+ * ("Kestrel_VLLM #34", section 3.7: after verification only the accepted
+ * prefix may remain applied to the state and the history.)
  */
 int gdn_commit(float *S, float *hist, const float *q, const float *k,
                const float *v, const float *g, const float *beta,
-               const float *xc_raw, int32_t conv_dim, int64_t n_units, int32_t M,
-               int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+               const float *xc_raw, int32_t conv_dim, int32_t ck, int64_t n_units,
+               int32_t M, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
                const int32_t *accepted, int32_t *status, void *stream);
 
 /*
@@ -261,6 +293,19 @@ int gdn_frontend_verify_m(const float *x, const float *Wa, const float *Wb,
  * write back in place).  Used by gdn_mark for its copy.
  */
 int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream);
+
+/*
+ * Measurement aid: the read-only floor ("Kestrel_VLLM #27", section 3.2: a
+ * read-only floor and a read+write floor bracket what a state stream can
+ * reach).  Streams n_floats floats of src with 128-bit non-temporal loads and
+ * writes words[c] = the XOR of the 32-bit words of floats
+ * [32768 c, min(32768 (c + 1), n_floats)) for c < gdn_stream_read_words(n),
+ * so that no load can be dropped and the result is checkable.  src, words:
+ * device memory (src 16-byte, words 4-byte aligned, not overlapping).
+ * n_floats == 0 is a no-op.  Errors: GDN_EINVAL.
+ */
+int64_t gdn_stream_read_words(int64_t n_floats);   /* < 0: n_floats < 1 */
+int gdn_stream_read(const float *src, int64_t n_floats, uint32_t *words, void *stream);
 
 /*
  * Weight packing for gdn_proj: copies a row-major weight matrix W [R][C] into

@@ -120,26 +120,32 @@ def test_rollback_refusals_need_no_device():
     acc = (C.c_int32 * 2)(0, 1)
     args = [fp(1 << 32), NULLS] + [fp((i + 2) << 32) for i in range(5)] + [NULLS]
     # never marked: one-shot state error
-    assert L.gdn_rollback(C.byref(s), *args, 10240, 4, acc, NULLS) == gdn.GDN_ESTATE
+    assert L.gdn_rollback(C.byref(s), *args, 10240, 4, 4, acc, NULLS) == gdn.GDN_ESTATE
     # an uninitialised slab
     bad = gdn.gdn_slab()
-    assert L.gdn_rollback(C.byref(bad), *args, 10240, 4, acc, NULLS) == gdn.GDN_ESTATE
+    assert L.gdn_rollback(C.byref(bad), *args, 10240, 4, 4, acc, NULLS) == gdn.GDN_ESTATE
     assert L.gdn_mark(C.byref(bad), fp(1 << 32), NULLS, NULLS) == gdn.GDN_ESTATE
     # armed state only (history not marked): a history rollback is refused
     s.armed = 1
     args_h = list(args)
     args_h[1] = fp(9 << 32)
-    assert L.gdn_rollback(C.byref(s), *args_h, 10240, 4, acc, NULLS) == gdn.GDN_ESTATE
+    assert L.gdn_rollback(C.byref(s), *args_h, 10240, 4, 4, acc, NULLS) == gdn.GDN_ESTATE
     # accepted out of range / M out of range
     acc_bad = (C.c_int32 * 2)(0, 5)
-    assert L.gdn_rollback(C.byref(s), *args, 10240, 4, acc_bad, NULLS) == gdn.GDN_EINVAL
-    assert L.gdn_rollback(C.byref(s), *args, 10240, 0, acc, NULLS) == gdn.GDN_EINVAL
-    assert L.gdn_rollback(C.byref(s), *args, 10240, 65, acc, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_rollback(C.byref(s), *args, 10240, 4, 4, acc_bad, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_rollback(C.byref(s), *args, 10240, 4, 0, acc, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_rollback(C.byref(s), *args, 10240, 4, 65, acc, NULLS) == gdn.GDN_EINVAL
     # S inside the slab
     args_s = list(args)
     args_s[0] = fp(4096)
-    assert L.gdn_rollback(C.byref(s), *args_s, 10240, 4, acc, NULLS) == gdn.GDN_EINVAL
-    assert s.armed == 1        # refusals leave the slab as it was
+    assert L.gdn_rollback(C.byref(s), *args_s, 10240, 4, 4, acc, NULLS) == gdn.GDN_EINVAL
+    # the conv kernel width: only ck = 4 is built; ignored without a history
+    s.armed = 3
+    assert L.gdn_rollback(C.byref(s), *args_h, 10240, 3, 4, acc, NULLS) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_rollback(C.byref(s), *args_h, 10240, 5, 4, acc, NULLS) == gdn.GDN_EUNSUPPORTED
+    # history size disagreeing with the slab's (conv_dim * (ck - 1))
+    assert L.gdn_rollback(C.byref(s), *args_h, 10236, 4, 4, acc, NULLS) == gdn.GDN_EINVAL
+    assert s.armed == 3        # refusals leave the slab as it was
 
 
 def test_mark_step_m_refusals_need_no_device():
@@ -168,16 +174,18 @@ def test_verify_commit_refusals_need_no_device():
     assert L.gdn_verify_m(S, q, k, v, g, beta, fp((2 << 32) + 4096), 4, 2, vh, kh, kd, vd,
                           NULLS) == gdn.GDN_EINVAL                   # o inside S
     acc = fp(20 << 32)
-    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 2, vh, kh, kd, vd, NULLS, NULLS,
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 4, 2, vh, kh, kd, vd, NULLS, NULLS,
                         NULLS) == gdn.GDN_EINVAL                       # no accepted array
-    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 2, vh, kh, kd, vd,
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 4, 2, vh, kh, kd, vd,
                         fp((20 << 32) + 2), NULLS, NULLS) == gdn.GDN_EINVAL   # misaligned
-    assert L.gdn_commit(S, hist, q, k, v, g, beta, NULLS, 10240, 4, 2, vh, kh, kd, vd, acc, NULLS,
+    assert L.gdn_commit(S, hist, q, k, v, g, beta, NULLS, 10240, 4, 4, 2, vh, kh, kd, vd, acc, NULLS,
                         NULLS) == gdn.GDN_EINVAL                       # history without raws
-    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 65, vh, kh, kd, vd, acc, NULLS,
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 4, 65, vh, kh, kd, vd, acc, NULLS,
                         NULLS) == gdn.GDN_EINVAL
-    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 0, 2, vh, kh, kd, vd, acc, NULLS,
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 0, 2, vh, kh, kd, vd, acc, NULLS,
                         NULLS) == gdn.GDN_OK                           # nothing to do
+    assert L.gdn_commit(S, hist, q, k, v, g, beta, xc, 10240, 3, 4, 2, vh, kh, kd, vd, acc, NULLS,
+                        NULLS) == gdn.GDN_EUNSUPPORTED                 # conv width 3 not built
     z, w = fp(30 << 32), fp(31 << 32)
     eps = C.c_float(1e-6)
     assert L.gdn_verify_m_gated(S, q, k, v, g, beta, z, w, eps, o, 4, 0, vh, kh, kd, vd,
@@ -204,6 +212,20 @@ def test_frontend_validation():
     p2 = list(ptrs)
     p2[9] = p2[8]                                   # k aliases q
     assert L.gdn_frontend(*p2, 4, 5120, cd, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+
+
+def test_stream_read_validation():
+    L = gdn.lib()
+    assert L.gdn_stream_read_words(0) < 0
+    assert L.gdn_stream_read_words(1) == 1
+    assert L.gdn_stream_read_words(32768) == 1
+    assert L.gdn_stream_read_words(32769) == 2
+    assert L.gdn_stream_read(fp(0), 100, fp(64), NULLS) == gdn.GDN_EINVAL    # words inside src
+    assert L.gdn_stream_read(fp(0), 100, fp((1 << 20) + 2),
+                             NULLS) == gdn.GDN_EINVAL                        # misaligned words
+    assert L.gdn_stream_read(fp(8), 100, fp(1 << 20), NULLS) == gdn.GDN_EINVAL  # src not 16-aligned
+    assert L.gdn_stream_read(fp(0), -1, fp(1 << 20), NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_stream_read(fp(0), 0, fp(1 << 20), NULLS) == gdn.GDN_OK
 
 
 def test_stream_copy_validation():
