@@ -3,9 +3,8 @@
 Floating point: per element |x - r| <= max(1e-5 |r|, 1e-6) on o, S and the
 front-end outputs.  Bit-exact: step_m against M single steps, rollback against
 single steps from the mark, rollback(0) against the marked bytes, the reset
-gate's closed form, the conv history, repeated runs.  Large workloads are
-checked on sampled units that the oracle recomputes one by one, in the same
-launch configuration the benchmark times (one launch over all units).
+gate's closed form, the conv history, repeated runs.  The full-size
+workloads are checked on every unit in test_gpu_full_size.py.
 """
 import ctypes as C
 
@@ -59,6 +58,37 @@ def ref_steps(orc, S, inp, dims, rows):
         orc.gdn_step(S, x["q"], x["k"], x["v"], x["g"], x["beta"], o, dims)
         outs.append(o)
     return outs
+
+
+def ref_cycle(orc, S0, inp, dims, acc, hist0=None, xc=None):
+    """Oracle of one speculative cycle on host copies: mark(S, hist), M
+    steps (o for every row), rollback(accepted) replaying the history frames.
+    Returns (o [M][N][vh][vd], S after the M steps, S after the rollback,
+    history after the rollback or None)."""
+    vh, kh, kd, vd = dims
+    M, N = inp["q"].shape[:2]
+    S = np.ascontiguousarray(S0).copy()
+    h = None if hist0 is None else np.ascontiguousarray(hist0).copy()
+    cd = 0 if xc is None else xc.shape[-1]
+    rs = orc.slab(N, dims, hist_floats=3 * cd)
+    rs.mark(S, h)
+    o = np.zeros((M, N, vh, vd), np.float32)
+    orc.gdn_step_m(S, *(inp[n] for n in NAMES), o, M, dims)
+    S_m = S.copy()
+    rs.rollback(S, h, inp, M, np.asarray(acc, np.int32), xc_raw=xc, conv_dim=cd, ck=4)
+    return o, S_m, S, h
+
+
+def ref_gated(orc, o_ref, z, w, eps):
+    """The oracle's gated RMSNorm of o_ref and the gated output's per-element
+    absolute floor: o's floor (1e-6) carried through the per-head scale
+    s = w silu(z) / sqrt(mean(o^2) + eps)."""
+    out = np.zeros_like(o_ref)
+    orc.gated_norm(o_ref, z, w, eps, out)
+    o64, z64 = o_ref.astype(np.float64), z.astype(np.float64)
+    rinv = 1.0 / np.sqrt(np.mean(o64 ** 2, axis=-1, keepdims=True) + eps)
+    scale = np.abs(rinv * w.astype(np.float64) * z64 / (1.0 + np.exp(-z64)))
+    return out, 1e-6 * scale
 
 
 # ---------------------------------------------------------------------------
@@ -121,10 +151,17 @@ def test_reset_gate_bit_exact_vs_oracle(orc):
         inp["g"].fill_(float("-inf"))
         S_h = host(S)
         x = {n: host(inp[n]) for n in NAMES}
-        gdn.step(S, *(inp[n] for n in NAMES))
+        o = gdn.step(S, *(inp[n] for n in NAMES))
         o_ref = np.zeros((N, dims[0], dims[3]), np.float32)
         orc.gdn_step(S_h, x["q"], x["k"], x["v"], x["g"], x["beta"], o_ref, dims)
         assert bits_equal(host(S), S_h)
+        # and the read-out: o = tmp (k . q) with tmp = v beta, per value head
+        assert_close(host(o), o_ref, "o reset gate")
+        rep = dims[0] // dims[1]
+        kq = np.einsum("nhd,nhd->nh", x["k"].astype(np.float64), x["q"].astype(np.float64))
+        o_closed = (x["v"].astype(np.float64) * x["beta"].astype(np.float64)[..., None]
+                    * np.repeat(kq, rep, axis=1)[..., None])
+        assert_close(host(o), o_closed, "o reset gate closed form")
 
 
 @pytest.mark.parametrize("dims,N,M", [(synth.DIMS128, 3, 1), (synth.DIMS64, 3, 1),
@@ -250,7 +287,7 @@ def test_single_step_geometries_agree_at_the_tile_boundary():
 
 @pytest.mark.parametrize("dims,N", [(synth.DIMS128, 24), (synth.DIMS64, 11), (synth.DIMS128, 8)])
 @pytest.mark.parametrize("M", [2, 8])
-def test_m_step_geometries_agree(dims, N, M):
+def test_m_step_geometries_agree(orc, dims, N, M):
     """Launches of fewer than 1024 tiles, M <= 8 and tiles x M <= 2048 run the
     few-tile kernels (split when ungated at kd = 128, else the wide geometry
     step after step), the others the deep geometry: a launch over N units
@@ -285,6 +322,18 @@ def test_m_step_geometries_agree(dims, N, M):
         for i, (a, b) in enumerate(zip(full, part)):
             sl = (slice(None), slice(lo, hi)) if a.ndim == 4 and i % 2 == 0 else slice(lo, hi)
             assert bits_equal(np.ascontiguousarray(a[sl]), b), (lo, hi, i)
+    # the full launch against the oracle: step_m, gated outputs, and the
+    # verify + commit cycle's state (= mark, M steps, rollback to the counts)
+    o, S, og, Sg, ov, Sv = full
+    x_h = {n: host(inp[n]) for n in NAMES}
+    o_ref, S_m, S_rb, _ = ref_cycle(orc, host(S0), x_h, dims, host(acc))
+    assert_close(o, o_ref, "o step_m")
+    assert_close(S, S_m, "S step_m")
+    assert bits_equal(Sg, S)
+    g_ref, g_floor = ref_gated(orc, o_ref, host(z), host(w), 1e-6)
+    assert_close(og, g_ref, "gated out", floor=g_floor)
+    assert_close(ov, g_ref, "verify_m_gated out", floor=g_floor)
+    assert_close(Sv, S_rb, "S after commit")
 
 
 @pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
@@ -343,7 +392,7 @@ def test_mark_rollback_bit_exact(orc, dims):
 
 
 @pytest.mark.parametrize("dims,M", [(synth.DIMS128, 8), (synth.DIMS64, 12), (synth.DIMS128, 1)])
-def test_mark_step_m_fused(dims, M):
+def test_mark_step_m_fused(orc, dims, M):
     """gdn_mark_step_m == gdn_mark + gdn_step_m: same state, outputs and
     snapshot bits (rollback(0) restores the marked bytes), history marked."""
     say(f"mark_step_m dims={dims} M={M}")
@@ -363,6 +412,10 @@ def test_mark_step_m_fused(dims, M):
     slab2.mark(S2, hist)
     o2 = gdn.step_m(S2, *(inp[n] for n in NAMES))
     assert bits_equal(host(S), host(S2)) and bits_equal(host(o), host(o2))
+    o_ref, S_m, _, _ = ref_cycle(orc, host(S_mark), {n: host(inp[n]) for n in NAMES}, dims,
+                                 [0] * N)
+    assert_close(host(o), o_ref, "o mark_step_m")
+    assert_close(host(S), S_m, "S mark_step_m")
     hist_mark = host(hist)
     hist.add_(1.0)
     slab.rollback(S, [0] * N, *(inp[n] for n in NAMES), hist=hist,
@@ -374,6 +427,45 @@ def test_mark_step_m_fused(dims, M):
     small = gdn.Slab(N - 1, dims)
     with pytest.raises((gdn.GdnError, ValueError)):
         small.mark_step_m(S, *(inp[n] for n in NAMES))
+
+
+@pytest.mark.parametrize("dims,B,M", [(synth.DIMS128, 4, 5), (synth.DIMS64, 3, 8),
+                                      (synth.DIMS128, 2, 1)])
+def test_mark_step_m_with_history_after_frontend_verify(orc, dims, B, M):
+    """The fused mark's history protocol: frontend_verify_m (the history is
+    only read), mark_step_m(S, hist), rollback(S, hist) to per-unit accepted
+    lengths; outputs, state and history against the oracle's chain (mark,
+    frontend_m, step_m, rollback), the history bit for bit."""
+    say(f"mark_step_m with history dims={dims} B={B} M={M}")
+    vh, kh, kd, vd = dims
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(19, "cuda")
+    S = synth.state(gen, B, dims, device="cuda")
+    w = synth.frontend_weights(gen, dims, dim=1024, device="cuda")
+    fe = synth.frontend_inputs(gen, B, dims, T=M, dim=1024, device="cuda")
+    hist = fe["hist"]
+    S_h, hist_h = host(S), host(hist)
+    acc = [(2 * b + 1) % (M + 1) for b in range(B)]
+    rows = gdn.frontend_verify_m(fe["x"], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"],
+                                 fe["xc_raw"], hist, w["conv_w"], dims)
+    assert bits_equal(host(hist), hist_h)
+    slab = gdn.Slab(B, dims, hist_floats_per_unit=3 * cd)
+    o = slab.mark_step_m(S, *(rows[n] for n in NAMES), hist=hist)
+    slab.rollback(S, acc, *(rows[n] for n in NAMES), hist=hist, xc_raw=fe["xc_raw"])
+    wh = {n: host(t) for n, t in w.items()}
+    ref = dict(q=np.zeros((M, B, kh, kd), np.float32), k=np.zeros((M, B, kh, kd), np.float32),
+               v=np.zeros((M, B, vh, vd), np.float32), g=np.zeros((M, B, vh), np.float32),
+               beta=np.zeros((M, B, vh), np.float32))
+    h_fe = hist_h.copy()
+    orc.gdn_frontend_m(host(fe["x"]), wh["Wa"], wh["Wb"], wh["A_log"], wh["dt_bias"],
+                       host(fe["xc_raw"]), h_fe, wh["conv_w"], ref["q"], ref["k"], ref["v"],
+                       ref["g"], ref["beta"], dims)
+    for n in NAMES:
+        assert_close(host(rows[n]), ref[n], f"frontend_verify_m {n}")
+    o_ref, _, S_rb, h_rb = ref_cycle(orc, S_h, ref, dims, acc, hist_h, host(fe["xc_raw"]))
+    assert_close(host(o), o_ref, "o")
+    assert_close(host(S), S_rb, "S after rollback")
+    assert bits_equal(host(hist), h_rb)
 
 
 @pytest.mark.parametrize("dims,M", [(synth.DIMS64, 12), (synth.DIMS128, 10)])
@@ -640,7 +732,7 @@ def test_step_gated_parity(orc, dims, M):
 
 @pytest.mark.parametrize("dims,M", [(synth.DIMS128, 1), (synth.DIMS128, 5), (synth.DIMS128, 10),
                                     (synth.DIMS64, 1), (synth.DIMS64, 6)])
-def test_verify_m_gated_equals_step_gated(dims, M):
+def test_verify_m_gated_equals_step_gated(orc, dims, M):
     """gdn_verify_m_gated gives the outputs of gdn_step_gated bit for bit
     (single-step, M-step and prefetching instances) and leaves S untouched."""
     say(f"verify_m_gated dims={dims} M={M}")
@@ -656,10 +748,14 @@ def test_verify_m_gated_equals_step_gated(dims, M):
     assert bits_equal(host(S), S0)
     out_s = gdn.step_gated(S.clone(), *(inp[n] for n in NAMES), z, w, 1e-6)
     assert bits_equal(host(out_v), host(out_s))
+    o_ref = np.zeros((M, N, vh, vd), np.float32)
+    orc.gdn_step_m(S0.copy(), *(host(inp[n]) for n in NAMES), o_ref, M, dims)
+    g_ref, g_floor = ref_gated(orc, o_ref, host(z), host(w), 1e-6)
+    assert_close(host(out_v), g_ref, "verify_m_gated out", floor=g_floor)
 
 
 @pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
-def test_verify_commit_equals_snapshot_protocol(dims):
+def test_verify_commit_equals_snapshot_protocol(orc, dims):
     """verify_m + commit(accepted) gives the same outputs, state and conv
     history, bit for bit, as mark + step_m + rollback(accepted); verify_m
     leaves the state untouched."""
@@ -691,6 +787,12 @@ def test_verify_commit_equals_snapshot_protocol(dims):
     assert bits_equal(host(S_a), host(S_b))
     assert bits_equal(host(h_a), host(h_b))
     assert int(status.item()) == 0
+    # both protocols against the oracle's mark, M steps, rollback
+    o_ref, _, S_rb, h_rb = ref_cycle(orc, host(S), {n: host(inp[n]) for n in NAMES}, dims, acc,
+                                     host(hist), host(xc))
+    assert_close(host(o_b), o_ref, "o verify_m")
+    assert_close(host(S_b), S_rb, "S after commit")
+    assert bits_equal(host(h_b), h_rb)
 
 
 @pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
@@ -725,7 +827,7 @@ def test_single_row_commit_and_rollback_with_history(dims):
     assert bits_equal(host(S_r), host(S_want)) and bits_equal(host(h_r), host(h_want))
 
 
-def test_commit_refuses_out_of_range_counts():
+def test_commit_refuses_out_of_range_counts(orc):
     """Device-supplied counts outside 0..M leave that unit unchanged and raise
     the status flag; the other units are committed normally."""
     dims = synth.DIMS128
@@ -750,9 +852,15 @@ def test_commit_refuses_out_of_range_counts():
         assert bits_equal(host(S[u:u + 1]), host(Su)), u
         seq = np.concatenate([host(h0[u]), host(xc[:a, u])], axis=0)
         assert bits_equal(host(hist[u]), seq[-3:]), u
+    # the oracle refuses such counts outright; the units it can take (the
+    # in-range ones, refused ones as accepted = 0) give the same result
+    _, _, S_rb, h_rb = ref_cycle(orc, host(S0), {n: host(inp[n]) for n in NAMES}, dims,
+                                 [1, 0, 0, 2], host(h0), host(xc))
+    assert_close(host(S), S_rb, "S after commit")
+    assert bits_equal(host(hist), h_rb)
 
 
-def test_verify_cycle_graph_replay():
+def test_verify_cycle_graph_replay(orc):
     """One layer's speculative cycle without a snapshot -- front end for the M
     draft rows (history read only), verify, commit with device-side accepted
     lengths -- captured as a graph and replayed three times against eager
@@ -794,6 +902,20 @@ def test_verify_cycle_graph_replay():
     o_s = gdn.step_m(S_s, *(rows_s[n] for n in NAMES))
     slab.rollback(S_s, host(acc), *(rows_s[n] for n in NAMES), hist=h_s, xc_raw=fe["xc_raw"])
     assert bits_equal(host(S_s), S_e) and bits_equal(host(h_s), h_e) and bits_equal(host(o_s), o_e)
+    # the cycle against the oracle's chain: mark, frontend_m, step_m, rollback
+    wh = {n: host(t) for n, t in w.items()}
+    ref = dict(q=np.zeros((M, B, kh, kd), np.float32), k=np.zeros((M, B, kh, kd), np.float32),
+               v=np.zeros((M, B, vh, vd), np.float32), g=np.zeros((M, B, vh), np.float32),
+               beta=np.zeros((M, B, vh), np.float32))
+    h_fe = host(h0)
+    orc.gdn_frontend_m(host(fe["x"]), wh["Wa"], wh["Wb"], wh["A_log"], wh["dt_bias"],
+                       host(fe["xc_raw"]), h_fe, wh["conv_w"], ref["q"], ref["k"], ref["v"],
+                       ref["g"], ref["beta"], dims)
+    o_ref, _, S_rb, h_rb = ref_cycle(orc, host(S0), ref, dims, host(acc), host(h0),
+                                     host(fe["xc_raw"]))
+    assert_close(o_e, o_ref, "o verify cycle")
+    assert_close(S_e, S_rb, "S verify cycle")
+    assert bits_equal(h_e, h_rb)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -819,7 +941,7 @@ def test_verify_cycle_graph_replay():
     del graph
 
 
-def test_graph_replay_matches_eager():
+def test_graph_replay_matches_eager(orc):
     """A captured chain of 8 single steps (the per-token launch chain) replays
     bit-identically to eager execution, several times, with eager work and
     synchronisations between the replays.  The captured path records kernel
@@ -833,6 +955,11 @@ def test_graph_replay_matches_eager():
     S_e = S0.clone()
     o_e = [gdn.step(S_e, *(x[n] for n in NAMES)) for x in rows]
     torch.cuda.synchronize()
+    S_ref = host(S0)
+    o_ref = ref_steps(orc, S_ref, {n: host(inp[n]) for n in NAMES}, dims, T)
+    for m in range(T):
+        assert_close(host(o_e[m]), o_ref[m], f"o step {m}")
+    assert_close(host(S_e), S_ref, "S after the chain")
     S_g = S0.clone()
     outs = [torch.empty((N, dims[0], dims[3]), device="cuda") for _ in range(T)]
     side = torch.cuda.Stream()
@@ -873,6 +1000,20 @@ def test_zero_sized_calls_are_no_ops():
     torch.cuda.synchronize()
 
 
+def test_stream_read_words():
+    """The read-only floor's chunk checksums equal the XOR of each 128 KiB
+    chunk's words, for sizes with a ragged last chunk and a 1..3-float tail."""
+    for n in (1, 3, 4, 32768, 32769, 32768 * 5 + 7, 1000003):
+        src = torch.randn(n, device="cuda")
+        words = gdn.stream_read(src)
+        x = host(src).view(np.uint32)
+        nc = (n + 32767) // 32768
+        want = np.array([np.bitwise_xor.reduce(x[32768 * c:32768 * (c + 1)]) for c in range(nc)],
+                        np.uint32)
+        assert words.numel() == nc, n
+        assert bits_equal(host(words).view(np.uint32), want), n
+
+
 def test_stream_copy_ragged():
     for n in (1, 3, 4, 1000003, 4 * 256 * 4 * 3 + 5):
         src = torch.randn(n, device="cuda")
@@ -881,123 +1022,6 @@ def test_stream_copy_ragged():
         assert bits_equal(host(dst), host(src)), n
         gdn.stream_copy(src, src)                  # in place: read and write back
         assert bits_equal(host(dst), host(src)), n
-
-
-# ---------------------------------------------------------------------------
-# full-size workloads, one launch over all units, sampled units recomputed
-# ---------------------------------------------------------------------------
-
-def _sample(N, rng, k=10):
-    idx = sorted(set([0, 1, N // 2, N - 2, N - 1] + list(rng.choice(N, k, replace=False))))
-    return idx
-
-
-@pytest.mark.parametrize("wl", [1, 4, 5])
-def test_full_size_step_sampled(orc, wl):
-    cfg = synth.WORKLOADS[wl]
-    dims = cfg["dims"]
-    N = cfg["seqs"] * cfg["layers"]
-    say(f"full-size step: {cfg['name']} units={N} dims={dims}")
-    gen = synth.make_gen(cfg["seed"], "cuda")
-    S = synth.state(gen, N, dims, device="cuda")
-    inp = synth.step_inputs(gen, N, dims, M=2, gate=cfg["gate"], device="cuda")
-    idx = _sample(N, np.random.default_rng(wl))
-    ii = torch.as_tensor(idx, device="cuda")
-    S_h = host(S.index_select(0, ii))
-    x_h = host_rows(inp, idx)
-    for m in range(2):
-        o = gdn.step(S, *(inp[n][m] for n in NAMES))
-        torch.cuda.synchronize()
-        assert torch.isfinite(o).all()
-        o_ref = ref_steps(orc, S_h, {n: x_h[n][m:m + 1] for n in NAMES}, dims, 1)[0]
-        assert_close(host(o.index_select(0, ii)), o_ref, f"o step {m}")
-        assert_close(host(S.index_select(0, ii)), S_h, f"S step {m}")
-    del S, inp
-
-
-def test_full_size_verify_cycle_sampled(orc):
-    """Speculative verify at full size: mark, step_m (M=8), rollback with an
-    accepted length per sequence shared by its 48 layers."""
-    cfg = synth.WORKLOADS[2]
-    dims = cfg["dims"]
-    L = cfg["layers"]
-    N = cfg["seqs"] * L
-    M = cfg["M"]
-    say(f"full-size verify: {cfg['name']} units={N}")
-    gen = synth.make_gen(cfg["seed"], "cuda")
-    S = synth.state(gen, N, dims, device="cuda")
-    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
-    rng = np.random.default_rng(2)
-    a_seq = rng.integers(0, M + 1, cfg["seqs"])
-    acc = np.repeat(a_seq, L).astype(np.int32)     # unit = seq * layers + layer
-    idx = _sample(N, rng)
-    ii = torch.as_tensor(idx, device="cuda")
-    S_mark_h = host(S.index_select(0, ii))
-    slab = gdn.Slab(N, dims)
-    slab.mark(S)
-    o_m = gdn.step_m(S, *(inp[n] for n in NAMES))
-    S_m_h = host(S.index_select(0, ii))
-    o_m_h = host(o_m.index_select(1, ii))
-    slab.rollback(S, acc, *(inp[n] for n in NAMES))
-    torch.cuda.synchronize()
-    x_h = host_rows(inp, idx)
-    S_ref = S_mark_h.copy()
-    o_ref = np.zeros((M, len(idx), dims[0], dims[3]), np.float32)
-    orc.gdn_step_m(S_ref, *(x_h[n] for n in NAMES), o_ref, M, dims)
-    assert_close(o_m_h, o_ref, "o step_m")
-    assert_close(S_m_h, S_ref, "S step_m")
-    S_rb = host(S.index_select(0, ii))
-    rs = orc.slab(len(idx), dims)
-    S_ref = S_mark_h.copy()
-    rs.mark(S_ref)
-    orc.gdn_step_m(S_ref, *(x_h[n] for n in NAMES), o_ref, M, dims)
-    rs.rollback(S_ref, None, x_h, M, acc[idx])
-    assert_close(S_rb, S_ref, "S rollback")
-    for j, u in enumerate(idx):
-        if acc[u] == 0:
-            assert bits_equal(S_rb[j], S_mark_h[j])
-        if acc[u] == M:
-            assert bits_equal(S_rb[j], S_m_h[j])
-    del S, inp, slab
-
-
-def test_full_size_frontend_step_sampled(orc):
-    """Front end + step, 128 rows x 1 layer, 32 steps; 12 rows recomputed."""
-    cfg = synth.WORKLOADS[3]
-    dims = cfg["dims"]
-    vh, kh, kd, vd = dims
-    B, T = cfg["seqs"], cfg["steps"]
-    say(f"full-size frontend+step: {cfg['name']}")
-    gen = synth.make_gen(cfg["seed"], "cuda")
-    S = synth.state(gen, B, dims, device="cuda")
-    w = synth.frontend_weights(gen, dims, device="cuda")
-    fe = synth.frontend_inputs(gen, B, dims, T=T, device="cuda")
-    idx = _sample(B, np.random.default_rng(3), k=6)
-    ii = torch.as_tensor(idx, device="cuda")
-    S_h = host(S.index_select(0, ii))
-    hist = fe["hist"]
-    hist_h = host(hist.index_select(0, ii))
-    wh = {n: host(t) for n, t in w.items()}
-    Bs = len(idx)
-    for t in range(T):
-        x, xc = fe["x"][t], fe["xc_raw"][t]
-        out = gdn.frontend(x, w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], xc, hist,
-                           w["conv_w"], dims)
-        o = gdn.step(S, out["q"], out["k"], out["v"], out["g"], out["beta"])
-        ref = dict(q=np.zeros((Bs, kh, kd), np.float32), k=np.zeros((Bs, kh, kd), np.float32),
-                   v=np.zeros((Bs, vh, vd), np.float32), g=np.zeros((Bs, vh), np.float32),
-                   beta=np.zeros((Bs, vh), np.float32))
-        orc.gdn_frontend(host(x.index_select(0, ii)), wh["Wa"], wh["Wb"], wh["A_log"],
-                         wh["dt_bias"], host(xc.index_select(0, ii)), hist_h, wh["conv_w"],
-                         ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"], dims)
-        for n in NAMES:
-            assert_close(host(out[n].index_select(0, ii)), ref[n], f"frontend {n} t={t}")
-        # the oracle's step runs on the oracle's own front-end outputs
-        o_ref = np.zeros((Bs, vh, vd), np.float32)
-        orc.gdn_step(S_h, ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"], o_ref, dims)
-        assert_close(host(o.index_select(0, ii)), o_ref, f"o t={t}")
-        assert_close(host(S.index_select(0, ii)), S_h, f"S t={t}")
-        assert bits_equal(host(hist.index_select(0, ii)), hist_h)
 
 
 def test_binding_refuses_mis_sized_tensors():

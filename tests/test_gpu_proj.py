@@ -277,6 +277,35 @@ def test_layer_decode_chain(orc):
         assert bits_equal(host(hist), hist_ref) or max_rel_pages(host(hist), hist_ref) <= 1e-4
 
 
+def oracle_layer_verify(orc, W, x, S0, hist0, accepted, dims, eps):
+    """The oracle's chain of one layer verifying M draft rows of B sequences:
+    input projections over all rows, mark(S, hist), front end for M rows, M
+    steps, gated norm, out_proj, rollback to the accepted lengths.  Returns
+    (y [M][B][dim], S, hist) after the rollback."""
+    vh, kh, kd, vd = dims
+    M, B, dim = x.shape
+    cd = synth.conv_dim_of(dims)
+    xh = x.reshape(M * B, dim)
+    xc_r = ref_proj(orc, xh, W["W_qkv"]).reshape(M, B, cd)
+    z_r = ref_proj(orc, xh, W["W_z"]).reshape(M, B, vh, vd)
+    fr = dict(q=np.zeros((M, B, kh, kd), np.float32), k=np.zeros((M, B, kh, kd), np.float32),
+              v=np.zeros((M, B, vh, vd), np.float32), g=np.zeros((M, B, vh), np.float32),
+              beta=np.zeros((M, B, vh), np.float32))
+    h_r = hist0.copy()
+    oslab = orc.slab(B, dims, hist_floats=3 * cd)
+    S_r = S0.copy()
+    oslab.mark(S_r, h_r)
+    orc.gdn_frontend_m(x, W["Wa"], W["Wb"], W["A_log"], W["dt_bias"], xc_r, h_r,
+                       W["conv_w"], fr["q"], fr["k"], fr["v"], fr["g"], fr["beta"], dims)
+    o_r = np.zeros((M, B, vh, vd), np.float32)
+    orc.gdn_step_m(S_r, *(fr[n] for n in NAMES), o_r, M, dims)
+    g_r = np.zeros_like(o_r)
+    orc.gated_norm(o_r, z_r, W["norm_w"], eps, g_r)
+    y_r = ref_proj(orc, g_r.reshape(M * B, vh * vd), W["W_out"]).reshape(M, B, dim)
+    oslab.rollback(S_r, h_r, fr, M, accepted, xc_raw=xc_r, conv_dim=cd)
+    return y_r, S_r, h_r
+
+
 def test_layer_verify_chain(orc):
     """One GDN layer verifying M draft rows for B sequences, as the M-row path
     runs it ("Kestrel_VLLM #34", section 3.6): the input projections over all
@@ -313,24 +342,7 @@ def test_layer_verify_chain(orc):
     slab.rollback(S, accepted, *rows, hist=hist, xc_raw=xc)
 
     # the oracle's chain from the same inputs
-    xh = host(x).reshape(M * B, dim)
-    xc_r = ref_proj(orc, xh, W["W_qkv"]).reshape(M, B, cd)
-    z_r = ref_proj(orc, xh, W["W_z"]).reshape(M, B, vh, vd)
-    fr = dict(q=np.zeros((M, B, kh, kd), np.float32), k=np.zeros((M, B, kh, kd), np.float32),
-              v=np.zeros((M, B, vh, vd), np.float32), g=np.zeros((M, B, vh), np.float32),
-              beta=np.zeros((M, B, vh), np.float32))
-    h_r = hist0.copy()
-    oslab = orc.slab(B, dims, hist_floats=3 * cd)
-    S_r = S0.copy()
-    oslab.mark(S_r, h_r)
-    orc.gdn_frontend_m(host(x), W["Wa"], W["Wb"], W["A_log"], W["dt_bias"], xc_r, h_r,
-                       W["conv_w"], fr["q"], fr["k"], fr["v"], fr["g"], fr["beta"], dims)
-    o_r = np.zeros((M, B, vh, vd), np.float32)
-    orc.gdn_step_m(S_r, *(fr[n] for n in NAMES), o_r, M, dims)
-    g_r = np.zeros_like(o_r)
-    orc.gated_norm(o_r, z_r, W["norm_w"], eps, g_r)
-    y_r = ref_proj(orc, g_r.reshape(M * B, vh * vd), W["W_out"]).reshape(M, B, dim)
-    oslab.rollback(S_r, h_r, fr, M, accepted, xc_raw=xc_r, conv_dim=cd)
+    y_r, S_r, h_r = oracle_layer_verify(orc, W, host(x), S0, hist0, accepted, dims, eps)
 
     for m in range(M):
         for b in range(B):
@@ -343,7 +355,7 @@ def test_layer_verify_chain(orc):
         assert bits_equal(host(hist)[b], np.ascontiguousarray(seq[-3:])), b
 
 
-def test_layer_verify_chain_snapshot_free_equals_snapshot():
+def test_layer_verify_chain_snapshot_free_equals_snapshot(orc):
     """The same layer verify without a snapshot: the input projections, the
     front end for M rows without advancing the history, the gated outputs
     without advancing the state, out_proj, then commit of the accepted
@@ -395,3 +407,16 @@ def test_layer_verify_chain_snapshot_free_equals_snapshot():
     assert bits_equal(host(y1), host(y2))
     assert bits_equal(host(S1), host(S2))
     assert bits_equal(host(h1), host(h2))
+    # and the snapshot-free cycle against the oracle's chain
+    W = {n: host(t) for n, t in {**pw, **fw}.items()}
+    y_r, S_r, h_r = oracle_layer_verify(orc, W, host(x), host(S0), host(hist0), accepted, dims,
+                                        eps)
+    y2h = host(y2).reshape(M, B, dim)
+    for m in range(M):
+        for b in range(B):
+            assert max_rel_pages(y2h[m, b], y_r[m, b]) <= 1e-4, (m, b)
+    assert_close(host(S2), S_r, "S after commit")
+    # the history frames are the projection's outputs (the GPU's own bits are
+    # checked as data movement above); against the oracle's projection they
+    # agree under the layer criterion
+    assert max_rel_pages(host(h2), h_r) <= 1e-4

@@ -366,7 +366,7 @@ def test_q4_layer_decode_chain(orc):
     assert max_rel_pages(host(S), S_r) <= 1e-4
 
 
-def test_q4_graph_replay_matches_eager():
+def test_q4_graph_replay_matches_eager(orc):
     """The layer's 4-bit projections captured as a HIP graph (in_proj: one
     workgroup per group; out_proj: two workgroups per group, whose fill
     kernel and atomic adds must run on every replay) replay bit-identically
@@ -384,6 +384,11 @@ def test_q4_graph_replay_matches_eager():
     e_xc, e_z = gdn.proj_q4(x, wq["W_qkv"], wq["W_z"])
     e_y = gdn.proj_q4(h, wq["W_out"])
     torch.cuda.synchronize()
+    # the eager results against the oracle (which the replays then equal)
+    for got, xin, n in ((e_xc, x, "W_qkv"), (e_z, x, "W_z"), (e_y, h, "W_out")):
+        xh = host(xin)
+        assert_close(host(got), ref_q4(orc, xh, *w[n]), n,
+                     floor=proj_floor(xh, decode_np(host(w[n][0]), host(w[n][1]))))
     xc, z, y = torch.empty_like(e_xc), torch.empty_like(e_z), torch.empty_like(e_y)
 
     def chain():
