@@ -63,7 +63,7 @@ def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
 _Q4_SECTION = b"// " + b"-" * 75 + b"\n// Dense layer projections with 4-bit weights"
 HASH_SECTIONS = {
     "recur_wide_kernel": ((b"namespace gdn {", b"// ----- wide geometry, several steps"),
-                          (b"// Launches of fewer than GDN_WIDEM_BELOW tiles", b"// Streaming copy")),
+                          (b"// Launches of fewer than kWidemBelow tiles", b"// Streaming copy")),
     "proj_kernel": ((b"namespace gdn {", b"// Recurrence\n"),
                     (b"// Dense layer projections", _Q4_SECTION), (b"}  // namespace gdn", None)),
     "proj_q4_kernel": ((b"namespace gdn {", b"// Recurrence\n"), (_Q4_SECTION, None)),
@@ -131,55 +131,158 @@ def cpu_threads():
     return max(1, min(16, n or 1))
 
 
-def cpu_baseline_step(S_gpu, pool, dims, units, rows):
-    """The CPU oracle, as it stands, on `units` units x `rows` steps, split
-    over host threads by unit (units are independent)."""
-    import oracle
+def cpu_info():
+    """Online host cores and the CPU model string."""
+    online = os.sysconf("SC_NPROCESSORS_ONLN") if hasattr(os, "sysconf") else None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return online, model
+
+
+def over_ranges(fn, n, chunk, threads):
+    """fn(lo, hi) over consecutive ranges of n units on a pool of host threads
+    (the oracle releases the GIL); results in range order."""
     from concurrent.futures import ThreadPoolExecutor
+    ranges = [(lo, min(lo + chunk, n)) for lo in range(0, n, chunk)]
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(lambda r: fn(*r), ranges))
 
+
+class Tol:
+    """Elements outside |x - r| <= max(1e-5 |r|, floor) and the pages'
+    max|err| / max|ref| ("Kestrel_VLLM #24", section 6), over many ranges."""
+
+    def __init__(self):
+        self.bad, self.n, self.max_err, self.max_ref = 0, 0, 0.0, 0.0
+
+    def add(self, x, r, floor=1e-6):
+        x = np.asarray(x, np.float64)
+        r = np.asarray(r, np.float64)
+        err = np.abs(x - r)
+        bad = (err > np.maximum(1e-5 * np.abs(r), floor)) | (np.isnan(x) != np.isnan(r))
+        self.bad += int(np.count_nonzero(bad))
+        self.n += x.size
+        if x.size:
+            self.max_err = max(self.max_err, float(np.nanmax(err)))
+            self.max_ref = max(self.max_ref, float(np.nanmax(np.abs(r))))
+        return self
+
+    def merge(self, o):
+        self.bad += o.bad
+        self.n += o.n
+        self.max_err = max(self.max_err, o.max_err)
+        self.max_ref = max(self.max_ref, o.max_ref)
+        return self
+
+    def rec(self):
+        return dict(elements=self.n, out_of_tolerance=self.bad,
+                    max_rel_pages=(self.max_err / self.max_ref) if self.max_ref else self.max_err)
+
+
+def merged(results, k):
+    t = Tol()
+    for r in results:
+        t.merge(r[k])
+    return t
+
+
+def gated_floor(o_ref, z, w, eps):
+    """o's absolute floor (1e-6) carried through the gated norm's per-head
+    scale s = w silu(z) / sqrt(mean(o^2) + eps)."""
+    o64, z64 = o_ref.astype(np.float64), z.astype(np.float64)
+    rinv = 1.0 / np.sqrt(np.mean(o64 ** 2, axis=-1, keepdims=True) + eps)
+    return 1e-6 * np.abs(rinv * w.astype(np.float64) * z64 / (1.0 + np.exp(-z64)))
+
+
+def decode_cpu_and_parity(S0, pool, dims, steps, gated=None):
+    """The CPU oracle, as it stands, on every unit of the workload for `steps`
+    decode steps (inputs cycled from the pool as in the timed loop), timed on
+    a pool of host threads, plus a single-thread run of the first 3 steps of
+    the first units; then the GPU reruns the same steps from the same initial
+    state (one launch over all units per step) and every element of o and of
+    the final S is compared with the oracle's.  gated = (z per pool entry,
+    norm_w, eps) for the gated-output workload."""
+    import oracle
     orc = oracle.load()
-    S = np.ascontiguousarray(S_gpu[:units].cpu().numpy())
-    xs = [{n: np.ascontiguousarray(pool[r % len(pool)][n][0, :units].cpu().numpy())
-           for n in NAMES} for r in range(rows)]
     vh, kh, kd, vd = dims
-    th = min(cpu_threads(), units)
-    chunks = np.array_split(np.arange(units), th)
+    N = S0.shape[0]
+    th = cpu_threads()
+    online, model = cpu_info()
+    xs = [{n: host(pool[r % len(pool)][n][0]) for n in NAMES} for r in range(steps)]
+    # single thread: the first 3 steps of the first units (about 1 s of work)
+    n1 = min(N, 64)
+    S1 = host(S0[:n1])
+    o1 = np.zeros((n1, vh, vd), np.float32)
+    t0 = time.perf_counter()
+    for r in range(min(3, steps)):
+        orc.gdn_step(S1, *(np.ascontiguousarray(xs[r][n][:n1]) for n in NAMES), o1, dims)
+    dt1 = time.perf_counter() - t0
+    hs1 = n1 * vh * min(3, steps)
+    # every unit, all threads, timed (in place on the host copy)
+    S_h = host(S0)
+    O_ref = np.zeros((steps, N, vh, vd), np.float32)
 
-    o_last = np.zeros((units, vh, vd), np.float32)
-
-    def work(ch):
-        lo, hi = int(ch[0]), int(ch[-1]) + 1
-        Sc = S[lo:hi]
-        o = o_last[lo:hi]
-        for x in xs:
-            orc.gdn_step(Sc, *(np.ascontiguousarray(x[n][lo:hi]) for n in NAMES), o, dims)
+    def work(lo, hi):
+        for r in range(steps):
+            orc.gdn_step(S_h[lo:hi], *(np.ascontiguousarray(xs[r][n][lo:hi]) for n in NAMES),
+                         O_ref[r, lo:hi], dims)
 
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(th) as ex:
-        list(ex.map(work, chunks))
+    over_ranges(work, N, max(1, (N + 4 * th - 1) // (4 * th)), th)
     dt = time.perf_counter() - t0
-    hs = units * vh * rows
-    res = dict(value=hs / dt, unit="head-steps/s", cores=th, kind="oracle",
-               sample=f"{units} units x {rows} steps ({hs} head-steps) of the same workload, "
-                      f"{dt:.2f} s wall on {th} threads")
-    return res, S, o_last
-
-
-def sample_parity(S0, pool, units, rows, S_ref, o_ref):
-    """The GPU's own run of the baseline's sample (same initial state and
-    inputs, single-step launches) against the oracle's result: elements
-    outside |x - r| <= max(1e-5 |r|, 1e-6), and the pages' max|err| / max|ref|."""
+    hs = N * vh * steps
+    cpu = dict(value=hs / dt, unit="head-steps/s", cores=th, kind="oracle",
+               sample=f"every unit of the workload ({N} units) x {steps} steps = {hs} head-steps, "
+                      f"{dt:.2f} s wall on {th} threads; single thread: the first "
+                      f"{min(3, steps)} steps of {n1} units, {dt1:.2f} s",
+               threads_used=th, online_cores=online, cpu_model=model,
+               single_thread_value=hs1 / dt1, single_thread_sample=f"{n1} units x {min(3, steps)} steps")
+    # the GPU on the same steps, then every element against the oracle
     S = S0.clone()
-    for r in range(rows):
-        o = gdn.step(S, *(pool[r % len(pool)][n][0, :units].contiguous() for n in NAMES))
-    out = {}
-    for name, got, ref in (("o", o, o_ref), ("S", S, S_ref)):
-        x = got.cpu().numpy().astype(np.float64)
-        r = ref.astype(np.float64)
-        err = np.abs(x - r)
-        out[f"{name}_elements_out_of_tolerance"] = int(np.sum(err > np.maximum(1e-5 * np.abs(r), 1e-6)))
-        out[f"{name}_max_rel_pages"] = float(err.max() / np.abs(r).max())
-    return dict(units=units, steps=rows, **out)
+    O = torch.empty((steps, N, vh, vd), device=S0.device)
+    for r in range(steps):
+        x = pool[r % len(pool)]
+        if gated:
+            gdn.step_gated(S, *(x[n] for n in NAMES), gated[0][r % len(pool)], gated[1],
+                           gated[2], out=O[r:r + 1])
+        else:
+            gdn.step(S, *(x[n][0] for n in NAMES), o=O[r])
+    torch.cuda.synchronize()
+    if gated:
+        z_h = [host(z) for z in gated[0]]
+        w_h = host(gated[1])
+
+    def check(lo, hi):
+        to, ts = Tol(), Tol()
+        for r in range(steps):
+            ref = O_ref[r, lo:hi]
+            if gated:
+                zz = np.ascontiguousarray(z_h[r % len(pool)][0, lo:hi])
+                out = np.zeros_like(ref)
+                orc.gated_norm(np.ascontiguousarray(ref), zz, w_h, gated[2], out)
+                to.add(host(O[r, lo:hi]), out, gated_floor(ref, zz, w_h, gated[2]))
+            else:
+                to.add(host(O[r, lo:hi]), ref)
+        ts.add(host(S[lo:hi]), S_h[lo:hi])
+        return to, ts
+
+    res = over_ranges(check, N, 32, th)
+    par = dict(units=N, steps=steps, launch="one launch over all units per step",
+               o=merged(res, 0).rec(), S=merged(res, 1).rec())
+    if gated:
+        par["o_is"] = "the gated output"
+    return cpu, par
+
+
+def host(t):
+    return np.ascontiguousarray(t.detach().cpu().numpy())
 
 
 def copy_floor(S, reps=5):
@@ -189,6 +292,15 @@ def copy_floor(S, reps=5):
     gdn.stream_copy(flat, flat)
     dt = timed(lambda i: gdn.stream_copy(flat, flat), reps, 1)
     return 2 * flat.numel() * 4 * reps / dt / 1e9
+
+
+def read_floor(S, reps=5):
+    """Read-only floor: stream the state with 128-bit non-temporal loads (one
+    checksum word per 128 KiB written, 0.003% of the bytes)."""
+    flat = S.view(-1)
+    words = gdn.stream_read(flat)
+    dt = timed(lambda i: gdn.stream_read(flat, words=words), reps, 1)
+    return flat.numel() * 4 * reps / dt / 1e9
 
 
 def bench_decode(cfg, steps, warmup, cpu):
@@ -243,6 +355,7 @@ def bench_decode(cfg, steps, warmup, cpu):
     bytes_launch = hs_per_step * bps
     achieved = bytes_launch / launch_s / 1e9
     floor = copy_floor(S)
+    rfloor = read_floor(S)
     key = {1: "b64x48", 4: "b512x8", 5: "b512x8_kd64", 7: "b64x48_gated"}.get(
         cfg["id"], f"cfg{cfg['id']}")
     traffic = recorded_traffic(key, bytes_launch)
@@ -252,16 +365,18 @@ def bench_decode(cfg, steps, warmup, cpu):
                       unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic),
         extra=dict(copy_floor_GBps=round(floor, 1),
                    frac_of_copy_floor=round(achieved / floor, 4),
+                   read_floor_GBps=round(rfloor, 1),
                    algorithmic_bytes_per_launch=int(bytes_launch),
                    bytes_per_head_step=round(bps, 2), head_steps_per_step=hs_per_step,
                    kernel="recur_wide_kernel", kernel_source_sha256_16=kernel_hash(),
                    **per_layer))
     if cpu:
-        units = min(N, 1024)
-        S0 = S[:units].clone()
-        res["cpu_baseline"], S_ref, o_ref = cpu_baseline_step(S, pool, dims, units=units, rows=8)
-        # outside the timed region: the GPU on the same sample, against the oracle
-        res["extra"]["parity_sample"] = sample_parity(S0, pool, units, 8, S_ref, o_ref)
+        # outside the timed region, from the state as it now stands
+        S0 = S.clone()
+        del S
+        res["cpu_baseline"], res["extra"]["parity_all_units"] = decode_cpu_and_parity(
+            S0, pool, dims, steps=3,
+            gated=([x["z"] for x in pool], norm_w, 1e-6) if gated else None)
     return res, dict(workload=cfg["name"], units=N, seqs=cfg["seqs"], layers=cfg["layers"],
                      vh=dims[0], kh=dims[1], kd=dims[2], vd=dims[3],
                      state_GB=round(N * vh * dims[2] * dims[3] * 4 / 1e9, 3),
@@ -309,9 +424,8 @@ def bench_latency(cfg, steps, warmup, cpu):
                           note="3 MiB state stays in L2/MALL: latency figure, not an HBM claim"))
     if cpu:
         pool1 = [{n: inp[n][m:m + 1] for n in NAMES} for m in range(T)]
-        S0 = S[:1].clone()
-        res["cpu_baseline"], S_ref, o_ref = cpu_baseline_step(S, pool1, dims, units=1, rows=T)
-        res["extra"]["parity_sample"] = sample_parity(S0, pool1, 1, T, S_ref, o_ref)
+        res["cpu_baseline"], res["extra"]["parity_all_units"] = decode_cpu_and_parity(
+            S.clone(), pool1, dims, steps=T)
     return res, dict(workload=cfg["name"], units=1, vh=vh, kd=dims[2], steps_per_iteration=T)
 
 
@@ -346,6 +460,7 @@ def bench_verify(cfg, steps, warmup, cpu):
         gdn.verify_m(S, *args, o=o)
         gdn.commit(S, acc_dev[i % 8], *args, status=status)
 
+    S_start = S.clone() if cpu else None
     dt = timed(one, steps, warmup)
     dt_unfused = timed(one_unfused, steps, 1)
     dt_vc = timed(one_verify_commit, steps, 1)
@@ -361,8 +476,51 @@ def bench_verify(cfg, steps, warmup, cpu):
                           cycle_ms_separate_mark=round(dt_unfused / steps * 1e3, 4),
                           cycle_ms_verify_commit=round(dt_vc / steps * 1e3, 4),
                           value_counts="drafted head-steps per second of the full cycle"))
+    if cpu:
+        res["extra"]["parity_all_units"] = verify_parity(S_start, inp, dims, accs[0])
     return res, dict(workload=cfg["name"], units=N, M=M, vh=vh, kd=dims[2],
                      cycle="gdn_mark_step_m(M=8) + gdn_rollback(accepted ~ U{0..8})")
+
+
+def verify_parity(S0, inp, dims, acc):
+    """One speculative cycle from S0 in both protocols on the GPU (the fused
+    mark + M steps + rollback, and verify + commit), bit-compared with each
+    other on the device, and every unit against the oracle's mark, M steps,
+    rollback."""
+    import oracle
+    orc = oracle.load()
+    vh, kh, kd, vd = dims
+    M, N = inp["q"].shape[:2]
+    args = [inp[n] for n in NAMES]
+    S = S0.clone()
+    slab = gdn.Slab(N, dims)
+    o = slab.mark_step_m(S, *args)
+    S_m = S.clone()
+    slab.rollback(S, acc, *args)
+    del slab
+    S_b = S0.clone()
+    o_b = gdn.verify_m(S_b, *args)
+    gdn.commit(S_b, torch.as_tensor(acc, device=S0.device), *args)
+    torch.cuda.synchronize()
+    same = lambda a, b: torch.equal(a.view(torch.int32), b.view(torch.int32))  # noqa: E731
+    protocols_bit_equal = same(o, o_b) and same(S, S_b)
+    del S_b, o_b
+
+    def check(lo, hi):
+        S_h = host(S0[lo:hi])
+        x_h = {n: host(inp[n][:, lo:hi]) for n in NAMES}
+        rs = orc.slab(hi - lo, dims)
+        rs.mark(S_h)
+        o_ref = np.zeros((M, hi - lo, vh, vd), np.float32)
+        orc.gdn_step_m(S_h, *(x_h[n] for n in NAMES), o_ref, M, dims)
+        to, tm = Tol().add(host(o[:, lo:hi]), o_ref), Tol().add(host(S_m[lo:hi]), S_h)
+        rs.rollback(S_h, None, x_h, M, acc[lo:hi])
+        return to, tm, Tol().add(host(S[lo:hi]), S_h)
+
+    res = over_ranges(check, N, 16, cpu_threads())
+    return dict(units=N, M=M, protocols_bit_equal=bool(protocols_bit_equal),
+                o=merged(res, 0).rec(), S_after_step_m=merged(res, 1).rec(),
+                S_after_rollback=merged(res, 2).rec())
 
 
 def bench_frontend(cfg, steps, warmup, cpu):
@@ -385,6 +543,7 @@ def bench_frontend(cfg, steps, warmup, cpu):
                      hist, w["conv_w"], dims, out=out)
         gdn.step(S, out["q"], out["k"], out["v"], out["g"], out["beta"], o=o)
 
+    S_start, hist_start = (S.clone(), hist.clone()) if cpu else (None, None)
     dt = timed(one, steps, warmup)
     cd = synth.conv_dim_of(dims)
     fe_bytes = (B * 5120 * 4 + 2 * vh * 5120 * 4 + B * cd * 4 + 2 * B * 3 * cd * 4
@@ -396,7 +555,54 @@ def bench_frontend(cfg, steps, warmup, cpu):
                              unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
                extra=dict(frontend_bytes=fe_bytes,
                           note="384 MiB state is 1.5x the MALL: partly cache-resident"))
+    if cpu:
+        res["extra"]["parity_all_units"] = frontend_parity(S_start, hist_start, w, fe, dims, T)
     return res, dict(workload=cfg["name"], units=B, vh=vh, kd=kd, dim=5120, conv_dim=cd)
+
+
+def frontend_parity(S0, hist0, w, fe, dims, T):
+    """T steps of front end + step from the given state and history on the
+    GPU, then every row's front-end outputs and o at every step, the final S
+    and the history against the oracle's chain (front end, then step on the
+    oracle's own outputs)."""
+    import oracle
+    orc = oracle.load()
+    vh, kh, kd, vd = dims
+    B = S0.shape[0]
+    S, hist = S0.clone(), hist0.clone()
+    F = {n: torch.empty((T,) + shp, device=S0.device) for n, shp in
+         (("q", (B, kh, kd)), ("k", (B, kh, kd)), ("v", (B, vh, vd)), ("g", (B, vh)),
+          ("beta", (B, vh)))}
+    O = torch.empty((T, B, vh, vd), device=S0.device)
+    for t in range(T):
+        out = {n: F[n][t] for n in NAMES}
+        gdn.frontend(fe["x"][t], w["Wa"], w["Wb"], w["A_log"], w["dt_bias"], fe["xc_raw"][t],
+                     hist, w["conv_w"], dims, out=out)
+        gdn.step(S, *(out[n] for n in NAMES), o=O[t])
+    torch.cuda.synchronize()
+    wh = {n: host(t) for n, t in w.items()}
+
+    def check(lo, hi):
+        n = hi - lo
+        tf, to = Tol(), Tol()
+        S_h, h_h = host(S0[lo:hi]), host(hist0[lo:hi])
+        for t in range(T):
+            ref = dict(q=np.zeros((n, kh, kd), np.float32), k=np.zeros((n, kh, kd), np.float32),
+                       v=np.zeros((n, vh, vd), np.float32), g=np.zeros((n, vh), np.float32),
+                       beta=np.zeros((n, vh), np.float32))
+            orc.gdn_frontend(host(fe["x"][t, lo:hi]), wh["Wa"], wh["Wb"], wh["A_log"],
+                             wh["dt_bias"], host(fe["xc_raw"][t, lo:hi]), h_h, wh["conv_w"],
+                             ref["q"], ref["k"], ref["v"], ref["g"], ref["beta"], dims)
+            for k in NAMES:
+                tf.add(host(F[k][t, lo:hi]), ref[k])
+            o_ref = np.zeros((n, vh, vd), np.float32)
+            orc.gdn_step(S_h, *(ref[k] for k in NAMES), o_ref, dims)
+            to.add(host(O[t, lo:hi]), o_ref)
+        return tf, to, Tol().add(host(S[lo:hi]), S_h), host(hist[lo:hi]).tobytes() == h_h.tobytes()
+
+    res = over_ranges(check, B, 8, cpu_threads())
+    return dict(rows=B, steps=T, frontend=merged(res, 0).rec(), o=merged(res, 1).rec(),
+                S=merged(res, 2).rec(), history_bit_exact=all(r[3] for r in res))
 
 
 def bench_verify_frontend(cfg, steps, warmup, cpu):
