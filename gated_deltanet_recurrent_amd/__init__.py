@@ -36,7 +36,8 @@ EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab
            "gdn_frontend_verify_m",
            "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy",
            "gdn_proj", "gdn_proj_pack", "gdn_verify_m_gated", "gdn_proj_q4_bytes",
-           "gdn_proj_q4_pack", "gdn_proj_q4", "gdn_stream_read", "gdn_stream_read_words")
+           "gdn_proj_q4_pack", "gdn_proj_q4", "gdn_stream_read", "gdn_stream_read_words",
+           "gdn_rollback_static")
 
 
 class GdnError(RuntimeError):
@@ -77,6 +78,7 @@ def lib():
     L.gdn_mark.argtypes = [C.POINTER(gdn_slab), P, P, P]
     L.gdn_mark_step_m.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I64, I32, I32, I32, I32, I32, P]
     L.gdn_rollback.argtypes = [C.POINTER(gdn_slab)] + [P] * 8 + [I32, I32, I32, P, P]
+    L.gdn_rollback_static.argtypes = L.gdn_rollback.argtypes
     L.gdn_frontend.argtypes = [P] * 13 + [I32] * 8 + [P]
     L.gdn_frontend_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_stream_copy.argtypes = [P, P, I64, P]
@@ -94,7 +96,7 @@ def lib():
     L.gdn_proj_q4_pack.argtypes = [P, P, P, I32, I32, P]
     L.gdn_proj_q4.argtypes = [P, I64, I32, P, I32, P, P, I32, P, P]
     for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark_step_m", "gdn_mark", "gdn_rollback",
-              "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_stream_read",
+              "gdn_rollback_static", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_stream_read",
               "gdn_verify_m",
               "gdn_commit", "gdn_frontend_verify_m", "gdn_proj", "gdn_proj_pack",
               "gdn_verify_m_gated", "gdn_proj_q4_pack", "gdn_proj_q4"):
@@ -251,8 +253,10 @@ class Slab:
         return o
 
     def rollback(self, S, accepted, q=None, k=None, v=None, g=None, beta=None, hist=None,
-                 xc_raw=None, M=None, stream=None):
-        """accepted: host int32 per unit (list, numpy or CPU tensor)."""
+                 xc_raw=None, M=None, stream=None, static_counts=False):
+        """accepted: host int32 per unit (list, numpy or CPU tensor).
+        static_counts: stage the counts in the library's own area
+        (gdn_rollback_static) instead of the slab's."""
         acc = torch.as_tensor(accepted, dtype=torch.int32).contiguous().cpu()
         if acc.numel() != self.s.n_units:
             raise ValueError("accepted must hold one entry per unit")
@@ -262,11 +266,11 @@ class Slab:
             hist.shape[-1] if hist is not None else 0)
         ns = self._state_sizes()[0]
         rows = _rows(S, q, k, v, g, beta, M) if q is not None else [None] * 5
-        _check(lib().gdn_rollback(C.byref(self.s), _sized(S, ns, "S"), self._hist(hist),
-                                  *rows,
-                                  _sized(xc_raw, M * self.s.n_units * conv_dim, "xc_raw"),
-                                  conv_dim, 4, M, C.c_void_p(acc.data_ptr()), _stream(stream)),
-               "gdn_rollback")
+        fn = lib().gdn_rollback_static if static_counts else lib().gdn_rollback
+        _check(fn(C.byref(self.s), _sized(S, ns, "S"), self._hist(hist), *rows,
+                  _sized(xc_raw, M * self.s.n_units * conv_dim, "xc_raw"),
+                  conv_dim, 4, M, C.c_void_p(acc.data_ptr()), _stream(stream)),
+               "gdn_rollback_static" if static_counts else "gdn_rollback")
 
 
 def _fe_args(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, out, dims, M, B, dim):

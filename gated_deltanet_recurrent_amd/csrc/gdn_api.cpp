@@ -80,7 +80,8 @@ const char *gdn_strerror(int rc) {
     case GDN_EINVAL: return "invalid argument (NULL or misaligned pointer, bad size, aliasing, M or accepted out of range)";
     case GDN_EUNSUPPORTED:
       return "unsupported shape (recurrence: kd == vd must be 64 or 128; projection: C a multiple "
-             "of 128, R of 16; or a launch too large)";
+             "of 128, R of 16; conv width other than 4; a launch too large; or more than 65536 "
+             "units for gdn_rollback_static)";
     case GDN_ESTATE: return "slab state error (not armed, history not marked, too small, or mismatched)";
     case GDN_EDEVICE: return "HIP runtime error while enqueuing";
     default: return "unknown error code";
@@ -231,10 +232,15 @@ int gdn_mark_step_m(gdn_slab *slab, float *S, const float *hist, const float *q,
   return GDN_OK;
 }
 
-int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const float *k,
-                 const float *v, const float *g, const float *beta, const float *xc_raw,
-                 int32_t conv_dim, int32_t ck, int32_t M, const int32_t *accepted,
-                 void *stream) {
+namespace {
+
+// gdn_rollback with the per-unit counts staged in `counts` (device, N int32):
+// the slab's count area, or the library's static one (counts == nullptr:
+// looked up after validation).
+int rollback_impl(gdn_slab *slab, float *S, float *hist, const float *q, const float *k,
+                  const float *v, const float *g, const float *beta, const float *xc_raw,
+                  int32_t conv_dim, int32_t ck, int32_t M, const int32_t *accepted,
+                  bool static_counts, void *stream) {
   if (!slab_valid(slab)) return GDN_ESTATE;
   if (!(slab->armed & 1)) return GDN_ESTATE;
   if (hist != nullptr && !(slab->armed & 2)) return GDN_ESTATE;
@@ -265,11 +271,13 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const fl
     if (overlaps(hist, N * slab->hist_floats * 4, slab->dev, slab->bytes)) return GDN_EINVAL;
     if (any && !ptr_ok(xc_raw)) return GDN_EINVAL;
   }
+  if (static_counts && N > gdn::kStaticCountsMax) return GDN_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
-  // accepted[] reaches the slab's count area through kernel arguments, so the
-  // host array is consumed before return and the counts are ordered on the
-  // stream before the kernels that read them.
+  // accepted[] reaches the count area through kernel arguments, so the host
+  // array is consumed before return and the counts are ordered on the stream
+  // before the kernels that read them.
   int32_t *d_acc = slab_accepted(slab);
+  if (static_counts && gdn::static_counts_area(&d_acc) != 0) return GDN_EDEVICE;
   int rc0 = enq(gdn::launch_stage_counts(d_acc, accepted, N, s));
   if (rc0) return rc0;
   // the history replay runs in the same launch as the state replay
@@ -279,6 +287,24 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const fl
   if (rc) return rc;
   slab->armed = 0;
   return GDN_OK;
+}
+
+}  // namespace
+
+int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q, const float *k,
+                 const float *v, const float *g, const float *beta, const float *xc_raw,
+                 int32_t conv_dim, int32_t ck, int32_t M, const int32_t *accepted,
+                 void *stream) {
+  return rollback_impl(slab, S, hist, q, k, v, g, beta, xc_raw, conv_dim, ck, M, accepted,
+                       false, stream);
+}
+
+int gdn_rollback_static(gdn_slab *slab, float *S, float *hist, const float *q, const float *k,
+                        const float *v, const float *g, const float *beta, const float *xc_raw,
+                        int32_t conv_dim, int32_t ck, int32_t M, const int32_t *accepted,
+                        void *stream) {
+  return rollback_impl(slab, S, hist, q, k, v, g, beta, xc_raw, conv_dim, ck, M, accepted,
+                       true, stream);
 }
 
 namespace {

@@ -38,6 +38,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace gdn {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -1152,6 +1154,35 @@ int launch_stage_counts(int32_t *dst, const int32_t *host, int64_t n, hipStream_
     const int rc = (int)hipGetLastError();
     if (rc) return rc;
   }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned count area for callers that cannot allocate: a file-scope
+// device array, one copy per GPU, whose device address is looked up once per
+// device (the array's name is a host-side stand-in in host code and must not
+// be passed to a kernel).  Every call on a GPU shares that GPU's copy.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) int32_t scratch[kStaticCountsMax];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+int static_counts_area(int32_t **area) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return e != hipSuccess ? (int)e : -1;
+    g_scratch_ptr[dev] = static_cast<int32_t *>(p);
+  }
+  *area = g_scratch_ptr[dev];
   return 0;
 }
 

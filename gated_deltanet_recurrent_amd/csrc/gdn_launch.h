@@ -43,6 +43,14 @@ int launch_read(const float *src, int64_t n, uint32_t *words, hipStream_t s);
 // array is not read after the call returns.
 int launch_stage_counts(int32_t *dst, const int32_t *host, int64_t n, hipStream_t s);
 
+// Units whose counts the library-owned count area holds (256 KiB).
+constexpr int64_t kStaticCountsMax = 1 << 16;
+
+// Device address of the library-owned count area of kStaticCountsMax int32
+// on the current device (looked up once per device, then cached); 0 on
+// success, else a HIP error code or -1.
+int static_counts_area(int32_t **area);
+
 // Conv-history replay (ck = 4): hist[u] = last 3 frames of
 // [src[u] frames..., xc_raw[0][u], ..., xc_raw[a-1][u]], a = accepted[u];
 // src may be hist itself.  a outside 0..M: the unit gets a = 0 and *status

@@ -16,7 +16,7 @@
  *  - Every pointer named as device memory is a device pointer (e.g. a torch
  *    tensor's data_ptr) owned by the caller, fp32 unless stated, contiguous,
  *    and 16-byte aligned.  The library allocates nothing and keeps no global
- *    mutable state.
+ *    mutable state other than gdn_rollback_static's count area.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
  *    call validates its arguments on the host, enqueues its kernels on the
  *    stream and returns without synchronising, except where noted.
@@ -178,6 +178,24 @@ int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q,
                  const float *k, const float *v, const float *g,
                  const float *beta, const float *xc_raw, int32_t conv_dim,
                  int32_t ck, int32_t M, const int32_t *accepted, void *stream);
+
+/*
+ * gdn_rollback for callers that cannot allocate device memory (code under
+ * graph capture, serving loops, harnesses that forbid allocation): the same
+ * arguments, refusals and results, bit for bit, but the per-unit counts are
+ * staged in a count area the library owns instead of the slab's: one static
+ * device array of 65536 int32 (256 KiB) per GPU, held until the process
+ * ends.  The call allocates nothing.  More than 65536 units (the slab's
+ * n_units) are refused with GDN_EUNSUPPORTED before anything is enqueued.
+ * Every call on one GPU shares that GPU's area and overwrites the counts of
+ * its own units before reading them; calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must be ordered by
+ * the caller.
+ */
+int gdn_rollback_static(gdn_slab *slab, float *S, float *hist, const float *q,
+                        const float *k, const float *v, const float *g,
+                        const float *beta, const float *xc_raw, int32_t conv_dim,
+                        int32_t ck, int32_t M, const int32_t *accepted, void *stream);
 
 /*
  * Speculative verify without a snapshot.  The M draft rows are evaluated
