@@ -617,8 +617,8 @@ def test_frontend_m_bit_exact_and_parity(orc, dims, B, M):
     the oracle's M-row front end within tolerance (history bit for bit).  The
     GEMV has three shapes (one row; 2 to 8 rows; more), and the cases pair
     each with the others: B = 1 against M = 3, 8 (2-8 rows) and 12 (more), B
-    = 3 or 5 (2-8 rows) against 9 or 15 rows (more, the first ragged).  The
-    conv of an M-row call runs its rows in parallel up to 8 sequences and
+    = 3 or 5 (2-8 rows) against 9 or 15 rows (more, the first ragged).
+    The conv of an M-row call runs its rows in parallel up to 8 sequences and
     slides one window per sequence beyond (B = 9, 10), as single-row calls
     always do."""
     say(f"frontend_m dims={dims} B={B} M={M}")
@@ -648,6 +648,42 @@ def test_frontend_m_bit_exact_and_parity(orc, dims, B, M):
     for n in NAMES:
         assert_close(host(out_m[n]), ref[n], f"frontend_m {n}")
     assert bits_equal(host(hist_m), h_ref)
+
+
+@pytest.mark.parametrize("dims,dim", [(synth.DIMS128, 5120), (synth.DIMS64, 5120),
+                                      ((6, 2, 64, 64), 1000), ((6, 3, 128, 128), 2052)])
+def test_frontend_gemv_rows_independent_of_row_count(orc, dims, dim):
+    """The paired GEMV of row r gives the same g and beta bits in calls of
+    every row count, across the three GEMV shapes that serve them (one row,
+    2 to 8 rows, more; the last ragged against its 8-row tiles), with dim a
+    multiple of the 2048-column lane stride or not; and the oracle agrees
+    within tolerance."""
+    say(f"GEMV row-count independence dims={dims} dim={dim}")
+    vh, kh, kd, vd = dims
+    gen = synth.make_gen(23, "cuda")
+    w = synth.frontend_weights(gen, dims, dim=dim, device="cuda")
+    Rmax = 300
+    fe = synth.frontend_inputs(gen, Rmax, dims, T=1, dim=dim, device="cuda")
+    gb = {}
+    for R in (1, 2, 3, 4, 5, 8, 9, 64, 128, 129, 300):
+        out = gdn.frontend(fe["x"][0, :R].contiguous(), w["Wa"], w["Wb"], w["A_log"],
+                           w["dt_bias"], fe["xc_raw"][0, :R].contiguous(),
+                           fe["hist"][:R].clone(), w["conv_w"], dims)
+        gb[R] = (host(out["g"]), host(out["beta"]))
+    for R, (g_, b_) in gb.items():
+        n = min(R, 64)
+        assert bits_equal(g_[:n], gb[300][0][:n]) and bits_equal(b_[:n], gb[300][1][:n]), R
+        assert bits_equal(g_[:1], gb[1][0]) and bits_equal(b_[:1], gb[1][1]), R
+    wh = {n: host(t) for n, t in w.items()}
+    R = 9
+    ref = dict(q=np.zeros((R, kh, kd), np.float32), k=np.zeros((R, kh, kd), np.float32),
+               v=np.zeros((R, vh, vd), np.float32), g=np.zeros((R, vh), np.float32),
+               beta=np.zeros((R, vh), np.float32))
+    orc.gdn_frontend(host(fe["x"][0, :R]), wh["Wa"], wh["Wb"], wh["A_log"], wh["dt_bias"],
+                     host(fe["xc_raw"][0, :R]), host(fe["hist"][:R]), wh["conv_w"], ref["q"],
+                     ref["k"], ref["v"], ref["g"], ref["beta"], dims)
+    assert_close(gb[9][0], ref["g"], "g")
+    assert_close(gb[9][1], ref["beta"], "beta")
 
 
 def test_verify_cycle_with_frontend(orc):
