@@ -1788,6 +1788,16 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
   return (int)hipGetLastError();
 }
 
+// y0[0..n0) = 0 and y1[0..n1) = 0: the fill before a launch whose two
+// half-workgroups add their folds into y with atomics.
+__global__ __launch_bounds__(256) void zero2_kernel(float *y0, int64_t n0, float *y1, int64_t n1) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n0)
+    y0[i] = 0.f;
+  else if (i - n0 < n1)
+    y1[i - n0] = 0.f;
+}
+
 // ---------------------------------------------------------------------------
 // Dense layer projections on the matrix cores: y[r][o] = sum_c W[o][c] x[r][c]
 // ("Kestrel_VLLM #24", Fig. 1 caption, steps 1 and 7: in_proj_qkv, in_proj_z
@@ -1812,14 +1822,24 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
 // 64-byte pieces and the call ran 25-30% slower at 1 row.
 //
 // Canonical summation, independent of the row count and of the tiling: C is
-// cut into PJ_SEG equal segments; each segment is summed by one MFMA chain
-// over its 16-column blocks in ascending order (block kb, MFMA step s adds
-// the terms of columns kb + 4 i + s, i = 0..3); the PJ_SEG segment sums are
-// then folded left to right.  A row's result therefore does not depend on
-// which other rows share the call, and every tile shape gives the same bits.
+// cut into PJ_SEG = 8 equal segments; each segment is summed by one MFMA
+// chain over its 16-column blocks in ascending order (block kb, MFMA step s
+// adds the terms of columns kb + 4 i + s, i = 0..3); segments 0..3 are
+// folded left to right, so are segments 4..7, and the two sums are added.  A
+// row's result therefore does not depend on which other rows share the call,
+// and every tile shape gives the same bits.
 //
 // A workgroup is PJ_SEG waves, wave w owning segment w for a tile of 16 RB
 // rows x 16 OJ outputs; the segment sums meet in LDS and are folded there.
+// When a launch of 2 to 16 rows has fewer tiles than twice the CUs (out_proj:
+// 320), each tile takes two workgroups of 4 waves instead, one per half of
+// the segments, and each adds its half's fold into y, which a fill kernel set
+// to zero.  Every segment sum is a chain started at +0, so no
+// fold is -0 and +0 + h = h exactly; with exactly two addends the result is
+// h0 + h1 whichever arrives first (fp addition is commutative), so both
+// shapes give the same bits, and out_proj's 640 half-tiles spread over the
+// CUs (8 rows: 27.8 -> 23.5 us).  At one row the fill kernel's launch costs
+// what the split gains, so one-row launches keep whole tiles.
 // Workgroups are ordered output-slab major, row-group minor, and laid out
 // contiguously per XCD, so the row groups sharing a weight slab run on one
 // L2.  Two products over the same x (in_proj_qkv and in_proj_z) share one
@@ -1828,6 +1848,7 @@ int launch_frontend(const float *x, const float *Wa, const float *Wb,
 
 constexpr int PJ_SEG = 8;                 // segments of C, one wave each
 constexpr int PJ_LANES = 64 * PJ_SEG;
+constexpr int64_t kPjSplitBelow = 512;    // few-row launches of fewer tiles: two halves each
 constexpr int64_t kPjMinWg = 128;
 constexpr int64_t kPjMinWg1 = 256;
 constexpr int64_t kPjU2Rows = 8;        // few rows: up to this many
@@ -1837,7 +1858,7 @@ struct ProjProblem {
   const float *W;
   float *y;
   int R;
-  int blocks;       // workgroups: (R / (16 OJ)) * row_groups
+  int blocks;       // workgroups: (R / (16 OJ)) * row_groups, twice that when split
 };
 
 struct ProjArgs {
@@ -1861,31 +1882,37 @@ static __device__ __forceinline__ f4 ld_w(rsrc_t r, int voff) {
       f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, STREAM ? POL_STREAM_LOAD : 0));
 }
 
-// RB row blocks x OJ output slabs per wave, U 16-column blocks per trip.
-template <int RB, int OJ, int U, bool STREAM>
-__global__ __launch_bounds__(PJ_LANES) void proj_kernel(ProjArgs a) {
-  __shared__ pj_acc red[PJ_SEG][RB * OJ][64];
+// RB row blocks x OJ output slabs per wave, U 16-column blocks per trip; NW
+// waves per workgroup (PJ_SEG: a whole tile; PJ_SEG / 2: half a tile, the
+// two halves of a tile in adjacent workgroups).
+template <int RB, int OJ, int U, bool STREAM, int NW>
+__global__ __launch_bounds__(64 * NW) void proj_kernel(ProjArgs a) {
+  constexpr bool SPLIT = NW < PJ_SEG;
+  __shared__ pj_acc red[NW][RB * OJ][64];
   const int b = (int)xcd_contiguous(blockIdx.x, gridDim.x);
   const bool second = b >= a.p[0].blocks;
   const float *W = second ? a.p[1].W : a.p[0].W;
   float *y = second ? a.p[1].y : a.p[0].y;
   const int R = second ? a.p[1].R : a.p[0].R;
-  const int lb = second ? b - a.p[0].blocks : b;
+  const int lbh = second ? b - a.p[0].blocks : b;
+  const int lb = SPLIT ? lbh >> 1 : lbh;            // the tile
+  const int half = SPLIT ? lbh & 1 : 0;
   const int slab = lb / a.row_groups, rgp = lb - slab * a.row_groups;
   const int o0 = slab * 16 * OJ;
   const int64_t r0 = (int64_t)rgp * 16 * RB;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int sgm = NW * half + wave;                 // this wave's segment
   const int j = l & 15, kq = l >> 4;
   const int C = a.C;
   const int seg = C / PJ_SEG;
-  const int k0 = wave * seg + 4 * kq;
+  const int k0 = sgm * seg + 4 * kq;
 
   // one buffer resource over the workgroup's OJ packed slabs (< 2 GiB); the
   // 16-column block at column c of slab oj starts at float oj 16 C + 16 c
   const rsrc_t wr = buf_rsrc(W + (int64_t)o0 * C, 16 * OJ * C * 4);
   int wo[OJ];
 #pragma unroll
-  for (int oj = 0; oj < OJ; oj++) wo[oj] = (16 * oj * C + 16 * wave * seg + 4 * l) * 4;
+  for (int oj = 0; oj < OJ; oj++) wo[oj] = (16 * oj * C + 16 * sgm * seg + 4 * l) * 4;
   const float *xp[RB];
   bool xon[RB];
 #pragma unroll
@@ -1987,18 +2014,32 @@ __global__ __launch_bounds__(PJ_LANES) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int oj = 0; oj < OJ; oj++) red[wave][rb * OJ + oj][l] = acc[rb][oj];
   __syncthreads();
-  // fold the segment sums left to right; element e = (tile, lane, register t)
-  // is float e of every segment's block of LDS
+  // fold the segment sums: segments 0..3 left to right, 4..7 likewise, then
+  // their sum (or this half's fold added into y); element e = (tile, lane,
+  // register t) is float e of every segment's block of LDS
   constexpr int ELEMS = RB * OJ * 256;
   const float *redf = reinterpret_cast<const float *>(red);
-  for (int e = threadIdx.x; e < ELEMS; e += PJ_LANES) {
+  for (int e = threadIdx.x; e < ELEMS; e += 64 * NW) {
     const int tile = e >> 8, ll = (e >> 2) & 63, t = e & 3;
-    float sum = redf[e];
+    float h0 = redf[e];
 #pragma unroll
-    for (int w = 1; w < PJ_SEG; w++) sum = sum + redf[w * ELEMS + e];
+    for (int w = 1; w < PJ_SEG / 2; w++) h0 = h0 + redf[w * ELEMS + e];
+    float sum = h0;
+    if constexpr (!SPLIT) {
+      float h1 = redf[(PJ_SEG / 2) * ELEMS + e];
+#pragma unroll
+      for (int w = PJ_SEG / 2 + 1; w < PJ_SEG; w++) h1 = h1 + redf[w * ELEMS + e];
+      sum = h0 + h1;
+    }
     const int rb = tile / OJ, oj = tile - rb * OJ;
     const int64_t row = r0 + 16 * rb + 4 * (ll >> 4) + t;
-    if (row < a.rows) y[row * R + o0 + 16 * oj + (ll & 15)] = sum;
+    if (row < a.rows) {
+      float *dst = &y[row * R + o0 + 16 * oj + (ll & 15)];
+      if constexpr (SPLIT)
+        atomicAdd(dst, sum);               // the other half adds the other fold
+      else
+        *dst = sum;
+    }
   }
 }
 
@@ -2041,18 +2082,35 @@ static ProjShape proj_shape(int64_t rows, int R0, int R1) {
   return sh;
 }
 
+static bool proj_split(const ProjShape &sh, int64_t rows, int64_t tiles) {
+  return rows >= 2 && sh.rb == 1 && sh.oj == 1 && tiles < kPjSplitBelow;
+}
+
 int64_t proj_workgroups(int64_t rows, int R0, int R1) {
   const ProjShape sh = proj_shape(rows, R0, R1);
-  return proj_tiles(rows, R0, R1, sh.rb, sh.oj);
+  const int64_t tiles = proj_tiles(rows, R0, R1, sh.rb, sh.oj);
+  return proj_split(sh, rows, tiles) ? 2 * tiles : tiles;
 }
 
 template <int RB, int OJ, int U>
 static void launch_proj_t(const ProjArgs &a, bool stream, hipStream_t s) {
   const dim3 grid((unsigned)(a.p[0].blocks + a.p[1].blocks));
   if (RB < 4 || stream)       // see ld_w
-    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, true>), grid, dim3(PJ_LANES), 0, s, a);
+    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, true, PJ_SEG>), grid, dim3(PJ_LANES), 0, s, a);
   else
-    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, RB < 4>), grid, dim3(PJ_LANES), 0, s, a);
+    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, RB < 4, PJ_SEG>), grid, dim3(PJ_LANES), 0, s, a);
+}
+
+// The split shape (one row block, weights streamed): two half-tile
+// workgroups of PJ_SEG / 2 waves per tile, after a fill kernel zeroed y.
+template <int OJ, int U>
+static void launch_proj_split(const ProjArgs &a, hipStream_t s) {
+  const int64_t n0 = a.rows * a.p[0].R, n1 = a.p[1].W ? a.rows * a.p[1].R : 0;
+  hipLaunchKernelGGL(zero2_kernel, dim3((unsigned)((n0 + n1 + 255) / 256)), dim3(256), 0, s,
+                     a.p[0].y, n0, a.p[1].y, n1);
+  const dim3 grid((unsigned)(a.p[0].blocks + a.p[1].blocks));
+  hipLaunchKernelGGL((proj_kernel<1, OJ, U, true, PJ_SEG / 2>), grid, dim3(PJ_LANES / 2), 0, s,
+                     a);
 }
 
 // Weight packing (one launch per matrix, pure data movement): thread i
@@ -2088,6 +2146,15 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
   a.p[0] = ProjProblem{W0, y0, R0, R0 / (16 * sh.oj) * sh.row_groups};
   a.p[1] = ProjProblem{W1, y1, R1, W1 ? R1 / (16 * sh.oj) * sh.row_groups : 0};
   const bool stream = sh.row_groups == 1;
+  if (proj_split(sh, rows, a.p[0].blocks + a.p[1].blocks)) {
+    a.p[0].blocks *= 2;
+    a.p[1].blocks *= 2;
+    if (rows <= kPjU2Rows)
+      launch_proj_split<1, 2>(a, s);
+    else
+      launch_proj_split<1, 4>(a, s);
+    return (int)hipGetLastError();
+  }
   switch (sh.rb * 8 + sh.oj) {
     // one row block: up to 8 rows, 2 blocks per trip unless the grid has
     // >= kPjMinWgFew workgroups (out_proj at one row 28.7 -> 24.4 us;
@@ -2327,15 +2394,6 @@ __global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
   }
 }
 
-__global__ __launch_bounds__(256) void q4_zero_kernel(float *y0, int64_t n0, float *y1,
-                                                      int64_t n1) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n0)
-    y0[i] = 0.f;
-  else if (i - n0 < n1)
-    y1[i - n0] = 0.f;
-}
-
 // 4-bit packing: thread (group g, block b, lane l) writes output 64 g + l's
 // 16 bytes of block b and its scale.
 __global__ __launch_bounds__(256) void proj_q4_pack_kernel(const uint8_t *q, const uint16_t *scale,
@@ -2400,7 +2458,7 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   a.p[1] = Q4Problem{static_cast<const uint8_t *>(Wq1), y1, R1, Wq1 ? R1 / 64 * f : 0};
   if (split) {
     const int64_t n0 = rows * R0, n1 = Wq1 ? rows * R1 : 0;
-    hipLaunchKernelGGL(q4_zero_kernel, dim3((unsigned)((n0 + n1 + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(zero2_kernel, dim3((unsigned)((n0 + n1 + 255) / 256)), dim3(256), 0, s,
                        y0, n0, y1, n1);
   }
   switch (rows) {

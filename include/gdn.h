@@ -354,8 +354,9 @@ int gdn_proj_pack(const float *W, float *Wp, int32_t R, int32_t C, void *stream)
  * Each row's result is independent of the other rows in the call and of the
  * row count, bit for bit: one call over M rows equals M one-row calls.  The
  * sum over c runs in a fixed order of fp32 operations (8 equal segments of C,
- * each an ascending chain of matrix-core steps, then folded left to right),
- * so it differs from a left fold by rounding only.
+ * each an ascending chain of matrix-core steps; segments 0..3 folded left to
+ * right, so are 4..7, and the two sums added), so it differs from a left
+ * fold by rounding only.
  * Ownership: every buffer belongs to the caller; nothing is allocated.
  * Errors: GDN_EINVAL for a null or misaligned pointer, rows < 0, C <= 0,
  * R <= 0, or an output overlapping an input or the other output;

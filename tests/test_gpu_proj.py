@@ -164,6 +164,34 @@ def test_proj_two_products_share_one_launch():
     assert bits_equal(host(y1), host(gdn.proj(x, W1)))
 
 
+def test_proj_split_tiles_equal_whole_tiles():
+    """Launches of 2 to 16 rows with fewer than 512 tiles run each tile as
+    two half-workgroups that add their folds into a zeroed y; one-row calls
+    and a call over 24 rows run whole tiles.  Rows of the out_proj size (5120 outputs) and of a
+    paired launch (2048 + 1024 outputs) give the same bits either way (the
+    oracle checks of test_proj_parity run split shapes at 1, 5 and 16 rows)."""
+    say("proj split vs whole tiles")
+    rows, C = 24, 1024
+    x, W = operands(53, rows, 5120, C)
+    _, Wa = operands(57, 1, 2048, C)
+    _, Wb = operands(59, 1, 1024, C)
+    Wp, Wap, Wbp = gdn.proj_pack(W), gdn.proj_pack(Wa), gdn.proj_pack(Wb)
+    full = host(gdn.proj(x, Wp))
+    fa, fb = (host(t) for t in gdn.proj(x, Wap, Wbp))
+    for lo, hi in ((0, 1), (5, 6), (0, 2), (3, 11), (8, 24)):
+        xs = x[lo:hi].contiguous()
+        assert bits_equal(host(gdn.proj(xs, Wp)), np.ascontiguousarray(full[lo:hi])), (lo, hi)
+        ya, yb = gdn.proj(xs, Wap, Wbp)
+        assert bits_equal(host(ya), np.ascontiguousarray(fa[lo:hi])), (lo, hi)
+        assert bits_equal(host(yb), np.ascontiguousarray(fb[lo:hi])), (lo, hi)
+    # y is zeroed by the call itself: a second call into the same output gives
+    # the same bits
+    y = torch.full((4, 5120), 3.0, device="cuda")
+    gdn.proj(x[:4].contiguous(), Wp, y0=y)
+    gdn.proj(x[:4].contiguous(), Wp, y0=y)
+    assert bits_equal(host(y), np.ascontiguousarray(full[:4]))
+
+
 @pytest.mark.parametrize("R,C", [(16, 128), (48, 640), (10240, 5120), (5120, 6144)])
 def test_proj_pack_layout(R, C):
     """gdn_proj_pack is the documented permutation, bit for bit."""
