@@ -46,6 +46,18 @@ METRIC = "GDN head-steps/sec and achieved HBM GB/s (% of MI355X peak), 1 GPU"
 KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_recurrent_amd", "csrc", "gdn_kernels.hip")
 
 
+def frontend_bytes(B, dims, M=1, write_hist=True, dim=5120):
+    """Algorithmic HBM bytes of one front-end launch over M rows of B units:
+    x and the raw conv inputs per row, Wa and Wb, the conv weights, the
+    3-frame history read once (and written once), and the q, k, v, g, beta
+    outputs per row."""
+    vh, kh, kd, vd = dims
+    cd = synth.conv_dim_of(dims)
+    return (M * B * dim * 4 + 2 * vh * dim * 4 + M * B * cd * 4
+            + (2 if write_hist else 1) * B * 3 * cd * 4 + cd * 16
+            + M * B * (2 * kh * kd + vh * vd + 2 * vh) * 4)
+
+
 def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
     """Algorithmic HBM bytes of one head-step when `rows` steps share one
     state read and one state write (rows=1: a plain step)."""
@@ -61,9 +73,21 @@ def head_step_bytes(dims, rows=1, write_o=True, read_state=True):
 # that an edit elsewhere in the file does not invalidate its recorded
 # counters.
 _Q4_SECTION = b"// " + b"-" * 75 + b"\n// Dense layer projections with 4-bit weights"
+_RECUR_COMMON = (b"namespace gdn {", b"// ----- wide geometry -")
+_RECUR_LAUNCH = (b"// Launches of fewer than kWidemBelow tiles", b"// Streaming copy")
+_HEAD = (b"namespace gdn {", b"// Recurrence\n")
 HASH_SECTIONS = {
     "recur_wide_kernel": ((b"namespace gdn {", b"// ----- wide geometry, several steps"),
-                          (b"// Launches of fewer than kWidemBelow tiles", b"// Streaming copy")),
+                          _RECUR_LAUNCH),
+    "recur_widem_kernel": (_RECUR_COMMON,
+                           (b"// ----- wide geometry, several steps", b"// ----- deep geometry"),
+                           _RECUR_LAUNCH),
+    "recur_deep_kernel": (_RECUR_COMMON, (b"// ----- deep geometry", b"// ----- split geometry"),
+                          _RECUR_LAUNCH),
+    "recur_split_kernel": (_RECUR_COMMON, (b"// ----- split geometry", _RECUR_LAUNCH[0]),
+                           _RECUR_LAUNCH),
+    "copy_kernel": (_HEAD, (b"// Streaming copy", b"// Per-unit step counts")),
+    "fe_kernel": (_HEAD, (b"// Front end, kernel A", b"// y0[0..n0) = 0")),
     "proj_kernel": ((b"namespace gdn {", b"// Recurrence\n"),
                     (b"// Dense layer projections", _Q4_SECTION), (b"}  // namespace gdn", None)),
     "proj_q4_kernel": ((b"namespace gdn {", b"// Recurrence\n"), (_Q4_SECTION, None)),
@@ -124,6 +148,12 @@ def timed_graph(fn, steps, warmup):
     with torch.cuda.graph(graph):
         fn(0)
     return timed(lambda i: graph.replay(), steps, warmup)
+
+
+def graph_launch_s(fn, steps, per_graph=10):
+    """Seconds per call of fn when per_graph calls are captured as one HIP
+    graph and replayed: the device-paced launch time, without host gaps."""
+    return timed_graph(lambda i: [fn() for _ in range(per_graph)], steps, 1) / (steps * per_graph)
 
 
 def cpu_threads():
@@ -401,7 +431,6 @@ def bench_latency(cfg, steps, warmup, cpu):
 
     dt = timed(one, steps, warmup)
     launch_s = dt / (steps * T)
-    achieved = head_step_bytes(dims) * vh / launch_s / 1e9
     # the same T-step chain captured once as a HIP graph and replayed
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -412,13 +441,18 @@ def bench_latency(cfg, steps, warmup, cpu):
     with torch.cuda.graph(graph):
         one(0)
     dt_g = timed(lambda i: graph.replay(), steps, warmup)
+    # the kernel's roofline from the graph replay: device-paced launches
+    achieved = head_step_bytes(dims) * vh / (dt_g / (steps * T)) / 1e9
     # the same T steps as one gdn_step_m(M=T) call
     o_m = torch.empty((T, 1, vh, dims[3]), device="cuda")
     dt_m = timed(lambda i: gdn.step_m(S, *(inp[n] for n in NAMES), o=o_m), steps, warmup)
     res = dict(value=vh * T * steps / dt, ms_per_step=dt / steps * 1e3,
                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
-                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
-               extra=dict(us_per_call=round(launch_s * 1e6, 3),
+                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4),
+                             traffic=recorded_traffic("b1x1", None, kernel="recur_split_kernel")),
+               extra=dict(kernel="recur_split_kernel (one gdn_step per launch, graph replay)",
+                          algorithmic_bytes_per_launch=int(head_step_bytes(dims) * vh),
+                          us_per_call=round(launch_s * 1e6, 3),
                           us_per_step_graph_replay=round(dt_g / (steps * T) * 1e6, 3),
                           us_per_step_step_m=round(dt_m / (steps * T) * 1e6, 3),
                           note="3 MiB state stays in L2/MALL: latency figure, not an HBM claim"))
@@ -429,7 +463,11 @@ def bench_latency(cfg, steps, warmup, cpu):
     return res, dict(workload=cfg["name"], units=1, vh=vh, kd=dims[2], steps_per_iteration=T)
 
 
-def bench_verify(cfg, steps, warmup, cpu):
+def bench_verify(cfg, steps, warmup, cpu, only=None):
+    """The speculative cycle.  only = "step_m", "verify_m" or "commit" times
+    that one call alone (the same inputs; every commit runs the first set of
+    accepted counts from the current state), so that a profiler sees that
+    call's launches only."""
     dims = cfg["dims"]
     vh = dims[0]
     L = cfg["layers"]
@@ -460,6 +498,31 @@ def bench_verify(cfg, steps, warmup, cpu):
         gdn.verify_m(S, *args, o=o)
         gdn.commit(S, acc_dev[i % 8], *args, status=status)
 
+    if only is not None:
+        call = {"step_m": lambda i: gdn.step_m(S, *args, o=o),
+                "verify_m": lambda i: gdn.verify_m(S, *args, o=o),
+                "commit": lambda i: gdn.commit(S, acc_dev[0], *args, status=status)}[only]
+        dt = timed(call, steps, warmup)
+        mean_a = float(accs[0].mean()) if only == "commit" else float(np.mean([a.mean() for a in accs]))
+        tile = dims[2] * dims[3] * 4
+        rows = N * vh * (M if only != "commit" else mean_a)
+        b = N * vh * M * head_step_bytes(dims, rows=M)
+        if only == "verify_m":            # no state write
+            b -= N * vh * tile
+        elif only == "commit":
+            # a unit with accepted rows reads and writes its state and reads
+            # those rows (no output); a unit with none is not touched
+            row = head_step_bytes(dims, rows=1, write_o=False) - 2 * tile
+            b = vh * float(((accs[0] > 0) * 2 * tile + accs[0] * row).sum())
+        achieved = b / (dt / steps) / 1e9
+        res = dict(value=rows * steps / dt, ms_per_step=dt / steps * 1e3,
+                   roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
+                                 unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4),
+                                 traffic=None),
+                   extra=dict(only=only, algorithmic_bytes_per_launch=int(b),
+                              kernel="recur_deep_kernel", mean_accepted=mean_a))
+        return res, dict(workload=cfg["name"], units=N, M=M, vh=vh, kd=dims[2], only=only)
+
     S_start = S.clone() if cpu else None
     dt = timed(one, steps, warmup)
     dt_unfused = timed(one_unfused, steps, 1)
@@ -471,8 +534,12 @@ def bench_verify(cfg, steps, warmup, cpu):
     mean_a = float(np.mean([a.mean() for a in accs]))
     res = dict(value=N * vh * M * steps / dt, ms_per_step=dt / steps * 1e3,
                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
-                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
-               extra=dict(step_m_ms=round(dt_m / steps * 1e3, 4), mean_accepted=mean_a,
+                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4),
+                             traffic=recorded_traffic("b32x48_m8_step_m", None,
+                                                      kernel="recur_deep_kernel")),
+               extra=dict(kernel="recur_deep_kernel (gdn_step_m alone)",
+                          algorithmic_bytes_per_launch=int(bytes_m),
+                          step_m_ms=round(dt_m / steps * 1e3, 4), mean_accepted=mean_a,
                           cycle_ms_separate_mark=round(dt_unfused / steps * 1e3, 4),
                           cycle_ms_verify_commit=round(dt_vc / steps * 1e3, 4),
                           value_counts="drafted head-steps per second of the full cycle"))
@@ -546,14 +613,27 @@ def bench_frontend(cfg, steps, warmup, cpu):
     S_start, hist_start = (S.clone(), hist.clone()) if cpu else (None, None)
     dt = timed(one, steps, warmup)
     cd = synth.conv_dim_of(dims)
-    fe_bytes = (B * 5120 * 4 + 2 * vh * 5120 * 4 + B * cd * 4 + 2 * B * 3 * cd * 4
-                + cd * 16 + B * (2 * kh * kd + vh * vd + 2 * vh) * 4)
-    total = B * vh * head_step_bytes(dims) + fe_bytes
-    achieved = total / (dt / steps) / 1e9
+    fe_bytes = frontend_bytes(B, dims)
+    step_bytes = B * vh * head_step_bytes(dims)
+    chain = (step_bytes + fe_bytes) / (dt / steps) / 1e9
+    # each kernel alone, device-paced: the step (the dominant kernel) and the front end
+    t_step = graph_launch_s(lambda: gdn.step(S, out["q"], out["k"], out["v"], out["g"],
+                                             out["beta"], o=o), steps)
+    t_fe = graph_launch_s(lambda: gdn.frontend(fe["x"][0], w["Wa"], w["Wb"], w["A_log"],
+                                               w["dt_bias"], fe["xc_raw"][0], hist, w["conv_w"],
+                                               dims, out=out), steps)
+    achieved = step_bytes / t_step / 1e9
     res = dict(value=B * vh * steps / dt, ms_per_step=dt / steps * 1e3,
                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
-                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=None),
-               extra=dict(frontend_bytes=fe_bytes,
+                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4),
+                             traffic=recorded_traffic("b128x1", None)),
+               extra=dict(kernel="recur_wide_kernel (gdn_step alone, graph replay)",
+                          algorithmic_bytes_per_launch=int(step_bytes),
+                          step_us=round(t_step * 1e6, 2),
+                          frontend_us=round(t_fe * 1e6, 2),
+                          frontend_bytes_per_launch=fe_bytes,
+                          frontend_GBps=round(fe_bytes / t_fe / 1e9, 1),
+                          chain_GBps=round(chain, 1),
                           note="384 MiB state is 1.5x the MALL: partly cache-resident"))
     if cpu:
         res["extra"]["parity_all_units"] = frontend_parity(S_start, hist_start, w, fe, dims, T)
@@ -646,10 +726,26 @@ def bench_verify_frontend(cfg, steps, warmup, cpu):
 
     dt = timed(one, steps, warmup)
     dt_vc = timed(one_verify_commit, steps, 1)
+    # the M-step recurrence and the M-row front end alone, for the rooflines
+    t_m = graph_launch_s(lambda: gdn.step_m(S, *args, o=o), steps)
+    bytes_m = B * vh * M * head_step_bytes(dims, rows=M)
+    achieved = bytes_m / t_m / 1e9
+    t_fe = graph_launch_s(lambda: gdn.frontend_m(fe["x"], w["Wa"], w["Wb"], w["A_log"],
+                                                 w["dt_bias"], fe["xc_raw"], hist, w["conv_w"],
+                                                 dims, out=rows), steps)
+    fe_b = frontend_bytes(B, dims, M=M)
     res = dict(value=B * vh * M * steps / dt, ms_per_step=dt / steps * 1e3,
-               roofline=dict(bound="hbm", achieved=None, peak=PEAK_HBM_GBPS, unit="GB/s",
-                             frac=None, traffic=None),
+               roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
+                             unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4),
+                             traffic=recorded_traffic("b128x1_m8_step_m", None,
+                                                      kernel="recur_deep_kernel")),
                extra=dict(value_counts="drafted head-steps per second of the full cycle",
+                          kernel="recur_deep_kernel (gdn_step_m alone, graph replay)",
+                          step_m_us=round(t_m * 1e6, 2),
+                          algorithmic_bytes_per_launch=int(bytes_m),
+                          frontend_m_us=round(t_fe * 1e6, 2),
+                          frontend_bytes_per_launch=int(fe_b),
+                          frontend_GBps=round(fe_b / t_fe / 1e9, 1),
                           cycle_ms_verify_commit=round(dt_vc / steps * 1e3, 4),
                           note="403 MB state: 1.6x the MALL, partly cache-resident"))
     return res, dict(workload=cfg["name"], units=B, M=M, vh=vh, kd=kd, conv_dim=cd,
@@ -861,6 +957,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=("step_m", "verify_m", "commit"),
+                    help="config 2: time this one call alone (for a profiler)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the library and this benchmark run on one GPU; --gpus {args.gpus} is not "
@@ -877,7 +975,13 @@ def main():
               6: bench_verify_frontend, 8: bench_layer, 9: bench_layer,
               10: bench_layer_verify, 11: bench_layer,
               12: bench_layer_verify}.get(args.config, bench_decode)
-    res, config = runner(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
+    if args.only is not None and args.config != 2:
+        print("bench.py: --only applies to --config 2", file=sys.stderr)
+        sys.exit(2)
+    if args.only is not None:
+        res, config = bench_verify(cfg, args.steps, args.warmup, False, only=args.only)
+    else:
+        res, config = runner(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
     line = dict(metric=METRIC, value=round(res["value"], 1), unit="head-steps/s", n_gpus=1,
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(res["ms_per_step"], 5),
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",

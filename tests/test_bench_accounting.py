@@ -58,3 +58,27 @@ def test_projection_shapes_reproduce_pages_weight_bytes():
     for block in (16, 64):                          # other block sizes miss the printed size
         other = large // 2 + (large // block) * 2 + 4 * (2 * vh * dim + cd * 4)
         assert round(other / 2**20, 1) != gold["q4_weights_per_layer_MiB"]
+
+
+def test_frontend_bytes_written_out():
+    # 128 rows of x (5120) and raw conv inputs (10240), Wa and Wb (48 x 5120
+    # each), conv weights (10240 x 4 taps), the 3-frame history read and
+    # written, and the q, k (16 x 128 each), v (48 x 128), g, beta outputs
+    B, cd, dim = 128, 10240, 5120
+    want = (B * dim + 2 * 48 * dim + B * cd + 2 * B * 3 * cd + cd * 4
+            + B * (2 * 16 * 128 + 48 * 128 + 2 * 48)) * 4
+    assert bench.frontend_bytes(B, synth.DIMS128) == want == 46743552
+    # M rows share one history read; frontend_verify_m writes no history
+    m8 = bench.frontend_bytes(B, synth.DIMS128, M=8, write_hist=False)
+    assert m8 == (8 * B * dim + 2 * 48 * dim + 8 * B * cd + B * 3 * cd + cd * 4
+                  + 8 * B * (2 * 16 * 128 + 48 * 128 + 2 * 48)) * 4
+
+
+def test_m_step_variants_bytes():
+    # verify_m reads the state once and writes none; a commit touches only
+    # units with accepted rows (read + write) and reads their accepted rows
+    tile = 128 * 128 * 4
+    step_m = bench.head_step_bytes(synth.DIMS128, rows=8) * 8
+    assert abs(step_m - (2 * tile + 8 * (512 + 512 + 8 + 1024 / 3))) < 1e-6
+    row_no_o = bench.head_step_bytes(synth.DIMS128, write_o=False) - 2 * tile
+    assert abs(row_no_o - (512 + 8 + 1024 / 3)) < 1e-9
