@@ -930,9 +930,11 @@ def bench_layer_verify(cfg, steps, warmup, cpu):
     wb = 9 / 16 if q4 else 4
     in_bytes = int((cd + vh * vd) * dim * wb) + rows * dim * 4 + rows * (cd + vh * vd) * 4
     t_in = dt_in / (steps * L)
-    roof = dict(bound="hbm", achieved=round(in_bytes / t_in / 1e9, 1), peak=PEAK_HBM_GBPS,
-                unit="GB/s", frac=round(in_bytes / t_in / 1e9 / PEAK_HBM_GBPS, 4), traffic=None)
     kname = "proj_q4_kernel" if q4 else "proj_kernel"
+    key = f"layer_q4_verify_b{B}m{M}" if q4 else f"layer_verify_b{B}m{M}"
+    roof = dict(bound="hbm", achieved=round(in_bytes / t_in / 1e9, 1), peak=PEAK_HBM_GBPS,
+                unit="GB/s", frac=round(in_bytes / t_in / 1e9 / PEAK_HBM_GBPS, 4),
+                traffic=recorded_traffic(key, in_bytes, kernel=kname))
     desc = "gdn_proj_q4" if q4 else "gdn_proj"
     res = dict(value=B * vh * M * L * steps / dt_g, ms_per_step=dt_g / steps * 1e3, roofline=roof,
                extra=dict(value_counts="drafted head-steps per second of the full cycle",
@@ -950,6 +952,40 @@ def bench_layer_verify(cfg, steps, warmup, cpu):
                            f"{desc}(W_out) + gdn_commit per layer")
 
 
+RUNNERS = {0: "bench_latency", 2: "bench_verify", 3: "bench_frontend",
+           6: "bench_verify_frontend", 8: "bench_layer", 9: "bench_layer",
+           10: "bench_layer_verify", 11: "bench_layer", 12: "bench_layer_verify"}
+
+
+def runner_of(config):
+    return globals()[RUNNERS.get(config, "bench_decode")]
+
+
+def other_workloads(steps, warmup, skip):
+    """Every other workload, timed the same way with fewer steps (no CPU
+    baseline, no parity pass), so that one default run measures all of them:
+    the result line of each, without its config and cpu fields."""
+    out = {}
+    for c in sorted(synth.WORKLOADS):
+        if c == skip:
+            continue
+        cfg = dict(synth.WORKLOADS[c])
+        cfg["id"] = c
+        torch.cuda.synchronize()
+        t0 = time.time()
+        res, config = runner_of(c)(cfg, steps, warmup, False)
+        torch.cuda.synchronize()
+        out[str(c)] = dict(workload=config["workload"], value=round(res["value"], 1),
+                           ms_per_step=round(res["ms_per_step"], 5), roofline=res["roofline"],
+                           extra={k: v for k, v in res.get("extra", {}).items()
+                                  if not isinstance(v, dict)},
+                           wall_s=round(time.time() - t0, 2))
+        torch.cuda.empty_cache()
+        print(f"bench.py: workload {c} done ({out[str(c)]['wall_s']} s)", file=sys.stderr,
+              flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -959,6 +995,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=("step_m", "verify_m", "commit"),
                     help="config 2: time this one call alone (for a profiler)")
+    ap.add_argument("--other-steps", type=int, default=20,
+                    help="the default workload also times every other workload with this "
+                         "many steps (0: skip them)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the library and this benchmark run on one GPU; --gpus {args.gpus} is not "
@@ -971,10 +1010,7 @@ def main():
     gdn.lib()
     cfg = dict(synth.WORKLOADS[args.config])
     cfg["id"] = args.config
-    runner = {0: bench_latency, 2: bench_verify, 3: bench_frontend,
-              6: bench_verify_frontend, 8: bench_layer, 9: bench_layer,
-              10: bench_layer_verify, 11: bench_layer,
-              12: bench_layer_verify}.get(args.config, bench_decode)
+    runner = runner_of(args.config)
     if args.only is not None and args.config != 2:
         print("bench.py: --only applies to --config 2", file=sys.stderr)
         sys.exit(2)
@@ -989,6 +1025,10 @@ def main():
     if "cpu_baseline" in res:
         line["cpu_baseline"] = res["cpu_baseline"]
     line["extra"] = res.get("extra", {})
+    if args.config == 1 and args.only is None and args.other_steps > 0:
+        # after the headline measurement, so that it runs on a fresh device
+        torch.cuda.empty_cache()
+        line["extra"]["workloads"] = other_workloads(args.other_steps, 2, skip=1)
     line["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(line), flush=True)
 
