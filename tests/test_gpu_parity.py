@@ -744,10 +744,16 @@ def test_step_gated_parity(orc, dims, M):
     S_h = host(S)
     out = gdn.step_gated(S, *(inp[n] for n in NAMES), z, w, eps)
     if M == 1:
-        gdn.step(S_plain, *(inp[n][0] for n in NAMES))
+        o_plain = gdn.step(S_plain, *(inp[n][0] for n in NAMES)).unsqueeze(0)
     else:
-        gdn.step_m(S_plain, *(inp[n] for n in NAMES))
+        o_plain = gdn.step_m(S_plain, *(inp[n] for n in NAMES))
     assert bits_equal(host(S), host(S_plain))
+    # the epilogue alone, at o's own bound: the gated kernel forms the same
+    # raw o as the ungated call (the same canonical tree), so its output is
+    # the oracle's gated norm of that o up to the norm's own rounding
+    g_own = np.zeros((M, N, vh, vd), np.float32)
+    orc.gated_norm(host(o_plain), host(z), host(w), eps, g_own)
+    assert_close(host(out), g_own, "gated epilogue on the GPU's o", rel=1e-5, floor=1e-6)
     o_ref = np.zeros((M, N, vh, vd), np.float32)
     orc.gdn_step_m(S_h, *(host(inp[n]) for n in NAMES), o_ref, M, dims)
     g_ref = np.zeros_like(o_ref)
@@ -788,6 +794,12 @@ def test_verify_m_gated_equals_step_gated(orc, dims, M):
     orc.gdn_step_m(S0.copy(), *(host(inp[n]) for n in NAMES), o_ref, M, dims)
     g_ref, g_floor = ref_gated(orc, o_ref, host(z), host(w), 1e-6)
     assert_close(host(out_v), g_ref, "verify_m_gated out", floor=g_floor)
+    # the epilogue at o's own bound, on the GPU's raw o of the same rows
+    o_gpu = gdn.verify_m(S, *(inp[n] for n in NAMES))
+    g_own = np.zeros_like(o_ref)
+    orc.gated_norm(host(o_gpu), host(z), host(w), 1e-6, g_own)
+    assert_close(host(out_v), g_own, "verify_m_gated epilogue on the GPU's o", rel=1e-5,
+                 floor=1e-6)
 
 
 @pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
