@@ -277,16 +277,39 @@ static __device__ __forceinline__ void chunk_load(ChunkRegs<KD, LANES, GATED> &c
                                                   const RecurArgs &a, int t, int64_t unit,
                                                   int head, int hh, int m0, int nr) {
   using C = ChunkRegs<KD, LANES, GATED>;
+  if constexpr (LANES % KD == 0) {
+    // element i of this lane is row t / KD + i LANES / KD, column t % KD:
+    // one base address per array and a uniform row stride
+    constexpr int RPI = LANES / KD;
+    const int col = t % KD, r0 = t / KD;
+    const int64_t urow = (int64_t)(m0 + r0) * a.n_units + unit;
+    const float *qp = a.q + (urow * a.kh + hh) * KD + col;
+    const float *kp = a.k + (urow * a.kh + hh) * KD + col;
+    const float *vp = a.v + (urow * a.vh + head) * KD + col;
+    const float *zp = GATED ? a.z + (urow * a.vh + head) * KD + col : nullptr;
+    const int64_t sqk = (int64_t)RPI * a.n_units * a.kh * KD;
+    const int64_t sv = (int64_t)RPI * a.n_units * a.vh * KD;
 #pragma unroll
-  for (int i = 0; i < C::P; i++) {
-    const int e = t + i * LANES;
-    const int r = e / KD, col = e % KD;
-    if (e < C::E && r < nr) {
-      const int64_t urow = (int64_t)(m0 + r) * a.n_units + unit;
-      c.q[i] = a.q[(urow * a.kh + hh) * KD + col];
-      c.k[i] = a.k[(urow * a.kh + hh) * KD + col];
-      c.v[i] = a.v[(urow * a.vh + head) * KD + col];
-      if constexpr (GATED) c.z[i] = a.z[(urow * a.vh + head) * KD + col];
+    for (int i = 0; i < C::P; i++) {
+      if (t + i * LANES < C::E && r0 + RPI * i < nr) {
+        c.q[i] = qp[i * sqk];
+        c.k[i] = kp[i * sqk];
+        c.v[i] = vp[i * sv];
+        if constexpr (GATED) c.z[i] = zp[i * sv];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::P; i++) {
+      const int e = t + i * LANES;
+      const int r = e / KD, col = e % KD;
+      if (e < C::E && r < nr) {
+        const int64_t urow = (int64_t)(m0 + r) * a.n_units + unit;
+        c.q[i] = a.q[(urow * a.kh + hh) * KD + col];
+        c.k[i] = a.k[(urow * a.kh + hh) * KD + col];
+        c.v[i] = a.v[(urow * a.vh + head) * KD + col];
+        if constexpr (GATED) c.z[i] = a.z[(urow * a.vh + head) * KD + col];
+      }
     }
   }
   if (t < 2 * MC) {
@@ -365,10 +388,13 @@ struct TileIdx {
 static __device__ __forceinline__ TileIdx tile_index(const RecurArgs &a, int kdkd, int tpw = 1,
                                                      int sub = 0) {
   TileIdx x;
-  const int64_t tile = xcd_contiguous(blockIdx.x, gridDim.x) * tpw + sub;
-  x.unit = tile / a.vh;
-  x.head = (int)(tile - x.unit * a.vh);
-  x.hh = x.head / (a.vh / a.kh);
+  // 32-bit: a launch has fewer than 2^32 work-items and at least 64 per
+  // tile, so tile indices stay below 2^26
+  const uint32_t tile = (uint32_t)(xcd_contiguous(blockIdx.x, gridDim.x) * tpw + sub);
+  const uint32_t unit = tile / (uint32_t)a.vh;
+  x.unit = unit;
+  x.head = (int)(tile - unit * (uint32_t)a.vh);
+  x.hh = (int)((uint32_t)x.head / (uint32_t)(a.vh / a.kh));
   x.steps = a.steps ? a.steps[x.unit] : a.M;
   if (x.steps < 0 || x.steps > a.M) {   // device-supplied counts: refuse the unit
     if (a.status != nullptr && threadIdx.x == 0) a.status[0] = 1;
