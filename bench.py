@@ -1004,6 +1004,9 @@ def main():
               "supported (every state unit is independent, so G GPUs would each run this "
               "same kernel on N/G units with no communication).", file=sys.stderr)
         sys.exit(2)
+    if args.only is not None and args.config != 2:
+        print("bench.py: --only applies to --config 2", file=sys.stderr)
+        sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py: no HIP device visible", file=sys.stderr)
         sys.exit(1)
@@ -1011,9 +1014,6 @@ def main():
     cfg = dict(synth.WORKLOADS[args.config])
     cfg["id"] = args.config
     runner = runner_of(args.config)
-    if args.only is not None and args.config != 2:
-        print("bench.py: --only applies to --config 2", file=sys.stderr)
-        sys.exit(2)
     if args.only is not None:
         res, config = bench_verify(cfg, args.steps, args.warmup, False, only=args.only)
     else:
