@@ -68,13 +68,15 @@ def operands(seed, rows, R, C):
 
 
 @pytest.mark.parametrize("rows,R,C", [(1, 64, 128), (5, 48, 640), (16, 256, 1024),
-                                      (17, 128, 512), (40, 96, 1152), (64, 512, 5120),
-                                      (70, 160, 6144), (150, 4096, 256), (48, 4096, 384)])
+                                      (17, 128, 512), (20, 48, 256), (40, 96, 1152),
+                                      (64, 512, 5120), (70, 160, 6144), (150, 4096, 256),
+                                      (48, 4096, 384)])
 def test_proj_parity(orc, rows, R, C):
     """Every tile shape against the oracle: 1, 2 and 4 row blocks, 1, 2 and 4
     output slabs per wave, one and several row groups (150 x 4096: 4 row
     blocks over 3 row groups, the weights read through L2), a ragged last row
-    group, segments with and without a tail."""
+    group, segments with and without a tail, and the two-workgroup split over
+    one (5 x 48) and two row groups (20 x 48: one row block per tile)."""
     say(f"proj rows={rows} R={R} C={C}")
     x, W = operands(20 + rows, rows, R, C)
     y = gdn.proj(x, gdn.proj_pack(W))
@@ -184,6 +186,14 @@ def test_proj_split_tiles_equal_whole_tiles():
         ya, yb = gdn.proj(xs, Wap, Wbp)
         assert bits_equal(host(ya), np.ascontiguousarray(fa[lo:hi])), (lo, hi)
         assert bits_equal(host(yb), np.ascontiguousarray(fb[lo:hi])), (lo, hi)
+    # the split over two row groups (20 rows, 48 outputs: one row block per
+    # tile) against the split over five (the same rows inside a 70-row call)
+    _, W48 = operands(61, 1, 48, C)
+    W48p = gdn.proj_pack(W48)
+    x20 = x[:20].contiguous()
+    y20 = host(gdn.proj(x20, W48p))
+    y70 = host(gdn.proj(torch.cat([x20] * 4)[:70].contiguous(), W48p))
+    assert bits_equal(y20, np.ascontiguousarray(y70[:20]))
     # y is zeroed by the call itself: a second call into the same output gives
     # the same bits
     y = torch.full((4, 5120), 3.0, device="cuda")
