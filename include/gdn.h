@@ -356,7 +356,10 @@ int gdn_proj_pack(const float *W, float *Wp, int32_t R, int32_t C, void *stream)
  * sum over c runs in a fixed order of fp32 operations (8 equal segments of C,
  * each an ascending chain of matrix-core steps; segments 0..3 folded left to
  * right, so are 4..7, and the two sums added), so it differs from a left
- * fold by rounding only.
+ * fold by rounding only.  Launches of 2 to 16 rows with few output tiles
+ * first zero y0 (and y1), then add two partial folds into each element, so
+ * y0 and y1 hold intermediate values until the call's work completes on the
+ * stream.
  * Ownership: every buffer belongs to the caller; nothing is allocated.
  * Errors: GDN_EINVAL for a null or misaligned pointer, rows < 0, C <= 0,
  * R <= 0, or an output overlapping an input or the other output;
