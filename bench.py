@@ -973,8 +973,15 @@ def other_workloads(steps, warmup, skip):
         cfg["id"] = c
         torch.cuda.synchronize()
         t0 = time.time()
-        res, config = runner_of(c)(cfg, steps, warmup, False)
-        torch.cuda.synchronize()
+        try:
+            res, config = runner_of(c)(cfg, steps, warmup, False)
+            torch.cuda.synchronize()
+        except Exception as e:  # noqa: BLE001 - recorded; the headline line must still print
+            out[str(c)] = dict(workload=cfg["name"], error=f"{type(e).__name__}: {e}")
+            print(f"bench.py: workload {c} failed: {out[str(c)]['error']}", file=sys.stderr,
+                  flush=True)
+            torch.cuda.empty_cache()
+            continue
         out[str(c)] = dict(workload=config["workload"], value=round(res["value"], 1),
                            ms_per_step=round(res["ms_per_step"], 5), roofline=res["roofline"],
                            extra={k: v for k, v in res.get("extra", {}).items()
