@@ -1879,6 +1879,7 @@ constexpr int64_t kPjMinWg = 128;
 constexpr int64_t kPjMinWg1 = 256;
 constexpr int64_t kPjU2Rows = 8;        // few rows: up to this many
 constexpr int64_t kPjMinWgFew = 1024;
+constexpr int64_t kPjStagedMin = 256;   // 4 x 4 tiles: staged fold from this many
 
 struct ProjProblem {
   const float *W;
@@ -1910,11 +1911,14 @@ static __device__ __forceinline__ f4 ld_w(rsrc_t r, int voff) {
 
 // RB row blocks x OJ output slabs per wave, U 16-column blocks per trip; NW
 // waves per workgroup (PJ_SEG: a whole tile; PJ_SEG / 2: half a tile, the
-// two halves of a tile in adjacent workgroups).
-template <int RB, int OJ, int U, bool STREAM, int NW>
+// two halves of a tile in adjacent workgroups).  STAGED (whole tiles only)
+// folds the segment sums through two LDS buffers instead of one block per
+// segment: 32 KiB instead of 128 KiB for a 4 x 4 tile.
+template <int RB, int OJ, int U, bool STREAM, int NW, bool STAGED = false>
 __global__ __launch_bounds__(64 * NW) void proj_kernel(ProjArgs a) {
   constexpr bool SPLIT = NW < PJ_SEG;
-  __shared__ pj_acc red[NW][RB * OJ][64];
+  static_assert(!(SPLIT && STAGED), "a half tile folds in one buffer");
+  __shared__ pj_acc red[STAGED ? 2 : NW][RB * OJ][64];
   const int b = (int)xcd_contiguous(blockIdx.x, gridDim.x);
   const bool second = b >= a.p[0].blocks;
   const float *W = second ? a.p[1].W : a.p[0].W;
@@ -2035,6 +2039,53 @@ __global__ __launch_bounds__(64 * NW) void proj_kernel(ProjArgs a) {
                                                              0, 0, 0);
   }
 
+  if constexpr (STAGED) {
+    // wave 0 left-folds segments 1..3 into its own sum, wave PJ_SEG / 2
+    // segments 5..7 into its own, one segment per round through buffer 0 or
+    // 1; then wave 0 adds the second fold and stores (the same operations, in
+    // the same order, as the one-buffer fold below)
+    constexpr int H = PJ_SEG / 2;
+#pragma unroll
+    for (int jj = 1; jj < H; jj++) {
+      if (wave == jj || wave == H + jj) {
+        const int bsel = wave == jj ? 0 : 1;
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+          for (int oj = 0; oj < OJ; oj++) red[bsel][rb * OJ + oj][l] = acc[rb][oj];
+      }
+      __syncthreads();
+      if (wave == 0 || wave == H) {
+        const int bsel = wave == 0 ? 0 : 1;
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+          for (int oj = 0; oj < OJ; oj++) acc[rb][oj] = acc[rb][oj] + red[bsel][rb * OJ + oj][l];
+      }
+      __syncthreads();
+    }
+    if (wave == H) {
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+        for (int oj = 0; oj < OJ; oj++) red[1][rb * OJ + oj][l] = acc[rb][oj];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+        for (int oj = 0; oj < OJ; oj++) {
+          const pj_acc sum = acc[rb][oj] + red[1][rb * OJ + oj][l];
+#pragma unroll
+          for (int t = 0; t < 4; t++) {
+            const int64_t row = r0 + 16 * rb + 4 * (l >> 4) + t;
+            if (row < a.rows) y[row * R + o0 + 16 * oj + (l & 15)] = sum[t];
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; rb++)
 #pragma unroll
@@ -2118,13 +2169,15 @@ int64_t proj_workgroups(int64_t rows, int R0, int R1) {
   return proj_split(sh, rows, tiles) ? 2 * tiles : tiles;
 }
 
-template <int RB, int OJ, int U>
+template <int RB, int OJ, int U, bool STAGED = false>
 static void launch_proj_t(const ProjArgs &a, bool stream, hipStream_t s) {
   const dim3 grid((unsigned)(a.p[0].blocks + a.p[1].blocks));
   if (RB < 4 || stream)       // see ld_w
-    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, true, PJ_SEG>), grid, dim3(PJ_LANES), 0, s, a);
+    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, true, PJ_SEG, STAGED>), grid, dim3(PJ_LANES), 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, RB < 4, PJ_SEG>), grid, dim3(PJ_LANES), 0, s, a);
+    hipLaunchKernelGGL((proj_kernel<RB, OJ, U, RB < 4, PJ_SEG, STAGED>), grid, dim3(PJ_LANES), 0,
+                       s, a);
 }
 
 // The split shape (one row block, weights streamed): two half-tile
@@ -2203,7 +2256,15 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
     case 2 * 8 + 4: launch_proj_t<2, 4, 2>(a, true, s); break;
     case 4 * 8 + 1: launch_proj_t<4, 1, 4>(a, stream, s); break;
     case 4 * 8 + 2: launch_proj_t<4, 2, 4>(a, stream, s); break;
-    default: launch_proj_t<4, 4, 2>(a, stream, s); break;
+    // 4 x 4: the staged fold measured faster with a workgroup or more per CU
+    // (in_proj at 64 rows, 256 tiles: 119.7 -> 114.3 us; 128 rows: 206.6 ->
+    // 203.6), slower below (out_proj at 128 rows, 160 tiles: 116.6 -> 117.2)
+    default:
+      if (a.p[0].blocks + a.p[1].blocks >= kPjStagedMin)
+        launch_proj_t<4, 4, 2, true>(a, stream, s);
+      else
+        launch_proj_t<4, 4, 2>(a, stream, s);
+      break;
   }
   return (int)hipGetLastError();
 }
