@@ -17,6 +17,7 @@ constexpr int32_t kMaxHeads = 4096;
 constexpr int32_t kSlabMagic = 0x47444e53;  // "GDNS"
 constexpr int64_t kAlign = 256;
 constexpr int32_t kConvK = 4;       // conv kernel width the kernels are built for
+constexpr int64_t kMaxHistFloats = (int64_t)1 << 24;   // per unit: (ck - 1) x conv_dim
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -37,11 +38,16 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
 
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Launch-size limit: the grid of the recurrence kernel (tiles x lanes
-// work-items) must stay below 2^32.
-bool grid_fits(int64_t n_units, int32_t vh, int32_t kd) {
-  const int64_t tiles = n_units * vh;
-  return tiles <= (int64_t)0xFFFFFFFF / gdn::recur_lanes(kd);
+// Launch-size limit: the grid of a recurrence launch must stay below 2^32
+// work-items.  No geometry gives a tile more lanes than recur_lanes(kd), and
+// a history replay appends, per unit, conv_dim / 4 lanes rounded up to a
+// workgroup of at most 1024 lanes.
+bool grid_fits(int64_t n_units, int32_t vh, int32_t kd, int32_t conv_dim = 0) {
+  const int64_t lim = 0xFFFFFFFF;
+  if (n_units > lim / vh) return false;
+  int64_t items = n_units * vh * gdn::recur_lanes(kd);
+  if (conv_dim > 0) items += n_units * ((int64_t)conv_dim / 4 + 1023);
+  return items <= lim;
 }
 
 int enq(int hip_rc) { return hip_rc == 0 ? GDN_OK : GDN_EDEVICE; }
@@ -130,6 +136,10 @@ int64_t gdn_slab_bytes(int64_t n_units, int32_t vh, int32_t kh, int32_t kd, int3
   int rc = check_dims(vh, kh, kd, vd);
   if (rc) return rc;
   if (n_units < 1 || hist_floats_per_unit < 0 || hist_floats_per_unit % 4 != 0) return GDN_EINVAL;
+  // a slab's units are replayed in one recurrence launch, so they obey its
+  // grid limit; both bounds also keep the byte counts below far from 2^63
+  if (!grid_fits(n_units, vh, kd) || hist_floats_per_unit > kMaxHistFloats)
+    return GDN_EUNSUPPORTED;
   const int64_t s_bytes = align_up(n_units * vh * (int64_t)kd * vd * 4);
   const int64_t h_bytes = align_up(n_units * hist_floats_per_unit * 4);
   const int64_t a_bytes = align_up(n_units * 4);
@@ -271,6 +281,7 @@ int rollback_impl(gdn_slab *slab, float *S, float *hist, const float *q, const f
     if (overlaps(hist, N * slab->hist_floats * 4, slab->dev, slab->bytes)) return GDN_EINVAL;
     if (any && !ptr_ok(xc_raw)) return GDN_EINVAL;
   }
+  if (!grid_fits(N, vh, kd, hist != nullptr ? conv_dim : 0)) return GDN_EUNSUPPORTED;
   if (static_counts && N > gdn::kStaticCountsMax) return GDN_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   // accepted[] reaches the count area through kernel arguments, so the host
@@ -331,14 +342,18 @@ int frontend_impl(const float *x, const float *Wa, const float *Wb, const float 
   const int64_t qkb = rows * kh * kd * 4, vb = rows * vh * vd * 4, gb = rows * vh * 4;
   const void *outs[5] = {q, k, v, g, beta};
   const int64_t ob[5] = {qkb, qkb, vb, gb, gb};
+  const int64_t wb = (int64_t)vh * dim * 4, cwb = (int64_t)conv_dim * ck * 4, hb1 = vh * 4;
+  const void *ins[7] = {x, xc_raw, Wa, Wb, conv_w, A_log, dt_bias};
+  const int64_t ib[7] = {xb, rawb, wb, wb, cwb, hb1, hb1};
   for (int i = 0; i < 5; i++) {
-    if (overlaps(outs[i], ob[i], hist, hb) || overlaps(outs[i], ob[i], xc_raw, rawb) ||
-        overlaps(outs[i], ob[i], x, xb))
-      return GDN_EINVAL;
+    if (overlaps(outs[i], ob[i], hist, hb)) return GDN_EINVAL;
+    for (int j = 0; j < 7; j++)
+      if (overlaps(outs[i], ob[i], ins[j], ib[j])) return GDN_EINVAL;
     for (int j = i + 1; j < 5; j++)
       if (overlaps(outs[i], ob[i], outs[j], ob[j])) return GDN_EINVAL;
   }
-  if (overlaps(hist, hb, xc_raw, rawb)) return GDN_EINVAL;
+  for (int j = 0; j < 7; j++)
+    if (overlaps(hist, hb, ins[j], ib[j])) return GDN_EINVAL;
   return enq(gdn::launch_frontend(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g,
                                   beta, B, M, dim, conv_dim, vh, kh, kd, write_hist,
                                   (hipStream_t)stream));
@@ -430,10 +445,14 @@ int gdn_commit(float *S, float *hist, const float *q, const float *k, const floa
   if (hist != nullptr) {
     if (!aligned16(hist) || !ptr_ok(xc_raw) || conv_dim <= 0 || conv_dim % 4 != 0)
       return GDN_EINVAL;
-    if (overlaps(hist, hb, S, sb) || overlaps(hist, hb, xc_raw, (int64_t)M * n_units * conv_dim * 4) ||
-        overlaps(hist, hb, accepted, n_units * 4))
+    if (!grid_fits(n_units, vh, kd, conv_dim)) return GDN_EUNSUPPORTED;
+    if (overlaps(hist, hb, S, sb) || overlaps(hist, hb, xc_raw, (int64_t)M * n_units * conv_dim * 4))
       return GDN_EINVAL;
+    for (int i = 0; i < 6; i++)
+      if (overlaps(hist, hb, ins[i], ib[i])) return GDN_EINVAL;
+    if (status != nullptr && overlaps(status, 4, hist, hb)) return GDN_EINVAL;
   }
+  if (status != nullptr && overlaps(status, 4, accepted, n_units * 4)) return GDN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   // the history replay runs in the same launch as the state replay
   return enq(gdn::launch_recur(kd, S, S, q, k, v, g, beta, nullptr, accepted, n_units, vh, kh, M, s,

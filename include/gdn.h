@@ -116,8 +116,11 @@ typedef struct gdn_slab {
  * one ("Kestrel_VLLM #34", section 3.5: the draft-row buffer is allocated for
  * the maximum row count), and queries the size before allocating
  * ("Kestrel_VLLM #24", section 10: a size query before the copy, a refusal
- * rather than a truncation).  Returns the byte count, or GDN_EINVAL /
- * GDN_EUNSUPPORTED for bad dims, n_units < 1 or a bad hist size. */
+ * rather than a truncation).  Returns the byte count, or GDN_EINVAL for bad
+ * dims, n_units < 1 or a hist size that is negative or not a multiple of 4;
+ * GDN_EUNSUPPORTED for an unsupported kd / vd, more units than one
+ * recurrence launch takes (n_units * vh tiles within the grid limit of
+ * gdn_step), or more than 2^24 history floats per unit. */
 int64_t gdn_slab_bytes(int64_t n_units, int32_t vh, int32_t kh, int32_t kd,
                        int32_t vd, int64_t hist_floats_per_unit);
 
@@ -172,7 +175,9 @@ int gdn_mark_step_m(gdn_slab *slab, float *S, const float *hist, const float *q,
  * accepted[u] == 0 restores the marked bytes exactly; accepted[u] == M
  * reproduces gdn_step_m bit for bit.  The slab is disarmed afterwards: a
  * rollback on a disarmed slab, or with hist when the history was not marked,
- * returns GDN_ESTATE and changes nothing.
+ * returns GDN_ESTATE and changes nothing.  A launch that would pass the grid
+ * limit (the units' tiles plus their history replay: fewer than 2^32
+ * work-items) returns GDN_EUNSUPPORTED.
  */
 int gdn_rollback(gdn_slab *slab, float *S, float *hist, const float *q,
                  const float *k, const float *v, const float *g,
@@ -240,6 +245,11 @@ int gdn_verify_m_gated(const float *S, const float *q, const float *k,
  * cleared by the library).  Units with accepted[u] == 0 are not touched.
  * ("Kestrel_VLLM #34", section 3.7: after verification only the accepted
  * prefix may remain applied to the state and the history.)
+ * Errors: GDN_EINVAL for M outside 1..64, n_units < 0, a null or misaligned
+ * pointer, or S, hist or status overlapping another array of the call;
+ * GDN_EUNSUPPORTED for the shapes gdn_step refuses, ck != 4 with a history,
+ * or a history replay that takes the launch past the grid limit (fewer than
+ * 2^32 work-items with the tiles).  n_units == 0 is a no-op.
  */
 int gdn_commit(float *S, float *hist, const float *q, const float *k,
                const float *v, const float *g, const float *beta,
@@ -266,6 +276,11 @@ int gdn_commit(float *S, float *hist, const float *q, const float *k,
  * hist [B][ck-1][conv_dim] in/out; conv_w [conv_dim][ck]; outputs q, k
  * [B][kh][kd], v [B][vh][vd], g, beta [B][vh] feed gdn_step with N = B.
  * conv_dim must equal 2*kh*kd + vh*vd; ck must be 4.
+ * Errors: GDN_EINVAL for a null or misaligned pointer, B < 0, dim not a
+ * positive multiple of 4, a conv_dim other than the one above, or an output
+ * (q, k, v, g, beta, hist) overlapping another array of the call;
+ * GDN_EUNSUPPORTED for the kd / vd gdn_step refuses, ck != 4, or a launch
+ * beyond the grid limit.  B == 0 is a no-op.
  */
 int gdn_frontend(const float *x, const float *Wa, const float *Wb,
                  const float *A_log, const float *dt_bias, const float *xc_raw,

@@ -88,6 +88,11 @@ def test_slab_bytes_and_init():
     assert L.gdn_slab_bytes(4, vh, kh, 32, 32, 0) == gdn.GDN_EUNSUPPORTED
     nb = L.gdn_slab_bytes(3, vh, kh, kd, vd, 0)
     assert nb == 3 * vh * kd * vd * 4 + 256
+    # a slab's units are replayed in one recurrence launch: the step's grid limit
+    assert L.gdn_slab_bytes((1 << 32) // (1024 * vh) + 1, vh, kh, kd, vd, 0) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_slab_bytes(1 << 40, vh, kh, kd, vd, 0) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_slab_bytes(4, vh, kh, kd, vd, (1 << 24) + 4) == gdn.GDN_EUNSUPPORTED
+    assert L.gdn_slab_bytes(4, vh, kh, kd, vd, 1 << 24) == 4 * vh * kd * vd * 4 + 4 * 4 * (1 << 24) + 256
     s = gdn.gdn_slab()
     assert L.gdn_slab_init(C.byref(s), fp(0), nb - 1, 3, vh, kh, kd, vd, 0) == gdn.GDN_ESTATE
     assert L.gdn_slab_init(C.byref(s), fp(16), nb, 3, vh, kh, kd, vd, 0) == gdn.GDN_EINVAL  # align
@@ -143,6 +148,16 @@ def test_rollback_refusals_need_no_device():
     s.armed = 3
     assert L.gdn_rollback(C.byref(s), *args_h, 10240, 3, 4, acc, NULLS) == gdn.GDN_EUNSUPPORTED
     assert L.gdn_rollback(C.byref(s), *args_h, 10240, 5, 4, acc, NULLS) == gdn.GDN_EUNSUPPORTED
+    # the most units one launch takes, with a history replay that passes the grid limit
+    n, cd = (1 << 32) // (1024 * vh), 1 << 22
+    nb = L.gdn_slab_bytes(n, vh, kh, kd, vd, 3 * cd)
+    assert nb > 0
+    big = gdn.gdn_slab()
+    assert L.gdn_slab_init(C.byref(big), fp(0), nb, n, vh, kh, kd, vd, 3 * cd) == 0
+    big.armed = 3
+    zeros = (C.c_int32 * n)()
+    args_big = [fp(1 << 44), fp(1 << 45)] + [NULLS] * 6
+    assert L.gdn_rollback(C.byref(big), *args_big, cd, 4, 4, zeros, NULLS) == gdn.GDN_EUNSUPPORTED
     # history size disagreeing with the slab's (conv_dim * (ck - 1))
     assert L.gdn_rollback(C.byref(s), *args_h, 10236, 4, 4, acc, NULLS) == gdn.GDN_EINVAL
     assert s.armed == 3        # refusals leave the slab as it was
@@ -186,6 +201,19 @@ def test_verify_commit_refusals_need_no_device():
                         NULLS) == gdn.GDN_OK                           # nothing to do
     assert L.gdn_commit(S, hist, q, k, v, g, beta, xc, 10240, 3, 4, 2, vh, kh, kd, vd, acc, NULLS,
                         NULLS) == gdn.GDN_EUNSUPPORTED                 # conv width 3 not built
+    # the written history inside an input row array; status inside accepted or the history
+    assert L.gdn_commit(S, fp((3 << 32) + 1024), q, k, v, g, beta, xc, 10240, 4, 4, 2, vh, kh,
+                        kd, vd, acc, NULLS, NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_commit(S, fp((6 << 32) + 16), q, k, v, g, beta, xc, 10240, 4, 4, 2, vh, kh, kd,
+                        vd, acc, NULLS, NULLS) == gdn.GDN_EINVAL      # inside g
+    assert L.gdn_commit(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 4, 2, vh, kh, kd, vd, acc,
+                        fp((20 << 32) + 4), NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_commit(S, hist, q, k, v, g, beta, xc, 10240, 4, 4, 2, vh, kh, kd, vd, acc,
+                        fp((10 << 32) + 64), NULLS) == gdn.GDN_EINVAL
+    # the history replay's workgroups count towards the grid limit: 64 units of
+    # 2^28 channels need 2^32 replay lanes
+    assert L.gdn_commit(S, hist, q, k, v, g, beta, xc, 1 << 28, 4, 64, 2, vh, kh, kd, vd, acc,
+                        NULLS, NULLS) == gdn.GDN_EUNSUPPORTED
     z, w = fp(30 << 32), fp(31 << 32)
     eps = C.c_float(1e-6)
     assert L.gdn_verify_m_gated(S, q, k, v, g, beta, z, w, eps, o, 4, 0, vh, kh, kd, vd,
@@ -212,6 +240,13 @@ def test_frontend_validation():
     p2 = list(ptrs)
     p2[9] = p2[8]                                   # k aliases q
     assert L.gdn_frontend(*p2, 4, 5120, cd, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL
+    # an output or the history inside a weight input
+    # (x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, q, k, v, g, beta)
+    for i, inside in ((8, (1 << 32) + 256), (10, (2 << 32) + 4096), (11, 3 << 32),
+                      (12, 4 << 32), (6, (7 << 32) + 64), (6, 16)):
+        p2 = list(ptrs)
+        p2[i] = fp(inside)
+        assert L.gdn_frontend(*p2, 4, 5120, cd, 4, vh, kh, kd, vd, NULLS) == gdn.GDN_EINVAL, i
 
 
 def test_stream_read_validation():
