@@ -1216,22 +1216,26 @@ int static_counts_area(int32_t **area) {
 // Conv-history rollback: pure data movement, bit-exact.
 // ---------------------------------------------------------------------------
 
+// One-dimensional grid, `chunks` workgroups of 256 float4 channels per unit
+// (a second grid dimension would cap the unit count at 65536).
 __global__ __launch_bounds__(256) void hist_replay_kernel(float *hist, const float *src,
                                                           const float *xc_raw,
                                                           const int32_t *accepted,
                                                           int64_t n_units, int conv_dim, int M,
-                                                          int32_t *status) {
-  hist_replay_at(hist, src, xc_raw, accepted, n_units, conv_dim, M, status, blockIdx.y,
-                 blockIdx.x * 256 + threadIdx.x, threadIdx.x == 0);
+                                                          int32_t *status, uint32_t chunks) {
+  const uint32_t u = blockIdx.x / chunks, c = blockIdx.x - u * chunks;
+  hist_replay_at(hist, src, xc_raw, accepted, n_units, conv_dim, M, status, u,
+                 (int)(c * 256 + threadIdx.x), threadIdx.x == 0 && c == 0);
 }
 
 int launch_hist_replay(float *hist, const float *src, const float *xc_raw,
                        const int32_t *accepted, int64_t n_units, int conv_dim, int M,
                        int32_t *status, hipStream_t s) {
   if (n_units <= 0) return 0;
-  dim3 grid((unsigned)((conv_dim / 4 + 255) / 256), (unsigned)n_units);
+  const uint32_t chunks = (uint32_t)((conv_dim / 4 + 255) / 256);
+  const dim3 grid((unsigned)(n_units * chunks));
   hipLaunchKernelGGL(hist_replay_kernel, grid, dim3(256), 0, s, hist, src, xc_raw, accepted,
-                     n_units, conv_dim, M, status);
+                     n_units, conv_dim, M, status, chunks);
   return (int)hipGetLastError();
 }
 

@@ -908,6 +908,36 @@ def test_commit_refuses_out_of_range_counts(orc):
     assert bits_equal(host(hist), h_rb)
 
 
+def test_commit_single_step_history_beyond_65536_units(orc):
+    """A one-step commit with a history replays it in a launch of its own; its
+    grid holds every unit in one dimension, so more than 65536 units (one key
+    and one value head of kd = 64 each: 1 GB of state) are all committed.
+    Checked against the oracle's cycle: S within tolerance, the history bit
+    for bit, refused counts leaving their unit unchanged."""
+    dims = (1, 1, 64, 64)
+    N, M = 65536 + 37, 1
+    say(f"commit M=1 with history, N={N} dims={dims}")
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(17, "cuda")
+    S = synth.state(gen, N, dims, device="cuda")
+    inp = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    hist = torch.randn((N, 3, cd), generator=gen, device="cuda")
+    xc = torch.randn((M, N, cd), generator=gen, device="cuda")
+    S0, h0 = host(S), host(hist)
+    acc = (torch.arange(N, device="cuda") % 2).to(torch.int32)
+    acc[-1] = 2                                   # out of range: this unit stays
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gdn.commit(S, acc, *(inp[n] for n in NAMES), hist=hist, xc_raw=xc, status=status)
+    assert int(status.item()) == 1
+    acc_ref = host(acc).copy()
+    acc_ref[-1] = 0
+    _, _, S_rb, h_rb = ref_cycle(orc, S0, {n: host(inp[n]) for n in NAMES}, dims, acc_ref, h0,
+                                 host(xc))
+    assert_close(host(S), S_rb, "S after commit")
+    assert bits_equal(host(hist), h_rb)
+    assert bits_equal(host(S[-1]), S0[-1]) and bits_equal(host(hist[-1]), h0[-1])
+
+
 def test_verify_cycle_graph_replay(orc):
     """One layer's speculative cycle without a snapshot -- front end for the M
     draft rows (history read only), verify, commit with device-side accepted
