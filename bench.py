@@ -246,8 +246,8 @@ def decode_cpu_and_parity(S0, pool, dims, steps, gated=None):
     th = cpu_threads()
     online, model = cpu_info()
     xs = [{n: host(pool[r % len(pool)][n][0]) for n in NAMES} for r in range(steps)]
-    # single thread: the first 3 steps of the first units (about 1 s of work)
-    n1 = min(N, 64)
+    # single thread: the first 3 steps of the first units (under a second of work)
+    n1 = min(N, 256)
     S1 = host(S0[:n1])
     o1 = np.zeros((n1, vh, vd), np.float32)
     t0 = time.perf_counter()
