@@ -33,7 +33,10 @@
  *      v, o     [M][N][vh][vd]
  *      g, beta  [M][N][vh]        g is the log-domain gate (<= 0 in use)
  *    The unit order inside N is the caller's (sequence-major in the tests).
- *  - Supported: kd == vd in {64, 128}, vh % kh == 0, vh <= 4096.
+ *  - Supported: kd == vd in {64, 128}, vh % kh == 0, vh <= 4096.  A launch
+ *    stays below 2^32 work-items: n_units * vh * 1024 (kd = 128) or
+ *    n_units * vh * 256 (kd = 64), plus any history replay; larger calls
+ *    return GDN_EUNSUPPORTED.
  *  - S must not overlap q, k, v, g, beta or o.
  */
 #ifndef GDN_H
