@@ -2134,10 +2134,25 @@ __global__ __launch_bounds__(64 * NW) void proj_kernel(ProjArgs a) {
 // more outputs), then the most row blocks per tile (up to the rows present)
 // that still leave >= kPjMinWg workgroups.  Measured at 64 rows:
 // out_proj (R = 5120) 2 row blocks x 4 slabs 70 us, 4 x 2 96 us, 4 x 4
-// 128 us; in_proj 4 x 4 128 us.  The choice never changes a result
-// (canonical summation above).
+// 128 us; in_proj 4 x 4 128 us.
+// That whole-tile choice is kept beyond 16 rows only while it fills the chip
+// evenly with little padding.  If it leaves CUs idle (fewer than
+// kPjFullTiles tiles), ends on a last round of workgroups that is mostly
+// empty (under 80% of its rounds' slots used), or, from 40 rows, pads the
+// rows by more than a quarter, the call runs split halves of one-row-block
+// tiles instead, with the widest slab group that still gives
+// kPjSplitTilesMin tiles.  Measured (8 weight sets from HBM) against the
+// whole-tile choice: out_proj at 17-32 rows 45 -> 39-42 us, 40-64 rows
+// 68 -> 42-59 us, 80-128 rows 119-123 -> 72-91 us, 256 rows 230 -> 175 us;
+// in_proj at 80 rows 197 -> 157 us, 96 rows 199 -> 183 us.  No choice
+// changes a result (canonical summation above).
+constexpr int64_t kPjFullTiles = 224;
+constexpr int64_t kPjSplitTilesMin = 192;
+constexpr int64_t kPjCUs = 256;
+
 struct ProjShape {
   int rb, oj, row_groups;
+  bool split;   // two half-tile workgroups per tile (one row block)
 };
 
 static int64_t proj_tiles(int64_t rows, int R0, int R1, int rb, int oj) {
@@ -2160,11 +2175,30 @@ static ProjShape proj_shape(int64_t rows, int R0, int R1) {
   sh.rb = rb_max;
   while (sh.rb > 1 && proj_tiles(rows, R0, R1, sh.rb, sh.oj) < kPjMinWg) sh.rb >>= 1;
   sh.row_groups = (int)((rows + 16 * sh.rb - 1) / (16 * sh.rb));
+  sh.split = false;
+  if (rows > 16) {
+    const int64_t t = proj_tiles(rows, R0, R1, sh.rb, sh.oj);
+    const int64_t rounds = (t + kPjCUs - 1) / kPjCUs;
+    const int64_t padded = (int64_t)sh.row_groups * 16 * sh.rb;
+    if (t < kPjFullTiles || 5 * t < 4 * rounds * kPjCUs || (rows >= 40 && 4 * padded > 5 * rows)) {
+      sh.rb = 1;
+      sh.oj = 1;
+      for (int oj = 4; oj > 1; oj >>= 1) {
+        const bool divides = (R0 / 16) % oj == 0 && (R1 / 16) % oj == 0;
+        if (divides && proj_tiles(rows, R0, R1, 1, oj) >= kPjSplitTilesMin) {
+          sh.oj = oj;
+          break;
+        }
+      }
+      sh.row_groups = (int)((rows + 15) / 16);
+      sh.split = true;
+    }
+  }
   return sh;
 }
 
 static bool proj_split(const ProjShape &sh, int64_t rows, int64_t tiles) {
-  return rows >= 2 && sh.rb == 1 && sh.oj == 1 && tiles < kPjSplitBelow;
+  return sh.split || (rows >= 2 && sh.rb == 1 && sh.oj == 1 && tiles < kPjSplitBelow);
 }
 
 int64_t proj_workgroups(int64_t rows, int R0, int R1) {
@@ -2184,16 +2218,21 @@ static void launch_proj_t(const ProjArgs &a, bool stream, hipStream_t s) {
                        s, a);
 }
 
-// The split shape (one row block, weights streamed): two half-tile
-// workgroups of PJ_SEG / 2 waves per tile, after a fill kernel zeroed y.
+// The split shape (one row block): two half-tile workgroups of PJ_SEG / 2
+// waves per tile, after a fill kernel zeroed y.  The weights are streamed
+// past the caches when one row group reads them once, as in ld_w.
 template <int OJ, int U>
-static void launch_proj_split(const ProjArgs &a, hipStream_t s) {
+static void launch_proj_split(const ProjArgs &a, bool stream, hipStream_t s) {
   const int64_t n0 = a.rows * a.p[0].R, n1 = a.p[1].W ? a.rows * a.p[1].R : 0;
   hipLaunchKernelGGL(zero2_kernel, dim3((unsigned)((n0 + n1 + 255) / 256)), dim3(256), 0, s,
                      a.p[0].y, n0, a.p[1].y, n1);
   const dim3 grid((unsigned)(a.p[0].blocks + a.p[1].blocks));
-  hipLaunchKernelGGL((proj_kernel<1, OJ, U, true, PJ_SEG / 2>), grid, dim3(PJ_LANES / 2), 0, s,
-                     a);
+  if (stream)
+    hipLaunchKernelGGL((proj_kernel<1, OJ, U, true, PJ_SEG / 2>), grid, dim3(PJ_LANES / 2), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((proj_kernel<1, OJ, U, false, PJ_SEG / 2>), grid, dim3(PJ_LANES / 2), 0,
+                       s, a);
 }
 
 // Weight packing (one launch per matrix, pure data movement): thread i
@@ -2232,10 +2271,14 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
   if (proj_split(sh, rows, a.p[0].blocks + a.p[1].blocks)) {
     a.p[0].blocks *= 2;
     a.p[1].blocks *= 2;
-    if (rows <= kPjU2Rows)
-      launch_proj_split<1, 2>(a, s);
+    if (sh.oj == 4)
+      launch_proj_split<4, 2>(a, stream, s);
+    else if (sh.oj == 2)
+      launch_proj_split<2, 4>(a, stream, s);
+    else if (rows <= kPjU2Rows)
+      launch_proj_split<1, 2>(a, stream, s);
     else
-      launch_proj_split<1, 4>(a, s);
+      launch_proj_split<1, 4>(a, stream, s);
     return (int)hipGetLastError();
   }
   switch (sh.rb * 8 + sh.oj) {

@@ -70,13 +70,20 @@ def operands(seed, rows, R, C):
 @pytest.mark.parametrize("rows,R,C", [(1, 64, 128), (5, 48, 640), (16, 256, 1024),
                                       (17, 128, 512), (20, 48, 256), (40, 96, 1152),
                                       (64, 512, 5120), (70, 160, 6144), (150, 4096, 256),
-                                      (48, 4096, 384)])
+                                      (48, 4096, 384), (24, 5120, 256), (48, 5120, 256),
+                                      (80, 2048, 256), (192, 5120, 128), (64, 16384, 128),
+                                      (20, 16384, 128), (64, 3600, 128), (64, 7200, 128),
+                                      (32, 3600, 128)])
 def test_proj_parity(orc, rows, R, C):
-    """Every tile shape against the oracle: 1, 2 and 4 row blocks, 1, 2 and 4
-    output slabs per wave, one and several row groups (150 x 4096: 4 row
-    blocks over 3 row groups, the weights read through L2), a ragged last row
-    group, segments with and without a tail, and the two-workgroup split over
-    one (5 x 48) and two row groups (20 x 48: one row block per tile)."""
+    """Every tile shape the calls choose, against the oracle.  Whole tiles:
+    1 row block at one row and up to 16 rows; 2 row blocks x 4 slabs per wave
+    over a ragged row group (20 x 16384); 4 x 4 with the staged fold (64 x
+    16384) and with the one-buffer fold over three row groups (192 x 5120,
+    weights read through L2); 4 x 1, 4 x 2 and 2 x 1 where the slab count is
+    odd (3600, 7200 outputs).  Split half-tile workgroups: one row group (5 x
+    48), several with one slab per wave (20 x 48, 17, 40, 64, 70 rows), with
+    two (24 x 5120, 80 x 2048) and four (48 x 5120, 48 x 4096, 150 x 4096)
+    slabs per wave.  Segments with and without a tail."""
     say(f"proj rows={rows} R={R} C={C}")
     x, W = operands(20 + rows, rows, R, C)
     y = gdn.proj(x, gdn.proj_pack(W))
@@ -87,8 +94,9 @@ def test_proj_parity(orc, rows, R, C):
 
 def test_proj_rows_are_independent_bit_exact():
     """A row gives the same bits whatever else shares the call: one call over
-    70 rows (4 row blocks per tile, ragged tail) against calls over 1, 6, 16
-    and 32 rows (1 and 2 row blocks per tile)."""
+    70 rows (split half tiles over five row groups, ragged tail) against
+    calls over 1 row (whole tiles), 6 and 16 rows (split, one row group) and
+    32 rows (split, two row groups)."""
     say("proj row independence")
     rows, R, C = 70, 96, 1536
     x, W = operands(31, rows, R, C)
@@ -100,15 +108,17 @@ def test_proj_rows_are_independent_bit_exact():
 
 
 def test_proj_rows_are_independent_across_tile_shapes():
-    """The same, with an output count that lets the call pick 1, 2 and 4 row
-    blocks per tile and several row groups: 150 rows against slices of 1, 20,
-    33, 64 and 100 rows."""
+    """The same, with an output count (16384) that gives each row count a
+    different shape: 150 rows (split halves of one-row-block tiles with four
+    slabs per wave, 10 row groups) against slices of 1 row (whole one-slab
+    tiles), 20 rows (2 x 4 whole tiles), 33 and 64 rows (4 x 4, staged fold),
+    128 rows (4 x 4 over two row groups) and 100 rows (split again)."""
     say("proj row independence, large R")
-    rows, R, C = 150, 4096, 256
+    rows, R, C = 150, 16384, 128
     x, W = operands(71, rows, R, C)
     Wp = gdn.proj_pack(W)
     full = host(gdn.proj(x, Wp))
-    for lo, hi in ((7, 8), (0, 20), (100, 133), (30, 94), (50, 150)):
+    for lo, hi in ((7, 8), (0, 20), (100, 133), (30, 94), (0, 128), (50, 150)):
         part = host(gdn.proj(x[lo:hi].contiguous(), Wp))
         assert bits_equal(part, np.ascontiguousarray(full[lo:hi])), (lo, hi)
 
@@ -194,6 +204,14 @@ def test_proj_split_tiles_equal_whole_tiles():
     y20 = host(gdn.proj(x20, W48p))
     y70 = host(gdn.proj(torch.cat([x20] * 4)[:70].contiguous(), W48p))
     assert bits_equal(y20, np.ascontiguousarray(y70[:20]))
+    # the split with four slabs per wave over three row groups (48 rows of
+    # 5120 outputs) against one-row calls and the two-slab split of 24 rows
+    x48 = torch.cat([x, x.flip(0)]).contiguous()
+    y48 = host(gdn.proj(x48, Wp))
+    assert bits_equal(np.ascontiguousarray(y48[:24]), full)
+    for r in (0, 30, 47):
+        one = host(gdn.proj(x48[r:r + 1].contiguous(), Wp))
+        assert bits_equal(one, np.ascontiguousarray(y48[r:r + 1])), r
     # y is zeroed by the call itself: a second call into the same output gives
     # the same bits
     y = torch.full((4, 5120), 3.0, device="cuda")
