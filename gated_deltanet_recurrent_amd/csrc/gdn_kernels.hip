@@ -1963,12 +1963,14 @@ __global__ __launch_bounds__(64 * NW) void proj_kernel(ProjArgs a) {
     for (int oj = 0; oj < OJ; oj++) acc[rb][oj] = pj_acc{0.f, 0.f, 0.f, 0.f};
 
   int kb = 0;
-  if constexpr (RB == 1) {
+  if constexpr (RB == 1 || (RB * OJ == 16 && U == 1)) {
     // software-pipelined: the loads of trip i + 1 are issued before the
     // MFMAs of trip i (same MFMA order as the plain loop below).  Measured
-    // 3-17% faster up to 16 rows (weights streamed at 6.6 TB/s); with 2 or 4
-    // row blocks the second set of operand registers costs more occupancy
-    // than it gains.
+    // 3-17% faster up to 16 rows (weights streamed at 6.6 TB/s).  4 x 4
+    // tiles take it with one column block per trip (162 VGPRs, as the plain
+    // loop with two) when the launch is one round of workgroups, which
+    // nothing else on the CU hides; with more rounds, and for the other tiles
+    // of 2 or 4 row blocks, the plain loop measured faster.
     f4 wn[U][OJ], xn[U][RB];
     auto issue = [&](int k) {
 #pragma unroll
@@ -2305,12 +2307,20 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
     case 4 * 8 + 2: launch_proj_t<4, 2, 4>(a, stream, s); break;
     // 4 x 4: the staged fold measured faster with a workgroup or more per CU
     // (in_proj at 64 rows, 256 tiles: 119.7 -> 114.3 us; 128 rows: 206.6 ->
-    // 203.6), slower below (out_proj at 128 rows, 160 tiles: 116.6 -> 117.2)
+    // 203.6), slower below (out_proj at 128 rows, 160 tiles: 116.6 -> 117.2).
+    // A staged launch of one round takes the pipelined loop (in_proj at 33
+    // and 64 rows: 102.9 -> 97.1 and 114.3 -> 107.9 us); with the one-buffer
+    // fold it measured slower (out_proj at 192 rows, 240 tiles: 117.9 ->
+    // 122.9 us), and so did launches of several rounds.
     default:
-      if (a.p[0].blocks + a.p[1].blocks >= kPjStagedMin)
-        launch_proj_t<4, 4, 2, true>(a, stream, s);
-      else
+      if (a.p[0].blocks + a.p[1].blocks >= kPjStagedMin) {
+        if (a.p[0].blocks + a.p[1].blocks <= kPjCUs)
+          launch_proj_t<4, 4, 1, true>(a, stream, s);
+        else
+          launch_proj_t<4, 4, 2, true>(a, stream, s);
+      } else {
         launch_proj_t<4, 4, 2>(a, stream, s);
+      }
       break;
   }
   return (int)hipGetLastError();
