@@ -1963,14 +1963,14 @@ __global__ __launch_bounds__(64 * NW) void proj_kernel(ProjArgs a) {
     for (int oj = 0; oj < OJ; oj++) acc[rb][oj] = pj_acc{0.f, 0.f, 0.f, 0.f};
 
   int kb = 0;
-  if constexpr (RB == 1 || (RB * OJ == 16 && U == 1)) {
+  if constexpr (RB == 1 || (RB * OJ >= 8 && U == 1)) {
     // software-pipelined: the loads of trip i + 1 are issued before the
     // MFMAs of trip i (same MFMA order as the plain loop below).  Measured
-    // 3-17% faster up to 16 rows (weights streamed at 6.6 TB/s).  4 x 4
-    // tiles take it with one column block per trip (162 VGPRs, as the plain
-    // loop with two) when the launch is one round of workgroups, which
-    // nothing else on the CU hides; with more rounds, and for the other tiles
-    // of 2 or 4 row blocks, the plain loop measured faster.
+    // 3-17% faster up to 16 rows (weights streamed at 6.6 TB/s).  The 2 x 4
+    // and 4 x 4 tiles take it with one column block per trip (103 and 162
+    // VGPRs) when the launch is one round of workgroups, whose load latency
+    // nothing else on the CU hides; with more rounds the plain loop with two
+    // blocks per trip measured faster.
     f4 wn[U][OJ], xn[U][RB];
     auto issue = [&](int k) {
 #pragma unroll
@@ -2302,7 +2302,12 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
     case 1 * 8 + 4: launch_proj_t<1, 4, 2>(a, true, s); break;
     case 2 * 8 + 1: launch_proj_t<2, 1, 4>(a, true, s); break;
     case 2 * 8 + 2: launch_proj_t<2, 2, 4>(a, true, s); break;
-    case 2 * 8 + 4: launch_proj_t<2, 4, 2>(a, true, s); break;
+    case 2 * 8 + 4:   // one round: pipelined (in_proj at 17 rows 61.6 -> 57.5 us)
+      if (a.p[0].blocks + a.p[1].blocks <= kPjCUs)
+        launch_proj_t<2, 4, 1>(a, true, s);
+      else
+        launch_proj_t<2, 4, 2>(a, true, s);
+      break;
     case 4 * 8 + 1: launch_proj_t<4, 1, 4>(a, stream, s); break;
     case 4 * 8 + 2: launch_proj_t<4, 2, 4>(a, stream, s); break;
     // 4 x 4: the staged fold measured faster with a workgroup or more per CU
