@@ -464,10 +464,10 @@ def bench_latency(cfg, steps, warmup, cpu):
 
 
 def bench_verify(cfg, steps, warmup, cpu, only=None):
-    """The speculative cycle.  only = "step_m", "verify_m" or "commit" times
-    that one call alone (the same inputs; every commit runs the first set of
-    accepted counts from the current state), so that a profiler sees that
-    call's launches only."""
+    """The speculative cycle.  only = "step_m", "verify_m", "commit" or
+    "commit_verify" times that one call alone (the same inputs; every commit
+    runs the first set of accepted counts from the current state), so that a
+    profiler sees that call's launches only."""
     dims = cfg["dims"]
     vh = dims[0]
     L = cfg["layers"]
@@ -498,12 +498,18 @@ def bench_verify(cfg, steps, warmup, cpu, only=None):
         gdn.verify_m(S, *args, o=o)
         gdn.commit(S, acc_dev[i % 8], *args, status=status)
 
+    def one_fused(i):   # steady state: the previous rows' commit and these rows' verify, one pass
+        gdn.commit_verify_m(S, acc_dev[i % 8], *args, *args, o=o, status=status)
+
     if only is not None:
         call = {"step_m": lambda i: gdn.step_m(S, *args, o=o),
                 "verify_m": lambda i: gdn.verify_m(S, *args, o=o),
-                "commit": lambda i: gdn.commit(S, acc_dev[0], *args, status=status)}[only]
+                "commit": lambda i: gdn.commit(S, acc_dev[0], *args, status=status),
+                "commit_verify": lambda i: gdn.commit_verify_m(S, acc_dev[0], *args, *args, o=o,
+                                                               status=status)}[only]
         dt = timed(call, steps, warmup)
-        mean_a = float(accs[0].mean()) if only == "commit" else float(np.mean([a.mean() for a in accs]))
+        mean_a = (float(accs[0].mean()) if only in ("commit", "commit_verify")
+                  else float(np.mean([a.mean() for a in accs])))
         tile = dims[2] * dims[3] * 4
         rows = N * vh * (M if only != "commit" else mean_a)
         b = N * vh * M * head_step_bytes(dims, rows=M)
@@ -514,6 +520,14 @@ def bench_verify(cfg, steps, warmup, cpu, only=None):
             # those rows (no output); a unit with none is not touched
             row = head_step_bytes(dims, rows=1, write_o=False) - 2 * tile
             b = vh * float(((accs[0] > 0) * 2 * tile + accs[0] * row).sum())
+        elif only == "commit_verify":
+            # every unit reads its state once and writes it back when it
+            # accepted rows; it reads those rows, then reads the M draft rows
+            # and writes their outputs
+            row = head_step_bytes(dims, rows=1, write_o=False) - 2 * tile
+            b = vh * float((tile + (accs[0] > 0) * tile + accs[0] * row).sum())
+            b += N * vh * M * (head_step_bytes(dims, rows=1) - 2 * tile)
+            rows = N * vh * M
         achieved = b / (dt / steps) / 1e9
         res = dict(value=rows * steps / dt, ms_per_step=dt / steps * 1e3,
                    roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
@@ -527,6 +541,7 @@ def bench_verify(cfg, steps, warmup, cpu, only=None):
     dt = timed(one, steps, warmup)
     dt_unfused = timed(one_unfused, steps, 1)
     dt_vc = timed(one_verify_commit, steps, 1)
+    dt_fused = timed(one_fused, steps, 1)
     # step_m alone, for the kernel roofline
     dt_m = timed(lambda i: gdn.step_m(S, *args, o=o), steps, 1)
     bytes_m = N * vh * M * head_step_bytes(dims, rows=M)
@@ -542,6 +557,7 @@ def bench_verify(cfg, steps, warmup, cpu, only=None):
                           step_m_ms=round(dt_m / steps * 1e3, 4), mean_accepted=mean_a,
                           cycle_ms_separate_mark=round(dt_unfused / steps * 1e3, 4),
                           cycle_ms_verify_commit=round(dt_vc / steps * 1e3, 4),
+                          cycle_ms_commit_verify_fused=round(dt_fused / steps * 1e3, 4),
                           value_counts="drafted head-steps per second of the full cycle"))
     if cpu:
         res["extra"]["parity_all_units"] = verify_parity(S_start, inp, dims, accs[0])
@@ -1000,7 +1016,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("step_m", "verify_m", "commit"),
+    ap.add_argument("--only", choices=("step_m", "verify_m", "commit", "commit_verify"),
                     help="config 2: time this one call alone (for a profiler)")
     ap.add_argument("--other-steps", type=int, default=20,
                     help="the default workload also times every other workload with this "

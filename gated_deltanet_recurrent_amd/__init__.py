@@ -37,7 +37,7 @@ EXPORTS = ("gdn_strerror", "gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab
            "gdn_mark", "gdn_rollback", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy",
            "gdn_proj", "gdn_proj_pack", "gdn_verify_m_gated", "gdn_proj_q4_bytes",
            "gdn_proj_q4_pack", "gdn_proj_q4", "gdn_stream_read", "gdn_stream_read_words",
-           "gdn_rollback_static")
+           "gdn_rollback_static", "gdn_commit_verify_m")
 
 
 class GdnError(RuntimeError):
@@ -87,6 +87,8 @@ def lib():
     L.gdn_stream_read_words.restype = I64
     L.gdn_verify_m.argtypes = [P] * 7 + [I64, I32, I32, I32, I32, I32, P]
     L.gdn_commit.argtypes = [P] * 8 + [I32, I32, I64, I32, I32, I32, I32, I32, P, P, P]
+    L.gdn_commit_verify_m.argtypes = ([P] * 8 + [I32, I32, I64, I32, P, P] + [P] * 6
+                                      + [I32, I32, I32, I32, I32, P])
     L.gdn_frontend_verify_m.argtypes = [P] * 13 + [I32] * 9 + [P]
     L.gdn_proj.argtypes = [P, I64, I32, P, I32, P, P, I32, P, P]
     L.gdn_proj_pack.argtypes = [P, P, I32, I32, P]
@@ -98,7 +100,8 @@ def lib():
     for f in ("gdn_step", "gdn_step_m", "gdn_step_gated", "gdn_slab_init", "gdn_mark_step_m", "gdn_mark", "gdn_rollback",
               "gdn_rollback_static", "gdn_frontend", "gdn_frontend_m", "gdn_stream_copy", "gdn_stream_read",
               "gdn_verify_m",
-              "gdn_commit", "gdn_frontend_verify_m", "gdn_proj", "gdn_proj_pack",
+              "gdn_commit", "gdn_commit_verify_m", "gdn_frontend_verify_m", "gdn_proj",
+              "gdn_proj_pack",
               "gdn_verify_m_gated", "gdn_proj_q4_pack", "gdn_proj_q4"):
         getattr(L, f).restype = C.c_int
     _lib = L
@@ -377,6 +380,25 @@ def commit(S, accepted, q, k, v, g, beta, hist=None, xc_raw=None, status=None, s
                             _sized(xc_raw, M * N * conv_dim, "xc_raw"), conv_dim, 4, N, M, vh, kh,
                             kd, vd, _int32_dev(accepted, "accepted", N),
                             _int32_dev(status, "status", 1), _stream(stream)), "gdn_commit")
+
+
+def commit_verify_m(S, accepted, q, k, v, g, beta, q2, k2, v2, g2, beta2, o=None, hist=None,
+                    xc_raw=None, status=None, stream=None):
+    """commit (the accepted prefix of the previous rows q..beta [M][N]) and
+    then verify_m of the next rows q2..beta2 [M2][N], in one pass over S
+    (gdn_commit_verify_m).  Returns o [M2][N][vh][vd]."""
+    N, vh, kh, kd, vd = _state_dims(S, q, v)
+    M, M2 = q.shape[0], q2.shape[0]
+    if o is None:
+        o = torch.empty((M2, N, vh, vd), dtype=torch.float32, device=S.device)
+    conv_dim = xc_raw.shape[-1] if xc_raw is not None else 0
+    _check(lib().gdn_commit_verify_m(
+        _dev(S, "S"), _sized(hist, N * 3 * conv_dim, "hist"), *_rows(S, q, k, v, g, beta, M),
+        _sized(xc_raw, M * N * conv_dim, "xc_raw"), conv_dim, 4, N, M,
+        _int32_dev(accepted, "accepted", N), _int32_dev(status, "status", 1),
+        *_rows(S, q2, k2, v2, g2, beta2, M2, o), M2, vh, kh, kd, vd, _stream(stream)),
+        "gdn_commit_verify_m")
+    return o
 
 
 def frontend_verify_m(x, Wa, Wb, A_log, dt_bias, xc_raw, hist, conv_w, dims, out=None,

@@ -416,10 +416,17 @@ int gdn_verify_m_gated(const float *S, const float *q, const float *k, const flo
                                M, (hipStream_t)stream, z, norm_w, eps));
 }
 
-int gdn_commit(float *S, float *hist, const float *q, const float *k, const float *v,
-               const float *g, const float *beta, const float *xc_raw, int32_t conv_dim,
-               int32_t ck, int64_t n_units, int32_t M, int32_t vh, int32_t kh, int32_t kd,
-               int32_t vd, const int32_t *accepted, int32_t *status, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The arguments of gdn_commit (also the first half of gdn_commit_verify_m).
+// n_units == 0 passes; the caller then launches nothing.
+int check_commit(const float *S, const float *hist, const float *q, const float *k,
+                 const float *v, const float *g, const float *beta, const float *xc_raw,
+                 int32_t conv_dim, int32_t ck, int64_t n_units, int32_t M, int32_t vh,
+                 int32_t kh, int32_t kd, int32_t vd, const int32_t *accepted,
+                 const int32_t *status) {
   if (M < 1 || M > kMaxM) return GDN_EINVAL;
   int rc = check_dims(vh, kh, kd, vd);
   if (rc) return rc;
@@ -453,11 +460,60 @@ int gdn_commit(float *S, float *hist, const float *q, const float *k, const floa
     if (status != nullptr && overlaps(status, 4, hist, hb)) return GDN_EINVAL;
   }
   if (status != nullptr && overlaps(status, 4, accepted, n_units * 4)) return GDN_EINVAL;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_commit(float *S, float *hist, const float *q, const float *k, const float *v,
+               const float *g, const float *beta, const float *xc_raw, int32_t conv_dim,
+               int32_t ck, int64_t n_units, int32_t M, int32_t vh, int32_t kh, int32_t kd,
+               int32_t vd, const int32_t *accepted, int32_t *status, void *stream) {
+  const int rc = check_commit(S, hist, q, k, v, g, beta, xc_raw, conv_dim, ck, n_units, M, vh, kh,
+                              kd, vd, accepted, status);
+  if (rc || n_units == 0) return rc;
   hipStream_t s = (hipStream_t)stream;
   // the history replay runs in the same launch as the state replay
   return enq(gdn::launch_recur(kd, S, S, q, k, v, g, beta, nullptr, accepted, n_units, vh, kh, M, s,
                                nullptr, nullptr, 0.0f, nullptr, status, hist, hist, xc_raw,
                                conv_dim));
+}
+
+int gdn_commit_verify_m(float *S, float *hist, const float *q, const float *k, const float *v,
+                        const float *g, const float *beta, const float *xc_raw, int32_t conv_dim,
+                        int32_t ck, int64_t n_units, int32_t M, const int32_t *accepted,
+                        int32_t *status, const float *q2, const float *k2, const float *v2,
+                        const float *g2, const float *beta2, float *o, int32_t M2, int32_t vh,
+                        int32_t kh, int32_t kd, int32_t vd, void *stream) {
+  int rc = check_commit(S, hist, q, k, v, g, beta, xc_raw, conv_dim, ck, n_units, M, vh, kh, kd,
+                        vd, accepted, status);
+  if (rc) return rc;
+  if (M2 < 1 || M2 > kMaxM) return GDN_EINVAL;
+  rc = check_step(S, q2, k2, v2, g2, beta2, o, n_units, M2, vh, kh, kd, vd);
+  if (rc || n_units == 0) return rc;
+  // the verify's outputs against everything else the call reads or writes,
+  // and the written history against the verify's rows
+  const int64_t qkb = (int64_t)M * n_units * kh * kd * 4, vb = (int64_t)M * n_units * vh * vd * 4,
+                gb = (int64_t)M * n_units * vh * 4;
+  const int64_t qkb2 = (int64_t)M2 * n_units * kh * kd * 4,
+                vb2 = (int64_t)M2 * n_units * vh * vd * 4, gb2 = (int64_t)M2 * n_units * vh * 4;
+  const int64_t hb = n_units * (kConvK - 1) * (int64_t)conv_dim * 4;
+  const void *first[7] = {q, k, v, g, beta, accepted, hist ? xc_raw : nullptr};
+  const int64_t fb[7] = {qkb, qkb, vb, gb, gb, n_units * 4, (int64_t)M * n_units * conv_dim * 4};
+  for (int i = 0; i < 7; i++)
+    if (overlaps(o, vb2, first[i], fb[i])) return GDN_EINVAL;
+  if (status != nullptr && overlaps(o, vb2, status, 4)) return GDN_EINVAL;
+  if (hist != nullptr) {
+    const void *second[6] = {q2, k2, v2, g2, beta2, o};
+    const int64_t sb2[6] = {qkb2, qkb2, vb2, gb2, gb2, vb2};
+    for (int i = 0; i < 6; i++)
+      if (overlaps(hist, hb, second[i], sb2[i])) return GDN_EINVAL;
+  }
+  return enq(gdn::launch_commit_verify(kd, S, q, k, v, g, beta, accepted, status, hist, xc_raw,
+                                       conv_dim, n_units, vh, kh, M, q2, k2, v2, g2, beta2, o, M2,
+                                       (hipStream_t)stream));
 }
 
 int gdn_stream_copy(float *dst, const float *src, int64_t n_floats, void *stream) {

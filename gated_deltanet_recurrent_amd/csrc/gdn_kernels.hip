@@ -244,6 +244,12 @@ struct RecurArgs {
   const float *xc_raw;   // [M][N][conv_dim]
   int conv_dim;
   int64_t tile_wgs;      // workgroups of the tiles; the rest replay history
+  // commit + verify in one pass (M-step kernel only; q2 == nullptr otherwise):
+  // after the steps[u] rows above are applied and the state stored, M2 rows
+  // of these inputs run from the stored state, outputs to o2, state not stored
+  const float *q2 = nullptr, *k2 = nullptr, *v2 = nullptr, *g2 = nullptr, *beta2 = nullptr;
+  float *o2 = nullptr;
+  int M2 = 0;
 };
 
 // Per-step inputs are staged through LDS in chunks of MC rows.  q and k are
@@ -687,7 +693,7 @@ static __device__ __forceinline__ void deep_partials(const f4 (&p)[4], f4 &w0, f
   }
 }
 
-template <int KD, bool MULTI, bool GATED>
+template <int KD, bool MULTI, bool GATED, bool FUSED = false>
 __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a) {
   using D = Deep<KD>;
   constexpr int LANES = D::LANES, RG = Canon<KD>::RG, CG = D::CG;
@@ -709,15 +715,15 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
   const int cg = t % CG, L = t / CG;
   const TileIdx ti = tile_index(a, KD * KD);
   const int steps = ti.steps;
-  // an in-place update with nothing to run leaves the tile as it is
-  if (steps == 0 && a.S_src == a.S_dst && a.snap == nullptr) return;
+  // an in-place update with nothing to run leaves the tile as it is (a fused
+  // call still runs the next verify's rows)
+  if (!FUSED && steps == 0 && a.S_src == a.S_dst && a.snap == nullptr) return;
   // element (i, j) of this lane: row 4L + i + RG*j
   const rsrc_t src = buf_rsrc(a.S_src + ti.tile_off, KD * KD * 4);
   const int lane_off = ((4 * L) * KD + 4 * cg) * 4;
 
   ChunkRegs<KD, LANES, GATED> cr;
   if (steps > 0) chunk_load<KD, LANES, GATED>(cr, a, t, ti.unit, ti.head, ti.hh, 0, steps < MC ? steps : MC);
-  const float *zprev = nullptr;
 
   f4 s[4][4];
 #pragma unroll
@@ -732,95 +738,124 @@ __global__ __launch_bounds__(Deep<KD>::LANES) void recur_deep_kernel(RecurArgs a
       for (int i = 0; i < 4; i++) st_stream(snp, lane_off, (i + RG * j) * KD * 4, s[i][j]);
   }
 
-  int buf = 0;
-  for (int m0 = 0; m0 < steps; m0 += MC) {
-    const int nr = steps - m0 < MC ? steps - m0 : MC;
-    Stage<KD, GATED> &sb = st[MULTI ? buf : 0];
-    chunk_store<KD, LANES, GATED>(sb, cr, t, nr);
-    __syncthreads();
-    if (MULTI && m0 + MC < steps) {
-      const int nn = steps - m0 - MC;
-      chunk_load<KD, LANES, GATED>(cr, a, t, ti.unit, ti.head, ti.hh, m0 + MC, nn < MC ? nn : MC);
+  // the step loop over nst rows of ra's inputs, outputs to ra.o when it is
+  // non-null (the first chunk already in cr); emit_last then writes the last
+  // row's output, which the cross-wave kernel holds back one step
+  const float *zprev = nullptr;
+  auto run = [&](const RecurArgs &ra, int nst) {
+    int buf = 0;
+    for (int m0 = 0; m0 < nst; m0 += MC) {
+      const int nr = nst - m0 < MC ? nst - m0 : MC;
+      Stage<KD, GATED> &sb = st[MULTI ? buf : 0];
+      chunk_store<KD, LANES, GATED>(sb, cr, t, nr);
+      __syncthreads();
+      if (MULTI && m0 + MC < nst) {
+        const int nn = nst - m0 - MC;
+        chunk_load<KD, LANES, GATED>(cr, ra, t, ti.unit, ti.head, ti.hh, m0 + MC, nn < MC ? nn : MC);
+      }
+      for (int r = 0; r < nr; r++) {
+        const int m = m0 + r;
+        const int64_t urow = (int64_t)m * ra.n_units + ti.unit;
+        const float alpha = sb.alpha[r];
+        f4 p[4], w0, w1 = splat(0.0f);
+        f4 kkr[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) kkr[i] = lds4(&sb.k[r][(4 * L + i) * 4]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const f4 kk = kkr[i];
+          p[i] = splat(0.0f);
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            s[i][j] = s[i][j] * alpha;
+            p[i] = fma4(s[i][j], splat(kk[j]), p[i]);
+          }
+        }
+        deep_partials<KD>(p, w0, w1);
+        f4 tmp;
+        if (XWAVE) {
+          s_red_k[2 * L][cg] = w0;
+          s_red_k[2 * L + 1][cg] = w1;
+          __syncthreads();
+          if (wave == 0) {
+            const f4 kv = tile_sum<KD>(s_red_k, lane);
+            if (lane < CG) s_tmp[lane] = (lds4(&sb.v[r][4 * lane]) - kv) * sb.beta[r];
+          } else if (wave == 1 && m > 0 && ra.o != nullptr) {
+            // the previous step's output, in parallel with wave 0's S^T k
+            const f4 ov = tile_sum<KD>(s_red_o, lane);
+            const int64_t prow = (int64_t)(m - 1) * ra.n_units + ti.unit;
+            emit_o<KD, GATED>(ra, prow, ti.head, lane % CG, lane < CG, ov, zprev);
+          }
+          __syncthreads();
+          tmp = s_tmp[cg];
+        } else {
+          const f4 kv = wave_fold<KD>(w0);
+          tmp = (lds4(&sb.v[r][4 * cg]) - kv) * sb.beta[r];
+        }
+        // rank-1 update, then S^T q with the updated state
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const f4 kk = kkr[i];
+          const f4 qq = lds4(&sb.q[r][(4 * L + i) * 4]);
+          p[i] = splat(0.0f);
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            s[i][j] = fma4(splat(kk[j]), tmp, s[i][j]);
+            p[i] = fma4(s[i][j], splat(qq[j]), p[i]);
+          }
+        }
+        deep_partials<KD>(p, w0, w1);
+        if (XWAVE) {
+          s_red_o[2 * L][cg] = w0;
+          s_red_o[2 * L + 1][cg] = w1;
+        } else if (ra.o != nullptr) {
+          const f4 ov = wave_fold<KD>(w0);
+          emit_o<KD, GATED>(ra, urow, ti.head, cg, L == 0, ov, &sb.z[GATED ? r : 0][0]);
+        }
+        if constexpr (GATED) zprev = &sb.z[r][0];
+      }
+      buf ^= 1;
     }
-    for (int r = 0; r < nr; r++) {
-      const int m = m0 + r;
-      const int64_t urow = (int64_t)m * a.n_units + ti.unit;
-      const float alpha = sb.alpha[r];
-      f4 p[4], w0, w1 = splat(0.0f);
-      f4 kkr[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) kkr[i] = lds4(&sb.k[r][(4 * L + i) * 4]);
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const f4 kk = kkr[i];
-        p[i] = splat(0.0f);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          s[i][j] = s[i][j] * alpha;
-          p[i] = fma4(s[i][j], splat(kk[j]), p[i]);
-        }
+  };
+  auto emit_last = [&](const RecurArgs &ra, int nst) {
+    if (XWAVE && nst > 0) {
+      __syncthreads();
+      if (wave == 0 && ra.o != nullptr) {
+        const f4 ov = tile_sum<KD>(s_red_o, lane);
+        const int64_t urow = (int64_t)(nst - 1) * ra.n_units + ti.unit;
+        emit_o<KD, GATED>(ra, urow, ti.head, lane % CG, lane < CG, ov, zprev);
       }
-      deep_partials<KD>(p, w0, w1);
-      f4 tmp;
-      if (XWAVE) {
-        s_red_k[2 * L][cg] = w0;
-        s_red_k[2 * L + 1][cg] = w1;
-        __syncthreads();
-        if (wave == 0) {
-          const f4 kv = tile_sum<KD>(s_red_k, lane);
-          if (lane < CG) s_tmp[lane] = (lds4(&sb.v[r][4 * lane]) - kv) * sb.beta[r];
-        } else if (wave == 1 && m > 0 && a.o != nullptr) {
-          // the previous step's output, in parallel with wave 0's S^T k
-          const f4 ov = tile_sum<KD>(s_red_o, lane);
-          const int64_t prow = (int64_t)(m - 1) * a.n_units + ti.unit;
-          emit_o<KD, GATED>(a, prow, ti.head, lane % CG, lane < CG, ov, zprev);
-        }
-        __syncthreads();
-        tmp = s_tmp[cg];
-      } else {
-        const f4 kv = wave_fold<KD>(w0);
-        tmp = (lds4(&sb.v[r][4 * cg]) - kv) * sb.beta[r];
-      }
-      // rank-1 update, then S^T q with the updated state
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const f4 kk = kkr[i];
-        const f4 qq = lds4(&sb.q[r][(4 * L + i) * 4]);
-        p[i] = splat(0.0f);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          s[i][j] = fma4(splat(kk[j]), tmp, s[i][j]);
-          p[i] = fma4(s[i][j], splat(qq[j]), p[i]);
-        }
-      }
-      deep_partials<KD>(p, w0, w1);
-      if (XWAVE) {
-        s_red_o[2 * L][cg] = w0;
-        s_red_o[2 * L + 1][cg] = w1;
-      } else if (a.o != nullptr) {
-        const f4 ov = wave_fold<KD>(w0);
-        emit_o<KD, GATED>(a, urow, ti.head, cg, L == 0, ov, &sb.z[GATED ? r : 0][0]);
-      }
-      if constexpr (GATED) zprev = &sb.z[r][0];
     }
-    buf ^= 1;
-  }
+  };
 
-  if (a.S_dst != nullptr) {            // null: outputs only, the state is left as it was
+  run(a, steps);
+  // null: outputs only, the state is left as it was; a fused call with no
+  // accepted rows leaves it too
+  if (a.S_dst != nullptr && (!FUSED || steps > 0)) {
     const rsrc_t dst = buf_rsrc(a.S_dst + ti.tile_off, KD * KD * 4);
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int i = 0; i < 4; i++) st_stream(dst, lane_off, (i + RG * j) * KD * 4, s[i][j]);
   }
+  emit_last(a, steps);
 
-  if (XWAVE && steps > 0) {
-    __syncthreads();
-    if (wave == 0 && a.o != nullptr) {
-      const f4 ov = tile_sum<KD>(s_red_o, lane);
-      const int64_t urow = (int64_t)(steps - 1) * a.n_units + ti.unit;
-      emit_o<KD, GATED>(a, urow, ti.head, lane % CG, lane < CG, ov, zprev);
-    }
+  if constexpr (FUSED) {
+    // the draft rows of the next verify, from the committed state in registers
+    RecurArgs b = a;
+    b.q = a.q2;
+    b.k = a.k2;
+    b.v = a.v2;
+    b.g = a.g2;
+    b.beta = a.beta2;
+    b.o = a.o2;
+    b.M = a.M2;
+    b.steps = nullptr;
+    __syncthreads();                   // the stage and fold buffers are reused
+    chunk_load<KD, LANES, GATED>(cr, b, t, ti.unit, ti.head, ti.hh, 0, b.M < MC ? b.M : MC);
+    zprev = nullptr;
+    run(b, b.M);
+    emit_last(b, b.M);
   }
 }
 
@@ -1056,6 +1091,57 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
       launch_recur_kd<64, true>(a, tiles, s);
     else
       launch_recur_kd<64, false>(a, tiles, s);
+  }
+  return (int)hipGetLastError();
+}
+
+// gdn_commit followed by gdn_verify_m, ungated, in one pass over the state:
+// the M-step kernel applies steps[u] rows of the first set, stores the tile,
+// and runs the M2 rows of the second set from the registers (outputs only).
+// Launches the few-tile kernels would serve run as those two launches
+// instead (the same bits).
+int launch_commit_verify(int kd, float *S, const float *q, const float *k, const float *v,
+                         const float *g, const float *beta, const int32_t *steps,
+                         int32_t *status, float *hist, const float *xc_raw, int conv_dim,
+                         int64_t n_units, int vh, int kh, int M, const float *q2,
+                         const float *k2, const float *v2, const float *g2,
+                         const float *beta2, float *o2, int M2, hipStream_t s) {
+  const int64_t tiles = n_units * vh;
+  if (tiles <= 0) return 0;
+  const bool few = tiles < kWidemBelow && (int64_t)(M > M2 ? M : M2) * tiles <= kFewTileRows;
+  if (few) {
+    int rc = launch_recur(kd, S, S, q, k, v, g, beta, nullptr, steps, n_units, vh, kh, M, s,
+                          nullptr, nullptr, 0.0f, nullptr, status, hist, hist, xc_raw, conv_dim);
+    if (rc) return rc;
+    return launch_recur(kd, S, nullptr, q2, k2, v2, g2, beta2, o2, nullptr, n_units, vh, kh, M2,
+                        s);
+  }
+  RecurArgs a{S, S, q, k, v, g, beta, nullptr, steps, nullptr, nullptr, 0.0f, nullptr, status,
+              n_units, vh, kh, M, hist, hist, xc_raw, conv_dim, tiles};
+  a.q2 = q2;
+  a.k2 = k2;
+  a.v2 = v2;
+  a.g2 = g2;
+  a.beta2 = beta2;
+  a.o2 = o2;
+  a.M2 = M2;
+  const bool multi = M > MC || M2 > MC;
+  if (kd == 128) {
+    const dim3 grid((unsigned)(tiles + hist_wgs(a, Deep<128>::LANES)));
+    if (multi)
+      hipLaunchKernelGGL((recur_deep_kernel<128, true, false, true>), grid,
+                         dim3(Deep<128>::LANES), 0, s, a);
+    else
+      hipLaunchKernelGGL((recur_deep_kernel<128, false, false, true>), grid,
+                         dim3(Deep<128>::LANES), 0, s, a);
+  } else {
+    const dim3 grid((unsigned)(tiles + hist_wgs(a, Deep<64>::LANES)));
+    if (multi)
+      hipLaunchKernelGGL((recur_deep_kernel<64, true, false, true>), grid, dim3(Deep<64>::LANES),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((recur_deep_kernel<64, false, false, true>), grid,
+                         dim3(Deep<64>::LANES), 0, s, a);
   }
   return (int)hipGetLastError();
 }

@@ -31,6 +31,14 @@ int launch_recur(int kd, const float *S_src, float *S_dst, const float *q,
                  const float *hist_src = nullptr, const float *xc_raw = nullptr,
                  int conv_dim = 0);
 
+// gdn_commit then gdn_verify_m (ungated) in one pass over the state.
+int launch_commit_verify(int kd, float *S, const float *q, const float *k, const float *v,
+                         const float *g, const float *beta, const int32_t *steps,
+                         int32_t *status, float *hist, const float *xc_raw, int conv_dim,
+                         int64_t n_units, int vh, int kh, int M, const float *q2,
+                         const float *k2, const float *v2, const float *g2,
+                         const float *beta2, float *o2, int M2, hipStream_t s);
+
 // 128-bit streaming copy of n floats (src == dst allowed).
 int launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
 

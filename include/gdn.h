@@ -261,6 +261,29 @@ int gdn_commit(float *S, float *hist, const float *q, const float *k,
                const int32_t *accepted, int32_t *status, void *stream);
 
 /*
+ * gdn_commit followed by gdn_verify_m, in one pass over the state: each unit
+ * applies accepted[u] rows of the first set (q, k, v, g, beta [M][N][...],
+ * the rows of the previous verify; hist and xc_raw as in gdn_commit), the
+ * committed state is stored, and the M2 rows of the second set (q2, k2, v2,
+ * g2, beta2 [M2][N][...], the next draft rows) run from it, writing o
+ * [M2][N][vh][vd] as gdn_verify_m does; the state is not advanced by them.
+ * Same results, bit for bit, as the two calls, with one read of the state
+ * instead of two per speculative cycle ("Kestrel_VLLM #34", section 3.7:
+ * only the accepted prefix remains applied; section 3.6: the draft rows are
+ * serial steps from the current state).  1 <= M, M2 <= 64; ungated outputs.
+ * Errors: those of gdn_commit and gdn_verify_m, and GDN_EINVAL when o or
+ * the history overlaps another array of the call.
+ */
+int gdn_commit_verify_m(float *S, float *hist, const float *q, const float *k,
+                        const float *v, const float *g, const float *beta,
+                        const float *xc_raw, int32_t conv_dim, int32_t ck,
+                        int64_t n_units, int32_t M, const int32_t *accepted,
+                        int32_t *status, const float *q2, const float *k2,
+                        const float *v2, const float *g2, const float *beta2, float *o,
+                        int32_t M2, int32_t vh, int32_t kh, int32_t kd, int32_t vd,
+                        void *stream);
+
+/*
  * Front end of one GDN layer for B rows ("Kestrel_VLLM #27", section 4.2:
  * the beta and a projections as one paired launch; "Kestrel_VLLM #24",
  * section 3 and Fig. 1 caption: gate/beta transform, depthwise causal conv +

@@ -210,6 +210,20 @@ def test_verify_commit_refusals_need_no_device():
                         fp((20 << 32) + 4), NULLS) == gdn.GDN_EINVAL
     assert L.gdn_commit(S, hist, q, k, v, g, beta, xc, 10240, 4, 4, 2, vh, kh, kd, vd, acc,
                         fp((10 << 32) + 64), NULLS) == gdn.GDN_EINVAL
+    # the fused commit + verify: M2 out of range; o inside S, inside a first-set
+    # row array, or the history inside a second-set row array
+    q2, k2, v2, g2, b2, o2 = (fp((40 + i) << 32) for i in range(6))
+    cv = lambda S_, hist_, o_, M2_, q2_=q2: L.gdn_commit_verify_m(  # noqa: E731
+        S_, hist_, q, k, v, g, beta, xc if hist_ else NULLS, 10240 if hist_ else 0, 4, 4, 2, acc,
+        NULLS, q2_, k2, v2, g2, b2, o_, M2_, vh, kh, kd, vd, NULLS)
+    assert cv(S, NULLS, o2, 0) == gdn.GDN_EINVAL
+    assert cv(S, NULLS, o2, 65) == gdn.GDN_EINVAL
+    assert cv(S, NULLS, fp((2 << 32) + 4096), 2) == gdn.GDN_EINVAL          # o inside S
+    assert cv(S, NULLS, fp((5 << 32) + 512), 2) == gdn.GDN_EINVAL           # o inside v
+    assert cv(S, hist, o2, 2, q2_=fp((10 << 32) + 256)) == gdn.GDN_EINVAL   # q2 inside the history
+    assert cv(S, NULLS, o2, 2, q2_=NULLS) == gdn.GDN_EINVAL
+    assert L.gdn_commit_verify_m(S, NULLS, q, k, v, g, beta, NULLS, 0, 4, 0, 2, acc, NULLS, q2, k2,
+                                 v2, g2, b2, o2, 2, vh, kh, kd, vd, NULLS) == gdn.GDN_OK
     # the history replay's workgroups count towards the grid limit: 64 units of
     # 2^28 channels need 2^32 replay lanes
     assert L.gdn_commit(S, hist, q, k, v, g, beta, xc, 1 << 28, 4, 64, 2, vh, kh, kd, vd, acc,

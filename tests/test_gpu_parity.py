@@ -938,6 +938,51 @@ def test_commit_single_step_history_beyond_65536_units(orc):
     assert bits_equal(host(S[-1]), S0[-1]) and bits_equal(host(hist[-1]), h0[-1])
 
 
+@pytest.mark.parametrize("dims,N,M,M2", [(synth.DIMS128, 24, 8, 8), (synth.DIMS64, 11, 3, 5),
+                                         (synth.DIMS128, 24, 10, 12), (synth.DIMS128, 1, 8, 8),
+                                         (synth.DIMS64, 2, 4, 4)])
+def test_commit_verify_fused_equals_two_calls(orc, dims, N, M, M2):
+    """gdn_commit_verify_m against gdn_commit followed by gdn_verify_m on the
+    same inputs: state, history, outputs and status word bit for bit, with one
+    out-of-range count (that unit keeps its state and history and still
+    verifies).  1152 and 1056 tiles run the fused M-step launch (12 rows
+    prefetched in one case), 48 and 192 tiles the two launches.  Then the
+    oracle: the committed state is the oracle's rollback to the accepted
+    rows, and the outputs its M2 steps from there."""
+    say(f"commit+verify fused dims={dims} N={N} M={M} M2={M2}")
+    vh, kh, kd, vd = dims
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(18 + N, "cuda")
+    S0 = synth.state(gen, N, dims, device="cuda")
+    prev = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    new = synth.step_inputs(gen, N, dims, M=M2, device="cuda")
+    h0 = torch.randn((N, 3, cd), generator=gen, device="cuda")
+    xc = torch.randn((M, N, cd), generator=gen, device="cuda")
+    acc = torch.randint(0, M + 1, (N,), generator=gen, device="cuda").to(torch.int32)
+    if N > 1:
+        acc[1] = M + 1                                  # refused: unit 1 stays as it is
+    S_a, h_a, st_a = S0.clone(), h0.clone(), torch.zeros(1, dtype=torch.int32, device="cuda")
+    o_a = gdn.commit_verify_m(S_a, acc, *(prev[n] for n in NAMES), *(new[n] for n in NAMES),
+                              hist=h_a, xc_raw=xc, status=st_a)
+    S_b, h_b, st_b = S0.clone(), h0.clone(), torch.zeros(1, dtype=torch.int32, device="cuda")
+    gdn.commit(S_b, acc, *(prev[n] for n in NAMES), hist=h_b, xc_raw=xc, status=st_b)
+    o_b = gdn.verify_m(S_b, *(new[n] for n in NAMES))
+    assert bits_equal(host(S_a), host(S_b))
+    assert bits_equal(host(h_a), host(h_b))
+    assert bits_equal(host(o_a), host(o_b))
+    assert int(st_a.item()) == int(st_b.item()) == (1 if N > 1 else 0)
+    acc_ref = host(acc).copy()
+    if N > 1:
+        acc_ref[1] = 0
+    _, _, S_rb, h_rb = ref_cycle(orc, host(S0), {n: host(prev[n]) for n in NAMES}, dims, acc_ref,
+                                 host(h0), host(xc))
+    assert_close(host(S_a), S_rb, "S after the fused commit")
+    assert bits_equal(host(h_a), h_rb)
+    o_ref = np.zeros((M2, N, vh, vd), np.float32)
+    orc.gdn_step_m(S_rb.copy(), *(host(new[n]) for n in NAMES), o_ref, M2, dims)
+    assert_close(host(o_a), o_ref, "o of the fused verify")
+
+
 def test_verify_cycle_graph_replay(orc):
     """One layer's speculative cycle without a snapshot -- front end for the M
     draft rows (history read only), verify, commit with device-side accepted
