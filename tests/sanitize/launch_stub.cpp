@@ -30,6 +30,14 @@ int launch_recur(int, const float *, float *, const float *, const float *, cons
   return launched();
 }
 
+int launch_commit_verify(int, float *, const float *, const float *, const float *,
+                         const float *, const float *, const int32_t *, int32_t *, float *,
+                         const float *, int, int64_t, int, int, int, const float *,
+                         const float *, const float *, const float *, const float *, float *,
+                         int, hipStream_t) {
+  return launched();
+}
+
 int launch_copy(float *, const float *, int64_t, hipStream_t) { return launched(); }
 
 int64_t read_chunks(int64_t n) {
