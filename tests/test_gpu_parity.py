@@ -983,6 +983,62 @@ def test_commit_verify_fused_equals_two_calls(orc, dims, N, M, M2):
     assert_close(host(o_a), o_ref, "o of the fused verify")
 
 
+def test_commit_verify_fused_graph_replay():
+    """Two steady-state cycles of the fused call (each commits the previous
+    rows' accepted prefix and verifies the next rows) captured as one graph on
+    the fused M-step path (1152 tiles) and replayed three times, with eager
+    work between replays: state, history and both cycles' outputs equal the
+    eager sequence bit for bit."""
+    dims = synth.DIMS128
+    vh, kh, kd, vd = dims
+    N, M = 24, 4
+    cd = synth.conv_dim_of(dims)
+    gen = synth.make_gen(23, "cuda")
+    S0 = synth.state(gen, N, dims, device="cuda")
+    r1 = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    r2 = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    r3 = synth.step_inputs(gen, N, dims, M=M, device="cuda")
+    h0 = torch.randn((N, 3, cd), generator=gen, device="cuda")
+    x1 = torch.randn((M, N, cd), generator=gen, device="cuda")
+    x2 = torch.randn((M, N, cd), generator=gen, device="cuda")
+    a1 = torch.randint(0, M + 1, (N,), generator=gen, device="cuda").to(torch.int32)
+    a2 = torch.randint(0, M + 1, (N,), generator=gen, device="cuda").to(torch.int32)
+    o2 = torch.empty((M, N, vh, vd), device="cuda")
+    o3 = torch.empty((M, N, vh, vd), device="cuda")
+    S, hist = S0.clone(), h0.clone()
+
+    def cycles():
+        gdn.commit_verify_m(S, a1, *(r1[n] for n in NAMES), *(r2[n] for n in NAMES), o=o2,
+                            hist=hist, xc_raw=x1)
+        gdn.commit_verify_m(S, a2, *(r2[n] for n in NAMES), *(r3[n] for n in NAMES), o=o3,
+                            hist=hist, xc_raw=x2)
+
+    cycles()
+    torch.cuda.synchronize()
+    S_e, h_e, o2_e, o3_e = host(S), host(hist), host(o2), host(o3)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        S.copy_(S0)
+        hist.copy_(h0)
+        cycles()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cycles()
+    for rep in range(3):
+        S.copy_(S0)
+        hist.copy_(h0)
+        o2.zero_()
+        o3.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert bits_equal(host(S), S_e) and bits_equal(host(hist), h_e), rep
+        assert bits_equal(host(o2), o2_e) and bits_equal(host(o3), o3_e), rep
+        gdn.step(S0.clone(), *(r1[n][0] for n in NAMES))   # eager work between replays
+
+
 def test_verify_cycle_graph_replay(orc):
     """One layer's speculative cycle without a snapshot -- front end for the M
     draft rows (history read only), verify, commit with device-side accepted
