@@ -2421,51 +2421,66 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 // Dense layer projections with 4-bit weights
 // ---------------------------------------------------------------------------
 //
-// Up to 16 rows the product is bound by the weight stream, and a 4-bit weight
-// is 0.56 bytes: the matrix-core kernel above, whose 16-row operand is mostly
-// empty at these sizes, would hold it near 1.5 TB/s of weights.  Here a lane
-// owns one output and a column segment.  It decodes each 32-column block of
-// its weights once and runs one fma chain per row against x, which all lanes
-// of a wave read at the same address (scalar loads, the next row's issued
-// before the current row's chain).
+// Up to 16 rows the product streams 0.56 bytes per weight.  A VALU kernel that
+// forms each weight n s in fp32 and runs an fma chain per row spends about
+// 1.75 + rows instructions per weight and is instruction-bound from 2 rows
+// on.  Here the products run on the fp16 matrix cores
+// (v_mfma_f32_16x16x32_f16, 16 row slots x 16 outputs x 32 columns, fp32
+// accumulation), with every operand exact:
+//  - the 4-bit value n is exact in binary16: two biased values u = n + 8 are
+//    masked into the mantissas of a binary16 pair, (w & m) | 0x6400 6400,
+//    giving 1024 + u or 1024 + 16 u, and one packed fp16 add or fma gives n
+//    (1024 + u - 1032, or (1024 + 16 u) / 16 - 72): nine instructions per 8
+//    weights;
+//  - x is scaled by a power of two 2^k per row and 256-column chunk (the
+//    chunk's largest magnitude lands in [2^14, 2^15)) and split into two
+//    binary16 parts, x1 = rn(2^k x) and x2 = rn(2^k x - x1), which hold 22 of
+//    its 24 significant bits; the two parts of a row take two row slots, so one
+//    instruction covers 8 rows;
+//  - the block's binary16 scale s multiplies the fp32 sum of the block in a
+//    mixed-precision fma (exact conversion, one rounding).
+// The MFMA's result for one output does not depend on the other slots or on
+// its own slot position, so a row's bits do not depend on the row count.
 //
-// Summation order of y[r][o], fixed and independent of the row count: C is
-// cut into 32 equal segments, each an ascending fma chain over its columns;
-// segments 0..15 are folded left to right, so are segments 16..31, and the
-// two sums are added.  Two launch shapes compute exactly that:
-//  - one workgroup per 64-output group (16 waves; wave w chains segments w
-//    and 16 + w into separate accumulators; both folds in LDS), for launches
-//    with enough groups to fill the chip;
-//  - two workgroups per group (workgroup h, wave w: segment 16 h + w), each
-//    folding its 16 segment sums and adding the result into y, which a fill
-//    kernel zeroed first.  With exactly two addends on +0 the result does not
-//    depend on their arrival order (fp addition is commutative, and a chain
-//    started at +0 never ends at -0), so it is bit-identical to the first
-//    shape.  Used when the launch has fewer groups than the chip has CUs
-//    (out_proj: 80 groups).
+// Summation order of y[r][o], fixed and independent of the row count: C is cut
+// into 4 quarters; in quarter q, for each chunk of 8 blocks of 32 columns,
+// cacc = +0 and for each block j in order cacc = fma(T_j, s[o][j], cacc) with
+// T_j = D1_j + D2_j (the MFMA dot products of the block's n with x1 and x2);
+// the chunk's cacc, scaled back by 2^-k, is added to acc_q (+0 first);
+// y = (acc_0 + acc_1) + (acc_2 + acc_3).  The launch shapes all compute
+// exactly that:
+//  - one 16-wave workgroup per group of 4 column tiles (64 outputs; wave =
+//    column tile x quarter), the quarter sums folded in LDS, for launches of
+//    up to 8 rows with enough groups to fill the chip;
+//  - two workgroups per group of 4 or 2 column tiles (quarters 0-1 and 2-3),
+//    each adding its half into y, which a fill kernel zeroed first.  With
+//    exactly two addends on +0 the result does not depend on their arrival
+//    order (fp addition is commutative, and none of these sums is -0), so the
+//    shapes give the same bits.  Used for launches with fewer groups than the
+//    chip has CUs (out_proj: 80 groups) and for 9 to 16 rows.
+// Each row's x is split once per workgroup.  For 1 to 3 rows all of it is
+// staged up front, compactly (only the live row slots; a slot past the rows
+// reads a live slot's x, and its result is never stored), and the K loop runs
+// without a barrier (proj_q4_pre_kernel).  For more rows it is staged chunk by
+// chunk into two alternating LDS buffers, one barrier per chunk, its loads
+// issued two chunks ahead (proj_q4_kernel).  Either way each lane converts 8
+// columns of a row, and the 32 lanes of a row's chunk reduce its largest
+// magnitude with lane exchanges.  The weights stream two chunks ahead of use.
 //
-// Decode: two 4-bit values are masked into the mantissas of a pair of
-// binary16 numbers in one instruction, (q & m) | 0x6400 6400, giving 1024 + u
-// or 1024 + 16 u (u = n + 8, as packed); one mixed-precision fma per weight
-// then forms n s exactly: (1024 + u) s - 1032 s, or (1024 + 16 u) (s / 16) -
-// 72 s.  Every product is exact in the fma and n s is representable, so the
-// single rounding is exact (1032 s and 72 s are exact in fp32 since 1032 and
-// 72 have two set bits each).
-//
-// Packed layout, per 64-output group g and 32-column block b (1152 bytes):
-// output 64 g + l holds 16 bytes at 16 l, where byte k of dword d holds
-// u = n + 8 (n the signed 4-bit value) of column 32 b + 8 d + k in its low
-// nibble and of column 32 b + 8 d + 4 + k in its high nibble; then the 64
-// binary16 scales of the block at 1024 + 2 l.
+// Packed layout, per 16-output column tile t and chunk m of 8 blocks of 32
+// columns (2304 bytes, t-major): dword 8 (16 d + o) + i holds output
+// 16 t + o's biased values u = n + 8 of columns 256 m + 32 i + 8 d + k,
+// k = 0..7, value k at bit 4 (k >> 1) + 16 (k & 1), so that lane 16 d + o
+// reads its 8 blocks of the chunk as 32 contiguous bytes; then at 2048 + 16 o
+// the 8 binary16 scales of output 16 t + o for the chunk's blocks.
 
-// launches with fewer 64-output groups than this take two workgroups per group
-constexpr int64_t kQ4SplitBelow = 256;
-constexpr int Q4_SEGS = 16;                    // waves per workgroup
-constexpr int Q4_LANES = 64 * Q4_SEGS;
-constexpr int Q4_BLOCK_BYTES = 1152;
-constexpr int Q4_PF = 4;                       // blocks in flight per wave
+// launches that one workgroup per 4 column tiles would give fewer workgroups
+// than this take two workgroups per group (of 4 or 2 tiles)
+constexpr int kQ4SplitBelow = 256;
+constexpr int Q4_CH = 8;                       // blocks per quarter per chunk
+constexpr int Q4_TC = 2304;                    // bytes per column tile and chunk
 // a buffer offset beyond every resource's range: the load returns zeros and
-// touches no memory (prefetch slots past a wave's last block)
+// touches no memory (prefetch of the chunk after the last)
 constexpr int Q4_OOB = (int)0x80000000u;
 
 struct Q4Problem {
@@ -2476,9 +2491,13 @@ struct Q4Problem {
 };
 struct Q4Args {
   const float *x;
+  int rows;
   int C;
   Q4Problem p[2];
 };
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 // (x & m) | c in one instruction: the mask from a scalar register, the
 // constant from a vector register (a VOP3 takes no literal on this target)
@@ -2487,176 +2506,464 @@ static __device__ __forceinline__ unsigned and_or(unsigned x, unsigned m, unsign
   __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
   return r;
 }
-static __device__ __forceinline__ float half_lo(unsigned p) {
-  return (float)__builtin_bit_cast(_Float16, (unsigned short)(p & 0xffffu));
-}
-static __device__ __forceinline__ float half_hi(unsigned p) {
-  return (float)__builtin_bit_cast(_Float16, (unsigned short)(p >> 16));
+
+// 8 biased 4-bit values of one output (one packed dword) -> the binary16
+// values n, exact, in column order
+static __device__ __forceinline__ h8 q4_decode(unsigned w, unsigned magic) {
+  const h2 m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const h2 r16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2 m72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const unsigned w8 = w >> 8;
+  const h2 a = __builtin_bit_cast(h2, and_or(w, 0x000f000fu, magic)) + m1032;
+  const h2 b = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w, 0x00f000f0u, magic)),
+                                         r16, m72);
+  const h2 c = __builtin_bit_cast(h2, and_or(w8, 0x000f000fu, magic)) + m1032;
+  const h2 d = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w8, 0x00f000f0u, magic)),
+                                         r16, m72);
+  return h8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-// SPLIT: two workgroups per group (each one half of C), else one
-template <int NR, bool SPLIT>
-__global__ __launch_bounds__(Q4_LANES) void proj_q4_kernel(Q4Args a) {
-  __shared__ float red[Q4_SEGS][NR][64];
-  const int b = (int)xcd_contiguous(blockIdx.x, gridDim.x);
-  const bool second = b >= a.p[0].wgs;
+// v - (float)h (h the low or high binary16 of p) in one mixed-precision fma:
+// exact, since h is v rounded to binary16
+template <bool HI>
+static __device__ __forceinline__ float minus_half(unsigned p, float v) {
+  float r;
+  if constexpr (HI)
+    __asm__("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+            : "=v"(r) : "v"(p), "v"(v));
+  else
+    __asm__("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+            : "=v"(r) : "v"(p), "v"(v));
+  return r;
+}
+
+static __device__ __forceinline__ unsigned pk_half(float a, float b) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f2v){a, b}, h2));
+}
+
+// 8 consecutive x of one row (v) -> the chunk's exponent k (shared by the 32
+// lanes of the row's chunk, which hold its 256 columns) and the two binary16
+// parts of 2^k v, each as 4 packed pairs
+static __device__ __forceinline__ int x_split(const f4 &x0, const f4 &x1, unsigned (&p1)[4],
+                                              unsigned (&p2)[4]) {
+  const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e++) m = fmaxf(m, fabsf(v[e]));     // NaN is passed over
+  m = fmaxf(m, lane_xor<16>(m));
+  m = fmaxf(m, lane_xor<8>(m));
+  m = fmaxf(m, lane_xor<4>(m));
+  m = fmaxf(m, lane_xor<2>(m));
+  m = fmaxf(m, lane_xor<1>(m));
+  // largest magnitude in [2^14, 2^15) after scaling (m = 0: any k)
+  const int k = 15 - __builtin_amdgcn_frexp_expf(m);
+  const h2 lo = {(_Float16)-65504.0f, (_Float16)-65504.0f};
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const float s0 = __builtin_amdgcn_ldexpf(v[2 * e], k);
+    const float s1 = __builtin_amdgcn_ldexpf(v[2 * e + 1], k);
+    p1[e] = pk_half(s0, s1);
+    // an infinite x gives a NaN residual: replaced by a finite value (max
+    // passes over NaN), so the infinity itself (x1) reaches the sum
+    const unsigned r = pk_half(minus_half<false>(p1[e], s0), minus_half<true>(p1[e], s1));
+    p2[e] = __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(h2, r), lo));
+  }
+  return k;
+}
+
+// NT: row tiles of 8 rows (rows <= 8 NT); SPLIT: two workgroups per group of
+// CT column tiles (quarters 0-1 and 2-3), else one (all four quarters)
+template <int NT, bool SPLIT, int CT>
+__global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Args a) {
+  static_assert(CT == 2 || CT == 4, "4 or 2 column tiles per workgroup");
+  constexpr int NQ = SPLIT ? 2 : 4;            // quarters per workgroup
+  constexpr int NTHR = 64 * CT * NQ;
+  constexpr int STAGE = NQ * Q4_CH * NT * 1024;
+  __shared__ __align__(16) unsigned char xs[2][STAGE];
+  __shared__ int kexp[2][NQ][8 * NT];
+  const int bid = (int)xcd_contiguous(blockIdx.x, gridDim.x);
+  const bool second = bid >= a.p[0].wgs;
   const uint8_t *W = second ? a.p[1].W : a.p[0].W;
   float *y = second ? a.p[1].y : a.p[0].y;
   const int R = second ? a.p[1].R : a.p[0].R;
-  const int gh = second ? b - a.p[0].wgs : b;
+  const int gh = second ? bid - a.p[0].wgs : bid;
   const int g = SPLIT ? gh >> 1 : gh;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int l = threadIdx.x & 63;
-  const int C = a.C, nblk = C / 32, sblk = nblk / (2 * Q4_SEGS);
-  // this wave's segments: one (SPLIT) or w and 16 + w, as trips t = 0 ..
-  // nt - 1 over blocks; trip t of the second segment starts at sblk
-  const int seg0 = SPLIT ? (gh & 1) * Q4_SEGS + wave : wave;
-  const int nt = SPLIT ? sblk : 2 * sblk;
-  auto blk_of = [&](int t) {
-    if constexpr (SPLIT)
-      return seg0 * sblk + t;
-    else
-      return t < sblk ? seg0 * sblk + t : (Q4_SEGS + wave) * sblk + (t - sblk);
-  };
-  // one buffer resource over the group's packed bytes (< 2^31 for C <= 2^22)
+  const int q0 = SPLIT ? 2 * (gh & 1) : 0;     // first quarter of this workgroup
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int ct = wave % CT, qw = wave / CT;
+  const int q = q0 + qw;
+  const int C = a.C, rows = a.rows, nblk = C / 32, Q = nblk / 4, nch = Q / Q4_CH;
+  const int tile = CT * g + ct;
   const rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(W + (int64_t)g * nblk * Q4_BLOCK_BYTES), 0, nblk * Q4_BLOCK_BYTES,
-      RSRC_FLAGS);
+      const_cast<uint8_t *>(W + (int64_t)tile * (nblk / Q4_CH) * Q4_TC), 0,
+      nblk / Q4_CH * Q4_TC, RSRC_FLAGS);
 
-  u4 qb[Q4_PF];
-  unsigned sb[Q4_PF];
-  // every trip issues its loads (no branch around them, so the wait counts
-  // stay exact and the prefetch depth holds); slots past the last trip read
-  // out of range
-  auto issue = [&](int slot, int t) {
-    const bool ok = t < nt;
-    const int soff = __builtin_amdgcn_readfirstlane((ok ? blk_of(t) : 0) * Q4_BLOCK_BYTES);
-    qb[slot] = __builtin_bit_cast(
-        u4, __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? 16 * l : Q4_OOB, soff,
-                                                  POL_STREAM_LOAD));
-    sb[slot] = __builtin_amdgcn_raw_buffer_load_b16(wr, ok ? 1024 + 2 * l : Q4_OOB, soff,
-                                                    POL_STREAM_LOAD);
-  };
-#pragma unroll
-  for (int p = 0; p < Q4_PF; p++) issue(p, p);
+  // zero both stage buffers: row slots past `rows` stay zero
+  for (int i = tid; i < 2 * STAGE / 16; i += NTHR)
+    reinterpret_cast<u4 *>(&xs[0][0])[i] = u4{0, 0, 0, 0};
 
-  float acc0[NR], acc1[NR];                    // first and second segment
+  // x staging: item = (quarter slot, row, block in chunk, d) with d, then the
+  // block, fastest, so the 32 lanes of a row's chunk are one half-wave; at
+  // most NQ 8 NT 32 items, ITEMS per lane.  Stage layout: per quarter slot,
+  // block and row tile a 1 KiB operand tile, row slot s of column group d at
+  // 16 (16 d + (s ^ i ^ 8 (d & 1))) for block i of the chunk.
+  constexpr int ITEMS = 4 * NT / CT;
+  const int nitems = NQ * rows * Q4_CH * 4;
+  // the lane's items, the same in every chunk: x element offset in chunk 0
+  // (-1: no item), LDS byte offset, exponent slot
+  int xoff[ITEMS], xdst[ITEMS], xkix[ITEMS];
 #pragma unroll
-  for (int r = 0; r < NR; r++) acc0[r] = acc1[r] = 0.f;
-  unsigned base = 0x64006400u;                 // binary16 1024 in both halves
-  __asm__("" : "+v"(base));                    // kept in a vector register
-  // x at the start of each of the wave's segments, row 0
-  const float *xs0 = a.x + seg0 * sblk * 32;
-  const float *xs1 = SPLIT ? xs0 : a.x + (Q4_SEGS + wave) * sblk * 32;
-  auto block = [&](const u4 &q, unsigned sbits, const float *xb, float (&acc)[NR]) {
-    const float sf = (float)__builtin_bit_cast(_Float16, (unsigned short)sbits);
-    const float m1032 = -1032.f * sf, sf16 = 0.0625f * sf, m72 = -72.f * sf;
-    float w[32];
-#pragma unroll
-    for (int d = 0; d < 4; d++) {
-      const unsigned qd = q[d], q8 = qd >> 8;
-      const unsigned p0 = and_or(qd, 0x000f000fu, base);   // nibbles 0, 4: 1024 + u
-      const unsigned p1 = and_or(qd, 0x00f000f0u, base);   // nibbles 1, 5: 1024 + 16 u
-      const unsigned p2 = and_or(q8, 0x000f000fu, base);   // nibbles 2, 6
-      const unsigned p3 = and_or(q8, 0x00f000f0u, base);   // nibbles 3, 7
-      // nibble j of word d is column 8 d + j / 2 + 4 (j % 2)
-      w[8 * d + 0] = __builtin_fmaf(half_lo(p0), sf, m1032);
-      w[8 * d + 2] = __builtin_fmaf(half_hi(p0), sf, m1032);
-      w[8 * d + 4] = __builtin_fmaf(half_lo(p1), sf16, m72);
-      w[8 * d + 6] = __builtin_fmaf(half_hi(p1), sf16, m72);
-      w[8 * d + 1] = __builtin_fmaf(half_lo(p2), sf, m1032);
-      w[8 * d + 3] = __builtin_fmaf(half_hi(p2), sf, m1032);
-      w[8 * d + 5] = __builtin_fmaf(half_lo(p3), sf16, m72);
-      w[8 * d + 7] = __builtin_fmaf(half_hi(p3), sf16, m72);
-    }
-    float xc[32], xn[32];
-#pragma unroll
-    for (int i = 0; i < 32; i++) xc[i] = xb[i];
-#pragma unroll
-    for (int r = 0; r < NR; r++) {
-      if (r + 1 < NR) {
-#pragma unroll
-        for (int i = 0; i < 32; i++) xn[i] = xb[(int64_t)(r + 1) * C + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 32; i++) acc[r] = __builtin_fmaf(w[i], xc[i], acc[r]);
-#pragma unroll
-      for (int i = 0; i < 32; i++) xc[i] = xn[i];
-    }
-  };
-
-  for (int t0 = 0; t0 < nt; t0 += Q4_PF) {
-#pragma unroll
-    for (int p = 0; p < Q4_PF; p++) {
-      // the slot is consumed before it is refilled, so each load lands in
-      // the register its consumer reads (no copies, no drain at the loop end)
-      const int t = t0 + p;
-      if (t < nt) {
-        if (SPLIT || t < sblk)
-          block(qb[p], sb[p], xs0 + t * 32, acc0);
-        else
-          block(qb[p], sb[p], xs1 + (t - sblk) * 32, acc1);
-      }
-      issue(p, t + Q4_PF);
-    }
+  for (int it = 0; it < ITEMS; it++) {
+    const int idx = tid + it * NTHR;
+    const bool ok = idx < nitems;
+    const int d = idx & 3, i = (idx >> 2) & 7, rest = idx >> 5;
+    const int bb = ok ? rest % rows : 0, qi = ok ? rest / rows : 0;
+    xoff[it] = ok ? bb * C + ((q0 + qi) * Q + i) * 32 + 8 * d : -1;
+    // slot 2 (bb % 8) of row d in block i's tile, swizzled (the 32 lanes of a
+    // row's chunk would otherwise store to one bank group)
+    xdst[it] = ((qi * Q4_CH + i) * NT + bb / 8) * 1024 +
+               16 * (16 * d + ((2 * (bb % 8)) ^ i ^ (8 * (d & 1))));
+    xkix[it] = qi * 8 * NT + bb;
   }
-
-  // left fold of the workgroup's 16 segment sums (per accumulator set)
-  const int r_f = threadIdx.x >> 6, l_f = threadIdx.x & 63;
-  auto fold = [&](float (&acc)[NR]) -> float {
+  // x of a chunk, in three register sets rotating with the weight sets
+  struct XSet {
+    f4 v[ITEMS][2];
+  };
+  // buffer loads with an out-of-range offset for a missing item: no branch,
+  // so the wait counts stay exact
+  const rsrc_t xr = buf_rsrc(a.x, rows * C * 4);
+  auto x_issue = [&](XSet &xv, int ch) {
 #pragma unroll
-    for (int r = 0; r < NR; r++) red[wave][r][l] = acc[r];
+    for (int it = 0; it < ITEMS; it++) {
+      const bool ok = xoff[it] >= 0 && ch < nch;
+      const int vo = ok ? 4 * (xoff[it] + ch * Q4_CH * 32) : Q4_OOB;
+      xv.v[it][0] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(xr, vo, 0, 0));
+      xv.v[it][1] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(xr, vo, 16, 0));
+    }
+  };
+  auto x_stage = [&](const XSet &xv, int ch) {
+    unsigned char *buf = xs[ch & 1];
+#pragma unroll
+    for (int it = 0; it < ITEMS; it++) {
+      unsigned p1[4], p2[4];
+      const int k = x_split(xv.v[it][0], xv.v[it][1], p1, p2);
+      if (xoff[it] >= 0) {
+        *reinterpret_cast<u4 *>(buf + xdst[it]) = u4{p1[0], p1[1], p1[2], p1[3]};
+        *reinterpret_cast<u4 *>(buf + (xdst[it] ^ 16)) = u4{p2[0], p2[1], p2[2], p2[3]};
+        if ((l & 31) == 0) (&kexp[ch & 1][0][0])[xkix[it]] = k;
+      }
+    }
+  };
+
+  // weights of chunk ch: the lane's 8 dwords (blocks q Q + ch CH + 0..7) and
+  // its output's 8 scales, three 128-bit loads
+  struct WSet {
+    u4 w0, w1, s;
+  };
+  auto w_issue = [&](WSet &ws, int ch) {
+    const bool ok = ch < nch;
+    const int so = __builtin_amdgcn_readfirstlane((ok ? q * nch + ch : 0) * Q4_TC);
+    ws.w0 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       wr, ok ? 32 * l : Q4_OOB, so, POL_STREAM_LOAD));
+    ws.w1 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       wr, ok ? 32 * l + 16 : Q4_OOB, so, POL_STREAM_LOAD));
+    ws.s = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                      wr, ok ? 2048 + 16 * (l & 15) : Q4_OOB, so,
+                                      POL_STREAM_LOAD));
+  };
+
+  // Loads return in order, so a chunk's x is requested two chunks ahead,
+  // before the weights it would otherwise wait behind.
+  WSet S0, S1, S2;
+  XSet X0, X1, X2;
+  x_issue(X0, 0);
+  w_issue(S0, 0);
+  x_issue(X1, 1);
+  w_issue(S1, 1);
+  __syncthreads();                             // zeroed buffers before staging
+  x_stage(X0, 0);
+  __syncthreads();
+
+  unsigned magic = 0x64006400u;                // binary16 1024 in both halves
+  __asm__("" : "+v"(magic));                   // kept in a vector register
+  float acc[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; t++) acc[t][0] = acc[t][1] = 0.f;
+
+  // one chunk: issue chunk ch + 2's x and weights, compute chunk ch, stage
+  // chunk ch + 1's x, one barrier
+  auto chunk = [&](const WSet &cur, WSet &pf, const XSet &xn, XSet &xf, int ch) {
+    x_issue(xf, ch + 2);
+    w_issue(pf, ch + 2);
+    if (ch < nch) {
+      // lane l reads slot l % 16 of row l / 16, at the writers' swizzled place
+      const unsigned char *buf = xs[ch & 1] + (qw * Q4_CH) * NT * 1024;
+      const int lx = 16 * (l ^ ((l >> 1) & 8));
+      float cacc[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; t++) cacc[t][0] = cacc[t][1] = 0.f;
+      // four blocks at a time: operands, products, then the chains
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        f4 D[4][NT];
+        float sv[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int i = 4 * h + j;
+          const h8 B = q4_decode(h ? cur.w1[j] : cur.w0[j], magic);
+          const unsigned sw = cur.s[i >> 1];
+          sv[j] = (float)__builtin_bit_cast(_Float16,
+                                            (unsigned short)((i & 1) ? sw >> 16 : sw & 0xffffu));
+#pragma unroll
+          for (int t = 0; t < NT; t++) {
+            const h8 A =
+                *reinterpret_cast<const h8 *>(buf + (i * NT + t) * 1024 + (lx ^ (16 * i)));
+            D[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int t = 0; t < NT; t++) {
+            cacc[t][0] = __builtin_fmaf(D[j][t].x + D[j][t].y, sv[j], cacc[t][0]);
+            cacc[t][1] = __builtin_fmaf(D[j][t].z + D[j][t].w, sv[j], cacc[t][1]);
+          }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+          const int k = kexp[ch & 1][qw][8 * t + 2 * (l >> 4) + r];
+          acc[t][r] = acc[t][r] + __builtin_amdgcn_ldexpf(cacc[t][r], -k);
+        }
+    }
+    if (ch + 1 < nch) x_stage(xn, ch + 1);
     __syncthreads();
-    float sum = 0.f;
-    if (threadIdx.x < NR * 64) {
-      sum = red[0][r_f][l_f];
-#pragma unroll
-      for (int w = 1; w < Q4_SEGS; w++) sum = sum + red[w][r_f][l_f];
-    }
-    return sum;
   };
-  float sum = fold(acc0);
-  if constexpr (!SPLIT) {
-    __syncthreads();                           // every fold read before the next writes
-    sum = sum + fold(acc1);
+  for (int ch = 0; ch < nch; ch += 3) {
+    chunk(S0, S2, X1, X2, ch);
+    chunk(S1, S0, X2, X0, ch + 1);
+    chunk(S2, S1, X0, X1, ch + 2);
   }
-  if (threadIdx.x < NR * 64) {
-    float *dst = y + (int64_t)r_f * R + 64 * g + l_f;
-    if constexpr (SPLIT)
-      atomicAdd(dst, sum);                     // two addends on +0: order-free
-    else
-      *dst = sum;
+
+  // fold the quarters: wave (ct, qw) -> LDS; the first quarter's waves add
+  float *fold = reinterpret_cast<float *>(&xs[0][0]);   // [ct][qw][t][r][64]
+#pragma unroll
+  for (int t = 0; t < NT; t++)
+#pragma unroll
+    for (int r = 0; r < 2; r++) fold[(((ct * NQ + qw) * NT + t) * 2 + r) * 64 + l] = acc[t][r];
+  __syncthreads();
+  if (qw == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+      for (int r = 0; r < 2; r++) {
+        auto at = [&](int qq) { return fold[(((ct * NQ + qq) * NT + t) * 2 + r) * 64 + l]; };
+        const int row = 8 * t + 2 * (l >> 4) + r;
+        float v = acc[t][r] + at(1);
+        if constexpr (!SPLIT) v = v + (at(2) + at(3));
+        if (row < rows) {
+          float *dst = y + (int64_t)row * R + 16 * tile + (l & 15);
+          if constexpr (SPLIT)
+            atomicAdd(dst, v);                 // two addends on +0: order-free
+          else
+            *dst = v;
+        }
+      }
   }
 }
 
-// 4-bit packing: thread (group g, block b, lane l) writes output 64 g + l's
-// 16 bytes of block b and its scale.
+// Launches of few rows stage all of their x once, compactly (only the live
+// row slots), and then run the K loop without barriers: LDS bytes for the x
+// parts of a workgroup's column range, and ints for its chunk exponents.
+constexpr int Q4_PRE_BYTES = 65536;
+constexpr int Q4_PRE_K = 256;
+
+// The same order as proj_q4_kernel for NR rows (1..3), every x chunk staged
+// in the prologue.
+template <bool SPLIT, int CT, int NR>
+__global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(Q4Args a) {
+  static_assert(CT == 2 || CT == 4, "4 or 2 column tiles per workgroup");
+  constexpr int NQ = SPLIT ? 2 : 4;            // quarters per workgroup
+  constexpr int NTHR = 64 * CT * NQ;
+  // x parts [block of the range][d][live slot][16 bytes]
+  __shared__ __align__(16) unsigned char xp[Q4_PRE_BYTES];
+  __shared__ int kp[Q4_PRE_K];                 // [row][chunk of the range]
+  const int bid = (int)xcd_contiguous(blockIdx.x, gridDim.x);
+  const bool second = bid >= a.p[0].wgs;
+  const uint8_t *W = second ? a.p[1].W : a.p[0].W;
+  float *y = second ? a.p[1].y : a.p[0].y;
+  const int R = second ? a.p[1].R : a.p[0].R;
+  const int gh = second ? bid - a.p[0].wgs : bid;
+  const int g = SPLIT ? gh >> 1 : gh;
+  const int q0 = SPLIT ? 2 * (gh & 1) : 0;     // first quarter of this workgroup
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int ct = wave % CT, qw = wave / CT;
+  const int q = q0 + qw;
+  constexpr int rows = NR, S2 = 2 * NR;       // live row slots
+  const int C = a.C, nblk = C / 32, Q = nblk / 4, nch = Q / Q4_CH;
+  const int ncw = NQ * nch;                    // chunks of the workgroup's range
+  const int tile = CT * g + ct;
+  const rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(W + (int64_t)tile * (nblk / Q4_CH) * Q4_TC), 0,
+      nblk / Q4_CH * Q4_TC, RSRC_FLAGS);
+
+  struct WSet {
+    u4 w0, w1, s;
+  };
+  auto w_issue = [&](WSet &ws, int ch) {
+    const bool ok = ch < nch;
+    const int so = __builtin_amdgcn_readfirstlane((ok ? q * nch + ch : 0) * Q4_TC);
+    ws.w0 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       wr, ok ? 32 * l : Q4_OOB, so, POL_STREAM_LOAD));
+    ws.w1 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       wr, ok ? 32 * l + 16 : Q4_OOB, so, POL_STREAM_LOAD));
+    ws.s = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                      wr, ok ? 2048 + 16 * (l & 15) : Q4_OOB, so,
+                                      POL_STREAM_LOAD));
+  };
+  // stage every chunk: item = (row, chunk, block in chunk, d) with d, then the
+  // block, fastest (the 32 lanes of a row's chunk are one half-wave); the
+  // trip count is uniform, so every exchange has its partner lane active.
+  // The first trip's x is requested before the first weights (loads return
+  // in order), so staging does not wait for the weight stream.
+  const int nitems = rows * ncw * 32;
+  const rsrc_t xr = buf_rsrc(a.x, rows * C * 4);
+  auto x_load = [&](int base, f4 &x0, f4 &x1) {
+    const int idx = base + tid;
+    const bool ok = idx < nitems;
+    const int d = idx & 3, i = (idx >> 2) & 7, rest = idx >> 5;
+    const int c = ok ? rest % ncw : 0, bb = ok ? rest / ncw : 0;
+    const int vo = ok ? 4 * (bb * C + (q0 * Q + c * Q4_CH + i) * 32 + 8 * d) : Q4_OOB;
+    x0 = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(xr, vo, 0, 0));
+    x1 = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(xr, vo, 16, 0));
+  };
+  f4 xn0, xn1;
+  x_load(0, xn0, xn1);
+  WSet S0, S1, S2w;
+  w_issue(S0, 0);
+  w_issue(S1, 1);
+  for (int base = 0; base < nitems; base += NTHR) {
+    const int idx = base + tid;
+    const bool ok = idx < nitems;
+    const int d = idx & 3, i = (idx >> 2) & 7, rest = idx >> 5;
+    const int c = ok ? rest % ncw : 0, bb = ok ? rest / ncw : 0;
+    f4 x0 = xn0, x1 = xn1;
+    if (base > 0) x_load(base, x0, x1);
+    unsigned p1[4], p2[4];
+    const int k = x_split(x0, x1, p1, p2);
+    if (ok) {
+      unsigned char *dst = xp + (((c * Q4_CH + i) * 4 + d) * S2 + 2 * bb) * 16;
+      *reinterpret_cast<u4 *>(dst) = u4{p1[0], p1[1], p1[2], p1[3]};
+      *reinterpret_cast<u4 *>(dst + 16) = u4{p2[0], p2[1], p2[2], p2[3]};
+      if ((l & 31) == 0) kp[bb * ncw + c] = k;
+    }
+  }
+  __syncthreads();
+
+  unsigned magic = 0x64006400u;                // binary16 1024 in both halves
+  __asm__("" : "+v"(magic));                   // kept in a vector register
+  const int sl = l & 15, dl = l >> 4;
+  // a slot past the rows reads a live slot's x: its results belong to no row
+  // and are never stored (a slot's result does not depend on the others)
+  const unsigned char *xl = xp + (dl * S2 + sl % S2) * 16;
+  float acc[2] = {0.f, 0.f};
+  int krow[2];
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
+    const int row = 2 * dl + r;
+    krow[r] = (row < rows ? row : 0) * ncw + qw * nch;
+  }
+  auto chunk = [&](const WSet &cur, WSet &pf, int ch) {
+    w_issue(pf, ch + 2);
+    if (ch < nch) {
+      const int jr0 = qw * Q + ch * Q4_CH;     // first block of the chunk in the range
+      float cacc[2] = {0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        f4 D[4];
+        float sv[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int i = 4 * h + j;
+          const h8 B = q4_decode(h ? cur.w1[j] : cur.w0[j], magic);
+          const unsigned sw = cur.s[i >> 1];
+          sv[j] = (float)__builtin_bit_cast(_Float16,
+                                            (unsigned short)((i & 1) ? sw >> 16 : sw & 0xffffu));
+          const h8 A = *reinterpret_cast<const h8 *>(xl + (jr0 + i) * 64 * S2);
+          D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0, 0, 0, 0}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          cacc[0] = __builtin_fmaf(D[j].x + D[j].y, sv[j], cacc[0]);
+          cacc[1] = __builtin_fmaf(D[j].z + D[j].w, sv[j], cacc[1]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 2; r++)
+        acc[r] = acc[r] + __builtin_amdgcn_ldexpf(cacc[r], -kp[krow[r] + ch]);
+    }
+  };
+  for (int ch = 0; ch < nch; ch += 3) {
+    chunk(S0, S2w, ch);
+    chunk(S1, S0, ch + 1);
+    chunk(S2w, S1, ch + 2);
+  }
+
+  // fold the quarters (as proj_q4_kernel)
+  __syncthreads();                             // every x read before the fold writes
+  float *fold = reinterpret_cast<float *>(xp);   // [ct][qw][r][64]
+#pragma unroll
+  for (int r = 0; r < 2; r++) fold[((ct * NQ + qw) * 2 + r) * 64 + l] = acc[r];
+  __syncthreads();
+  if (qw == 0) {
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      auto at = [&](int qq) { return fold[((ct * NQ + qq) * 2 + r) * 64 + l]; };
+      const int row = 2 * dl + r;
+      float v = acc[r] + at(1);
+      if constexpr (!SPLIT) v = v + (at(2) + at(3));
+      if (row < rows) {
+        float *dst = y + (int64_t)row * R + 16 * tile + sl;
+        if constexpr (SPLIT)
+          atomicAdd(dst, v);                   // two addends on +0: order-free
+        else
+          *dst = v;
+      }
+    }
+  }
+}
+
+// 4-bit packing: thread (output o, block b) writes o's four dwords of block b
+// and its scale.
 __global__ __launch_bounds__(256) void proj_q4_pack_kernel(const uint8_t *q, const uint16_t *scale,
                                                            uint8_t *Wq, int C, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const int l = (int)(i & 63);
-  const int64_t gb = i >> 6;                   // g * (C / 32) + b
   const int nblk = C / 32;
-  const int64_t g = gb / nblk;
-  const int bb = (int)(gb - g * nblk);
-  const int64_t o = 64 * g + l;
+  const int64_t o = i / nblk;
+  const int bb = (int)(i - o * nblk);
+  const int64_t t = o >> 4;
+  const int oi = (int)(o & 15), m = bb / Q4_CH, i8 = bb % Q4_CH;
   const uint8_t *src = q + o * (C / 2) + 16 * bb;
   auto u = [&](int c) -> unsigned {            // biased value of column c of the block
     const unsigned by = src[c >> 1];
     return (((c & 1) ? by >> 4 : by) & 15u) ^ 8u;
   };
-  u4 out;
+  unsigned *dst = reinterpret_cast<unsigned *>(Wq + (t * (nblk / Q4_CH) + m) * Q4_TC);
 #pragma unroll
   for (int d = 0; d < 4; d++) {
     unsigned wd = 0;
 #pragma unroll
-    for (int k = 0; k < 4; k++) wd |= (u(8 * d + k) | (u(8 * d + 4 + k) << 4)) << (8 * k);
-    out[d] = wd;
+    for (int k = 0; k < 8; k++) wd |= u(8 * d + k) << (4 * (k >> 1) + 16 * (k & 1));
+    dst[8 * (16 * d + oi) + i8] = wd;
   }
-  uint8_t *dst = Wq + gb * Q4_BLOCK_BYTES;
-  *reinterpret_cast<u4 *>(dst + 16 * l) = out;
-  reinterpret_cast<uint16_t *>(dst + 1024)[l] = scale[o * nblk + bb];
+  reinterpret_cast<uint16_t *>(dst + 512 + 4 * oi)[i8] = scale[o * nblk + bb];
 }
 
 int launch_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int R, int C,
@@ -2668,52 +2975,60 @@ int launch_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int R
   return (int)hipGetLastError();
 }
 
-template <int NR>
-static void launch_q4_rows(const Q4Args &a, bool split, hipStream_t s) {
-  const dim3 grid((unsigned)(a.p[0].wgs + a.p[1].wgs));
-  if (split)
-    hipLaunchKernelGGL((proj_q4_kernel<NR, true>), grid, dim3(Q4_LANES), 0, s, a);
+template <int NT, bool SPLIT, int CT>
+static void launch_q4(const Q4Args &a, hipStream_t s) {
+  hipLaunchKernelGGL((proj_q4_kernel<NT, SPLIT, CT>), dim3((unsigned)(a.p[0].wgs + a.p[1].wgs)),
+                     dim3(64 * CT * (SPLIT ? 2 : 4)), 0, s, a);
+}
+template <bool SPLIT, int CT>
+static void launch_q4_pre(const Q4Args &a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.p[0].wgs + a.p[1].wgs)), block(64 * CT * (SPLIT ? 2 : 4));
+  if (a.rows == 1)
+    hipLaunchKernelGGL((proj_q4_pre_kernel<SPLIT, CT, 1>), grid, block, 0, s, a);
+  else if (a.rows == 2)
+    hipLaunchKernelGGL((proj_q4_pre_kernel<SPLIT, CT, 2>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((proj_q4_kernel<NR, false>), grid, dim3(Q4_LANES), 0, s, a);
+    hipLaunchKernelGGL((proj_q4_pre_kernel<SPLIT, CT, 3>), grid, block, 0, s, a);
 }
 
 int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0, float *y0,
                    const void *Wq1, int R1, float *y1, hipStream_t s) {
   if (rows <= 0) return 0;
-  if (rows > 16 || C % (64 * Q4_SEGS) != 0) return (int)hipErrorInvalidValue;
-  // two workgroups per group when one per group would leave CUs idle (both
-  // shapes give the same bits)
-  const int groups = R0 / 64 + (Wq1 ? R1 / 64 : 0);
-  const bool split = groups < kQ4SplitBelow;
+  if (rows > 16 || C % 1024 != 0) return (int)hipErrorInvalidValue;
+  // Launch shape (every shape gives the same bits): one 16-wave workgroup per
+  // 4 column tiles when that fills the chip and rows <= 8; else two
+  // workgroups per group of CT tiles (the 9-16 row instance of one
+  // workgroup per group would be held to 128 VGPRs), CT = 4, or, up to 8
+  // rows, 2 when 4 gives fewer than kQ4SplitBelow workgroups.
+  const int tiles = R0 / 16 + (Wq1 ? R1 / 16 : 0);
+  const bool split = tiles / 4 < kQ4SplitBelow || rows > 8;
+  int ct = 4;
+  if (split && rows <= 8 && 2 * tiles / 4 < kQ4SplitBelow) ct = 2;
   const int f = split ? 2 : 1;
   Q4Args a{};
   a.x = x;
+  a.rows = (int)rows;
   a.C = C;
-  a.p[0] = Q4Problem{static_cast<const uint8_t *>(Wq0), y0, R0, R0 / 64 * f};
-  a.p[1] = Q4Problem{static_cast<const uint8_t *>(Wq1), y1, R1, Wq1 ? R1 / 64 * f : 0};
+  a.p[0] = Q4Problem{static_cast<const uint8_t *>(Wq0), y0, R0, R0 / 16 / ct * f};
+  a.p[1] = Q4Problem{static_cast<const uint8_t *>(Wq1), y1, R1, Wq1 ? R1 / 16 / ct * f : 0};
   if (split) {
     const int64_t n0 = rows * R0, n1 = Wq1 ? rows * R1 : 0;
     hipLaunchKernelGGL(zero2_kernel, dim3((unsigned)((n0 + n1 + 255) / 256)), dim3(256), 0, s,
                        y0, n0, y1, n1);
   }
-  switch (rows) {
-    case 1: launch_q4_rows<1>(a, split, s); break;
-    case 2: launch_q4_rows<2>(a, split, s); break;
-    case 3: launch_q4_rows<3>(a, split, s); break;
-    case 4: launch_q4_rows<4>(a, split, s); break;
-    case 5: launch_q4_rows<5>(a, split, s); break;
-    case 6: launch_q4_rows<6>(a, split, s); break;
-    case 7: launch_q4_rows<7>(a, split, s); break;
-    case 8: launch_q4_rows<8>(a, split, s); break;
-    case 9: launch_q4_rows<9>(a, split, s); break;
-    case 10: launch_q4_rows<10>(a, split, s); break;
-    case 11: launch_q4_rows<11>(a, split, s); break;
-    case 12: launch_q4_rows<12>(a, split, s); break;
-    case 13: launch_q4_rows<13>(a, split, s); break;
-    case 14: launch_q4_rows<14>(a, split, s); break;
-    case 15: launch_q4_rows<15>(a, split, s); break;
-    default: launch_q4_rows<16>(a, split, s); break;
-  }
+  // all of a workgroup's x staged up front when it fits
+  const int range = split ? C / 2 : C;
+  const bool pre = rows <= 3 && (int64_t)range / 32 * 128 * rows <= Q4_PRE_BYTES &&
+                   (int64_t)range / 256 * rows <= Q4_PRE_K;
+  if (pre)
+    !split ? launch_q4_pre<false, 4>(a, s)
+           : ct == 4 ? launch_q4_pre<true, 4>(a, s) : launch_q4_pre<true, 2>(a, s);
+  else if (!split)
+    launch_q4<1, false, 4>(a, s);
+  else if (rows <= 8)
+    ct == 4 ? launch_q4<1, true, 4>(a, s) : launch_q4<1, true, 2>(a, s);
+  else
+    launch_q4<2, true, 4>(a, s);
   return (int)hipGetLastError();
 }
 

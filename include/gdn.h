@@ -429,12 +429,12 @@ int64_t gdn_proj_q4_bytes(int32_t R, int32_t C);
  *     element 2 i + 1 in the high nibble, each a two's-complement value -8..7;
  *   scale [R][C / 32] finite binary16 bit patterns, scale b covering elements
  *     32 b .. 32 b + 31 of its row.
- * The packed order, per group g of 64 rows and 32-column block b (1152
- * bytes): row 64 g + l holds 16 bytes at offset 16 l, where byte k of 32-bit
- * word d holds n + 8 of column 32 b + 8 d + k in its low nibble and of column
- * 32 b + 8 d + 4 + k in its high nibble; the 64 scales of the block follow at
- * offset 1024 + 2 l.  Groups and blocks are stored g-major.  No value is
- * rounded: the packing is a re-arrangement plus the fixed offset of 8.
+ * The packed order, per tile t of 16 rows and chunk m of 256 columns (2304
+ * bytes, t-major): 32-bit word 8 (16 d + o) + i holds the biased values
+ * u = n + 8 of row 16 t + o, columns 256 m + 32 i + 8 d + k (k = 0..7), value
+ * k at bit 4 (k >> 1) + 16 (k & 1); then at offset 2048 + 16 o the 8 scales of
+ * row 16 t + o for the chunk's blocks i = 0..7.  No value is rounded: the
+ * packing is a re-arrangement plus the fixed offset of 8.
  *   q, scale, Wq: device arrays, 16-byte aligned, Wq of gdn_proj_q4_bytes(R, C)
  *   bytes, not overlapping the sources.
  * Errors: GDN_EINVAL for a null or misaligned pointer, R <= 0, C <= 0 or
@@ -450,12 +450,19 @@ int gdn_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int32_t 
  * x[r][c], with W0[o][c] = n * s formed exactly in fp32 from the 4-bit value n
  * and its block's scale s, and y1 likewise from Wq1 in the same launch
  * ("Kestrel_VLLM #24", section 8 and Fig. 1 caption, steps 1 and 7).
- * The sum runs in a fixed order of fp32 operations: C is cut into 32 equal
- * segments, each an ascending chain of fused multiply-adds; segments 0..15
- * are folded left to right, so are segments 16..31, and the two sums are
- * added.  It differs from a left fold by rounding only, and a row's result
- * does not depend on the other rows of the call, on their number, or on
- * whether the matrix shares the launch with a second one.
+ * The sum runs in a fixed order: for each row and 256-column chunk, x is
+ * scaled by a power of two 2^k (its largest magnitude in [2^14, 2^15)) and
+ * split into two binary16 parts x1 = rn(2^k x), x2 = rn(2^k x - x1); the fp16
+ * matrix cores form each 32-column block's sums of n x1 and of n x2 (exact
+ * products, fp32 accumulation), their fp32 sum T is scaled by s in one fused
+ * multiply-add per block, chained over the chunk's 8 blocks from +0 and
+ * scaled back by 2^-k; C is cut into 4 quarters whose chunk results are added
+ * in order, and y = (q0 + q1) + (q2 + q3).  x2 holds the 22nd and lower
+ * significant bits of x that x1 misses, so the result is within fp32
+ * reordering error of the exact sum; an infinite x makes every output of its
+ * row NaN or infinite, as IEEE arithmetic would.  A row's result does not
+ * depend on the other rows of the call, on their number, or on whether the
+ * matrix shares the launch with a second one.
  *   x [rows][C] fp32; y0 [rows][R0], y1 [rows][R1] fp32; Wq0, Wq1 packed
  *   (16-byte aligned; Wq1 == NULL requires R1 == 0 and y1 == NULL).
  * Ownership: every buffer belongs to the caller; nothing is allocated.

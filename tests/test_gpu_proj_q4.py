@@ -4,8 +4,10 @@ gdn_proj_q4), through the C ABI.
 The 4-bit reading ("Kestrel_VLLM #24", sections 8 and 12): each weight is a
 signed 4-bit value times the binary16 scale of its block of 32, exact in fp32.
 Floating point: per element |y - r| <= max(1e-5 |r|, 1e-6 sum_c |W[o][c] x[c]|)
-against the oracle's proj_q4 (a strict left fold; the kernel sums 32 segments
-of fused multiply-adds in two folds of 16, so the two differ by rounding only).
+against the oracle's proj_q4 (a strict left fold of w x with w = n s; the
+kernel forms the products n x on the fp16 matrix cores from x split into two
+binary16 parts that hold its 22 leading bits, and scales each 32-column block's
+sum by s, so the two differ by rounding and by at most 2^-22 |w x| per term).
 Bit-exact: every result when all partial sums are exact (integer-valued x,
 power-of-two scales: any order gives the same bits), a row's result against
 the same row in calls of every other row count, one launch of two products
@@ -58,20 +60,24 @@ def decode_np(q, sc):
 
 def pack_q4_np(q, sc):
     """The packed order documented in include/gdn.h, by index arithmetic: per
-    64-row group g and 32-column block b, row 64 g + l owns 16 bytes at 16 l,
-    byte k of word d = (n + 8 of column 8 d + k) | (n + 8 of column 8 d + 4 + k)
-    << 4; then the block's 64 scales."""
+    16-row column tile t and chunk m of 8 blocks of 32 columns (2304 bytes),
+    dword 8 (16 d + o) + i = sum over k of (n + 8 of row 16 t + o, column
+    256 m + 32 i + 8 d + k) << (4 (k >> 1) + 16 (k & 1)); then at 2048 + 16 o
+    row 16 t + o's 8 scales of the chunk."""
     q = np.asarray(q, np.uint8)
     R, C = q.shape[0], 2 * q.shape[1]
-    nib = np.empty((R, C), np.uint8)
+    nib = np.empty((R, C), np.uint32)
     nib[:, 0::2] = q & 15
     nib[:, 1::2] = q >> 4
-    u = (nib ^ 8).reshape(R, C // 32, 4, 2, 4)            # row, block, d, half, k
-    byte = (u[:, :, :, 0, :] | (u[:, :, :, 1, :] << 4)).reshape(R, C // 32, 16)
-    vals = byte.reshape(R // 64, 64, C // 32, 16).transpose(0, 2, 1, 3).reshape(R // 64, C // 32, 1024)
-    scl = np.ascontiguousarray(np.asarray(sc).view(np.uint16).reshape(R // 64, 64, C // 32)
-                               .transpose(0, 2, 1))
-    out = np.concatenate([vals, scl.view(np.uint8).reshape(R // 64, C // 32, 128)], axis=2)
+    u = (nib ^ 8).reshape(R // 16, 16, C // 256, 8, 4, 8)   # t, o, m, i, d, k
+    shift = np.array([4 * (k >> 1) + 16 * (k & 1) for k in range(8)], np.uint32)
+    dw = np.bitwise_or.reduce(u << shift, axis=5)             # t, o, m, i, d
+    vals = np.ascontiguousarray(dw.transpose(0, 2, 4, 1, 3)).view(np.uint8)
+    vals = vals.reshape(R // 16, C // 256, 2048)
+    scl = np.asarray(sc).view(np.uint16).reshape(R // 16, 16, C // 256, 8)
+    scl = np.ascontiguousarray(scl.transpose(0, 2, 1, 3)).view(np.uint8)
+    scl = scl.reshape(R // 16, C // 256, 256)
+    out = np.concatenate([vals, scl], axis=2)
     return np.ascontiguousarray(out.reshape(R // 64, 36 * C))
 
 
@@ -121,10 +127,11 @@ def test_q4_exact_when_every_partial_sum_is_exact(orc, rows, R, C):
 
 @pytest.mark.parametrize("rows,R,C", [(2, 64, 131072), (1, 16384, 16384)])
 def test_q4_large_sizes_exact(orc, rows, R, C):
-    """Long segments (C = 2^17: 128 blocks per wave, two workgroups per
-    group) and a launch of 256 groups (one workgroup per group) with
-    C = 2^14, on exactly summable operands (integer x, power-of-two scales):
-    bit-exact against the oracle."""
+    """Long quarters (C = 2^17: 128 chunks of x staged per workgroup, two
+    workgroups per group) and a launch of 256 groups (one workgroup per
+    group) with C = 2^14, whose one row of x just fills the up-front stage,
+    on exactly summable operands (integer x, power-of-two scales): bit-exact
+    against the oracle."""
     say(f"proj_q4 large rows={rows} R={R} C={C}")
     gen = synth.make_gen(151 + rows, "cuda")
     q = torch.randint(0, 256, (R, C // 2), generator=gen, device="cuda").to(torch.uint8)
@@ -228,6 +235,22 @@ def test_q4_nan_in_x_reaches_only_its_row(rows, R):
     nan[r, :] = True
     assert np.array_equal(np.isnan(y), nan)
     assert bits_equal(y[~nan], clean[~nan])
+
+
+def test_q4_staging_variants_agree_bit_for_bit():
+    """At the layer's in_proj size (C = 5120, 16384 outputs) calls of 1-3 rows
+    stage all of x up front and calls of 4-8 rows stage it chunk by chunk:
+    every row of an 8-row call equals the same row in the calls of 1..7 rows,
+    in either variant."""
+    say("proj_q4 staging variants")
+    C, R = 5120, 16384
+    x, q, sc = q4_operands(157, 8, R, C)
+    Wq = gdn.proj_q4_pack(q, sc)
+    full = host(gdn.proj_q4(x, Wq))
+    for n in range(1, 8):
+        lo = 8 - n
+        part = host(gdn.proj_q4(x[lo:].contiguous(), Wq))
+        assert bits_equal(part, np.ascontiguousarray(full[lo:])), n
 
 
 def test_q4_launch_shapes_agree_bit_for_bit():
