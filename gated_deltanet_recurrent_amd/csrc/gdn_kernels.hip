@@ -2433,10 +2433,13 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 //    (1024 + u - 1032, or (1024 + 16 u) / 16 - 72): nine instructions per 8
 //    weights;
 //  - x is scaled by a power of two 2^k per row and 256-column chunk (the
-//    chunk's largest magnitude lands in [2^14, 2^15)) and split into two
-//    binary16 parts, x1 = rn(2^k x) and x2 = rn(2^k x - x1), which hold 22 of
-//    its 24 significant bits; the two parts of a row take two row slots, so one
-//    instruction covers 8 rows;
+//    chunk's largest magnitude lands in [2^14, 2^15)) and split into three
+//    binary16 parts, x1 = rn(2^k x), x2 = rn(2^k x - x1) and x3 =
+//    rn(2^k x - x1 - x2), whose sum is 2^k x exactly for every element of at
+//    least 2^-15 of the chunk's largest magnitude (11 + 11 + 11 bits hold its
+//    24; a smaller one is off by under 2^-39 of that magnitude); the parts of
+//    a row take three of the four row slots one lane of the product holds,
+//    so one instruction covers 4 rows;
 //  - the block's binary16 scale s multiplies the fp32 sum of the block in a
 //    mixed-precision fma (exact conversion, one rounding).
 // The MFMA's result for one output does not depend on the other slots or on
@@ -2445,19 +2448,20 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 // Summation order of y[r][o], fixed and independent of the row count: C is cut
 // into 4 quarters; in quarter q, for each chunk of 8 blocks of 32 columns,
 // cacc = +0 and for each block j in order cacc = fma(T_j, s[o][j], cacc) with
-// T_j = D1_j + D2_j (the MFMA dot products of the block's n with x1 and x2);
+// T_j = (D1_j + D2_j) + D3_j (the MFMA dot products of the block's n with x1,
+// x2 and x3);
 // the chunk's cacc, scaled back by 2^-k, is added to acc_q (+0 first);
 // y = (acc_0 + acc_1) + (acc_2 + acc_3).  The launch shapes all compute
 // exactly that:
 //  - one 16-wave workgroup per group of 4 column tiles (64 outputs; wave =
 //    column tile x quarter), the quarter sums folded in LDS, for launches of
-//    up to 8 rows with enough groups to fill the chip;
+//    up to 4 rows with enough groups to fill the chip;
 //  - two workgroups per group of 4 or 2 column tiles (quarters 0-1 and 2-3),
 //    each adding its half into y, which a fill kernel zeroed first.  With
 //    exactly two addends on +0 the result does not depend on their arrival
 //    order (fp addition is commutative, and none of these sums is -0), so the
 //    shapes give the same bits.  Used for launches with fewer groups than the
-//    chip has CUs (out_proj: 80 groups) and for 9 to 16 rows.
+//    chip has CUs (out_proj: 80 groups) and for 5 to 16 rows.
 // Each row's x is split once per workgroup.  For 1 to 3 rows all of it is
 // staged up front, compactly (only the live row slots; a slot past the rows
 // reads a live slot's x, and its result is never stored), and the K loop runs
@@ -2499,12 +2503,13 @@ struct Q4Args {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-// (x & m) | c in one instruction: the mask from a scalar register, the
-// constant from a vector register (a VOP3 takes no literal on this target)
+// (x & m) | c: one v_and_or_b32.  No inline assembly may write a vector
+// register in these kernels: the compiler's hazard checks do not see its
+// writes, and a result lane that no code reads (the pad slot of the matrix
+// product) is written late by the matrix core, over whatever the compiler
+// placed in that register meanwhile.
 static __device__ __forceinline__ unsigned and_or(unsigned x, unsigned m, unsigned c) {
-  unsigned r;
-  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
-  return r;
+  return (x & m) | c;
 }
 
 // 8 biased 4-bit values of one output (one packed dword) -> the binary16
@@ -2523,18 +2528,12 @@ static __device__ __forceinline__ h8 q4_decode(unsigned w, unsigned magic) {
   return h8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-// v - (float)h (h the low or high binary16 of p) in one mixed-precision fma:
-// exact, since h is v rounded to binary16
+// v - (float)h (h the low or high binary16 of p): exact, since h is v
+// rounded to binary16
 template <bool HI>
 static __device__ __forceinline__ float minus_half(unsigned p, float v) {
-  float r;
-  if constexpr (HI)
-    __asm__("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-            : "=v"(r) : "v"(p), "v"(v));
-  else
-    __asm__("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
-            : "=v"(r) : "v"(p), "v"(v));
-  return r;
+  const float h = (float)__builtin_bit_cast(_Float16, (unsigned short)(HI ? p >> 16 : p & 0xffffu));
+  return __builtin_fmaf(h, -1.0f, v);
 }
 
 static __device__ __forceinline__ unsigned pk_half(float a, float b) {
@@ -2542,11 +2541,13 @@ static __device__ __forceinline__ unsigned pk_half(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f2v){a, b}, h2));
 }
 
-// 8 consecutive x of one row (v) -> the chunk's exponent k (shared by the 32
-// lanes of the row's chunk, which hold its 256 columns) and the two binary16
-// parts of 2^k v, each as 4 packed pairs
+// 8 consecutive x of one row -> the chunk's exponent k (shared by the 32 lanes
+// of the row's chunk, which hold its 256 columns) and the three binary16 parts
+// of 2^k x, each as 4 packed pairs.  A residual of an infinite x is NaN: a
+// packed max (which passes over NaN) replaces it by a finite value, so the
+// infinity itself reaches the sum through the first part.
 static __device__ __forceinline__ int x_split(const f4 &x0, const f4 &x1, unsigned (&p1)[4],
-                                              unsigned (&p2)[4]) {
+                                              unsigned (&p2)[4], unsigned (&p3)[4]) {
   const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
   float m = 0.f;
 #pragma unroll
@@ -2559,20 +2560,24 @@ static __device__ __forceinline__ int x_split(const f4 &x0, const f4 &x1, unsign
   // largest magnitude in [2^14, 2^15) after scaling (m = 0: any k)
   const int k = 15 - __builtin_amdgcn_frexp_expf(m);
   const h2 lo = {(_Float16)-65504.0f, (_Float16)-65504.0f};
+  auto clamp = [&](unsigned r) {
+    return __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(h2, r), lo));
+  };
 #pragma unroll
   for (int e = 0; e < 4; e++) {
     const float s0 = __builtin_amdgcn_ldexpf(v[2 * e], k);
     const float s1 = __builtin_amdgcn_ldexpf(v[2 * e + 1], k);
     p1[e] = pk_half(s0, s1);
-    // an infinite x gives a NaN residual: replaced by a finite value (max
-    // passes over NaN), so the infinity itself (x1) reaches the sum
-    const unsigned r = pk_half(minus_half<false>(p1[e], s0), minus_half<true>(p1[e], s1));
-    p2[e] = __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(h2, r), lo));
+    const float r0 = minus_half<false>(p1[e], s0), r1 = minus_half<true>(p1[e], s1);
+    const unsigned q2 = pk_half(r0, r1);
+    const float t0 = minus_half<false>(q2, r0), t1 = minus_half<true>(q2, r1);
+    p2[e] = clamp(q2);
+    p3[e] = clamp(pk_half(t0, t1));
   }
   return k;
 }
 
-// NT: row tiles of 8 rows (rows <= 8 NT); SPLIT: two workgroups per group of
+// NT: row tiles of 4 rows (rows <= 4 NT); SPLIT: two workgroups per group of
 // CT column tiles (quarters 0-1 and 2-3), else one (all four quarters)
 template <int NT, bool SPLIT, int CT>
 __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Args a) {
@@ -2581,7 +2586,7 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
   constexpr int NTHR = 64 * CT * NQ;
   constexpr int STAGE = NQ * Q4_CH * NT * 1024;
   __shared__ __align__(16) unsigned char xs[2][STAGE];
-  __shared__ int kexp[2][NQ][8 * NT];
+  __shared__ int kexp[2][NQ][4 * NT];
   const int bid = (int)xcd_contiguous(blockIdx.x, gridDim.x);
   const bool second = bid >= a.p[0].wgs;
   const uint8_t *W = second ? a.p[1].W : a.p[0].W;
@@ -2601,16 +2606,18 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
       const_cast<uint8_t *>(W + (int64_t)tile * (nblk / Q4_CH) * Q4_TC), 0,
       nblk / Q4_CH * Q4_TC, RSRC_FLAGS);
 
-  // zero both stage buffers: row slots past `rows` stay zero
+  // zero both stage buffers: the pad slot of every row and the slots past
+  // `rows` stay zero
   for (int i = tid; i < 2 * STAGE / 16; i += NTHR)
     reinterpret_cast<u4 *>(&xs[0][0])[i] = u4{0, 0, 0, 0};
 
   // x staging: item = (quarter slot, row, block in chunk, d) with d, then the
   // block, fastest, so the 32 lanes of a row's chunk are one half-wave; at
-  // most NQ 8 NT 32 items, ITEMS per lane.  Stage layout: per quarter slot,
+  // most NQ 4 NT 32 items, ITEMS per lane.  Stage layout: per quarter slot,
   // block and row tile a 1 KiB operand tile, row slot s of column group d at
-  // 16 (16 d + (s ^ i ^ 8 (d & 1))) for block i of the chunk.
-  constexpr int ITEMS = 4 * NT / CT;
+  // 16 (16 d + (s ^ i ^ 8 (d & 1))) for block i of the chunk (row r, part p:
+  // slot 4 (r % 4) + p).
+  constexpr int ITEMS = (2 * NT + CT - 1) / CT;
   const int nitems = NQ * rows * Q4_CH * 4;
   // the lane's items, the same in every chunk: x element offset in chunk 0
   // (-1: no item), LDS byte offset, exponent slot
@@ -2622,11 +2629,9 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
     const int d = idx & 3, i = (idx >> 2) & 7, rest = idx >> 5;
     const int bb = ok ? rest % rows : 0, qi = ok ? rest / rows : 0;
     xoff[it] = ok ? bb * C + ((q0 + qi) * Q + i) * 32 + 8 * d : -1;
-    // slot 2 (bb % 8) of row d in block i's tile, swizzled (the 32 lanes of a
-    // row's chunk would otherwise store to one bank group)
-    xdst[it] = ((qi * Q4_CH + i) * NT + bb / 8) * 1024 +
-               16 * (16 * d + ((2 * (bb % 8)) ^ i ^ (8 * (d & 1))));
-    xkix[it] = qi * 8 * NT + bb;
+    xdst[it] = ((qi * Q4_CH + i) * NT + bb / 4) * 1024 +
+               16 * (16 * d + ((4 * (bb % 4)) ^ i ^ (8 * (d & 1))));
+    xkix[it] = qi * 4 * NT + bb;
   }
   // x of a chunk, in three register sets rotating with the weight sets
   struct XSet {
@@ -2648,11 +2653,12 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
     unsigned char *buf = xs[ch & 1];
 #pragma unroll
     for (int it = 0; it < ITEMS; it++) {
-      unsigned p1[4], p2[4];
-      const int k = x_split(xv.v[it][0], xv.v[it][1], p1, p2);
+      unsigned p1[4], p2[4], p3[4];
+      const int k = x_split(xv.v[it][0], xv.v[it][1], p1, p2, p3);
       if (xoff[it] >= 0) {
         *reinterpret_cast<u4 *>(buf + xdst[it]) = u4{p1[0], p1[1], p1[2], p1[3]};
         *reinterpret_cast<u4 *>(buf + (xdst[it] ^ 16)) = u4{p2[0], p2[1], p2[2], p2[3]};
+        *reinterpret_cast<u4 *>(buf + (xdst[it] ^ 32)) = u4{p3[0], p3[1], p3[2], p3[3]};
         if ((l & 31) == 0) (&kexp[ch & 1][0][0])[xkix[it]] = k;
       }
     }
@@ -2689,9 +2695,10 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
 
   unsigned magic = 0x64006400u;                // binary16 1024 in both halves
   __asm__("" : "+v"(magic));                   // kept in a vector register
-  float acc[NT][2];
+  float acc[NT];
 #pragma unroll
-  for (int t = 0; t < NT; t++) acc[t][0] = acc[t][1] = 0.f;
+  for (int t = 0; t < NT; t++) acc[t] = 0.f;
+  constexpr int GB = NT == 1 ? 4 : 2;          // blocks whose products are in flight together
 
   // one chunk: issue chunk ch + 2's x and weights, compute chunk ch, stage
   // chunk ch + 1's x, one barrier
@@ -2699,21 +2706,21 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
     x_issue(xf, ch + 2);
     w_issue(pf, ch + 2);
     if (ch < nch) {
-      // lane l reads slot l % 16 of row l / 16, at the writers' swizzled place
+      // lane l reads slot l % 16 of column group l / 16, at the writers'
+      // swizzled place
       const unsigned char *buf = xs[ch & 1] + (qw * Q4_CH) * NT * 1024;
       const int lx = 16 * (l ^ ((l >> 1) & 8));
-      float cacc[NT][2];
+      float cacc[NT];
 #pragma unroll
-      for (int t = 0; t < NT; t++) cacc[t][0] = cacc[t][1] = 0.f;
-      // four blocks at a time: operands, products, then the chains
+      for (int t = 0; t < NT; t++) cacc[t] = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; h++) {
-        f4 D[4][NT];
-        float sv[4];
+      for (int h = 0; h < Q4_CH / GB; h++) {
+        f4 D[GB][NT];
+        float sv[GB];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int i = 4 * h + j;
-          const h8 B = q4_decode(h ? cur.w1[j] : cur.w0[j], magic);
+        for (int j = 0; j < GB; j++) {
+          const int i = GB * h + j;
+          const h8 B = q4_decode(i < 4 ? cur.w0[i] : cur.w1[i - 4], magic);
           const unsigned sw = cur.s[i >> 1];
           sv[j] = (float)__builtin_bit_cast(_Float16,
                                             (unsigned short)((i & 1) ? sw >> 16 : sw & 0xffffu));
@@ -2724,21 +2731,18 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
             D[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0, 0, 0, 0}, 0, 0, 0);
           }
         }
+        // the lane's row of each tile: its three parts' sums
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < GB; j++)
 #pragma unroll
-          for (int t = 0; t < NT; t++) {
-            cacc[t][0] = __builtin_fmaf(D[j][t].x + D[j][t].y, sv[j], cacc[t][0]);
-            cacc[t][1] = __builtin_fmaf(D[j][t].z + D[j][t].w, sv[j], cacc[t][1]);
-          }
+          for (int t = 0; t < NT; t++)
+            cacc[t] = __builtin_fmaf((D[j][t].x + D[j][t].y) + D[j][t].z, sv[j], cacc[t]);
       }
 #pragma unroll
-      for (int t = 0; t < NT; t++)
-#pragma unroll
-        for (int r = 0; r < 2; r++) {
-          const int k = kexp[ch & 1][qw][8 * t + 2 * (l >> 4) + r];
-          acc[t][r] = acc[t][r] + __builtin_amdgcn_ldexpf(cacc[t][r], -k);
-        }
+      for (int t = 0; t < NT; t++) {
+        const int k = kexp[ch & 1][qw][4 * t + (l >> 4)];
+        acc[t] = acc[t] + __builtin_amdgcn_ldexpf(cacc[t], -k);
+      }
     }
     if (ch + 1 < nch) x_stage(xn, ch + 1);
     __syncthreads();
@@ -2750,36 +2754,33 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
   }
 
   // fold the quarters: wave (ct, qw) -> LDS; the first quarter's waves add
-  float *fold = reinterpret_cast<float *>(&xs[0][0]);   // [ct][qw][t][r][64]
+  float *fold = reinterpret_cast<float *>(&xs[0][0]);   // [ct][qw][t][64]
 #pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int r = 0; r < 2; r++) fold[(((ct * NQ + qw) * NT + t) * 2 + r) * 64 + l] = acc[t][r];
+  for (int t = 0; t < NT; t++) fold[((ct * NQ + qw) * NT + t) * 64 + l] = acc[t];
   __syncthreads();
   if (qw == 0) {
 #pragma unroll
-    for (int t = 0; t < NT; t++)
-#pragma unroll
-      for (int r = 0; r < 2; r++) {
-        auto at = [&](int qq) { return fold[(((ct * NQ + qq) * NT + t) * 2 + r) * 64 + l]; };
-        const int row = 8 * t + 2 * (l >> 4) + r;
-        float v = acc[t][r] + at(1);
-        if constexpr (!SPLIT) v = v + (at(2) + at(3));
-        if (row < rows) {
-          float *dst = y + (int64_t)row * R + 16 * tile + (l & 15);
-          if constexpr (SPLIT)
-            atomicAdd(dst, v);                 // two addends on +0: order-free
-          else
-            *dst = v;
-        }
+    for (int t = 0; t < NT; t++) {
+      auto at = [&](int qq) { return fold[((ct * NQ + qq) * NT + t) * 64 + l]; };
+      const int row = 4 * t + (l >> 4);
+      float v = acc[t] + at(1);
+      if constexpr (!SPLIT) v = v + (at(2) + at(3));
+      if (row < rows) {
+        float *dst = y + (int64_t)row * R + 16 * tile + (l & 15);
+        if constexpr (SPLIT)
+          atomicAdd(dst, v);                   // two addends on +0: order-free
+        else
+          *dst = v;
       }
+    }
   }
 }
 
-// Launches of few rows stage all of their x once, compactly (only the live
-// row slots), and then run the K loop without barriers: LDS bytes for the x
-// parts of a workgroup's column range, and ints for its chunk exponents.
-constexpr int Q4_PRE_BYTES = 65536;
+// Launches of few rows stage all of their x once, compactly (the three parts
+// of each live row), and then run the K loop without barriers: LDS bytes for
+// the x parts of a workgroup's column range (half of C when split: two such
+// workgroups fit a CU), and ints for its chunk exponents.
+constexpr int q4_pre_bytes(bool split) { return split ? 57344 : 98304; }
 constexpr int Q4_PRE_K = 256;
 
 // The same order as proj_q4_kernel for NR rows (1..3), every x chunk staged
@@ -2789,8 +2790,8 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
   static_assert(CT == 2 || CT == 4, "4 or 2 column tiles per workgroup");
   constexpr int NQ = SPLIT ? 2 : 4;            // quarters per workgroup
   constexpr int NTHR = 64 * CT * NQ;
-  // x parts [block of the range][d][live slot][16 bytes]
-  __shared__ __align__(16) unsigned char xp[Q4_PRE_BYTES];
+  // x parts [block of the range][d][row][part][16 bytes]
+  __shared__ __align__(16) unsigned char xp[q4_pre_bytes(SPLIT)];
   __shared__ int kp[Q4_PRE_K];                 // [row][chunk of the range]
   const int bid = (int)xcd_contiguous(blockIdx.x, gridDim.x);
   const bool second = bid >= a.p[0].wgs;
@@ -2805,7 +2806,7 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
   const int l = tid & 63;
   const int ct = wave % CT, qw = wave / CT;
   const int q = q0 + qw;
-  constexpr int rows = NR, S2 = 2 * NR;       // live row slots
+  constexpr int rows = NR, S3 = 3 * NR;        // live row slots (three parts per row)
   const int C = a.C, nblk = C / 32, Q = nblk / 4, nch = Q / Q4_CH;
   const int ncw = NQ * nch;                    // chunks of the workgroup's range
   const int tile = CT * g + ct;
@@ -2827,6 +2828,7 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
                                       wr, ok ? 2048 + 16 * (l & 15) : Q4_OOB, so,
                                       POL_STREAM_LOAD));
   };
+
   // stage every chunk: item = (row, chunk, block in chunk, d) with d, then the
   // block, fastest (the 32 lanes of a row's chunk are one half-wave); the
   // trip count is uniform, so every exchange has its partner lane active.
@@ -2855,12 +2857,13 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
     const int c = ok ? rest % ncw : 0, bb = ok ? rest / ncw : 0;
     f4 x0 = xn0, x1 = xn1;
     if (base > 0) x_load(base, x0, x1);
-    unsigned p1[4], p2[4];
-    const int k = x_split(x0, x1, p1, p2);
+    unsigned p1[4], p2[4], p3[4];
+    const int k = x_split(x0, x1, p1, p2, p3);
     if (ok) {
-      unsigned char *dst = xp + (((c * Q4_CH + i) * 4 + d) * S2 + 2 * bb) * 16;
+      unsigned char *dst = xp + (((c * Q4_CH + i) * 4 + d) * S3 + 3 * bb) * 16;
       *reinterpret_cast<u4 *>(dst) = u4{p1[0], p1[1], p1[2], p1[3]};
       *reinterpret_cast<u4 *>(dst + 16) = u4{p2[0], p2[1], p2[2], p2[3]};
+      *reinterpret_cast<u4 *>(dst + 32) = u4{p3[0], p3[1], p3[2], p3[3]};
       if ((l & 31) == 0) kp[bb * ncw + c] = k;
     }
   }
@@ -2868,22 +2871,21 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
 
   unsigned magic = 0x64006400u;                // binary16 1024 in both halves
   __asm__("" : "+v"(magic));                   // kept in a vector register
+  // lane l supplies row slot l % 16 (row (l % 16) / 4, part l % 4) of column
+  // group l / 16; a row past `rows` and the pad part read a live slot's x:
+  // their results belong to no row and are never stored (a slot's result
+  // does not depend on the others)
   const int sl = l & 15, dl = l >> 4;
-  // a slot past the rows reads a live slot's x: its results belong to no row
-  // and are never stored (a slot's result does not depend on the others)
-  const unsigned char *xl = xp + (dl * S2 + sl % S2) * 16;
-  float acc[2] = {0.f, 0.f};
-  int krow[2];
-#pragma unroll
-  for (int r = 0; r < 2; r++) {
-    const int row = 2 * dl + r;
-    krow[r] = (row < rows ? row : 0) * ncw + qw * nch;
-  }
+  const int lrow = (sl >> 2) % rows, lpart = (sl & 3) == 3 ? 0 : (sl & 3);
+  const unsigned char *xl = xp + (dl * S3 + 3 * lrow + lpart) * 16;
+  const int row = l >> 4;                      // the lane's result row
+  const int krow = (row < rows ? row : 0) * ncw + qw * nch;
+  float acc = 0.f;
   auto chunk = [&](const WSet &cur, WSet &pf, int ch) {
     w_issue(pf, ch + 2);
     if (ch < nch) {
       const int jr0 = qw * Q + ch * Q4_CH;     // first block of the chunk in the range
-      float cacc[2] = {0.f, 0.f};
+      float cacc = 0.f;
 #pragma unroll
       for (int h = 0; h < 2; h++) {
         f4 D[4];
@@ -2895,18 +2897,14 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
           const unsigned sw = cur.s[i >> 1];
           sv[j] = (float)__builtin_bit_cast(_Float16,
                                             (unsigned short)((i & 1) ? sw >> 16 : sw & 0xffffu));
-          const h8 A = *reinterpret_cast<const h8 *>(xl + (jr0 + i) * 64 * S2);
+          const h8 A = *reinterpret_cast<const h8 *>(xl + (jr0 + i) * 64 * S3);
           D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0, 0, 0, 0}, 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          cacc[0] = __builtin_fmaf(D[j].x + D[j].y, sv[j], cacc[0]);
-          cacc[1] = __builtin_fmaf(D[j].z + D[j].w, sv[j], cacc[1]);
-        }
+        for (int j = 0; j < 4; j++)
+          cacc = __builtin_fmaf((D[j].x + D[j].y) + D[j].z, sv[j], cacc);
       }
-#pragma unroll
-      for (int r = 0; r < 2; r++)
-        acc[r] = acc[r] + __builtin_amdgcn_ldexpf(cacc[r], -kp[krow[r] + ch]);
+      acc = acc + __builtin_amdgcn_ldexpf(cacc, -kp[krow + ch]);
     }
   };
   for (int ch = 0; ch < nch; ch += 3) {
@@ -2917,24 +2915,19 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
 
   // fold the quarters (as proj_q4_kernel)
   __syncthreads();                             // every x read before the fold writes
-  float *fold = reinterpret_cast<float *>(xp);   // [ct][qw][r][64]
-#pragma unroll
-  for (int r = 0; r < 2; r++) fold[((ct * NQ + qw) * 2 + r) * 64 + l] = acc[r];
+  float *fold = reinterpret_cast<float *>(xp);   // [ct][qw][64]
+  fold[(ct * NQ + qw) * 64 + l] = acc;
   __syncthreads();
   if (qw == 0) {
-#pragma unroll
-    for (int r = 0; r < 2; r++) {
-      auto at = [&](int qq) { return fold[((ct * NQ + qq) * 2 + r) * 64 + l]; };
-      const int row = 2 * dl + r;
-      float v = acc[r] + at(1);
-      if constexpr (!SPLIT) v = v + (at(2) + at(3));
-      if (row < rows) {
-        float *dst = y + (int64_t)row * R + 16 * tile + sl;
-        if constexpr (SPLIT)
-          atomicAdd(dst, v);                   // two addends on +0: order-free
-        else
-          *dst = v;
-      }
+    auto at = [&](int qq) { return fold[(ct * NQ + qq) * 64 + l]; };
+    float v = acc + at(1);
+    if constexpr (!SPLIT) v = v + (at(2) + at(3));
+    if (row < rows) {
+      float *dst = y + (int64_t)row * R + 16 * tile + sl;
+      if constexpr (SPLIT)
+        atomicAdd(dst, v);                     // two addends on +0: order-free
+      else
+        *dst = v;
     }
   }
 }
@@ -2996,12 +2989,12 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   if (rows <= 0) return 0;
   if (rows > 16 || C % 1024 != 0) return (int)hipErrorInvalidValue;
   // Launch shape (every shape gives the same bits): one 16-wave workgroup per
-  // 4 column tiles when that fills the chip and rows <= 8; else two
-  // workgroups per group of CT tiles (the 9-16 row instance of one
+  // 4 column tiles when that fills the chip and rows <= 4; else two
+  // workgroups per group of CT tiles (the 5-16 row instances of one
   // workgroup per group would be held to 128 VGPRs), CT = 4, or, up to 8
   // rows, 2 when 4 gives fewer than kQ4SplitBelow workgroups.
   const int tiles = R0 / 16 + (Wq1 ? R1 / 16 : 0);
-  const bool split = tiles / 4 < kQ4SplitBelow || rows > 8;
+  const bool split = tiles / 4 < kQ4SplitBelow || rows > 4;
   int ct = 4;
   if (split && rows <= 8 && 2 * tiles / 4 < kQ4SplitBelow) ct = 2;
   const int f = split ? 2 : 1;
@@ -3018,17 +3011,19 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   }
   // all of a workgroup's x staged up front when it fits
   const int range = split ? C / 2 : C;
-  const bool pre = rows <= 3 && (int64_t)range / 32 * 128 * rows <= Q4_PRE_BYTES &&
+  const bool pre = rows <= 3 && (int64_t)range / 32 * 192 * rows <= q4_pre_bytes(split) &&
                    (int64_t)range / 256 * rows <= Q4_PRE_K;
   if (pre)
     !split ? launch_q4_pre<false, 4>(a, s)
            : ct == 4 ? launch_q4_pre<true, 4>(a, s) : launch_q4_pre<true, 2>(a, s);
   else if (!split)
     launch_q4<1, false, 4>(a, s);
-  else if (rows <= 8)
+  else if (rows <= 4)
     ct == 4 ? launch_q4<1, true, 4>(a, s) : launch_q4<1, true, 2>(a, s);
+  else if (rows <= 8)
+    ct == 4 ? launch_q4<2, true, 4>(a, s) : launch_q4<2, true, 2>(a, s);
   else
-    launch_q4<2, true, 4>(a, s);
+    launch_q4<4, true, 4>(a, s);
   return (int)hipGetLastError();
 }
 

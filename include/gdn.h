@@ -452,17 +452,19 @@ int gdn_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int32_t 
  * ("Kestrel_VLLM #24", section 8 and Fig. 1 caption, steps 1 and 7).
  * The sum runs in a fixed order: for each row and 256-column chunk, x is
  * scaled by a power of two 2^k (its largest magnitude in [2^14, 2^15)) and
- * split into two binary16 parts x1 = rn(2^k x), x2 = rn(2^k x - x1); the fp16
- * matrix cores form each 32-column block's sums of n x1 and of n x2 (exact
- * products, fp32 accumulation), their fp32 sum T is scaled by s in one fused
- * multiply-add per block, chained over the chunk's 8 blocks from +0 and
- * scaled back by 2^-k; C is cut into 4 quarters whose chunk results are added
- * in order, and y = (q0 + q1) + (q2 + q3).  x2 holds the 22nd and lower
- * significant bits of x that x1 misses, so the result is within fp32
- * reordering error of the exact sum; an infinite x makes every output of its
- * row NaN or infinite, as IEEE arithmetic would.  A row's result does not
- * depend on the other rows of the call, on their number, or on whether the
- * matrix shares the launch with a second one.
+ * split into three binary16 parts x1 = rn(2^k x), x2 = rn(2^k x - x1),
+ * x3 = rn(2^k x - x1 - x2), which add up to 2^k x exactly (for elements of at
+ * least 2^-15 of the chunk's largest magnitude; smaller ones to within 2^-39
+ * of it); the fp16 matrix cores form each 32-column block's sums of n x1,
+ * n x2 and n x3 (exact products, fp32 accumulation), their fp32 sum T is
+ * scaled by s in one fused multiply-add per block, chained over the chunk's 8
+ * blocks from +0 and scaled back by 2^-k; C is cut into 4 quarters whose
+ * chunk results are added in order, and y = (q0 + q1) + (q2 + q3).  So the
+ * result differs from a left fold of the fp32 products by rounding only; an
+ * infinite x makes every output of its row NaN or infinite, as IEEE
+ * arithmetic would.  A row's result does not depend on the other rows of the
+ * call, on their number, or on whether the matrix shares the launch with a
+ * second one.
  *   x [rows][C] fp32; y0 [rows][R0], y1 [rows][R1] fp32; Wq0, Wq1 packed
  *   (16-byte aligned; Wq1 == NULL requires R1 == 0 and y1 == NULL).
  * Ownership: every buffer belongs to the caller; nothing is allocated.

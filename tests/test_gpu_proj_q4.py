@@ -5,9 +5,9 @@ The 4-bit reading ("Kestrel_VLLM #24", sections 8 and 12): each weight is a
 signed 4-bit value times the binary16 scale of its block of 32, exact in fp32.
 Floating point: per element |y - r| <= max(1e-5 |r|, 1e-6 sum_c |W[o][c] x[c]|)
 against the oracle's proj_q4 (a strict left fold of w x with w = n s; the
-kernel forms the products n x on the fp16 matrix cores from x split into two
-binary16 parts that hold its 22 leading bits, and scales each 32-column block's
-sum by s, so the two differ by rounding and by at most 2^-22 |w x| per term).
+kernel forms the products n x on the fp16 matrix cores from x split exactly
+into three binary16 parts, and scales each 32-column block's sum by s, so the
+two differ by rounding only).
 Bit-exact: every result when all partial sums are exact (integer-valued x,
 power-of-two scales: any order gives the same bits), a row's result against
 the same row in calls of every other row count, one launch of two products
