@@ -2461,7 +2461,8 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 //    exactly two addends on +0 the result does not depend on their arrival
 //    order (fp addition is commutative, and none of these sums is -0), so the
 //    shapes give the same bits.  Used for launches with fewer groups than the
-//    chip has CUs (out_proj: 80 groups) and for 5 to 16 rows.
+//    chip has CUs (out_proj: 80 groups) and for 5 to 16 rows; at 5 to 8 rows
+//    each wave takes two column tiles, which share every x operand read.
 // Each row's x is split once per workgroup.  For 1 to 3 rows all of it is
 // staged up front, compactly (only the live row slots; a slot past the rows
 // reads a live slot's x, and its result is never stored), and the K loop runs
@@ -2578,10 +2579,12 @@ static __device__ __forceinline__ int x_split(const f4 &x0, const f4 &x1, unsign
 }
 
 // NT: row tiles of 4 rows (rows <= 4 NT); SPLIT: two workgroups per group of
-// CT column tiles (quarters 0-1 and 2-3), else one (all four quarters)
-template <int NT, bool SPLIT, int CT>
+// CT TW column tiles (quarters 0-1 and 2-3), else one (all four quarters); TW:
+// column tiles per wave, which share each x operand read
+template <int NT, bool SPLIT, int CT, int TW>
 __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Args a) {
-  static_assert(CT == 2 || CT == 4, "4 or 2 column tiles per workgroup");
+  static_assert(CT == 2 || CT == 4, "4 or 2 wave columns per workgroup");
+  static_assert(TW == 1 || TW == 2, "1 or 2 column tiles per wave");
   constexpr int NQ = SPLIT ? 2 : 4;            // quarters per workgroup
   constexpr int NTHR = 64 * CT * NQ;
   constexpr int STAGE = NQ * Q4_CH * NT * 1024;
@@ -2601,10 +2604,10 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
   const int ct = wave % CT, qw = wave / CT;
   const int q = q0 + qw;
   const int C = a.C, rows = a.rows, nblk = C / 32, Q = nblk / 4, nch = Q / Q4_CH;
-  const int tile = CT * g + ct;
+  const int tile = (CT * g + ct) * TW;         // the wave's first column tile
+  const int tbytes = nblk / Q4_CH * Q4_TC;     // packed bytes of one column tile
   const rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(W + (int64_t)tile * (nblk / Q4_CH) * Q4_TC), 0,
-      nblk / Q4_CH * Q4_TC, RSRC_FLAGS);
+      const_cast<uint8_t *>(W + (int64_t)tile * tbytes), 0, TW * tbytes, RSRC_FLAGS);
 
   // zero both stage buffers: the pad slot of every row and the slots past
   // `rows` stay zero
@@ -2664,21 +2667,26 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
     }
   };
 
-  // weights of chunk ch: the lane's 8 dwords (blocks q Q + ch CH + 0..7) and
-  // its output's 8 scales, three 128-bit loads
+  // weights of chunk ch, per column tile of the wave: the lane's 8 dwords
+  // (blocks q Q + ch CH + 0..7) and its output's 8 scales, three 128-bit loads
   struct WSet {
-    u4 w0, w1, s;
+    u4 w0[TW], w1[TW], s[TW];
   };
   auto w_issue = [&](WSet &ws, int ch) {
     const bool ok = ch < nch;
     const int so = __builtin_amdgcn_readfirstlane((ok ? q * nch + ch : 0) * Q4_TC);
-    ws.w0 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       wr, ok ? 32 * l : Q4_OOB, so, POL_STREAM_LOAD));
-    ws.w1 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       wr, ok ? 32 * l + 16 : Q4_OOB, so, POL_STREAM_LOAD));
-    ws.s = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                      wr, ok ? 2048 + 16 * (l & 15) : Q4_OOB, so,
-                                      POL_STREAM_LOAD));
+#pragma unroll
+    for (int tw = 0; tw < TW; tw++) {
+      ws.w0[tw] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             wr, ok ? 32 * l : Q4_OOB, so + tw * tbytes,
+                                             POL_STREAM_LOAD));
+      ws.w1[tw] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             wr, ok ? 32 * l + 16 : Q4_OOB, so + tw * tbytes,
+                                             POL_STREAM_LOAD));
+      ws.s[tw] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            wr, ok ? 2048 + 16 * (l & 15) : Q4_OOB,
+                                            so + tw * tbytes, POL_STREAM_LOAD));
+    }
   };
 
   // Loads return in order, so a chunk's x is requested two chunks ahead,
@@ -2695,10 +2703,13 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
 
   unsigned magic = 0x64006400u;                // binary16 1024 in both halves
   __asm__("" : "+v"(magic));                   // kept in a vector register
-  float acc[NT];
+  float acc[TW][NT];
 #pragma unroll
-  for (int t = 0; t < NT; t++) acc[t] = 0.f;
-  constexpr int GB = NT == 1 ? 4 : 2;          // blocks whose products are in flight together
+  for (int tw = 0; tw < TW; tw++)
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[tw][t] = 0.f;
+  // blocks whose products are in flight together
+  constexpr int GB = TW == 1 ? (NT == 1 ? 4 : 2) : (NT <= 2 ? 2 : 1);
 
   // one chunk: issue chunk ch + 2's x and weights, compute chunk ch, stage
   // chunk ch + 1's x, one barrier
@@ -2710,25 +2721,34 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
       // swizzled place
       const unsigned char *buf = xs[ch & 1] + (qw * Q4_CH) * NT * 1024;
       const int lx = 16 * (l ^ ((l >> 1) & 8));
-      float cacc[NT];
+      float cacc[TW][NT];
 #pragma unroll
-      for (int t = 0; t < NT; t++) cacc[t] = 0.f;
+      for (int tw = 0; tw < TW; tw++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) cacc[tw][t] = 0.f;
 #pragma unroll
       for (int h = 0; h < Q4_CH / GB; h++) {
-        f4 D[GB][NT];
-        float sv[GB];
+        f4 D[GB][NT][TW];
+        float sv[GB][TW];
 #pragma unroll
         for (int j = 0; j < GB; j++) {
           const int i = GB * h + j;
-          const h8 B = q4_decode(i < 4 ? cur.w0[i] : cur.w1[i - 4], magic);
-          const unsigned sw = cur.s[i >> 1];
-          sv[j] = (float)__builtin_bit_cast(_Float16,
-                                            (unsigned short)((i & 1) ? sw >> 16 : sw & 0xffffu));
+          h8 B[TW];
+#pragma unroll
+          for (int tw = 0; tw < TW; tw++) {
+            B[tw] = q4_decode(i < 4 ? cur.w0[tw][i] : cur.w1[tw][i - 4], magic);
+            const unsigned sw = cur.s[tw][i >> 1];
+            sv[j][tw] = (float)__builtin_bit_cast(
+                _Float16, (unsigned short)((i & 1) ? sw >> 16 : sw & 0xffffu));
+          }
 #pragma unroll
           for (int t = 0; t < NT; t++) {
             const h8 A =
                 *reinterpret_cast<const h8 *>(buf + (i * NT + t) * 1024 + (lx ^ (16 * i)));
-            D[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, f4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+            for (int tw = 0; tw < TW; tw++)
+              D[j][t][tw] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[tw], f4{0, 0, 0, 0}, 0, 0, 0);
           }
         }
         // the lane's row of each tile: its three parts' sums
@@ -2736,12 +2756,17 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
         for (int j = 0; j < GB; j++)
 #pragma unroll
           for (int t = 0; t < NT; t++)
-            cacc[t] = __builtin_fmaf((D[j][t].x + D[j][t].y) + D[j][t].z, sv[j], cacc[t]);
+#pragma unroll
+            for (int tw = 0; tw < TW; tw++)
+              cacc[tw][t] = __builtin_fmaf((D[j][t][tw].x + D[j][t][tw].y) + D[j][t][tw].z,
+                                           sv[j][tw], cacc[tw][t]);
       }
 #pragma unroll
       for (int t = 0; t < NT; t++) {
         const int k = kexp[ch & 1][qw][4 * t + (l >> 4)];
-        acc[t] = acc[t] + __builtin_amdgcn_ldexpf(cacc[t], -k);
+#pragma unroll
+        for (int tw = 0; tw < TW; tw++)
+          acc[tw][t] = acc[tw][t] + __builtin_amdgcn_ldexpf(cacc[tw][t], -k);
       }
     }
     if (ch + 1 < nch) x_stage(xn, ch + 1);
@@ -2754,25 +2779,30 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
   }
 
   // fold the quarters: wave (ct, qw) -> LDS; the first quarter's waves add
-  float *fold = reinterpret_cast<float *>(&xs[0][0]);   // [ct][qw][t][64]
+  float *fold = reinterpret_cast<float *>(&xs[0][0]);   // [ct][qw][tw][t][64]
+  static_assert(CT * NQ * TW * NT * 256 <= 2 * STAGE, "fold fits the stage buffers");
 #pragma unroll
-  for (int t = 0; t < NT; t++) fold[((ct * NQ + qw) * NT + t) * 64 + l] = acc[t];
+  for (int tw = 0; tw < TW; tw++)
+#pragma unroll
+    for (int t = 0; t < NT; t++) fold[(((ct * NQ + qw) * TW + tw) * NT + t) * 64 + l] = acc[tw][t];
   __syncthreads();
   if (qw == 0) {
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
-      auto at = [&](int qq) { return fold[((ct * NQ + qq) * NT + t) * 64 + l]; };
-      const int row = 4 * t + (l >> 4);
-      float v = acc[t] + at(1);
-      if constexpr (!SPLIT) v = v + (at(2) + at(3));
-      if (row < rows) {
-        float *dst = y + (int64_t)row * R + 16 * tile + (l & 15);
-        if constexpr (SPLIT)
-          atomicAdd(dst, v);                   // two addends on +0: order-free
-        else
-          *dst = v;
+    for (int tw = 0; tw < TW; tw++)
+#pragma unroll
+      for (int t = 0; t < NT; t++) {
+        auto at = [&](int qq) { return fold[(((ct * NQ + qq) * TW + tw) * NT + t) * 64 + l]; };
+        const int row = 4 * t + (l >> 4);
+        float v = acc[tw][t] + at(1);
+        if constexpr (!SPLIT) v = v + (at(2) + at(3));
+        if (row < rows) {
+          float *dst = y + (int64_t)row * R + 16 * (tile + tw) + (l & 15);
+          if constexpr (SPLIT)
+            atomicAdd(dst, v);                 // two addends on +0: order-free
+          else
+            *dst = v;
+        }
       }
-    }
   }
 }
 
@@ -2971,9 +3001,9 @@ int launch_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int R
   return (int)hipGetLastError();
 }
 
-template <int NT, bool SPLIT, int CT>
+template <int NT, bool SPLIT, int CT, int TW = 1>
 static void launch_q4(const Q4Args &a, hipStream_t s) {
-  hipLaunchKernelGGL((proj_q4_kernel<NT, SPLIT, CT>), dim3((unsigned)(a.p[0].wgs + a.p[1].wgs)),
+  hipLaunchKernelGGL((proj_q4_kernel<NT, SPLIT, CT, TW>), dim3((unsigned)(a.p[0].wgs + a.p[1].wgs)),
                      dim3(64 * CT * (SPLIT ? 2 : 4)), 0, s, a);
 }
 template <bool SPLIT, int CT>
@@ -2993,24 +3023,29 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   if (rows > 16 || C % 1024 != 0) return (int)hipErrorInvalidValue;
   // Launch shape (every shape gives the same bits): one 16-wave workgroup per
   // 4 column tiles when that fills the chip and rows <= 4; else two
-  // workgroups per group of CT tiles (the 5-16 row instances of one
+  // workgroups per group of CT TW tiles (the 5-16 row instances of one
   // workgroup per group would be held to 128 VGPRs), CT = 4, or, up to 8
-  // rows, 2 when 4 gives fewer than kQ4SplitBelow workgroups.
+  // rows, 2 when 4 gives fewer than kQ4SplitBelow workgroups; TW = 2 for 5-8
+  // rows (at 9-16 rows the pair of tiles would spill).
   const int tiles = R0 / 16 + (Wq1 ? R1 / 16 : 0);
   // one row, too few groups of 4 tiles, enough single tiles: one workgroup
   // per tile, the up-front stage of x small enough for four per CU
   const bool tile1 = rows == 1 && tiles / 4 < kQ4SplitBelow && tiles >= kQ4SplitBelow &&
                      C / 32 * 192 <= q4_pre_bytes(false, 1);
+  // 5-8 rows: two column tiles per wave (one x operand read serves both;
+  // also where that leaves fewer workgroups than CUs)
+  const bool pair = rows > 4 && rows <= 8 && R0 % 128 == 0 && (!Wq1 || R1 % 128 == 0);
   const bool split = (tiles / 4 < kQ4SplitBelow || rows > 4) && !tile1;
   int ct = tile1 ? 1 : 4;
   if (split && rows <= 8 && 2 * tiles / 4 < kQ4SplitBelow) ct = 2;
   const int f = split ? 2 : 1;
+  const int tw = pair ? 2 : 1;
   Q4Args a{};
   a.x = x;
   a.rows = (int)rows;
   a.C = C;
-  a.p[0] = Q4Problem{static_cast<const uint8_t *>(Wq0), y0, R0, R0 / 16 / ct * f};
-  a.p[1] = Q4Problem{static_cast<const uint8_t *>(Wq1), y1, R1, Wq1 ? R1 / 16 / ct * f : 0};
+  a.p[0] = Q4Problem{static_cast<const uint8_t *>(Wq0), y0, R0, R0 / 16 / (ct * tw) * f};
+  a.p[1] = Q4Problem{static_cast<const uint8_t *>(Wq1), y1, R1, Wq1 ? R1 / 16 / (ct * tw) * f : 0};
   if (split) {
     const int64_t n0 = rows * R0, n1 = Wq1 ? rows * R1 : 0;
     hipLaunchKernelGGL(zero2_kernel, dim3((unsigned)((n0 + n1 + 255) / 256)), dim3(256), 0, s,
@@ -3031,7 +3066,8 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   else if (rows <= 4)
     ct == 4 ? launch_q4<1, true, 4>(a, s) : launch_q4<1, true, 2>(a, s);
   else if (rows <= 8)
-    ct == 4 ? launch_q4<2, true, 4>(a, s) : launch_q4<2, true, 2>(a, s);
+    tw == 2 ? (ct == 4 ? launch_q4<2, true, 4, 2>(a, s) : launch_q4<2, true, 2, 2>(a, s))
+            : (ct == 4 ? launch_q4<2, true, 4>(a, s) : launch_q4<2, true, 2>(a, s));
   else
     launch_q4<4, true, 4>(a, s);
   return (int)hipGetLastError();

@@ -109,7 +109,7 @@ def test_q4_pack_layout(R, C):
 
 @pytest.mark.parametrize("rows,R,C", [(1, 64, 1024), (3, 192, 2048), (8, 320, 3072),
                                       (16, 512, 5120), (1, 10240, 5120), (16, 5120, 6144),
-                                      (5, 16384, 1024)])
+                                      (5, 16384, 1024), (8, 5120, 1024), (6, 384, 2048)])
 def test_q4_exact_when_every_partial_sum_is_exact(orc, rows, R, C):
     """Integer x in [-3, 3] and power-of-two scales 2^-2 .. 2^2: every product
     and partial sum is a multiple of 2^-2 below 2^22, so any summation order
@@ -239,12 +239,29 @@ def test_q4_nan_in_x_reaches_only_its_row(rows, R):
 
 def test_q4_staging_variants_agree_bit_for_bit():
     """At the layer's in_proj size (C = 5120, 16384 outputs) calls of 1-3 rows
-    stage all of x up front and calls of 4-8 rows stage it chunk by chunk:
-    every row of an 8-row call equals the same row in the calls of 1..7 rows,
-    in either variant."""
+    stage all of x up front and calls of 4-8 rows stage it chunk by chunk
+    (5-8 rows with two column tiles per wave): every row of an 8-row call
+    equals the same row in the calls of 1..7 rows, in either variant."""
     say("proj_q4 staging variants")
     C, R = 5120, 16384
     x, q, sc = q4_operands(157, 8, R, C)
+    Wq = gdn.proj_q4_pack(q, sc)
+    full = host(gdn.proj_q4(x, Wq))
+    for n in range(1, 8):
+        lo = 8 - n
+        part = host(gdn.proj_q4(x[lo:].contiguous(), Wq))
+        assert bits_equal(part, np.ascontiguousarray(full[lo:])), n
+
+
+def test_q4_paired_tiles_agree_bit_for_bit():
+    """At the layer's out_proj size (C = 6144, 5120 outputs: fewer 64-output
+    groups than CUs) a call of 5-8 rows runs two column tiles per wave in two
+    workgroups per group of 4 tiles, 4 rows two workgroups per group of 2
+    tiles, 2-3 rows the up-front staging and 1 row one workgroup per tile:
+    every row of an 8-row call equals the same row in the calls of 1..7 rows."""
+    say("proj_q4 paired tiles")
+    C, R = 6144, 5120
+    x, q, sc = q4_operands(163, 8, R, C)
     Wq = gdn.proj_q4_pack(q, sc)
     full = host(gdn.proj_q4(x, Wq))
     for n in range(1, 8):
