@@ -2530,11 +2530,14 @@ static __device__ __forceinline__ h8 q4_decode(unsigned w, unsigned magic) {
 }
 
 // v - (float)h (h the low or high binary16 of p): exact, since h is v
-// rounded to binary16
+// rounded to binary16.  m1 is -1 held in a register the compiler cannot see
+// through, so the fma stays one mixed-precision instruction reading the
+// binary16 half directly (with a literal -1 it becomes a conversion and a
+// subtraction).
 template <bool HI>
-static __device__ __forceinline__ float minus_half(unsigned p, float v) {
+static __device__ __forceinline__ float minus_half(unsigned p, float v, float m1) {
   const float h = (float)__builtin_bit_cast(_Float16, (unsigned short)(HI ? p >> 16 : p & 0xffffu));
-  return __builtin_fmaf(h, -1.0f, v);
+  return __builtin_fmaf(h, m1, v);
 }
 
 static __device__ __forceinline__ unsigned pk_half(float a, float b) {
@@ -2546,9 +2549,11 @@ static __device__ __forceinline__ unsigned pk_half(float a, float b) {
 // of the row's chunk, which hold its 256 columns) and the three binary16 parts
 // of 2^k x, each as 4 packed pairs.  A residual of an infinite x is NaN: a
 // packed max (which passes over NaN) replaces it by a finite value, so the
-// infinity itself reaches the sum through the first part.
+// infinity itself reaches the sum through the first part; the max is skipped
+// when no lane of the wave holds an infinite x (it would change nothing).
+// m1: -1 (minus_half).  Every lane of the wave calls this together.
 static __device__ __forceinline__ int x_split(const f4 &x0, const f4 &x1, unsigned (&p1)[4],
-                                              unsigned (&p2)[4], unsigned (&p3)[4]) {
+                                              unsigned (&p2)[4], unsigned (&p3)[4], float m1) {
   const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
   float m = 0.f;
 #pragma unroll
@@ -2560,20 +2565,25 @@ static __device__ __forceinline__ int x_split(const f4 &x0, const f4 &x1, unsign
   m = fmaxf(m, lane_xor<1>(m));
   // largest magnitude in [2^14, 2^15) after scaling (m = 0: any k)
   const int k = 15 - __builtin_amdgcn_frexp_expf(m);
-  const h2 lo = {(_Float16)-65504.0f, (_Float16)-65504.0f};
-  auto clamp = [&](unsigned r) {
-    return __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(h2, r), lo));
-  };
 #pragma unroll
   for (int e = 0; e < 4; e++) {
     const float s0 = __builtin_amdgcn_ldexpf(v[2 * e], k);
     const float s1 = __builtin_amdgcn_ldexpf(v[2 * e + 1], k);
     p1[e] = pk_half(s0, s1);
-    const float r0 = minus_half<false>(p1[e], s0), r1 = minus_half<true>(p1[e], s1);
-    const unsigned q2 = pk_half(r0, r1);
-    const float t0 = minus_half<false>(q2, r0), t1 = minus_half<true>(q2, r1);
-    p2[e] = clamp(q2);
-    p3[e] = clamp(pk_half(t0, t1));
+    const float r0 = minus_half<false>(p1[e], s0, m1), r1 = minus_half<true>(p1[e], s1, m1);
+    p2[e] = pk_half(r0, r1);
+    const float t0 = minus_half<false>(p2[e], r0, m1), t1 = minus_half<true>(p2[e], r1, m1);
+    p3[e] = pk_half(t0, t1);
+  }
+  if (__builtin_amdgcn_ballot_w64(m > 3.4028235e38f) != 0) {   // an infinite x in the wave
+    const h2 lo = {(_Float16)-65504.0f, (_Float16)-65504.0f};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      p2[e] = __builtin_bit_cast(unsigned,
+                                 __builtin_elementwise_max(__builtin_bit_cast(h2, p2[e]), lo));
+      p3[e] = __builtin_bit_cast(unsigned,
+                                 __builtin_elementwise_max(__builtin_bit_cast(h2, p3[e]), lo));
+    }
   }
   return k;
 }
@@ -2601,6 +2611,8 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
+  float m1 = -1.0f;                            // x_split's -1, kept in a register
+  __asm__("" : "+v"(m1));                      // (no instruction; defined before any product)
   const int ct = wave % CT, qw = wave / CT;
   const int q = q0 + qw;
   const int C = a.C, rows = a.rows, nblk = C / 32, Q = nblk / 4, nch = Q / Q4_CH;
@@ -2657,7 +2669,7 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
 #pragma unroll
     for (int it = 0; it < ITEMS; it++) {
       unsigned p1[4], p2[4], p3[4];
-      const int k = x_split(xv.v[it][0], xv.v[it][1], p1, p2, p3);
+      const int k = x_split(xv.v[it][0], xv.v[it][1], p1, p2, p3, m1);
       if (xoff[it] >= 0) {
         *reinterpret_cast<u4 *>(buf + xdst[it]) = u4{p1[0], p1[1], p1[2], p1[3]};
         *reinterpret_cast<u4 *>(buf + (xdst[it] ^ 16)) = u4{p2[0], p2[1], p2[2], p2[3]};
@@ -2837,6 +2849,8 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
+  float m1 = -1.0f;                            // x_split's -1, kept in a register
+  __asm__("" : "+v"(m1));                      // (no instruction; defined before any product)
   const int ct = wave % CT, qw = wave / CT;
   const int q = q0 + qw;
   constexpr int rows = NR, S3 = 3 * NR;        // live row slots (three parts per row)
@@ -2891,7 +2905,7 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(
     f4 x0 = xn0, x1 = xn1;
     if (base > 0) x_load(base, x0, x1);
     unsigned p1[4], p2[4], p3[4];
-    const int k = x_split(x0, x1, p1, p2, p3);
+    const int k = x_split(x0, x1, p1, p2, p3, m1);
     if (ok) {
       unsigned char *dst = xp + (((c * Q4_CH + i) * 4 + d) * S3 + 3 * bb) * 16;
       *reinterpret_cast<u4 *>(dst) = u4{p1[0], p1[1], p1[2], p1[3]};
