@@ -2547,23 +2547,37 @@ static __device__ __forceinline__ unsigned pk_half(float a, float b) {
 
 // 8 consecutive x of one row -> the chunk's exponent k (shared by the 32 lanes
 // of the row's chunk, which hold its 256 columns) and the three binary16 parts
-// of 2^k x, each as 4 packed pairs.  A residual of an infinite x is NaN: a
-// packed max (which passes over NaN) replaces it by a finite value, so the
-// infinity itself reaches the sum through the first part; the max is skipped
-// when no lane of the wave holds an infinite x (it would change nothing).
-// m1: -1 (minus_half).  Every lane of the wave calls this together.
+// of 2^k x, each as 4 packed pairs.  An infinite x: k comes from the chunk's
+// largest finite magnitude (an infinite one would leave k = 15 and overflow
+// the chunk's other values to infinities), the infinity reaches the sum
+// through the first part, and its NaN residuals are replaced by finite values
+// with a packed max (which passes over NaN); waves without an infinite x skip
+// both.  m1: -1 (minus_half).  Every lane of the wave calls this together.
 static __device__ __forceinline__ int x_split(const f4 &x0, const f4 &x1, unsigned (&p1)[4],
                                               unsigned (&p2)[4], unsigned (&p3)[4], float m1) {
   const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
   float m = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; e++) m = fmaxf(m, fabsf(v[e]));     // NaN is passed over
-  m = fmaxf(m, lane_xor<16>(m));
-  m = fmaxf(m, lane_xor<8>(m));
-  m = fmaxf(m, lane_xor<4>(m));
-  m = fmaxf(m, lane_xor<2>(m));
-  m = fmaxf(m, lane_xor<1>(m));
-  // largest magnitude in [2^14, 2^15) after scaling (m = 0: any k)
+  auto half_wave_max = [](float mm) {
+    mm = fmaxf(mm, lane_xor<16>(mm));
+    mm = fmaxf(mm, lane_xor<8>(mm));
+    mm = fmaxf(mm, lane_xor<4>(mm));
+    mm = fmaxf(mm, lane_xor<2>(mm));
+    return fmaxf(mm, lane_xor<1>(mm));
+  };
+  m = half_wave_max(m);
+  const bool inf = __builtin_amdgcn_ballot_w64(m > 3.4028235e38f) != 0;   // wave-uniform
+  if (inf) {
+    m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float a = fabsf(v[e]);
+      m = fmaxf(m, a <= 3.4028235e38f ? a : 0.f);
+    }
+    m = half_wave_max(m);
+  }
+  // largest finite magnitude in [2^14, 2^15) after scaling (m = 0: any k)
   const int k = 15 - __builtin_amdgcn_frexp_expf(m);
 #pragma unroll
   for (int e = 0; e < 4; e++) {
@@ -2575,7 +2589,7 @@ static __device__ __forceinline__ int x_split(const f4 &x0, const f4 &x1, unsign
     const float t0 = minus_half<false>(p2[e], r0, m1), t1 = minus_half<true>(p2[e], r1, m1);
     p3[e] = pk_half(t0, t1);
   }
-  if (__builtin_amdgcn_ballot_w64(m > 3.4028235e38f) != 0) {   // an infinite x in the wave
+  if (inf) {
     const h2 lo = {(_Float16)-65504.0f, (_Float16)-65504.0f};
 #pragma unroll
     for (int e = 0; e < 4; e++) {

@@ -237,6 +237,39 @@ def test_q4_nan_in_x_reaches_only_its_row(rows, R):
     assert bits_equal(y[~nan], clean[~nan])
 
 
+@pytest.mark.parametrize("rows,R", [(1, 16384), (1, 5120), (3, 192), (4, 192), (8, 256),
+                                    (8, 16384), (16, 192)])
+def test_q4_infinite_x_matches_oracle(orc, rows, R):
+    """An infinite x (IEEE: w x is +-inf, NaN where w is 0, and +inf and -inf
+    in one row give NaN) gives the oracle's class in every output of its row:
+    +inf, -inf or NaN, with the row's other values scaled by the largest
+    finite magnitude of their chunk (x of magnitude up to 12 here, which a
+    scale set by the infinity would overflow in binary16).  Rows without one
+    keep the bits of the call without infinities.  Every launch shape: one
+    row with one or four tiles per workgroup, the up-front staging, one and
+    two column tiles per wave, four row tiles."""
+    say(f"proj_q4 infinite x rows={rows} R={R}")
+    C = 2048
+    x, q, sc = q4_operands(167, rows, R, C)
+    x = x * 3.0
+    Wq = gdn.proj_q4_pack(q, sc)
+    clean = host(gdn.proj_q4(x, Wq))
+    xi = x.clone()
+    r = rows // 2
+    xi[r, 5] = float("inf")
+    if rows >= 3:
+        xi[0, C - 7] = float("-inf")
+        xi[rows - 1, 300] = float("inf")
+        xi[rows - 1, 301] = float("-inf")
+    y = host(gdn.proj_q4(xi, Wq))
+    ref = ref_q4(orc, host(xi), q, sc)
+    for cls in (np.isnan, np.isposinf, np.isneginf):
+        assert np.array_equal(cls(y), cls(ref)), cls.__name__
+    hit = ~np.isfinite(host(xi)).all(axis=1)
+    assert (~np.isfinite(ref[hit])).all()
+    assert bits_equal(np.ascontiguousarray(y[~hit]), np.ascontiguousarray(clean[~hit]))
+
+
 def test_q4_staging_variants_agree_bit_for_bit():
     """At the layer's in_proj size (C = 5120, 16384 outputs) calls of 1-3 rows
     stage all of x up front and calls of 4-8 rows stage it chunk by chunk
