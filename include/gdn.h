@@ -461,8 +461,9 @@ int gdn_proj_q4_pack(const uint8_t *q, const uint16_t *scale, void *Wq, int32_t 
  * blocks from +0 and scaled back by 2^-k; C is cut into 4 quarters whose
  * chunk results are added in order, and y = (q0 + q1) + (q2 + q3).  So the
  * result differs from a left fold of the fp32 products by rounding only; an
- * infinite x makes every output of its row NaN or infinite, as IEEE
- * arithmetic would.  A row's result does not depend on the other rows of the
+ * infinite x makes every output of its row +inf, -inf or NaN, the class the
+ * left fold gives (the chunk's scale 2^k then comes from its largest finite
+ * magnitude).  A row's result does not depend on the other rows of the
  * call, on their number, or on whether the matrix shares the launch with a
  * second one.
  *   x [rows][C] fp32; y0 [rows][R0], y1 [rows][R1] fp32; Wq0, Wq1 packed
