@@ -364,14 +364,16 @@ def test_q4_refuses_more_than_16_rows_and_accepts_none():
 
 @pytest.mark.parametrize("dims", [synth.DIMS128, synth.DIMS64])
 def test_q4_layer_sizes_sampled(orc, dims):
-    """The layer's full projection sizes with 4-bit weights at 1 and 16 rows,
-    in the launches the benchmark times, on rows the oracle recomputes."""
+    """The layer's full projection sizes with 4-bit weights at 1, 8 and 16
+    rows, in the launches the benchmark times (8 rows: two column tiles per
+    wave, in_proj_qkv and in_proj_z in one launch), on rows the oracle
+    recomputes."""
     vh, kh, kd, vd = dims
     dim = synth.FE_DIM
     gen = synth.make_gen(113, "cuda")
     w = synth.proj_weights_q4(gen, dims, device="cuda")
     wq = {n: gdn.proj_q4_pack(*w[n]) for n in ("W_qkv", "W_z", "W_out")}
-    for rows, pick in ((1, [0]), (16, [0, 9, 15])):
+    for rows, pick in ((1, [0]), (8, [0, 5, 7]), (16, [0, 9, 15])):
         say(f"proj_q4 layer sizes dims={dims} rows={rows}")
         x = torch.randn((rows, dim), generator=gen, device="cuda")
         h = torch.randn((rows, vh * vd), generator=gen, device="cuda")
