@@ -270,6 +270,34 @@ def test_q4_infinite_x_matches_oracle(orc, rows, R):
     assert bits_equal(np.ascontiguousarray(y[~hit]), np.ascontiguousarray(clean[~hit]))
 
 
+@pytest.mark.parametrize("rows,R", [(1, 16384), (3, 192), (8, 256), (16, 192)])
+def test_q4_extreme_magnitudes_of_x(orc, rows, R):
+    """Rows of x near 1e30 and near 1e-30 (each 256-column chunk takes its
+    own power-of-two scale, far from the usual k), and rows that mix 1e20 and
+    1e-20 inside one chunk (the small values lie below 2^-15 of the chunk's
+    largest and keep only what the three parts hold): within the projection
+    tolerance of the oracle, in every launch shape."""
+    say(f"proj_q4 extreme magnitudes rows={rows} R={R}")
+    C = 2048
+    x, q, sc = q4_operands(173, rows, R, C)
+    scale = torch.ones((rows, C), device="cuda")
+    for r in range(rows):
+        kind = r % 3
+        if kind == 0:
+            scale[r] = 1e30
+        elif kind == 1:
+            scale[r] = 1e-30
+        else:
+            scale[r, 0::2] = 1e20
+            scale[r, 1::2] = 1e-20
+    xe = (x * scale).contiguous()
+    y = host(gdn.proj_q4(xe, gdn.proj_q4_pack(q, sc)))
+    xh = host(xe)
+    assert np.isfinite(y).all()
+    assert_close(y, ref_q4(orc, xh, q, sc), f"proj_q4 extreme {rows}x{R}", rel=1e-5,
+                 floor=proj_floor(xh, decode_np(host(q), host(sc))))
+
+
 def test_q4_staging_variants_agree_bit_for_bit():
     """At the layer's in_proj size (C = 5120, 16384 outputs) calls of 1-3 rows
     stage all of x up front and calls of 4-8 rows stage it chunk by chunk
