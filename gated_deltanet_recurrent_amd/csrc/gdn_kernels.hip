@@ -30,8 +30,9 @@
 // (M draft rows of a few sequences run their conv rows in parallel).
 // Projections (Fig. 1 caption, steps 1 and 7): f32 weights on the fp32
 // matrix cores in packed operand order, and 4-bit weights with binary16 block
-// scales on a VALU kernel (section 8 and 12), each with a fixed summation
-// order independent of the row count.
+// scales (section 8 and 12) on the fp16 matrix cores, the values decoded
+// exactly and x split exactly into three binary16 parts; each with a fixed
+// summation order independent of the row count.
 #include "gdn_launch.h"
 
 #include <hip/hip_runtime.h>
