@@ -2457,7 +2457,7 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 //  - one 16-wave workgroup per group of 4 column tiles (64 outputs; wave =
 //    column tile x quarter), the quarter sums folded in LDS, for launches of
 //    up to 4 rows with enough groups to fill the chip;
-//  - two workgroups per group of 4 or 2 column tiles (quarters 0-1 and 2-3),
+//  - two workgroups per group of 4 column tiles (quarters 0-1 and 2-3),
 //    each adding its half into y, which a fill kernel zeroed first.  With
 //    exactly two addends on +0 the result does not depend on their arrival
 //    order (fp addition is commutative, and none of these sums is -0), so the
@@ -2481,7 +2481,7 @@ int launch_proj(const float *x, int64_t rows, int C, const float *W0, int R0, fl
 // the 8 binary16 scales of output 16 t + o for the chunk's blocks.
 
 // launches that one workgroup per 4 column tiles would give fewer workgroups
-// than this take two workgroups per group (of 4 or 2 tiles)
+// than this take two workgroups per group
 constexpr int kQ4SplitBelow = 256;
 constexpr int Q4_CH = 8;                       // blocks per quarter per chunk
 constexpr int Q4_TC = 2304;                    // bytes per column tile and chunk
@@ -3052,21 +3052,22 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   if (rows > 16 || C % 1024 != 0) return (int)hipErrorInvalidValue;
   // Launch shape (every shape gives the same bits): one 16-wave workgroup per
   // 4 column tiles when that fills the chip and rows <= 4; else two
-  // workgroups per group of CT TW tiles (the 5-16 row instances of one
-  // workgroup per group would be held to 128 VGPRs), CT = 4, or, up to 8
-  // rows, 2 when 4 gives fewer than kQ4SplitBelow workgroups; TW = 2 for 5-8
-  // rows (at 9-16 rows the pair of tiles would spill).
+  // workgroups per group of 4 TW tiles (the 5-16 row instances of one
+  // workgroup per group would be held to 128 VGPRs), TW = 2 for 5-8 rows when
+  // the groups of 8 tiles still fill the chip (at 9-16 rows the pair of tiles
+  // would spill).  Fewer, fuller workgroups beat more of 2 tiles each: with 4
+  // wave columns the split of x is shared by twice the waves.
   const int tiles = R0 / 16 + (Wq1 ? R1 / 16 : 0);
   // one row, too few groups of 4 tiles, enough single tiles: one workgroup
   // per tile, the up-front stage of x small enough for four per CU
   const bool tile1 = rows == 1 && tiles / 4 < kQ4SplitBelow && tiles >= kQ4SplitBelow &&
                      C / 32 * 192 <= q4_pre_bytes(false, 1);
-  // 5-8 rows: two column tiles per wave (one x operand read serves both;
-  // also where that leaves fewer workgroups than CUs)
-  const bool pair = rows > 4 && rows <= 8 && R0 % 128 == 0 && (!Wq1 || R1 % 128 == 0);
+  // 5-8 rows: two column tiles per wave (one x operand read serves both)
+  // when two workgroups per group of 8 tiles still fill the chip
+  const bool pair = rows > 4 && rows <= 8 && R0 % 128 == 0 && (!Wq1 || R1 % 128 == 0) &&
+                    tiles / 8 * 2 >= kQ4SplitBelow;
   const bool split = (tiles / 4 < kQ4SplitBelow || rows > 4) && !tile1;
-  int ct = tile1 ? 1 : 4;
-  if (split && rows <= 8 && 2 * tiles / 4 < kQ4SplitBelow) ct = 2;
+  const int ct = tile1 ? 1 : 4;
   const int f = split ? 2 : 1;
   const int tw = pair ? 2 : 1;
   Q4Args a{};
@@ -3088,15 +3089,13 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
     hipLaunchKernelGGL((proj_q4_pre_kernel<false, 1, 1>), dim3((unsigned)(a.p[0].wgs + a.p[1].wgs)),
                        dim3(256), 0, s, a);
   else if (pre)
-    !split ? launch_q4_pre<false, 4>(a, s)
-           : ct == 4 ? launch_q4_pre<true, 4>(a, s) : launch_q4_pre<true, 2>(a, s);
+    !split ? launch_q4_pre<false, 4>(a, s) : launch_q4_pre<true, 4>(a, s);
   else if (!split)
     launch_q4<1, false, 4>(a, s);
   else if (rows <= 4)
-    ct == 4 ? launch_q4<1, true, 4>(a, s) : launch_q4<1, true, 2>(a, s);
+    launch_q4<1, true, 4>(a, s);
   else if (rows <= 8)
-    tw == 2 ? (ct == 4 ? launch_q4<2, true, 4, 2>(a, s) : launch_q4<2, true, 2, 2>(a, s))
-            : (ct == 4 ? launch_q4<2, true, 4>(a, s) : launch_q4<2, true, 2>(a, s));
+    tw == 2 ? launch_q4<2, true, 4, 2>(a, s) : launch_q4<2, true, 4>(a, s);
   else
     launch_q4<4, true, 4>(a, s);
   return (int)hipGetLastError();

@@ -316,10 +316,10 @@ def test_q4_staging_variants_agree_bit_for_bit():
 
 def test_q4_paired_tiles_agree_bit_for_bit():
     """At the layer's out_proj size (C = 6144, 5120 outputs: fewer 64-output
-    groups than CUs) a call of 5-8 rows runs two column tiles per wave in two
-    workgroups per group of 4 tiles, 4 rows two workgroups per group of 2
-    tiles, 2-3 rows the up-front staging and 1 row one workgroup per tile:
-    every row of an 8-row call equals the same row in the calls of 1..7 rows."""
+    groups than CUs) a call of 4-8 rows runs two workgroups per group of 4
+    column tiles (one tile per wave: too few groups of 8 tiles to pair them),
+    2-3 rows the up-front staging and 1 row one workgroup per tile: every row
+    of an 8-row call equals the same row in the calls of 1..7 rows."""
     say("proj_q4 paired tiles")
     C, R = 6144, 5120
     x, q, sc = q4_operands(163, 8, R, C)
