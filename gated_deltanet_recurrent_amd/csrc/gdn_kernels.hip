@@ -2836,19 +2836,22 @@ __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_kernel(Q4Ar
 // Launches of few rows stage all of their x once, compactly (the three parts
 // of each live row), and then run the K loop without barriers: LDS bytes for
 // the x parts of a workgroup's column range (half of C when split: two such
-// workgroups fit a CU), and ints for its chunk exponents.
-constexpr int q4_pre_bytes(bool split) { return split ? 57344 : 98304; }
+// workgroups fit a CU; one row of C <= 6826 for one column tile per
+// workgroup: four fit), and ints for its chunk exponents.
+constexpr int q4_pre_bytes(bool split, int ct) {
+  return split ? 57344 : ct == 1 ? 40960 : 98304;
+}
 constexpr int Q4_PRE_K = 256;
 
 // The same order as proj_q4_kernel for NR rows (1..3), every x chunk staged
 // in the prologue.
 template <bool SPLIT, int CT, int NR>
 __global__ __launch_bounds__(64 * CT * (SPLIT ? 2 : 4)) void proj_q4_pre_kernel(Q4Args a) {
-  static_assert(CT == 4, "4 column tiles per workgroup");
+  static_assert(CT == 1 || CT == 2 || CT == 4, "4, 2 or 1 column tiles per workgroup");
   constexpr int NQ = SPLIT ? 2 : 4;            // quarters per workgroup
   constexpr int NTHR = 64 * CT * NQ;
   // x parts [block of the range][d][row][part][16 bytes]
-  __shared__ __align__(16) unsigned char xp[q4_pre_bytes(SPLIT)];
+  __shared__ __align__(16) unsigned char xp[q4_pre_bytes(SPLIT, CT)];
   __shared__ int kp[Q4_PRE_K];                 // [row][chunk of the range]
   const int bid = (int)xcd_contiguous(blockIdx.x, gridDim.x);
   const bool second = bid >= a.p[0].wgs;
@@ -3055,12 +3058,16 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   // would spill).  Fewer, fuller workgroups beat more of 2 tiles each: with 4
   // wave columns the split of x is shared by twice the waves.
   const int tiles = R0 / 16 + (Wq1 ? R1 / 16 : 0);
+  // one row, too few groups of 4 tiles, enough single tiles: one workgroup
+  // per tile, the up-front stage of x small enough for four per CU
+  const bool tile1 = rows == 1 && tiles / 4 < kQ4SplitBelow && tiles >= kQ4SplitBelow &&
+                     C / 32 * 192 <= q4_pre_bytes(false, 1);
   // 5-8 rows: two column tiles per wave (one x operand read serves both)
   // when two workgroups per group of 8 tiles still fill the chip
   const bool pair = rows > 4 && rows <= 8 && R0 % 128 == 0 && (!Wq1 || R1 % 128 == 0) &&
                     tiles / 8 * 2 >= kQ4SplitBelow;
-  const bool split = tiles / 4 < kQ4SplitBelow || rows > 4;
-  const int ct = 4;
+  const bool split = (tiles / 4 < kQ4SplitBelow || rows > 4) && !tile1;
+  const int ct = tile1 ? 1 : 4;
   const int f = split ? 2 : 1;
   const int tw = pair ? 2 : 1;
   Q4Args a{};
@@ -3076,9 +3083,12 @@ int launch_proj_q4(const float *x, int64_t rows, int C, const void *Wq0, int R0,
   }
   // all of a workgroup's x staged up front when it fits
   const int range = split ? C / 2 : C;
-  const bool pre = rows <= 3 && (int64_t)range / 32 * 192 * rows <= q4_pre_bytes(split) &&
+  const bool pre = rows <= 3 && (int64_t)range / 32 * 192 * rows <= q4_pre_bytes(split, ct) &&
                    (int64_t)range / 256 * rows <= Q4_PRE_K;
-  if (pre)
+  if (tile1)
+    hipLaunchKernelGGL((proj_q4_pre_kernel<false, 1, 1>), dim3((unsigned)(a.p[0].wgs + a.p[1].wgs)),
+                       dim3(256), 0, s, a);
+  else if (pre)
     !split ? launch_q4_pre<false, 4>(a, s) : launch_q4_pre<true, 4>(a, s);
   else if (!split)
     launch_q4<1, false, 4>(a, s);

@@ -245,9 +245,9 @@ def test_q4_infinite_x_matches_oracle(orc, rows, R):
     +inf, -inf or NaN, with the row's other values scaled by the largest
     finite magnitude of their chunk (x of magnitude up to 12 here, which a
     scale set by the infinity would overflow in binary16).  Rows without one
-    keep the bits of the call without infinities.  Every launch shape: the
-    up-front staging whole and split, one and two column tiles per wave, four
-    row tiles."""
+    keep the bits of the call without infinities.  Every launch shape: one
+    row with one or four tiles per workgroup, the up-front staging, one and
+    two column tiles per wave, four row tiles."""
     say(f"proj_q4 infinite x rows={rows} R={R}")
     C = 2048
     x, q, sc = q4_operands(167, rows, R, C)
@@ -317,9 +317,9 @@ def test_q4_staging_variants_agree_bit_for_bit():
 def test_q4_paired_tiles_agree_bit_for_bit():
     """At the layer's out_proj size (C = 6144, 5120 outputs: fewer 64-output
     groups than CUs) a call of 4-8 rows runs two workgroups per group of 4
-    column tiles (one tile per wave: too few groups of 8 tiles to pair them)
-    and 1-3 rows the up-front staging in the same split: every row of an
-    8-row call equals the same row in the calls of 1..7 rows."""
+    column tiles (one tile per wave: too few groups of 8 tiles to pair them),
+    2-3 rows the up-front staging and 1 row one workgroup per tile: every row
+    of an 8-row call equals the same row in the calls of 1..7 rows."""
     say("proj_q4 paired tiles")
     C, R = 6144, 5120
     x, q, sc = q4_operands(163, 8, R, C)
